@@ -1,0 +1,125 @@
+"""LoftQ's alternating minimisation of ||W - (Q + BA)||_F, step by step.
+
+Test infrastructure only (see the package docstring).
+
+The pages ([LoftQ blog] §2.2-2.3, §3.2; [PEFT guide] "LoftQ 初始化"):
+  * objective: min over Q and a rank-r Delta = BA of ||W - (Q + Delta)||_F^2;
+  * quantization step: with Delta fixed, quantize the residual W - Delta
+    (round-to-nearest);
+  * low-rank step: with Q fixed, Delta = best rank-r approximation of W - Q;
+  * alternate a preset number of times (iterative_steps, default 5);
+  * the one-step variant (replace_lora_weights_loftq) is a single alternation
+    that keeps NF4(W) as the base and only refits the LoRA weights.
+
+Readings:
+  * Delta_0 = 0, so alternation 1 quantizes W itself; T = 0 is plain NF4 QLoRA
+    (B = A = 0).
+  * Q is NF4 with blockwise-64 absmax; with double quant on, the codes are chosen
+    with the fp32 absmax and Q is reconstructed with the double-quantized a'.
+  * The residual W - B A is formed in fp64 and rounded once to fp32 before
+    quantization.
+  * objective[0] = ||W - Q_1|| / ||W|| (plain NF4 error); objective[t] =
+    ||W - Q_t - B_t A_t|| / ||W|| for t = 1..T, each computed directly.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from .nf4 import quantize_residual, dequantize
+from .double_quant import double_quant, dq_scales_expand
+from .rng import rademacher_sketch
+from .lowrank import exact_svd, randomized_svd, lora_factors
+
+__all__ = ["loftq_step", "loftq_init", "objective"]
+
+
+def _residual(W32: np.ndarray, B, A) -> np.ndarray:
+    if B is None:
+        return np.asarray(W32, dtype=np.float32)
+    prod = np.asarray(B, dtype=np.float64) @ np.asarray(A, dtype=np.float64)
+    return (np.asarray(W32, dtype=np.float64) - prod).astype(np.float32)
+
+
+def loftq_step(W32: np.ndarray, B_prev, A_prev, *, rank: int, t: int = 1, blocksize: int = 64,
+               double_quant_on: bool = True, dq_blocksize: int = 256, exact: bool = False,
+               oversample: int = 8, power_iters: int = 2, seed: int = 42, omega=None) -> dict:
+    """One alternation: Q_t = NF4(W - B_prev A_prev), then (B_t, A_t) = SVD_r(W - deq Q_t)."""
+    W32 = np.asarray(W32, dtype=np.float32)
+    d, k = W32.shape
+    R = _residual(W32, B_prev, A_prev)
+    codes, absmax = quantize_residual(R.ravel(), blocksize)
+    out = dict(R=R, codes=codes, absmax=absmax)
+    if double_quant_on:
+        qa, s = double_quant(absmax, dq_blocksize)
+        scale = dq_scales_expand(qa, s, dq_blocksize)
+        out.update(qabsmax=qa, dq_scale=s)
+    else:
+        scale = absmax
+    out["scale"] = scale
+    E = dequantize(codes, scale, blocksize, W=W32.ravel()).reshape(d, k)
+    out["E"] = E
+    out["E_sumsq"] = float(np.sum(E.astype(np.float64) ** 2))
+    if exact:
+        U, s_r, V = exact_svd(E, rank)
+    else:
+        l = rank + oversample
+        if omega is None:
+            omega = rademacher_sketch(seed, t, k, l)
+        U, s_r, V = randomized_svd(E, rank, omega, power_iters)
+        out["omega"] = omega
+    B, A = lora_factors(U, s_r, V)
+    out.update(B=B, A=A, sigma=s_r, U=U, V=V)
+    return out
+
+
+def objective(W32: np.ndarray, codes: np.ndarray, scale: np.ndarray, B, A, blocksize: int = 64) -> float:
+    """||W - deq(Q) - BA||_F / ||W||_F in fp64."""
+    W = np.asarray(W32, dtype=np.float64)
+    deq = dequantize(codes, scale, blocksize).astype(np.float64).reshape(W.shape)
+    res = W - deq
+    if B is not None:
+        res = res - np.asarray(B, dtype=np.float64) @ np.asarray(A, dtype=np.float64)
+    return float(np.sqrt(np.sum(res * res)) / np.sqrt(np.sum(W * W)))
+
+
+def loftq_init(W32: np.ndarray, *, rank: int, iterative_steps: int = 5, blocksize: int = 64,
+               double_quant_on: bool = True, dq_blocksize: int = 256, exact: bool = False,
+               oversample: int = 8, power_iters: int = 2, seed: int = 42, keep_steps: bool = False) -> dict:
+    """The whole initialisation: T alternations from Delta_0 = 0, objective per alternation."""
+    W32 = np.asarray(W32, dtype=np.float32)
+    d, k = W32.shape
+    T = int(iterative_steps)
+    kw = dict(rank=rank, blocksize=blocksize, double_quant_on=double_quant_on, dq_blocksize=dq_blocksize,
+              exact=exact, oversample=oversample, power_iters=power_iters, seed=seed)
+    obj = np.zeros(T + 1)
+    steps = []
+    B = A = None
+    if T == 0:
+        codes, absmax = quantize_residual(W32.ravel(), blocksize)
+        res = dict(codes=codes, absmax=absmax)
+        if double_quant_on:
+            qa, s = double_quant(absmax, dq_blocksize)
+            res.update(qabsmax=qa, dq_scale=s)
+            scale = dq_scales_expand(qa, s, dq_blocksize)
+        else:
+            scale = absmax
+        obj[0] = objective(W32, codes, scale, None, None, blocksize)
+        res.update(B=np.zeros((d, rank)), A=np.zeros((rank, k)), sigma=np.zeros(rank), objective=obj)
+        return res
+    last = None
+    for t in range(1, T + 1):
+        st = loftq_step(W32, B, A, t=t, **kw)
+        if t == 1:
+            obj[0] = objective(W32, st["codes"], st["scale"], None, None, blocksize)
+        obj[t] = objective(W32, st["codes"], st["scale"], st["B"], st["A"], blocksize)
+        B, A = st["B"], st["A"]
+        last = st
+        if keep_steps:
+            steps.append(st)
+    res = {key: last[key] for key in ("codes", "absmax", "B", "A", "sigma", "scale")}
+    if double_quant_on:
+        res.update(qabsmax=last["qabsmax"], dq_scale=last["dq_scale"])
+    res["objective"] = obj
+    if keep_steps:
+        res["steps"] = steps
+    return res
