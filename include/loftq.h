@@ -1,0 +1,157 @@
+/*
+ * libloftq: LoftQ initialisation (NF4 + double quant + rank-r SVD) on one
+ * AMD Instinct MI355X (gfx950).  C ABI.
+ *
+ * LoftQ initialises a quantized base Q and a LoRA adapter BA for each linear
+ * layer W (d x k, y = W x) by alternately minimising ||W - (Q + BA)||_F:
+ * quantize the residual W - BA with Delta = BA fixed, then refit BA as the
+ * best rank-r approximation of W - Q with Q fixed ("LoftQ：协同优化量化与LoRA，
+ * 实现高效大语言模型微调", §2.2-2.3).  Q is QLoRA's 4-bit NormalFloat with
+ * blockwise absmax scaling and optional double quantization of the absmax
+ * constants ("QLoRA论文概述", NF4 and double-quantization bullets; PEFT guide
+ * "量化", BitsAndBytesConfig bullets).
+ *
+ * Conventions for every call:
+ *   - Matrices are row-major.  W is rows x cols (d x k); B is rows x r and A is
+ *     r x cols (LoRA's B in R^{d x r}, A in R^{r x k}, "参数高效微调：LoRA、Adapter
+ *     与 QLoRA", §2.2).
+ *   - Pointers marked [device] are device memory on the current HIP device;
+ *     [host] pointers are host memory.  Device pointers must be 16-byte aligned.
+ *   - The caller owns every buffer.  The library allocates no device memory on
+ *     any call; scratch comes from the caller's workspace.
+ *   - `stream` is a hipStream_t (NULL = the null stream).  Work is enqueued
+ *     asynchronously; outputs are valid once the caller synchronises the
+ *     stream.  Calls on different streams share no mutable state.
+ *   - Arguments are validated before anything is enqueued; on any error no
+ *     output is written.
+ *   - Inputs must be finite (NaN/Inf give unspecified codes, never a fault).
+ *   - NF4 block size is 64 consecutive elements of the row-major flattening;
+ *     a ragged last block is allowed.  Packed codes hold two per byte, element
+ *     2i in the high nibble; the byte count is ceil(rows*cols / 2).
+ */
+#ifndef LOFTQ_H
+#define LOFTQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  LOFTQ_OK = 0,
+  LOFTQ_ERR_INVALID_ARG = 1,  /* null pointer, bad size/shape, misalignment */
+  LOFTQ_ERR_UNSUPPORTED = 2,  /* bits != 4, blocksize != 64, dq_blocksize != 256, too-large exact SVD */
+  LOFTQ_ERR_WORKSPACE = 3,    /* workspace smaller than the *_workspace_bytes query */
+  LOFTQ_ERR_HIP = 4           /* a HIP runtime call or kernel launch failed */
+} loftq_status_t;
+
+typedef enum { LOFTQ_F32 = 0, LOFTQ_BF16 = 1 } loftq_dtype_t;
+
+/* Mirrors loftq_config {bits, iterative_steps, seed} and LoraConfig.r from the
+ * LoftQ blog (§3.2) and bnb_4bit_use_double_quant from the PEFT guide. */
+typedef struct {
+  int32_t bits;             /* must be 4 */
+  int32_t iterative_steps;  /* T >= 0 alternations; 0 = plain NF4 (B = A = 0) */
+  int32_t rank;             /* r >= 1 */
+  int32_t blocksize;        /* must be 64 */
+  int32_t double_quant;     /* 0 or 1 */
+  int32_t dq_blocksize;     /* must be 256 */
+  int32_t oversample;       /* p >= 0; sketch width l = r + p (randomized SVD) */
+  int32_t power_iters;      /* q >= 0 subspace iterations (randomized SVD) */
+  int32_t exact_svd;        /* 1: exact SVD (min(rows, cols) <= 512); 0: randomized */
+  int32_t reserved;         /* must be 0 */
+  uint64_t seed;            /* sketch seed (loftq_config seed, default 42) */
+} loftq_config_t;
+
+/* Quantization step ("LoftQ...", §2.3: quantize the residual W - Delta; the
+ * QLoRA blog "QLoRA技术解析...", §2.1: absmax-normalise then nearest codebook
+ * entry).  R = W - B A (B, A both NULL: R = W), formed in fp32; per block of 64,
+ * a = max |R| (absmax[b], fp32); x = fl32(R / a) (a = 0: x = 0); code = index of
+ * the nearest NF4 level, ties to the lower index.
+ *   W      [device] rows x cols of dtype wdt
+ *   B, A   [device] fp32 rows x r and r x cols, or both NULL (then r is ignored)
+ *   packed [device] ceil(rows*cols/2) bytes out
+ *   absmax [device] ceil(rows*cols/64) fp32 out
+ * Codes and absmax are bit-exact against an fp32 reference when B = A = NULL. */
+loftq_status_t loftq_nf4_quantize(const void* W, loftq_dtype_t wdt, int64_t rows, int64_t cols,
+                                  const float* B, const float* A, int32_t r, int32_t blocksize,
+                                  uint8_t* packed, float* absmax, void* stream);
+
+/* Double quantization ("QLoRA论文概述", double-quantization bullet: quantize the
+ * quantization constants again).  Per group of dq_blocksize consecutive absmax
+ * values (ragged last group allowed): s = fl32(max / 127),
+ * q = clamp(rint_even(fl32(a / s)), 0, 127) (s = 0: q = 0); reconstruction
+ * a' = fl32(q * s).
+ *   absmax   [device] nblocks fp32 (non-negative)
+ *   qabsmax  [device] nblocks int8 out
+ *   dq_scale [device] ceil(nblocks/dq_blocksize) fp32 out */
+loftq_status_t loftq_double_quant(const float* absmax, int64_t nblocks, int32_t dq_blocksize,
+                                  int8_t* qabsmax, float* dq_scale, void* stream);
+
+/* Dequantization, optionally fused with the subtraction W - deq(Q) that feeds
+ * the low-rank step ("LoftQ...", §2.3: the SVD of W - Q).  deq = fl32(c[code]*a')
+ * with a' = absmax[b] (qabsmax == NULL) or fl32(qabsmax[b] * dq_scale[b/dq_bs]);
+ * out = deq (W == NULL) or fl32(W - deq).
+ *   packed           [device] codes from loftq_nf4_quantize
+ *   absmax           [device] or NULL when qabsmax/dq_scale are given
+ *   qabsmax,dq_scale [device] or both NULL
+ *   W                [device] or NULL
+ *   out              [device] rows*cols fp32 out
+ *   sumsq            [device] 1 double out (sum of out^2) or NULL */
+loftq_status_t loftq_nf4_dequantize(const uint8_t* packed, const float* absmax, const int8_t* qabsmax,
+                                    const float* dq_scale, int64_t rows, int64_t cols, int32_t blocksize,
+                                    int32_t dq_blocksize, const void* W, loftq_dtype_t wdt, float* out,
+                                    double* sumsq, void* stream);
+
+/* Low-rank step ("LoftQ...", §2.3: best rank-r approximation of W - Q from its
+ * r largest singular triplets, Delta = U_r S_r V_r^T).  exact = 1: the SVD of E
+ * itself (one-sided Jacobi, min(rows, cols) <= 512).  exact = 0: randomized
+ * subspace iteration with sketch width l = r + oversample (l <= min(rows, cols),
+ * l <= 128) and power_iters rounds; the sketch is `omega` (cols x l fp32) or, if
+ * NULL, the +-1 SplitMix64 sketch of (seed, t).  Outputs B = U_r S_r^{1/2},
+ * A = S_r^{1/2} V_r^T, sigma = S_r (descending).
+ *   E      [device] rows x cols fp32
+ *   B, A   [device] rows x r, r x cols fp32 out
+ *   sigma  [device] r fp32 out
+ *   ws     [device] loftq_lowrank_svd_workspace_bytes(...) bytes */
+loftq_status_t loftq_lowrank_svd(const float* E, int64_t rows, int64_t cols, int32_t r, int32_t oversample,
+                                 int32_t power_iters, int32_t exact, const float* omega, uint64_t seed,
+                                 int32_t t, float* B, float* A, float* sigma, void* ws, size_t ws_bytes,
+                                 void* stream);
+size_t loftq_lowrank_svd_workspace_bytes(int64_t rows, int64_t cols, int32_t r, int32_t oversample,
+                                         int32_t exact);
+
+/* The whole initialisation ("LoftQ...", §2.3 and §3.2; PEFT guide "LoftQ 初始化"):
+ * Delta_0 = 0; for t = 1..T: Q_t = NF4(W - B_{t-1} A_{t-1}) (+ double quant),
+ * (B_t, A_t) = rank-r SVD of W - deq(Q_t).  Outputs the final Q_T (packed,
+ * absmax, and qabsmax/dq_scale when double_quant), B_T, A_T, sigma of
+ * alternation T, and objective[t] = ||W - deq(Q_t) - B_t A_t||_F / ||W||_F for
+ * t = 0..T (objective[0] = plain NF4 error ||W - deq(Q_1)|| / ||W||).
+ *   cfg               [host]
+ *   packed, absmax    [device] as loftq_nf4_quantize
+ *   qabsmax, dq_scale [device] as loftq_double_quant (ignored if !double_quant)
+ *   B, A, sigma       [device] as loftq_lowrank_svd
+ *   objective         [device] T+1 doubles out
+ *   ws                [device] loftq_workspace_bytes(rows, cols, cfg) bytes */
+loftq_status_t loftq_init(const void* W, loftq_dtype_t wdt, int64_t rows, int64_t cols,
+                          const loftq_config_t* cfg, uint8_t* packed, float* absmax, int8_t* qabsmax,
+                          float* dq_scale, float* B, float* A, double* objective, float* sigma, void* ws,
+                          size_t ws_bytes, void* stream);
+size_t loftq_workspace_bytes(int64_t rows, int64_t cols, const loftq_config_t* cfg);
+
+/* Fills cfg with the defaults (bits 4, T 5, r 16, blocksize 64, double quant on,
+ * dq_blocksize 256, p 8, q 2, randomized, seed 42). [host] */
+void loftq_default_config(loftq_config_t* cfg);
+
+/* Static message for a status code. */
+const char* loftq_status_string(loftq_status_t status);
+
+/* The 16 NF4 levels the library uses, ascending (index 7 = 0). [host] out16 */
+void loftq_nf4_codebook(float* out16);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* LOFTQ_H */

@@ -1,0 +1,228 @@
+"""ctypes binding for libloftq: LoftQ initialisation on AMD Instinct MI355X (gfx950).
+
+Argument marshalling only.  Every step of the computation runs in the HIP
+kernels of ``libloftq.so`` (built in-tree by ``_build.build()``); torch is used
+for device memory and the current stream.  Importing this package without the
+built library raises ImportError: there is no CPU fallback.
+
+The functions carry the C entry points' names (see include/loftq.h):
+    loftq_nf4_quantize, loftq_double_quant, loftq_nf4_dequantize,
+    loftq_lowrank_svd, loftq_init
+and return freshly allocated torch tensors on the input's device.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libloftq.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"libloftq.so is not built ({LIB_PATH}); run __graft_entry__.build() first")
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+LOFTQ_F32, LOFTQ_BF16 = 0, 1
+STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported configuration", 3: "workspace too small",
+          4: "HIP runtime error"}
+
+EXPORTS = ["loftq_nf4_quantize", "loftq_double_quant", "loftq_nf4_dequantize", "loftq_lowrank_svd",
+           "loftq_lowrank_svd_workspace_bytes", "loftq_init", "loftq_workspace_bytes", "loftq_default_config",
+           "loftq_status_string", "loftq_nf4_codebook"]
+
+
+class LoftqConfig(ctypes.Structure):
+    _fields_ = [("bits", ctypes.c_int32), ("iterative_steps", ctypes.c_int32), ("rank", ctypes.c_int32),
+                ("blocksize", ctypes.c_int32), ("double_quant", ctypes.c_int32), ("dq_blocksize", ctypes.c_int32),
+                ("oversample", ctypes.c_int32), ("power_iters", ctypes.c_int32), ("exact_svd", ctypes.c_int32),
+                ("reserved", ctypes.c_int32), ("seed", ctypes.c_uint64)]
+
+
+_P, _I64, _I32, _U64, _SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_uint64, ctypes.c_size_t
+
+
+def _sig(name, res, args):
+    f = getattr(_lib, name, None)
+    if f is None:
+        return None
+    f.restype, f.argtypes = res, args
+    return f
+
+
+_c_quant = _sig("loftq_nf4_quantize", ctypes.c_int, [_P, ctypes.c_int, _I64, _I64, _P, _P, _I32, _I32, _P, _P, _P])
+_c_dq = _sig("loftq_double_quant", ctypes.c_int, [_P, _I64, _I32, _P, _P, _P])
+_c_deq = _sig("loftq_nf4_dequantize", ctypes.c_int,
+              [_P, _P, _P, _P, _I64, _I64, _I32, _I32, _P, ctypes.c_int, _P, _P, _P])
+_c_svd = _sig("loftq_lowrank_svd", ctypes.c_int,
+              [_P, _I64, _I64, _I32, _I32, _I32, _I32, _P, _U64, _I32, _P, _P, _P, _P, _SZ, _P])
+_c_svd_ws = _sig("loftq_lowrank_svd_workspace_bytes", _SZ, [_I64, _I64, _I32, _I32, _I32])
+_c_init = _sig("loftq_init", ctypes.c_int,
+               [_P, ctypes.c_int, _I64, _I64, ctypes.POINTER(LoftqConfig), _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ,
+                _P])
+_c_init_ws = _sig("loftq_workspace_bytes", _SZ, [_I64, _I64, ctypes.POINTER(LoftqConfig)])
+_c_defaults = _sig("loftq_default_config", None, [ctypes.POINTER(LoftqConfig)])
+_c_status = _sig("loftq_status_string", ctypes.c_char_p, [ctypes.c_int])
+_c_codebook = _sig("loftq_nf4_codebook", None, [ctypes.POINTER(ctypes.c_float)])
+
+
+class LoftqError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        super().__init__(f"{fn}: {STATUS.get(status, status)} (status {status})")
+
+
+def _check(fn: str, st: int) -> None:
+    if st != 0:
+        raise LoftqError(fn, st)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _wdtype(W: torch.Tensor) -> int:
+    if W.dtype == torch.float32:
+        return LOFTQ_F32
+    if W.dtype == torch.bfloat16:
+        return LOFTQ_BF16
+    raise TypeError("W must be float32 or bfloat16")
+
+
+def _contig(t: torch.Tensor, what: str) -> torch.Tensor:
+    if not t.is_cuda or not t.is_contiguous():
+        raise ValueError(f"{what} must be a contiguous device tensor")
+    return t
+
+
+def exported_symbols():
+    """Names from include/loftq.h that the loaded library exports."""
+    return [name for name in EXPORTS if hasattr(_lib, name)]
+
+
+def nf4_codebook() -> list:
+    buf = (ctypes.c_float * 16)()
+    _c_codebook(buf)
+    return list(buf)
+
+
+def default_config(**overrides) -> LoftqConfig:
+    cfg = LoftqConfig()
+    _c_defaults(ctypes.byref(cfg))
+    for k, v in overrides.items():
+        if not hasattr(cfg, k):
+            raise KeyError(k)
+        setattr(cfg, k, int(v))
+    return cfg
+
+
+def loftq_nf4_quantize(W: torch.Tensor, B: Optional[torch.Tensor] = None, A: Optional[torch.Tensor] = None,
+                       packed: Optional[torch.Tensor] = None, absmax: Optional[torch.Tensor] = None, stream=None):
+    """Quantize R = W - B A (or W) to packed NF4 codes and blockwise absmax."""
+    _contig(W, "W")
+    rows, cols = (W.shape[0], W.shape[1]) if W.dim() == 2 else (1, W.numel())
+    n = rows * cols
+    r = 0
+    if B is not None:
+        _contig(B, "B"), _contig(A, "A")
+        r = B.shape[1]
+    if packed is None:
+        packed = torch.empty((n + 1) // 2, dtype=torch.uint8, device=W.device)
+    if absmax is None:
+        absmax = torch.empty((n + 63) // 64, dtype=torch.float32, device=W.device)
+    _check("loftq_nf4_quantize", _c_quant(_ptr(W), _wdtype(W), rows, cols, _ptr(B), _ptr(A), r, 64, _ptr(packed),
+                                          _ptr(absmax), _stream(stream)))
+    return packed, absmax
+
+
+def loftq_double_quant(absmax: torch.Tensor, stream=None):
+    _contig(absmax, "absmax")
+    nb = absmax.numel()
+    q = torch.empty(nb, dtype=torch.int8, device=absmax.device)
+    s = torch.empty((nb + 255) // 256, dtype=torch.float32, device=absmax.device)
+    _check("loftq_double_quant", _c_dq(_ptr(absmax), nb, 256, _ptr(q), _ptr(s), _stream(stream)))
+    return q, s
+
+
+def loftq_nf4_dequantize(packed: torch.Tensor, shape, absmax: Optional[torch.Tensor] = None,
+                         qabsmax: Optional[torch.Tensor] = None, dq_scale: Optional[torch.Tensor] = None,
+                         W: Optional[torch.Tensor] = None, with_sumsq: bool = False, stream=None):
+    """deq(Q), or W - deq(Q) when W is given; optionally also sum of squares (fp64)."""
+    rows, cols = shape
+    out = torch.empty((rows, cols), dtype=torch.float32, device=packed.device)
+    ss = torch.empty(1, dtype=torch.float64, device=packed.device) if with_sumsq else None
+    wdt = _wdtype(W) if W is not None else LOFTQ_F32
+    _check("loftq_nf4_dequantize",
+           _c_deq(_ptr(packed), _ptr(absmax), _ptr(qabsmax), _ptr(dq_scale), rows, cols, 64, 256, _ptr(W), wdt,
+                  _ptr(out), _ptr(ss), _stream(stream)))
+    return (out, ss) if with_sumsq else out
+
+
+def lowrank_workspace_bytes(rows: int, cols: int, r: int, oversample: int, exact: bool) -> int:
+    return int(_c_svd_ws(rows, cols, r, oversample, int(bool(exact))))
+
+
+def loftq_lowrank_svd(E: torch.Tensor, r: int, oversample: int = 8, power_iters: int = 2, exact: bool = False,
+                      omega: Optional[torch.Tensor] = None, seed: int = 42, t: int = 1, stream=None):
+    """Rank-r factors (B, A, sigma) of E by exact or randomized SVD."""
+    _contig(E, "E")
+    rows, cols = E.shape
+    ws_bytes = lowrank_workspace_bytes(rows, cols, r, oversample, exact)
+    ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=E.device)
+    B = torch.empty((rows, r), dtype=torch.float32, device=E.device)
+    A = torch.empty((r, cols), dtype=torch.float32, device=E.device)
+    sigma = torch.empty(r, dtype=torch.float32, device=E.device)
+    _check("loftq_lowrank_svd",
+           _c_svd(_ptr(E), rows, cols, r, oversample, power_iters, int(bool(exact)), _ptr(omega), seed, t, _ptr(B),
+                  _ptr(A), _ptr(sigma), _ptr(ws), ws_bytes, _stream(stream)))
+    return B, A, sigma
+
+
+def workspace_bytes(rows: int, cols: int, cfg: LoftqConfig) -> int:
+    return int(_c_init_ws(rows, cols, ctypes.byref(cfg)))
+
+
+class InitBuffers:
+    """Caller-owned outputs and workspace for repeated loftq_init calls on one shape."""
+
+    def __init__(self, rows: int, cols: int, cfg: LoftqConfig, device="cuda"):
+        n = rows * cols
+        nb = (n + 63) // 64
+        self.cfg = cfg
+        self.packed = torch.empty((n + 1) // 2, dtype=torch.uint8, device=device)
+        self.absmax = torch.empty(nb, dtype=torch.float32, device=device)
+        self.qabsmax = torch.empty(max(nb, 1), dtype=torch.int8, device=device)
+        self.dq_scale = torch.empty(max((nb + 255) // 256, 1), dtype=torch.float32, device=device)
+        self.B = torch.empty((rows, cfg.rank), dtype=torch.float32, device=device)
+        self.A = torch.empty((cfg.rank, cols), dtype=torch.float32, device=device)
+        self.sigma = torch.empty(cfg.rank, dtype=torch.float32, device=device)
+        self.objective = torch.empty(cfg.iterative_steps + 1, dtype=torch.float64, device=device)
+        self.ws_bytes = workspace_bytes(rows, cols, cfg)
+        self.ws = torch.empty(max(self.ws_bytes, 16), dtype=torch.uint8, device=device)
+
+
+def loftq_init(W: torch.Tensor, cfg: Optional[LoftqConfig] = None, buffers: Optional[InitBuffers] = None,
+               stream=None, **overrides):
+    """LoftQ initialisation of one matrix; returns a dict of device tensors."""
+    _contig(W, "W")
+    if cfg is None:
+        cfg = default_config(**overrides)
+    rows, cols = W.shape
+    bufs = buffers if buffers is not None else InitBuffers(rows, cols, cfg, W.device)
+    _check("loftq_init",
+           _c_init(_ptr(W), _wdtype(W), rows, cols, ctypes.byref(cfg), _ptr(bufs.packed), _ptr(bufs.absmax),
+                   _ptr(bufs.qabsmax), _ptr(bufs.dq_scale), _ptr(bufs.B), _ptr(bufs.A), _ptr(bufs.objective),
+                   _ptr(bufs.sigma), _ptr(bufs.ws), bufs.ws_bytes, _stream(stream)))
+    out = dict(packed=bufs.packed, absmax=bufs.absmax, B=bufs.B, A=bufs.A, sigma=bufs.sigma,
+               objective=bufs.objective)
+    if cfg.double_quant:
+        out.update(qabsmax=bufs.qabsmax, dq_scale=bufs.dq_scale)
+    return out

@@ -1,0 +1,51 @@
+// Internal declarations shared by the libloftq translation units.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/loftq.h"
+
+namespace loftq {
+
+// NF4 tables handed to kernels by value (kernel arguments), built once on the
+// host from the quantile definition of the levels.
+//
+// Encoding uses a 33-cell uniform grid over x in [-1, 1]: cell g covers
+// [-1 + g/16, -1 + (g+1)/16) (cell 32 holds x >= 1).  Each cell contains at
+// most one decision threshold; cell_base[g] counts the thresholds below the
+// cell and cell_thr[g] is the threshold inside it (+inf if none), so the code
+// of x in cell g is cell_base[g] + (x > cell_thr[g]).
+struct Nf4Tables {
+  float level[16];      // ascending NF4 levels, fp32
+  float thr[15];        // thr[j]: for fp32 x, x > thr[j]  <=>  x > (level[j]+level[j+1])/2
+  float cell_thr[33];
+  int32_t cell_base[33];
+  int32_t valid;        // 1 if every grid invariant held at construction
+};
+
+const Nf4Tables& nf4_tables();
+
+// Window (absolute, in x units) inside which the fast path's x' = R * (1/a)
+// may disagree with fl32(R / a) about a threshold; such elements are redone with
+// an IEEE division.  |x' - fl32(R/a)| <= 3 * 2^-24 for |x| <= 1.
+constexpr float kDangerWindow = 9.5367431640625e-07f;  // 2^-20
+
+// ---- launchers (quant_kernels.hip) ----
+hipError_t launch_nf4_quantize(const void* W, loftq_dtype_t wdt, int64_t rows, int64_t cols,
+                               const float* B, const float* A, int r, uint8_t* packed, float* absmax,
+                               hipStream_t s);
+hipError_t launch_double_quant(const float* absmax, int64_t nblocks, int dqbs, int8_t* q, float* scale,
+                               hipStream_t s);
+// partial: per-workgroup sum of squares (deterministic) when non-null, else
+// atomically accumulated into sumsq (which is zeroed first) when sumsq non-null.
+hipError_t launch_nf4_dequantize(const uint8_t* packed, const float* absmax, const int8_t* q,
+                                 const float* dqscale, int64_t n, int dqbs, const void* W,
+                                 loftq_dtype_t wdt, float* out, double* partials, int* nparts,
+                                 double* sumsq, hipStream_t s);
+int dequant_num_partials(int64_t n);
+hipError_t launch_sumsq_weight(const void* W, loftq_dtype_t wdt, int64_t n, double* partials, int nparts,
+                               hipStream_t s);
+int sumsq_num_partials(int64_t n);
+
+}  // namespace loftq

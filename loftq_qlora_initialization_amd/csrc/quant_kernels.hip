@@ -1,0 +1,500 @@
+// NF4 quantize (optionally fused with the residual W - B A), double quant and
+// dequant(-subtract) kernels for gfx950.
+//
+// Work unit: a "group" of 16 consecutive elements of the row-major flattening,
+// four groups per 64-element absmax block.  The four lanes of a DPP quad hold one
+// block, so the block absmax takes two quad_perm exchanges and no LDS.  A group
+// is two 16-byte loads for bf16 (four for fp32) and one 8-byte store of packed
+// nibbles, so every wave moves contiguous 2 KB (bf16) in and 512 B out.
+//
+// Encoding: x' = R * (1/a) (one multiply), cell g = int(16 x' + 16) of a 33-cell
+// grid held in LDS, code = base[g] + (x' > thr[g]).  x' can differ from the
+// defined fl32(R / a) by at most 3 * 2^-24, so whenever x' lies within 2^-20 of
+// the cell's threshold the element is redone with an IEEE division and a full
+// threshold count.  Codes are therefore bit-identical to fl32(R / a) rounding.
+#include <float.h>
+
+#include "internal.h"
+
+namespace loftq {
+namespace {
+
+constexpr int kThreads = 256;
+
+__device__ __forceinline__ float quad_xor1(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float quad_xor2(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float quad_max(float v) {
+  v = fmaxf(v, quad_xor1(v));
+  return fmaxf(v, quad_xor2(v));
+}
+
+__device__ __forceinline__ void load16(const uint16_t* __restrict__ p, float v[16]) {
+  const uint4 a = *reinterpret_cast<const uint4*>(p);
+  const uint4 b = *reinterpret_cast<const uint4*>(p + 8);
+  const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    v[2 * i] = __uint_as_float(w[i] << 16);
+    v[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+  }
+}
+__device__ __forceinline__ void load16(const float* __restrict__ p, float v[16]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float4 q = reinterpret_cast<const float4*>(p)[i];
+    v[4 * i] = q.x; v[4 * i + 1] = q.y; v[4 * i + 2] = q.z; v[4 * i + 3] = q.w;
+  }
+}
+__device__ __forceinline__ float load1(const uint16_t* p, int64_t i) {
+  return __uint_as_float(static_cast<uint32_t>(p[i]) << 16);
+}
+__device__ __forceinline__ float load1(const float* p, int64_t i) { return p[i]; }
+
+struct EncodeLds {
+  float2 cell[33];  // (threshold, base code as int bits)
+  float thr[15];
+  float level[16];
+};
+
+__device__ __forceinline__ void fill_lds(EncodeLds& s, const Nf4Tables& t) {
+  const int tid = threadIdx.x;
+  if (tid < 33) s.cell[tid] = make_float2(t.cell_thr[tid], __int_as_float(t.cell_base[tid]));
+  if (tid < 15) s.thr[tid] = t.thr[tid];
+  if (tid < 16) s.level[tid] = t.level[tid];
+}
+
+// Exact reference decision for one value: count of thresholds strictly below x.
+__device__ __forceinline__ uint32_t exact_code(float r, float a, const EncodeLds& s) {
+  const float x = (a > 0.f) ? r / a : 0.f;
+  uint32_t c = 0;
+#pragma unroll
+  for (int j = 0; j < 15; ++j) c += (x > s.thr[j]) ? 1u : 0u;
+  return c;
+}
+
+__device__ __forceinline__ int nib_shift(int e) { return 8 * ((e >> 1) & 3) + ((e & 1) ? 0 : 4); }
+
+// Encode 16 residual values sharing absmax a into two packed 32-bit words.
+__device__ __forceinline__ uint2 encode16(const float v[16], float a, const EncodeLds& s) {
+  const float inv = (a > 0.f) ? 1.0f / a : 0.f;
+  uint32_t danger = (a > 0.f && a < FLT_MIN) ? 0xFFFFu : 0u;
+  uint32_t w0 = 0, w1 = 0;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) {
+    const float x = v[e] * inv;
+    const float gf = __builtin_amdgcn_fmed3f(fmaf(x, 16.f, 16.f), 0.f, 32.f);
+    const float2 c = s.cell[static_cast<int>(gf)];
+    const uint32_t code = static_cast<uint32_t>(__float_as_int(c.y)) + ((x > c.x) ? 1u : 0u);
+    if (fabsf(x - c.x) < kDangerWindow) danger |= 1u << e;
+    if (e < 8) w0 |= code << nib_shift(e);
+    else w1 |= code << nib_shift(e);
+  }
+  if (danger) {
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      if (danger & (1u << e)) {
+        const uint32_t code = exact_code(v[e], a, s);
+        const int sh = nib_shift(e);
+        if (e < 8) w0 = (w0 & ~(0xFu << sh)) | (code << sh);
+        else w1 = (w1 & ~(0xFu << sh)) | (code << sh);
+      }
+    }
+  }
+  return make_uint2(w0, w1);
+}
+
+// ---------------------------------------------------------------------------
+// Quantize full 64-blocks of R = W (no adapter).  One thread per group; the
+// grid-stride loop advances whole quads, so a quad is always uniformly active.
+template <typename T>
+__global__ __launch_bounds__(kThreads) void quantize_plain_kernel(const T* __restrict__ W, int64_t ngroups,
+                                                                  uint8_t* __restrict__ packed,
+                                                                  float* __restrict__ absmax, Nf4Tables tab) {
+  __shared__ EncodeLds s;
+  fill_lds(s, tab);
+  __syncthreads();
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * kThreads;
+  for (int64_t g = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x; g < ngroups; g += stride) {
+    float v[16];
+    load16(W + g * 16, v);
+    float m = 0.f;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) m = fmaxf(m, fabsf(v[e]));
+    const float a = quad_max(m);
+    const uint2 w = encode16(v, a, s);
+    reinterpret_cast<uint2*>(packed)[g] = w;
+    if ((threadIdx.x & 3) == 0) absmax[g >> 2] = a;
+  }
+}
+
+// Any shape, any tail, optional adapter: one quad per 64-block with per-element
+// bounds and per-element (row, col) indexing.  Used for ragged tails and for
+// adapters on matrices whose column count is not a multiple of 64.
+template <typename T>
+__global__ __launch_bounds__(kThreads) void quantize_generic_kernel(const T* __restrict__ W, int64_t n,
+                                                                    int64_t cols, const float* __restrict__ B,
+                                                                    const float* __restrict__ A, int r,
+                                                                    int64_t block_begin, int64_t block_end,
+                                                                    uint8_t* __restrict__ packed,
+                                                                    float* __restrict__ absmax, Nf4Tables tab) {
+  __shared__ EncodeLds s;
+  fill_lds(s, tab);
+  __syncthreads();
+  const int64_t quads = static_cast<int64_t>(gridDim.x) * (kThreads / 4);
+  const int sub = threadIdx.x & 3;
+  for (int64_t blk = block_begin + static_cast<int64_t>(blockIdx.x) * (kThreads / 4) + (threadIdx.x >> 2);
+       blk < block_end; blk += quads) {
+    const int64_t base = blk * 64 + sub * 16;
+    float v[16];
+    float m = 0.f;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int64_t i = base + e;
+      float x = 0.f;
+      if (i < n) {
+        x = load1(W, i);
+        if (B != nullptr) {
+          const int64_t row = i / cols, col = i - row * cols;
+          float acc = 0.f;
+          for (int p = 0; p < r; ++p) acc = fmaf(B[row * r + p], A[static_cast<int64_t>(p) * cols + col], acc);
+          x = x - acc;
+        }
+      }
+      v[e] = x;
+      m = fmaxf(m, fabsf(x));
+    }
+    const float a = quad_max(m);
+    const uint2 w = encode16(v, a, s);
+    uint32_t word[2] = {w.x, w.y};
+#pragma unroll
+    for (int e = 0; e < 16; ++e)  // elements past the end leave a zero nibble
+      if (base + e >= n) word[e >> 3] &= ~(0xFu << nib_shift(e));
+#pragma unroll
+    for (int b = 0; b < 8; ++b) {
+      const int64_t i = base + 2 * b;
+      if (i < n) packed[i >> 1] = static_cast<uint8_t>((word[b >> 2] >> (8 * (b & 3))) & 0xFFu);
+    }
+    if (sub == 0) absmax[blk] = a;
+  }
+}
+
+// Fused residual R = W - B A on a 32-row x 256-column tile (cols % 64 == 0).
+// Thread t owns column group t % 16 of rows 2 (t / 16) and 2 (t / 16) + 1, so a
+// DPP quad holds four consecutive column groups of the same rows = one block
+// per row.  B and A are staged through LDS in rank chunks of 16.
+constexpr int kTileRows = 32, kTileCols = 256, kRankChunk = 16;
+
+template <typename T>
+__global__ __launch_bounds__(kThreads) void quantize_fused_kernel(const T* __restrict__ W, int64_t rows,
+                                                                  int64_t cols, const float* __restrict__ B,
+                                                                  const float* __restrict__ A, int r,
+                                                                  uint8_t* __restrict__ packed,
+                                                                  float* __restrict__ absmax, Nf4Tables tab) {
+  __shared__ EncodeLds s;
+  __shared__ float As[kRankChunk][kTileCols];
+  __shared__ float Bs[kTileRows][kRankChunk + 1];
+  fill_lds(s, tab);
+  const int tid = threadIdx.x;
+  const int cg = tid & 15, rq = tid >> 4;
+  const int64_t tiles_c = cols / kTileCols + ((cols % kTileCols) ? 1 : 0);
+  const int64_t tile_r = blockIdx.x / tiles_c, tile_c = blockIdx.x % tiles_c;
+  const int64_t row0 = tile_r * kTileRows + 2 * rq;
+  const int64_t col0 = tile_c * kTileCols + cg * 16;
+  const bool col_ok = col0 < cols;          // cols % 64 == 0 => whole quads agree
+  float acc[2][16];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[i][e] = 0.f;
+
+  for (int p0 = 0; p0 < r; p0 += kRankChunk) {
+    const int pc = min(kRankChunk, r - p0);
+    __syncthreads();
+    for (int idx = tid; idx < kRankChunk * kTileCols; idx += kThreads) {
+      const int p = idx / kTileCols, c = idx % kTileCols;
+      const int64_t gc = tile_c * kTileCols + c;
+      As[p][c] = (p < pc && gc < cols) ? A[static_cast<int64_t>(p0 + p) * cols + gc] : 0.f;
+    }
+    for (int idx = tid; idx < kTileRows * kRankChunk; idx += kThreads) {
+      const int rr = idx / kRankChunk, p = idx % kRankChunk;
+      const int64_t gr = tile_r * kTileRows + rr;
+      Bs[rr][p] = (p < pc && gr < rows) ? B[gr * r + p0 + p] : 0.f;
+    }
+    __syncthreads();
+    for (int p = 0; p < pc; ++p) {
+      const float b0 = Bs[2 * rq][p], b1 = Bs[2 * rq + 1][p];
+      const float4* ap = reinterpret_cast<const float4*>(&As[p][cg * 16]);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float4 av = ap[q];
+        acc[0][4 * q] = fmaf(b0, av.x, acc[0][4 * q]);
+        acc[0][4 * q + 1] = fmaf(b0, av.y, acc[0][4 * q + 1]);
+        acc[0][4 * q + 2] = fmaf(b0, av.z, acc[0][4 * q + 2]);
+        acc[0][4 * q + 3] = fmaf(b0, av.w, acc[0][4 * q + 3]);
+        acc[1][4 * q] = fmaf(b1, av.x, acc[1][4 * q]);
+        acc[1][4 * q + 1] = fmaf(b1, av.y, acc[1][4 * q + 1]);
+        acc[1][4 * q + 2] = fmaf(b1, av.z, acc[1][4 * q + 2]);
+        acc[1][4 * q + 3] = fmaf(b1, av.w, acc[1][4 * q + 3]);
+      }
+    }
+  }
+  if (r == 0) __syncthreads();
+
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int64_t row = row0 + i;
+    const bool ok = col_ok && row < rows;
+    float v[16];
+    float m = 0.f;
+    if (ok) {
+      load16(W + row * cols + col0, v);
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        v[e] = v[e] - acc[i][e];
+        m = fmaxf(m, fabsf(v[e]));
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) v[e] = 0.f;
+    }
+    const float a = quad_max(m);
+    if (ok) {
+      const uint2 w = encode16(v, a, s);
+      const int64_t g = (row * cols + col0) >> 4;
+      reinterpret_cast<uint2*>(packed)[g] = w;
+      if ((tid & 3) == 0) absmax[g >> 2] = a;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Double quant: one workgroup of 256 per group of dq_blocksize (= 256) absmax.
+__global__ __launch_bounds__(256) void double_quant_kernel(const float* __restrict__ absmax, int64_t nb, int dqbs,
+                                                           int8_t* __restrict__ q, float* __restrict__ scale) {
+  __shared__ float red[4];
+  const int64_t base = static_cast<int64_t>(blockIdx.x) * dqbs;
+  const int tid = threadIdx.x;
+  const bool ok = tid < dqbs && base + tid < nb;
+  const float a = ok ? absmax[base + tid] : 0.f;
+  float m = a;
+  for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+  if ((tid & 63) == 0) red[tid >> 6] = m;
+  __syncthreads();
+  m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  const float sc = m / 127.0f;
+  if (tid == 0) scale[blockIdx.x] = sc;
+  if (ok) {
+    int v = 0;
+    if (sc != 0.f) v = static_cast<int>(fminf(fmaxf(rintf(a / sc), 0.f), 127.f));
+    q[base + tid] = static_cast<int8_t>(v);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Dequant: out = deq or W - deq, plus sum of out^2.
+constexpr int kDeqMaxBlocks = 2048;
+
+template <typename T, bool kHasW, bool kDQ>
+__global__ __launch_bounds__(kThreads) void dequant_kernel(const uint8_t* __restrict__ packed,
+                                                           const float* __restrict__ absmax,
+                                                           const int8_t* __restrict__ qa,
+                                                           const float* __restrict__ dqs, int dqbs, int64_t n,
+                                                           const T* __restrict__ W, float* __restrict__ out,
+                                                           double* __restrict__ partials,
+                                                           double* __restrict__ sumsq, Nf4Tables tab) {
+  __shared__ float lvl[16];
+  __shared__ double red[kThreads / 64];
+  if (threadIdx.x < 16) lvl[threadIdx.x] = tab.level[threadIdx.x];
+  __syncthreads();
+  const int64_t ngroups = n >> 4;
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * kThreads;
+  double acc = 0.0;
+  for (int64_t g = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x; g < ngroups; g += stride) {
+    const int64_t b = g >> 2;
+    const float a = kDQ ? static_cast<float>(qa[b]) * dqs[b / dqbs] : absmax[b];
+    const uint2 pw = reinterpret_cast<const uint2*>(packed)[g];
+    float w[16];
+    if (kHasW) load16(W + g * 16, w);
+    float o[16];
+    float ss = 0.f;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const uint32_t word = (e < 8) ? pw.x : pw.y;
+      const uint32_t code = (word >> nib_shift(e)) & 0xFu;
+      const float d = lvl[code] * a;
+      o[e] = kHasW ? (w[e] - d) : d;
+      ss = fmaf(o[e], o[e], ss);
+    }
+    float4* op = reinterpret_cast<float4*>(out + g * 16);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) op[q] = make_float4(o[4 * q], o[4 * q + 1], o[4 * q + 2], o[4 * q + 3]);
+    acc += static_cast<double>(ss);
+  }
+  // ragged tail (fewer than 16 elements), handled by thread 0 of workgroup 0
+  if (blockIdx.x == 0 && threadIdx.x == 0) {
+    float ss = 0.f;
+    for (int64_t i = ngroups * 16; i < n; ++i) {
+      const int64_t b = i >> 6;
+      const float a = kDQ ? static_cast<float>(qa[b]) * dqs[b / dqbs] : absmax[b];
+      const uint32_t code = (packed[i >> 1] >> ((i & 1) ? 0 : 4)) & 0xFu;
+      const float d = lvl[code] * a;
+      const float o = kHasW ? (load1(W, i) - d) : d;
+      out[i] = o;
+      ss = fmaf(o, o, ss);
+    }
+    acc += static_cast<double>(ss);
+  }
+  for (int off = 32; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = acc;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    double t = 0.0;
+    for (int i = 0; i < kThreads / 64; ++i) t += red[i];
+    if (partials) partials[blockIdx.x] = t;
+    else if (sumsq) atomicAdd(sumsq, t);
+  }
+}
+
+__global__ void zero_double_kernel(double* p) { *p = 0.0; }
+
+// Sum of squares of W (for ||W||_F), per-workgroup partials.
+template <typename T>
+__global__ __launch_bounds__(kThreads) void sumsq_kernel(const T* __restrict__ W, int64_t n,
+                                                         double* __restrict__ partials) {
+  __shared__ double red[kThreads / 64];
+  const int64_t ngroups = n >> 4;
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * kThreads;
+  double acc = 0.0;
+  for (int64_t g = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x; g < ngroups; g += stride) {
+    float v[16];
+    load16(W + g * 16, v);
+    float ss = 0.f;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) ss = fmaf(v[e], v[e], ss);
+    acc += static_cast<double>(ss);
+  }
+  if (blockIdx.x == 0 && threadIdx.x == 0)
+    for (int64_t i = ngroups * 16; i < n; ++i) {
+      const double x = load1(W, i);
+      acc += x * x;
+    }
+  for (int off = 32; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = acc;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    double t = 0.0;
+    for (int i = 0; i < kThreads / 64; ++i) t += red[i];
+    partials[blockIdx.x] = t;
+  }
+}
+
+int grid_for_groups(int64_t ngroups, int per_thread) {
+  int64_t blocks = (ngroups + static_cast<int64_t>(kThreads) * per_thread - 1) / (static_cast<int64_t>(kThreads) * per_thread);
+  if (blocks < 1) blocks = 1;
+  if (blocks > 65536) blocks = 65536;
+  return static_cast<int>(blocks);
+}
+
+template <typename T>
+hipError_t quantize_typed(const T* W, int64_t rows, int64_t cols, const float* B, const float* A, int r,
+                          uint8_t* packed, float* absmax, hipStream_t s) {
+  const Nf4Tables& tab = nf4_tables();
+  const int64_t n = rows * cols;
+  if (n == 0) return hipSuccess;
+  const int64_t nblocks = (n + 63) / 64;
+  if (B == nullptr) {
+    const int64_t full = n / 64;
+    if (full > 0) {
+      hipLaunchKernelGGL(quantize_plain_kernel<T>, dim3(grid_for_groups(full * 4, 2)), dim3(kThreads), 0, s, W,
+                         full * 4, packed, absmax, tab);
+    }
+    if (full < nblocks) {
+      hipLaunchKernelGGL(quantize_generic_kernel<T>, dim3(1), dim3(kThreads), 0, s, W, n, cols,
+                         static_cast<const float*>(nullptr), static_cast<const float*>(nullptr), 0, full, nblocks,
+                         packed, absmax, tab);
+    }
+  } else if (cols % 64 == 0) {
+    const int64_t tiles = ((rows + kTileRows - 1) / kTileRows) * ((cols + kTileCols - 1) / kTileCols);
+    hipLaunchKernelGGL(quantize_fused_kernel<T>, dim3(static_cast<unsigned>(tiles)), dim3(kThreads), 0, s, W, rows,
+                       cols, B, A, r, packed, absmax, tab);
+  } else {
+    int64_t grid = (nblocks + (kThreads / 4) - 1) / (kThreads / 4);
+    if (grid > 65536) grid = 65536;
+    hipLaunchKernelGGL(quantize_generic_kernel<T>, dim3(static_cast<unsigned>(grid)), dim3(kThreads), 0, s, W, n,
+                       cols, B, A, r, static_cast<int64_t>(0), nblocks, packed, absmax, tab);
+  }
+  return hipGetLastError();
+}
+
+template <typename T>
+hipError_t dequant_typed(const uint8_t* packed, const float* absmax, const int8_t* q, const float* dqs, int64_t n,
+                         int dqbs, const T* W, float* out, double* partials, double* sumsq, hipStream_t s) {
+  const Nf4Tables& tab = nf4_tables();
+  const int grid = dequant_num_partials(n);
+  if (partials == nullptr && sumsq != nullptr) hipLaunchKernelGGL(zero_double_kernel, dim3(1), dim3(1), 0, s, sumsq);
+  const bool dq = q != nullptr;
+#define LQ_DEQ(HW, DQ)                                                                                            \
+  hipLaunchKernelGGL((dequant_kernel<T, HW, DQ>), dim3(grid), dim3(kThreads), 0, s, packed, absmax, q, dqs, dqbs, \
+                     n, W, out, partials, sumsq, tab)
+  if (W != nullptr) {
+    if (dq) LQ_DEQ(true, true); else LQ_DEQ(true, false);
+  } else {
+    if (dq) LQ_DEQ(false, true); else LQ_DEQ(false, false);
+  }
+#undef LQ_DEQ
+  return hipGetLastError();
+}
+
+}  // namespace
+
+int dequant_num_partials(int64_t n) {
+  int g = grid_for_groups((n >> 4) + 1, 4);
+  return g > kDeqMaxBlocks ? kDeqMaxBlocks : g;
+}
+int sumsq_num_partials(int64_t n) { return dequant_num_partials(n); }
+
+hipError_t launch_nf4_quantize(const void* W, loftq_dtype_t wdt, int64_t rows, int64_t cols, const float* B,
+                               const float* A, int r, uint8_t* packed, float* absmax, hipStream_t s) {
+  if (wdt == LOFTQ_BF16)
+    return quantize_typed(static_cast<const uint16_t*>(W), rows, cols, B, A, r, packed, absmax, s);
+  return quantize_typed(static_cast<const float*>(W), rows, cols, B, A, r, packed, absmax, s);
+}
+
+hipError_t launch_double_quant(const float* absmax, int64_t nblocks, int dqbs, int8_t* q, float* scale,
+                               hipStream_t s) {
+  if (nblocks == 0) return hipSuccess;
+  const int64_t groups = (nblocks + dqbs - 1) / dqbs;
+  hipLaunchKernelGGL(double_quant_kernel, dim3(static_cast<unsigned>(groups)), dim3(256), 0, s, absmax, nblocks,
+                     dqbs, q, scale);
+  return hipGetLastError();
+}
+
+hipError_t launch_nf4_dequantize(const uint8_t* packed, const float* absmax, const int8_t* q, const float* dqscale,
+                                 int64_t n, int dqbs, const void* W, loftq_dtype_t wdt, float* out, double* partials,
+                                 int* nparts, double* sumsq, hipStream_t s) {
+  if (nparts) *nparts = dequant_num_partials(n);
+  if (n == 0) {
+    if (sumsq && !partials) hipLaunchKernelGGL(zero_double_kernel, dim3(1), dim3(1), 0, s, sumsq);
+    return hipGetLastError();
+  }
+  if (wdt == LOFTQ_BF16)
+    return dequant_typed(packed, absmax, q, dqscale, n, dqbs, static_cast<const uint16_t*>(W), out, partials, sumsq, s);
+  return dequant_typed(packed, absmax, q, dqscale, n, dqbs, static_cast<const float*>(W), out, partials, sumsq, s);
+}
+
+hipError_t launch_sumsq_weight(const void* W, loftq_dtype_t wdt, int64_t n, double* partials, int nparts,
+                               hipStream_t s) {
+  if (wdt == LOFTQ_BF16)
+    hipLaunchKernelGGL(sumsq_kernel<uint16_t>, dim3(nparts), dim3(kThreads), 0, s,
+                       static_cast<const uint16_t*>(W), n, partials);
+  else
+    hipLaunchKernelGGL(sumsq_kernel<float>, dim3(nparts), dim3(kThreads), 0, s, static_cast<const float*>(W), n,
+                       partials);
+  return hipGetLastError();
+}
+
+}  // namespace loftq

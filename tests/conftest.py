@@ -33,3 +33,12 @@ def lib():
         pytest.skip("no GPU")
     import loftq_qlora_initialization_amd as lq
     return lq
+
+
+@pytest.fixture(autouse=True)
+def _announce_gpu_case(request):
+    """Name each GPU test on the real stderr before it runs, so a run that dies mid-test says where."""
+    if request.node.get_closest_marker("gpu") is not None:
+        sys.__stderr__.write(f"[gpu-case] {request.node.nodeid}\n")
+        sys.__stderr__.flush()
+    yield
