@@ -1,0 +1,145 @@
+// C-ABI entry points for the low-rank step and the whole alternating initialisation.
+#include "lowrank.h"
+
+namespace loftq {
+namespace {
+
+int64_t align256(int64_t x) { return (x + 255) / 256 * 256; }
+
+// Validation of the low-rank step's shape parameters (shared by both calls).
+loftq_status_t check_svd_shape(int64_t rows, int64_t cols, int32_t r, int32_t oversample, int32_t exact) {
+  if (!shape_ok(rows, cols) || rows < 1 || cols < 1 || r < 1 || oversample < 0) return LOFTQ_ERR_INVALID_ARG;
+  if (exact != 0 && exact != 1) return LOFTQ_ERR_INVALID_ARG;
+  const int64_t mn = rows < cols ? rows : cols;
+  if (exact) {
+    if (r > mn) return LOFTQ_ERR_INVALID_ARG;
+    if (mn > kMaxExact) return LOFTQ_ERR_UNSUPPORTED;
+  } else {
+    const int64_t l = static_cast<int64_t>(r) + oversample;
+    if (l > mn) return LOFTQ_ERR_INVALID_ARG;
+    if (l > kMaxL || r > kMaxR) return LOFTQ_ERR_UNSUPPORTED;
+  }
+  return LOFTQ_OK;
+}
+
+struct InitPlan {
+  SvdPlan svd;
+  int ne, nw;
+  int64_t off_e, off_eparts, off_wparts, off_svd, bytes;
+};
+
+InitPlan make_init_plan(int64_t rows, int64_t cols, const loftq_config_t& c) {
+  InitPlan p{};
+  p.svd = make_svd_plan(rows, cols, c.rank, c.oversample, c.exact_svd != 0);
+  const int64_t n = rows * cols;
+  p.ne = dequant_num_partials(n);
+  p.nw = sumsq_num_partials(n);
+  int64_t off = 0;
+  p.off_e = off;      off += align256(n * 4);
+  p.off_eparts = off; off += align256(static_cast<int64_t>(p.ne) * 8);
+  p.off_wparts = off; off += align256(static_cast<int64_t>(p.nw) * 8);
+  p.off_svd = off;    off += align256(p.svd.bytes);
+  p.bytes = off;
+  return p;
+}
+
+loftq_status_t check_config(int64_t rows, int64_t cols, const loftq_config_t* c) {
+  if (c == nullptr) return LOFTQ_ERR_INVALID_ARG;
+  if (c->bits != 4 || c->blocksize != 64 || c->dq_blocksize != 256) return LOFTQ_ERR_UNSUPPORTED;
+  if (c->iterative_steps < 0 || c->iterative_steps > 1000 || c->power_iters < 0 || c->power_iters > 64 ||
+      c->reserved != 0 || (c->double_quant != 0 && c->double_quant != 1))
+    return LOFTQ_ERR_INVALID_ARG;
+  return check_svd_shape(rows, cols, c->rank, c->oversample, c->exact_svd);
+}
+
+}  // namespace
+}  // namespace loftq
+
+using namespace loftq;
+
+extern "C" {
+
+size_t loftq_lowrank_svd_workspace_bytes(int64_t rows, int64_t cols, int32_t r, int32_t oversample, int32_t exact) {
+  if (check_svd_shape(rows, cols, r, oversample, exact) != LOFTQ_OK) return 0;
+  return static_cast<size_t>(make_svd_plan(rows, cols, r, oversample, exact != 0).bytes);
+}
+
+loftq_status_t loftq_lowrank_svd(const float* E, int64_t rows, int64_t cols, int32_t r, int32_t oversample,
+                                 int32_t power_iters, int32_t exact, const float* omega, uint64_t seed, int32_t t,
+                                 float* B, float* A, float* sigma, void* ws, size_t ws_bytes, void* stream) {
+  loftq_status_t st = check_svd_shape(rows, cols, r, oversample, exact);
+  if (st != LOFTQ_OK) return st;
+  if (power_iters < 0 || power_iters > 64 || t < 1) return LOFTQ_ERR_INVALID_ARG;
+  if (!E || !B || !A || !sigma || !ws) return LOFTQ_ERR_INVALID_ARG;
+  if (!aligned16(E) || !aligned16(B) || !aligned16(A) || !aligned16(sigma) || !aligned16(ws) ||
+      (omega && !aligned16(omega)))
+    return LOFTQ_ERR_INVALID_ARG;
+  const SvdPlan pl = make_svd_plan(rows, cols, r, oversample, exact != 0);
+  if (ws_bytes < static_cast<size_t>(pl.bytes)) return LOFTQ_ERR_WORKSPACE;
+  const ObjectiveArgs none{nullptr, 0, nullptr, 0, nullptr};
+  return from_hip(run_lowrank(E, pl, power_iters, omega, seed, t, B, A, sigma, static_cast<char*>(ws), none,
+                              static_cast<hipStream_t>(stream)));
+}
+
+size_t loftq_workspace_bytes(int64_t rows, int64_t cols, const loftq_config_t* cfg) {
+  if (check_config(rows, cols, cfg) != LOFTQ_OK) return 0;
+  return static_cast<size_t>(make_init_plan(rows, cols, *cfg).bytes);
+}
+
+loftq_status_t loftq_init(const void* W, loftq_dtype_t wdt, int64_t rows, int64_t cols, const loftq_config_t* cfg,
+                          uint8_t* packed, float* absmax, int8_t* qabsmax, float* dq_scale, float* B, float* A,
+                          double* objective, float* sigma, void* ws, size_t ws_bytes, void* stream) {
+  loftq_status_t st = check_config(rows, cols, cfg);
+  if (st != LOFTQ_OK) return st;
+  if (wdt != LOFTQ_F32 && wdt != LOFTQ_BF16) return LOFTQ_ERR_INVALID_ARG;
+  if (!nf4_tables().valid) return LOFTQ_ERR_UNSUPPORTED;
+  const bool dq = cfg->double_quant != 0;
+  if (!W || !packed || !absmax || !B || !A || !objective || !sigma || !ws) return LOFTQ_ERR_INVALID_ARG;
+  if (dq && (!qabsmax || !dq_scale)) return LOFTQ_ERR_INVALID_ARG;
+  const void* ptrs[] = {W, packed, absmax, B, A, objective, sigma, ws};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return LOFTQ_ERR_INVALID_ARG;
+  if (dq && (!aligned16(qabsmax) || !aligned16(dq_scale))) return LOFTQ_ERR_INVALID_ARG;
+  const InitPlan pl = make_init_plan(rows, cols, *cfg);
+  if (ws_bytes < static_cast<size_t>(pl.bytes)) return LOFTQ_ERR_WORKSPACE;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* w = static_cast<char*>(ws);
+  float* E = reinterpret_cast<float*>(w + pl.off_e);
+  double* eparts = reinterpret_cast<double*>(w + pl.off_eparts);
+  double* wparts = reinterpret_cast<double*>(w + pl.off_wparts);
+  char* svd_ws = w + pl.off_svd;
+  const int64_t n = rows * cols;
+  const int64_t nb = (n + 63) / 64;
+  const int r = cfg->rank;
+  const int T = cfg->iterative_steps;
+
+  hipError_t e = launch_sumsq_weight(W, wdt, n, wparts, pl.nw, s);
+  auto quant_step = [&](const float* Bp, const float* Ap) -> hipError_t {
+    hipError_t x = launch_nf4_quantize(W, wdt, rows, cols, Bp, Ap, r, packed, absmax, s);
+    if (x == hipSuccess && dq) x = launch_double_quant(absmax, nb, cfg->dq_blocksize, qabsmax, dq_scale, s);
+    if (x == hipSuccess)
+      x = launch_nf4_dequantize(packed, dq ? nullptr : absmax, dq ? qabsmax : nullptr, dq ? dq_scale : nullptr, n,
+                                cfg->dq_blocksize, W, wdt, E, eparts, nullptr, nullptr, s);
+    return x;
+  };
+  const ObjectiveArgs obj0{eparts, pl.ne, wparts, pl.nw, objective};
+  if (T == 0) {
+    if (e == hipSuccess) e = quant_step(nullptr, nullptr);
+    if (e == hipSuccess) e = run_objective(obj0, s);
+    if (e == hipSuccess) e = run_fill(B, rows * r, 0.f, s);
+    if (e == hipSuccess) e = run_fill(A, static_cast<int64_t>(r) * cols, 0.f, s);
+    if (e == hipSuccess) e = run_fill(sigma, r, 0.f, s);
+    return from_hip(e);
+  }
+  for (int t = 1; t <= T && e == hipSuccess; ++t) {
+    e = quant_step(t == 1 ? nullptr : B, t == 1 ? nullptr : A);
+    if (e == hipSuccess && t == 1) e = run_objective(obj0, s);
+    const ObjectiveArgs objt{eparts, pl.ne, wparts, pl.nw, objective + t};
+    if (e == hipSuccess)
+      e = run_lowrank(E, pl.svd, cfg->power_iters, nullptr, cfg->seed, t, B, A, sigma, svd_ws, objt, s);
+  }
+  return from_hip(e);
+}
+
+}  // extern "C"
