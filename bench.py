@@ -1,0 +1,168 @@
+#!/usr/bin/env python
+"""LoftQ initialisation throughput on one AMD Instinct MI355X.
+
+A step is one loftq_init of the workload's weight (all T alternations: NF4
+quantize of the residual, double quant, dequant-subtract, randomized rank-r SVD,
+objective) with W already resident in HBM.  `value` is matrix elements per second
+(rows * cols per step).  The JSON line also carries:
+  roofline      the dominant streaming kernel: algorithmic bytes per launch over
+                its average launch time, timed with HIP events that the library
+                records around each launch on its own stream during a separate
+                profiled pass over the same steps;
+  nf4_quantize  the same for the NF4 quantize kernel (the metric's second part);
+  cpu_baseline  the CPU oracle on a bounded row sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "LoftQ init matrix-elements/s (T alternations) + NF4 quantize GB/s vs HBM peak"
+HBM_PEAK_GBS = 8000.0   # MI355X HBM3E
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="c2", help="c1, c2, c3 or c5")
+    ap.add_argument("--cpu-rows", type=int, default=2048, help="rows of the workload timed on the CPU oracle")
+    ap.add_argument("--skip-cpu", action="store_true", help="omit the CPU oracle leg")
+    return ap.parse_args()
+
+
+def algorithmic_bytes(name, w, rows, cols):
+    """Bytes the method must move per launch of a kernel (inputs read once, outputs written once)."""
+    n = rows * cols
+    nb = -(-n // 64)
+    ng = -(-nb // 256)
+    wb = 2 if w.dtype == "bf16" else 4
+    l = w.rank + w.oversample
+    scales = (nb + 4 * ng) if w.double_quant else 4 * nb
+    table = {
+        "nf4_quantize": n * wb + -(-n // 2) + 4 * nb,
+        "nf4_quantize_fused": n * wb + -(-n // 2) + 4 * nb + 4 * w.rank * (rows + cols),
+        "double_quant": 4 * nb + nb + 4 * ng,
+        "nf4_dequantize": n * wb + -(-n // 2) + scales + 4 * n,
+        "gemm_nn": 4 * n + 4 * cols * l + 4 * rows * l,
+        "gemm_tn": 4 * n + 4 * rows * l + 4 * cols * l,
+        "sumsq_weight": n * wb,
+    }
+    return table.get(name)
+
+
+def cpu_baseline(w, rows):
+    import numpy as np
+    import oracle
+    from loftq_qlora_initialization_amd import synth
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    except Exception:   # threadpoolctl absent: report the interpreter's own thread
+        cores = 1
+    rows = min(rows, w.rows)
+    _, W = synth.make_weight(w, rows=rows)
+    kw = dict(rank=w.rank, iterative_steps=w.iterative_steps, double_quant_on=w.double_quant, exact=w.exact_svd,
+              oversample=w.oversample, power_iters=w.power_iters, seed=w.sketch_seed)
+    t0 = time.perf_counter()
+    oracle.loftq_init(W, **kw)
+    dt = time.perf_counter() - t0
+    return {"value": rows * w.cols / dt, "unit": "elements/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"first {rows} of {w.rows} rows of {w.name}, same r/p/q/T/double-quant, one loftq_init "
+                      f"({dt:.1f} s)"}
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (the per-GPU kernels are what "
+              "one device runs; run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    import loftq_qlora_initialization_amd as lq
+    from loftq_qlora_initialization_amd import synth
+
+    w = synth.workload(args.workload)
+    bits, _ = synth.make_weight(w)
+    if w.dtype == "bf16":
+        Wd = torch.from_numpy(bits.view(np.int16)).cuda().view(torch.bfloat16)
+    else:
+        Wd = torch.from_numpy(bits).cuda()
+    cfg = lq.default_config(iterative_steps=w.iterative_steps, rank=w.rank, oversample=w.oversample,
+                            power_iters=w.power_iters, double_quant=int(w.double_quant),
+                            exact_svd=int(w.exact_svd), seed=w.sketch_seed)
+    bufs = lq.InitBuffers(w.rows, w.cols, cfg)
+    for _ in range(args.warmup):
+        lq.loftq_init(Wd, cfg, buffers=bufs)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        lq.loftq_init(Wd, cfg, buffers=bufs)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms_per_step = 1e3 * elapsed / args.steps
+    value = w.numel * args.steps / elapsed
+
+    # profiled pass: HIP events around every library launch, same steps on the same stream
+    lq.profile_enable(True)
+    for _ in range(args.steps):
+        lq.loftq_init(Wd, cfg, buffers=bufs)
+    torch.cuda.synchronize()
+    lq.profile_enable(False)
+    prof = lq.profile_collect()
+    kernels = {}
+    for name, (launches, total_ms) in sorted(prof.items(), key=lambda kv: -kv[1][1]):
+        avg_us = 1e3 * total_ms / launches
+        entry = {"launches_per_step": launches / args.steps, "avg_us": round(avg_us, 3),
+                 "share": round(total_ms / sum(v[1] for v in prof.values()), 4)}
+        nbytes = algorithmic_bytes(name, w, w.rows, w.cols)
+        if nbytes is not None:
+            entry["GBps"] = round(nbytes / (avg_us * 1e-6) / 1e9, 1)
+        kernels[name] = entry
+    streaming = [k for k in kernels if "GBps" in kernels[k]]
+    dom = max(streaming, key=lambda k: kernels[k]["share"])
+    achieved = kernels[dom]["GBps"]
+    roofline = {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                "bytes_per_launch": algorithmic_bytes(dom, w, w.rows, w.cols),
+                "avg_us": kernels[dom]["avg_us"]}
+    qname = "nf4_quantize" if "nf4_quantize" in kernels else None
+    nf4 = None
+    if qname:
+        g = kernels[qname]["GBps"]
+        nf4 = {"kernel": qname, "achieved": g, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(g / HBM_PEAK_GBS, 4),
+               "avg_us": kernels[qname]["avg_us"]}
+        if "nf4_quantize_fused" in kernels:
+            gf = kernels["nf4_quantize_fused"]["GBps"]
+            nf4["fused_residual"] = {"achieved": gf, "frac": round(gf / HBM_PEAK_GBS, 4),
+                                     "avg_us": kernels["nf4_quantize_fused"]["avg_us"]}
+
+    obj = bufs.objective.cpu().numpy().tolist()
+    line = {
+        "metric": METRIC, "value": value, "unit": "elements/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": w.name, "rows": w.rows, "cols": w.cols, "storage": w.dtype, "rank": w.rank,
+                   "iterative_steps": w.iterative_steps, "oversample": w.oversample, "power_iters": w.power_iters,
+                   "double_quant": w.double_quant, "blocksize": 64, "dq_blocksize": 256},
+        "roofline": roofline, "nf4_quantize": nf4, "objective": obj, "kernels": kernels,
+    }
+    if not args.skip_cpu:
+        line["cpu_baseline"] = cpu_baseline(w, args.cpu_rows)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

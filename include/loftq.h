@@ -109,7 +109,7 @@ loftq_status_t loftq_nf4_dequantize(const uint8_t* packed, const float* absmax, 
  * r largest singular triplets, Delta = U_r S_r V_r^T).  exact = 1: the SVD of E
  * itself (one-sided Jacobi, min(rows, cols) <= 512).  exact = 0: randomized
  * subspace iteration with sketch width l = r + oversample (l <= min(rows, cols),
- * l <= 128) and power_iters rounds; the sketch is `omega` (cols x l fp32) or, if
+ * l <= 96, r <= 64) and power_iters rounds; the sketch is `omega` (cols x l fp32) or, if
  * NULL, the +-1 SplitMix64 sketch of (seed, t).  Outputs B = U_r S_r^{1/2},
  * A = S_r^{1/2} V_r^T, sigma = S_r (descending).
  *   E      [device] rows x cols fp32
@@ -150,6 +150,17 @@ const char* loftq_status_string(loftq_status_t status);
 
 /* The 16 NF4 levels the library uses, ascending (index 7 = 0). [host] out16 */
 void loftq_nf4_codebook(float* out16);
+
+/* Kernel timing for measurement.  While enabled, every kernel the library
+ * enqueues is bracketed by two HIP events recorded on that launch's stream
+ * (no extra synchronisation is added to the stream).  loftq_profile_collect
+ * waits for the recorded events, sums elapsed time per kernel name, clears the
+ * records and returns the number of kernel names written (at most max_entries).
+ *   names    [host] max_entries * 64 chars (NUL-terminated names), or NULL
+ *   launches [host] max_entries launch counts, or NULL
+ *   total_ms [host] max_entries summed durations in milliseconds, or NULL */
+void loftq_profile_enable(int on);
+int loftq_profile_collect(int max_entries, char* names, int64_t* launches, double* total_ms);
 
 #ifdef __cplusplus
 }

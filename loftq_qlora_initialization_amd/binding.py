@@ -32,7 +32,7 @@ STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported configuration", 3: "wo
 
 EXPORTS = ["loftq_nf4_quantize", "loftq_double_quant", "loftq_nf4_dequantize", "loftq_lowrank_svd",
            "loftq_lowrank_svd_workspace_bytes", "loftq_init", "loftq_workspace_bytes", "loftq_default_config",
-           "loftq_status_string", "loftq_nf4_codebook"]
+           "loftq_status_string", "loftq_nf4_codebook", "loftq_profile_enable", "loftq_profile_collect"]
 
 
 class LoftqConfig(ctypes.Structure):
@@ -67,6 +67,8 @@ _c_init_ws = _sig("loftq_workspace_bytes", _SZ, [_I64, _I64, ctypes.POINTER(Loft
 _c_defaults = _sig("loftq_default_config", None, [ctypes.POINTER(LoftqConfig)])
 _c_status = _sig("loftq_status_string", ctypes.c_char_p, [ctypes.c_int])
 _c_codebook = _sig("loftq_nf4_codebook", None, [ctypes.POINTER(ctypes.c_float)])
+_c_prof_on = _sig("loftq_profile_enable", None, [ctypes.c_int])
+_c_prof_get = _sig("loftq_profile_collect", ctypes.c_int, [ctypes.c_int, ctypes.c_char_p, _P, _P])
 
 
 class LoftqError(RuntimeError):
@@ -225,4 +227,22 @@ def loftq_init(W: torch.Tensor, cfg: Optional[LoftqConfig] = None, buffers: Opti
                objective=bufs.objective)
     if cfg.double_quant:
         out.update(qabsmax=bufs.qabsmax, dq_scale=bufs.dq_scale)
+    return out
+
+
+def profile_enable(on: bool = True) -> None:
+    """Bracket every library kernel launch with HIP events on its stream (measurement only)."""
+    _c_prof_on(1 if on else 0)
+
+
+def profile_collect(max_entries: int = 64) -> dict:
+    """{kernel name: (launches, total milliseconds)} for the launches recorded since the last collect."""
+    names = ctypes.create_string_buffer(64 * max_entries)
+    launches = (ctypes.c_int64 * max_entries)()
+    total = (ctypes.c_double * max_entries)()
+    n = _c_prof_get(max_entries, names, ctypes.cast(launches, ctypes.c_void_p), ctypes.cast(total, ctypes.c_void_p))
+    out = {}
+    for i in range(n):
+        nm = names.raw[64 * i:64 * i + 64].split(b"\0", 1)[0].decode()
+        out[nm] = (int(launches[i]), float(total[i]))
     return out

@@ -24,20 +24,19 @@ loftq_status_t check_svd_shape(int64_t rows, int64_t cols, int32_t r, int32_t ov
 
 struct InitPlan {
   SvdPlan svd;
-  int ne, nw;
-  int64_t off_e, off_eparts, off_wparts, off_svd, bytes;
+  int nparts;
+  int64_t off_e, off_parts, off_wparts, off_svd, bytes;
 };
 
 InitPlan make_init_plan(int64_t rows, int64_t cols, const loftq_config_t& c) {
   InitPlan p{};
   p.svd = make_svd_plan(rows, cols, c.rank, c.oversample, c.exact_svd != 0);
   const int64_t n = rows * cols;
-  p.ne = dequant_num_partials(n);
-  p.nw = sumsq_num_partials(n);
+  p.nparts = dequant_num_partials(n);
   int64_t off = 0;
   p.off_e = off;      off += align256(n * 4);
-  p.off_eparts = off; off += align256(static_cast<int64_t>(p.ne) * 8);
-  p.off_wparts = off; off += align256(static_cast<int64_t>(p.nw) * 8);
+  p.off_parts = off;  off += align256(static_cast<int64_t>(p.nparts) * 8);
+  p.off_wparts = off; off += align256(static_cast<int64_t>(p.nparts) * 8);
   p.off_svd = off;    off += align256(p.svd.bytes);
   p.bytes = off;
   return p;
@@ -106,7 +105,7 @@ loftq_status_t loftq_init(const void* W, loftq_dtype_t wdt, int64_t rows, int64_
   hipStream_t s = static_cast<hipStream_t>(stream);
   char* w = static_cast<char*>(ws);
   float* E = reinterpret_cast<float*>(w + pl.off_e);
-  double* eparts = reinterpret_cast<double*>(w + pl.off_eparts);
+  double* eparts = reinterpret_cast<double*>(w + pl.off_parts);
   double* wparts = reinterpret_cast<double*>(w + pl.off_wparts);
   char* svd_ws = w + pl.off_svd;
   const int64_t n = rows * cols;
@@ -114,7 +113,7 @@ loftq_status_t loftq_init(const void* W, loftq_dtype_t wdt, int64_t rows, int64_
   const int r = cfg->rank;
   const int T = cfg->iterative_steps;
 
-  hipError_t e = launch_sumsq_weight(W, wdt, n, wparts, pl.nw, s);
+  hipError_t e = launch_sumsq_weight(W, wdt, n, wparts, nullptr, nullptr, s);
   auto quant_step = [&](const float* Bp, const float* Ap) -> hipError_t {
     hipError_t x = launch_nf4_quantize(W, wdt, rows, cols, Bp, Ap, r, packed, absmax, s);
     if (x == hipSuccess && dq) x = launch_double_quant(absmax, nb, cfg->dq_blocksize, qabsmax, dq_scale, s);
@@ -123,7 +122,7 @@ loftq_status_t loftq_init(const void* W, loftq_dtype_t wdt, int64_t rows, int64_
                                 cfg->dq_blocksize, W, wdt, E, eparts, nullptr, nullptr, s);
     return x;
   };
-  const ObjectiveArgs obj0{eparts, pl.ne, wparts, pl.nw, objective};
+  const ObjectiveArgs obj0{eparts, pl.nparts, wparts, pl.nparts, objective};
   if (T == 0) {
     if (e == hipSuccess) e = quant_step(nullptr, nullptr);
     if (e == hipSuccess) e = run_objective(obj0, s);
@@ -135,7 +134,7 @@ loftq_status_t loftq_init(const void* W, loftq_dtype_t wdt, int64_t rows, int64_
   for (int t = 1; t <= T && e == hipSuccess; ++t) {
     e = quant_step(t == 1 ? nullptr : B, t == 1 ? nullptr : A);
     if (e == hipSuccess && t == 1) e = run_objective(obj0, s);
-    const ObjectiveArgs objt{eparts, pl.ne, wparts, pl.nw, objective + t};
+    const ObjectiveArgs objt{eparts, pl.nparts, wparts, pl.nparts, objective + t};
     if (e == hipSuccess)
       e = run_lowrank(E, pl.svd, cfg->power_iters, nullptr, cfg->seed, t, B, A, sigma, svd_ws, objt, s);
   }

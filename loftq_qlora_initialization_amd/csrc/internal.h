@@ -8,6 +8,27 @@
 
 namespace loftq {
 
+// Brackets one kernel launch with HIP events on its stream while kernel timing
+// is enabled (loftq_profile_enable); a no-op otherwise.
+class ProfScope {
+ public:
+  ProfScope(const char* name, hipStream_t s);
+  ~ProfScope();
+  ProfScope(const ProfScope&) = delete;
+  ProfScope& operator=(const ProfScope&) = delete;
+
+ private:
+  const char* name_;
+  hipStream_t stream_;
+  hipEvent_t start_;
+};
+
+#define LQ_LAUNCH(NAME, KERNEL, GRID, BLOCK, SHMEM, STREAM, ...)              \
+  do {                                                                      \
+    ::loftq::ProfScope lq_prof_scope_(NAME, STREAM);                        \
+    hipLaunchKernelGGL(KERNEL, GRID, BLOCK, SHMEM, STREAM, __VA_ARGS__);     \
+  } while (0)
+
 // NF4 tables handed to kernels by value (kernel arguments), built once on the
 // host from the quantile definition of the levels.
 //
@@ -37,15 +58,16 @@ hipError_t launch_nf4_quantize(const void* W, loftq_dtype_t wdt, int64_t rows, i
                                hipStream_t s);
 hipError_t launch_double_quant(const float* absmax, int64_t nblocks, int dqbs, int8_t* q, float* scale,
                                hipStream_t s);
-// partial: per-workgroup sum of squares (deterministic) when non-null, else
-// atomically accumulated into sumsq (which is zeroed first) when sumsq non-null.
+// Sum of squares of the output: with `partials`, one fp64 partial per workgroup
+// (dequant_num_partials(n) of them, summed in a fixed order by the consumer);
+// otherwise, with `sumsq`, accumulated into *sumsq with atomics (after zeroing it).
+// `counter` is unused.
 hipError_t launch_nf4_dequantize(const uint8_t* packed, const float* absmax, const int8_t* q,
                                  const float* dqscale, int64_t n, int dqbs, const void* W,
-                                 loftq_dtype_t wdt, float* out, double* partials, int* nparts,
+                                 loftq_dtype_t wdt, float* out, double* partials, unsigned* counter,
                                  double* sumsq, hipStream_t s);
 int dequant_num_partials(int64_t n);
-hipError_t launch_sumsq_weight(const void* W, loftq_dtype_t wdt, int64_t n, double* partials, int nparts,
-                               hipStream_t s);
-int sumsq_num_partials(int64_t n);
+hipError_t launch_sumsq_weight(const void* W, loftq_dtype_t wdt, int64_t n, double* partials, unsigned* counter,
+                               double* sumsq, hipStream_t s);
 
 }  // namespace loftq

@@ -3,44 +3,27 @@
 // The low-rank step of LoftQ takes the r largest singular triplets of W - Q
 // ("LoftQ：协同优化量化与LoRA，实现高效大语言模型微调", §2.3).  Large matrices use
 // randomized subspace iteration (Halko, Martinsson and Tropp 2011, Alg. 4.4/5.1):
-//   Y = E Omega;  Q = orth(Y);  repeat q: Z = orth(E^T Q), Q = orth(E Z);
+//   Y = E Omega;  Q = orth(Y);  repeat q: Z = E^T Q, Q = orth(E Z);
 //   C = E^T Q;  the SVD of Q^T E = C^T comes from the eigen-decomposition of
-//   C^T C (l x l, fp64), corrected for any residual non-orthogonality of Q.
+//   C^T C (l x l, fp64).
+// orth(P) is CholQR: fp64 Gram P^T P = R^T R, then P R^-1.
 // Tiny matrices use an exact one-sided Jacobi SVD of E itself.
 //
-// Kernels:
+// Kernels (besides the thin products in gemm_kernels.hip):
 //   sketch        counter-based +-1 test matrix (SplitMix64)
-//   gemm_nn       split-K partials of E X   (X: k x l), fp32 MFMA 16x16x4
-//   gemm_tn       split-K partials of E^T Y (Y: d x l), fp32 MFMA 16x16x4
-//   reduce_gram   sum of the split-K partials (fixed order) + fp64 Gram partials
-//   chol_inv      fp64 Cholesky of a Gram matrix and the inverse of its factor
-//   small_svd     single-workgroup fp64 Jacobi eigen-solver on the l x l core
-//   panel_small   Q = P R^-1, B = Q S_B and A = (C S_A)^T (+ fp64 Gram partials)
+//   reduce_gram   fixed-order sum of the split-K partials (+ fp64 Gram partials)
+//   gram_sum      fixed-order sum of the Gram partials
+//   small_kernel  single workgroup: Cholesky and R^-1 (orthonormalisation), or
+//                 the l x l core solve (one-sided Jacobi)
+//   panel_small   P S for a row panel P and a small S: Q = P R^-1, B = Q S_B,
+//                 A = (C S_A)^T
 //   exact_jacobi  single-workgroup one-sided Jacobi SVD for tiny matrices
 // Every reduction runs in a fixed order, so results are deterministic.
 #include "lowrank.h"
+#include "reduce.h"
 
 namespace loftq {
 namespace {
-
-typedef float floatx4 __attribute__((ext_vector_type(4)));
-
-// v_mfma_f32_16x16x4_f32: lane L supplies A[L%16][L/16] and B[L/16][L%16];
-// lane L receives D[4*(L/16)+v][L%16] in accumulator component v.
-__device__ __forceinline__ floatx4 mfma16x16x4(float a, float b, floatx4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
-}
-
-__device__ __forceinline__ void load4(const float* __restrict__ M, int64_t row, int64_t nrows, int64_t ld,
-                                      int64_t c0, int64_t cend, bool vec_ok, float out[4]) {
-  if (row < nrows && vec_ok && c0 + 3 < cend) {
-    const float4 v = *reinterpret_cast<const float4*>(M + row * ld + c0);
-    out[0] = v.x; out[1] = v.y; out[2] = v.z; out[3] = v.w;
-  } else {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) out[j] = (row < nrows && c0 + j < cend) ? M[row * ld + c0 + j] : 0.f;
-  }
-}
 
 // ---------------------------------------------------------------------------
 __global__ void sketch_kernel(uint64_t seed, int t, int64_t k, int l, float* __restrict__ out) {
@@ -55,165 +38,25 @@ __global__ void sketch_kernel(uint64_t seed, int t, int64_t k, int l, float* __r
   out[idx] = (z >> 63) ? -1.f : 1.f;
 }
 
-// ---------------------------------------------------------------------------
-// part[s][i][n] = sum_{j in split s} E[i][j] X[j][n].  A workgroup is 4 waves on
-// 64*RT consecutive rows and one K split; X's chunk is staged once in LDS and
-// shared by the 4 waves.  Each lane loads 4 consecutive k of one row per 16-k
-// sub-chunk and feeds them to 4 MFMAs (the k order inside a sub-chunk is a
-// permutation, matched on the X side).
-constexpr int kNnKc = 64;
+__device__ __forceinline__ int packed_index(int a, int b, int l) { return a * l - (a * (a - 1)) / 2 + (b - a); }
 
-template <int NT, int RT>
-__global__ __launch_bounds__(256) void gemm_nn_kernel(const float* __restrict__ E, int64_t d, int64_t k,
-                                                      const float* __restrict__ X, int l, int64_t kper,
-                                                      float* __restrict__ part) {
-  constexpr int LP = 16 * NT, XS = LP + 4;
-  __shared__ float Xs[kNnKc * XS];
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, g = lane >> 4, li = lane & 15;
-  const int64_t row_base = static_cast<int64_t>(blockIdx.x) * (64 * RT) + wave * (16 * RT);
-  const int64_t kb = static_cast<int64_t>(blockIdx.y) * kper;
-  const int64_t ke = (kb + kper < k) ? kb + kper : k;
-  const bool vec_ok = (k & 3) == 0;
-  floatx4 acc[RT][NT];
-#pragma unroll
-  for (int a = 0; a < RT; ++a)
-#pragma unroll
-    for (int b = 0; b < NT; ++b) acc[a][b] = floatx4{0.f, 0.f, 0.f, 0.f};
-
-  for (int64_t kc = kb; kc < ke; kc += kNnKc) {
-    __syncthreads();
-    for (int idx = threadIdx.x; idx < kNnKc * LP; idx += 256) {
-      const int kk = idx / LP, n = idx - kk * LP;
-      const int64_t gk = kc + kk;
-      Xs[kk * XS + n] = (gk < ke && n < l) ? X[gk * l + n] : 0.f;
-    }
-    __syncthreads();
-#pragma unroll
-    for (int sc = 0; sc < kNnKc / 16; ++sc) {
-      const int64_t k0 = kc + sc * 16 + 4 * g;
-      float a[RT][4];
-#pragma unroll
-      for (int rt = 0; rt < RT; ++rt) load4(E, row_base + rt * 16 + li, d, k, k0, ke, vec_ok, a[rt]);
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        float b[NT];
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) b[nt] = Xs[(sc * 16 + 4 * g + s) * XS + nt * 16 + li];
-#pragma unroll
-        for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-          for (int nt = 0; nt < NT; ++nt) acc[rt][nt] = mfma16x16x4(a[rt][s], b[nt], acc[rt][nt]);
-      }
-    }
-  }
-#pragma unroll
-  for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int64_t row = row_base + rt * 16 + 4 * g + v;
-        if (row < d) part[(static_cast<int64_t>(blockIdx.y) * d + row) * LP + nt * 16 + li] = acc[rt][nt][v];
-      }
-}
-
-// part[s][j][n] = sum_{i in split s} E[i][j] Y[i][n].  A workgroup is 4 waves on
-// 256 consecutive columns (64 per wave) and one row split; Y's row chunk is
-// staged once in LDS.  A lane's float4 covers 4 columns that belong to 4
-// interleaved 16-column MFMA tiles (tile j holds columns c0 + 4m + j).
-constexpr int kTnRc = 64;
-
-template <int NT>
-__global__ __launch_bounds__(256) void gemm_tn_kernel(const float* __restrict__ E, int64_t d, int64_t k,
-                                                      const float* __restrict__ Y, int l, int64_t rper,
-                                                      float* __restrict__ part) {
-  constexpr int LP = 16 * NT, YS = (LP % 32 == 0) ? LP + 16 : LP;
-  __shared__ float Ys[kTnRc * YS];
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, g = lane >> 4, li = lane & 15;
-  const int64_t col_base = static_cast<int64_t>(blockIdx.x) * 256 + wave * 64;
-  const int64_t rb = static_cast<int64_t>(blockIdx.y) * rper;
-  const int64_t re = (rb + rper < d) ? rb + rper : d;
-  const bool vec_ok = (k & 3) == 0;
-  floatx4 acc[4][NT];
-#pragma unroll
-  for (int a = 0; a < 4; ++a)
-#pragma unroll
-    for (int b = 0; b < NT; ++b) acc[a][b] = floatx4{0.f, 0.f, 0.f, 0.f};
-
-  for (int64_t rc = rb; rc < re; rc += kTnRc) {
-    __syncthreads();
-    for (int idx = threadIdx.x; idx < kTnRc * LP; idx += 256) {
-      const int rr = idx / LP, n = idx - rr * LP;
-      const int64_t gr = rc + rr;
-      Ys[rr * YS + n] = (gr < re && n < l) ? Y[gr * l + n] : 0.f;
-    }
-    __syncthreads();
-#pragma unroll 4
-    for (int sub = 0; sub < kTnRc / 4; ++sub) {
-      float a[4];
-      load4(E, rc + sub * 4 + g, re, k, col_base + 4 * li, k, vec_ok, a);
-      float b[NT];
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) b[nt] = Ys[(sub * 4 + g) * YS + nt * 16 + li];
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) acc[j][nt] = mfma16x16x4(a[j], b[nt], acc[j][nt]);
-    }
-  }
-#pragma unroll
-  for (int j = 0; j < 4; ++j)
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int64_t col = col_base + 4 * (4 * g + v) + j;
-        if (col < k) part[(static_cast<int64_t>(blockIdx.y) * k + col) * LP + nt * 16 + li] = acc[j][nt][v];
-      }
-}
-
-// ---------------------------------------------------------------------------
-// Gram partial of kRows rows held in LDS (row stride ld): entries a <= b, fp64.
-__device__ void gram_from_lds(const float* rows, int ld, int nrows, int l, double* out) {
-  const int total = l * l;
-  for (int e = threadIdx.x; e < total; e += blockDim.x) {
+// Gram partial (upper triangle, packed) of `nrows` rows held in LDS (row stride ld).
+__device__ void gram_partial(const float* rows, int ld, int nrows, int l, double* out) {
+  for (int e = threadIdx.x; e < l * l; e += blockDim.x) {
     const int a = e / l, b = e - a * l;
     if (b < a) continue;
     double s = 0.0;
-    for (int rr = 0; rr < nrows; ++rr) s += static_cast<double>(rows[rr * ld + a]) * static_cast<double>(rows[rr * ld + b]);
-    out[a * l + b] = s;
-    out[b * l + a] = s;
+    for (int rr = 0; rr < nrows; ++rr)
+      s += static_cast<double>(rows[rr * ld + a]) * static_cast<double>(rows[rr * ld + b]);
+    out[packed_index(a, b, l)] = s;
   }
 }
 
-template <int NT>
-__global__ __launch_bounds__(256) void reduce_gram_kernel(const float* __restrict__ part, int S, int64_t m, int l,
-                                                          float* __restrict__ out, double* __restrict__ gram_parts) {
-  constexpr int LP = 16 * NT;
-  __shared__ float rows[kGramRows * (LP + 1)];
-  const int64_t r0 = static_cast<int64_t>(blockIdx.x) * kGramRows;
-  for (int idx = threadIdx.x; idx < kGramRows * LP; idx += blockDim.x) {
-    const int rr = idx / LP, n = idx - rr * LP;
-    const int64_t row = r0 + rr;
-    float s = 0.f;
-    if (row < m && n < l) {
-      for (int p = 0; p < S; ++p) s += part[(static_cast<int64_t>(p) * m + row) * LP + n];
-      out[row * l + n] = s;
-    }
-    rows[rr * (LP + 1) + n] = s;
-  }
-  if (gram_parts == nullptr) return;
-  __syncthreads();
-  gram_from_lds(rows, LP + 1, kGramRows, l, gram_parts + static_cast<int64_t>(blockIdx.x) * l * l);
-}
-
-// ---------------------------------------------------------------------------
-// fp64 dense helpers on LDS matrices (row stride ld), whole workgroup.
-__device__ void sum_parts(const double* __restrict__ parts, int nparts, int l, double* M, int ld) {
+// Full symmetric l x l (row stride ld) from a packed upper triangle in global memory.
+__device__ void unpack_sym(const double* __restrict__ pk, int l, double* M, int ld) {
   for (int e = threadIdx.x; e < l * l; e += blockDim.x) {
-    double s = 0.0;
-    for (int p = 0; p < nparts; ++p) s += parts[static_cast<int64_t>(p) * l * l + e];
-    M[(e / l) * ld + (e % l)] = s;
+    const int a = e / l, b = e - a * l;
+    M[a * ld + b] = (a <= b) ? pk[packed_index(a, b, l)] : pk[packed_index(b, a, l)];
   }
 }
 
@@ -257,178 +100,277 @@ __device__ void inv_upper(const double* G, int ld, int l, const double* rdiag, d
   __syncthreads();
 }
 
-__global__ __launch_bounds__(256) void chol_inv_kernel(const double* __restrict__ parts, int nparts, int l,
-                                                       float* __restrict__ Rinv) {
-  __shared__ double G[kMaxL * kMaxL];
-  __shared__ double X[kMaxL * kMaxL];
-  __shared__ double rdiag[kMaxL];
-  __shared__ double tmp[1];
-  sum_parts(parts, nparts, l, G, l);
-  __syncthreads();
-  chol_upper(G, l, l, rdiag, tmp);
-  inv_upper(G, l, l, rdiag, X, l);
-  for (int e = threadIdx.x; e < l * l; e += blockDim.x) Rinv[e] = static_cast<float>(X[e]);
-}
-
-// ---------------------------------------------------------------------------
 // Round-robin (circle) schedule: position 0 is fixed, the others rotate.
 __device__ __forceinline__ int rr_player(int pos, int rnd, int n) {
   return pos == 0 ? 0 : 1 + (pos - 1 + rnd) % (n - 1);
 }
 
-// The l x l core.  Inputs: Gram partials of Q (G_Q = Q^T Q) and of C = E^T Q
-// (M = C^T C).  With R the Cholesky factor of G_Q, Q R^-1 is orthonormal and
-// H = R^-T M R^-1 = (Q R^-1)^T E E^T (Q R^-1).  Cyclic Jacobi (round-robin pairs,
-// fp64) diagonalises H = U diag(lambda) U^T while the rotations accumulate onto
-// R^-1, giving V = R^-1 U.  Then sigma = sqrt(lambda) (descending) and
-//   S_B = V_r diag(sigma^1/2),  S_A = V_r diag(sigma^-1/2),
-// so B = Q S_B and A = (C S_A)^T.
-__global__ __launch_bounds__(256) void small_svd_kernel(const double* __restrict__ gq_parts, int ngq,
-                                                        const double* __restrict__ m_parts, int nm, int l, int r,
-                                                        float* __restrict__ SB, float* __restrict__ SA,
-                                                        float* __restrict__ sigma, double* __restrict__ stats,
-                                                        ObjectiveArgs obj) {
-  __shared__ double H[kMaxL * kMaxL];
-  __shared__ double V[kMaxL * kMaxL];
-  __shared__ double rdiag[kMaxL];
-  __shared__ double pc[kMaxL / 2], ps[kMaxL / 2];
-  __shared__ int pp[kMaxL / 2], pq[kMaxL / 2];
-  __shared__ int order[kMaxL];
-  __shared__ int rotated;
-  __shared__ double tmp[1];
-  const int n = l + (l & 1);
-  const int tid = threadIdx.x, bs = blockDim.x;
-  for (int e = tid; e < n * n; e += bs) { H[e] = 0.0; V[e] = 0.0; }
-  __syncthreads();
-  sum_parts(gq_parts, ngq, l, H, n);
-  __syncthreads();
-  chol_upper(H, n, l, rdiag, tmp);
-  inv_upper(H, n, l, rdiag, V, n);
-  for (int e = tid; e < n * n; e += bs) H[e] = 0.0;
-  __syncthreads();
-  sum_parts(m_parts, nm, l, H, n);
-  __syncthreads();
-  // T = M X in place, row by row from the right (X upper triangular)
-  for (int a = tid; a < l; a += bs)
-    for (int c = l - 1; c >= 0; --c) {
-      double s = 0.0;
-      for (int b = 0; b <= c; ++b) s += H[a * n + b] * V[b * n + c];
-      H[a * n + c] = s;
-    }
-  __syncthreads();
-  // H = X^T T in place, column by column from the bottom
-  for (int c = tid; c < l; c += bs)
-    for (int a = l - 1; a >= 0; --a) {
-      double s = 0.0;
-      for (int b = 0; b <= a; ++b) s += V[b * n + a] * H[b * n + c];
-      H[a * n + c] = s;
-    }
-  __syncthreads();
-  for (int e = tid; e < l * l; e += bs) {
-    const int a = e / l, b = e % l;
-    if (a < b) {
-      const double s = 0.5 * (H[a * n + b] + H[b * n + a]);
-      H[a * n + b] = s;
-      H[b * n + a] = s;
-    }
+// All threads of the workgroup call this; thread 0 writes the objective.
+__device__ void write_objective(const ObjectiveArgs& o, double sig2) {
+  if (o.out == nullptr) return;
+  const double es = block_sum_fixed(o.e_parts, o.ne);
+  const double ws = block_sum_fixed(o.w_parts, o.nw);
+  if (threadIdx.x == 0) {
+    const double num = es - sig2;
+    *o.out = ws > 0.0 ? sqrt((num > 0.0 ? num : 0.0) / ws) : 0.0;
   }
-  __syncthreads();
+}
 
-  for (int sweep = 0; sweep < 40; ++sweep) {
-    if (tid == 0) rotated = 0;
+// Sum of P Gram partials (packed upper triangles, E = l(l+1)/2 doubles each)
+// into one packed total.  Workgroup: 64 entries x 4 part groups; part group g
+// sums partials g, g+4, ... with 8 loads in flight, then the four group sums
+// are added in a fixed order.
+__global__ __launch_bounds__(256) void gram_sum_kernel(const double* __restrict__ parts, int P, int E,
+                                                       double* __restrict__ total) {
+  __shared__ double acc[4][64];
+  const int el = threadIdx.x & 63, pg = threadIdx.x >> 6;
+  const int e = blockIdx.x * 64 + el;
+  double s = 0.0;
+  if (e < E) {
+    int p = pg;
+    for (; p + 28 < P; p += 32) {
+      double v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = parts[static_cast<int64_t>(p + 4 * u) * E + e];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) s += v[u];
+    }
+    for (; p < P; p += 4) s += parts[static_cast<int64_t>(p) * E + e];
+  }
+  acc[pg][el] = s;
+  __syncthreads();
+  if (pg == 0 && e < E) total[e] = ((acc[0][el] + acc[1][el]) + acc[2][el]) + acc[3][el];
+}
+
+// fp64 lane exchange inside a DPP row (16 lanes) or quad.
+template <int CTRL>
+__device__ __forceinline__ double dpp_f64(double v) {
+  const int lo = __builtin_amdgcn_update_dpp(0, __double2loint(v), CTRL, 0xF, 0xF, false);
+  const int hi = __builtin_amdgcn_update_dpp(0, __double2hiint(v), CTRL, 0xF, 0xF, false);
+  return __hiloint2double(hi, lo);
+}
+
+// Sum over an aligned group of G lanes (G = 16: row rotations; G = 4: quad
+// exchanges).  Every lane of the group ends with the bit-identical total.
+template <int G>
+__device__ __forceinline__ double group_sum(double v) {
+  if (G == 16) {
+    v += dpp_f64<0x128>(v);   // row_ror:8
+    v += dpp_f64<0x124>(v);   // row_ror:4
+    v += dpp_f64<0x122>(v);   // row_ror:2
+    v += dpp_f64<0x121>(v);   // row_ror:1
+  } else {
+    v += dpp_f64<0xB1>(v);    // quad_perm xor 1
+    v += dpp_f64<0x4E>(v);    // quad_perm xor 2
+  }
+  return v;
+}
+
+// 1/x and 1/sqrt(x) in fp64: hardware estimate plus two Newton steps.
+__device__ __forceinline__ double rcp_f64(double x) {
+  double r = __builtin_amdgcn_rcp(x);
+  r = fma(r, fma(-x, r, 1.0), r);
+  r = fma(r, fma(-x, r, 1.0), r);
+  return r;
+}
+__device__ __forceinline__ double rsq_f64(double x) {
+  double y = __builtin_amdgcn_rsq(x);
+  y = y * fma(-0.5 * x * y, y, 1.5);
+  y = y * fma(-0.5 * x * y, y, 1.5);
+  return y;
+}
+
+// One-sided Jacobi sweeps on the n columns of K (column-major, LDS), rotations
+// accumulated in V (fp32, column-major).  Pair i of a round is owned by lanes
+// [G i, G i + G); each lane holds rows sub, sub + G, ... of the pair's columns
+// in registers for the round.
+template <int G>
+__device__ void jacobi_sweeps(double* K, float* V, const uint16_t* sched, int n, int l, int* flags) {
+  constexpr int RMAX = (kMaxL + 1 + G - 1) / G;
+  const int tid = threadIdx.x;
+  const int pair = tid / G, sub = tid - pair * G;
+  const bool active = pair < n / 2;
+  for (int sweep = 0; sweep < 30; ++sweep) {
+    if (tid == 0) { flags[0] = 0; flags[1] = sweep + 1; }
     __syncthreads();
     for (int rnd = 0; rnd < n - 1; ++rnd) {
-      for (int i = tid; i < n / 2; i += bs) {
-        const int pa = rr_player(i, rnd, n), pb = rr_player(n - 1 - i, rnd, n);
-        const int p = min(pa, pb), q = max(pa, pb);
-        double c = 1.0, s = 0.0;
-        if (q < l) {
-          const double app = H[p * n + p], aqq = H[q * n + q], apq = H[p * n + q];
-          if (apq != 0.0 && fabs(apq) > 1e-14 * sqrt(fabs(app * aqq))) {
-            const double theta = (aqq - app) / (2.0 * apq);
-            const double t = (theta >= 0.0 ? 1.0 : -1.0) / (fabs(theta) + sqrt(1.0 + theta * theta));
-            c = 1.0 / sqrt(1.0 + t * t);
-            s = t * c;
-            rotated = 1;
-          }
+      if (active) {
+        const int pq = sched[rnd * (n / 2) + pair];
+        const int p = pq & 0xFF, q = pq >> 8;
+        double kp[RMAX], kq[RMAX];
+        float vp[RMAX], vq[RMAX];
+        double al = 0.0, be = 0.0, ga = 0.0;
+#pragma unroll
+        for (int i = 0; i < RMAX; ++i) {
+          const int row = sub + G * i;
+          const bool ok = row < n;
+          kp[i] = ok ? K[p * n + row] : 0.0;
+          kq[i] = ok ? K[q * n + row] : 0.0;
+          vp[i] = ok ? V[p * n + row] : 0.f;
+          vq[i] = ok ? V[q * n + row] : 0.f;
+          al = fma(kp[i], kp[i], al);
+          be = fma(kq[i], kq[i], be);
+          ga = fma(kp[i], kq[i], ga);
         }
-        pc[i] = c; ps[i] = s; pp[i] = p; pq[i] = q;
-      }
-      __syncthreads();
-      for (int idx = tid; idx < (n / 2) * n; idx += bs) {
-        const int i = idx / n, j = idx - i * n;
-        const double s = ps[i];
-        if (s == 0.0) continue;
-        const double c = pc[i];
-        const int p = pp[i], q = pq[i];
-        const double hp = H[p * n + j], hq = H[q * n + j];
-        H[p * n + j] = c * hp - s * hq;
-        H[q * n + j] = s * hp + c * hq;
-      }
-      __syncthreads();
-      for (int idx = tid; idx < (n / 2) * n; idx += bs) {
-        const int i = idx / n, j = idx - i * n;
-        const double s = ps[i];
-        if (s == 0.0) continue;
-        const double c = pc[i];
-        const int p = pp[i], q = pq[i];
-        const double hp = H[j * n + p], hq = H[j * n + q];
-        H[j * n + p] = c * hp - s * hq;
-        H[j * n + q] = s * hp + c * hq;
-        if (j == p) H[p * n + q] = 0.0;
-        if (j == q) H[q * n + p] = 0.0;
-        const double vp = V[j * n + p], vq = V[j * n + q];
-        V[j * n + p] = c * vp - s * vq;
-        V[j * n + q] = s * vp + c * vq;
+        al = group_sum<G>(al);
+        be = group_sum<G>(be);
+        ga = group_sum<G>(ga);
+        if (q < l && ga != 0.0 && fabs(ga) > 1e-10 * sqrt(al * be)) {
+          const double zeta = 0.5 * (be - al) * rcp_f64(ga);
+          const double az = fabs(zeta);
+          double t = (az > 1e8) ? 0.5 * rcp_f64(az) : rcp_f64(az + (1.0 + zeta * zeta) * rsq_f64(1.0 + zeta * zeta));
+          t = zeta >= 0.0 ? t : -t;
+          const double c = rsq_f64(1.0 + t * t), s = c * t;
+          const float cf = static_cast<float>(c), sf = static_cast<float>(s);
+#pragma unroll
+          for (int i = 0; i < RMAX; ++i) {
+            const int row = sub + G * i;
+            if (row < n) {
+              K[p * n + row] = c * kp[i] - s * kq[i];
+              K[q * n + row] = s * kp[i] + c * kq[i];
+              V[p * n + row] = cf * vp[i] - sf * vq[i];
+              V[q * n + row] = sf * vp[i] + cf * vq[i];
+            }
+          }
+          if (sub == 0) flags[0] = 1;
+        }
       }
       __syncthreads();
     }
-    if (!rotated) break;
+    const int rotated = flags[0];
     __syncthreads();
+    if (!rotated) break;
   }
+}
 
-  for (int a = tid; a < l; a += bs) {
-    const double la = H[a * n + a];
+// LDS of small_kernel (doubles): G (l x l), X or K (l x l), V (fp32 l x l), small arrays.
+constexpr int kSmallDoubles = 2 * kMaxL * kMaxL + (kMaxL * kMaxL) / 2 + 4 * kMaxL + 64 + (kMaxL * kMaxL) / 8;
+
+// Single workgroup (256 threads) on the l x l Gram of a panel.
+//   mode 1: R^-1 of its Cholesky factor R (G = R^T R), written as fp32 Rinv.
+//   mode 2: the core solve.  Q is orthonormal (fp64 Gram and Cholesky; its fp32
+//     rounding leaves Q^T Q = I to ~1e-7), so Q^T E = C^T and its singular values
+//     are those of K, the Cholesky factor of H = C^T C (H = K^T K).  One-sided
+//     Jacobi orthogonalises K's columns, K V = U diag(sigma), accumulating V (the
+//     eigenvectors of H); round-robin pairs, each pair's two columns owned by a
+//     group of g lanes.  sigma descending; S_B = V_r diag(sigma^1/2) and
+//     S_A = V_r diag(sigma^-1/2), so B = Q S_B and A = (C S_A)^T.
+__global__ __launch_bounds__(256) void small_kernel(const double* __restrict__ gram, int l, int mode,
+                                                    float* __restrict__ Rinv, int r, float* __restrict__ SB,
+                                                    float* __restrict__ SA, float* __restrict__ sigma,
+                                                    double* __restrict__ stats, ObjectiveArgs obj) {
+  __shared__ double smem[kSmallDoubles];
+  const int tid = threadIdx.x;
+  double* G = smem;                                   // l x l, then R (strict upper) / unused
+  double* K = G + kMaxL * kMaxL;                      // mode 1: X = R^-1; mode 2: K column-major (n x n)
+  float* V = reinterpret_cast<float*>(K + kMaxL * kMaxL);   // n x n column-major
+  double* rdiag = reinterpret_cast<double*>(V + kMaxL * kMaxL);
+  double* norm2 = rdiag + kMaxL;
+  int* order = reinterpret_cast<int*>(norm2 + kMaxL);
+  int* flags = order + kMaxL;
+  double* tmp = reinterpret_cast<double*>(flags + 4);
+  unpack_sym(gram, l, G, l);
+  __syncthreads();
+  chol_upper(G, l, l, rdiag, tmp);
+  if (mode == 1) {
+    inv_upper(G, l, l, rdiag, K, l);
+    for (int e = tid; e < l * l; e += 256) Rinv[e] = static_cast<float>(K[e]);
+    return;
+  }
+  const int n = l + (l & 1);
+  // K(:, c) = R(:, c): column-major, K[c * n + row]
+  for (int e = tid; e < n * n; e += 256) {
+    const int c = e / n, row = e - c * n;
+    double v = 0.0;
+    if (c < l && row < l) v = (row == c) ? rdiag[c] : (row < c ? G[row * l + c] : 0.0);
+    K[e] = v;
+    V[e] = (row == c) ? 1.f : 0.f;
+  }
+  uint16_t* sched = reinterpret_cast<uint16_t*>(tmp + 8);   // [rnd][pair] -> p | q << 8
+  for (int e = tid; e < (n - 1) * (n / 2); e += 256) {
+    const int rnd = e / (n / 2), i = e - rnd * (n / 2);
+    const int pa = rr_player(i, rnd, n), pb = rr_player(n - 1 - i, rnd, n);
+    sched[e] = static_cast<uint16_t>(min(pa, pb) | (max(pa, pb) << 8));
+  }
+  if (tid == 0) flags[1] = 0;
+  __syncthreads();
+  if (n <= 32) jacobi_sweeps<16>(K, V, sched, n, l, flags);
+  else jacobi_sweeps<4>(K, V, sched, n, l, flags);
+  for (int c = tid; c < l; c += 256) {
+    double s = 0.0;
+    for (int row = 0; row < n; ++row) s += K[c * n + row] * K[c * n + row];
+    norm2[c] = s;
+  }
+  __syncthreads();
+  for (int a = tid; a < l; a += 256) {
+    const double la = norm2[a];
     int rank = 0;
-    for (int b = 0; b < l; ++b) {
-      const double lb = H[b * n + b];
-      rank += (lb > la || (lb == la && b < a)) ? 1 : 0;
-    }
+    for (int b = 0; b < l; ++b) rank += (norm2[b] > la || (norm2[b] == la && b < a)) ? 1 : 0;
     order[rank] = a;
   }
   __syncthreads();
-  for (int idx = tid; idx < l * r; idx += bs) {
+  for (int idx = tid; idx < l * r; idx += 256) {
     const int row = idx / r, c = idx - row * r;
     const int a = order[c];
-    const double sg = sqrt(fmax(H[a * n + a], 0.0));
+    const double sg = sqrt(norm2[a]);
     const double sq = sqrt(sg);
-    SB[row * r + c] = static_cast<float>(V[row * n + a] * sq);
-    SA[row * r + c] = sg > 0.0 ? static_cast<float>(V[row * n + a] / sq) : 0.f;
+    SB[row * r + c] = static_cast<float>(V[a * n + row] * sq);
+    SA[row * r + c] = sg > 0.0 ? static_cast<float>(V[a * n + row] / sq) : 0.f;
   }
-  for (int c = tid; c < r; c += bs) sigma[c] = static_cast<float>(sqrt(fmax(H[order[c] * n + order[c]], 0.0)));
-  if (tid == 0) {
-    double s2 = 0.0;
-    for (int c = 0; c < r; ++c) s2 += fmax(H[order[c] * n + order[c]], 0.0);
-    if (stats) stats[0] = s2;
-    write_objective(obj, s2);
+  for (int c = tid; c < r; c += 256) sigma[c] = static_cast<float>(sqrt(norm2[order[c]]));
+  double s2 = 0.0;
+  for (int c = 0; c < r; ++c) s2 += norm2[order[c]];
+  if (tid == 0 && stats) {
+    stats[0] = s2;
+    stats[1] = static_cast<double>(flags[1]);
   }
+  write_objective(obj, s2);
+}
+
+// out = sum_s part[s] (fixed order) for a 64-row tile and the fp64 Gram partial
+// (packed upper triangle) of the tile.
+template <int NT>
+__global__ __launch_bounds__(256) void reduce_gram_kernel(const float* __restrict__ part, int S, int64_t m, int l,
+                                                          float* __restrict__ out, double* __restrict__ gram_parts) {
+  // gram_parts == nullptr: the sum only
+  constexpr int LP = 16 * NT;
+  __shared__ float rows[kGramRows * (LP + 1)];
+  const int64_t r0 = static_cast<int64_t>(blockIdx.x) * kGramRows;
+  const int64_t stride = m * LP;
+  for (int idx = threadIdx.x; idx < kGramRows * LP; idx += blockDim.x) {
+    const int rr = idx / LP, n = idx - rr * LP;
+    const int64_t row = r0 + rr;
+    float s = 0.f;
+    if (row < m && n < l) {
+      const float* pp = part + row * LP + n;
+      for (int p = 0; p < S; p += 16) {
+        float v[16];
+#pragma unroll
+        for (int u = 0; u < 16; ++u) v[u] = (p + u < S) ? pp[(p + u) * stride] : 0.f;
+#pragma unroll
+        for (int u = 0; u < 16; ++u) s += v[u];
+      }
+      out[row * l + n] = s;
+    }
+    rows[rr * (LP + 1) + n] = s;
+  }
+  if (gram_parts == nullptr) return;
+  __syncthreads();
+  gram_partial(rows, LP + 1, kGramRows, l, gram_parts + static_cast<int64_t>(blockIdx.x) * (l * (l + 1) / 2));
 }
 
 // ---------------------------------------------------------------------------
 // Panel times small matrix: out = P S (m x w) or its transpose (w x m), with P
 // m x l and S l x w (upper triangular when `upper`).  64 rows of P and all of S
-// are staged in LDS; optional fp64 Gram partials of the product.  Serves both
-// Q = P R^-1 (orthonormalisation) and the factor products B = Q S_B and
+// are staged in LDS.  Serves Q = P R^-1 and the factor products B = Q S_B and
 // A = (C S_A)^T.
 __global__ __launch_bounds__(256) void panel_small_kernel(const float* __restrict__ P, int64_t m, int l,
                                                           const float* __restrict__ S, int w, int upper,
-                                                          float* __restrict__ out, int transpose_out,
-                                                          double* __restrict__ gram_parts) {
+                                                          float* __restrict__ out, int transpose_out) {
   __shared__ float Ps[kPanelRows * (kMaxL + 1)];
   __shared__ float Ss[kMaxL * kMaxL];
-  __shared__ float Os[kPanelRows * (kMaxL + 1)];
   const int64_t r0 = static_cast<int64_t>(blockIdx.x) * kPanelRows;
-  const int ldp = l + 1, ldo = w + 1;
+  const int ldp = l + 1;
   for (int idx = threadIdx.x; idx < kPanelRows * l; idx += blockDim.x) {
     const int rr = idx / l, a = idx - rr * l;
     const int64_t row = r0 + rr;
@@ -448,11 +390,7 @@ __global__ __launch_bounds__(256) void panel_small_kernel(const float* __restric
       if (transpose_out) out[static_cast<int64_t>(c) * m + row] = acc;
       else out[row * w + c] = acc;
     }
-    Os[rr * ldo + c] = row < m ? acc : 0.f;
   }
-  if (gram_parts == nullptr) return;
-  __syncthreads();
-  gram_from_lds(Os, ldo, kPanelRows, w, gram_parts + static_cast<int64_t>(blockIdx.x) * w * w);
 }
 
 // ---------------------------------------------------------------------------
@@ -479,9 +417,11 @@ __global__ __launch_bounds__(1024) void exact_jacobi_kernel(const float* __restr
     Xw[e] = x;
   }
   __syncthreads();
+  int sweeps = 0;
   for (int sweep = 0; sweep < 60; ++sweep) {
     if (tid == 0) rotated = 0;
     __syncthreads();
+    sweeps = sweep + 1;
     for (int rnd = 0; rnd < N - 1; ++rnd) {
       for (int i = wave; i < N / 2; i += nwaves) {
         const int pa = rr_player(i, rnd, N), pb = rr_player(N - 1 - i, rnd, N);
@@ -512,8 +452,9 @@ __global__ __launch_bounds__(1024) void exact_jacobi_kernel(const float* __restr
       }
       __syncthreads();
     }
-    if (!rotated) break;
+    const int rot = rotated;
     __syncthreads();
+    if (!rot) break;
   }
   for (int v = wave; v < n; v += nwaves) {
     const double* xv = Xw + static_cast<int64_t>(v) * len;
@@ -531,7 +472,7 @@ __global__ __launch_bounds__(1024) void exact_jacobi_kernel(const float* __restr
   }
   __syncthreads();
   // Vector x_j = sigma_j u_j (u_j a unit singular vector on the long side).
-  // Long side factor: x_j / sqrt(sigma_j).  Short side: E-product with x_j times sigma_j^(-3/2).
+  // Long-side factor: x_j / sqrt(sigma_j).  Short side: E-product with x_j times sigma_j^(-3/2).
   const int64_t other = trans ? d : k;
   for (int64_t e = tid; e < static_cast<int64_t>(r) * (len + other); e += blockDim.x) {
     const int c = static_cast<int>(e / (len + other));
@@ -557,80 +498,54 @@ __global__ __launch_bounds__(1024) void exact_jacobi_kernel(const float* __restr
     }
   }
   if (tid < r) sigma[tid] = static_cast<float>(sqrt(norm2[order[tid]]));
-  if (tid == 0) {
-    double s2 = 0.0;
-    for (int c = 0; c < r; ++c) s2 += norm2[order[c]];
-    if (stats) stats[0] = s2;
-    write_objective(obj, s2);
+  double s2 = 0.0;
+  for (int c = 0; c < r; ++c) s2 += norm2[order[c]];
+  if (tid == 0 && stats) {
+    stats[0] = s2;
+    stats[1] = sweeps;
   }
+  write_objective(obj, s2);
 }
 
-__global__ void objective_kernel(ObjectiveArgs obj) {
-  if (threadIdx.x == 0 && blockIdx.x == 0) write_objective(obj, 0.0);
-}
+__global__ __launch_bounds__(256) void objective_kernel(ObjectiveArgs obj) { write_objective(obj, 0.0); }
 
 __global__ void fill_kernel(float* __restrict__ p, int64_t n, float v) {
   const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
   if (i < n) p[i] = v;
 }
 
+__global__ void zero_u32_kernel(unsigned* __restrict__ p, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0u;
+}
+
 // ---------------------------------------------------------------------------
-template <int NT>
-void gemm_nn_launch(const float* E, int64_t d, int64_t k, const float* X, int l, const SvdPlan& pl, float* part,
-                    hipStream_t s) {
-  if (NT <= 2)
-    hipLaunchKernelGGL((gemm_nn_kernel<NT, 1>), dim3(pl.nn_row_blocks, pl.nn_splits), dim3(256), 0, s, E, d, k, X, l,
-                       pl.nn_kper, part);
-  else
-    hipLaunchKernelGGL((gemm_nn_kernel<NT, 2>), dim3(pl.nn_row_blocks, pl.nn_splits), dim3(256), 0, s, E, d, k, X, l,
-                       pl.nn_kper, part);
-}
-
-template <int NT>
-struct Ops {
-  static void product(bool transposed, const float* E, int64_t d, int64_t k, const float* panel, int l,
-                      const SvdPlan& pl, float* part, float* out, double* gram, hipStream_t s) {
-    const int64_t m = transposed ? k : d;
-    if (transposed) {
-      hipLaunchKernelGGL((gemm_tn_kernel<NT>), dim3(pl.tn_col_blocks, pl.tn_splits), dim3(256), 0, s, E, d, k, panel,
-                         l, pl.tn_rper, part);
-    } else {
-      gemm_nn_launch<NT>(E, d, k, panel, l, pl, part, s);
-    }
-    const int S = transposed ? pl.tn_splits : pl.nn_splits;
-    const int blocks = static_cast<int>((m + kGramRows - 1) / kGramRows);
-    hipLaunchKernelGGL((reduce_gram_kernel<NT>), dim3(blocks), dim3(256), 0, s, part, S, m, l, out, gram);
-  }
-};
-
-template <template <int> class F, typename... Args>
-void dispatch_nt(int nt, Args... args) {
-  switch (nt) {
-    case 1: F<1>::run(args...); break;
-    case 2: F<2>::run(args...); break;
-    case 3: F<3>::run(args...); break;
-    case 4: F<4>::run(args...); break;
-    case 5: F<5>::run(args...); break;
-    default: F<6>::run(args...); break;
-  }
-}
-
-template <int NT>
-struct ProductF {
-  static void run(bool tr, const float* E, int64_t d, int64_t k, const float* panel, int l, const SvdPlan* pl,
-                  float* part, float* out, double* gram, hipStream_t s) {
-    Ops<NT>::product(tr, E, d, k, panel, l, *pl, part, out, gram, s);
-  }
-};
-void panel_small(const float* P, int64_t m, int l, const float* S, int w, bool upper, float* out, bool tr,
-                 double* gram, hipStream_t s) {
-  const int blocks = static_cast<int>((m + kPanelRows - 1) / kPanelRows);
-  hipLaunchKernelGGL(panel_small_kernel, dim3(blocks), dim3(256), 0, s, P, m, l, S, w, upper ? 1 : 0, out,
-                     tr ? 1 : 0, gram);
-}
-
 int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+template <int NT>
+void reduce_typed(const float* part, int S, int64_t m, int l, float* out, double* gram_parts, hipStream_t s) {
+  const int blocks = static_cast<int>(cdiv(m, kGramRows));
+  LQ_LAUNCH("reduce_gram", (reduce_gram_kernel<NT>), dim3(blocks), dim3(256), 0, s, part, S, m, l, out, gram_parts);
+}
+
+void launch_reduce(int nt, const float* part, int S, int64_t m, int l, float* out, double* gram_parts,
+                   hipStream_t s) {
+  switch (nt) {
+    case 1: reduce_typed<1>(part, S, m, l, out, gram_parts, s); break;
+    case 2: reduce_typed<2>(part, S, m, l, out, gram_parts, s); break;
+    case 3: reduce_typed<3>(part, S, m, l, out, gram_parts, s); break;
+    case 4: reduce_typed<4>(part, S, m, l, out, gram_parts, s); break;
+    default: reduce_typed<5>(part, S, m, l, out, gram_parts, s); break;
+  }
+}
+
+void panel_small(const float* P, int64_t m, int l, const float* S, int w, bool upper, float* out, bool tr,
+                 hipStream_t s) {
+  const int blocks = static_cast<int>(cdiv(m, kPanelRows));
+  LQ_LAUNCH("panel_small", panel_small_kernel, dim3(blocks), dim3(256), 0, s, P, m, l, S, w, upper ? 1 : 0, out,
+            tr ? 1 : 0);
+}
 
 }  // namespace
 
@@ -638,14 +553,14 @@ int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 SvdPlan make_svd_plan(int64_t d, int64_t k, int r, int oversample, bool exact) {
   SvdPlan p{};
   p.d = d; p.k = k; p.r = r; p.exact = exact;
+  int64_t off = 0;
+  auto take = [&](int64_t bytes) { const int64_t o = off; off += round_up(bytes, 256); return o; };
   if (exact) {
     const int64_t n = d < k ? d : k;
     p.l = static_cast<int>(n);
-    p.bytes = 0;
-    p.off_x = 0;
-    p.bytes = round_up(static_cast<int64_t>(n + 1) * (d > k ? d : k) * 8, 256);
-    p.off_stats = p.bytes;
-    p.bytes += 256;
+    p.off_x = take((n + 1) * (d > k ? d : k) * 8);
+    p.off_stats = take(64);
+    p.bytes = off;
     return p;
   }
   const int l = r + oversample;
@@ -653,37 +568,38 @@ SvdPlan make_svd_plan(int64_t d, int64_t k, int r, int oversample, bool exact) {
   p.nt = static_cast<int>(cdiv(l, 16));
   const int LP = 16 * p.nt;
   const int rt = p.nt <= 2 ? 1 : 2;
-  const int64_t target = 768;
+  const int64_t target = 512;
+  // gemm_nn: row blocks of 64 * rt rows, K splits of a multiple of the K chunk;
+  // split-K partials kept under ~8% of E's bytes (S * LP / k).
   p.nn_row_blocks = static_cast<int>(cdiv(d, 64 * rt));
   int64_t s_nn = cdiv(target, p.nn_row_blocks);
-  int64_t max_s = k / 256 > 1 ? k / 256 : 1;
-  if (s_nn > max_s) s_nn = max_s;
+  int64_t cap = (k * 8) / (100 * LP);
+  if (cap < 1) cap = 1;
+  if (s_nn > cap) s_nn = cap;
   if (s_nn < 1) s_nn = 1;
-  p.nn_kper = round_up(cdiv(k, s_nn), kNnKc);
+  p.nn_kper = round_up(cdiv(k, s_nn), kNnChunk);
   p.nn_splits = static_cast<int>(cdiv(k, p.nn_kper));
-  p.tn_col_blocks = static_cast<int>(cdiv(k, 256));
+  // gemm_tn: column blocks of 128, row splits of a multiple of two row chunks.
+  p.tn_col_blocks = static_cast<int>(cdiv(k, 128));
   int64_t s_tn = cdiv(target, p.tn_col_blocks);
-  max_s = d / 128 > 1 ? d / 128 : 1;
-  if (s_tn > max_s) s_tn = max_s;
+  cap = (d * 8) / (100 * LP);
+  if (cap < 1) cap = 1;
+  if (s_tn > cap) s_tn = cap;
   if (s_tn < 1) s_tn = 1;
-  p.tn_rper = round_up(cdiv(d, s_tn), kTnRc);
+  p.tn_rper = round_up(cdiv(d, s_tn), 2 * kTnChunk);
   p.tn_splits = static_cast<int>(cdiv(d, p.tn_rper));
   p.gram_parts_d = static_cast<int>(cdiv(d, kGramRows));
   p.gram_parts_k = static_cast<int>(cdiv(k, kGramRows));
-  p.gram_parts_qy = static_cast<int>(cdiv(d, kPanelRows));
-  int64_t gp = p.gram_parts_d > p.gram_parts_k ? p.gram_parts_d : p.gram_parts_k;
-  if (p.gram_parts_qy > gp) gp = p.gram_parts_qy;
-  int64_t off = 0;
-  auto take = [&](int64_t bytes) { const int64_t o = off; off += round_up(bytes, 256); return o; };
+  const int64_t gp = p.gram_parts_d > p.gram_parts_k ? p.gram_parts_d : p.gram_parts_k;
+  const int64_t E = static_cast<int64_t>(l) * (l + 1) / 2;
   p.off_omega = take(k * l * 4);
   p.off_y = take(d * l * 4);
   p.off_qy = take(d * l * 4);
   p.off_z = take(k * l * 4);
-  p.off_qz = take(k * l * 4);
   const int64_t part_rows = (p.nn_splits * d > p.tn_splits * k) ? p.nn_splits * d : p.tn_splits * k;
   p.off_part = take(part_rows * LP * 4);
-  p.off_gram1 = take(gp * l * l * 8);
-  p.off_gram2 = take(gp * l * l * 8);
+  p.off_gram_parts = take(gp * E * 8);
+  p.off_gram_total = take(E * 8);
   p.off_rinv = take(static_cast<int64_t>(l) * l * 4);
   p.off_sb = take(static_cast<int64_t>(l) * r * 4);
   p.off_sa = take(static_cast<int64_t>(l) * r * 4);
@@ -694,18 +610,18 @@ SvdPlan make_svd_plan(int64_t d, int64_t k, int r, int oversample, bool exact) {
 
 hipError_t run_sketch(uint64_t seed, int t, int64_t k, int l, float* out, hipStream_t s) {
   const int64_t n = k * l;
-  hipLaunchKernelGGL(sketch_kernel, dim3(static_cast<unsigned>(cdiv(n, 256))), dim3(256), 0, s, seed, t, k, l, out);
+  LQ_LAUNCH("sketch", sketch_kernel, dim3(static_cast<unsigned>(cdiv(n, 256))), dim3(256), 0, s, seed, t, k, l, out);
   return hipGetLastError();
 }
 
 hipError_t run_fill(float* p, int64_t n, float v, hipStream_t s) {
   if (n <= 0) return hipSuccess;
-  hipLaunchKernelGGL(fill_kernel, dim3(static_cast<unsigned>(cdiv(n, 256))), dim3(256), 0, s, p, n, v);
+  LQ_LAUNCH("fill", fill_kernel, dim3(static_cast<unsigned>(cdiv(n, 256))), dim3(256), 0, s, p, n, v);
   return hipGetLastError();
 }
 
 hipError_t run_objective(const ObjectiveArgs& obj, hipStream_t s) {
-  hipLaunchKernelGGL(objective_kernel, dim3(1), dim3(64), 0, s, obj);
+  LQ_LAUNCH("objective", objective_kernel, dim3(1), dim3(256), 0, s, obj);
   return hipGetLastError();
 }
 
@@ -715,47 +631,55 @@ hipError_t run_lowrank(const float* E, const SvdPlan& pl, int q, const float* om
   const int r = pl.r, l = pl.l;
   if (pl.exact) {
     double* Xw = reinterpret_cast<double*>(ws + pl.off_x);
-    hipLaunchKernelGGL(exact_jacobi_kernel, dim3(1), dim3(1024), 0, s, E, d, k, r, Xw, B, A, sigma,
-                       reinterpret_cast<double*>(ws + pl.off_stats), obj);
+    LQ_LAUNCH("exact_jacobi", exact_jacobi_kernel, dim3(1), dim3(1024), 0, s, E, d, k, r, Xw, B, A, sigma,
+              reinterpret_cast<double*>(ws + pl.off_stats), obj);
     return hipGetLastError();
   }
   float* Om = reinterpret_cast<float*>(ws + pl.off_omega);
   float* Y = reinterpret_cast<float*>(ws + pl.off_y);
   float* Qy = reinterpret_cast<float*>(ws + pl.off_qy);
   float* Z = reinterpret_cast<float*>(ws + pl.off_z);
-  float* Qz = reinterpret_cast<float*>(ws + pl.off_qz);
   float* part = reinterpret_cast<float*>(ws + pl.off_part);
-  double* g1 = reinterpret_cast<double*>(ws + pl.off_gram1);
-  double* g2 = reinterpret_cast<double*>(ws + pl.off_gram2);
+  double* gparts = reinterpret_cast<double*>(ws + pl.off_gram_parts);
   float* Rinv = reinterpret_cast<float*>(ws + pl.off_rinv);
   float* SB = reinterpret_cast<float*>(ws + pl.off_sb);
   float* SA = reinterpret_cast<float*>(ws + pl.off_sa);
   double* stats = reinterpret_cast<double*>(ws + pl.off_stats);
-  const int nt = pl.nt;
+  const ObjectiveArgs none{nullptr, 0, nullptr, 0, nullptr};
   const float* X0 = omega;
   if (X0 == nullptr) {
     hipError_t e = run_sketch(seed, t, k, l, Om, s);
     if (e != hipSuccess) return e;
     X0 = Om;
   }
-  // Y = E Omega; Q = orth(Y)
-  dispatch_nt<ProductF>(nt, false, E, d, k, X0, l, &pl, part, Y, g1, s);
-  hipLaunchKernelGGL(chol_inv_kernel, dim3(1), dim3(l <= 32 ? 64 : 256), 0, s, g1, pl.gram_parts_d, l, Rinv);
+  double* gtotal = reinterpret_cast<double*>(ws + pl.off_gram_total);
+  const int E_ = l * (l + 1) / 2;
+  // product and split-K reduction; mode 1 then orthonormalises (Gram, Cholesky,
+  // R^-1), mode 2 runs the core solve, mode 0 keeps the raw product
+  auto product = [&](bool transposed, const float* panel, float* out, int mode) {
+    launch_gemm(transposed, E, d, k, panel, l, pl, part, s);
+    const int64_t m = transposed ? k : d;
+    launch_reduce(pl.nt, part, transposed ? pl.tn_splits : pl.nn_splits, m, l, out, mode ? gparts : nullptr, s);
+    if (mode == 0) return;
+    const int P = transposed ? pl.gram_parts_k : pl.gram_parts_d;
+    LQ_LAUNCH("gram_sum", gram_sum_kernel, dim3((E_ + 63) / 64), dim3(256), 0, s, gparts, P, E_, gtotal);
+    LQ_LAUNCH(mode == 1 ? "chol_inv" : "core_svd", small_kernel, dim3(1), dim3(256), 0, s, gtotal, l, mode, Rinv, r,
+              SB, SA, sigma, stats, mode == 2 ? obj : none);
+  };
+  // Y = E Omega; R^-1 of its Gram.  Each power iteration multiplies by E^T and
+  // E and re-orthonormalises Y only: span(E Z) does not depend on Z's basis, so
+  // orthonormalising Z as well would not change the subspace.
+  product(false, X0, Y, 1);
   for (int it = 0; it < q; ++it) {
-    panel_small(Y, d, l, Rinv, l, true, Qy, false, nullptr, s);
-    dispatch_nt<ProductF>(nt, true, E, d, k, Qy, l, &pl, part, Z, g1, s);
-    hipLaunchKernelGGL(chol_inv_kernel, dim3(1), dim3(l <= 32 ? 64 : 256), 0, s, g1, pl.gram_parts_k, l, Rinv);
-    panel_small(Z, k, l, Rinv, l, true, Qz, false, nullptr, s);
-    dispatch_nt<ProductF>(nt, false, E, d, k, Qz, l, &pl, part, Y, g1, s);
-    hipLaunchKernelGGL(chol_inv_kernel, dim3(1), dim3(l <= 32 ? 64 : 256), 0, s, g1, pl.gram_parts_d, l, Rinv);
+    panel_small(Y, d, l, Rinv, l, true, Qy, false, s);
+    product(true, Qy, Z, 0);
+    product(false, Z, Y, 1);
   }
-  // Q (with its Gram for the orthogonality correction), C = E^T Q with M = C^T C
-  panel_small(Y, d, l, Rinv, l, true, Qy, false, g2, s);
-  dispatch_nt<ProductF>(nt, true, E, d, k, Qy, l, &pl, part, Z, g1, s);
-  hipLaunchKernelGGL(small_svd_kernel, dim3(1), dim3(l <= 32 ? 64 : 256), 0, s, g2, pl.gram_parts_qy, g1,
-                     pl.gram_parts_k, l, r, SB, SA, sigma, stats, obj);
-  panel_small(Qy, d, l, SB, r, false, B, false, nullptr, s);
-  panel_small(Z, k, l, SA, r, false, A, true, nullptr, s);
+  // Q = Y R^-1; C = E^T Q, then the core solve on C^T C
+  panel_small(Y, d, l, Rinv, l, true, Qy, false, s);
+  product(true, Qy, Z, 2);
+  panel_small(Qy, d, l, SB, r, false, B, false, s);
+  panel_small(Z, k, l, SA, r, false, A, true, s);
   return hipGetLastError();
 }
 

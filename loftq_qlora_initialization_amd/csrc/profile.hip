@@ -1,0 +1,84 @@
+// Per-kernel launch timing: while enabled, every kernel the library enqueues is
+// bracketed by a pair of HIP events recorded on the launch's own stream.
+// Collection synchronises those events and sums the elapsed time per kernel.
+#include <atomic>
+#include <cstring>
+#include <map>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "internal.h"
+
+namespace loftq {
+namespace {
+
+struct Rec {
+  const char* name;
+  hipEvent_t start, stop;
+};
+
+std::atomic<int> g_enabled{0};
+std::mutex g_mu;
+std::vector<Rec> g_recs;
+
+}  // namespace
+
+ProfScope::ProfScope(const char* name, hipStream_t s) : name_(name), stream_(s), start_(nullptr) {
+  if (!g_enabled.load(std::memory_order_relaxed)) return;
+  if (hipEventCreate(&start_) != hipSuccess) { start_ = nullptr; return; }
+  if (hipEventRecord(start_, s) != hipSuccess) { (void)hipEventDestroy(start_); start_ = nullptr; }
+}
+
+ProfScope::~ProfScope() {
+  if (!start_) return;
+  hipEvent_t stop = nullptr;
+  if (hipEventCreate(&stop) != hipSuccess || hipEventRecord(stop, stream_) != hipSuccess) {
+    if (stop) (void)hipEventDestroy(stop);
+    (void)hipEventDestroy(start_);
+    return;
+  }
+  std::lock_guard<std::mutex> lk(g_mu);
+  g_recs.push_back(Rec{name_, start_, stop});
+}
+
+}  // namespace loftq
+
+using namespace loftq;
+
+extern "C" {
+
+void loftq_profile_enable(int on) { g_enabled.store(on ? 1 : 0); }
+
+int loftq_profile_collect(int max_entries, char* names, int64_t* launches, double* total_ms) {
+  std::vector<Rec> recs;
+  {
+    std::lock_guard<std::mutex> lk(g_mu);
+    recs.swap(g_recs);
+  }
+  std::map<std::string, std::pair<int64_t, double>> agg;
+  for (const Rec& r : recs) {
+    float ms = 0.f;
+    if (hipEventSynchronize(r.stop) == hipSuccess && hipEventElapsedTime(&ms, r.start, r.stop) == hipSuccess) {
+      auto& e = agg[r.name];
+      e.first += 1;
+      e.second += ms;
+    }
+    (void)hipEventDestroy(r.start);
+    (void)hipEventDestroy(r.stop);
+  }
+  int i = 0;
+  for (const auto& kv : agg) {
+    if (i >= max_entries) break;
+    if (names) {
+      std::strncpy(names + 64 * i, kv.first.c_str(), 63);
+      names[64 * i + 63] = '\0';
+    }
+    if (launches) launches[i] = kv.second.first;
+    if (total_ms) total_ms[i] = kv.second.second;
+    ++i;
+  }
+  return i;
+}
+
+}  // extern "C"

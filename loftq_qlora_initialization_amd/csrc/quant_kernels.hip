@@ -15,6 +15,7 @@
 #include <float.h>
 
 #include "internal.h"
+#include "reduce.h"
 
 namespace loftq {
 namespace {
@@ -305,6 +306,7 @@ __global__ __launch_bounds__(kThreads) void dequant_kernel(const uint8_t* __rest
                                                            const float* __restrict__ dqs, int dqbs, int64_t n,
                                                            const T* __restrict__ W, float* __restrict__ out,
                                                            double* __restrict__ partials,
+                                                           unsigned* __restrict__ counter,
                                                            double* __restrict__ sumsq, Nf4Tables tab) {
   __shared__ float lvl[16];
   __shared__ double red[kThreads / 64];
@@ -351,11 +353,11 @@ __global__ __launch_bounds__(kThreads) void dequant_kernel(const uint8_t* __rest
   for (int off = 32; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = acc;
   __syncthreads();
+  double t = 0.0;
+  for (int i = 0; i < kThreads / 64; ++i) t += red[i];
   if (threadIdx.x == 0) {
-    double t = 0.0;
-    for (int i = 0; i < kThreads / 64; ++i) t += red[i];
-    if (partials) partials[blockIdx.x] = t;
-    else if (sumsq) atomicAdd(sumsq, t);
+    if (partials != nullptr) partials[blockIdx.x] = t;
+    else if (sumsq != nullptr) atomicAdd(sumsq, t);
   }
 }
 
@@ -364,7 +366,9 @@ __global__ void zero_double_kernel(double* p) { *p = 0.0; }
 // Sum of squares of W (for ||W||_F), per-workgroup partials.
 template <typename T>
 __global__ __launch_bounds__(kThreads) void sumsq_kernel(const T* __restrict__ W, int64_t n,
-                                                         double* __restrict__ partials) {
+                                                         double* __restrict__ partials,
+                                                         unsigned* __restrict__ counter,
+                                                         double* __restrict__ sumsq) {
   __shared__ double red[kThreads / 64];
   const int64_t ngroups = n >> 4;
   const int64_t stride = static_cast<int64_t>(gridDim.x) * kThreads;
@@ -385,11 +389,9 @@ __global__ __launch_bounds__(kThreads) void sumsq_kernel(const T* __restrict__ W
   for (int off = 32; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = acc;
   __syncthreads();
-  if (threadIdx.x == 0) {
-    double t = 0.0;
-    for (int i = 0; i < kThreads / 64; ++i) t += red[i];
-    partials[blockIdx.x] = t;
-  }
+  double t = 0.0;
+  for (int i = 0; i < kThreads / 64; ++i) t += red[i];
+  if (threadIdx.x == 0) partials[blockIdx.x] = t;
 }
 
 int grid_for_groups(int64_t ngroups, int per_thread) {
@@ -409,22 +411,22 @@ hipError_t quantize_typed(const T* W, int64_t rows, int64_t cols, const float* B
   if (B == nullptr) {
     const int64_t full = n / 64;
     if (full > 0) {
-      hipLaunchKernelGGL(quantize_plain_kernel<T>, dim3(grid_for_groups(full * 4, 2)), dim3(kThreads), 0, s, W,
+      LQ_LAUNCH("nf4_quantize", quantize_plain_kernel<T>, dim3(grid_for_groups(full * 4, 2)), dim3(kThreads), 0, s, W,
                          full * 4, packed, absmax, tab);
     }
     if (full < nblocks) {
-      hipLaunchKernelGGL(quantize_generic_kernel<T>, dim3(1), dim3(kThreads), 0, s, W, n, cols,
+      LQ_LAUNCH("nf4_quantize_generic", quantize_generic_kernel<T>, dim3(1), dim3(kThreads), 0, s, W, n, cols,
                          static_cast<const float*>(nullptr), static_cast<const float*>(nullptr), 0, full, nblocks,
                          packed, absmax, tab);
     }
   } else if (cols % 64 == 0) {
     const int64_t tiles = ((rows + kTileRows - 1) / kTileRows) * ((cols + kTileCols - 1) / kTileCols);
-    hipLaunchKernelGGL(quantize_fused_kernel<T>, dim3(static_cast<unsigned>(tiles)), dim3(kThreads), 0, s, W, rows,
+    LQ_LAUNCH("nf4_quantize_fused", quantize_fused_kernel<T>, dim3(static_cast<unsigned>(tiles)), dim3(kThreads), 0, s, W, rows,
                        cols, B, A, r, packed, absmax, tab);
   } else {
     int64_t grid = (nblocks + (kThreads / 4) - 1) / (kThreads / 4);
     if (grid > 65536) grid = 65536;
-    hipLaunchKernelGGL(quantize_generic_kernel<T>, dim3(static_cast<unsigned>(grid)), dim3(kThreads), 0, s, W, n,
+    LQ_LAUNCH("nf4_quantize_generic", quantize_generic_kernel<T>, dim3(static_cast<unsigned>(grid)), dim3(kThreads), 0, s, W, n,
                        cols, B, A, r, static_cast<int64_t>(0), nblocks, packed, absmax, tab);
   }
   return hipGetLastError();
@@ -432,14 +434,15 @@ hipError_t quantize_typed(const T* W, int64_t rows, int64_t cols, const float* B
 
 template <typename T>
 hipError_t dequant_typed(const uint8_t* packed, const float* absmax, const int8_t* q, const float* dqs, int64_t n,
-                         int dqbs, const T* W, float* out, double* partials, double* sumsq, hipStream_t s) {
+                         int dqbs, const T* W, float* out, double* partials, unsigned* counter, double* sumsq,
+                         hipStream_t s) {
   const Nf4Tables& tab = nf4_tables();
   const int grid = dequant_num_partials(n);
-  if (partials == nullptr && sumsq != nullptr) hipLaunchKernelGGL(zero_double_kernel, dim3(1), dim3(1), 0, s, sumsq);
+  if (partials == nullptr && sumsq != nullptr) LQ_LAUNCH("zero", zero_double_kernel, dim3(1), dim3(1), 0, s, sumsq);
   const bool dq = q != nullptr;
 #define LQ_DEQ(HW, DQ)                                                                                            \
-  hipLaunchKernelGGL((dequant_kernel<T, HW, DQ>), dim3(grid), dim3(kThreads), 0, s, packed, absmax, q, dqs, dqbs, \
-                     n, W, out, partials, sumsq, tab)
+  LQ_LAUNCH("nf4_dequantize", (dequant_kernel<T, HW, DQ>), dim3(grid), dim3(kThreads), 0, s, packed, absmax, q,   \
+            dqs, dqbs, n, W, out, partials, counter, sumsq, tab)
   if (W != nullptr) {
     if (dq) LQ_DEQ(true, true); else LQ_DEQ(true, false);
   } else {
@@ -455,7 +458,6 @@ int dequant_num_partials(int64_t n) {
   int g = grid_for_groups((n >> 4) + 1, 4);
   return g > kDeqMaxBlocks ? kDeqMaxBlocks : g;
 }
-int sumsq_num_partials(int64_t n) { return dequant_num_partials(n); }
 
 hipError_t launch_nf4_quantize(const void* W, loftq_dtype_t wdt, int64_t rows, int64_t cols, const float* B,
                                const float* A, int r, uint8_t* packed, float* absmax, hipStream_t s) {
@@ -468,32 +470,34 @@ hipError_t launch_double_quant(const float* absmax, int64_t nblocks, int dqbs, i
                                hipStream_t s) {
   if (nblocks == 0) return hipSuccess;
   const int64_t groups = (nblocks + dqbs - 1) / dqbs;
-  hipLaunchKernelGGL(double_quant_kernel, dim3(static_cast<unsigned>(groups)), dim3(256), 0, s, absmax, nblocks,
+  LQ_LAUNCH("double_quant", double_quant_kernel, dim3(static_cast<unsigned>(groups)), dim3(256), 0, s, absmax, nblocks,
                      dqbs, q, scale);
   return hipGetLastError();
 }
 
 hipError_t launch_nf4_dequantize(const uint8_t* packed, const float* absmax, const int8_t* q, const float* dqscale,
                                  int64_t n, int dqbs, const void* W, loftq_dtype_t wdt, float* out, double* partials,
-                                 int* nparts, double* sumsq, hipStream_t s) {
-  if (nparts) *nparts = dequant_num_partials(n);
+                                 unsigned* counter, double* sumsq, hipStream_t s) {
   if (n == 0) {
-    if (sumsq && !partials) hipLaunchKernelGGL(zero_double_kernel, dim3(1), dim3(1), 0, s, sumsq);
+    if (sumsq) LQ_LAUNCH("zero", zero_double_kernel, dim3(1), dim3(1), 0, s, sumsq);
     return hipGetLastError();
   }
   if (wdt == LOFTQ_BF16)
-    return dequant_typed(packed, absmax, q, dqscale, n, dqbs, static_cast<const uint16_t*>(W), out, partials, sumsq, s);
-  return dequant_typed(packed, absmax, q, dqscale, n, dqbs, static_cast<const float*>(W), out, partials, sumsq, s);
+    return dequant_typed(packed, absmax, q, dqscale, n, dqbs, static_cast<const uint16_t*>(W), out, partials, counter,
+                         sumsq, s);
+  return dequant_typed(packed, absmax, q, dqscale, n, dqbs, static_cast<const float*>(W), out, partials, counter,
+                       sumsq, s);
 }
 
-hipError_t launch_sumsq_weight(const void* W, loftq_dtype_t wdt, int64_t n, double* partials, int nparts,
-                               hipStream_t s) {
+hipError_t launch_sumsq_weight(const void* W, loftq_dtype_t wdt, int64_t n, double* partials, unsigned* counter,
+                               double* sumsq, hipStream_t s) {
+  const int nparts = dequant_num_partials(n);
   if (wdt == LOFTQ_BF16)
-    hipLaunchKernelGGL(sumsq_kernel<uint16_t>, dim3(nparts), dim3(kThreads), 0, s,
-                       static_cast<const uint16_t*>(W), n, partials);
+    LQ_LAUNCH("sumsq_weight", sumsq_kernel<uint16_t>, dim3(nparts), dim3(kThreads), 0, s,
+              static_cast<const uint16_t*>(W), n, partials, counter, sumsq);
   else
-    hipLaunchKernelGGL(sumsq_kernel<float>, dim3(nparts), dim3(kThreads), 0, s, static_cast<const float*>(W), n,
-                       partials);
+    LQ_LAUNCH("sumsq_weight", sumsq_kernel<float>, dim3(nparts), dim3(kThreads), 0, s, static_cast<const float*>(W), n,
+              partials, counter, sumsq);
   return hipGetLastError();
 }
 
