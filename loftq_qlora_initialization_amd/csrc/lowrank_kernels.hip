@@ -6,7 +6,7 @@
 //   Y = E Omega;  Q = orth(Y);  repeat q: Z = E^T Q, Q = orth(E Z);
 //   C = E^T Q;  the SVD of Q^T E = C^T comes from the eigen-decomposition of
 //   C^T C (l x l, fp64).
-// orth(P) is CholQR: fp64 Gram P^T P = R^T R, then P R^-1.
+// orth(P) is CholQR: fp64 Gram P^T P = R^T R (fp64 Cholesky), then P R^-1.
 // Tiny matrices use an exact one-sided Jacobi SVD of E itself.
 //
 // Kernels (besides the thin products in gemm_kernels.hip):
@@ -15,8 +15,8 @@
 //   gram_sum      fixed-order sum of the Gram partials
 //   small_kernel  single workgroup: Cholesky and R^-1 (orthonormalisation), or
 //                 the l x l core solve (one-sided Jacobi)
-//   panel_small   P S for a row panel P and a small S: Q = P R^-1, B = Q S_B,
-//                 A = (C S_A)^T
+//   trsm_rows     Q = Y R^-1 by forward substitution, one row per thread
+//   panel_small   P S for a row panel P and a small S: B = Q S_B, A = (C S_A)^T
 //   exact_jacobi  single-workgroup one-sided Jacobi SVD for tiny matrices
 // Every reduction runs in a fixed order, so results are deterministic.
 #include "lowrank.h"
@@ -62,9 +62,11 @@ __device__ void unpack_sym(const double* __restrict__ pk, int l, double* M, int 
 
 // In-place upper Cholesky G = R^T R.  R's strict upper triangle replaces G's;
 // its diagonal goes to rdiag.  A pivot at or below 1e-13 of the largest diagonal
-// gives a zero row (that direction of the panel is dropped).
+// gives a zero row (that direction of the panel is dropped).  Threads form a
+// 16 x 16 grid over the trailing submatrix (blockDim 256).
 __device__ void chol_upper(double* G, int ld, int l, double* rdiag, double* scratch1) {
-  if (threadIdx.x == 0) {
+  const int tid = threadIdx.x, ty = tid >> 4, tx = tid & 15;
+  if (tid == 0) {
     double m = 0.0;
     for (int a = 0; a < l; ++a) m = fmax(m, G[a * ld + a]);
     scratch1[0] = m;
@@ -74,30 +76,16 @@ __device__ void chol_upper(double* G, int ld, int l, double* rdiag, double* scra
   for (int j = 0; j < l; ++j) {
     const double piv = G[j * ld + j];
     const double rjj = (piv > tol && piv > 0.0) ? sqrt(piv) : 0.0;
-    for (int c = j + 1 + threadIdx.x; c < l; c += blockDim.x) G[j * ld + c] = rjj > 0.0 ? G[j * ld + c] / rjj : 0.0;
-    if (threadIdx.x == 0) rdiag[j] = rjj;
+    const double inv = rjj > 0.0 ? 1.0 / rjj : 0.0;
+    for (int c = j + 1 + tid; c < l; c += blockDim.x) G[j * ld + c] *= inv;
+    if (tid == 0) rdiag[j] = rjj;
     __syncthreads();
-    const int rem = l - j - 1;
-    for (int idx = threadIdx.x; idx < rem * rem; idx += blockDim.x) {
-      const int a = j + 1 + idx / rem, b = j + 1 + idx % rem;
-      if (b >= a) G[a * ld + b] -= G[j * ld + a] * G[j * ld + b];
+    for (int a = j + 1 + ty; a < l; a += 16) {
+      const double rja = G[j * ld + a];
+      for (int b = a + tx; b < l; b += 16) G[a * ld + b] -= rja * G[j * ld + b];
     }
     __syncthreads();
   }
-}
-
-// X = R^-1 (upper triangular) from chol_upper's output; zero rows stay zero.
-__device__ void inv_upper(const double* G, int ld, int l, const double* rdiag, double* X, int ldx) {
-  for (int c = threadIdx.x; c < l; c += blockDim.x) {
-    X[c * ldx + c] = rdiag[c] > 0.0 ? 1.0 / rdiag[c] : 0.0;
-    for (int a = c - 1; a >= 0; --a) {
-      double s = 0.0;
-      for (int b = a + 1; b <= c; ++b) s += G[a * ld + b] * X[b * ldx + c];
-      X[a * ldx + c] = rdiag[a] > 0.0 ? -s / rdiag[a] : 0.0;
-    }
-    for (int a = c + 1; a < l; ++a) X[a * ldx + c] = 0.0;
-  }
-  __syncthreads();
 }
 
 // Round-robin (circle) schedule: position 0 is fixed, the others rotate.
@@ -145,8 +133,8 @@ __global__ __launch_bounds__(256) void gram_sum_kernel(const double* __restrict_
 // fp64 lane exchange inside a DPP row (16 lanes) or quad.
 template <int CTRL>
 __device__ __forceinline__ double dpp_f64(double v) {
-  const int lo = __builtin_amdgcn_update_dpp(0, __double2loint(v), CTRL, 0xF, 0xF, false);
-  const int hi = __builtin_amdgcn_update_dpp(0, __double2hiint(v), CTRL, 0xF, 0xF, false);
+  const int lo = __builtin_amdgcn_mov_dpp(__double2loint(v), CTRL, 0xF, 0xF, true);
+  const int hi = __builtin_amdgcn_mov_dpp(__double2hiint(v), CTRL, 0xF, 0xF, true);
   return __hiloint2double(hi, lo);
 }
 
@@ -180,16 +168,22 @@ __device__ __forceinline__ double rsq_f64(double x) {
   return y;
 }
 
-// One-sided Jacobi sweeps on the n columns of K (column-major, LDS), rotations
-// accumulated in V (fp32, column-major).  Pair i of a round is owned by lanes
-// [G i, G i + G); each lane holds rows sub, sub + G, ... of the pair's columns
-// in registers for the round.
+// Rows per lane of the Jacobi groups: 16-lane groups serve n <= 32, 4-lane
+// groups n <= kMaxL.  K and V keep ld >= G * rows(G) rows, zero beyond n.
 template <int G>
-__device__ void jacobi_sweeps(double* K, float* V, const uint16_t* sched, int n, int l, int* flags) {
-  constexpr int RMAX = (kMaxL + 1 + G - 1) / G;
+constexpr int jacobi_rows() { return G == 16 ? 2 : (kMaxL + 3) / 4; }
+
+// One-sided Jacobi sweeps on the n columns of K (column-major, LDS, column
+// stride ld), rotations accumulated in V (fp32, same layout).  Pair i of a round
+// is owned by lanes [G i, G i + G); lane `sub` holds rows sub, sub + G, ... of
+// the pair's two columns in registers for the round.  A pair rotates while
+// |k_p . k_q| > 1e-7 |k_p| |k_q|.
+template <int G>
+__device__ void jacobi_sweeps(double* K, float* V, const uint16_t* sched, int n, int ld, int l, int* flags) {
+  constexpr int RMAX = jacobi_rows<G>();
   const int tid = threadIdx.x;
   const int pair = tid / G, sub = tid - pair * G;
-  const bool active = pair < n / 2;
+  const bool active = pair < n / 2;   // G * (n / 2) <= blockDim.x
   for (int sweep = 0; sweep < 30; ++sweep) {
     if (tid == 0) { flags[0] = 0; flags[1] = sweep + 1; }
     __syncthreads();
@@ -197,25 +191,30 @@ __device__ void jacobi_sweeps(double* K, float* V, const uint16_t* sched, int n,
       if (active) {
         const int pq = sched[rnd * (n / 2) + pair];
         const int p = pq & 0xFF, q = pq >> 8;
-        double kp[RMAX], kq[RMAX];
-        float vp[RMAX], vq[RMAX];
+        double* kp = K + p * ld + sub;
+        double* kq = K + q * ld + sub;
+        float* vp = V + p * ld + sub;
+        float* vq = V + q * ld + sub;
+        double xp[RMAX], xq[RMAX];
+        float yp[RMAX], yq[RMAX];
         double al = 0.0, be = 0.0, ga = 0.0;
 #pragma unroll
         for (int i = 0; i < RMAX; ++i) {
-          const int row = sub + G * i;
-          const bool ok = row < n;
-          kp[i] = ok ? K[p * n + row] : 0.0;
-          kq[i] = ok ? K[q * n + row] : 0.0;
-          vp[i] = ok ? V[p * n + row] : 0.f;
-          vq[i] = ok ? V[q * n + row] : 0.f;
-          al = fma(kp[i], kp[i], al);
-          be = fma(kq[i], kq[i], be);
-          ga = fma(kp[i], kq[i], ga);
+          xp[i] = kp[G * i];
+          xq[i] = kq[G * i];
+          yp[i] = vp[G * i];
+          yq[i] = vq[G * i];
+        }
+#pragma unroll
+        for (int i = 0; i < RMAX; ++i) {
+          al = fma(xp[i], xp[i], al);
+          be = fma(xq[i], xq[i], be);
+          ga = fma(xp[i], xq[i], ga);
         }
         al = group_sum<G>(al);
         be = group_sum<G>(be);
         ga = group_sum<G>(ga);
-        if (q < l && ga != 0.0 && fabs(ga) > 1e-10 * sqrt(al * be)) {
+        if (q < l && ga * ga > 1e-14 * (al * be) && ga != 0.0) {
           const double zeta = 0.5 * (be - al) * rcp_f64(ga);
           const double az = fabs(zeta);
           double t = (az > 1e8) ? 0.5 * rcp_f64(az) : rcp_f64(az + (1.0 + zeta * zeta) * rsq_f64(1.0 + zeta * zeta));
@@ -224,13 +223,10 @@ __device__ void jacobi_sweeps(double* K, float* V, const uint16_t* sched, int n,
           const float cf = static_cast<float>(c), sf = static_cast<float>(s);
 #pragma unroll
           for (int i = 0; i < RMAX; ++i) {
-            const int row = sub + G * i;
-            if (row < n) {
-              K[p * n + row] = c * kp[i] - s * kq[i];
-              K[q * n + row] = s * kp[i] + c * kq[i];
-              V[p * n + row] = cf * vp[i] - sf * vq[i];
-              V[q * n + row] = sf * vp[i] + cf * vq[i];
-            }
+            kp[G * i] = c * xp[i] - s * xq[i];
+            kq[G * i] = s * xp[i] + c * xq[i];
+            vp[G * i] = cf * yp[i] - sf * yq[i];
+            vq[G * i] = sf * yp[i] + cf * yq[i];
           }
           if (sub == 0) flags[0] = 1;
         }
@@ -244,10 +240,11 @@ __device__ void jacobi_sweeps(double* K, float* V, const uint16_t* sched, int n,
 }
 
 // LDS of small_kernel (doubles): G (l x l), X or K (l x l), V (fp32 l x l), small arrays.
-constexpr int kSmallDoubles = 2 * kMaxL * kMaxL + (kMaxL * kMaxL) / 2 + 4 * kMaxL + 64 + (kMaxL * kMaxL) / 8;
+constexpr int kSmallDoubles = 2 * kMaxL * (kMaxL + 1) + (kMaxL * (kMaxL + 1)) / 2 + 4 * kMaxL + 64 + (kMaxL * kMaxL) / 8;
 
 // Single workgroup (256 threads) on the l x l Gram of a panel.
-//   mode 1: R^-1 of its Cholesky factor R (G = R^T R), written as fp32 Rinv.
+//   mode 1: its Cholesky factor R (G = R^T R), written to Rinv as fp32 with the
+//     strict upper triangle of R and 1/R[a][a] on the diagonal.
 //   mode 2: the core solve.  Q is orthonormal (fp64 Gram and Cholesky; its fp32
 //     rounding leaves Q^T Q = I to ~1e-7), so Q^T E = C^T and its singular values
 //     are those of K, the Cholesky factor of H = C^T C (H = K^T K).  One-sided
@@ -261,63 +258,74 @@ __global__ __launch_bounds__(256) void small_kernel(const double* __restrict__ g
                                                     double* __restrict__ stats, ObjectiveArgs obj) {
   __shared__ double smem[kSmallDoubles];
   const int tid = threadIdx.x;
-  double* G = smem;                                   // l x l, then R (strict upper) / unused
-  double* K = G + kMaxL * kMaxL;                      // mode 1: X = R^-1; mode 2: K column-major (n x n)
-  float* V = reinterpret_cast<float*>(K + kMaxL * kMaxL);   // n x n column-major
-  double* rdiag = reinterpret_cast<double*>(V + kMaxL * kMaxL);
+  // odd leading dimensions (in doubles) keep rows/columns on distinct LDS banks
+  const int ldg = l | 1;
+  const int n = l + (l & 1);
+  const bool wide = blockDim.x >= 16 * (n / 2);                 // 16-lane Jacobi groups
+  const int kr = wide ? 16 * jacobi_rows<16>() : 4 * jacobi_rows<4>();
+  const int ldk = (kr > n ? kr : n) + 1;
+  double* G = smem;                                   // l x ldg, then R (strict upper)
+  double* K = G + kMaxL * (kMaxL + 1);                // mode 1: X = R^-1 (l x ldg); mode 2: K column-major (n x ldk)
+  float* V = reinterpret_cast<float*>(K + kMaxL * (kMaxL + 1));   // n x ldk column-major
+  double* rdiag = reinterpret_cast<double*>(V + kMaxL * (kMaxL + 1));
   double* norm2 = rdiag + kMaxL;
   int* order = reinterpret_cast<int*>(norm2 + kMaxL);
   int* flags = order + kMaxL;
   double* tmp = reinterpret_cast<double*>(flags + 4);
-  unpack_sym(gram, l, G, l);
+  unpack_sym(gram, l, G, ldg);
   __syncthreads();
-  chol_upper(G, l, l, rdiag, tmp);
+  chol_upper(G, ldg, l, rdiag, tmp);
   if (mode == 1) {
-    inv_upper(G, l, l, rdiag, K, l);
-    for (int e = tid; e < l * l; e += 256) Rinv[e] = static_cast<float>(K[e]);
+    // R (upper, fp32, row-major l x l; diagonal as 1/R[a][a], 0 for a dropped direction)
+    for (int e = tid; e < l * l; e += blockDim.x) {
+      const int a = e / l, b = e - a * l;
+      float v = 0.f;
+      if (a == b) v = rdiag[a] > 0.0 ? static_cast<float>(1.0 / rdiag[a]) : 0.f;
+      else if (a < b) v = static_cast<float>(G[a * ldg + b]);
+      Rinv[e] = v;
+    }
     return;
   }
-  const int n = l + (l & 1);
-  // K(:, c) = R(:, c): column-major, K[c * n + row]
-  for (int e = tid; e < n * n; e += 256) {
-    const int c = e / n, row = e - c * n;
+  // K(:, c) = R(:, c): column-major, K[c * ldk + row]; rows n..ldk-1 stay zero
+  for (int e = tid; e < n * ldk; e += blockDim.x) {
+    const int c = e / ldk, row = e - c * ldk;
     double v = 0.0;
-    if (c < l && row < l) v = (row == c) ? rdiag[c] : (row < c ? G[row * l + c] : 0.0);
+    if (c < l && row < l) v = (row == c) ? rdiag[c] : (row < c ? G[row * ldg + c] : 0.0);
     K[e] = v;
     V[e] = (row == c) ? 1.f : 0.f;
   }
   uint16_t* sched = reinterpret_cast<uint16_t*>(tmp + 8);   // [rnd][pair] -> p | q << 8
-  for (int e = tid; e < (n - 1) * (n / 2); e += 256) {
+  for (int e = tid; e < (n - 1) * (n / 2); e += blockDim.x) {
     const int rnd = e / (n / 2), i = e - rnd * (n / 2);
     const int pa = rr_player(i, rnd, n), pb = rr_player(n - 1 - i, rnd, n);
     sched[e] = static_cast<uint16_t>(min(pa, pb) | (max(pa, pb) << 8));
   }
   if (tid == 0) flags[1] = 0;
   __syncthreads();
-  if (n <= 32) jacobi_sweeps<16>(K, V, sched, n, l, flags);
-  else jacobi_sweeps<4>(K, V, sched, n, l, flags);
-  for (int c = tid; c < l; c += 256) {
+  if (wide) jacobi_sweeps<16>(K, V, sched, n, ldk, l, flags);
+  else jacobi_sweeps<4>(K, V, sched, n, ldk, l, flags);
+  for (int c = tid; c < l; c += blockDim.x) {
     double s = 0.0;
-    for (int row = 0; row < n; ++row) s += K[c * n + row] * K[c * n + row];
+    for (int row = 0; row < n; ++row) s += K[c * ldk + row] * K[c * ldk + row];
     norm2[c] = s;
   }
   __syncthreads();
-  for (int a = tid; a < l; a += 256) {
+  for (int a = tid; a < l; a += blockDim.x) {
     const double la = norm2[a];
     int rank = 0;
     for (int b = 0; b < l; ++b) rank += (norm2[b] > la || (norm2[b] == la && b < a)) ? 1 : 0;
     order[rank] = a;
   }
   __syncthreads();
-  for (int idx = tid; idx < l * r; idx += 256) {
+  for (int idx = tid; idx < l * r; idx += blockDim.x) {
     const int row = idx / r, c = idx - row * r;
     const int a = order[c];
     const double sg = sqrt(norm2[a]);
     const double sq = sqrt(sg);
-    SB[row * r + c] = static_cast<float>(V[a * n + row] * sq);
-    SA[row * r + c] = sg > 0.0 ? static_cast<float>(V[a * n + row] / sq) : 0.f;
+    SB[row * r + c] = static_cast<float>(V[a * ldk + row] * sq);
+    SA[row * r + c] = sg > 0.0 ? static_cast<float>(V[a * ldk + row] / sq) : 0.f;
   }
-  for (int c = tid; c < r; c += 256) sigma[c] = static_cast<float>(sqrt(norm2[order[c]]));
+  for (int c = tid; c < r; c += blockDim.x) sigma[c] = static_cast<float>(sqrt(norm2[order[c]]));
   double s2 = 0.0;
   for (int c = 0; c < r; ++c) s2 += norm2[order[c]];
   if (tid == 0 && stats) {
@@ -391,6 +399,36 @@ __global__ __launch_bounds__(256) void panel_small_kernel(const float* __restric
       else out[row * w + c] = acc;
     }
   }
+}
+
+// Q = Y R^-1 row by row: R from small_kernel mode 1 (strict upper triangle and
+// 1/R[a][a] on the diagonal, fp32).  Forward substitution q R = y with q in
+// registers; R is read from LDS as a broadcast (all lanes the same address).
+template <int NT>
+__global__ __launch_bounds__(256) void trsm_rows_kernel(const float* __restrict__ Y, int64_t m, int l,
+                                                        const float* __restrict__ R, float* __restrict__ Q) {
+  constexpr int LP = 16 * NT;
+  __shared__ float Rs[LP * LP];
+  for (int e = threadIdx.x; e < LP * LP; e += blockDim.x) {
+    const int a = e / LP, b = e - a * LP;
+    Rs[e] = (a < l && b < l) ? R[a * l + b] : 0.f;
+  }
+  __syncthreads();
+  const int64_t row = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (row >= m) return;
+  const float* y = Y + row * l;
+  float q[LP];
+#pragma unroll
+  for (int c = 0; c < LP; ++c) {
+    float s = (c < l) ? y[c] : 0.f;
+#pragma unroll
+    for (int a = 0; a < c; ++a) s = fmaf(-q[a], Rs[a * LP + c], s);
+    q[c] = s * Rs[c * LP + c];
+  }
+  float* o = Q + row * l;
+#pragma unroll
+  for (int c = 0; c < LP; ++c)
+    if (c < l) o[c] = q[c];
 }
 
 // ---------------------------------------------------------------------------
@@ -540,6 +578,22 @@ void launch_reduce(int nt, const float* part, int S, int64_t m, int l, float* ou
   }
 }
 
+template <int NT>
+void trsm_typed(const float* Y, int64_t m, int l, const float* R, float* Q, hipStream_t s) {
+  LQ_LAUNCH("trsm_rows", (trsm_rows_kernel<NT>), dim3(static_cast<unsigned>(cdiv(m, 256))), dim3(256), 0, s, Y, m, l,
+            R, Q);
+}
+
+void launch_trsm(int nt, const float* Y, int64_t m, int l, const float* R, float* Q, hipStream_t s) {
+  switch (nt) {
+    case 1: trsm_typed<1>(Y, m, l, R, Q, s); break;
+    case 2: trsm_typed<2>(Y, m, l, R, Q, s); break;
+    case 3: trsm_typed<3>(Y, m, l, R, Q, s); break;
+    case 4: trsm_typed<4>(Y, m, l, R, Q, s); break;
+    default: trsm_typed<5>(Y, m, l, R, Q, s); break;
+  }
+}
+
 void panel_small(const float* P, int64_t m, int l, const float* S, int w, bool upper, float* out, bool tr,
                  hipStream_t s) {
   const int blocks = static_cast<int>(cdiv(m, kPanelRows));
@@ -671,12 +725,12 @@ hipError_t run_lowrank(const float* E, const SvdPlan& pl, int q, const float* om
   // orthonormalising Z as well would not change the subspace.
   product(false, X0, Y, 1);
   for (int it = 0; it < q; ++it) {
-    panel_small(Y, d, l, Rinv, l, true, Qy, false, s);
+    launch_trsm(pl.nt, Y, d, l, Rinv, Qy, s);
     product(true, Qy, Z, 0);
     product(false, Z, Y, 1);
   }
   // Q = Y R^-1; C = E^T Q, then the core solve on C^T C
-  panel_small(Y, d, l, Rinv, l, true, Qy, false, s);
+  launch_trsm(pl.nt, Y, d, l, Rinv, Qy, s);
   product(true, Qy, Z, 2);
   panel_small(Qy, d, l, SB, r, false, B, false, s);
   panel_small(Z, k, l, SA, r, false, A, true, s);
