@@ -1,10 +1,19 @@
 // Thin products of the randomized SVD on fp32 MFMA (v_mfma_f32_16x16x4_f32):
 //   gemm_nn: part[s] = E[:, K_s] X[K_s, :]      (E d x k row-major, X k x l)
 //   gemm_tn: part[s] = E[R_s, :]^T Y[R_s, :]    (Y d x l)
-// Both stream E exactly once per product; the skinny operand (X or Y, at most a
-// few MB) is staged through LDS and shared by the workgroup's waves.  E loads of
-// the next chunk are issued before the MFMAs of the current one (register double
-// buffering).  Split-K partials are summed in fixed order by reduce_gram.
+// Both stream E exactly once per product.  The skinny operand (X or Y) is held
+// in fragment order (frag_index), so the B operand of one MFMA K-step group is a
+// single coalesced float4 load per lane, read straight from L2/L1 — no LDS
+// staging and no barrier in the main loop.  Each wave keeps D steps of E and of
+// the skinny operand in flight in a register ring.  Waves of a workgroup that
+// share output rows split the contraction and are summed through LDS at the
+// end; split-K partials across workgroups are summed in fixed order by
+// reduce_gram.
+//
+// Out-of-range rows/columns of E are clamped to valid addresses rather than
+// branched around: the matching rows of the skinny operand are zero (its
+// buffers are zero-padded to the splits' full extent), and garbage output
+// rows/columns are never stored.
 #include "lowrank.h"
 
 namespace loftq {
@@ -18,98 +27,124 @@ __device__ __forceinline__ floatx4 mfma16x16x4(float a, float b, floatx4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
-__device__ __forceinline__ float4 load4g(const float* __restrict__ M, int64_t row, int64_t nrows, int64_t ld,
-                                         int64_t c0, int64_t cend, bool vec_ok) {
-  if (row < nrows && vec_ok && c0 + 3 < cend) return *reinterpret_cast<const float4*>(M + row * ld + c0);
-  float o[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) o[j] = (row < nrows && c0 + j < cend) ? M[row * ld + c0 + j] : 0.f;
-  return make_float4(o[0], o[1], o[2], o[3]);
-}
-
 __device__ __forceinline__ float comp(const float4& v, int j) {
   return j == 0 ? v.x : (j == 1 ? v.y : (j == 2 ? v.z : v.w));
 }
 
+// Four consecutive floats of row `p` starting at column c (c % 4 == 0 when VEC),
+// columns clamped into [0, n).
+template <bool VEC>
+__device__ __forceinline__ float4 load_run4(const float* __restrict__ p, int64_t c, int64_t n) {
+  if (VEC) {
+    c = c < n - 4 ? c : n - 4;
+    return *reinterpret_cast<const float4*>(p + c);
+  }
+  float o[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int64_t ci = c + i < n ? c + i : n - 1;
+    o[i] = p[ci];
+  }
+  return make_float4(o[0], o[1], o[2], o[3]);
+}
+
+// Launch shapes (compile-time per tile count NT = ceil(l / 16)).
+template <int NT>
+struct NnCfg {
+  static constexpr int RT = NT <= 2 ? 1 : 2;   // 16-row MFMA tiles per wave
+  static constexpr int D = NT <= 2 ? 4 : 2;    // register ring depth (K steps of 16)
+  static constexpr int WR = NT <= 2 ? 4 : 2;   // waves along rows
+  static constexpr int WK = NT <= 2 ? 1 : 2;   // waves splitting the workgroup's K range
+};
+template <int NT>
+struct TnCfg {
+  static constexpr int D = 2;
+  static constexpr int WC = 2;                 // waves along columns (64 columns each)
+  static constexpr int WR = 2;                 // waves splitting the workgroup's rows
+};
+
 // ---------------------------------------------------------------------------
-// gemm_nn: workgroup = 4 waves x (16 * RT) rows, one K split.  Per 128-wide K
-// chunk a lane holds 8 float4 of E per row tile: float4 j covers k = kc + 16 j +
-// 4 g .. +3 of row li (g = lane / 16, li = lane % 16).  MFMA step s of sub-chunk
-// j uses component s, i.e. K index g <-> k = kc + 16 j + 4 g + s; the X operand
-// is read from LDS with the same mapping.
-template <int NT, int RT>
-__global__ __launch_bounds__(256) void gemm_nn_kernel(const float* __restrict__ E, int64_t d, int64_t k,
-                                                      const float* __restrict__ X, int l, int64_t kper,
-                                                      float* __restrict__ part) {
-  constexpr int LP = 16 * NT, XS = LP + 4, KC = kNnChunk, NJ = KC / 16;
-  constexpr int XPER = (KC * LP + 255) / 256;
-  __shared__ float Xs[KC * XS];
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g = lane >> 4, li = lane & 15;
-  const int64_t row_base = static_cast<int64_t>(blockIdx.x) * (64 * RT) + wave * (16 * RT);
-  const int64_t kb = static_cast<int64_t>(blockIdx.y) * kper;
-  const int64_t ke = (kb + kper < k) ? kb + kper : k;
-  const bool vec_ok = (k & 3) == 0;
+// gemm_nn.  Wave (wr, wk) owns rows row0 .. row0 + 16 RT and the K range
+// [kb, kb + kper / WK).  K step j covers k = kb + 16 j .. + 15: lane (li, g)
+// loads E[row][kb + 16 j + 4 g .. + 3] per row tile and the fragment-order X
+// float4 of (step, tile); MFMA s of the step uses component s of both, i.e.
+// K index g <-> k = kb + 16 j + 4 g + s.
+template <int NT, bool VEC>
+__global__ __launch_bounds__(64 * NnCfg<NT>::WR * NnCfg<NT>::WK) void gemm_nn_kernel(
+    const float* __restrict__ E, int64_t d, int64_t k, const float* __restrict__ Xf, int64_t kper,
+    float* __restrict__ part) {
+  using C = NnCfg<NT>;
+  constexpr int LP = 16 * NT, RT = C::RT, D = C::D, WR = C::WR, WK = C::WK;
+  __shared__ float red[(WK > 1 ? WK - 1 : 1) * WR * 16 * RT * LP];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, wr = w % WR, wk = w / WR;
+  const int g = lane >> 4, li = lane & 15;
+  const int64_t row0 = (static_cast<int64_t>(blockIdx.x) * WR + wr) * 16 * RT;
+  const int64_t kw = kper / WK;
+  const int64_t kb = static_cast<int64_t>(blockIdx.y) * kper + wk * kw;
+  const int nsteps = static_cast<int>(kw / 16);   // a multiple of D
+  const float* erow[RT];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    int64_t r = row0 + rt * 16 + li;
+    r = r < d ? r : d - 1;
+    erow[rt] = E + r * k;
+  }
+  const float* xp = Xf + (kb / 16) * NT * 256 + lane * 4;
   floatx4 acc[RT][NT];
 #pragma unroll
   for (int a = 0; a < RT; ++a)
 #pragma unroll
     for (int b = 0; b < NT; ++b) acc[a][b] = floatx4{0.f, 0.f, 0.f, 0.f};
-
-  float4 ecur[RT][NJ], enext[RT][NJ];
-  float xreg[XPER];
-  auto load_e = [&](int64_t kc, float4 (&dst)[RT][NJ]) {
+  float4 eb[D][RT], xb[D][NT];
+  auto load = [&](int u, int j) {
+    const int64_t c = kb + 16 * j + 4 * g;
 #pragma unroll
-    for (int rt = 0; rt < RT; ++rt)
+    for (int rt = 0; rt < RT; ++rt) eb[u][rt] = load_run4<VEC>(erow[rt], c, k);
 #pragma unroll
-      for (int j = 0; j < NJ; ++j) dst[rt][j] = load4g(E, row_base + rt * 16 + li, d, k, kc + 16 * j + 4 * g, ke, vec_ok);
+    for (int nt = 0; nt < NT; ++nt)
+      xb[u][nt] = *reinterpret_cast<const float4*>(xp + (static_cast<int64_t>(j) * NT + nt) * 256);
   };
-  auto load_x = [&](int64_t kc) {
+  auto compute = [&](int u) {
 #pragma unroll
-    for (int u = 0; u < XPER; ++u) {
-      const int idx = tid + 256 * u;
-      const int kk = idx / LP, n = idx - kk * LP;
-      const int64_t gk = kc + kk;
-      xreg[u] = (idx < KC * LP && gk < ke && n < l) ? X[gk * l + n] : 0.f;
-    }
-  };
-  if (kb < ke) {
-    load_e(kb, ecur);
-    load_x(kb);
-  }
-  for (int64_t kc = kb; kc < ke; kc += KC) {
-    __syncthreads();
-#pragma unroll
-    for (int u = 0; u < XPER; ++u) {
-      const int idx = tid + 256 * u;
-      if (idx < KC * LP) {
-        const int kk = idx / LP, n = idx - kk * LP;
-        Xs[kk * XS + n] = xreg[u];
-      }
-    }
-    __syncthreads();
-    const bool more = kc + KC < ke;
-    if (more) {
-      load_e(kc + KC, enext);
-      load_x(kc + KC);
-    }
-#pragma unroll
-    for (int j = 0; j < NJ; ++j)
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        float b[NT];
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) b[nt] = Xs[(16 * j + 4 * g + s) * XS + nt * 16 + li];
-#pragma unroll
-        for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-          for (int nt = 0; nt < NT; ++nt) acc[rt][nt] = mfma16x16x4(comp(ecur[rt][j], s), b[nt], acc[rt][nt]);
-      }
-    if (more) {
+    for (int s = 0; s < 4; ++s)
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-        for (int j = 0; j < NJ; ++j) ecur[rt][j] = enext[rt][j];
+        for (int nt = 0; nt < NT; ++nt) acc[rt][nt] = mfma16x16x4(comp(eb[u][rt], s), comp(xb[u][nt], s), acc[rt][nt]);
+  };
+#pragma unroll
+  for (int u = 0; u < D; ++u) load(u, u);
+  const int rounds = nsteps / D;
+  for (int rd = 0; rd + 1 < rounds; ++rd) {
+#pragma unroll
+    for (int u = 0; u < D; ++u) {
+      compute(u);
+      load(u, (rd + 1) * D + u);
     }
+  }
+#pragma unroll
+  for (int u = 0; u < D; ++u) compute(u);
+  if (WK > 1) {
+    if (wk > 0) {
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+          for (int v = 0; v < 4; ++v)
+            red[(((wk - 1) * WR + wr) * 16 * RT + rt * 16 + 4 * g + v) * LP + nt * 16 + li] = acc[rt][nt][v];
+    }
+    __syncthreads();
+    if (wk > 0) return;
+#pragma unroll
+    for (int q = 1; q < WK; ++q)
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+          for (int v = 0; v < 4; ++v)
+            acc[rt][nt][v] += red[(((q - 1) * WR + wr) * 16 * RT + rt * 16 + 4 * g + v) * LP + nt * 16 + li];
   }
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt)
@@ -117,149 +152,151 @@ __global__ __launch_bounds__(256) void gemm_nn_kernel(const float* __restrict__ 
     for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
-        const int64_t row = row_base + rt * 16 + 4 * g + v;
+        const int64_t row = row0 + rt * 16 + 4 * g + v;
         if (row < d) part[(static_cast<int64_t>(blockIdx.y) * d + row) * LP + nt * 16 + li] = acc[rt][nt][v];
       }
 }
 
 // ---------------------------------------------------------------------------
-// gemm_tn: workgroup = 2 column tiles (64 columns each) x 2 row groups, one row
-// split of `rper` rows; each row group walks half of the split's rows, and the
-// two row groups' accumulators are summed through LDS at the end.  A lane's
-// float4 covers 4 columns that belong to 4 interleaved 16-column MFMA tiles
-// (tile j holds columns c0 + 4m + j); K index g <-> row r0 + 4 i + g.
-template <int NT>
-__global__ __launch_bounds__(256) void gemm_tn_kernel(const float* __restrict__ E, int64_t d, int64_t k,
-                                                      const float* __restrict__ Y, int l, int64_t rper,
-                                                      float* __restrict__ part) {
-  constexpr int LP = 16 * NT, YS = (LP % 32 == 0) ? LP + 16 : LP, RC = kTnChunk, NI = RC / 4;
-  constexpr int YPER = (RC * LP + 127) / 128;
-  __shared__ float Ys[2][RC * YS];
-  __shared__ float Red[2][64 * LP];
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g = lane >> 4, li = lane & 15;
-  const int ct = wave & 1, rg = wave >> 1;       // column tile, row group
-  const int ltid = tid & 127;                    // thread index within the row group's two waves
-  const int64_t col_base = static_cast<int64_t>(blockIdx.x) * 128 + ct * 64;
-  const int64_t rb = static_cast<int64_t>(blockIdx.y) * rper;
-  const int64_t re_split = (rb + rper < d) ? rb + rper : d;
-  const int64_t half = ((rper / 2) + RC - 1) / RC * RC;
-  const int64_t r_lo = rb + rg * half;
-  const int64_t r_hi = (rg == 0) ? ((rb + half < re_split) ? rb + half : re_split) : re_split;
-  const bool vec_ok = (k & 3) == 0;
+// gemm_tn.  Wave (wc, wr) owns columns c0 .. c0 + 63 and its share of the
+// workgroup's rows: [rb, rb + rper / WR).  Lane (li, g) covers columns c0 + 4 li
+// .. + 3, which belong to four interleaved 16-column MFMA tiles (tile jm holds
+// columns c0 + 4 m + jm).  Row step j covers rows rb + 16 j .. + 15; MFMA i of
+// the step takes rows rb + 16 j + 4 g + i (K index g), matching component i of
+// the fragment-order Y float4.
+template <int NT, bool VEC>
+__global__ __launch_bounds__(64 * TnCfg<NT>::WC * TnCfg<NT>::WR) void gemm_tn_kernel(
+    const float* __restrict__ E, int64_t d, int64_t k, const float* __restrict__ Yf, int64_t rper,
+    float* __restrict__ part) {
+  using C = TnCfg<NT>;
+  constexpr int LP = 16 * NT, D = C::D, WC = C::WC, WR = C::WR;
+  __shared__ float red[(WR > 1 ? WR - 1 : 1) * WC * 64 * LP];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, wc = w % WC, wr = w / WC;
+  const int g = lane >> 4, li = lane & 15;
+  const int64_t c0 = (static_cast<int64_t>(blockIdx.x) * WC + wc) * 64;
+  const int64_t cl = c0 + 4 * li;
+  const int64_t rw = rper / WR;
+  const int64_t rb = static_cast<int64_t>(blockIdx.y) * rper + wr * rw;
+  const int nsteps = static_cast<int>(rw / 16);   // a multiple of D
+  const float* yp = Yf + (rb / 16) * NT * 256 + lane * 4;
   floatx4 acc[4][NT];
 #pragma unroll
   for (int a = 0; a < 4; ++a)
 #pragma unroll
     for (int b = 0; b < NT; ++b) acc[a][b] = floatx4{0.f, 0.f, 0.f, 0.f};
-
-  float4 ecur[NI], enext[NI];
-  float yreg[YPER];
-  auto load_e = [&](int64_t rc, float4 (&dst)[NI]) {
+  float4 eb[D][4], yb[D][NT];
+  auto load = [&](int u, int j) {
 #pragma unroll
-    for (int i = 0; i < NI; ++i) dst[i] = load4g(E, rc + 4 * i + g, r_hi, k, col_base + 4 * li, k, vec_ok);
-  };
-  auto load_y = [&](int64_t rc) {
-#pragma unroll
-    for (int u = 0; u < YPER; ++u) {
-      const int idx = ltid + 128 * u;
-      const int rr = idx / LP, n = idx - rr * LP;
-      const int64_t gr = rc + rr;
-      yreg[u] = (idx < RC * LP && gr < r_hi && n < l) ? Y[gr * l + n] : 0.f;
+    for (int i = 0; i < 4; ++i) {
+      int64_t r = rb + 16 * j + 4 * g + i;
+      r = r < d ? r : d - 1;
+      eb[u][i] = load_run4<VEC>(E + r * k, cl, k);
     }
-  };
-  // both row groups run the same number of chunk iterations (barriers are uniform)
-  const int64_t nchunks = (half + RC - 1) / RC;
-  if (r_lo < r_hi) {
-    load_e(r_lo, ecur);
-    load_y(r_lo);
-  }
-  for (int64_t c = 0; c < nchunks; ++c) {
-    const int64_t rc = r_lo + c * RC;
-    const bool active = rc < r_hi;
-    __syncthreads();
-    if (active) {
 #pragma unroll
-      for (int u = 0; u < YPER; ++u) {
-        const int idx = ltid + 128 * u;
-        if (idx < RC * LP) {
-          const int rr = idx / LP, n = idx - rr * LP;
-          Ys[rg][rr * YS + n] = yreg[u];
-        }
+    for (int nt = 0; nt < NT; ++nt)
+      yb[u][nt] = *reinterpret_cast<const float4*>(yp + (static_cast<int64_t>(j) * NT + nt) * 256);
+  };
+  auto compute = [&](int u) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int jm = 0; jm < 4; ++jm)
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) acc[jm][nt] = mfma16x16x4(comp(eb[u][i], jm), comp(yb[u][nt], i), acc[jm][nt]);
+  };
+#pragma unroll
+  for (int u = 0; u < D; ++u) load(u, u);
+  const int rounds = nsteps / D;
+  for (int rd = 0; rd + 1 < rounds; ++rd) {
+#pragma unroll
+    for (int u = 0; u < D; ++u) {
+      compute(u);
+      load(u, (rd + 1) * D + u);
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < D; ++u) compute(u);
+  // lane (li, g), tile jm, component v holds column c0 + 4 (4 g + v) + jm, output n = 16 nt + li
+  if (WR > 1) {
+    if (wr > 0) {
+#pragma unroll
+      for (int jm = 0; jm < 4; ++jm)
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+          for (int v = 0; v < 4; ++v)
+            red[(((wr - 1) * WC + wc) * 64 + 4 * (4 * g + v) + jm) * LP + nt * 16 + li] = acc[jm][nt][v];
+    }
+    __syncthreads();
+    if (wr > 0) return;
+#pragma unroll
+    for (int q = 1; q < WR; ++q)
+#pragma unroll
+      for (int jm = 0; jm < 4; ++jm)
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+          for (int v = 0; v < 4; ++v)
+            acc[jm][nt][v] += red[(((q - 1) * WC + wc) * 64 + 4 * (4 * g + v) + jm) * LP + nt * 16 + li];
+  }
+#pragma unroll
+  for (int jm = 0; jm < 4; ++jm)
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int64_t col = c0 + 4 * (4 * g + v) + jm;
+        if (col < k) part[(static_cast<int64_t>(blockIdx.y) * k + col) * LP + nt * 16 + li] = acc[jm][nt][v];
       }
-    }
-    __syncthreads();
-    if (!active) continue;
-    const bool more = rc + RC < r_hi;
-    if (more) {
-      load_e(rc + RC, enext);
-      load_y(rc + RC);
-    }
-#pragma unroll
-    for (int i = 0; i < NI; ++i) {
-      float b[NT];
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) b[nt] = Ys[rg][(4 * i + g) * YS + nt * 16 + li];
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) acc[j][nt] = mfma16x16x4(comp(ecur[i], j), b[nt], acc[j][nt]);
-    }
-    if (more) {
-#pragma unroll
-      for (int i = 0; i < NI; ++i) ecur[i] = enext[i];
-    }
-  }
-  // row group 1 hands its accumulators to row group 0 through LDS
-  __syncthreads();
-  if (rg == 1) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-        for (int v = 0; v < 4; ++v) Red[ct][(4 * (4 * g + v) + j) * LP + nt * 16 + li] = acc[j][nt][v];
-  }
-  __syncthreads();
-  if (rg == 0) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const int cl = 4 * (4 * g + v) + j;
-          const int64_t col = col_base + cl;
-          const float val = acc[j][nt][v] + Red[ct][cl * LP + nt * 16 + li];
-          if (col < k) part[(static_cast<int64_t>(blockIdx.y) * k + col) * LP + nt * 16 + li] = val;
-        }
-  }
 }
 
 template <int NT>
-void gemm_typed(bool transposed, const float* E, int64_t d, int64_t k, const float* panel, int l, const SvdPlan& pl,
-                float* part, hipStream_t s) {
+GemmShape shape_typed(bool transposed) {
   if (transposed) {
-    LQ_LAUNCH("gemm_tn", (gemm_tn_kernel<NT>), dim3(pl.tn_col_blocks, pl.tn_splits), dim3(256), 0, s, E, d, k,
-              panel, l, pl.tn_rper, part);
-  } else if (NT <= 2) {
-    LQ_LAUNCH("gemm_nn", (gemm_nn_kernel<NT, 1>), dim3(pl.nn_row_blocks, pl.nn_splits), dim3(256), 0, s, E, d, k,
-              panel, l, pl.nn_kper, part);
+    using C = TnCfg<NT>;
+    return GemmShape{64 * C::WC, 16 * C::D * C::WR};
+  }
+  using C = NnCfg<NT>;
+  return GemmShape{16 * C::RT * C::WR, 16 * C::D * C::WK};
+}
+
+template <int NT>
+void gemm_typed(bool transposed, const float* E, int64_t d, int64_t k, const float* panel, const SvdPlan& pl,
+                float* part, hipStream_t s) {
+  const bool vec = (k & 3) == 0 && k >= 4;
+  if (transposed) {
+    constexpr int threads = 64 * TnCfg<NT>::WC * TnCfg<NT>::WR;
+    const dim3 grid(pl.tn_col_blocks, pl.tn_splits);
+    if (vec) LQ_LAUNCH("gemm_tn", (gemm_tn_kernel<NT, true>), grid, dim3(threads), 0, s, E, d, k, panel, pl.tn_rper, part);
+    else LQ_LAUNCH("gemm_tn", (gemm_tn_kernel<NT, false>), grid, dim3(threads), 0, s, E, d, k, panel, pl.tn_rper, part);
   } else {
-    LQ_LAUNCH("gemm_nn", (gemm_nn_kernel<NT, 2>), dim3(pl.nn_row_blocks, pl.nn_splits), dim3(256), 0, s, E, d, k,
-              panel, l, pl.nn_kper, part);
+    constexpr int threads = 64 * NnCfg<NT>::WR * NnCfg<NT>::WK;
+    const dim3 grid(pl.nn_row_blocks, pl.nn_splits);
+    if (vec) LQ_LAUNCH("gemm_nn", (gemm_nn_kernel<NT, true>), grid, dim3(threads), 0, s, E, d, k, panel, pl.nn_kper, part);
+    else LQ_LAUNCH("gemm_nn", (gemm_nn_kernel<NT, false>), grid, dim3(threads), 0, s, E, d, k, panel, pl.nn_kper, part);
   }
 }
 
 }  // namespace
 
-void launch_gemm(bool transposed, const float* E, int64_t d, int64_t k, const float* panel, int l, const SvdPlan& pl,
+GemmShape gemm_shape(bool transposed, int nt) {
+  switch (nt) {
+    case 1: return shape_typed<1>(transposed);
+    case 2: return shape_typed<2>(transposed);
+    case 3: return shape_typed<3>(transposed);
+    case 4: return shape_typed<4>(transposed);
+    default: return shape_typed<5>(transposed);
+  }
+}
+
+void launch_gemm(bool transposed, const float* E, int64_t d, int64_t k, const float* panel, const SvdPlan& pl,
                  float* part, hipStream_t s) {
   switch (pl.nt) {
-    case 1: gemm_typed<1>(transposed, E, d, k, panel, l, pl, part, s); break;
-    case 2: gemm_typed<2>(transposed, E, d, k, panel, l, pl, part, s); break;
-    case 3: gemm_typed<3>(transposed, E, d, k, panel, l, pl, part, s); break;
-    case 4: gemm_typed<4>(transposed, E, d, k, panel, l, pl, part, s); break;
-    default: gemm_typed<5>(transposed, E, d, k, panel, l, pl, part, s); break;
+    case 1: gemm_typed<1>(transposed, E, d, k, panel, pl, part, s); break;
+    case 2: gemm_typed<2>(transposed, E, d, k, panel, pl, part, s); break;
+    case 3: gemm_typed<3>(transposed, E, d, k, panel, pl, part, s); break;
+    case 4: gemm_typed<4>(transposed, E, d, k, panel, pl, part, s); break;
+    default: gemm_typed<5>(transposed, E, d, k, panel, pl, part, s); break;
   }
 }
 

@@ -10,8 +10,6 @@ constexpr int kMaxR = 64;        // rank limit of the randomized path's factor k
 constexpr int kMaxExact = 512;   // exact SVD: min(rows, cols) limit
 constexpr int kGramRows = 32;    // rows per workgroup (and fp64 Gram partial) of reduce_gram
 constexpr int kPanelRows = 64;   // rows per workgroup (and Gram partial) of the panel x small kernel
-constexpr int kNnChunk = 64;     // K chunk of gemm_nn
-constexpr int kTnChunk = 32;     // row chunk of gemm_tn
 
 // Where the objective of an alternation goes: ||E||^2 and ||W||^2 arrive as
 // per-workgroup partial sums (summed in a fixed order by the consumer);
@@ -24,6 +22,23 @@ struct ObjectiveArgs {
   double* out;
 };
 
+// Skinny panels that feed the thin products as their B operand (the sketch,
+// Q = Y R^-1 and Z = E^T Q) are stored in fragment order: 16-row blocks, each
+// a run of NT = ceil(l / 16) tiles of 16 x 16 floats, element (rho, c) of a
+// tile at ((rho % 16) / 4) * 64 + (c % 16) * 4 + rho % 4.  Lane 16 g + i of a
+// wave then finds the four K-steps it feeds to one MFMA group in a single
+// float4.  Rows beyond the panel and columns beyond l are stored as zeros.
+__host__ __device__ __forceinline__ int64_t frag_index(int64_t rho, int c, int nt) {
+  return ((rho >> 4) * nt + (c >> 4)) * 256 + ((rho & 15) >> 2) * 64 + (c & 15) * 4 + (rho & 3);
+}
+
+// Workgroup tile of a thin product: rows (gemm_nn) or columns (gemm_tn) per
+// workgroup, and the granularity of its split of the contracted dimension.
+struct GemmShape {
+  int tile;
+  int unit;
+};
+
 // Workspace layout and launch shapes of one low-rank step (byte offsets into ws).
 struct SvdPlan {
   int64_t d, k;
@@ -34,6 +49,7 @@ struct SvdPlan {
   int tn_col_blocks, tn_splits;
   int64_t tn_rper;
   int gram_parts_d, gram_parts_k;
+  int64_t k_pad, d_pad;   // fragment-order panel rows: nn_splits * nn_kper and tn_splits * tn_rper
   int64_t off_omega, off_y, off_qy, off_z, off_part, off_gram_parts, off_gram_total, off_rinv, off_sb, off_sa;
   int64_t off_stats, off_x;
   int64_t bytes;
@@ -42,10 +58,11 @@ struct SvdPlan {
 SvdPlan make_svd_plan(int64_t d, int64_t k, int r, int oversample, bool exact);
 hipError_t run_lowrank(const float* E, const SvdPlan& pl, int q, const float* omega, uint64_t seed, int t, float* B,
                        float* A, float* sigma, char* ws, const ObjectiveArgs& obj, hipStream_t s);
-hipError_t run_sketch(uint64_t seed, int t, int64_t k, int l, float* out, hipStream_t s);
+hipError_t run_sketch(uint64_t seed, int t, int64_t k, int l, int nt, int64_t rows, float* out, hipStream_t s);
 hipError_t run_fill(float* p, int64_t n, float v, hipStream_t s);
 hipError_t run_objective(const ObjectiveArgs& obj, hipStream_t s);
-void launch_gemm(bool transposed, const float* E, int64_t d, int64_t k, const float* panel, int l, const SvdPlan& pl,
+GemmShape gemm_shape(bool transposed, int nt);
+void launch_gemm(bool transposed, const float* E, int64_t d, int64_t k, const float* panel, const SvdPlan& pl,
                  float* part, hipStream_t s);
 
 bool aligned16(const void* p);

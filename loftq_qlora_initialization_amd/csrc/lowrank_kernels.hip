@@ -26,16 +26,41 @@ namespace loftq {
 namespace {
 
 // ---------------------------------------------------------------------------
-__global__ void sketch_kernel(uint64_t seed, int t, int64_t k, int l, float* __restrict__ out) {
+// Element (i, j) of the k x l test matrix of alternation t is drawn from
+// counter ((t - 1) k + i) l + j; written in fragment order over `rows` rows
+// (zero beyond k and l).
+__global__ void sketch_kernel(uint64_t seed, int t, int64_t k, int l, int nt, int64_t rows, float* __restrict__ out) {
   const int64_t idx = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (idx >= k * l) return;
-  const uint64_t c = static_cast<uint64_t>(t - 1) * static_cast<uint64_t>(k) * static_cast<uint64_t>(l) +
-                     static_cast<uint64_t>(idx);
-  uint64_t z = seed + (c + 1) * 0x9E3779B97F4A7C15ull;
-  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
-  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
-  z ^= z >> 31;
-  out[idx] = (z >> 63) ? -1.f : 1.f;
+  if (idx >= rows * 16 * nt) return;
+  const int64_t blk = idx / (256 * nt);
+  const int e = static_cast<int>(idx - blk * 256 * nt);
+  const int tile = e >> 8, f = e & 255;
+  const int64_t i = blk * 16 + ((f >> 6) << 2) + (f & 3);
+  const int j = tile * 16 + ((f >> 2) & 15);
+  float v = 0.f;
+  if (i < k && j < l) {
+    const uint64_t c = (static_cast<uint64_t>(t - 1) * static_cast<uint64_t>(k) + static_cast<uint64_t>(i)) *
+                           static_cast<uint64_t>(l) + static_cast<uint64_t>(j);
+    uint64_t z = seed + (c + 1) * 0x9E3779B97F4A7C15ull;
+    z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+    z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+    z ^= z >> 31;
+    v = (z >> 63) ? -1.f : 1.f;
+  }
+  out[idx] = v;
+}
+
+// Row-major n x l panel to fragment order over `rows` rows (zero padding).
+__global__ void to_frag_kernel(const float* __restrict__ src, int64_t n, int l, int nt, int64_t rows,
+                               float* __restrict__ out) {
+  const int64_t idx = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (idx >= rows * 16 * nt) return;
+  const int64_t blk = idx / (256 * nt);
+  const int e = static_cast<int>(idx - blk * 256 * nt);
+  const int tile = e >> 8, f = e & 255;
+  const int64_t i = blk * 16 + ((f >> 6) << 2) + (f & 3);
+  const int j = tile * 16 + ((f >> 2) & 15);
+  out[idx] = (i < n && j < l) ? src[i * l + j] : 0.f;
 }
 
 __device__ __forceinline__ int packed_index(int a, int b, int l) { return a * l - (a * (a - 1)) / 2 + (b - a); }
@@ -335,12 +360,15 @@ __global__ __launch_bounds__(256) void small_kernel(const double* __restrict__ g
   write_objective(obj, s2);
 }
 
-// out = sum_s part[s] (fixed order) for a 64-row tile and the fp64 Gram partial
-// (packed upper triangle) of the tile.
+// Sum of the split-K partials, sum_s part[s], in fixed order for a tile of
+// kGramRows rows, written row-major (out_rm, m x l) and/or in fragment order
+// (out_frag, zero-padded to m_pad rows), plus the fp64 Gram partial (packed
+// upper triangle) of the tile when gram_parts is given.
 template <int NT>
-__global__ __launch_bounds__(256) void reduce_gram_kernel(const float* __restrict__ part, int S, int64_t m, int l,
-                                                          float* __restrict__ out, double* __restrict__ gram_parts) {
-  // gram_parts == nullptr: the sum only
+__global__ __launch_bounds__(256) void reduce_gram_kernel(const float* __restrict__ part, int S, int64_t m,
+                                                          int64_t m_pad, int l, float* __restrict__ out_rm,
+                                                          float* __restrict__ out_frag,
+                                                          double* __restrict__ gram_parts) {
   constexpr int LP = 16 * NT;
   __shared__ float rows[kGramRows * (LP + 1)];
   const int64_t r0 = static_cast<int64_t>(blockIdx.x) * kGramRows;
@@ -358,22 +386,23 @@ __global__ __launch_bounds__(256) void reduce_gram_kernel(const float* __restric
 #pragma unroll
         for (int u = 0; u < 16; ++u) s += v[u];
       }
-      out[row * l + n] = s;
+      if (out_rm) out_rm[row * l + n] = s;
     }
+    if (out_frag && row < m_pad) out_frag[frag_index(row, n, NT)] = s;
     rows[rr * (LP + 1) + n] = s;
   }
-  if (gram_parts == nullptr) return;
+  if (gram_parts == nullptr || r0 >= m) return;
   __syncthreads();
   gram_partial(rows, LP + 1, kGramRows, l, gram_parts + static_cast<int64_t>(blockIdx.x) * (l * (l + 1) / 2));
 }
 
 // ---------------------------------------------------------------------------
 // Panel times small matrix: out = P S (m x w) or its transpose (w x m), with P
-// m x l and S l x w (upper triangular when `upper`).  64 rows of P and all of S
-// are staged in LDS.  Serves Q = P R^-1 and the factor products B = Q S_B and
+// an m x l panel in fragment order (nt tiles) and S l x w.  64 rows of P and all
+// of S are staged in LDS.  Serves the factor products B = Q S_B and
 // A = (C S_A)^T.
-__global__ __launch_bounds__(256) void panel_small_kernel(const float* __restrict__ P, int64_t m, int l,
-                                                          const float* __restrict__ S, int w, int upper,
+__global__ __launch_bounds__(256) void panel_small_kernel(const float* __restrict__ P, int64_t m, int l, int nt,
+                                                          const float* __restrict__ S, int w,
                                                           float* __restrict__ out, int transpose_out) {
   __shared__ float Ps[kPanelRows * (kMaxL + 1)];
   __shared__ float Ss[kMaxL * kMaxL];
@@ -382,7 +411,7 @@ __global__ __launch_bounds__(256) void panel_small_kernel(const float* __restric
   for (int idx = threadIdx.x; idx < kPanelRows * l; idx += blockDim.x) {
     const int rr = idx / l, a = idx - rr * l;
     const int64_t row = r0 + rr;
-    Ps[rr * ldp + a] = row < m ? P[row * l + a] : 0.f;
+    Ps[rr * ldp + a] = row < m ? P[frag_index(row, a, nt)] : 0.f;
   }
   for (int idx = threadIdx.x; idx < l * w; idx += blockDim.x) Ss[idx] = S[idx];
   __syncthreads();
@@ -390,9 +419,8 @@ __global__ __launch_bounds__(256) void panel_small_kernel(const float* __restric
     int rr, c;
     if (transpose_out) { rr = idx % kPanelRows; c = idx / kPanelRows; }
     else { rr = idx / w; c = idx - rr * w; }
-    const int amax = upper ? (c + 1 < l ? c + 1 : l) : l;
     float acc = 0.f;
-    for (int a = 0; a < amax; ++a) acc = fmaf(Ps[rr * ldp + a], Ss[a * w + c], acc);
+    for (int a = 0; a < l; ++a) acc = fmaf(Ps[rr * ldp + a], Ss[a * w + c], acc);
     const int64_t row = r0 + rr;
     if (row < m) {
       if (transpose_out) out[static_cast<int64_t>(c) * m + row] = acc;
@@ -404,8 +432,9 @@ __global__ __launch_bounds__(256) void panel_small_kernel(const float* __restric
 // Q = Y R^-1 row by row: R from small_kernel mode 1 (strict upper triangle and
 // 1/R[a][a] on the diagonal, fp32).  Forward substitution q R = y with q in
 // registers; R is read from LDS as a broadcast (all lanes the same address).
+// Y is row-major (m x l); Q is written in fragment order over m_pad rows.
 template <int NT>
-__global__ __launch_bounds__(256) void trsm_rows_kernel(const float* __restrict__ Y, int64_t m, int l,
+__global__ __launch_bounds__(256) void trsm_rows_kernel(const float* __restrict__ Y, int64_t m, int64_t m_pad, int l,
                                                         const float* __restrict__ R, float* __restrict__ Q) {
   constexpr int LP = 16 * NT;
   __shared__ float Rs[LP * LP];
@@ -415,20 +444,23 @@ __global__ __launch_bounds__(256) void trsm_rows_kernel(const float* __restrict_
   }
   __syncthreads();
   const int64_t row = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (row >= m) return;
-  const float* y = Y + row * l;
+  if (row >= m_pad) return;
   float q[LP];
+  if (row < m) {
+    const float* y = Y + row * l;
 #pragma unroll
-  for (int c = 0; c < LP; ++c) {
-    float s = (c < l) ? y[c] : 0.f;
+    for (int c = 0; c < LP; ++c) {
+      float s = (c < l) ? y[c] : 0.f;
 #pragma unroll
-    for (int a = 0; a < c; ++a) s = fmaf(-q[a], Rs[a * LP + c], s);
-    q[c] = s * Rs[c * LP + c];
+      for (int a = 0; a < c; ++a) s = fmaf(-q[a], Rs[a * LP + c], s);
+      q[c] = s * Rs[c * LP + c];
+    }
+  } else {
+#pragma unroll
+    for (int c = 0; c < LP; ++c) q[c] = 0.f;
   }
-  float* o = Q + row * l;
 #pragma unroll
-  for (int c = 0; c < LP; ++c)
-    if (c < l) o[c] = q[c];
+  for (int c = 0; c < LP; ++c) Q[frag_index(row, c, NT)] = q[c];
 }
 
 // ---------------------------------------------------------------------------
@@ -562,43 +594,43 @@ int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 template <int NT>
-void reduce_typed(const float* part, int S, int64_t m, int l, float* out, double* gram_parts, hipStream_t s) {
-  const int blocks = static_cast<int>(cdiv(m, kGramRows));
-  LQ_LAUNCH("reduce_gram", (reduce_gram_kernel<NT>), dim3(blocks), dim3(256), 0, s, part, S, m, l, out, gram_parts);
+void reduce_typed(const float* part, int S, int64_t m, int64_t m_pad, int l, float* out_rm, float* out_frag,
+                  double* gram_parts, hipStream_t s) {
+  const int blocks = static_cast<int>(cdiv(out_frag ? m_pad : m, kGramRows));
+  LQ_LAUNCH("reduce_gram", (reduce_gram_kernel<NT>), dim3(blocks), dim3(256), 0, s, part, S, m, m_pad, l, out_rm,
+            out_frag, gram_parts);
 }
 
-void launch_reduce(int nt, const float* part, int S, int64_t m, int l, float* out, double* gram_parts,
-                   hipStream_t s) {
+void launch_reduce(int nt, const float* part, int S, int64_t m, int64_t m_pad, int l, float* out_rm, float* out_frag,
+                   double* gram_parts, hipStream_t s) {
   switch (nt) {
-    case 1: reduce_typed<1>(part, S, m, l, out, gram_parts, s); break;
-    case 2: reduce_typed<2>(part, S, m, l, out, gram_parts, s); break;
-    case 3: reduce_typed<3>(part, S, m, l, out, gram_parts, s); break;
-    case 4: reduce_typed<4>(part, S, m, l, out, gram_parts, s); break;
-    default: reduce_typed<5>(part, S, m, l, out, gram_parts, s); break;
+    case 1: reduce_typed<1>(part, S, m, m_pad, l, out_rm, out_frag, gram_parts, s); break;
+    case 2: reduce_typed<2>(part, S, m, m_pad, l, out_rm, out_frag, gram_parts, s); break;
+    case 3: reduce_typed<3>(part, S, m, m_pad, l, out_rm, out_frag, gram_parts, s); break;
+    case 4: reduce_typed<4>(part, S, m, m_pad, l, out_rm, out_frag, gram_parts, s); break;
+    default: reduce_typed<5>(part, S, m, m_pad, l, out_rm, out_frag, gram_parts, s); break;
   }
 }
 
 template <int NT>
-void trsm_typed(const float* Y, int64_t m, int l, const float* R, float* Q, hipStream_t s) {
-  LQ_LAUNCH("trsm_rows", (trsm_rows_kernel<NT>), dim3(static_cast<unsigned>(cdiv(m, 256))), dim3(256), 0, s, Y, m, l,
-            R, Q);
+void trsm_typed(const float* Y, int64_t m, int64_t m_pad, int l, const float* R, float* Q, hipStream_t s) {
+  LQ_LAUNCH("trsm_rows", (trsm_rows_kernel<NT>), dim3(static_cast<unsigned>(cdiv(m_pad, 256))), dim3(256), 0, s, Y, m,
+            m_pad, l, R, Q);
 }
 
-void launch_trsm(int nt, const float* Y, int64_t m, int l, const float* R, float* Q, hipStream_t s) {
+void launch_trsm(int nt, const float* Y, int64_t m, int64_t m_pad, int l, const float* R, float* Q, hipStream_t s) {
   switch (nt) {
-    case 1: trsm_typed<1>(Y, m, l, R, Q, s); break;
-    case 2: trsm_typed<2>(Y, m, l, R, Q, s); break;
-    case 3: trsm_typed<3>(Y, m, l, R, Q, s); break;
-    case 4: trsm_typed<4>(Y, m, l, R, Q, s); break;
-    default: trsm_typed<5>(Y, m, l, R, Q, s); break;
+    case 1: trsm_typed<1>(Y, m, m_pad, l, R, Q, s); break;
+    case 2: trsm_typed<2>(Y, m, m_pad, l, R, Q, s); break;
+    case 3: trsm_typed<3>(Y, m, m_pad, l, R, Q, s); break;
+    case 4: trsm_typed<4>(Y, m, m_pad, l, R, Q, s); break;
+    default: trsm_typed<5>(Y, m, m_pad, l, R, Q, s); break;
   }
 }
 
-void panel_small(const float* P, int64_t m, int l, const float* S, int w, bool upper, float* out, bool tr,
-                 hipStream_t s) {
+void panel_small(const float* P, int64_t m, int l, int nt, const float* S, int w, float* out, bool tr, hipStream_t s) {
   const int blocks = static_cast<int>(cdiv(m, kPanelRows));
-  LQ_LAUNCH("panel_small", panel_small_kernel, dim3(blocks), dim3(256), 0, s, P, m, l, S, w, upper ? 1 : 0, out,
-            tr ? 1 : 0);
+  LQ_LAUNCH("panel_small", panel_small_kernel, dim3(blocks), dim3(256), 0, s, P, m, l, nt, S, w, out, tr ? 1 : 0);
 }
 
 }  // namespace
@@ -621,35 +653,35 @@ SvdPlan make_svd_plan(int64_t d, int64_t k, int r, int oversample, bool exact) {
   p.l = l;
   p.nt = static_cast<int>(cdiv(l, 16));
   const int LP = 16 * p.nt;
-  const int rt = p.nt <= 2 ? 1 : 2;
-  const int64_t target = 512;
-  // gemm_nn: row blocks of 64 * rt rows, K splits of a multiple of the K chunk;
-  // split-K partials kept under ~8% of E's bytes (S * LP / k).
-  p.nn_row_blocks = static_cast<int>(cdiv(d, 64 * rt));
-  int64_t s_nn = cdiv(target, p.nn_row_blocks);
-  int64_t cap = (k * 8) / (100 * LP);
-  if (cap < 1) cap = 1;
-  if (s_nn > cap) s_nn = cap;
-  if (s_nn < 1) s_nn = 1;
-  p.nn_kper = round_up(cdiv(k, s_nn), kNnChunk);
-  p.nn_splits = static_cast<int>(cdiv(k, p.nn_kper));
-  // gemm_tn: column blocks of 128, row splits of a multiple of two row chunks.
-  p.tn_col_blocks = static_cast<int>(cdiv(k, 128));
-  int64_t s_tn = cdiv(target, p.tn_col_blocks);
-  cap = (d * 8) / (100 * LP);
-  if (cap < 1) cap = 1;
-  if (s_tn > cap) s_tn = cap;
-  if (s_tn < 1) s_tn = 1;
-  p.tn_rper = round_up(cdiv(d, s_tn), 2 * kTnChunk);
-  p.tn_splits = static_cast<int>(cdiv(d, p.tn_rper));
+  const int64_t target = 512;   // workgroups per product (256 CUs, two each)
+  // Split of the contraction: enough workgroups to fill the chip, split-K
+  // partials kept under ~8% of E's bytes (S * LP / len), each split at least
+  // one unit of the kernel's K granularity.
+  auto choose = [&](int64_t tiles, int64_t len, int unit, int64_t& per) {
+    int64_t sp = cdiv(target, tiles);
+    int64_t cap = (len * 8) / (100 * LP);
+    if (cap < 1) cap = 1;
+    if (sp > cap) sp = cap;
+    if (sp > cdiv(len, unit)) sp = cdiv(len, unit);
+    if (sp < 1) sp = 1;
+    per = round_up(cdiv(len, sp), unit);
+    return static_cast<int>(cdiv(len, per));
+  };
+  const GemmShape nn = gemm_shape(false, p.nt), tn = gemm_shape(true, p.nt);
+  p.nn_row_blocks = static_cast<int>(cdiv(d, nn.tile));
+  p.nn_splits = choose(p.nn_row_blocks, k, nn.unit, p.nn_kper);
+  p.tn_col_blocks = static_cast<int>(cdiv(k, tn.tile));
+  p.tn_splits = choose(p.tn_col_blocks, d, tn.unit, p.tn_rper);
+  p.k_pad = p.nn_splits * p.nn_kper;
+  p.d_pad = p.tn_splits * p.tn_rper;
   p.gram_parts_d = static_cast<int>(cdiv(d, kGramRows));
   p.gram_parts_k = static_cast<int>(cdiv(k, kGramRows));
   const int64_t gp = p.gram_parts_d > p.gram_parts_k ? p.gram_parts_d : p.gram_parts_k;
   const int64_t E = static_cast<int64_t>(l) * (l + 1) / 2;
-  p.off_omega = take(k * l * 4);
+  p.off_omega = take(p.k_pad * LP * 4);
   p.off_y = take(d * l * 4);
-  p.off_qy = take(d * l * 4);
-  p.off_z = take(k * l * 4);
+  p.off_qy = take(p.d_pad * LP * 4);
+  p.off_z = take(p.k_pad * LP * 4);
   const int64_t part_rows = (p.nn_splits * d > p.tn_splits * k) ? p.nn_splits * d : p.tn_splits * k;
   p.off_part = take(part_rows * LP * 4);
   p.off_gram_parts = take(gp * E * 8);
@@ -662,9 +694,10 @@ SvdPlan make_svd_plan(int64_t d, int64_t k, int r, int oversample, bool exact) {
   return p;
 }
 
-hipError_t run_sketch(uint64_t seed, int t, int64_t k, int l, float* out, hipStream_t s) {
-  const int64_t n = k * l;
-  LQ_LAUNCH("sketch", sketch_kernel, dim3(static_cast<unsigned>(cdiv(n, 256))), dim3(256), 0, s, seed, t, k, l, out);
+hipError_t run_sketch(uint64_t seed, int t, int64_t k, int l, int nt, int64_t rows, float* out, hipStream_t s) {
+  const int64_t n = rows * 16 * nt;
+  LQ_LAUNCH("sketch", sketch_kernel, dim3(static_cast<unsigned>(cdiv(n, 256))), dim3(256), 0, s, seed, t, k, l, nt,
+            rows, out);
   return hipGetLastError();
 }
 
@@ -700,20 +733,25 @@ hipError_t run_lowrank(const float* E, const SvdPlan& pl, int q, const float* om
   float* SA = reinterpret_cast<float*>(ws + pl.off_sa);
   double* stats = reinterpret_cast<double*>(ws + pl.off_stats);
   const ObjectiveArgs none{nullptr, 0, nullptr, 0, nullptr};
-  const float* X0 = omega;
-  if (X0 == nullptr) {
-    hipError_t e = run_sketch(seed, t, k, l, Om, s);
+  const int64_t nfrag = pl.k_pad * 16 * pl.nt;
+  if (omega == nullptr) {
+    hipError_t e = run_sketch(seed, t, k, l, pl.nt, pl.k_pad, Om, s);
     if (e != hipSuccess) return e;
-    X0 = Om;
+  } else {
+    LQ_LAUNCH("to_frag", to_frag_kernel, dim3(static_cast<unsigned>(cdiv(nfrag, 256))), dim3(256), 0, s, omega, k, l,
+              pl.nt, pl.k_pad, Om);
   }
   double* gtotal = reinterpret_cast<double*>(ws + pl.off_gram_total);
   const int E_ = l * (l + 1) / 2;
   // product and split-K reduction; mode 1 then orthonormalises (Gram, Cholesky,
-  // R^-1), mode 2 runs the core solve, mode 0 keeps the raw product
-  auto product = [&](bool transposed, const float* panel, float* out, int mode) {
-    launch_gemm(transposed, E, d, k, panel, l, pl, part, s);
-    const int64_t m = transposed ? k : d;
-    launch_reduce(pl.nt, part, transposed ? pl.tn_splits : pl.nn_splits, m, l, out, mode ? gparts : nullptr, s);
+  // R^-1), mode 2 runs the core solve, mode 0 keeps the raw product.  E Z goes
+  // to Y (row-major, d x l); E^T Q goes to Z (fragment order, k_pad rows).
+  auto product = [&](bool transposed, const float* panel, int mode) {
+    launch_gemm(transposed, E, d, k, panel, pl, part, s);
+    if (transposed)
+      launch_reduce(pl.nt, part, pl.tn_splits, k, pl.k_pad, l, nullptr, Z, mode ? gparts : nullptr, s);
+    else
+      launch_reduce(pl.nt, part, pl.nn_splits, d, d, l, Y, nullptr, mode ? gparts : nullptr, s);
     if (mode == 0) return;
     const int P = transposed ? pl.gram_parts_k : pl.gram_parts_d;
     LQ_LAUNCH("gram_sum", gram_sum_kernel, dim3((E_ + 63) / 64), dim3(256), 0, s, gparts, P, E_, gtotal);
@@ -723,17 +761,17 @@ hipError_t run_lowrank(const float* E, const SvdPlan& pl, int q, const float* om
   // Y = E Omega; R^-1 of its Gram.  Each power iteration multiplies by E^T and
   // E and re-orthonormalises Y only: span(E Z) does not depend on Z's basis, so
   // orthonormalising Z as well would not change the subspace.
-  product(false, X0, Y, 1);
+  product(false, Om, 1);
   for (int it = 0; it < q; ++it) {
-    launch_trsm(pl.nt, Y, d, l, Rinv, Qy, s);
-    product(true, Qy, Z, 0);
-    product(false, Z, Y, 1);
+    launch_trsm(pl.nt, Y, d, pl.d_pad, l, Rinv, Qy, s);
+    product(true, Qy, 0);
+    product(false, Z, 1);
   }
   // Q = Y R^-1; C = E^T Q, then the core solve on C^T C
-  launch_trsm(pl.nt, Y, d, l, Rinv, Qy, s);
-  product(true, Qy, Z, 2);
-  panel_small(Qy, d, l, SB, r, false, B, false, s);
-  panel_small(Z, k, l, SA, r, false, A, true, s);
+  launch_trsm(pl.nt, Y, d, pl.d_pad, l, Rinv, Qy, s);
+  product(true, Qy, 2);
+  panel_small(Qy, d, l, pl.nt, SB, r, B, false, s);
+  panel_small(Z, k, l, pl.nt, SA, r, A, true, s);
   return hipGetLastError();
 }
 
