@@ -23,7 +23,7 @@ struct ObjectiveArgs {
 };
 
 // Skinny panels that feed the thin products as their B operand (the sketch,
-// Q = Y R^-1 and Z = E^T Q) are stored in fragment order: 16-row blocks, each
+// Y and Z = E^T Q) are stored in fragment order: 16-row blocks, each
 // a run of NT = ceil(l / 16) tiles of 16 x 16 floats, element (rho, c) of a
 // tile at ((rho % 16) / 4) * 64 + (c % 16) * 4 + rho % 4.  Lane 16 g + i of a
 // wave then finds the four K-steps it feeds to one MFMA group in a single
@@ -50,7 +50,7 @@ struct SvdPlan {
   int64_t tn_rper;
   int gram_parts_d, gram_parts_k;
   int64_t k_pad, d_pad;   // fragment-order panel rows: nn_splits * nn_kper and tn_splits * tn_rper
-  int64_t off_omega, off_y, off_qy, off_z, off_part, off_gram_parts, off_gram_total, off_rinv, off_sb, off_sa;
+  int64_t off_omega, off_y, off_z, off_part, off_gram_parts, off_gram_total, off_rinv, off_sb, off_sa;
   int64_t off_stats, off_x;
   int64_t bytes;
 };

@@ -6,7 +6,9 @@
 //   Y = E Omega;  Q = orth(Y);  repeat q: Z = E^T Q, Q = orth(E Z);
 //   C = E^T Q;  the SVD of Q^T E = C^T comes from the eigen-decomposition of
 //   C^T C (l x l, fp64).
-// orth(P) is CholQR: fp64 Gram P^T P = R^T R (fp64 Cholesky), then P R^-1.
+// orth(Y) is CholQR: fp64 Gram Y^T Y = R^T R (fp64 Cholesky), Q = Y R^-1.  Q is
+// never formed: E^T Q = (E^T Y) R^-1 is applied to the summed rows of E^T Y in
+// the split-K reduction, and B = Q S_B = Y (R^-1 S_B).
 // Tiny matrices use an exact one-sided Jacobi SVD of E itself.
 //
 // Kernels (besides the thin products in gemm_kernels.hip):
@@ -15,7 +17,6 @@
 //   gram_sum      fixed-order sum of the Gram partials
 //   small_kernel  single workgroup: Cholesky and R^-1 (orthonormalisation), or
 //                 the l x l core solve (one-sided Jacobi)
-//   trsm_rows     Q = Y R^-1 by forward substitution, one row per thread
 //   panel_small   P S for a row panel P and a small S: B = Q S_B, A = (C S_A)^T
 //   exact_jacobi  single-workgroup one-sided Jacobi SVD for tiny matrices
 // Every reduction runs in a fixed order, so results are deterministic.
@@ -268,17 +269,20 @@ __device__ void jacobi_sweeps(double* K, float* V, const uint16_t* sched, int n,
 constexpr int kSmallDoubles = 2 * kMaxL * (kMaxL + 1) + (kMaxL * (kMaxL + 1)) / 2 + 4 * kMaxL + 64 + (kMaxL * kMaxL) / 8;
 
 // Single workgroup (256 threads) on the l x l Gram of a panel.
-//   mode 1: its Cholesky factor R (G = R^T R), written to Rinv as fp32 with the
-//     strict upper triangle of R and 1/R[a][a] on the diagonal.
+//   mode 1: X = R^-1 for the Cholesky factor R of the Gram (G = R^T R), written
+//     to Xinv as fp32 (l x l row-major, upper triangular).  A direction whose
+//     pivot was dropped gets a zero column, so Y X matches forward substitution
+//     with that component set to zero.
 //   mode 2: the core solve.  Q is orthonormal (fp64 Gram and Cholesky; its fp32
 //     rounding leaves Q^T Q = I to ~1e-7), so Q^T E = C^T and its singular values
 //     are those of K, the Cholesky factor of H = C^T C (H = K^T K).  One-sided
 //     Jacobi orthogonalises K's columns, K V = U diag(sigma), accumulating V (the
 //     eigenvectors of H); round-robin pairs, each pair's two columns owned by a
-//     group of g lanes.  sigma descending; S_B = V_r diag(sigma^1/2) and
-//     S_A = V_r diag(sigma^-1/2), so B = Q S_B and A = (C S_A)^T.
+//     group of g lanes.  sigma descending; S_A = V_r diag(sigma^-1/2) so that
+//     A = (C S_A)^T, and SB = X V_r diag(sigma^1/2) with Xinv the R^-1 of the
+//     panel Y (Q = Y X), so that B = Y SB.
 __global__ __launch_bounds__(256) void small_kernel(const double* __restrict__ gram, int l, int mode,
-                                                    float* __restrict__ Rinv, int r, float* __restrict__ SB,
+                                                    float* __restrict__ Xinv, int r, float* __restrict__ SB,
                                                     float* __restrict__ SA, float* __restrict__ sigma,
                                                     double* __restrict__ stats, ObjectiveArgs obj) {
   __shared__ double smem[kSmallDoubles];
@@ -301,13 +305,28 @@ __global__ __launch_bounds__(256) void small_kernel(const double* __restrict__ g
   __syncthreads();
   chol_upper(G, ldg, l, rdiag, tmp);
   if (mode == 1) {
-    // R (upper, fp32, row-major l x l; diagonal as 1/R[a][a], 0 for a dropped direction)
+    // 1/R[c][c] (0 for a dropped direction) in norm2; row b of X by thread b:
+    // X[b][c] = (delta_bc - sum_{b <= a < c} X[b][a] R[a][c]) / R[c][c]
+    for (int c = tid; c < l; c += blockDim.x) norm2[c] = rdiag[c] > 0.0 ? 1.0 / rdiag[c] : 0.0;
+    __syncthreads();
+    double* X = K;
+    for (int b = tid; b < l; b += blockDim.x) {
+      for (int c = 0; c < b; ++c) X[b * ldg + c] = 0.0;
+      for (int c = b; c < l; ++c) {
+        double s0 = (c == b) ? 1.0 : 0.0, s1 = 0.0;
+        int a = b;
+        for (; a + 1 < c; a += 2) {
+          s0 = fma(-X[b * ldg + a], G[a * ldg + c], s0);
+          s1 = fma(-X[b * ldg + a + 1], G[(a + 1) * ldg + c], s1);
+        }
+        if (a < c) s0 = fma(-X[b * ldg + a], G[a * ldg + c], s0);
+        X[b * ldg + c] = (s0 + s1) * norm2[c];
+      }
+    }
+    __syncthreads();
     for (int e = tid; e < l * l; e += blockDim.x) {
       const int a = e / l, b = e - a * l;
-      float v = 0.f;
-      if (a == b) v = rdiag[a] > 0.0 ? static_cast<float>(1.0 / rdiag[a]) : 0.f;
-      else if (a < b) v = static_cast<float>(G[a * ldg + b]);
-      Rinv[e] = v;
+      Xinv[e] = static_cast<float>(X[a * ldg + b]);
     }
     return;
   }
@@ -347,7 +366,10 @@ __global__ __launch_bounds__(256) void small_kernel(const double* __restrict__ g
     const int a = order[c];
     const double sg = sqrt(norm2[a]);
     const double sq = sqrt(sg);
-    SB[row * r + c] = static_cast<float>(V[a * ldk + row] * sq);
+    // SB[row][c] = sum_{j >= row} X[row][j] V[j][a] sqrt(sigma)
+    double acc = 0.0;
+    for (int j = row; j < l; ++j) acc = fma(static_cast<double>(Xinv[row * l + j]), static_cast<double>(V[a * ldk + j]), acc);
+    SB[row * r + c] = static_cast<float>(acc * sq);
     SA[row * r + c] = sg > 0.0 ? static_cast<float>(V[a * ldk + row] / sq) : 0.f;
   }
   for (int c = tid; c < r; c += blockDim.x) sigma[c] = static_cast<float>(sqrt(norm2[order[c]]));
@@ -360,19 +382,212 @@ __global__ __launch_bounds__(256) void small_kernel(const double* __restrict__ g
   write_objective(obj, s2);
 }
 
+// ---------------------------------------------------------------------------
+// The same two solves for l <= 32.
+//
+// Cholesky by one wave: lane b keeps column b of the Gram (rows 0..LM-1) in
+// registers.  Step j takes the pivot from lane j and row j of R from the lanes
+// after it by readlane, then updates the trailing columns.  Entries below the
+// diagonal pick up values that are never read back into the upper triangle and
+// are dropped at the end.  For INV the same steps carry T = R^-T (lane b holds
+// column b of T, starting from the identity): row j of T is divided by R[j][j]
+// and rows a > j lose R[j][a] times it; then X = R^-1 = T^T, i.e. lane b holds
+// row b of X.  A pivot at or below 1e-13 of the largest diagonal entry drops
+// its direction (zero row of R, zero column of X).
+__device__ __forceinline__ double bcast_lane(double v, int lane) {
+  const int lo = __builtin_amdgcn_readlane(__double2loint(v), lane);
+  const int hi = __builtin_amdgcn_readlane(__double2hiint(v), lane);
+  return __hiloint2double(hi, lo);
+}
+
+template <int LM, bool INV>
+__device__ __forceinline__ void chol_wave(const double* __restrict__ gram, int l, double (&g)[LM], double (&t)[LM]) {
+  const int b = threadIdx.x & 63;
+#pragma unroll
+  for (int a = 0; a < LM; ++a) {
+    g[a] = (a <= b && b < l) ? gram[packed_index(a, b, l)] : 0.0;
+    if (INV) t[a] = (a == b) ? 1.0 : 0.0;
+  }
+  double dg = b < l ? gram[packed_index(b, b, l)] : 0.0;
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) dg = fmax(dg, __shfl_xor(dg, off));
+  const double tol = 1e-13 * dg;
+#pragma unroll
+  for (int j = 0; j < LM; ++j) {
+    if (j < l) {
+      const double piv = bcast_lane(g[j], j);
+      const bool keep = piv > tol && piv > 0.0;
+      const double inv = keep ? rsq_f64(piv) : 0.0;   // 1 / R[j][j]
+      const double rjj = piv * inv;
+      g[j] = b > j ? g[j] * inv : (b == j ? rjj : g[j]);
+      if (INV) t[j] *= inv;
+#pragma unroll
+      for (int a = j + 1; a < LM; ++a) {
+        const double rja = bcast_lane(g[j], a);
+        g[a] = fma(-rja, g[j], g[a]);
+        if (INV) t[a] = fma(-rja, t[j], t[a]);
+      }
+    }
+  }
+}
+
+// mode 1 for l <= LM: X = R^-1 (fp32, row-major l x l) by one wave.
+template <int LM>
+__global__ __launch_bounds__(64) void chol_inv_wave_kernel(const double* __restrict__ gram, int l,
+                                                           float* __restrict__ Xinv) {
+  double g[LM], t[LM];
+  chol_wave<LM, true>(gram, l, g, t);
+  const int lane = threadIdx.x;
+  if (lane < l) {
+#pragma unroll
+    for (int a = 0; a < LM; ++a)
+      if (a < l) Xinv[lane * l + a] = static_cast<float>(t[a]);
+  }
+}
+
+// mode 2 for l <= LM (LM <= 32), 256 threads.  Wave 0 factors H = K^T K; then
+// one-sided Jacobi on K's columns with pair i of a round owned by lanes
+// 16 i .. 16 i + 15 (rows sub and sub + 16).  Round-robin positions advance by
+// one per round, so each lane tracks its pair's two players in registers.  The
+// rotation angle is taken in fp32 (it only sets how much of the pair's coupling
+// is removed); c = (1 + t^2)^-1/2 is exact to fp64 so the rotation stays
+// orthogonal.  V (fp32) accumulates the rotations.
+template <int LM>
+__global__ __launch_bounds__(256) void core_small_kernel(const double* __restrict__ gram, int l,
+                                                         const float* __restrict__ Xinv, int r, float* __restrict__ SB,
+                                                         float* __restrict__ SA, float* __restrict__ sigma,
+                                                         double* __restrict__ stats, ObjectiveArgs obj) {
+  constexpr int LD = 33;
+  __shared__ double K[32 * LD];
+  __shared__ float V[32 * LD];
+  __shared__ float Xs[32 * 32];
+  __shared__ double norm2[32];
+  __shared__ int order[32];
+  const int tid = threadIdx.x;
+  for (int e = tid; e < 32 * LD; e += blockDim.x) {
+    const int c = e / LD, row = e - c * LD;
+    V[e] = (row == c) ? 1.f : 0.f;
+  }
+  for (int e = tid; e < l * l; e += blockDim.x) Xs[e] = Xinv[e];
+  if (tid < 64) {
+    double g[LM], t[LM];
+    chol_wave<LM, false>(gram, l, g, t);
+    if (tid < 32) {
+#pragma unroll
+      for (int a = 0; a < 32; ++a) K[tid * LD + a] = (a < LM && a <= tid && tid < l) ? g[a < LM ? a : 0] : 0.0;
+    }
+  }
+  __syncthreads();
+  const int n = l + (l & 1);
+  const int pair = tid >> 4, sub = tid & 15;
+  const bool active = pair < n / 2;
+  int pa = pair, pb = n - 1 - pair;   // round 0 players
+  int sweeps = 0;
+  for (int sweep = 0; sweep < 30; ++sweep) {
+    int rot = 0;
+    for (int rnd = 0; rnd < n - 1; ++rnd) {
+      if (active) {
+        const int p = pa < pb ? pa : pb, q = pa < pb ? pb : pa;
+        double* kp = K + p * LD + sub;
+        double* kq = K + q * LD + sub;
+        float* vp = V + p * LD + sub;
+        float* vq = V + q * LD + sub;
+        const double xp0 = kp[0], xp1 = kp[16], xq0 = kq[0], xq1 = kq[16];
+        const float yp0 = vp[0], yp1 = vp[16], yq0 = vq[0], yq1 = vq[16];
+        double al = fma(xp1, xp1, xp0 * xp0);
+        double be = fma(xq1, xq1, xq0 * xq0);
+        double ga = fma(xp1, xq1, xp0 * xq0);
+        al = group_sum<16>(al);
+        be = group_sum<16>(be);
+        ga = group_sum<16>(ga);
+        if (q < l && ga * ga > 1e-14 * (al * be) && ga != 0.0) {
+          const double w = be - al;
+          double rg = __builtin_amdgcn_rcp(ga);
+          rg = fma(rg, fma(-ga, rg, 1.0), rg);
+          const double zeta = 0.5 * w * rg;
+          double t;
+          if (fabs(zeta) > 1e8) {
+            double rw = __builtin_amdgcn_rcp(w);
+            rw = fma(rw, fma(-w, rw, 1.0), rw);
+            t = ga * rw;
+          } else {
+            const float zf = static_cast<float>(fabs(zeta));
+            const float tf = __builtin_amdgcn_rcpf(zf + __builtin_amdgcn_sqrtf(fmaf(zf, zf, 1.0f)));
+            t = zeta >= 0.0 ? static_cast<double>(tf) : -static_cast<double>(tf);
+          }
+          const double c = rsq_f64(fma(t, t, 1.0)), s = c * t;
+          const float cf = static_cast<float>(c), sf = static_cast<float>(s);
+          kp[0] = c * xp0 - s * xq0;
+          kq[0] = s * xp0 + c * xq0;
+          kp[16] = c * xp1 - s * xq1;
+          kq[16] = s * xp1 + c * xq1;
+          vp[0] = cf * yp0 - sf * yq0;
+          vq[0] = sf * yp0 + cf * yq0;
+          vp[16] = cf * yp1 - sf * yq1;
+          vq[16] = sf * yp1 + cf * yq1;
+          rot = 1;
+        }
+      }
+      // advance the circle: players 1 .. n-1 move up one position
+      pa = pa == 0 ? 0 : (pa == n - 1 ? 1 : pa + 1);
+      pb = pb == 0 ? 0 : (pb == n - 1 ? 1 : pb + 1);
+      __syncthreads();
+    }
+    sweeps = sweep + 1;
+    if (!__syncthreads_or(rot)) break;
+  }
+  if (tid < l) {
+    double s = 0.0;
+    for (int row = 0; row < n; ++row) s += K[tid * LD + row] * K[tid * LD + row];
+    norm2[tid] = s;
+  }
+  __syncthreads();
+  if (tid < l) {
+    const double la = norm2[tid];
+    int rank = 0;
+    for (int b = 0; b < l; ++b) rank += (norm2[b] > la || (norm2[b] == la && b < tid)) ? 1 : 0;
+    order[rank] = tid;
+  }
+  __syncthreads();
+  for (int idx = tid; idx < l * r; idx += blockDim.x) {
+    const int row = idx / r, c = idx - row * r;
+    const int a = order[c];
+    const double sg = sqrt(norm2[a]);
+    const double sq = sqrt(sg);
+    double acc = 0.0;
+    for (int j = row; j < l; ++j) acc = fma(static_cast<double>(Xs[row * l + j]), static_cast<double>(V[a * LD + j]), acc);
+    SB[row * r + c] = static_cast<float>(acc * sq);
+    SA[row * r + c] = sg > 0.0 ? static_cast<float>(V[a * LD + row] / sq) : 0.f;
+  }
+  if (tid < r) sigma[tid] = static_cast<float>(sqrt(norm2[order[tid]]));
+  double s2 = 0.0;
+  for (int c = 0; c < r; ++c) s2 += norm2[order[c]];
+  if (tid == 0 && stats) {
+    stats[0] = s2;
+    stats[1] = static_cast<double>(sweeps);
+  }
+  write_objective(obj, s2);
+}
+
 // Sum of the split-K partials, sum_s part[s], in fixed order for a tile of
-// kGramRows rows, written row-major (out_rm, m x l) and/or in fragment order
-// (out_frag, zero-padded to m_pad rows), plus the fp64 Gram partial (packed
-// upper triangle) of the tile when gram_parts is given.
+// kGramRows rows, optionally right-multiplied by X (l x l fp32, upper
+// triangular), written in fragment order (zero-padded to m_pad rows), plus the
+// fp64 Gram partial (packed upper triangle) of the tile when gram_parts is given.
 template <int NT>
 __global__ __launch_bounds__(256) void reduce_gram_kernel(const float* __restrict__ part, int S, int64_t m,
-                                                          int64_t m_pad, int l, float* __restrict__ out_rm,
-                                                          float* __restrict__ out_frag,
-                                                          double* __restrict__ gram_parts) {
-  constexpr int LP = 16 * NT;
+                                                          int64_t m_pad, int l, const float* __restrict__ X,
+                                                          float* __restrict__ out, double* __restrict__ gram_parts) {
+  constexpr int LP = 16 * NT, PER = (kGramRows * LP + 255) / 256;
   __shared__ float rows[kGramRows * (LP + 1)];
+  __shared__ float Xs[LP * LP];
   const int64_t r0 = static_cast<int64_t>(blockIdx.x) * kGramRows;
   const int64_t stride = m * LP;
+  if (X) {
+    for (int e = threadIdx.x; e < LP * LP; e += blockDim.x) {
+      const int a = e / LP, b = e - a * LP;
+      Xs[e] = (a < l && b < l) ? X[a * l + b] : 0.f;
+    }
+  }
   for (int idx = threadIdx.x; idx < kGramRows * LP; idx += blockDim.x) {
     const int rr = idx / LP, n = idx - rr * LP;
     const int64_t row = r0 + rr;
@@ -386,10 +601,34 @@ __global__ __launch_bounds__(256) void reduce_gram_kernel(const float* __restric
 #pragma unroll
         for (int u = 0; u < 16; ++u) s += v[u];
       }
-      if (out_rm) out_rm[row * l + n] = s;
     }
-    if (out_frag && row < m_pad) out_frag[frag_index(row, n, NT)] = s;
     rows[rr * (LP + 1) + n] = s;
+  }
+  if (X) {
+    __syncthreads();
+    float t[PER];
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int idx = threadIdx.x + 256 * u;
+      float acc = 0.f;
+      if (idx < kGramRows * LP) {
+        const int rr = idx / LP, n = idx - rr * LP;
+        for (int a = 0; a <= n; ++a) acc = fmaf(rows[rr * (LP + 1) + a], Xs[a * LP + n], acc);
+      }
+      t[u] = acc;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int idx = threadIdx.x + 256 * u;
+      if (idx < kGramRows * LP) rows[(idx / LP) * (LP + 1) + idx % LP] = t[u];
+    }
+    __syncthreads();
+  }
+  for (int idx = threadIdx.x; idx < kGramRows * LP; idx += blockDim.x) {
+    const int rr = idx / LP, n = idx - rr * LP;
+    const int64_t row = r0 + rr;
+    if (row < m_pad) out[frag_index(row, n, NT)] = rows[rr * (LP + 1) + n];
   }
   if (gram_parts == nullptr || r0 >= m) return;
   __syncthreads();
@@ -427,40 +666,6 @@ __global__ __launch_bounds__(256) void panel_small_kernel(const float* __restric
       else out[row * w + c] = acc;
     }
   }
-}
-
-// Q = Y R^-1 row by row: R from small_kernel mode 1 (strict upper triangle and
-// 1/R[a][a] on the diagonal, fp32).  Forward substitution q R = y with q in
-// registers; R is read from LDS as a broadcast (all lanes the same address).
-// Y is row-major (m x l); Q is written in fragment order over m_pad rows.
-template <int NT>
-__global__ __launch_bounds__(256) void trsm_rows_kernel(const float* __restrict__ Y, int64_t m, int64_t m_pad, int l,
-                                                        const float* __restrict__ R, float* __restrict__ Q) {
-  constexpr int LP = 16 * NT;
-  __shared__ float Rs[LP * LP];
-  for (int e = threadIdx.x; e < LP * LP; e += blockDim.x) {
-    const int a = e / LP, b = e - a * LP;
-    Rs[e] = (a < l && b < l) ? R[a * l + b] : 0.f;
-  }
-  __syncthreads();
-  const int64_t row = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (row >= m_pad) return;
-  float q[LP];
-  if (row < m) {
-    const float* y = Y + row * l;
-#pragma unroll
-    for (int c = 0; c < LP; ++c) {
-      float s = (c < l) ? y[c] : 0.f;
-#pragma unroll
-      for (int a = 0; a < c; ++a) s = fmaf(-q[a], Rs[a * LP + c], s);
-      q[c] = s * Rs[c * LP + c];
-    }
-  } else {
-#pragma unroll
-    for (int c = 0; c < LP; ++c) q[c] = 0.f;
-  }
-#pragma unroll
-  for (int c = 0; c < LP; ++c) Q[frag_index(row, c, NT)] = q[c];
 }
 
 // ---------------------------------------------------------------------------
@@ -594,38 +799,40 @@ int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 template <int NT>
-void reduce_typed(const float* part, int S, int64_t m, int64_t m_pad, int l, float* out_rm, float* out_frag,
+void reduce_typed(const float* part, int S, int64_t m, int64_t m_pad, int l, const float* X, float* out,
                   double* gram_parts, hipStream_t s) {
-  const int blocks = static_cast<int>(cdiv(out_frag ? m_pad : m, kGramRows));
-  LQ_LAUNCH("reduce_gram", (reduce_gram_kernel<NT>), dim3(blocks), dim3(256), 0, s, part, S, m, m_pad, l, out_rm,
-            out_frag, gram_parts);
+  const int blocks = static_cast<int>(cdiv(m_pad, kGramRows));
+  LQ_LAUNCH("reduce_gram", (reduce_gram_kernel<NT>), dim3(blocks), dim3(256), 0, s, part, S, m, m_pad, l, X, out,
+            gram_parts);
 }
 
-void launch_reduce(int nt, const float* part, int S, int64_t m, int64_t m_pad, int l, float* out_rm, float* out_frag,
+void launch_reduce(int nt, const float* part, int S, int64_t m, int64_t m_pad, int l, const float* X, float* out,
                    double* gram_parts, hipStream_t s) {
   switch (nt) {
-    case 1: reduce_typed<1>(part, S, m, m_pad, l, out_rm, out_frag, gram_parts, s); break;
-    case 2: reduce_typed<2>(part, S, m, m_pad, l, out_rm, out_frag, gram_parts, s); break;
-    case 3: reduce_typed<3>(part, S, m, m_pad, l, out_rm, out_frag, gram_parts, s); break;
-    case 4: reduce_typed<4>(part, S, m, m_pad, l, out_rm, out_frag, gram_parts, s); break;
-    default: reduce_typed<5>(part, S, m, m_pad, l, out_rm, out_frag, gram_parts, s); break;
+    case 1: reduce_typed<1>(part, S, m, m_pad, l, X, out, gram_parts, s); break;
+    case 2: reduce_typed<2>(part, S, m, m_pad, l, X, out, gram_parts, s); break;
+    case 3: reduce_typed<3>(part, S, m, m_pad, l, X, out, gram_parts, s); break;
+    case 4: reduce_typed<4>(part, S, m, m_pad, l, X, out, gram_parts, s); break;
+    default: reduce_typed<5>(part, S, m, m_pad, l, X, out, gram_parts, s); break;
   }
 }
 
-template <int NT>
-void trsm_typed(const float* Y, int64_t m, int64_t m_pad, int l, const float* R, float* Q, hipStream_t s) {
-  LQ_LAUNCH("trsm_rows", (trsm_rows_kernel<NT>), dim3(static_cast<unsigned>(cdiv(m_pad, 256))), dim3(256), 0, s, Y, m,
-            m_pad, l, R, Q);
+template <int LM>
+void small_wave_typed(int mode, const double* gram, int l, float* Xinv, int r, float* SB, float* SA, float* sigma,
+                      double* stats, const ObjectiveArgs& obj, hipStream_t s) {
+  if (mode == 1)
+    LQ_LAUNCH("chol_inv", chol_inv_wave_kernel<LM>, dim3(1), dim3(64), 0, s, gram, l, Xinv);
+  else
+    LQ_LAUNCH("core_svd", core_small_kernel<LM>, dim3(1), dim3(256), 0, s, gram, l, Xinv, r, SB, SA, sigma, stats, obj);
 }
 
-void launch_trsm(int nt, const float* Y, int64_t m, int64_t m_pad, int l, const float* R, float* Q, hipStream_t s) {
-  switch (nt) {
-    case 1: trsm_typed<1>(Y, m, m_pad, l, R, Q, s); break;
-    case 2: trsm_typed<2>(Y, m, m_pad, l, R, Q, s); break;
-    case 3: trsm_typed<3>(Y, m, m_pad, l, R, Q, s); break;
-    case 4: trsm_typed<4>(Y, m, m_pad, l, R, Q, s); break;
-    default: trsm_typed<5>(Y, m, m_pad, l, R, Q, s); break;
-  }
+// l <= 32: the register Cholesky is unrolled for the smallest of 8/16/24/32 rows that holds l.
+void launch_small_wave(int mode, const double* gram, int l, float* Xinv, int r, float* SB, float* SA, float* sigma,
+                       double* stats, const ObjectiveArgs& obj, hipStream_t s) {
+  if (l <= 8) small_wave_typed<8>(mode, gram, l, Xinv, r, SB, SA, sigma, stats, obj, s);
+  else if (l <= 16) small_wave_typed<16>(mode, gram, l, Xinv, r, SB, SA, sigma, stats, obj, s);
+  else if (l <= 24) small_wave_typed<24>(mode, gram, l, Xinv, r, SB, SA, sigma, stats, obj, s);
+  else small_wave_typed<32>(mode, gram, l, Xinv, r, SB, SA, sigma, stats, obj, s);
 }
 
 void panel_small(const float* P, int64_t m, int l, int nt, const float* S, int w, float* out, bool tr, hipStream_t s) {
@@ -679,8 +886,7 @@ SvdPlan make_svd_plan(int64_t d, int64_t k, int r, int oversample, bool exact) {
   const int64_t gp = p.gram_parts_d > p.gram_parts_k ? p.gram_parts_d : p.gram_parts_k;
   const int64_t E = static_cast<int64_t>(l) * (l + 1) / 2;
   p.off_omega = take(p.k_pad * LP * 4);
-  p.off_y = take(d * l * 4);
-  p.off_qy = take(p.d_pad * LP * 4);
+  p.off_y = take(p.d_pad * LP * 4);
   p.off_z = take(p.k_pad * LP * 4);
   const int64_t part_rows = (p.nn_splits * d > p.tn_splits * k) ? p.nn_splits * d : p.tn_splits * k;
   p.off_part = take(part_rows * LP * 4);
@@ -724,11 +930,10 @@ hipError_t run_lowrank(const float* E, const SvdPlan& pl, int q, const float* om
   }
   float* Om = reinterpret_cast<float*>(ws + pl.off_omega);
   float* Y = reinterpret_cast<float*>(ws + pl.off_y);
-  float* Qy = reinterpret_cast<float*>(ws + pl.off_qy);
   float* Z = reinterpret_cast<float*>(ws + pl.off_z);
   float* part = reinterpret_cast<float*>(ws + pl.off_part);
   double* gparts = reinterpret_cast<double*>(ws + pl.off_gram_parts);
-  float* Rinv = reinterpret_cast<float*>(ws + pl.off_rinv);
+  float* Xinv = reinterpret_cast<float*>(ws + pl.off_rinv);
   float* SB = reinterpret_cast<float*>(ws + pl.off_sb);
   float* SA = reinterpret_cast<float*>(ws + pl.off_sa);
   double* stats = reinterpret_cast<double*>(ws + pl.off_stats);
@@ -744,33 +949,35 @@ hipError_t run_lowrank(const float* E, const SvdPlan& pl, int q, const float* om
   double* gtotal = reinterpret_cast<double*>(ws + pl.off_gram_total);
   const int E_ = l * (l + 1) / 2;
   // product and split-K reduction; mode 1 then orthonormalises (Gram, Cholesky,
-  // R^-1), mode 2 runs the core solve, mode 0 keeps the raw product.  E Z goes
-  // to Y (row-major, d x l); E^T Q goes to Z (fragment order, k_pad rows).
+  // X = R^-1), mode 2 runs the core solve, mode 0 keeps the product.  E P goes
+  // to Y (fragment order, d_pad rows, not orthonormalised: Q = Y X); E^T Y goes
+  // through X to Z = E^T Q (fragment order, k_pad rows).
   auto product = [&](bool transposed, const float* panel, int mode) {
     launch_gemm(transposed, E, d, k, panel, pl, part, s);
     if (transposed)
-      launch_reduce(pl.nt, part, pl.tn_splits, k, pl.k_pad, l, nullptr, Z, mode ? gparts : nullptr, s);
+      launch_reduce(pl.nt, part, pl.tn_splits, k, pl.k_pad, l, Xinv, Z, mode ? gparts : nullptr, s);
     else
-      launch_reduce(pl.nt, part, pl.nn_splits, d, d, l, Y, nullptr, mode ? gparts : nullptr, s);
+      launch_reduce(pl.nt, part, pl.nn_splits, d, pl.d_pad, l, nullptr, Y, mode ? gparts : nullptr, s);
     if (mode == 0) return;
     const int P = transposed ? pl.gram_parts_k : pl.gram_parts_d;
     LQ_LAUNCH("gram_sum", gram_sum_kernel, dim3((E_ + 63) / 64), dim3(256), 0, s, gparts, P, E_, gtotal);
-    LQ_LAUNCH(mode == 1 ? "chol_inv" : "core_svd", small_kernel, dim3(1), dim3(256), 0, s, gtotal, l, mode, Rinv, r,
-              SB, SA, sigma, stats, mode == 2 ? obj : none);
+    if (l <= 32)
+      launch_small_wave(mode, gtotal, l, Xinv, r, SB, SA, sigma, stats, mode == 2 ? obj : none, s);
+    else
+      LQ_LAUNCH(mode == 1 ? "chol_inv" : "core_svd", small_kernel, dim3(1), dim3(256), 0, s, gtotal, l, mode, Xinv, r,
+                SB, SA, sigma, stats, mode == 2 ? obj : none);
   };
-  // Y = E Omega; R^-1 of its Gram.  Each power iteration multiplies by E^T and
-  // E and re-orthonormalises Y only: span(E Z) does not depend on Z's basis, so
-  // orthonormalising Z as well would not change the subspace.
+  // Y = E Omega; X = R^-1 of its Gram.  Each power iteration multiplies by E^T
+  // and E and re-orthonormalises Y only: span(E Z) does not depend on Z's basis,
+  // so orthonormalising Z as well would not change the subspace.
   product(false, Om, 1);
   for (int it = 0; it < q; ++it) {
-    launch_trsm(pl.nt, Y, d, pl.d_pad, l, Rinv, Qy, s);
-    product(true, Qy, 0);
+    product(true, Y, 0);
     product(false, Z, 1);
   }
-  // Q = Y R^-1; C = E^T Q, then the core solve on C^T C
-  launch_trsm(pl.nt, Y, d, pl.d_pad, l, Rinv, Qy, s);
-  product(true, Qy, 2);
-  panel_small(Qy, d, l, pl.nt, SB, r, B, false, s);
+  // C = E^T Q = (E^T Y) X, then the core solve on C^T C
+  product(true, Y, 2);
+  panel_small(Y, d, l, pl.nt, SB, r, B, false, s);
   panel_small(Z, k, l, pl.nt, SA, r, A, true, s);
   return hipGetLastError();
 }
