@@ -131,29 +131,34 @@ __device__ void write_objective(const ObjectiveArgs& o, double sig2) {
 }
 
 // Sum of P Gram partials (packed upper triangles, E = l(l+1)/2 doubles each)
-// into one packed total.  Workgroup: 64 entries x 4 part groups; part group g
-// sums partials g, g+4, ... with 8 loads in flight, then the four group sums
-// are added in a fixed order.
-__global__ __launch_bounds__(256) void gram_sum_kernel(const double* __restrict__ parts, int P, int E,
-                                                       double* __restrict__ total) {
-  __shared__ double acc[4][64];
+// into one packed total.  Workgroup: 64 entries x 16 part groups; part group g
+// sums partials g, g+16, ... (eight loads in flight), then the sixteen group
+// sums are added in a fixed order.
+__global__ __launch_bounds__(1024) void gram_sum_kernel(const double* __restrict__ parts, int P, int E,
+                                                        double* __restrict__ total) {
+  __shared__ double acc[16][64];
   const int el = threadIdx.x & 63, pg = threadIdx.x >> 6;
   const int e = blockIdx.x * 64 + el;
   double s = 0.0;
   if (e < E) {
     int p = pg;
-    for (; p + 28 < P; p += 32) {
+    for (; p + 112 < P; p += 128) {
       double v[8];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) v[u] = parts[static_cast<int64_t>(p + 4 * u) * E + e];
+      for (int u = 0; u < 8; ++u) v[u] = parts[static_cast<int64_t>(p + 16 * u) * E + e];
 #pragma unroll
       for (int u = 0; u < 8; ++u) s += v[u];
     }
-    for (; p < P; p += 4) s += parts[static_cast<int64_t>(p) * E + e];
+    for (; p < P; p += 16) s += parts[static_cast<int64_t>(p) * E + e];
   }
   acc[pg][el] = s;
   __syncthreads();
-  if (pg == 0 && e < E) total[e] = ((acc[0][el] + acc[1][el]) + acc[2][el]) + acc[3][el];
+  if (pg == 0 && e < E) {
+    double t = 0.0;
+#pragma unroll
+    for (int g = 0; g < 16; ++g) t += acc[g][el];
+    total[e] = t;
+  }
 }
 
 // fp64 lane exchange inside a DPP row (16 lanes) or quad.
@@ -451,7 +456,8 @@ __global__ __launch_bounds__(64) void chol_inv_wave_kernel(const double* __restr
 // one per round, so each lane tracks its pair's two players in registers.  The
 // rotation angle is taken in fp32 (it only sets how much of the pair's coupling
 // is removed); c = (1 + t^2)^-1/2 is exact to fp64 so the rotation stays
-// orthogonal.  V (fp32) accumulates the rotations.
+// orthogonal.  V (fp32) accumulates the rotations.  Pairs with |cos| <= 1e-7
+// are skipped; the sweeps stop after one in which no pair had |cos| > 1e-4.
 template <int LM>
 __global__ __launch_bounds__(256) void core_small_kernel(const double* __restrict__ gram, int l,
                                                          const float* __restrict__ Xinv, int r, float* __restrict__ SB,
@@ -484,7 +490,7 @@ __global__ __launch_bounds__(256) void core_small_kernel(const double* __restric
   int pa = pair, pb = n - 1 - pair;   // round 0 players
   int sweeps = 0;
   for (int sweep = 0; sweep < 30; ++sweep) {
-    int rot = 0;
+    int big = 0;   // a rotation with |cos| above 1e-4 in this sweep
     for (int rnd = 0; rnd < n - 1; ++rnd) {
       if (active) {
         const int p = pa < pb ? pa : pb, q = pa < pb ? pb : pa;
@@ -500,22 +506,25 @@ __global__ __launch_bounds__(256) void core_small_kernel(const double* __restric
         al = group_sum<16>(al);
         be = group_sum<16>(be);
         ga = group_sum<16>(ga);
-        if (q < l && ga * ga > 1e-14 * (al * be) && ga != 0.0) {
+        const double g2 = ga * ga, ab = al * be;
+        if (q < l && g2 > 1e-14 * ab && ga != 0.0) {
+          // zeta = (be - al) / (2 ga) and t = sgn / (|zeta| + sqrt(1 + zeta^2)) to
+          // ~fp32 accuracy; c = (1 + t^2)^-1/2 with one Newton step on the hardware
+          // estimate (fp64-exact), s = c t.
           const double w = be - al;
-          double rg = __builtin_amdgcn_rcp(ga);
-          rg = fma(rg, fma(-ga, rg, 1.0), rg);
-          const double zeta = 0.5 * w * rg;
+          const double zeta = 0.5 * w * __builtin_amdgcn_rcp(ga);
           double t;
           if (fabs(zeta) > 1e8) {
-            double rw = __builtin_amdgcn_rcp(w);
-            rw = fma(rw, fma(-w, rw, 1.0), rw);
-            t = ga * rw;
+            t = ga * __builtin_amdgcn_rcp(w);
           } else {
             const float zf = static_cast<float>(fabs(zeta));
             const float tf = __builtin_amdgcn_rcpf(zf + __builtin_amdgcn_sqrtf(fmaf(zf, zf, 1.0f)));
             t = zeta >= 0.0 ? static_cast<double>(tf) : -static_cast<double>(tf);
           }
-          const double c = rsq_f64(fma(t, t, 1.0)), s = c * t;
+          const double u = fma(t, t, 1.0);
+          double c = __builtin_amdgcn_rsq(u);
+          c = c * fma(-0.5 * u * c, c, 1.5);
+          const double s = c * t;
           const float cf = static_cast<float>(c), sf = static_cast<float>(s);
           kp[0] = c * xp0 - s * xq0;
           kq[0] = s * xp0 + c * xq0;
@@ -525,7 +534,7 @@ __global__ __launch_bounds__(256) void core_small_kernel(const double* __restric
           vq[0] = sf * yp0 + cf * yq0;
           vp[16] = cf * yp1 - sf * yq1;
           vq[16] = sf * yp1 + cf * yq1;
-          rot = 1;
+          big |= g2 > 1e-8 * ab;
         }
       }
       // advance the circle: players 1 .. n-1 move up one position
@@ -534,7 +543,9 @@ __global__ __launch_bounds__(256) void core_small_kernel(const double* __restric
       __syncthreads();
     }
     sweeps = sweep + 1;
-    if (!__syncthreads_or(rot)) break;
+    // quadratic convergence: after a sweep whose rotations all had |cos| <= 1e-4
+    // the remaining coupling is ~1e-8 relative, so no verification sweep is run
+    if (!__syncthreads_or(big)) break;
   }
   if (tid < l) {
     double s = 0.0;
@@ -588,21 +599,39 @@ __global__ __launch_bounds__(256) void reduce_gram_kernel(const float* __restric
       Xs[e] = (a < l && b < l) ? X[a * l + b] : 0.f;
     }
   }
-  for (int idx = threadIdx.x; idx < kGramRows * LP; idx += blockDim.x) {
+  // every thread sums its PER elements over the S partials, four partials of
+  // all its elements in flight at a time, each element in ascending s order
+  float acc[PER];
+  int64_t off[PER];
+  bool ok[PER];
+#pragma unroll
+  for (int u = 0; u < PER; ++u) {
+    const int idx = threadIdx.x + 256 * u;
     const int rr = idx / LP, n = idx - rr * LP;
     const int64_t row = r0 + rr;
-    float s = 0.f;
-    if (row < m && n < l) {
-      const float* pp = part + row * LP + n;
-      for (int p = 0; p < S; p += 16) {
-        float v[16];
+    ok[u] = idx < kGramRows * LP && row < m && n < l;
+    off[u] = ok[u] ? row * LP + n : 0;
+    acc[u] = 0.f;
+  }
+  int p = 0;
+  for (; p + 4 <= S; p += 4) {
+    float v[4][PER];
 #pragma unroll
-        for (int u = 0; u < 16; ++u) v[u] = (p + u < S) ? pp[(p + u) * stride] : 0.f;
+    for (int q = 0; q < 4; ++q)
 #pragma unroll
-        for (int u = 0; u < 16; ++u) s += v[u];
-      }
-    }
-    rows[rr * (LP + 1) + n] = s;
+      for (int u = 0; u < PER; ++u) v[q][u] = ok[u] ? part[(p + q) * stride + off[u]] : 0.f;
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int u = 0; u < PER; ++u) acc[u] += v[q][u];
+  }
+  for (; p < S; ++p)
+#pragma unroll
+    for (int u = 0; u < PER; ++u) acc[u] += ok[u] ? part[p * stride + off[u]] : 0.f;
+#pragma unroll
+  for (int u = 0; u < PER; ++u) {
+    const int idx = threadIdx.x + 256 * u;
+    if (idx < kGramRows * LP) rows[(idx / LP) * (LP + 1) + idx % LP] = acc[u];
   }
   if (X) {
     __syncthreads();
@@ -860,18 +889,30 @@ SvdPlan make_svd_plan(int64_t d, int64_t k, int r, int oversample, bool exact) {
   p.l = l;
   p.nt = static_cast<int>(cdiv(l, 16));
   const int LP = 16 * p.nt;
-  const int64_t target = 512;   // workgroups per product (256 CUs, two each)
-  // Split of the contraction: enough workgroups to fill the chip, split-K
-  // partials kept under ~8% of E's bytes (S * LP / len), each split at least
-  // one unit of the kernel's K granularity.
+  // Split of the contraction (split-K count S): among the counts that keep the
+  // split-K partials under ~8% of E's bytes (S * LP / len) and give every split
+  // at least one unit of the kernel's K granularity, the smallest S whose grid
+  // best fills the 256 CUs of the chip -- score = (occupancy of the last wave
+  // of workgroups) x min(1, workgroups / 512).
+  constexpr int64_t kCUs = 256;
   auto choose = [&](int64_t tiles, int64_t len, int unit, int64_t& per) {
-    int64_t sp = cdiv(target, tiles);
     int64_t cap = (len * 8) / (100 * LP);
     if (cap < 1) cap = 1;
-    if (sp > cap) sp = cap;
-    if (sp > cdiv(len, unit)) sp = cdiv(len, unit);
-    if (sp < 1) sp = 1;
-    per = round_up(cdiv(len, sp), unit);
+    if (cap > cdiv(len, unit)) cap = cdiv(len, unit);
+    int64_t best_s = 1;
+    double best = -1.0;
+    for (int64_t sp = 1; sp <= cap; ++sp) {
+      const int64_t ps = round_up(cdiv(len, sp), unit);
+      if (cdiv(len, ps) != sp) continue;   // rounding merges this count into another
+      const int64_t wgs = tiles * sp;
+      const double fill = static_cast<double>(wgs) / static_cast<double>(kCUs * cdiv(wgs, kCUs));
+      const double busy = wgs >= 2 * kCUs ? 1.0 : static_cast<double>(wgs) / static_cast<double>(2 * kCUs);
+      if (fill * busy > best + 1e-9) {
+        best = fill * busy;
+        best_s = sp;
+      }
+    }
+    per = round_up(cdiv(len, best_s), unit);
     return static_cast<int>(cdiv(len, per));
   };
   const GemmShape nn = gemm_shape(false, p.nt), tn = gemm_shape(true, p.nt);
@@ -960,7 +1001,7 @@ hipError_t run_lowrank(const float* E, const SvdPlan& pl, int q, const float* om
       launch_reduce(pl.nt, part, pl.nn_splits, d, pl.d_pad, l, nullptr, Y, mode ? gparts : nullptr, s);
     if (mode == 0) return;
     const int P = transposed ? pl.gram_parts_k : pl.gram_parts_d;
-    LQ_LAUNCH("gram_sum", gram_sum_kernel, dim3((E_ + 63) / 64), dim3(256), 0, s, gparts, P, E_, gtotal);
+    LQ_LAUNCH("gram_sum", gram_sum_kernel, dim3((E_ + 63) / 64), dim3(1024), 0, s, gparts, P, E_, gtotal);
     if (l <= 32)
       launch_small_wave(mode, gtotal, l, Xinv, r, SB, SA, sigma, stats, mode == 2 ? obj : none, s);
     else
