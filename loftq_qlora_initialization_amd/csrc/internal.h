@@ -1,6 +1,7 @@
 // Internal declarations shared by the libloftq translation units.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -8,25 +9,30 @@
 
 namespace loftq {
 
-// Brackets one kernel launch with HIP events on its stream while kernel timing
-// is enabled (loftq_profile_enable); a no-op otherwise.
+// While kernel timing is enabled (loftq_profile_enable), supplies a start/stop
+// event pair that the launch itself records around the kernel's execution
+// (hipExtLaunchKernel), and files it under the kernel's name; otherwise both
+// events are null and the launch is a plain one.
 class ProfScope {
  public:
-  ProfScope(const char* name, hipStream_t s);
+  explicit ProfScope(const char* name);
   ~ProfScope();
   ProfScope(const ProfScope&) = delete;
   ProfScope& operator=(const ProfScope&) = delete;
+  hipEvent_t start() const { return start_; }
+  hipEvent_t stop() const { return stop_; }
 
  private:
   const char* name_;
-  hipStream_t stream_;
   hipEvent_t start_;
+  hipEvent_t stop_;
 };
 
-#define LQ_LAUNCH(NAME, KERNEL, GRID, BLOCK, SHMEM, STREAM, ...)              \
-  do {                                                                      \
-    ::loftq::ProfScope lq_prof_scope_(NAME, STREAM);                        \
-    hipLaunchKernelGGL(KERNEL, GRID, BLOCK, SHMEM, STREAM, __VA_ARGS__);     \
+#define LQ_LAUNCH(NAME, KERNEL, GRID, BLOCK, SHMEM, STREAM, ...)                                             \
+  do {                                                                                                     \
+    ::loftq::ProfScope lq_prof_scope_(NAME);                                                               \
+    hipExtLaunchKernelGGL(KERNEL, GRID, BLOCK, SHMEM, STREAM, lq_prof_scope_.start(), lq_prof_scope_.stop(), \
+                          0, __VA_ARGS__);                                                                 \
   } while (0)
 
 // NF4 tables handed to kernels by value (kernel arguments), built once on the

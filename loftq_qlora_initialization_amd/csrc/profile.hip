@@ -1,6 +1,7 @@
 // Per-kernel launch timing: while enabled, every kernel the library enqueues is
-// bracketed by a pair of HIP events recorded on the launch's own stream.
-// Collection synchronises those events and sums the elapsed time per kernel.
+// launched with a start/stop HIP event pair that the launch records around the
+// kernel's own execution on its stream.  Collection synchronises those events
+// and sums the elapsed time per kernel.
 #include <atomic>
 #include <cstring>
 #include <map>
@@ -24,22 +25,22 @@ std::vector<Rec> g_recs;
 
 }  // namespace
 
-ProfScope::ProfScope(const char* name, hipStream_t s) : name_(name), stream_(s), start_(nullptr) {
+ProfScope::ProfScope(const char* name) : name_(name), start_(nullptr), stop_(nullptr) {
   if (!g_enabled.load(std::memory_order_relaxed)) return;
-  if (hipEventCreate(&start_) != hipSuccess) { start_ = nullptr; return; }
-  if (hipEventRecord(start_, s) != hipSuccess) { (void)hipEventDestroy(start_); start_ = nullptr; }
+  if (hipEventCreate(&start_) != hipSuccess) {
+    start_ = nullptr;
+    return;
+  }
+  if (hipEventCreate(&stop_) != hipSuccess) {
+    (void)hipEventDestroy(start_);
+    start_ = stop_ = nullptr;
+  }
 }
 
 ProfScope::~ProfScope() {
   if (!start_) return;
-  hipEvent_t stop = nullptr;
-  if (hipEventCreate(&stop) != hipSuccess || hipEventRecord(stop, stream_) != hipSuccess) {
-    if (stop) (void)hipEventDestroy(stop);
-    (void)hipEventDestroy(start_);
-    return;
-  }
   std::lock_guard<std::mutex> lk(g_mu);
-  g_recs.push_back(Rec{name_, start_, stop});
+  g_recs.push_back(Rec{name_, start_, stop_});
 }
 
 }  // namespace loftq
