@@ -47,6 +47,7 @@ struct Nf4Tables {
   float level[16];      // ascending NF4 levels, fp32
   float thr[15];        // thr[j]: for fp32 x, x > thr[j]  <=>  x > (level[j]+level[j+1])/2
   float cell_thr[33];
+  float cell_thr16[33]; // fl32(16 cell_thr + 16) (+inf where cell_thr is +inf)
   int32_t cell_base[33];
   int32_t valid;        // 1 if every grid invariant held at construction
 };
@@ -57,6 +58,11 @@ const Nf4Tables& nf4_tables();
 // may disagree with fl32(R / a) about a threshold; such elements are redone with
 // an IEEE division.  |x' - fl32(R/a)| <= 3 * 2^-24 for |x| <= 1.
 constexpr float kDangerWindow = 9.5367431640625e-07f;  // 2^-20
+// The same window for the encoder's y = fma(R, 16 rcp(a), 16) against the
+// cell thresholds fl32(16 thr + 16): |y - (16 fl32(R/a) + 16)| <= 2^-18 (rcp
+// within 1 ulp, one rounding of the product-sum, 16 x the quotient's rounding)
+// and |thr16 - (16 thr + 16)| <= 2^-19, both well inside 2^-16.
+constexpr float kDangerWindow16 = 1.52587890625e-05f;  // 2^-16
 
 // ---- launchers (quant_kernels.hip) ----
 hipError_t launch_nf4_quantize(const void* W, loftq_dtype_t wdt, int64_t rows, int64_t cols,

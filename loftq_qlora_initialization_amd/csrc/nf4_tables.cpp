@@ -90,6 +90,10 @@ Nf4Tables build() {
     if (inside > 1) ok = false;
     t.cell_base[g] = below;
   }
+  // The encoder compares y = 16 x + 16 (computed in fp32) with fl32(16 thr + 16).
+  for (int g = 0; g < 33; ++g)
+    t.cell_thr16[g] = std::isinf(t.cell_thr[g]) ? t.cell_thr[g]
+                                                : static_cast<float>(16.0 * static_cast<double>(t.cell_thr[g]) + 16.0);
   // Threshold ordering sanity (levels strictly increasing).
   for (int j = 0; j + 1 < 15; ++j)
     if (!(thr[j] < thr[j + 1])) ok = false;

@@ -7,11 +7,12 @@
 // is two 16-byte loads for bf16 (four for fp32) and one 8-byte store of packed
 // nibbles, so every wave moves contiguous 2 KB (bf16) in and 512 B out.
 //
-// Encoding: x' = R * (1/a) (one multiply), cell g = int(16 x' + 16) of a 33-cell
-// grid held in LDS, code = base[g] + (x' > thr[g]).  x' can differ from the
-// defined fl32(R / a) by at most 3 * 2^-24, so whenever x' lies within 2^-20 of
-// the cell's threshold the element is redone with an IEEE division and a full
-// threshold count.  Codes are therefore bit-identical to fl32(R / a) rounding.
+// Encoding: y = fma(R, 16 rcp(a), 16), cell g = int(y) of a 33-cell grid held
+// in LDS, code = base[g] + (y > thr16[g]) with thr16 = fl32(16 thr + 16).  y can
+// differ from 16 fl32(R / a) + 16 by far less than the 2^-16 window, so any
+// element whose y lies within the window of its cell's threshold is redone
+// with an IEEE division and a full threshold count.  Codes are therefore
+// bit-identical to fl32(R / a) rounding.
 #include <float.h>
 
 #include "internal.h"
@@ -56,14 +57,14 @@ __device__ __forceinline__ float load1(const uint16_t* p, int64_t i) {
 __device__ __forceinline__ float load1(const float* p, int64_t i) { return p[i]; }
 
 struct EncodeLds {
-  float2 cell[33];  // (threshold, base code as int bits)
+  float2 cell[33];  // (fl32(16 threshold + 16), base code as int bits); +inf where the cell has none
   float thr[15];
   float level[16];
 };
 
 __device__ __forceinline__ void fill_lds(EncodeLds& s, const Nf4Tables& t) {
   const int tid = threadIdx.x;
-  if (tid < 33) s.cell[tid] = make_float2(t.cell_thr[tid], __int_as_float(t.cell_base[tid]));
+  if (tid < 33) s.cell[tid] = make_float2(t.cell_thr16[tid], __int_as_float(t.cell_base[tid]));
   if (tid < 15) s.thr[tid] = t.thr[tid];
   if (tid < 16) s.level[tid] = t.level[tid];
 }
@@ -80,17 +81,25 @@ __device__ __forceinline__ uint32_t exact_code(float r, float a, const EncodeLds
 __device__ __forceinline__ int nib_shift(int e) { return 8 * ((e >> 1) & 3) + ((e & 1) ? 0 : 4); }
 
 // Encode 16 residual values sharing absmax a into two packed 32-bit words.
+// y = 16 x + 16 is formed straight from the value, y = fma(v, 16 rcp(a), 16), and
+// lands in cell int(y) of the grid (unsigned conversion saturates below 0, and
+// x <= 1 + 2^-22 keeps y below 33); the cell stores (fl32(16 thr + 16), base)
+// and code = base + (y > thr16).  y differs from 16 fl32(v / a) + 16 by less
+// than 2^-18 and thr16 from 16 thr + 16 by at most 2^-19, so outside the
+// window |y - thr16| < 2^-16 the comparison decides exactly as fl32(v / a) >
+// thr; elements inside it (and every element of a subnormal-absmax block) are
+// redone with an IEEE division and a full threshold count.
 __device__ __forceinline__ uint2 encode16(const float v[16], float a, const EncodeLds& s) {
-  const float inv = (a > 0.f) ? 1.0f / a : 0.f;
+  const float inv16 = (a > 0.f) ? 16.f * __builtin_amdgcn_rcpf(a) : 0.f;
   uint32_t danger = (a > 0.f && a < FLT_MIN) ? 0xFFFFu : 0u;
   uint32_t w0 = 0, w1 = 0;
 #pragma unroll
   for (int e = 0; e < 16; ++e) {
-    const float x = v[e] * inv;
-    const float gf = __builtin_amdgcn_fmed3f(fmaf(x, 16.f, 16.f), 0.f, 32.f);
-    const float2 c = s.cell[static_cast<int>(gf)];
-    const uint32_t code = static_cast<uint32_t>(__float_as_int(c.y)) + ((x > c.x) ? 1u : 0u);
-    if (fabsf(x - c.x) < kDangerWindow) danger |= 1u << e;
+    const float y = fmaf(v[e], inv16, 16.f);
+    const float2 c = s.cell[static_cast<uint32_t>(y)];
+    const float d = y - c.x;
+    const uint32_t code = static_cast<uint32_t>(__float_as_int(c.y)) + ((d > 0.f) ? 1u : 0u);
+    if (fabsf(d) < kDangerWindow16) danger |= 1u << e;
     if (e < 8) w0 |= code << nib_shift(e);
     else w1 |= code << nib_shift(e);
   }
@@ -122,7 +131,7 @@ __global__ __launch_bounds__(kThreads) void quantize_plain_kernel(const T* __res
   for (int64_t g = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x; g < ngroups; g += stride) {
     float v[16];
     load16(W + g * 16, v);
-    float m = 0.f;
+    float m = 0.f;  // (one group per thread at the launch size below)
 #pragma unroll
     for (int e = 0; e < 16; ++e) m = fmaxf(m, fabsf(v[e]));
     const float a = quad_max(m);
@@ -183,91 +192,160 @@ __global__ __launch_bounds__(kThreads) void quantize_generic_kernel(const T* __r
   }
 }
 
-// Fused residual R = W - B A on a 32-row x 256-column tile (cols % 64 == 0).
-// Thread t owns column group t % 16 of rows 2 (t / 16) and 2 (t / 16) + 1, so a
-// DPP quad holds four consecutive column groups of the same rows = one block
-// per row.  B and A are staged through LDS in rank chunks of 16.
-constexpr int kTileRows = 32, kTileCols = 256, kRankChunk = 16;
-
 template <typename T>
-__global__ __launch_bounds__(kThreads) void quantize_fused_kernel(const T* __restrict__ W, int64_t rows,
-                                                                  int64_t cols, const float* __restrict__ B,
-                                                                  const float* __restrict__ A, int r,
-                                                                  uint8_t* __restrict__ packed,
-                                                                  float* __restrict__ absmax, Nf4Tables tab) {
-  __shared__ EncodeLds s;
-  __shared__ float As[kRankChunk][kTileCols];
-  __shared__ float Bs[kTileRows][kRankChunk + 1];
-  fill_lds(s, tab);
-  const int tid = threadIdx.x;
-  const int cg = tid & 15, rq = tid >> 4;
-  const int64_t tiles_c = cols / kTileCols + ((cols % kTileCols) ? 1 : 0);
-  const int64_t tile_r = blockIdx.x / tiles_c, tile_c = blockIdx.x % tiles_c;
-  const int64_t row0 = tile_r * kTileRows + 2 * rq;
-  const int64_t col0 = tile_c * kTileCols + cg * 16;
-  const bool col_ok = col0 < cols;          // cols % 64 == 0 => whole quads agree
-  float acc[2][16];
+__device__ __forceinline__ void load16_raw(const T* __restrict__ p, uint4 (&raw)[4]) {
+  if (sizeof(T) == 2) {
+    raw[0] = reinterpret_cast<const uint4*>(p)[0];
+    raw[1] = reinterpret_cast<const uint4*>(p)[1];
+  } else {
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < 4; ++i) raw[i] = reinterpret_cast<const uint4*>(p)[i];
+  }
+}
+template <typename T>
+__device__ __forceinline__ void raw_to_f32(const uint4 (&raw)[4], float v[16]) {
+  if (sizeof(T) == 2) {
+    const uint32_t w[8] = {raw[0].x, raw[0].y, raw[0].z, raw[0].w, raw[1].x, raw[1].y, raw[1].z, raw[1].w};
 #pragma unroll
-    for (int e = 0; e < 16; ++e) acc[i][e] = 0.f;
-
-  for (int p0 = 0; p0 < r; p0 += kRankChunk) {
-    const int pc = min(kRankChunk, r - p0);
-    __syncthreads();
-    for (int idx = tid; idx < kRankChunk * kTileCols; idx += kThreads) {
-      const int p = idx / kTileCols, c = idx % kTileCols;
-      const int64_t gc = tile_c * kTileCols + c;
-      As[p][c] = (p < pc && gc < cols) ? A[static_cast<int64_t>(p0 + p) * cols + gc] : 0.f;
+    for (int i = 0; i < 8; ++i) {
+      v[2 * i] = __uint_as_float(w[i] << 16);
+      v[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
     }
-    for (int idx = tid; idx < kTileRows * kRankChunk; idx += kThreads) {
-      const int rr = idx / kRankChunk, p = idx % kRankChunk;
-      const int64_t gr = tile_r * kTileRows + rr;
-      Bs[rr][p] = (p < pc && gr < rows) ? B[gr * r + p0 + p] : 0.f;
-    }
-    __syncthreads();
-    for (int p = 0; p < pc; ++p) {
-      const float b0 = Bs[2 * rq][p], b1 = Bs[2 * rq + 1][p];
-      const float4* ap = reinterpret_cast<const float4*>(&As[p][cg * 16]);
+  } else {
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const float4 av = ap[q];
-        acc[0][4 * q] = fmaf(b0, av.x, acc[0][4 * q]);
-        acc[0][4 * q + 1] = fmaf(b0, av.y, acc[0][4 * q + 1]);
-        acc[0][4 * q + 2] = fmaf(b0, av.z, acc[0][4 * q + 2]);
-        acc[0][4 * q + 3] = fmaf(b0, av.w, acc[0][4 * q + 3]);
-        acc[1][4 * q] = fmaf(b1, av.x, acc[1][4 * q]);
-        acc[1][4 * q + 1] = fmaf(b1, av.y, acc[1][4 * q + 1]);
-        acc[1][4 * q + 2] = fmaf(b1, av.z, acc[1][4 * q + 2]);
-        acc[1][4 * q + 3] = fmaf(b1, av.w, acc[1][4 * q + 3]);
-      }
+    for (int i = 0; i < 4; ++i) {
+      v[4 * i] = __uint_as_float(raw[i].x);
+      v[4 * i + 1] = __uint_as_float(raw[i].y);
+      v[4 * i + 2] = __uint_as_float(raw[i].z);
+      v[4 * i + 3] = __uint_as_float(raw[i].w);
     }
   }
-  if (r == 0) __syncthreads();
+}
 
+// Fused residual R = W - B A (cols % 64 == 0, r <= 64), workgroup of 4 waves on
+// a strip of SW = 64 NBS columns, walking nrb batches of BR = 16 RB rows
+// (NBS RB = 4).
+//
+// Phase 1 (matrix cores): wave w multiplies the 16-row group w / NBS of the
+// batch by 64-column block w % NBS on fp32 MFMA (v_mfma_f32_16x16x4_f32: lane L
+// supplies A[L%16][L/16] and B[L/16][L%16] and receives D[4(L/16)+v][L%16]),
+// with M = 16 columns (tile t of the block holds columns 16 t .. 16 t + 15),
+// N = 16 rows, K = 4 rank indices; rank index p = KK k + kk for K-step kk and
+// K slot k, so a lane's B operands are KK consecutive entries of its row.  The
+// strip's A sits in LDS in operand order (one float4 per lane and K-step: the
+// four tiles).  B A goes to an LDS tile, row-major.
+// Phase 2 (encode): thread q takes 16-element group q of the batch tile (row
+// q / (SW / 16)), so a wave reads W in runs of SW contiguous columns and a DPP
+// quad holds one 64-element block, exactly as in the plain kernel.  W of the
+// group is loaded before phase 1.
+constexpr int kFusedThreads = 256, kFusedMaxR = 64;
+
+template <int R16>
+struct FusedCfg {
+  static constexpr int NBS = R16 <= 16 ? 4 : 2;                     // 64-column blocks per strip
+  static constexpr int RB = 4 / NBS;                                 // 16-row groups per batch
+  static constexpr int SW = 64 * NBS;                                // strip width (A in LDS: SW x R16 fp32 <= 32 KB)
+  static constexpr int BR = 16 * RB;                                 // rows per batch (BA tile BR x SW fp32)
+  static constexpr int KK = R16 / 4;                                 // MFMA K-steps
+  static constexpr int LDT = SW + 4;                                 // BA tile row stride (floats)
+};
+
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+
+template <typename T, int R16>
+__global__ __launch_bounds__(kFusedThreads) void quantize_fused_kernel(const T* __restrict__ W, int64_t rows,
+                                                                       int64_t cols, const float* __restrict__ B,
+                                                                       const float* __restrict__ A, int r, int nrb,
+                                                                       uint8_t* __restrict__ packed,
+                                                                       float* __restrict__ absmax, Nf4Tables tab) {
+  using C = FusedCfg<R16>;
+  constexpr int NBS = C::NBS, SW = C::SW, BR = C::BR, KK = C::KK, LDT = C::LDT;
+  __shared__ EncodeLds s;
+  __shared__ float4 As[NBS * KK * 64];    // [blk][kk][lane] -> tiles 0..3
+  __shared__ float BAs[BR * LDT];
+  fill_lds(s, tab);
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, li = lane & 15, g = lane >> 4;
+  const int64_t nstrips = cols / SW + ((cols % SW) ? 1 : 0);
+  const int64_t strip = blockIdx.x % nstrips, chunk = blockIdx.x / nstrips;
+  const int64_t col0 = strip * SW;
+  const int strip_cols = static_cast<int>((cols - col0) < SW ? (cols - col0) : SW);
+  // operand slot (blk, kk, lane = 16 k + j) holds A[KK k + kk][col0 + 64 blk + 16 t + j] for tiles t = 0..3
+  for (int slot = tid; slot < NBS * KK * 64; slot += kFusedThreads) {
+    const int blk = slot / (KK * 64), rem = slot - blk * (KK * 64);
+    const int kk = rem >> 6, k = (rem >> 4) & 3, j = rem & 15;
+    const int p = KK * k + kk, c = 64 * blk + j;
+    float val[4];
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int64_t row = row0 + i;
-    const bool ok = col_ok && row < rows;
-    float v[16];
-    float m = 0.f;
-    if (ok) {
-      load16(W + row * cols + col0, v);
+    for (int t = 0; t < 4; ++t)
+      val[t] = (p < r && c + 16 * t < strip_cols) ? A[static_cast<int64_t>(p) * cols + col0 + c + 16 * t] : 0.f;
+    As[slot] = make_float4(val[0], val[1], val[2], val[3]);
+  }
+  const int bw = wave % NBS, rgw = wave / NBS;   // phase-1 block and row group of this wave
+  const bool blk_ok = 64 * bw < strip_cols;
+  constexpr int GPR = SW / 16;                   // phase-2 groups per tile row
+  const int qrow = tid / GPR, qc = 16 * (tid - qrow * GPR);
+  const bool q_ok = qc < strip_cols;
+  for (int rb = 0; rb < nrb; ++rb) {
+    const int64_t row0 = (chunk * nrb + rb) * BR;
+    if (row0 >= rows) break;
+    // W of this thread's phase-2 group (row clamped; rows past the end are not stored)
+    uint4 wraw[4];
+    {
+      int64_t row = row0 + qrow;
+      row = row < rows ? row : rows - 1;
+      load16_raw(W + row * cols + col0 + (q_ok ? qc : 0), wraw);
+    }
+    // B operands: lane (li, g) of row group rgw, K slot g: B[row][KK g .. KK g + KK - 1]
+    float bop[KK];
+    {
+      const int64_t row = row0 + 16 * rgw + li;
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        v[e] = v[e] - acc[i][e];
-        m = fmaxf(m, fabsf(v[e]));
+      for (int kk = 0; kk < KK; ++kk) {
+        const int pidx = KK * g + kk;
+        bop[kk] = (row < rows && pidx < r) ? B[row * r + pidx] : 0.f;
       }
-    } else {
+    }
+    __syncthreads();   // A staged (first batch) / previous batch's tile consumed
+    if (blk_ok) {
+      floatx4 acc[4];
 #pragma unroll
-      for (int e = 0; e < 16; ++e) v[e] = 0.f;
+      for (int t = 0; t < 4; ++t) acc[t] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) {
+        const float4 a4 = As[(bw * KK + kk) * 64 + lane];
+        acc[0] = __builtin_amdgcn_mfma_f32_16x16x4f32(a4.x, bop[kk], acc[0], 0, 0, 0);
+        acc[1] = __builtin_amdgcn_mfma_f32_16x16x4f32(a4.y, bop[kk], acc[1], 0, 0, 0);
+        acc[2] = __builtin_amdgcn_mfma_f32_16x16x4f32(a4.z, bop[kk], acc[2], 0, 0, 0);
+        acc[3] = __builtin_amdgcn_mfma_f32_16x16x4f32(a4.w, bop[kk], acc[3], 0, 0, 0);
+      }
+      // lane (li, g), tile t, component v: row 16 rgw + li, column 64 bw + 16 t + 4 g + v
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+        *reinterpret_cast<float4*>(&BAs[(16 * rgw + li) * LDT + 64 * bw + 16 * t + 4 * g]) =
+            make_float4(acc[t][0], acc[t][1], acc[t][2], acc[t][3]);
+    }
+    __syncthreads();
+    float v[16];
+    raw_to_f32<T>(wraw, v);
+    const float4* bp = reinterpret_cast<const float4*>(&BAs[qrow * LDT + qc]);
+    float m = 0.f;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float4 ba = bp[q];
+      v[4 * q] = v[4 * q] - ba.x;
+      v[4 * q + 1] = v[4 * q + 1] - ba.y;
+      v[4 * q + 2] = v[4 * q + 2] - ba.z;
+      v[4 * q + 3] = v[4 * q + 3] - ba.w;
+#pragma unroll
+      for (int e = 4 * q; e < 4 * q + 4; ++e) m = fmaxf(m, fabsf(v[e]));
     }
     const float a = quad_max(m);
-    if (ok) {
-      const uint2 w = encode16(v, a, s);
-      const int64_t g = (row * cols + col0) >> 4;
-      reinterpret_cast<uint2*>(packed)[g] = w;
-      if ((tid & 3) == 0) absmax[g >> 2] = a;
+    const uint2 w = encode16(v, a, s);
+    const int64_t row = row0 + qrow;
+    if (q_ok && row < rows) {
+      const int64_t e0 = row * cols + col0 + qc;
+      reinterpret_cast<uint2*>(packed)[e0 >> 4] = w;
+      if ((tid & 3) == 0) absmax[e0 >> 6] = a;
     }
   }
 }
@@ -411,7 +489,7 @@ hipError_t quantize_typed(const T* W, int64_t rows, int64_t cols, const float* B
   if (B == nullptr) {
     const int64_t full = n / 64;
     if (full > 0) {
-      LQ_LAUNCH("nf4_quantize", quantize_plain_kernel<T>, dim3(grid_for_groups(full * 4, 2)), dim3(kThreads), 0, s, W,
+      LQ_LAUNCH("nf4_quantize", quantize_plain_kernel<T>, dim3(grid_for_groups(full * 4, 1)), dim3(kThreads), 0, s, W,
                          full * 4, packed, absmax, tab);
     }
     if (full < nblocks) {
@@ -419,10 +497,27 @@ hipError_t quantize_typed(const T* W, int64_t rows, int64_t cols, const float* B
                          static_cast<const float*>(nullptr), static_cast<const float*>(nullptr), 0, full, nblocks,
                          packed, absmax, tab);
     }
-  } else if (cols % 64 == 0) {
-    const int64_t tiles = ((rows + kTileRows - 1) / kTileRows) * ((cols + kTileCols - 1) / kTileCols);
-    LQ_LAUNCH("nf4_quantize_fused", quantize_fused_kernel<T>, dim3(static_cast<unsigned>(tiles)), dim3(kThreads), 0, s, W, rows,
-                       cols, B, A, r, packed, absmax, tab);
+  } else if (cols % 64 == 0 && r <= kFusedMaxR) {
+    const int r16 = (r + 15) / 16 * 16;
+    const int sw = r16 <= 16 ? 256 : 128;
+    const int br = 16 * (4 / (sw / 64));
+    const int64_t nstrips = (cols + sw - 1) / sw;
+    const int64_t batches = (rows + br - 1) / br;
+    // about four workgroups per CU over the strips; each walks nrb row batches
+    int64_t chunks = (1024 + nstrips - 1) / nstrips;
+    if (chunks > batches) chunks = batches;
+    if (chunks < 1) chunks = 1;
+    const int nrb = static_cast<int>((batches + chunks - 1) / chunks);
+    chunks = (batches + nrb - 1) / nrb;
+    const dim3 grid(static_cast<unsigned>(nstrips * chunks));
+#define LQ_FUSED(R16)                                                                                              \
+  LQ_LAUNCH("nf4_quantize_fused", (quantize_fused_kernel<T, R16>), grid, dim3(kFusedThreads), 0, s, W, rows, cols, B, \
+            A, r, nrb, packed, absmax, tab)
+    if (r16 == 16) LQ_FUSED(16);
+    else if (r16 == 32) LQ_FUSED(32);
+    else if (r16 == 48) LQ_FUSED(48);
+    else LQ_FUSED(64);
+#undef LQ_FUSED
   } else {
     int64_t grid = (nblocks + (kThreads / 4) - 1) / (kThreads / 4);
     if (grid > 65536) grid = 65536;
