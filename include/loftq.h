@@ -109,7 +109,7 @@ loftq_status_t loftq_nf4_dequantize(const uint8_t* packed, const float* absmax, 
  * r largest singular triplets, Delta = U_r S_r V_r^T).  exact = 1: the SVD of E
  * itself (one-sided Jacobi, min(rows, cols) <= 512).  exact = 0: randomized
  * subspace iteration with sketch width l = r + oversample (l <= min(rows, cols),
- * l <= 96, r <= 64) and power_iters rounds; the sketch is `omega` (cols x l fp32) or, if
+ * l <= 80, r <= 64) and power_iters rounds; the sketch is `omega` (cols x l fp32) or, if
  * NULL, the +-1 SplitMix64 sketch of (seed, t).  Outputs B = U_r S_r^{1/2},
  * A = S_r^{1/2} V_r^T, sigma = S_r (descending).
  *   E      [device] rows x cols fp32
