@@ -1,0 +1,193 @@
+"""GPU parity at the full workload sizes, through the same call the benchmark times
+(one loftq_init per matrix with caller-owned InitBuffers).
+
+4096x4096 (r=16, T=5): the oracle runs the whole matrix, free-running (objective
+per alternation within 1e-3 relative) and teacher-forced per alternation (codes
+mismatch <= 1e-4, bit-exact at t=1; sigma within 1e-4).
+
+11008x4096 (r=64), 8192x28672 (r=64) and two module shapes of the 32-layer
+decoder (gate 11008x4096 and down 4096x11008, r=16): the oracle checks sampled
+outputs one by one and the low-rank step on the device's own residual:
+  * sampled 256-block groups of the last alternation's residual
+    W - B_{T-1} A_{T-1} (B_{T-1}, A_{T-1} from a T-1 run, which is the same
+    computation's prefix): NF4 codes (mismatch <= 1e-4), absmax (rtol 1e-6) and the
+    8-bit double quant of the device's absmax (bit-exact);
+  * the last alternation's SVD teacher-forced: the oracle's randomized SVD of
+    E_T = W - deq(Q_T) built from the device's codes, with the same sketch, gives
+    sigma within 1e-4 relative; the device factors satisfy B^T B = A A^T = diag(sigma);
+  * the final objective recomputed in fp64 from the device outputs, within 1e-4.
+At t=1 the whole chain is also checked on sampled groups bit for bit (Q_1 = NF4(W))."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from loftq_qlora_initialization_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+SIGMA_RTOL = 1e-4
+GROUP = 64 * 256          # elements per double-quant group
+N_SAMPLED_GROUPS = 48
+
+
+def dev_w(bits, w):
+    if w.dtype == "bf16":
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).cuda().view(torch.bfloat16)
+    return torch.from_numpy(np.ascontiguousarray(bits, dtype=np.float32)).cuda()
+
+
+def host(t):
+    torch.cuda.synchronize()
+    return t.cpu().numpy()
+
+
+def cfg_of(lib, w, T=None):
+    return lib.default_config(iterative_steps=w.iterative_steps if T is None else T, rank=w.rank,
+                              oversample=w.oversample, power_iters=w.power_iters, double_quant=int(w.double_quant),
+                              exact_svd=int(w.exact_svd), seed=w.sketch_seed)
+
+
+def run_init(lib, w, Wd, T=None):
+    cfg = cfg_of(lib, w, T)
+    bufs = lib.InitBuffers(w.rows, w.cols, cfg)
+    lib.loftq_init(Wd, cfg, buffers=bufs)
+    return {k: host(getattr(bufs, k)) for k in ("packed", "absmax", "qabsmax", "dq_scale", "B", "A", "sigma",
+                                                 "objective")}
+
+
+def sampled_groups(n, seed):
+    ng = -(-n // GROUP)
+    rng = np.random.default_rng(seed)
+    pick = rng.choice(ng, size=min(N_SAMPLED_GROUPS - 2, ng), replace=False)
+    return np.unique(np.concatenate([pick, [0, ng - 1]]))
+
+
+def group_residual(W, cols, g, n, B=None, A=None):
+    """The fp32 residual of double-quant group g (its element range of the row-major matrix)."""
+    lo, hi = g * GROUP, min((g + 1) * GROUP, n)
+    r0, r1 = lo // cols, (hi - 1) // cols + 1
+    rows = W[r0:r1]
+    if B is not None:
+        rows = (rows.astype(np.float64) - B[r0:r1].astype(np.float64) @ A.astype(np.float64)).astype(np.float32)
+    return rows.ravel()[lo - r0 * cols: hi - r0 * cols]
+
+
+def check_groups(out, W, w, groups, B=None, A=None, exact=False):
+    n = w.numel
+    mism = total = 0
+    for g in groups:
+        R = group_residual(W, w.cols, g, n, B, A)
+        codes, am = oracle.quantize_residual(R)
+        lo = g * GROUP
+        dcodes = oracle.unpack_nibbles(out["packed"][lo // 2: lo // 2 + (R.size + 1) // 2], R.size)[:R.size]
+        b0, nbk = lo // 64, am.size
+        dam = out["absmax"][b0:b0 + nbk]
+        if exact:
+            assert np.array_equal(dcodes, codes), g
+            assert np.array_equal(dam, am), g
+        else:
+            mism += int(np.sum(dcodes != codes))
+            assert np.allclose(dam, am, rtol=1e-6, atol=0), g
+        total += R.size
+        # the 8-bit double quant, teacher-forced on the device's own absmax of this group
+        qa, s = oracle.double_quant(dam)
+        assert np.array_equal(out["qabsmax"][b0:b0 + nbk], qa), g
+        assert out["dq_scale"][g] == np.float32(s[0]), g
+    assert mism <= 1e-4 * total, (mism, total)
+
+
+def check_last_svd(lib, out, W, w):
+    """sigma_T against the oracle's randomized SVD of the device's own E_T, same sketch."""
+    d, k = W.shape
+    codes = oracle.unpack_nibbles(out["packed"], d * k)
+    scale = oracle.dq_scales_expand(out["qabsmax"], out["dq_scale"])
+    E = oracle.dequantize(codes, scale, W=W.ravel()).reshape(d, k)
+    del codes
+    om = oracle.rademacher_sketch(w.sketch_seed, w.iterative_steps, k, w.rank + w.oversample)
+    _, s_ref, _ = oracle.randomized_svd(E, w.rank, om, w.power_iters)
+    del E
+    s = out["sigma"].astype(np.float64)
+    rel = float(np.max(np.abs(s - s_ref) / s_ref))
+    assert rel <= SIGMA_RTOL, rel
+    B64, A64 = out["B"].astype(np.float64), out["A"].astype(np.float64)
+    assert np.allclose(B64.T @ B64, np.diag(s), atol=2e-5 * s[0])
+    assert np.allclose(A64 @ A64.T, np.diag(s), atol=2e-5 * s[0])
+    direct = oracle.objective(W, oracle.unpack_nibbles(out["packed"], d * k), scale, out["B"], out["A"])
+    assert abs(direct - out["objective"][-1]) <= 1e-4 * direct, (direct, out["objective"][-1])
+
+
+def _big_cases():
+    specs = synth.c4_matrix_specs()
+    return [pytest.param(synth.workload("c3"), id="c3_11008x4096_r64"),
+            pytest.param(synth.workload("c5"), id="c5_8192x28672_r64"),
+            pytest.param(specs[4], id="c4_gate_11008x4096_r16"),
+            pytest.param(specs[6], id="c4_down_4096x11008_r16")]
+
+
+@pytest.mark.timeout(600)
+def test_c2_full_free_running(lib):
+    w = synth.workload("c2")
+    bits, W = synth.make_weight(w)
+    out = run_init(lib, w, dev_w(bits, w))
+    ref = oracle.loftq_init(W, rank=w.rank, iterative_steps=w.iterative_steps, double_quant_on=w.double_quant,
+                            exact=w.exact_svd, oversample=w.oversample, power_iters=w.power_iters,
+                            seed=w.sketch_seed)
+    obj = out["objective"]
+    # Q_1 = NF4(W) is bit-exact; the device sums the fp32-rounded residual, so the norm may differ
+    # by at most 2^-24 relative (plus fp64 summation order)
+    assert abs(obj[0] - ref["objective"][0]) <= 1e-7 * ref["objective"][0]
+    assert np.allclose(obj, ref["objective"], rtol=1e-3, atol=0), (obj, ref["objective"])
+    assert np.all(np.diff(obj) < 0)
+    check_last_svd(lib, out, W, w)
+
+
+@pytest.mark.timeout(600)
+def test_c2_full_teacher_forced(lib):
+    """Every alternation of the 4096x4096 workload, the oracle taking the device's inputs."""
+    w = synth.workload("c2")
+    bits, W = synth.make_weight(w)
+    Wd = dev_w(bits, w)
+    d, k = W.shape
+    W64 = W.astype(np.float64)
+    Bd = Ad = Bh = Ah = None
+    for t in range(1, w.iterative_steps + 1):
+        packed, am = lib.loftq_nf4_quantize(Wd, Bd, Ad)
+        R = W if Bh is None else (W64 - Bh.astype(np.float64) @ Ah.astype(np.float64)).astype(np.float32)
+        ocodes, oam = oracle.quantize_residual(R.ravel())
+        dcodes = oracle.unpack_nibbles(host(packed), d * k)
+        mis = float(np.mean(dcodes != ocodes))
+        assert mis <= (0.0 if t == 1 else 1e-4), (t, mis)
+        dam = host(am)
+        assert np.allclose(dam, oam, rtol=1e-6, atol=0), t
+        q, s = lib.loftq_double_quant(am)
+        oq, os_ = oracle.double_quant(dam)
+        assert np.array_equal(host(q), oq) and np.array_equal(host(s), os_.astype(np.float32)), t
+        E_d = lib.loftq_nf4_dequantize(packed, (d, k), qabsmax=q, dq_scale=s, W=Wd)
+        E = host(E_d)
+        Eo = oracle.dequantize(dcodes, oracle.dq_scales_expand(oq, os_), W=W.ravel()).reshape(d, k)
+        assert np.array_equal(E, Eo), t
+        Bd, Ad, sd = lib.loftq_lowrank_svd(E_d, w.rank, w.oversample, w.power_iters, seed=w.sketch_seed, t=t)
+        Bh, Ah, sh = host(Bd), host(Ad), host(sd).astype(np.float64)
+        om = oracle.rademacher_sketch(w.sketch_seed, t, k, w.rank + w.oversample)
+        _, s_ref, _ = oracle.randomized_svd(E, w.rank, om, w.power_iters)
+        rel = float(np.max(np.abs(sh - s_ref) / s_ref))
+        assert rel <= SIGMA_RTOL, (t, rel)
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("w", _big_cases())
+def test_full_init_sampled(lib, w):
+    bits, W = synth.make_weight(w)
+    Wd = dev_w(bits, w)
+    del bits
+    prev = run_init(lib, w, Wd, T=w.iterative_steps - 1)
+    out = run_init(lib, w, Wd)
+    one = run_init(lib, w, Wd, T=1)
+    del Wd
+    torch.cuda.empty_cache()
+    groups = sampled_groups(w.numel, w.seed)
+    check_groups(one, W, w, groups, exact=True)
+    check_groups(out, W, w, groups, prev["B"], prev["A"])
+    assert out["objective"][-1] < out["objective"][0]
+    check_last_svd(lib, out, W, w)
