@@ -375,7 +375,32 @@ __global__ __launch_bounds__(256) void double_quant_kernel(const float* __restri
 
 // ---------------------------------------------------------------------------
 // Dequant: out = deq or W - deq, plus sum of out^2.
+//
+// Whole 1024-element slices go one per wave: lane L handles elements
+// 256 q + 4 L .. + 3 of the slice for q = 0..3, so the code, weight and output
+// accesses of every instruction are one contiguous run (the float4 stores write
+// 1 KB each).  Storing a thread's 64 contiguous output bytes as four float4
+// instead leaves each store instruction strided and costs about 1.6x.  The
+// ragged end (n mod 1024 elements) is done by workgroup 0 after its slices.
 constexpr int kDeqMaxBlocks = 2048;
+
+__device__ __forceinline__ void load4(const uint16_t* __restrict__ p, float v[4]) {
+  const uint2 a = *reinterpret_cast<const uint2*>(p);
+  v[0] = __uint_as_float(a.x << 16);
+  v[1] = __uint_as_float(a.x & 0xFFFF0000u);
+  v[2] = __uint_as_float(a.y << 16);
+  v[3] = __uint_as_float(a.y & 0xFFFF0000u);
+}
+__device__ __forceinline__ void load4(const float* __restrict__ p, float v[4]) {
+  const float4 a = *reinterpret_cast<const float4*>(p);
+  v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+}
+
+template <bool kDQ>
+__device__ __forceinline__ float block_scale(const float* __restrict__ absmax, const int8_t* __restrict__ qa,
+                                             const float* __restrict__ dqs, int dqbs, int64_t b) {
+  return kDQ ? static_cast<float>(qa[b]) * dqs[b / dqbs] : absmax[b];
+}
 
 template <typename T, bool kHasW, bool kDQ>
 __global__ __launch_bounds__(kThreads) void dequant_kernel(const uint8_t* __restrict__ packed,
@@ -384,49 +409,71 @@ __global__ __launch_bounds__(kThreads) void dequant_kernel(const uint8_t* __rest
                                                            const float* __restrict__ dqs, int dqbs, int64_t n,
                                                            const T* __restrict__ W, float* __restrict__ out,
                                                            double* __restrict__ partials,
-                                                           unsigned* __restrict__ counter,
                                                            double* __restrict__ sumsq, Nf4Tables tab) {
   __shared__ float lvl[16];
   __shared__ double red[kThreads / 64];
   if (threadIdx.x < 16) lvl[threadIdx.x] = tab.level[threadIdx.x];
   __syncthreads();
-  const int64_t ngroups = n >> 4;
-  const int64_t stride = static_cast<int64_t>(gridDim.x) * kThreads;
+  const int lane = threadIdx.x & 63;
+  const int64_t nslices = n >> 10;
+  const int64_t nwaves = static_cast<int64_t>(gridDim.x) * (kThreads / 64);
   double acc = 0.0;
-  for (int64_t g = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x; g < ngroups; g += stride) {
-    const int64_t b = g >> 2;
-    const float a = kDQ ? static_cast<float>(qa[b]) * dqs[b / dqbs] : absmax[b];
-    const uint2 pw = reinterpret_cast<const uint2*>(packed)[g];
-    float w[16];
-    if (kHasW) load16(W + g * 16, w);
-    float o[16];
+  for (int64_t sl = (static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x) >> 6; sl < nslices; sl += nwaves) {
+    const int64_t base = (sl << 10) + 4 * lane;
+    uint32_t cw[4];
+    float a[4], w[4][4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int64_t e = base + 256 * q;
+      cw[q] = reinterpret_cast<const uint16_t*>(packed)[e >> 2];
+      a[q] = block_scale<kDQ>(absmax, qa, dqs, dqbs, e >> 6);
+      if (kHasW) load4(W + e, w[q]);
+    }
     float ss = 0.f;
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const uint32_t word = (e < 8) ? pw.x : pw.y;
-      const uint32_t code = (word >> nib_shift(e)) & 0xFu;
-      const float d = lvl[code] * a;
-      o[e] = kHasW ? (w[e] - d) : d;
-      ss = fmaf(o[e], o[e], ss);
-    }
-    float4* op = reinterpret_cast<float4*>(out + g * 16);
+    for (int q = 0; q < 4; ++q) {
+      float o[4];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) op[q] = make_float4(o[4 * q], o[4 * q + 1], o[4 * q + 2], o[4 * q + 3]);
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t code = (cw[q] >> nib_shift(j)) & 0xFu;
+        const float d = lvl[code] * a[q];
+        o[j] = kHasW ? (w[q][j] - d) : d;
+        ss = fmaf(o[j], o[j], ss);
+      }
+      *reinterpret_cast<float4*>(out + base + 256 * q) = make_float4(o[0], o[1], o[2], o[3]);
+    }
     acc += static_cast<double>(ss);
   }
-  // ragged tail (fewer than 16 elements), handled by thread 0 of workgroup 0
-  if (blockIdx.x == 0 && threadIdx.x == 0) {
-    float ss = 0.f;
-    for (int64_t i = ngroups * 16; i < n; ++i) {
-      const int64_t b = i >> 6;
-      const float a = kDQ ? static_cast<float>(qa[b]) * dqs[b / dqbs] : absmax[b];
-      const uint32_t code = (packed[i >> 1] >> ((i & 1) ? 0 : 4)) & 0xFu;
-      const float d = lvl[code] * a;
-      const float o = kHasW ? (load1(W, i) - d) : d;
-      out[i] = o;
-      ss = fmaf(o, o, ss);
+  // ragged end: whole groups of 16 by the threads of workgroup 0, then the last
+  // few elements by its thread 0
+  if (blockIdx.x == 0) {
+    const int64_t ngroups = n >> 4;
+    for (int64_t g = (nslices << 6) + threadIdx.x; g < ngroups; g += kThreads) {
+      const float sc = block_scale<kDQ>(absmax, qa, dqs, dqbs, g >> 2);
+      const uint2 pw = reinterpret_cast<const uint2*>(packed)[g];
+      float ss = 0.f;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const uint32_t code = (((e < 8) ? pw.x : pw.y) >> nib_shift(e)) & 0xFu;
+        const float d = lvl[code] * sc;
+        const float o = kHasW ? (load1(W, g * 16 + e) - d) : d;
+        out[g * 16 + e] = o;
+        ss = fmaf(o, o, ss);
+      }
+      acc += static_cast<double>(ss);
     }
-    acc += static_cast<double>(ss);
+    if (threadIdx.x == 0) {
+      float ss = 0.f;
+      for (int64_t i = ngroups * 16; i < n; ++i) {
+        const float sc = block_scale<kDQ>(absmax, qa, dqs, dqbs, i >> 6);
+        const uint32_t code = (packed[i >> 1] >> ((i & 1) ? 0 : 4)) & 0xFu;
+        const float d = lvl[code] * sc;
+        const float o = kHasW ? (load1(W, i) - d) : d;
+        out[i] = o;
+        ss = fmaf(o, o, ss);
+      }
+      acc += static_cast<double>(ss);
+    }
   }
   for (int off = 32; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = acc;
@@ -537,7 +584,7 @@ hipError_t dequant_typed(const uint8_t* packed, const float* absmax, const int8_
   const bool dq = q != nullptr;
 #define LQ_DEQ(HW, DQ)                                                                                            \
   LQ_LAUNCH("nf4_dequantize", (dequant_kernel<T, HW, DQ>), dim3(grid), dim3(kThreads), 0, s, packed, absmax, q,   \
-            dqs, dqbs, n, W, out, partials, counter, sumsq, tab)
+            dqs, dqbs, n, W, out, partials, sumsq, tab)
   if (W != nullptr) {
     if (dq) LQ_DEQ(true, true); else LQ_DEQ(true, false);
   } else {
