@@ -222,132 +222,111 @@ __device__ __forceinline__ void raw_to_f32(const uint4 (&raw)[4], float v[16]) {
   }
 }
 
-// Fused residual R = W - B A (cols % 64 == 0, r <= 64), workgroup of 4 waves on
-// a strip of SW = 64 NBS columns, walking nrb batches of BR = 16 RB rows
-// (NBS RB = 4).
+// Fused residual R = W - B A (cols % 64 == 0, r <= 64).  Each wave owns one
+// 64-column block column and walks a run of 16-row tiles of it; waves share
+// nothing, so there is no LDS tile and no barrier after the table fill.
 //
-// Phase 1 (matrix cores): wave w multiplies the 16-row group w / NBS of the
-// batch by 64-column block w % NBS on fp32 MFMA (v_mfma_f32_16x16x4_f32: lane L
-// supplies A[L%16][L/16] and B[L/16][L%16] and receives D[4(L/16)+v][L%16]),
-// with M = 16 columns (tile t of the block holds columns 16 t .. 16 t + 15),
-// N = 16 rows, K = 4 rank indices; rank index p = KK k + kk for K-step kk and
-// K slot k, so a lane's B operands are KK consecutive entries of its row.  The
-// strip's A sits in LDS in operand order (one float4 per lane and K-step: the
-// four tiles).  B A goes to an LDS tile, row-major.
-// Phase 2 (encode): thread q takes 16-element group q of the batch tile (row
-// q / (SW / 16)), so a wave reads W in runs of SW contiguous columns and a DPP
-// quad holds one 64-element block, exactly as in the plain kernel.  W of the
-// group is loaded before phase 1.
+// B A of a tile comes from fp32 MFMA (v_mfma_f32_16x16x4_f32: lane L supplies
+// A_op[L%16][L/16] and B_op[L/16][L%16] and receives D[4(L/16)+v][L%16]) with
+// M = 16 columns, N = 16 rows and K = 4 rank indices p = KK k + kk (K-step kk,
+// slot k).  MFMA tile t maps its M index m to block column
+// 16 (m >> 2) + 4 t + (m & 3), so lane (li, g) ends up holding row li, columns
+// 16 g .. 16 g + 15 of the block: exactly the 16-element group it loaded from W,
+// with the block's four groups in lanes li, li + 16, li + 32, li + 48.  A's
+// operands (4 tiles x KK values per lane) stay in registers for the whole run;
+// the next tile's W and B operands are loaded before the current tile is
+// computed.
 constexpr int kFusedThreads = 256, kFusedMaxR = 64;
-
-template <int R16>
-struct FusedCfg {
-  static constexpr int NBS = R16 <= 16 ? 4 : 2;                     // 64-column blocks per strip
-  static constexpr int RB = 4 / NBS;                                 // 16-row groups per batch
-  static constexpr int SW = 64 * NBS;                                // strip width (A in LDS: SW x R16 fp32 <= 32 KB)
-  static constexpr int BR = 16 * RB;                                 // rows per batch (BA tile BR x SW fp32)
-  static constexpr int KK = R16 / 4;                                 // MFMA K-steps
-  static constexpr int LDT = SW + 4;                                 // BA tile row stride (floats)
-};
+constexpr int64_t kFusedWaves = 3072;
 
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 
-template <typename T, int R16>
-__global__ __launch_bounds__(kFusedThreads) void quantize_fused_kernel(const T* __restrict__ W, int64_t rows,
+template <typename T, int R16, bool kFullR>
+__global__ __launch_bounds__(kFusedThreads) __attribute__((amdgpu_waves_per_eu(R16 <= 16 ? 4 : 2))) void quantize_fused_kernel(const T* __restrict__ W, int64_t rows,
                                                                        int64_t cols, const float* __restrict__ B,
-                                                                       const float* __restrict__ A, int r, int nrb,
+                                                                       const float* __restrict__ A, int r, int tpw,
                                                                        uint8_t* __restrict__ packed,
                                                                        float* __restrict__ absmax, Nf4Tables tab) {
-  using C = FusedCfg<R16>;
-  constexpr int NBS = C::NBS, SW = C::SW, BR = C::BR, KK = C::KK, LDT = C::LDT;
+  constexpr int KK = R16 / 4;
   __shared__ EncodeLds s;
-  __shared__ float4 As[NBS * KK * 64];    // [blk][kk][lane] -> tiles 0..3
-  __shared__ float BAs[BR * LDT];
   fill_lds(s, tab);
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, li = lane & 15, g = lane >> 4;
-  const int64_t nstrips = cols / SW + ((cols % SW) ? 1 : 0);
-  const int64_t strip = blockIdx.x % nstrips, chunk = blockIdx.x / nstrips;
-  const int64_t col0 = strip * SW;
-  const int strip_cols = static_cast<int>((cols - col0) < SW ? (cols - col0) : SW);
-  // operand slot (blk, kk, lane = 16 k + j) holds A[KK k + kk][col0 + 64 blk + 16 t + j] for tiles t = 0..3
-  for (int slot = tid; slot < NBS * KK * 64; slot += kFusedThreads) {
-    const int blk = slot / (KK * 64), rem = slot - blk * (KK * 64);
-    const int kk = rem >> 6, k = (rem >> 4) & 3, j = rem & 15;
-    const int p = KK * k + kk, c = 64 * blk + j;
-    float val[4];
+  __syncthreads();
+  const int lane = threadIdx.x & 63, li = lane & 15, g = lane >> 4;
+  const int64_t nbc = cols >> 6;
+  const int64_t wave = (static_cast<int64_t>(blockIdx.x) * kFusedThreads + threadIdx.x) >> 6;
+  const int64_t bc = wave % nbc, chunk = wave / nbc;
+  const int64_t ntiles = (rows + 15) >> 4;
+  const int64_t t0 = chunk * tpw;
+  if (t0 >= ntiles) return;
+  const int64_t t1 = (t0 + tpw < ntiles) ? t0 + tpw : ntiles;
+  const int64_t col0 = bc << 6;
+  float aop[KK][4];
+  {
+    const int64_t cbase = col0 + 16 * (li >> 2) + (li & 3);
 #pragma unroll
-    for (int t = 0; t < 4; ++t)
-      val[t] = (p < r && c + 16 * t < strip_cols) ? A[static_cast<int64_t>(p) * cols + col0 + c + 16 * t] : 0.f;
-    As[slot] = make_float4(val[0], val[1], val[2], val[3]);
+    for (int kk = 0; kk < KK; ++kk) {
+      const int p = KK * g + kk;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) aop[kk][t] = (kFullR || p < r) ? A[static_cast<int64_t>(p) * cols + cbase + 4 * t] : 0.f;
+    }
   }
-  const int bw = wave % NBS, rgw = wave / NBS;   // phase-1 block and row group of this wave
-  const bool blk_ok = 64 * bw < strip_cols;
-  constexpr int GPR = SW / 16;                   // phase-2 groups per tile row
-  const int qrow = tid / GPR, qc = 16 * (tid - qrow * GPR);
-  const bool q_ok = qc < strip_cols;
-  for (int rb = 0; rb < nrb; ++rb) {
-    const int64_t row0 = (chunk * nrb + rb) * BR;
-    if (row0 >= rows) break;
-    // W of this thread's phase-2 group (row clamped; rows past the end are not stored)
-    uint4 wraw[4];
-    {
-      int64_t row = row0 + qrow;
-      row = row < rows ? row : rows - 1;
-      load16_raw(W + row * cols + col0 + (q_ok ? qc : 0), wraw);
-    }
-    // B operands: lane (li, g) of row group rgw, K slot g: B[row][KK g .. KK g + KK - 1]
-    float bop[KK];
-    {
-      const int64_t row = row0 + 16 * rgw + li;
+  auto load_tile = [&](int64_t tile, uint4 (&raw)[4], float (&bop)[KK]) {
+    const int64_t row = (tile << 4) + li;
+    const int64_t rc = row < rows ? row : rows - 1;
+    load16_raw(W + rc * cols + col0 + 16 * g, raw);
+    if (kFullR) {
+#pragma unroll
+      for (int q = 0; q < KK / 4; ++q) {
+        const float4 b4 = *reinterpret_cast<const float4*>(B + rc * R16 + KK * g + 4 * q);
+        bop[4 * q] = b4.x; bop[4 * q + 1] = b4.y; bop[4 * q + 2] = b4.z; bop[4 * q + 3] = b4.w;
+      }
+    } else {
 #pragma unroll
       for (int kk = 0; kk < KK; ++kk) {
-        const int pidx = KK * g + kk;
-        bop[kk] = (row < rows && pidx < r) ? B[row * r + pidx] : 0.f;
+        const int p = KK * g + kk;
+        bop[kk] = (p < r) ? B[rc * r + p] : 0.f;
       }
     }
-    __syncthreads();   // A staged (first batch) / previous batch's tile consumed
-    if (blk_ok) {
-      floatx4 acc[4];
+  };
+  auto do_tile = [&](int64_t tile, const uint4 (&raw)[4], const float (&bop)[KK]) {
+    floatx4 acc[4];
 #pragma unroll
-      for (int t = 0; t < 4; ++t) acc[t] = floatx4{0.f, 0.f, 0.f, 0.f};
+    for (int t = 0; t < 4; ++t) acc[t] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int kk = 0; kk < KK; ++kk) {
-        const float4 a4 = As[(bw * KK + kk) * 64 + lane];
-        acc[0] = __builtin_amdgcn_mfma_f32_16x16x4f32(a4.x, bop[kk], acc[0], 0, 0, 0);
-        acc[1] = __builtin_amdgcn_mfma_f32_16x16x4f32(a4.y, bop[kk], acc[1], 0, 0, 0);
-        acc[2] = __builtin_amdgcn_mfma_f32_16x16x4f32(a4.z, bop[kk], acc[2], 0, 0, 0);
-        acc[3] = __builtin_amdgcn_mfma_f32_16x16x4f32(a4.w, bop[kk], acc[3], 0, 0, 0);
-      }
-      // lane (li, g), tile t, component v: row 16 rgw + li, column 64 bw + 16 t + 4 g + v
+    for (int kk = 0; kk < KK; ++kk)
 #pragma unroll
-      for (int t = 0; t < 4; ++t)
-        *reinterpret_cast<float4*>(&BAs[(16 * rgw + li) * LDT + 64 * bw + 16 * t + 4 * g]) =
-            make_float4(acc[t][0], acc[t][1], acc[t][2], acc[t][3]);
-    }
-    __syncthreads();
+      for (int t = 0; t < 4; ++t) acc[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(aop[kk][t], bop[kk], acc[t], 0, 0, 0);
     float v[16];
-    raw_to_f32<T>(wraw, v);
-    const float4* bp = reinterpret_cast<const float4*>(&BAs[qrow * LDT + qc]);
+    raw_to_f32<T>(raw, v);
     float m = 0.f;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const float4 ba = bp[q];
-      v[4 * q] = v[4 * q] - ba.x;
-      v[4 * q + 1] = v[4 * q + 1] - ba.y;
-      v[4 * q + 2] = v[4 * q + 2] - ba.z;
-      v[4 * q + 3] = v[4 * q + 3] - ba.w;
+    for (int t = 0; t < 4; ++t)
 #pragma unroll
-      for (int e = 4 * q; e < 4 * q + 4; ++e) m = fmaxf(m, fabsf(v[e]));
-    }
-    const float a = quad_max(m);
-    const uint2 w = encode16(v, a, s);
-    const int64_t row = row0 + qrow;
-    if (q_ok && row < rows) {
-      const int64_t e0 = row * cols + col0 + qc;
+      for (int q = 0; q < 4; ++q) {
+        v[4 * t + q] -= acc[t][q];
+        m = fmaxf(m, fabsf(v[4 * t + q]));
+      }
+    m = fmaxf(m, __shfl_xor(m, 16));
+    m = fmaxf(m, __shfl_xor(m, 32));
+    const uint2 w = encode16(v, m, s);
+    const int64_t row = (tile << 4) + li;
+    if (row < rows) {
+      const int64_t e0 = row * cols + col0 + 16 * g;
       reinterpret_cast<uint2*>(packed)[e0 >> 4] = w;
-      if ((tid & 3) == 0) absmax[e0 >> 6] = a;
+      if (g == 0) absmax[e0 >> 6] = m;
     }
+  };
+  uint4 raw0[4], raw1[4];
+  float bop0[KK], bop1[KK];
+  load_tile(t0, raw0, bop0);
+  int64_t tile = t0;
+  for (; tile + 1 < t1; tile += 2) {
+    load_tile(tile + 1, raw1, bop1);
+    do_tile(tile, raw0, bop0);
+    if (tile + 2 < t1) load_tile(tile + 2, raw0, bop0);
+    do_tile(tile + 1, raw1, bop1);
   }
+  if (tile < t1) do_tile(tile, raw0, bop0);
 }
 
 // ---------------------------------------------------------------------------
@@ -546,20 +525,23 @@ hipError_t quantize_typed(const T* W, int64_t rows, int64_t cols, const float* B
     }
   } else if (cols % 64 == 0 && r <= kFusedMaxR) {
     const int r16 = (r + 15) / 16 * 16;
-    const int sw = r16 <= 16 ? 256 : 128;
-    const int br = 16 * (4 / (sw / 64));
-    const int64_t nstrips = (cols + sw - 1) / sw;
-    const int64_t batches = (rows + br - 1) / br;
-    // about four workgroups per CU over the strips; each walks nrb row batches
-    int64_t chunks = (1024 + nstrips - 1) / nstrips;
-    if (chunks > batches) chunks = batches;
-    if (chunks < 1) chunks = 1;
-    const int nrb = static_cast<int>((batches + chunks - 1) / chunks);
-    chunks = (batches + nrb - 1) / nrb;
-    const dim3 grid(static_cast<unsigned>(nstrips * chunks));
+    const int64_t nbc = cols / 64, ntiles = (rows + 15) / 16;
+    // about kFusedWaves waves in all, each a run of tiles of one block column
+    int64_t tpw = (nbc * ntiles + kFusedWaves - 1) / kFusedWaves;
+    if (tpw < 1) tpw = 1;
+    const int64_t chunks = (ntiles + tpw - 1) / tpw;
+    const int64_t waves = nbc * chunks;
+    const dim3 grid(static_cast<unsigned>((waves + 3) / 4));
+    const bool full = (r == r16);
 #define LQ_FUSED(R16)                                                                                              \
-  LQ_LAUNCH("nf4_quantize_fused", (quantize_fused_kernel<T, R16>), grid, dim3(kFusedThreads), 0, s, W, rows, cols, B, \
-            A, r, nrb, packed, absmax, tab)
+  do {                                                                                                             \
+    if (full)                                                                                                      \
+      LQ_LAUNCH("nf4_quantize_fused", (quantize_fused_kernel<T, R16, true>), grid, dim3(kFusedThreads), 0, s, W,   \
+                rows, cols, B, A, r, static_cast<int>(tpw), packed, absmax, tab);                                  \
+    else                                                                                                           \
+      LQ_LAUNCH("nf4_quantize_fused", (quantize_fused_kernel<T, R16, false>), grid, dim3(kFusedThreads), 0, s, W,  \
+                rows, cols, B, A, r, static_cast<int>(tpw), packed, absmax, tab);                                  \
+  } while (0)
     if (r16 == 16) LQ_FUSED(16);
     else if (r16 == 32) LQ_FUSED(32);
     else if (r16 == 48) LQ_FUSED(48);
