@@ -15,6 +15,7 @@
 // buffers are zero-padded to the splits' full extent), and garbage output
 // rows/columns are never stored.
 #include "lowrank.h"
+#include "small_solve.h"
 
 namespace loftq {
 namespace {
@@ -164,13 +165,33 @@ __global__ __launch_bounds__(64 * NnCfg<NT>::WR * NnCfg<NT>::WK) void gemm_nn_ke
 // columns c0 + 4 m + jm).  Row step j covers rows rb + 16 j .. + 15; MFMA i of
 // the step takes rows rb + 16 j + 4 g + i (K index g), matching component i of
 // the fragment-order Y float4.
-template <int NT, bool VEC>
+template <int NT, bool VEC, int LMJ>
 __global__ __launch_bounds__(64 * TnCfg<NT>::WC * TnCfg<NT>::WR) void gemm_tn_kernel(
     const float* __restrict__ E, int64_t d, int64_t k, const float* __restrict__ Yf, int64_t rper,
-    float* __restrict__ part) {
+    float* __restrict__ part, CholJob job) {
   using C = TnCfg<NT>;
   constexpr int LP = 16 * NT, D = C::D, WC = C::WC, WR = C::WR;
-  __shared__ float red[(WR > 1 ? WR - 1 : 1) * WC * 64 * LP];
+  constexpr int kRedFloats = (WR > 1 ? WR - 1 : 1) * WC * 64 * LP;
+  constexpr int kJobDoubles = LMJ > 0 ? 5 * (LMJ * (LMJ + 1) / 2) + 64 : 1;
+  constexpr int kLdsBytes = 4 * kRedFloats > 8 * kJobDoubles ? 4 * kRedFloats : 8 * kJobDoubles;
+  __shared__ __align__(16) char lds_raw[kLdsBytes];
+  float* red = reinterpret_cast<float*>(lds_raw);
+  // LMJ > 0: the extra last column of workgroups carries a Cholesky job; its
+  // row 0 sums the Gram partials of Y and factors them (X = R^-1 for the
+  // reduction that follows this product), l <= LMJ
+  if constexpr (LMJ > 0) {
+    if (blockIdx.x == gridDim.x - 1) {
+      if (blockIdx.y == 0) {
+        // a latency-bound serial chain sharing its CU with streaming waves: let
+        // it win instruction arbitration
+        __builtin_amdgcn_s_setprio(3);
+        double* lds = reinterpret_cast<double*>(lds_raw);
+        const double* gram = gram_sum_block<LMJ>(job.parts, job.P, job.l, lds);
+        if (threadIdx.x < 64) chol_inv_to<LMJ>(gram, job.l, job.Xinv, lds);
+      }
+      return;
+    }
+  }
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, wc = w % WC, wr = w / WC;
   const int g = lane >> 4, li = lane & 15;
   const int64_t c0 = (static_cast<int64_t>(blockIdx.x) * WC + wc) * 64;
@@ -262,13 +283,25 @@ GemmShape shape_typed(bool transposed) {
 
 template <int NT>
 void gemm_typed(bool transposed, const float* E, int64_t d, int64_t k, const float* panel, const SvdPlan& pl,
-                float* part, hipStream_t s) {
+                float* part, const CholJob& job, hipStream_t s) {
   const bool vec = (k & 3) == 0 && k >= 4;
   if (transposed) {
     constexpr int threads = 64 * TnCfg<NT>::WC * TnCfg<NT>::WR;
-    const dim3 grid(pl.tn_col_blocks, pl.tn_splits);
-    if (vec) LQ_LAUNCH("gemm_tn", (gemm_tn_kernel<NT, true>), grid, dim3(threads), 0, s, E, d, k, panel, pl.tn_rper, part);
-    else LQ_LAUNCH("gemm_tn", (gemm_tn_kernel<NT, false>), grid, dim3(threads), 0, s, E, d, k, panel, pl.tn_rper, part);
+    const dim3 grid(pl.tn_col_blocks + (job.parts != nullptr ? 1 : 0), pl.tn_splits);
+#define LQ_TN(V, LMJ) \
+  LQ_LAUNCH("gemm_tn", (gemm_tn_kernel<NT, V, LMJ>), grid, dim3(threads), 0, s, E, d, k, panel, pl.tn_rper, part, job)
+    // register tile of the ride-along Cholesky: the smallest of 16 / 24 / 32 rows that holds l
+    const int lmj = job.parts == nullptr ? 0 : (job.l <= 16 ? 16 : (job.l <= 24 ? 24 : 32));
+    if constexpr (NT == 1) {
+      if (vec) { if (lmj) LQ_TN(true, 16); else LQ_TN(true, 0); }
+      else { if (lmj) LQ_TN(false, 16); else LQ_TN(false, 0); }
+    } else if constexpr (NT == 2) {
+      if (vec) { if (lmj == 16) LQ_TN(true, 16); else if (lmj == 24) LQ_TN(true, 24); else if (lmj) LQ_TN(true, 32); else LQ_TN(true, 0); }
+      else { if (lmj == 16) LQ_TN(false, 16); else if (lmj == 24) LQ_TN(false, 24); else if (lmj) LQ_TN(false, 32); else LQ_TN(false, 0); }
+    } else {
+      if (vec) LQ_TN(true, 0); else LQ_TN(false, 0);
+    }
+#undef LQ_TN
   } else {
     constexpr int threads = 64 * NnCfg<NT>::WR * NnCfg<NT>::WK;
     const dim3 grid(pl.nn_row_blocks, pl.nn_splits);
@@ -290,13 +323,15 @@ GemmShape gemm_shape(bool transposed, int nt) {
 }
 
 void launch_gemm(bool transposed, const float* E, int64_t d, int64_t k, const float* panel, const SvdPlan& pl,
-                 float* part, hipStream_t s) {
+                 float* part, const CholJob& job, hipStream_t s) {
+  const CholJob none{nullptr, 0, 0, nullptr};
+  const CholJob& j = (transposed && pl.nt <= 2) ? job : none;
   switch (pl.nt) {
-    case 1: gemm_typed<1>(transposed, E, d, k, panel, pl, part, s); break;
-    case 2: gemm_typed<2>(transposed, E, d, k, panel, pl, part, s); break;
-    case 3: gemm_typed<3>(transposed, E, d, k, panel, pl, part, s); break;
-    case 4: gemm_typed<4>(transposed, E, d, k, panel, pl, part, s); break;
-    default: gemm_typed<5>(transposed, E, d, k, panel, pl, part, s); break;
+    case 1: gemm_typed<1>(transposed, E, d, k, panel, pl, part, j, s); break;
+    case 2: gemm_typed<2>(transposed, E, d, k, panel, pl, part, j, s); break;
+    case 3: gemm_typed<3>(transposed, E, d, k, panel, pl, part, j, s); break;
+    case 4: gemm_typed<4>(transposed, E, d, k, panel, pl, part, j, s); break;
+    default: gemm_typed<5>(transposed, E, d, k, panel, pl, part, j, s); break;
   }
 }
 

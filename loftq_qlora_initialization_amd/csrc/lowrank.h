@@ -8,7 +8,8 @@ namespace loftq {
 constexpr int kMaxL = 80;        // randomized sketch width l = r + p (fp64 l x l core lives in LDS)
 constexpr int kMaxR = 64;        // rank limit of the randomized path's factor kernels
 constexpr int kMaxExact = 512;   // exact SVD: min(rows, cols) limit
-constexpr int kGramRows = 32;    // rows per workgroup (and fp64 Gram partial) of reduce_gram
+constexpr int kGramRows = 64;    // rows per workgroup (and fp64 Gram partial) of reduce_gram
+constexpr int kReduceThreads = 512;
 constexpr int kPanelRows = 64;   // rows per workgroup (and Gram partial) of the panel x small kernel
 
 // Where the objective of an alternation goes: ||E||^2 and ||W||^2 arrive as
@@ -62,8 +63,19 @@ hipError_t run_sketch(uint64_t seed, int t, int64_t k, int l, int nt, int64_t ro
 hipError_t run_fill(float* p, int64_t n, float v, hipStream_t s);
 hipError_t run_objective(const ObjectiveArgs& obj, hipStream_t s);
 GemmShape gemm_shape(bool transposed, int nt);
+
+// A Cholesky that rides along with a thin product E^T Y (l <= 32 only): one
+// extra workgroup sums the P fp64 Gram partials of Y (parts) and writes
+// X = R^-1 (fp32 l x l) while the other workgroups stream E.  parts == nullptr:
+// no job.
+struct CholJob {
+  const double* parts;
+  int P;
+  int l;
+  float* Xinv;
+};
 void launch_gemm(bool transposed, const float* E, int64_t d, int64_t k, const float* panel, const SvdPlan& pl,
-                 float* part, hipStream_t s);
+                 float* part, const CholJob& job, hipStream_t s);
 
 bool aligned16(const void* p);
 bool shape_ok(int64_t rows, int64_t cols);

@@ -22,6 +22,7 @@
 // Every reduction runs in a fixed order, so results are deterministic.
 #include "lowrank.h"
 #include "reduce.h"
+#include "small_solve.h"
 
 namespace loftq {
 namespace {
@@ -62,20 +63,6 @@ __global__ void to_frag_kernel(const float* __restrict__ src, int64_t n, int l, 
   const int64_t i = blk * 16 + ((f >> 6) << 2) + (f & 3);
   const int j = tile * 16 + ((f >> 2) & 15);
   out[idx] = (i < n && j < l) ? src[i * l + j] : 0.f;
-}
-
-__device__ __forceinline__ int packed_index(int a, int b, int l) { return a * l - (a * (a - 1)) / 2 + (b - a); }
-
-// Gram partial (upper triangle, packed) of `nrows` rows held in LDS (row stride ld).
-__device__ void gram_partial(const float* rows, int ld, int nrows, int l, double* out) {
-  for (int e = threadIdx.x; e < l * l; e += blockDim.x) {
-    const int a = e / l, b = e - a * l;
-    if (b < a) continue;
-    double s = 0.0;
-    for (int rr = 0; rr < nrows; ++rr)
-      s += static_cast<double>(rows[rr * ld + a]) * static_cast<double>(rows[rr * ld + b]);
-    out[packed_index(a, b, l)] = s;
-  }
 }
 
 // Full symmetric l x l (row stride ld) from a packed upper triangle in global memory.
@@ -183,20 +170,6 @@ __device__ __forceinline__ double group_sum(double v) {
     v += dpp_f64<0x4E>(v);    // quad_perm xor 2
   }
   return v;
-}
-
-// 1/x and 1/sqrt(x) in fp64: hardware estimate plus two Newton steps.
-__device__ __forceinline__ double rcp_f64(double x) {
-  double r = __builtin_amdgcn_rcp(x);
-  r = fma(r, fma(-x, r, 1.0), r);
-  r = fma(r, fma(-x, r, 1.0), r);
-  return r;
-}
-__device__ __forceinline__ double rsq_f64(double x) {
-  double y = __builtin_amdgcn_rsq(x);
-  y = y * fma(-0.5 * x * y, y, 1.5);
-  y = y * fma(-0.5 * x * y, y, 1.5);
-  return y;
 }
 
 // Rows per lane of the Jacobi groups: 16-lane groups serve n <= 32, 4-lane
@@ -388,60 +361,15 @@ __global__ __launch_bounds__(256) void small_kernel(const double* __restrict__ g
 }
 
 // ---------------------------------------------------------------------------
-// The same two solves for l <= 32.
+// The same two solves for l <= 32, on the register Cholesky of chol_wave.
 //
-// Cholesky by one wave: lane b keeps column b of the Gram (rows 0..LM-1) in
-// registers.  Step j takes the pivot from lane j and row j of R from the lanes
-// after it by readlane, then updates the trailing columns.  Entries below the
-// diagonal pick up values that are never read back into the upper triangle and
-// are dropped at the end.  For INV the same steps carry T = R^-T (lane b holds
-// column b of T, starting from the identity): row j of T is divided by R[j][j]
-// and rows a > j lose R[j][a] times it; then X = R^-1 = T^T, i.e. lane b holds
-// row b of X.  A pivot at or below 1e-13 of the largest diagonal entry drops
-// its direction (zero row of R, zero column of X).
-__device__ __forceinline__ double bcast_lane(double v, int lane) {
-  const int lo = __builtin_amdgcn_readlane(__double2loint(v), lane);
-  const int hi = __builtin_amdgcn_readlane(__double2hiint(v), lane);
-  return __hiloint2double(hi, lo);
-}
-
-template <int LM, bool INV>
-__device__ __forceinline__ void chol_wave(const double* __restrict__ gram, int l, double (&g)[LM], double (&t)[LM]) {
-  const int b = threadIdx.x & 63;
-#pragma unroll
-  for (int a = 0; a < LM; ++a) {
-    g[a] = (a <= b && b < l) ? gram[packed_index(a, b, l)] : 0.0;
-    if (INV) t[a] = (a == b) ? 1.0 : 0.0;
-  }
-  double dg = b < l ? gram[packed_index(b, b, l)] : 0.0;
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) dg = fmax(dg, __shfl_xor(dg, off));
-  const double tol = 1e-13 * dg;
-#pragma unroll
-  for (int j = 0; j < LM; ++j) {
-    if (j < l) {
-      const double piv = bcast_lane(g[j], j);
-      const bool keep = piv > tol && piv > 0.0;
-      const double inv = keep ? rsq_f64(piv) : 0.0;   // 1 / R[j][j]
-      const double rjj = piv * inv;
-      g[j] = b > j ? g[j] * inv : (b == j ? rjj : g[j]);
-      if (INV) t[j] *= inv;
-#pragma unroll
-      for (int a = j + 1; a < LM; ++a) {
-        const double rja = bcast_lane(g[j], a);
-        g[a] = fma(-rja, g[j], g[a]);
-        if (INV) t[a] = fma(-rja, t[j], t[a]);
-      }
-    }
-  }
-}
-
 // mode 1 for l <= LM: X = R^-1 (fp32, row-major l x l) by one wave.
 template <int LM>
 __global__ __launch_bounds__(64) void chol_inv_wave_kernel(const double* __restrict__ gram, int l,
                                                            float* __restrict__ Xinv) {
+  __shared__ double rowbuf[64];
   double g[LM], t[LM];
-  chol_wave<LM, true>(gram, l, g, t);
+  chol_wave<LM, true>(gram, l, g, t, rowbuf);
   const int lane = threadIdx.x;
   if (lane < l) {
 #pragma unroll
@@ -477,7 +405,7 @@ __global__ __launch_bounds__(256) void core_small_kernel(const double* __restric
   for (int e = tid; e < l * l; e += blockDim.x) Xs[e] = Xinv[e];
   if (tid < 64) {
     double g[LM], t[LM];
-    chol_wave<LM, false>(gram, l, g, t);
+    chol_wave<LM, false>(gram, l, g, t, K);   // K doubles as the row buffer until it is filled
     if (tid < 32) {
 #pragma unroll
       for (int a = 0; a < 32; ++a) K[tid * LD + a] = (a < LM && a <= tid && tid < l) ? g[a < LM ? a : 0] : 0.0;
@@ -582,21 +510,24 @@ __global__ __launch_bounds__(256) void core_small_kernel(const double* __restric
 
 // Sum of the split-K partials, sum_s part[s], in fixed order for a tile of
 // kGramRows rows, optionally right-multiplied by X (l x l fp32, upper
-// triangular), written in fragment order (zero-padded to m_pad rows), plus the
-// fp64 Gram partial (packed upper triangle) of the tile when gram_parts is given.
+// triangular; entries below the diagonal are ignored), written in fragment
+// order (zero-padded to m_pad rows), plus the fp64 Gram partial (packed upper
+// triangle) of the tile when gram_parts is given.  Every loop over the tile's
+// rows or X's rows has a compile-time trip count, so its LDS reads issue
+// back to back.
 template <int NT>
-__global__ __launch_bounds__(256) void reduce_gram_kernel(const float* __restrict__ part, int S, int64_t m,
+__global__ __launch_bounds__(kReduceThreads) void reduce_gram_kernel(const float* __restrict__ part, int S, int64_t m,
                                                           int64_t m_pad, int l, const float* __restrict__ X,
                                                           float* __restrict__ out, double* __restrict__ gram_parts) {
-  constexpr int LP = 16 * NT, PER = (kGramRows * LP + 255) / 256;
-  __shared__ float rows[kGramRows * (LP + 1)];
+  constexpr int LP = 16 * NT, PER = (kGramRows * LP + kReduceThreads - 1) / kReduceThreads, LDR = LP + 1;
+  __shared__ float rows[kGramRows * LDR];
   __shared__ float Xs[LP * LP];
   const int64_t r0 = static_cast<int64_t>(blockIdx.x) * kGramRows;
   const int64_t stride = m * LP;
   if (X) {
     for (int e = threadIdx.x; e < LP * LP; e += blockDim.x) {
       const int a = e / LP, b = e - a * LP;
-      Xs[e] = (a < l && b < l) ? X[a * l + b] : 0.f;
+      Xs[e] = (a <= b && b < l) ? X[a * l + b] : 0.f;
     }
   }
   // every thread sums its PER elements over the S partials, four partials of
@@ -606,7 +537,7 @@ __global__ __launch_bounds__(256) void reduce_gram_kernel(const float* __restric
   bool ok[PER];
 #pragma unroll
   for (int u = 0; u < PER; ++u) {
-    const int idx = threadIdx.x + 256 * u;
+    const int idx = threadIdx.x + kReduceThreads * u;
     const int rr = idx / LP, n = idx - rr * LP;
     const int64_t row = r0 + rr;
     ok[u] = idx < kGramRows * LP && row < m && n < l;
@@ -630,38 +561,52 @@ __global__ __launch_bounds__(256) void reduce_gram_kernel(const float* __restric
     for (int u = 0; u < PER; ++u) acc[u] += ok[u] ? part[p * stride + off[u]] : 0.f;
 #pragma unroll
   for (int u = 0; u < PER; ++u) {
-    const int idx = threadIdx.x + 256 * u;
-    if (idx < kGramRows * LP) rows[(idx / LP) * (LP + 1) + idx % LP] = acc[u];
+    const int idx = threadIdx.x + kReduceThreads * u;
+    if (idx < kGramRows * LP) rows[(idx / LP) * LDR + idx % LP] = acc[u];
   }
+  __syncthreads();
   if (X) {
-    __syncthreads();
     float t[PER];
 #pragma unroll
     for (int u = 0; u < PER; ++u) {
-      const int idx = threadIdx.x + 256 * u;
-      float acc = 0.f;
+      const int idx = threadIdx.x + kReduceThreads * u;
+      float a = 0.f;
       if (idx < kGramRows * LP) {
         const int rr = idx / LP, n = idx - rr * LP;
-        for (int a = 0; a <= n; ++a) acc = fmaf(rows[rr * (LP + 1) + a], Xs[a * LP + n], acc);
+#pragma unroll
+        for (int j = 0; j < LP; ++j) a = fmaf(rows[rr * LDR + j], Xs[j * LP + n], a);
       }
-      t[u] = acc;
+      t[u] = a;
     }
     __syncthreads();
 #pragma unroll
     for (int u = 0; u < PER; ++u) {
-      const int idx = threadIdx.x + 256 * u;
-      if (idx < kGramRows * LP) rows[(idx / LP) * (LP + 1) + idx % LP] = t[u];
+      const int idx = threadIdx.x + kReduceThreads * u;
+      if (idx < kGramRows * LP) rows[(idx / LP) * LDR + idx % LP] = t[u];
     }
     __syncthreads();
   }
-  for (int idx = threadIdx.x; idx < kGramRows * LP; idx += blockDim.x) {
-    const int rr = idx / LP, n = idx - rr * LP;
-    const int64_t row = r0 + rr;
-    if (row < m_pad) out[frag_index(row, n, NT)] = rows[rr * (LP + 1) + n];
+  // fragment-order output: a thread writes rows 4 q .. 4 q + 3 of one column as one float4
+  for (int qd = threadIdx.x; qd < (kGramRows / 4) * LP; qd += blockDim.x) {
+    const int n = qd % LP, q = qd / LP;
+    const int64_t row = r0 + 4 * q;
+    if (row < m_pad)
+      *reinterpret_cast<float4*>(out + frag_index(row, n, NT)) =
+          make_float4(rows[(4 * q) * LDR + n], rows[(4 * q + 1) * LDR + n], rows[(4 * q + 2) * LDR + n],
+                      rows[(4 * q + 3) * LDR + n]);
   }
   if (gram_parts == nullptr || r0 >= m) return;
-  __syncthreads();
-  gram_partial(rows, LP + 1, kGramRows, l, gram_parts + static_cast<int64_t>(blockIdx.x) * (l * (l + 1) / 2));
+  // Gram partial: entry (a, b), a <= b, summed over the tile's rows in order
+  double* gp = gram_parts + static_cast<int64_t>(blockIdx.x) * (l * (l + 1) / 2);
+  for (int e = threadIdx.x; e < l * l; e += blockDim.x) {
+    const int a = e / l, b = e - a * l;
+    if (b < a) continue;
+    double sum = 0.0;
+#pragma unroll
+    for (int rr = 0; rr < kGramRows; ++rr)
+      sum = fma(static_cast<double>(rows[rr * LDR + a]), static_cast<double>(rows[rr * LDR + b]), sum);
+    gp[packed_index(a, b, l)] = sum;
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -831,7 +776,7 @@ template <int NT>
 void reduce_typed(const float* part, int S, int64_t m, int64_t m_pad, int l, const float* X, float* out,
                   double* gram_parts, hipStream_t s) {
   const int blocks = static_cast<int>(cdiv(m_pad, kGramRows));
-  LQ_LAUNCH("reduce_gram", (reduce_gram_kernel<NT>), dim3(blocks), dim3(256), 0, s, part, S, m, m_pad, l, X, out,
+  LQ_LAUNCH("reduce_gram", (reduce_gram_kernel<NT>), dim3(blocks), dim3(kReduceThreads), 0, s, part, S, m, m_pad, l, X, out,
             gram_parts);
 }
 
@@ -993,13 +938,24 @@ hipError_t run_lowrank(const float* E, const SvdPlan& pl, int q, const float* om
   // X = R^-1), mode 2 runs the core solve, mode 0 keeps the product.  E P goes
   // to Y (fragment order, d_pad rows, not orthonormalised: Q = Y X); E^T Y goes
   // through X to Z = E^T Q (fragment order, k_pad rows).
+  // For l <= 32 the Cholesky of Y's Gram (mode 1) needs no launch of its own:
+  // it rides along with the E^T Y product that always follows, whose split-K
+  // reduction is the first consumer of X.
+  const bool ride = l <= 32;
+  bool pending = false;
   auto product = [&](bool transposed, const float* panel, int mode) {
-    launch_gemm(transposed, E, d, k, panel, pl, part, s);
+    const CholJob job{pending ? gparts : nullptr, pl.gram_parts_d, l, Xinv};
+    launch_gemm(transposed, E, d, k, panel, pl, part, job, s);
+    if (transposed) pending = false;
     if (transposed)
       launch_reduce(pl.nt, part, pl.tn_splits, k, pl.k_pad, l, Xinv, Z, mode ? gparts : nullptr, s);
     else
       launch_reduce(pl.nt, part, pl.nn_splits, d, pl.d_pad, l, nullptr, Y, mode ? gparts : nullptr, s);
     if (mode == 0) return;
+    if (mode == 1 && ride) {
+      pending = true;
+      return;
+    }
     const int P = transposed ? pl.gram_parts_k : pl.gram_parts_d;
     LQ_LAUNCH("gram_sum", gram_sum_kernel, dim3((E_ + 63) / 64), dim3(1024), 0, s, gparts, P, E_, gtotal);
     if (l <= 32)
