@@ -172,6 +172,21 @@ __device__ __forceinline__ double group_sum(double v) {
   return v;
 }
 
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, true));
+}
+// fp32 sum over an aligned 16-lane row; every lane ends with the same total.
+template <int G>
+__device__ __forceinline__ float group_sumf(float v) {
+  static_assert(G == 16, "16-lane rows only");
+  v += dpp_f32<0x128>(v);   // row_ror:8
+  v += dpp_f32<0x124>(v);   // row_ror:4
+  v += dpp_f32<0x122>(v);   // row_ror:2
+  v += dpp_f32<0x121>(v);   // row_ror:1
+  return v;
+}
+
 // Rows per lane of the Jacobi groups: 16-lane groups serve n <= 32, 4-lane
 // groups n <= kMaxL.  K and V keep ld >= G * rows(G) rows, zero beyond n.
 template <int G>
@@ -378,25 +393,29 @@ __global__ __launch_bounds__(64) void chol_inv_wave_kernel(const double* __restr
   }
 }
 
-// mode 2 for l <= LM (LM <= 32), 256 threads.  Wave 0 factors H = K^T K; then
-// one-sided Jacobi on K's columns with pair i of a round owned by lanes
+// mode 2 for l <= LM (LM <= 32), 256 threads.  Wave 0 factors H = R^T R in
+// fp64; K = R scaled by a power of two (exact) is then swept in fp32 by
+// one-sided Jacobi on its columns, with pair i of a round owned by lanes
 // 16 i .. 16 i + 15 (rows sub and sub + 16).  Round-robin positions advance by
-// one per round, so each lane tracks its pair's two players in registers.  The
-// rotation angle is taken in fp32 (it only sets how much of the pair's coupling
-// is removed); c = (1 + t^2)^-1/2 is exact to fp64 so the rotation stays
-// orthogonal.  V (fp32) accumulates the rotations.  Pairs with |cos| <= 1e-7
-// are skipped; the sweeps stop after one in which no pair had |cos| > 1e-4.
+// one per round, so each lane tracks its pair's two players in registers.
+// One-sided Jacobi keeps high relative accuracy of the singular values in the
+// working precision, so fp32 sweeps hold the top-r values to ~1e-6 relative;
+// the column norms are summed in fp64 at the end.  V (fp32) accumulates the
+// rotations.  Pairs with |cos| <= 1e-7 are left alone (c = 1, s = 0); the
+// sweeps stop after one in which no pair had |cos| > 1e-4.
 template <int LM>
 __global__ __launch_bounds__(256) void core_small_kernel(const double* __restrict__ gram, int l,
                                                          const float* __restrict__ Xinv, int r, float* __restrict__ SB,
                                                          float* __restrict__ SA, float* __restrict__ sigma,
                                                          double* __restrict__ stats, ObjectiveArgs obj) {
   constexpr int LD = 33;
-  __shared__ double K[32 * LD];
+  __shared__ double Kd[32 * LD / 2 + 32];   // row buffer of the Cholesky
+  __shared__ float K[32 * LD];
   __shared__ float V[32 * LD];
   __shared__ float Xs[32 * 32];
   __shared__ double norm2[32];
   __shared__ int order[32];
+  __shared__ double kscale;
   const int tid = threadIdx.x;
   for (int e = tid; e < 32 * LD; e += blockDim.x) {
     const int c = e / LD, row = e - c * LD;
@@ -405,10 +424,20 @@ __global__ __launch_bounds__(256) void core_small_kernel(const double* __restric
   for (int e = tid; e < l * l; e += blockDim.x) Xs[e] = Xinv[e];
   if (tid < 64) {
     double g[LM], t[LM];
-    chol_wave<LM, false>(gram, l, g, t, K);   // K doubles as the row buffer until it is filled
+    chol_wave<LM, false>(gram, l, g, t, Kd);
+    // K = 2^-e R with 2^e at the scale of R's largest entry, so the fp32 sweeps
+    // neither overflow nor underflow whatever the magnitude of E
+    double m = 0.0;
+#pragma unroll
+    for (int a = 0; a < LM; ++a) m = fmax(m, (a <= tid && tid < l) ? fabs(g[a]) : 0.0);
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) m = fmax(m, __shfl_xor(m, off));
+    const double sc = m > 0.0 ? ldexp(1.0, -ilogb(m)) : 1.0;
+    if (tid == 0) kscale = sc;
     if (tid < 32) {
 #pragma unroll
-      for (int a = 0; a < 32; ++a) K[tid * LD + a] = (a < LM && a <= tid && tid < l) ? g[a < LM ? a : 0] : 0.0;
+      for (int a = 0; a < 32; ++a)
+        K[tid * LD + a] = (a < LM && a <= tid && tid < l) ? static_cast<float>(g[a < LM ? a : 0] * sc) : 0.f;
     }
   }
   __syncthreads();
@@ -422,50 +451,39 @@ __global__ __launch_bounds__(256) void core_small_kernel(const double* __restric
     for (int rnd = 0; rnd < n - 1; ++rnd) {
       if (active) {
         const int p = pa < pb ? pa : pb, q = pa < pb ? pb : pa;
-        double* kp = K + p * LD + sub;
-        double* kq = K + q * LD + sub;
+        float* kp = K + p * LD + sub;
+        float* kq = K + q * LD + sub;
         float* vp = V + p * LD + sub;
         float* vq = V + q * LD + sub;
-        const double xp0 = kp[0], xp1 = kp[16], xq0 = kq[0], xq1 = kq[16];
+        const float xp0 = kp[0], xp1 = kp[16], xq0 = kq[0], xq1 = kq[16];
         const float yp0 = vp[0], yp1 = vp[16], yq0 = vq[0], yq1 = vq[16];
-        double al = fma(xp1, xp1, xp0 * xp0);
-        double be = fma(xq1, xq1, xq0 * xq0);
-        double ga = fma(xp1, xq1, xp0 * xq0);
-        al = group_sum<16>(al);
-        be = group_sum<16>(be);
-        ga = group_sum<16>(ga);
-        const double g2 = ga * ga, ab = al * be;
-        if (q < l && g2 > 1e-14 * ab && ga != 0.0) {
-          // zeta = (be - al) / (2 ga) and t = sgn / (|zeta| + sqrt(1 + zeta^2)) to
-          // ~fp32 accuracy; c = (1 + t^2)^-1/2 with one Newton step on the hardware
-          // estimate (fp64-exact), s = c t.
-          const double w = be - al;
-          const double zeta = 0.5 * w * __builtin_amdgcn_rcp(ga);
-          double t;
-          if (fabs(zeta) > 1e8) {
-            t = ga * __builtin_amdgcn_rcp(w);
-          } else {
-            const float zf = static_cast<float>(fabs(zeta));
-            const float tf = __builtin_amdgcn_rcpf(zf + __builtin_amdgcn_sqrtf(fmaf(zf, zf, 1.0f)));
-            t = zeta >= 0.0 ? static_cast<double>(tf) : -static_cast<double>(tf);
-          }
-          const double u = fma(t, t, 1.0);
-          double c = __builtin_amdgcn_rsq(u);
-          c = c * fma(-0.5 * u * c, c, 1.5);
-          const double s = c * t;
-          const float cf = static_cast<float>(c), sf = static_cast<float>(s);
-          kp[0] = c * xp0 - s * xq0;
-          kq[0] = s * xp0 + c * xq0;
-          kp[16] = c * xp1 - s * xq1;
-          kq[16] = s * xp1 + c * xq1;
-          vp[0] = cf * yp0 - sf * yq0;
-          vq[0] = sf * yp0 + cf * yq0;
-          vp[16] = cf * yp1 - sf * yq1;
-          vq[16] = sf * yp1 + cf * yq1;
-          big |= g2 > 1e-8 * ab;
-        }
+        float al = fmaf(xp1, xp1, xp0 * xp0);
+        float be = fmaf(xq1, xq1, xq0 * xq0);
+        float ga = fmaf(xp1, xq1, xp0 * xq0);
+        al = group_sumf<16>(al);
+        be = group_sumf<16>(be);
+        ga = group_sumf<16>(ga);
+        const float g2 = ga * ga, ab = al * be;
+        // rotation by theta with tan 2 theta = 2 ga / (be - al), |theta| <= pi / 4:
+        // cos 2 theta = |be - al| / h, sin 2 theta = sgn(be - al) 2 ga / h with
+        // h = hypot(be - al, 2 ga); c = sqrt((1 + cos 2 theta) / 2), s = sin 2 theta / (2 c)
+        const bool doit = q < l && g2 > 1e-14f * ab && ga != 0.f;
+        const float dd = be - al;
+        const float ri = __builtin_amdgcn_rsqf(fmaf(dd, dd, 4.f * g2));
+        const float hc = fmaf(0.5f * fabsf(dd), ri, 0.5f);
+        const float c = doit ? __builtin_amdgcn_sqrtf(hc) : 1.f;
+        const float sn = doit ? (dd >= 0.f ? ga : -ga) * ri * __builtin_amdgcn_rsqf(hc) : 0.f;
+        kp[0] = c * xp0 - sn * xq0;
+        kq[0] = sn * xp0 + c * xq0;
+        kp[16] = c * xp1 - sn * xq1;
+        kq[16] = sn * xp1 + c * xq1;
+        vp[0] = c * yp0 - sn * yq0;
+        vq[0] = sn * yp0 + c * yq0;
+        vp[16] = c * yp1 - sn * yq1;
+        vq[16] = sn * yp1 + c * yq1;
+        big |= (doit && g2 > 1e-8f * ab) ? 1 : 0;
       }
-      // advance the circle: players 1 .. n-1 move up one position
+  // advance the circle: players 1 .. n-1 move up one position
       pa = pa == 0 ? 0 : (pa == n - 1 ? 1 : pa + 1);
       pb = pb == 0 ? 0 : (pb == n - 1 ? 1 : pb + 1);
       __syncthreads();
@@ -477,8 +495,8 @@ __global__ __launch_bounds__(256) void core_small_kernel(const double* __restric
   }
   if (tid < l) {
     double s = 0.0;
-    for (int row = 0; row < n; ++row) s += K[tid * LD + row] * K[tid * LD + row];
-    norm2[tid] = s;
+    for (int row = 0; row < n; ++row) s += static_cast<double>(K[tid * LD + row]) * static_cast<double>(K[tid * LD + row]);
+    norm2[tid] = s / (kscale * kscale);
   }
   __syncthreads();
   if (tid < l) {
