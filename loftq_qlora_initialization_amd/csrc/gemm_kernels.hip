@@ -178,13 +178,11 @@ __global__ __launch_bounds__(64 * TnCfg<NT>::WC * TnCfg<NT>::WR) void gemm_tn_ke
   float* red = reinterpret_cast<float*>(lds_raw);
   // LMJ > 0: the extra last column of workgroups carries a Cholesky job; its
   // row 0 sums the Gram partials of Y and factors them (X = R^-1 for the
-  // reduction that follows this product), l <= LMJ
+  // reduction that follows this product), l <= LMJ.  The plan leaves a CU free
+  // for it.
   if constexpr (LMJ > 0) {
     if (blockIdx.x == gridDim.x - 1) {
       if (blockIdx.y == 0) {
-        // a latency-bound serial chain sharing its CU with streaming waves: let
-        // it win instruction arbitration
-        __builtin_amdgcn_s_setprio(3);
         double* lds = reinterpret_cast<double*>(lds_raw);
         const double* gram = gram_sum_block<LMJ>(job.parts, job.P, job.l, lds);
         if (threadIdx.x < 64) chol_inv_to<LMJ>(gram, job.l, job.Xinv, lds);

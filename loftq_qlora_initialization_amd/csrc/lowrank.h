@@ -50,6 +50,7 @@ struct SvdPlan {
   int tn_col_blocks, tn_splits;
   int64_t tn_rper;
   int gram_parts_d, gram_parts_k;
+  bool ride;              // l <= 32 Cholesky rides along with E^T Y (see make_svd_plan)
   int64_t k_pad, d_pad;   // fragment-order panel rows: nn_splits * nn_kper and tn_splits * tn_rper
   int64_t off_omega, off_y, off_z, off_part, off_gram_parts, off_gram_total, off_rinv, off_sb, off_sa;
   int64_t off_stats, off_x;

@@ -858,16 +858,19 @@ SvdPlan make_svd_plan(int64_t d, int64_t k, int r, int oversample, bool exact) {
   // best fills the 256 CUs of the chip -- score = (occupancy of the last wave
   // of workgroups) x min(1, workgroups / 512).
   constexpr int64_t kCUs = 256;
-  auto choose = [&](int64_t tiles, int64_t len, int unit, int64_t& per) {
+  // max_wgs > 0 only admits counts whose grid stays within max_wgs workgroups;
+  // returns 0 if none does.
+  auto choose = [&](int64_t tiles, int64_t len, int unit, int64_t max_wgs, int64_t& per) {
     int64_t cap = (len * 8) / (100 * LP);
     if (cap < 1) cap = 1;
     if (cap > cdiv(len, unit)) cap = cdiv(len, unit);
-    int64_t best_s = 1;
+    int64_t best_s = 0;
     double best = -1.0;
     for (int64_t sp = 1; sp <= cap; ++sp) {
       const int64_t ps = round_up(cdiv(len, sp), unit);
       if (cdiv(len, ps) != sp) continue;   // rounding merges this count into another
       const int64_t wgs = tiles * sp;
+      if (max_wgs > 0 && wgs > max_wgs) continue;
       const double fill = static_cast<double>(wgs) / static_cast<double>(kCUs * cdiv(wgs, kCUs));
       const double busy = wgs >= 2 * kCUs ? 1.0 : static_cast<double>(wgs) / static_cast<double>(2 * kCUs);
       if (fill * busy > best + 1e-9) {
@@ -875,14 +878,29 @@ SvdPlan make_svd_plan(int64_t d, int64_t k, int r, int oversample, bool exact) {
         best_s = sp;
       }
     }
+    if (best_s == 0) return 0;
     per = round_up(cdiv(len, best_s), unit);
     return static_cast<int>(cdiv(len, per));
   };
   const GemmShape nn = gemm_shape(false, p.nt), tn = gemm_shape(true, p.nt);
   p.nn_row_blocks = static_cast<int>(cdiv(d, nn.tile));
-  p.nn_splits = choose(p.nn_row_blocks, k, nn.unit, p.nn_kper);
+  p.nn_splits = choose(p.nn_row_blocks, k, nn.unit, 0, p.nn_kper);
   p.tn_col_blocks = static_cast<int>(cdiv(k, tn.tile));
-  p.tn_splits = choose(p.tn_col_blocks, d, tn.unit, p.tn_rper);
+  p.tn_splits = choose(p.tn_col_blocks, d, tn.unit, 0, p.tn_rper);
+  // The Cholesky that rides along with E^T Y (l <= 32) is a serial chain that
+  // slows several-fold when a streaming workgroup shares its CU, so it rides
+  // only where a split leaves a CU free while still covering at least three
+  // quarters of the chip; otherwise it keeps launches of its own.
+  p.ride = false;
+  if (l <= 32) {
+    int64_t rper = 0;
+    const int sr = choose(p.tn_col_blocks, d, tn.unit, kCUs - 1, rper);
+    if (sr > 0 && p.tn_col_blocks * sr * 4 >= 3 * kCUs) {
+      p.ride = true;
+      p.tn_splits = sr;
+      p.tn_rper = rper;
+    }
+  }
   p.k_pad = p.nn_splits * p.nn_kper;
   p.d_pad = p.tn_splits * p.tn_rper;
   p.gram_parts_d = static_cast<int>(cdiv(d, kGramRows));
@@ -959,7 +977,7 @@ hipError_t run_lowrank(const float* E, const SvdPlan& pl, int q, const float* om
   // For l <= 32 the Cholesky of Y's Gram (mode 1) needs no launch of its own:
   // it rides along with the E^T Y product that always follows, whose split-K
   // reduction is the first consumer of X.
-  const bool ride = l <= 32;
+  const bool ride = pl.ride;
   bool pending = false;
   auto product = [&](bool transposed, const float* panel, int mode) {
     const CholJob job{pending ? gparts : nullptr, pl.gram_parts_d, l, Xinv};
