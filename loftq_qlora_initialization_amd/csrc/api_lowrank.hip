@@ -22,10 +22,14 @@ loftq_status_t check_svd_shape(int64_t rows, int64_t cols, int32_t r, int32_t ov
   return LOFTQ_OK;
 }
 
+// Sketches drawn per launch: alternations t .. t + kSketchBatch - 1 at once.
+constexpr int kSketchBatch = 8;
+
 struct InitPlan {
   SvdPlan svd;
   int nparts;
-  int64_t off_e, off_parts, off_wparts, off_svd, bytes;
+  int64_t sketch_floats;   // one alternation's sketch in fragment order (0 for the exact SVD)
+  int64_t off_e, off_parts, off_wparts, off_sketch, off_svd, bytes;
 };
 
 InitPlan make_init_plan(int64_t rows, int64_t cols, const loftq_config_t& c) {
@@ -33,10 +37,13 @@ InitPlan make_init_plan(int64_t rows, int64_t cols, const loftq_config_t& c) {
   p.svd = make_svd_plan(rows, cols, c.rank, c.oversample, c.exact_svd != 0);
   const int64_t n = rows * cols;
   p.nparts = dequant_num_partials(n);
+  p.sketch_floats = p.svd.exact ? 0 : p.svd.k_pad * 16 * p.svd.nt;
+  const int batch = c.iterative_steps < kSketchBatch ? c.iterative_steps : kSketchBatch;
   int64_t off = 0;
   p.off_e = off;      off += align256(n * 4);
   p.off_parts = off;  off += align256(static_cast<int64_t>(p.nparts) * 8);
   p.off_wparts = off; off += align256(static_cast<int64_t>(p.nparts) * 8);
+  p.off_sketch = off; off += align256(p.sketch_floats * 4 * (batch > 0 ? batch : 0));
   p.off_svd = off;    off += align256(p.svd.bytes);
   p.bytes = off;
   return p;
@@ -75,8 +82,8 @@ loftq_status_t loftq_lowrank_svd(const float* E, int64_t rows, int64_t cols, int
     return LOFTQ_ERR_INVALID_ARG;
   const SvdPlan pl = make_svd_plan(rows, cols, r, oversample, exact != 0);
   if (ws_bytes < static_cast<size_t>(pl.bytes)) return LOFTQ_ERR_WORKSPACE;
-  const ObjectiveArgs none{nullptr, 0, nullptr, 0, nullptr};
-  return from_hip(run_lowrank(E, pl, power_iters, omega, seed, t, B, A, sigma, static_cast<char*>(ws), none,
+  const ObjectiveArgs none{nullptr, 0, nullptr, 0, nullptr, nullptr};
+  return from_hip(run_lowrank(E, pl, power_iters, omega, nullptr, seed, t, B, A, sigma, static_cast<char*>(ws), none,
                               static_cast<hipStream_t>(stream)));
 }
 
@@ -113,18 +120,20 @@ loftq_status_t loftq_init(const void* W, loftq_dtype_t wdt, int64_t rows, int64_
   const int r = cfg->rank;
   const int T = cfg->iterative_steps;
 
-  hipError_t e = launch_sumsq_weight(W, wdt, n, wparts, nullptr, nullptr, s);
-  auto quant_step = [&](const float* Bp, const float* Ap) -> hipError_t {
+  float* sketches = reinterpret_cast<float*>(w + pl.off_sketch);
+  // the first dequant also leaves the partials of ||W||^2 (W is read there anyway)
+  auto quant_step = [&](const float* Bp, const float* Ap, bool first) -> hipError_t {
     hipError_t x = launch_nf4_quantize(W, wdt, rows, cols, Bp, Ap, r, packed, absmax, s);
     if (x == hipSuccess && dq) x = launch_double_quant(absmax, nb, cfg->dq_blocksize, qabsmax, dq_scale, s);
     if (x == hipSuccess)
       x = launch_nf4_dequantize(packed, dq ? nullptr : absmax, dq ? qabsmax : nullptr, dq ? dq_scale : nullptr, n,
-                                cfg->dq_blocksize, W, wdt, E, eparts, nullptr, nullptr, s);
+                                cfg->dq_blocksize, W, wdt, E, eparts, first ? wparts : nullptr, nullptr, s);
     return x;
   };
-  const ObjectiveArgs obj0{eparts, pl.nparts, wparts, pl.nparts, objective};
+  hipError_t e = hipSuccess;
   if (T == 0) {
-    if (e == hipSuccess) e = quant_step(nullptr, nullptr);
+    const ObjectiveArgs obj0{eparts, pl.nparts, wparts, pl.nparts, objective, nullptr};
+    if (e == hipSuccess) e = quant_step(nullptr, nullptr, true);
     if (e == hipSuccess) e = run_objective(obj0, s);
     if (e == hipSuccess) e = run_fill(B, rows * r, 0.f, s);
     if (e == hipSuccess) e = run_fill(A, static_cast<int64_t>(r) * cols, 0.f, s);
@@ -132,11 +141,20 @@ loftq_status_t loftq_init(const void* W, loftq_dtype_t wdt, int64_t rows, int64_
     return from_hip(e);
   }
   for (int t = 1; t <= T && e == hipSuccess; ++t) {
-    e = quant_step(t == 1 ? nullptr : B, t == 1 ? nullptr : A);
-    if (e == hipSuccess && t == 1) e = run_objective(obj0, s);
-    const ObjectiveArgs objt{eparts, pl.nparts, wparts, pl.nparts, objective + t};
+    e = quant_step(t == 1 ? nullptr : B, t == 1 ? nullptr : A, t == 1);
+    // alternation 1's solve also writes objective[0] (the error of plain NF4)
+    const ObjectiveArgs objt{eparts, pl.nparts, wparts, pl.nparts, objective + t, t == 1 ? objective : nullptr};
+    const float* om = nullptr;
+    if (pl.sketch_floats > 0) {
+      const int slot = (t - 1) % kSketchBatch;
+      if (slot == 0 && e == hipSuccess) {
+        const int count = (T - t + 1) < kSketchBatch ? (T - t + 1) : kSketchBatch;
+        e = run_sketch(cfg->seed, t, count, cols, pl.svd.l, pl.svd.nt, pl.svd.k_pad, sketches, s);
+      }
+      om = sketches + slot * pl.sketch_floats;
+    }
     if (e == hipSuccess)
-      e = run_lowrank(E, pl.svd, cfg->power_iters, nullptr, cfg->seed, t, B, A, sigma, svd_ws, objt, s);
+      e = run_lowrank(E, pl.svd, cfg->power_iters, nullptr, om, cfg->seed, t, B, A, sigma, svd_ws, objt, s);
   }
   return from_hip(e);
 }

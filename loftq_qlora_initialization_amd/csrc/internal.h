@@ -73,10 +73,10 @@ hipError_t launch_double_quant(const float* absmax, int64_t nblocks, int dqbs, i
 // Sum of squares of the output: with `partials`, one fp64 partial per workgroup
 // (dequant_num_partials(n) of them, summed in a fixed order by the consumer);
 // otherwise, with `sumsq`, accumulated into *sumsq with atomics (after zeroing it).
-// `counter` is unused.
+// With W and `wpartials`, the same per-workgroup partials of sum W^2 as well.
 hipError_t launch_nf4_dequantize(const uint8_t* packed, const float* absmax, const int8_t* q,
                                  const float* dqscale, int64_t n, int dqbs, const void* W,
-                                 loftq_dtype_t wdt, float* out, double* partials, unsigned* counter,
+                                 loftq_dtype_t wdt, float* out, double* partials, double* wpartials,
                                  double* sumsq, hipStream_t s);
 int dequant_num_partials(int64_t n);
 hipError_t launch_sumsq_weight(const void* W, loftq_dtype_t wdt, int64_t n, double* partials, unsigned* counter,

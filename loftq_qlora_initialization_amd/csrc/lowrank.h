@@ -14,13 +14,15 @@ constexpr int kPanelRows = 64;   // rows per workgroup (and Gram partial) of the
 
 // Where the objective of an alternation goes: ||E||^2 and ||W||^2 arrive as
 // per-workgroup partial sums (summed in a fixed order by the consumer);
-// out = sqrt(max(||E||^2 - sum sigma^2, 0) / ||W||^2).
+// out = sqrt(max(||E||^2 - sum sigma^2, 0) / ||W||^2), and, when out0 is set,
+// out0 = sqrt(||E||^2 / ||W||^2) (the plain-quantization error before any refit).
 struct ObjectiveArgs {
   const double* e_parts;
   int ne;
   const double* w_parts;
   int nw;
   double* out;
+  double* out0;
 };
 
 // Skinny panels that feed the thin products as their B operand (the sketch,
@@ -58,9 +60,14 @@ struct SvdPlan {
 };
 
 SvdPlan make_svd_plan(int64_t d, int64_t k, int r, int oversample, bool exact);
-hipError_t run_lowrank(const float* E, const SvdPlan& pl, int q, const float* omega, uint64_t seed, int t, float* B,
-                       float* A, float* sigma, char* ws, const ObjectiveArgs& obj, hipStream_t s);
-hipError_t run_sketch(uint64_t seed, int t, int64_t k, int l, int nt, int64_t rows, float* out, hipStream_t s);
+// omega: caller's k x l sketch (row-major), or omega_frag: a sketch already in
+// fragment order over k_pad rows, or neither: the sketch of alternation t is drawn.
+hipError_t run_lowrank(const float* E, const SvdPlan& pl, int q, const float* omega, const float* omega_frag,
+                       uint64_t seed, int t, float* B, float* A, float* sigma, char* ws, const ObjectiveArgs& obj,
+                       hipStream_t s);
+// Sketches of alternations t .. t + count - 1, each rows x 16 nt floats in fragment order, back to back.
+hipError_t run_sketch(uint64_t seed, int t, int count, int64_t k, int l, int nt, int64_t rows, float* out,
+                      hipStream_t s);
 hipError_t run_fill(float* p, int64_t n, float v, hipStream_t s);
 hipError_t run_objective(const ObjectiveArgs& obj, hipStream_t s);
 GemmShape gemm_shape(bool transposed, int nt);

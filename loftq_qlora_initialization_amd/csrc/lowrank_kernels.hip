@@ -31,9 +31,11 @@ namespace {
 // Element (i, j) of the k x l test matrix of alternation t is drawn from
 // counter ((t - 1) k + i) l + j; written in fragment order over `rows` rows
 // (zero beyond k and l).
-__global__ void sketch_kernel(uint64_t seed, int t, int64_t k, int l, int nt, int64_t rows, float* __restrict__ out) {
+__global__ void sketch_kernel(uint64_t seed, int t0, int64_t k, int l, int nt, int64_t rows, float* __restrict__ out) {
   const int64_t idx = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
   if (idx >= rows * 16 * nt) return;
+  const int t = t0 + static_cast<int>(blockIdx.y);   // one sketch per grid row
+  out += static_cast<int64_t>(blockIdx.y) * rows * 16 * nt;
   const int64_t blk = idx / (256 * nt);
   const int e = static_cast<int>(idx - blk * 256 * nt);
   const int tile = e >> 8, f = e & 255;
@@ -114,6 +116,7 @@ __device__ void write_objective(const ObjectiveArgs& o, double sig2) {
   if (threadIdx.x == 0) {
     const double num = es - sig2;
     *o.out = ws > 0.0 ? sqrt((num > 0.0 ? num : 0.0) / ws) : 0.0;
+    if (o.out0 != nullptr) *o.out0 = ws > 0.0 ? sqrt(es / ws) : 0.0;
   }
 }
 
@@ -630,14 +633,27 @@ __global__ __launch_bounds__(kReduceThreads) void reduce_gram_kernel(const float
 // ---------------------------------------------------------------------------
 // Panel times small matrix: out = P S (m x w) or its transpose (w x m), with P
 // an m x l panel in fragment order (nt tiles) and S l x w.  64 rows of P and all
-// of S are staged in LDS.  Serves the factor products B = Q S_B and
-// A = (C S_A)^T.
-__global__ __launch_bounds__(256) void panel_small_kernel(const float* __restrict__ P, int64_t m, int l, int nt,
-                                                          const float* __restrict__ S, int w,
-                                                          float* __restrict__ out, int transpose_out) {
+// of S are staged in LDS.  One launch serves both factor products: workgroups
+// [0, nb0) take job 0 (B = Q S_B) and the rest job 1 (A = (C S_A)^T).
+struct PanelJob {
+  const float* P;
+  int64_t m;
+  const float* S;
+  float* out;
+  int transpose_out;
+};
+
+__global__ __launch_bounds__(256) void panel_small_kernel(PanelJob j0, PanelJob j1, int nb0, int l, int nt, int w) {
   __shared__ float Ps[kPanelRows * (kMaxL + 1)];
   __shared__ float Ss[kMaxL * kMaxL];
-  const int64_t r0 = static_cast<int64_t>(blockIdx.x) * kPanelRows;
+  const bool second = static_cast<int>(blockIdx.x) >= nb0;
+  const PanelJob& jb = second ? j1 : j0;
+  const float* __restrict__ P = jb.P;
+  const float* __restrict__ S = jb.S;
+  float* __restrict__ out = jb.out;
+  const int64_t m = jb.m;
+  const int transpose_out = jb.transpose_out;
+  const int64_t r0 = static_cast<int64_t>(second ? blockIdx.x - nb0 : blockIdx.x) * kPanelRows;
   const int ldp = l + 1;
   for (int idx = threadIdx.x; idx < kPanelRows * l; idx += blockDim.x) {
     const int rr = idx / l, a = idx - rr * l;
@@ -827,9 +843,9 @@ void launch_small_wave(int mode, const double* gram, int l, float* Xinv, int r, 
   else small_wave_typed<32>(mode, gram, l, Xinv, r, SB, SA, sigma, stats, obj, s);
 }
 
-void panel_small(const float* P, int64_t m, int l, int nt, const float* S, int w, float* out, bool tr, hipStream_t s) {
-  const int blocks = static_cast<int>(cdiv(m, kPanelRows));
-  LQ_LAUNCH("panel_small", panel_small_kernel, dim3(blocks), dim3(256), 0, s, P, m, l, nt, S, w, out, tr ? 1 : 0);
+void panels(const PanelJob& j0, const PanelJob& j1, int l, int nt, int w, hipStream_t s) {
+  const int nb0 = static_cast<int>(cdiv(j0.m, kPanelRows)), nb1 = static_cast<int>(cdiv(j1.m, kPanelRows));
+  LQ_LAUNCH("panel_small", panel_small_kernel, dim3(nb0 + nb1), dim3(256), 0, s, j0, j1, nb0, l, nt, w);
 }
 
 }  // namespace
@@ -922,10 +938,11 @@ SvdPlan make_svd_plan(int64_t d, int64_t k, int r, int oversample, bool exact) {
   return p;
 }
 
-hipError_t run_sketch(uint64_t seed, int t, int64_t k, int l, int nt, int64_t rows, float* out, hipStream_t s) {
+hipError_t run_sketch(uint64_t seed, int t, int count, int64_t k, int l, int nt, int64_t rows, float* out,
+                      hipStream_t s) {
   const int64_t n = rows * 16 * nt;
-  LQ_LAUNCH("sketch", sketch_kernel, dim3(static_cast<unsigned>(cdiv(n, 256))), dim3(256), 0, s, seed, t, k, l, nt,
-            rows, out);
+  LQ_LAUNCH("sketch", sketch_kernel, dim3(static_cast<unsigned>(cdiv(n, 256)), static_cast<unsigned>(count)), dim3(256),
+            0, s, seed, t, k, l, nt, rows, out);
   return hipGetLastError();
 }
 
@@ -940,8 +957,9 @@ hipError_t run_objective(const ObjectiveArgs& obj, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t run_lowrank(const float* E, const SvdPlan& pl, int q, const float* omega, uint64_t seed, int t, float* B,
-                       float* A, float* sigma, char* ws, const ObjectiveArgs& obj, hipStream_t s) {
+hipError_t run_lowrank(const float* E, const SvdPlan& pl, int q, const float* omega, const float* omega_frag,
+                       uint64_t seed, int t, float* B, float* A, float* sigma, char* ws, const ObjectiveArgs& obj,
+                       hipStream_t s) {
   const int64_t d = pl.d, k = pl.k;
   const int r = pl.r, l = pl.l;
   if (pl.exact) {
@@ -950,7 +968,8 @@ hipError_t run_lowrank(const float* E, const SvdPlan& pl, int q, const float* om
               reinterpret_cast<double*>(ws + pl.off_stats), obj);
     return hipGetLastError();
   }
-  float* Om = reinterpret_cast<float*>(ws + pl.off_omega);
+  const float* Om = omega_frag != nullptr ? omega_frag : reinterpret_cast<float*>(ws + pl.off_omega);
+  float* Om_ws = reinterpret_cast<float*>(ws + pl.off_omega);
   float* Y = reinterpret_cast<float*>(ws + pl.off_y);
   float* Z = reinterpret_cast<float*>(ws + pl.off_z);
   float* part = reinterpret_cast<float*>(ws + pl.off_part);
@@ -959,14 +978,15 @@ hipError_t run_lowrank(const float* E, const SvdPlan& pl, int q, const float* om
   float* SB = reinterpret_cast<float*>(ws + pl.off_sb);
   float* SA = reinterpret_cast<float*>(ws + pl.off_sa);
   double* stats = reinterpret_cast<double*>(ws + pl.off_stats);
-  const ObjectiveArgs none{nullptr, 0, nullptr, 0, nullptr};
+  const ObjectiveArgs none{nullptr, 0, nullptr, 0, nullptr, nullptr};
   const int64_t nfrag = pl.k_pad * 16 * pl.nt;
-  if (omega == nullptr) {
-    hipError_t e = run_sketch(seed, t, k, l, pl.nt, pl.k_pad, Om, s);
-    if (e != hipSuccess) return e;
-  } else {
+  if (omega != nullptr) {
     LQ_LAUNCH("to_frag", to_frag_kernel, dim3(static_cast<unsigned>(cdiv(nfrag, 256))), dim3(256), 0, s, omega, k, l,
-              pl.nt, pl.k_pad, Om);
+              pl.nt, pl.k_pad, Om_ws);
+    Om = Om_ws;
+  } else if (omega_frag == nullptr) {
+    hipError_t e = run_sketch(seed, t, 1, k, l, pl.nt, pl.k_pad, Om_ws, s);
+    if (e != hipSuccess) return e;
   }
   double* gtotal = reinterpret_cast<double*>(ws + pl.off_gram_total);
   const int E_ = l * (l + 1) / 2;
@@ -1010,8 +1030,7 @@ hipError_t run_lowrank(const float* E, const SvdPlan& pl, int q, const float* om
   }
   // C = E^T Q = (E^T Y) X, then the core solve on C^T C
   product(true, Y, 2);
-  panel_small(Y, d, l, pl.nt, SB, r, B, false, s);
-  panel_small(Z, k, l, pl.nt, SA, r, A, true, s);
+  panels(PanelJob{Y, d, SB, B, 0}, PanelJob{Z, k, SA, A, 1}, l, pl.nt, r, s);
   return hipGetLastError();
 }
 

@@ -388,15 +388,17 @@ __global__ __launch_bounds__(kThreads) void dequant_kernel(const uint8_t* __rest
                                                            const float* __restrict__ dqs, int dqbs, int64_t n,
                                                            const T* __restrict__ W, float* __restrict__ out,
                                                            double* __restrict__ partials,
+                                                           double* __restrict__ wpartials,
                                                            double* __restrict__ sumsq, Nf4Tables tab) {
   __shared__ float lvl[16];
-  __shared__ double red[kThreads / 64];
+  __shared__ double red[2 * (kThreads / 64)];
+  const bool wsum = kHasW && wpartials != nullptr;
   if (threadIdx.x < 16) lvl[threadIdx.x] = tab.level[threadIdx.x];
   __syncthreads();
   const int lane = threadIdx.x & 63;
   const int64_t nslices = n >> 10;
   const int64_t nwaves = static_cast<int64_t>(gridDim.x) * (kThreads / 64);
-  double acc = 0.0;
+  double acc = 0.0, wacc = 0.0;
   for (int64_t sl = (static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x) >> 6; sl < nslices; sl += nwaves) {
     const int64_t base = (sl << 10) + 4 * lane;
     uint32_t cw[4];
@@ -408,7 +410,7 @@ __global__ __launch_bounds__(kThreads) void dequant_kernel(const uint8_t* __rest
       a[q] = block_scale<kDQ>(absmax, qa, dqs, dqbs, e >> 6);
       if (kHasW) load4(W + e, w[q]);
     }
-    float ss = 0.f;
+    float ss = 0.f, ws = 0.f;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       float o[4];
@@ -418,10 +420,12 @@ __global__ __launch_bounds__(kThreads) void dequant_kernel(const uint8_t* __rest
         const float d = lvl[code] * a[q];
         o[j] = kHasW ? (w[q][j] - d) : d;
         ss = fmaf(o[j], o[j], ss);
+        if (kHasW) ws = fmaf(w[q][j], w[q][j], ws);
       }
       *reinterpret_cast<float4*>(out + base + 256 * q) = make_float4(o[0], o[1], o[2], o[3]);
     }
     acc += static_cast<double>(ss);
+    wacc += static_cast<double>(ws);
   }
   // ragged end: whole groups of 16 by the threads of workgroup 0, then the last
   // few elements by its thread 0
@@ -430,38 +434,54 @@ __global__ __launch_bounds__(kThreads) void dequant_kernel(const uint8_t* __rest
     for (int64_t g = (nslices << 6) + threadIdx.x; g < ngroups; g += kThreads) {
       const float sc = block_scale<kDQ>(absmax, qa, dqs, dqbs, g >> 2);
       const uint2 pw = reinterpret_cast<const uint2*>(packed)[g];
-      float ss = 0.f;
+      float ss = 0.f, ws = 0.f;
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         const uint32_t code = (((e < 8) ? pw.x : pw.y) >> nib_shift(e)) & 0xFu;
         const float d = lvl[code] * sc;
-        const float o = kHasW ? (load1(W, g * 16 + e) - d) : d;
+        const float wv = kHasW ? load1(W, g * 16 + e) : 0.f;
+        const float o = kHasW ? (wv - d) : d;
         out[g * 16 + e] = o;
         ss = fmaf(o, o, ss);
+        ws = fmaf(wv, wv, ws);
       }
       acc += static_cast<double>(ss);
+      wacc += static_cast<double>(ws);
     }
     if (threadIdx.x == 0) {
-      float ss = 0.f;
+      float ss = 0.f, ws = 0.f;
       for (int64_t i = ngroups * 16; i < n; ++i) {
         const float sc = block_scale<kDQ>(absmax, qa, dqs, dqbs, i >> 6);
         const uint32_t code = (packed[i >> 1] >> ((i & 1) ? 0 : 4)) & 0xFu;
         const float d = lvl[code] * sc;
-        const float o = kHasW ? (load1(W, i) - d) : d;
+        const float wv = kHasW ? load1(W, i) : 0.f;
+        const float o = kHasW ? (wv - d) : d;
         out[i] = o;
         ss = fmaf(o, o, ss);
+        ws = fmaf(wv, wv, ws);
       }
       acc += static_cast<double>(ss);
+      wacc += static_cast<double>(ws);
     }
   }
-  for (int off = 32; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = acc;
+  for (int off = 32; off > 0; off >>= 1) {
+    acc += __shfl_xor(acc, off);
+    if (wsum) wacc += __shfl_xor(wacc, off);
+  }
+  if ((threadIdx.x & 63) == 0) {
+    red[threadIdx.x >> 6] = acc;
+    red[kThreads / 64 + (threadIdx.x >> 6)] = wacc;
+  }
   __syncthreads();
-  double t = 0.0;
-  for (int i = 0; i < kThreads / 64; ++i) t += red[i];
+  double t = 0.0, tw = 0.0;
+  for (int i = 0; i < kThreads / 64; ++i) {
+    t += red[i];
+    tw += red[kThreads / 64 + i];
+  }
   if (threadIdx.x == 0) {
     if (partials != nullptr) partials[blockIdx.x] = t;
     else if (sumsq != nullptr) atomicAdd(sumsq, t);
+    if (wsum) wpartials[blockIdx.x] = tw;
   }
 }
 
@@ -558,7 +578,7 @@ hipError_t quantize_typed(const T* W, int64_t rows, int64_t cols, const float* B
 
 template <typename T>
 hipError_t dequant_typed(const uint8_t* packed, const float* absmax, const int8_t* q, const float* dqs, int64_t n,
-                         int dqbs, const T* W, float* out, double* partials, unsigned* counter, double* sumsq,
+                         int dqbs, const T* W, float* out, double* partials, double* wpartials, double* sumsq,
                          hipStream_t s) {
   const Nf4Tables& tab = nf4_tables();
   const int grid = dequant_num_partials(n);
@@ -566,7 +586,7 @@ hipError_t dequant_typed(const uint8_t* packed, const float* absmax, const int8_
   const bool dq = q != nullptr;
 #define LQ_DEQ(HW, DQ)                                                                                            \
   LQ_LAUNCH("nf4_dequantize", (dequant_kernel<T, HW, DQ>), dim3(grid), dim3(kThreads), 0, s, packed, absmax, q,   \
-            dqs, dqbs, n, W, out, partials, sumsq, tab)
+            dqs, dqbs, n, W, out, partials, wpartials, sumsq, tab)
   if (W != nullptr) {
     if (dq) LQ_DEQ(true, true); else LQ_DEQ(true, false);
   } else {
@@ -601,15 +621,15 @@ hipError_t launch_double_quant(const float* absmax, int64_t nblocks, int dqbs, i
 
 hipError_t launch_nf4_dequantize(const uint8_t* packed, const float* absmax, const int8_t* q, const float* dqscale,
                                  int64_t n, int dqbs, const void* W, loftq_dtype_t wdt, float* out, double* partials,
-                                 unsigned* counter, double* sumsq, hipStream_t s) {
+                                 double* wpartials, double* sumsq, hipStream_t s) {
   if (n == 0) {
     if (sumsq) LQ_LAUNCH("zero", zero_double_kernel, dim3(1), dim3(1), 0, s, sumsq);
     return hipGetLastError();
   }
   if (wdt == LOFTQ_BF16)
-    return dequant_typed(packed, absmax, q, dqscale, n, dqbs, static_cast<const uint16_t*>(W), out, partials, counter,
-                         sumsq, s);
-  return dequant_typed(packed, absmax, q, dqscale, n, dqbs, static_cast<const float*>(W), out, partials, counter,
+    return dequant_typed(packed, absmax, q, dqscale, n, dqbs, static_cast<const uint16_t*>(W), out, partials,
+                         wpartials, sumsq, s);
+  return dequant_typed(packed, absmax, q, dqscale, n, dqbs, static_cast<const float*>(W), out, partials, wpartials,
                        sumsq, s);
 }
 
