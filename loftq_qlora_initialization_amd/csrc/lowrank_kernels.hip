@@ -529,6 +529,196 @@ __global__ __launch_bounds__(256) void core_small_kernel(const double* __restric
   write_objective(obj, s2);
 }
 
+// ---------------------------------------------------------------------------
+// The two solves for 32 < l <= kMaxL, by one workgroup of kWideThreads = 640
+// threads (pair i of a Jacobi round on lanes 16 i .. 16 i + 15).
+//
+// chol_lds: right-looking Cholesky of the fp64 Gram held (full, symmetric) in
+// LDS, one barrier per column.  Step j: every thread reads the pivot itself;
+// the trailing block loses the outer product of row j (unscaled, times the
+// pivot's inverse); the scaled row j of R goes to Rm when given (a separate
+// array, so no thread overwrites what another still reads).  With T given, the same steps
+// build X = R^-1 the way chol_wave does (rows of T = R^-T), writing each
+// finished row of T straight into X's column.
+constexpr int kWideThreads = 640;
+constexpr int kWideLd = kMaxL + 1;
+
+__device__ void chol_lds(double* G, double* Rm, double* T, float* X, int l, double* scratch) {
+  const int tid = threadIdx.x, nt = blockDim.x;
+  if (tid < 64) {
+    double m = 0.0;
+    for (int a = tid; a < l; a += 64) m = fmax(m, G[a * kWideLd + a]);
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) m = fmax(m, __shfl_xor(m, off));
+    if (tid == 0) scratch[0] = m;
+  }
+  __syncthreads();
+  const double tol = 1e-13 * scratch[0];
+  for (int j = 0; j < l; ++j) {
+    const double piv = G[j * kWideLd + j];
+    const bool keep = piv > tol && piv > 0.0;
+    const double inv = keep ? rsq_f64(piv) : 0.0;   // 1 / R[j][j]
+    const int tail = l - 1 - j;
+    // trailing update G[a][b] -= R[j][a] R[j][b], a, b > j (both triangles)
+    for (int e = tid; e < tail * tail; e += nt) {
+      const int a = j + 1 + e / tail, b = j + 1 + e % tail;
+      G[a * kWideLd + b] = fma(-(G[j * kWideLd + a] * inv), G[j * kWideLd + b] * inv, G[a * kWideLd + b]);
+    }
+    // row j of R (when wanted)
+    if (Rm != nullptr)
+      for (int b = j + tid; b < l; b += nt) Rm[j * kWideLd + b] = (b == j) ? piv * inv : G[j * kWideLd + b] * inv;
+    if (T != nullptr) {
+      // T[j] is final after this step (scaled by inv); rows a > j lose R[j][a] T[j]
+      for (int e = tid; e < (tail + 1) * (j + 1); e += nt) {
+        const int ar = e / (j + 1), c = e % (j + 1);
+        const int a = j + ar;
+        const double tj = T[j * kWideLd + c] * inv;
+        if (ar == 0) X[c * l + j] = static_cast<float>(tj);   // X = T^T
+        else T[a * kWideLd + c] = fma(-(G[j * kWideLd + a] * inv), tj, T[a * kWideLd + c]);
+      }
+    }
+    __syncthreads();
+  }
+}
+
+template <int MODE>
+__global__ __launch_bounds__(kWideThreads) void solve_wide_kernel(const double* __restrict__ gram, int l,
+                                                                  float* __restrict__ Xinv, int r,
+                                                                  float* __restrict__ SB, float* __restrict__ SA,
+                                                                  float* __restrict__ sigma, double* __restrict__ stats,
+                                                                  ObjectiveArgs obj) {
+  constexpr int NB = kMaxL * kWideLd;
+  __shared__ double G[NB];
+  __shared__ double Rm[NB];
+  __shared__ float Kf[MODE == 2 ? NB : 1];
+  __shared__ float V[MODE == 2 ? NB : 1];
+  __shared__ double norm2[kMaxL];
+  __shared__ int order[kMaxL];
+  __shared__ double scratch[2];
+  const int tid = threadIdx.x, nt = blockDim.x;
+  for (int e = tid; e < l * l; e += nt) {
+    const int a = e / l, b = e - a * l;
+    G[a * kWideLd + b] = (a <= b) ? gram[packed_index(a, b, l)] : gram[packed_index(b, a, l)];
+  }
+  if (MODE == 1) {
+    // Rm doubles as T (identity to start); R itself is not needed for X
+    for (int e = tid; e < NB; e += nt) Rm[e] = 0.0;
+    __syncthreads();
+    for (int a = tid; a < l; a += nt) Rm[a * kWideLd + a] = 1.0;
+    for (int e = tid; e < l * l; e += nt) Xinv[e] = 0.f;
+    __syncthreads();
+    chol_lds(G, nullptr, Rm, Xinv, l, scratch);
+    return;
+  }
+  __syncthreads();
+  chol_lds(G, Rm, nullptr, nullptr, l, scratch);
+  // K = 2^-e R (column c of K = column c of R), fp32, with 2^e at the scale of R's largest entry
+  if (tid < 64) {
+    double m = 0.0;
+    for (int a = tid; a < l; a += 64) m = fmax(m, fabs(Rm[a * kWideLd + a]));
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) m = fmax(m, __shfl_xor(m, off));
+    if (tid == 0) scratch[1] = m > 0.0 ? ldexp(1.0, -ilogb(m)) : 1.0;
+  }
+  __syncthreads();
+  const double ksc = scratch[1];
+  const int n = l + (l & 1);
+  for (int e = tid; e < kMaxL * kWideLd; e += nt) {
+    const int c = e / kWideLd, row = e - c * kWideLd;
+    Kf[e] = (c < l && row <= c) ? static_cast<float>(Rm[row * kWideLd + c] * ksc) : 0.f;
+    V[e] = (row == c) ? 1.f : 0.f;
+  }
+  __syncthreads();
+  // one-sided Jacobi, fp32, 16 lanes per pair (rows sub + 16 i)
+  constexpr int RL = (kMaxL + 15) / 16;
+  const int pair = tid >> 4, sub = tid & 15;
+  const bool active = pair < n / 2;
+  int pa = pair, pb = n - 1 - pair;
+  int sweeps = 0;
+  for (int sweep = 0; sweep < 40; ++sweep) {
+    int big = 0;
+    for (int rnd = 0; rnd < n - 1; ++rnd) {
+      if (active) {
+        const int p = pa < pb ? pa : pb, q = pa < pb ? pb : pa;
+        float* kp = Kf + p * kWideLd + sub;
+        float* kq = Kf + q * kWideLd + sub;
+        float* vp = V + p * kWideLd + sub;
+        float* vq = V + q * kWideLd + sub;
+        float xp[RL], xq[RL], yp[RL], yq[RL];
+        float al = 0.f, be = 0.f, ga = 0.f;
+#pragma unroll
+        for (int i = 0; i < RL; ++i) {
+          const bool in = sub + 16 * i < n;
+          xp[i] = in ? kp[16 * i] : 0.f;
+          xq[i] = in ? kq[16 * i] : 0.f;
+          yp[i] = in ? vp[16 * i] : 0.f;
+          yq[i] = in ? vq[16 * i] : 0.f;
+          al = fmaf(xp[i], xp[i], al);
+          be = fmaf(xq[i], xq[i], be);
+          ga = fmaf(xp[i], xq[i], ga);
+        }
+        al = group_sumf<16>(al);
+        be = group_sumf<16>(be);
+        ga = group_sumf<16>(ga);
+        const float g2 = ga * ga, ab = al * be;
+        const bool doit = q < l && g2 > 1e-14f * ab && ga != 0.f;
+        const float dd = be - al;
+        const float ri = __builtin_amdgcn_rsqf(fmaf(dd, dd, 4.f * g2));
+        const float hc = fmaf(0.5f * fabsf(dd), ri, 0.5f);
+        const float c = doit ? __builtin_amdgcn_sqrtf(hc) : 1.f;
+        const float sn = doit ? (dd >= 0.f ? ga : -ga) * ri * __builtin_amdgcn_rsqf(hc) : 0.f;
+#pragma unroll
+        for (int i = 0; i < RL; ++i) {
+          if (sub + 16 * i < n) {
+            kp[16 * i] = c * xp[i] - sn * xq[i];
+            kq[16 * i] = sn * xp[i] + c * xq[i];
+            vp[16 * i] = c * yp[i] - sn * yq[i];
+            vq[16 * i] = sn * yp[i] + c * yq[i];
+          }
+        }
+        big |= (doit && g2 > 1e-8f * ab) ? 1 : 0;
+      }
+      pa = pa == 0 ? 0 : (pa == n - 1 ? 1 : pa + 1);
+      pb = pb == 0 ? 0 : (pb == n - 1 ? 1 : pb + 1);
+      __syncthreads();
+    }
+    sweeps = sweep + 1;
+    if (!__syncthreads_or(big)) break;
+  }
+  if (tid < l) {
+    double sum = 0.0;
+    for (int row = 0; row < n; ++row)
+      sum += static_cast<double>(Kf[tid * kWideLd + row]) * static_cast<double>(Kf[tid * kWideLd + row]);
+    norm2[tid] = sum / (ksc * ksc);
+  }
+  __syncthreads();
+  if (tid < l) {
+    const double la = norm2[tid];
+    int rank = 0;
+    for (int b = 0; b < l; ++b) rank += (norm2[b] > la || (norm2[b] == la && b < tid)) ? 1 : 0;
+    order[rank] = tid;
+  }
+  __syncthreads();
+  for (int idx = tid; idx < l * r; idx += nt) {
+    const int row = idx / r, c = idx - row * r;
+    const int a = order[c];
+    const double sg = sqrt(norm2[a]);
+    const double sq = sqrt(sg);
+    double acc = 0.0;
+    for (int j = row; j < l; ++j) acc = fma(static_cast<double>(Xinv[row * l + j]), static_cast<double>(V[a * kWideLd + j]), acc);
+    SB[row * r + c] = static_cast<float>(acc * sq);
+    SA[row * r + c] = sg > 0.0 ? static_cast<float>(V[a * kWideLd + row] / sq) : 0.f;
+  }
+  if (tid < r) sigma[tid] = static_cast<float>(sqrt(norm2[order[tid]]));
+  double s2 = 0.0;
+  for (int c = 0; c < r; ++c) s2 += norm2[order[c]];
+  if (tid == 0 && stats) {
+    stats[0] = s2;
+    stats[1] = static_cast<double>(sweeps);
+  }
+  write_objective(obj, s2);
+}
+
 // Sum of the split-K partials, sum_s part[s], in fixed order for a tile of
 // kGramRows rows, optionally right-multiplied by X (l x l fp32, upper
 // triangular; entries below the diagonal are ignored), written in fragment
@@ -541,6 +731,9 @@ __global__ __launch_bounds__(kReduceThreads) void reduce_gram_kernel(const float
                                                           int64_t m_pad, int l, const float* __restrict__ X,
                                                           float* __restrict__ out, double* __restrict__ gram_parts) {
   constexpr int LP = 16 * NT, PER = (kGramRows * LP + kReduceThreads - 1) / kReduceThreads, LDR = LP + 1;
+  // wide panels (NT >= 3) keep fewer loads in flight and unroll less, so the
+  // per-thread state fits the register file of a 512-thread workgroup
+  constexpr int QB = NT <= 2 ? 4 : 2, JU = NT <= 2 ? LP : 16, RU = NT <= 2 ? kGramRows : 16;
   __shared__ float rows[kGramRows * LDR];
   __shared__ float Xs[LP * LP];
   const int64_t r0 = static_cast<int64_t>(blockIdx.x) * kGramRows;
@@ -551,35 +744,34 @@ __global__ __launch_bounds__(kReduceThreads) void reduce_gram_kernel(const float
       Xs[e] = (a <= b && b < l) ? X[a * l + b] : 0.f;
     }
   }
-  // every thread sums its PER elements over the S partials, four partials of
-  // all its elements in flight at a time, each element in ascending s order
+  // every thread sums its PER elements over the S partials, QB partials of all
+  // its elements in flight at a time, each element in ascending s order
   float acc[PER];
-  int64_t off[PER];
-  bool ok[PER];
+  int off[PER];   // row offset within the tile times LP plus column; -1: nothing to load
 #pragma unroll
   for (int u = 0; u < PER; ++u) {
     const int idx = threadIdx.x + kReduceThreads * u;
     const int rr = idx / LP, n = idx - rr * LP;
-    const int64_t row = r0 + rr;
-    ok[u] = idx < kGramRows * LP && row < m && n < l;
-    off[u] = ok[u] ? row * LP + n : 0;
+    const bool ok = idx < kGramRows * LP && r0 + rr < m && n < l;
+    off[u] = ok ? idx : -1;
     acc[u] = 0.f;
   }
+  const float* base = part + r0 * LP;
   int p = 0;
-  for (; p + 4 <= S; p += 4) {
-    float v[4][PER];
+  for (; p + QB <= S; p += QB) {
+    float v[QB][PER];
 #pragma unroll
-    for (int q = 0; q < 4; ++q)
+    for (int q = 0; q < QB; ++q)
 #pragma unroll
-      for (int u = 0; u < PER; ++u) v[q][u] = ok[u] ? part[(p + q) * stride + off[u]] : 0.f;
+      for (int u = 0; u < PER; ++u) v[q][u] = off[u] >= 0 ? base[(p + q) * stride + off[u]] : 0.f;
 #pragma unroll
-    for (int q = 0; q < 4; ++q)
+    for (int q = 0; q < QB; ++q)
 #pragma unroll
       for (int u = 0; u < PER; ++u) acc[u] += v[q][u];
   }
   for (; p < S; ++p)
 #pragma unroll
-    for (int u = 0; u < PER; ++u) acc[u] += ok[u] ? part[p * stride + off[u]] : 0.f;
+    for (int u = 0; u < PER; ++u) acc[u] += off[u] >= 0 ? base[p * stride + off[u]] : 0.f;
 #pragma unroll
   for (int u = 0; u < PER; ++u) {
     const int idx = threadIdx.x + kReduceThreads * u;
@@ -587,23 +779,23 @@ __global__ __launch_bounds__(kReduceThreads) void reduce_gram_kernel(const float
   }
   __syncthreads();
   if (X) {
-    float t[PER];
+    // the products go back into acc (all reads of `rows` finish before the barrier)
 #pragma unroll
     for (int u = 0; u < PER; ++u) {
       const int idx = threadIdx.x + kReduceThreads * u;
       float a = 0.f;
       if (idx < kGramRows * LP) {
         const int rr = idx / LP, n = idx - rr * LP;
-#pragma unroll
+#pragma unroll JU
         for (int j = 0; j < LP; ++j) a = fmaf(rows[rr * LDR + j], Xs[j * LP + n], a);
       }
-      t[u] = a;
+      acc[u] = a;
     }
     __syncthreads();
 #pragma unroll
     for (int u = 0; u < PER; ++u) {
       const int idx = threadIdx.x + kReduceThreads * u;
-      if (idx < kGramRows * LP) rows[(idx / LP) * LDR + idx % LP] = t[u];
+      if (idx < kGramRows * LP) rows[(idx / LP) * LDR + idx % LP] = acc[u];
     }
     __syncthreads();
   }
@@ -623,7 +815,7 @@ __global__ __launch_bounds__(kReduceThreads) void reduce_gram_kernel(const float
     const int a = e / l, b = e - a * l;
     if (b < a) continue;
     double sum = 0.0;
-#pragma unroll
+#pragma unroll RU
     for (int rr = 0; rr < kGramRows; ++rr)
       sum = fma(static_cast<double>(rows[rr * LDR + a]), static_cast<double>(rows[rr * LDR + b]), sum);
     gp[packed_index(a, b, l)] = sum;
@@ -1016,9 +1208,12 @@ hipError_t run_lowrank(const float* E, const SvdPlan& pl, int q, const float* om
     LQ_LAUNCH("gram_sum", gram_sum_kernel, dim3((E_ + 63) / 64), dim3(1024), 0, s, gparts, P, E_, gtotal);
     if (l <= 32)
       launch_small_wave(mode, gtotal, l, Xinv, r, SB, SA, sigma, stats, mode == 2 ? obj : none, s);
+    else if (mode == 1)
+      LQ_LAUNCH("chol_inv", solve_wide_kernel<1>, dim3(1), dim3(kWideThreads), 0, s, gtotal, l, Xinv, r, SB, SA, sigma,
+                stats, none);
     else
-      LQ_LAUNCH(mode == 1 ? "chol_inv" : "core_svd", small_kernel, dim3(1), dim3(256), 0, s, gtotal, l, mode, Xinv, r,
-                SB, SA, sigma, stats, mode == 2 ? obj : none);
+      LQ_LAUNCH("core_svd", solve_wide_kernel<2>, dim3(1), dim3(kWideThreads), 0, s, gtotal, l, Xinv, r, SB, SA, sigma,
+                stats, obj);
   };
   // Y = E Omega; X = R^-1 of its Gram.  Each power iteration multiplies by E^T
   // and E and re-orthonormalises Y only: span(E Z) does not depend on Z's basis,
