@@ -533,21 +533,39 @@ __global__ __launch_bounds__(256) void core_small_kernel(const double* __restric
 // The two solves for 32 < l <= kMaxL, by one workgroup of kWideThreads = 640
 // threads (pair i of a Jacobi round on lanes 16 i .. 16 i + 15).
 //
-// chol_lds: right-looking Cholesky of the fp64 Gram held (full, symmetric) in
-// LDS, one barrier per column.  Step j: every thread reads the pivot itself;
-// the trailing block loses the outer product of row j (unscaled, times the
-// pivot's inverse); the scaled row j of R goes to Rm when given (a separate
-// array, so no thread overwrites what another still reads).  With T given, the same steps
-// build X = R^-1 the way chol_wave does (rows of T = R^-T), writing each
-// finished row of T straight into X's column.
+// chol_wide: right-looking Cholesky of the fp64 Gram with the matrix in
+// registers: wave w owns rows w, w + 10, ..., lane c owns columns c and c + 64,
+// 16 entries per thread.  Step j: the owner of row j publishes it (and row j of
+// T) through a double-buffered LDS row, one barrier, then every thread takes the
+// pivot and updates its own entries with the outer product of row j.  Updates
+// are unconditional: entries of finished rows and columns pick up values that
+// are never read again.  R's rows go to Rm when given; with INV the same steps
+// build X = R^-1 the way chol_wave does (T = R^-T, lane c holding its columns
+// of T's rows), each finished row of T written straight into X's column.
 constexpr int kWideThreads = 640;
 constexpr int kWideLd = kMaxL + 1;
+constexpr int kWideWaves = kWideThreads / 64;
+constexpr int kWideRows = (kMaxL + kWideWaves - 1) / kWideWaves;
 
-__device__ void chol_lds(double* G, double* Rm, double* T, float* X, int l, double* scratch) {
-  const int tid = threadIdx.x, nt = blockDim.x;
+template <bool INV>
+__device__ void chol_wide(const double* __restrict__ gram, int l, double* Rm, float* __restrict__ X, double* rowbuf,
+                          double* scratch) {
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  double g[kWideRows][2], t[kWideRows][2];
+#pragma unroll
+  for (int i = 0; i < kWideRows; ++i)
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      const int a = w + kWideWaves * i, b = lane + 64 * c;
+      const bool in = a < l && b < l;
+      const int pi = !in ? 0 : (a <= b ? packed_index(a, b, l) : packed_index(b, a, l));
+      const double v = gram[pi];
+      g[i][c] = in ? v : 0.0;
+      if (INV) t[i][c] = (a == b) ? 1.0 : 0.0;
+    }
   if (tid < 64) {
     double m = 0.0;
-    for (int a = tid; a < l; a += 64) m = fmax(m, G[a * kWideLd + a]);
+    for (int a = tid; a < l; a += 64) m = fmax(m, gram[packed_index(a, a, l)]);
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) m = fmax(m, __shfl_xor(m, off));
     if (tid == 0) scratch[0] = m;
@@ -555,30 +573,60 @@ __device__ void chol_lds(double* G, double* Rm, double* T, float* X, int l, doub
   __syncthreads();
   const double tol = 1e-13 * scratch[0];
   for (int j = 0; j < l; ++j) {
-    const double piv = G[j * kWideLd + j];
-    const bool keep = piv > tol && piv > 0.0;
-    const double inv = keep ? rsq_f64(piv) : 0.0;   // 1 / R[j][j]
-    const int tail = l - 1 - j;
-    // trailing update G[a][b] -= R[j][a] R[j][b], a, b > j (both triangles)
-    for (int e = tid; e < tail * tail; e += nt) {
-      const int a = j + 1 + e / tail, b = j + 1 + e % tail;
-      G[a * kWideLd + b] = fma(-(G[j * kWideLd + a] * inv), G[j * kWideLd + b] * inv, G[a * kWideLd + b]);
-    }
-    // row j of R (when wanted)
-    if (Rm != nullptr)
-      for (int b = j + tid; b < l; b += nt) Rm[j * kWideLd + b] = (b == j) ? piv * inv : G[j * kWideLd + b] * inv;
-    if (T != nullptr) {
-      // T[j] is final after this step (scaled by inv); rows a > j lose R[j][a] T[j]
-      for (int e = tid; e < (tail + 1) * (j + 1); e += nt) {
-        const int ar = e / (j + 1), c = e % (j + 1);
-        const int a = j + ar;
-        const double tj = T[j * kWideLd + c] * inv;
-        if (ar == 0) X[c * l + j] = static_cast<float>(tj);   // X = T^T
-        else T[a * kWideLd + c] = fma(-(G[j * kWideLd + a] * inv), tj, T[a * kWideLd + c]);
-      }
+    double* rb = rowbuf + (j & 1) * 2 * kWideLd;   // [G row j | T row j]
+    if (w == j % kWideWaves) {
+      const int ij = j / kWideWaves;
+#pragma unroll
+      for (int i = 0; i < kWideRows; ++i)
+        if (i == ij) {
+#pragma unroll
+          for (int c = 0; c < 2; ++c) {
+            const int b = lane + 64 * c;
+            if (b < kWideLd) {
+              rb[b] = g[i][c];
+              if (INV) rb[kWideLd + b] = t[i][c];
+            }
+          }
+        }
     }
     __syncthreads();
+    const double piv = rb[j];
+    const bool keep = piv > tol && piv > 0.0;
+    const double inv = keep ? rsq_f64(piv) : 0.0;   // 1 / R[j][j]
+    double rjb[2], tjb[2];
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      const int b = lane + 64 * c;
+      const int bb = b < kWideLd ? b : 0;
+      rjb[c] = rb[bb] * inv;                        // R[j][b] (b > j)
+      if (INV) tjb[c] = rb[kWideLd + bb] * inv;     // final T[j][b]
+    }
+    if (Rm != nullptr && w == 0) {
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        const int b = lane + 64 * c;
+        if (b >= j && b < l) Rm[j * kWideLd + b] = (b == j) ? piv * inv : rjb[c];
+      }
+    }
+    if (INV && w == 0) {
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        const int b = lane + 64 * c;
+        if (b <= j) X[b * l + j] = static_cast<float>(tjb[c]);   // X = T^T
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < kWideRows; ++i) {
+      const int a = w + kWideWaves * i;
+      const double rja = rb[a < kWideLd ? a : 0] * inv;   // R[j][a]
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        g[i][c] = fma(-rja, rjb[c], g[i][c]);
+        if (INV) t[i][c] = fma(-rja, tjb[c], t[i][c]);
+      }
+    }
   }
+  __syncthreads();
 }
 
 template <int MODE>
@@ -588,30 +636,20 @@ __global__ __launch_bounds__(kWideThreads) void solve_wide_kernel(const double* 
                                                                   float* __restrict__ sigma, double* __restrict__ stats,
                                                                   ObjectiveArgs obj) {
   constexpr int NB = kMaxL * kWideLd;
-  __shared__ double G[NB];
-  __shared__ double Rm[NB];
+  __shared__ double Rm[MODE == 2 ? NB : 1];
   __shared__ float Kf[MODE == 2 ? NB : 1];
   __shared__ float V[MODE == 2 ? NB : 1];
+  __shared__ double rowbuf[4 * kWideLd];
   __shared__ double norm2[kMaxL];
   __shared__ int order[kMaxL];
   __shared__ double scratch[2];
   const int tid = threadIdx.x, nt = blockDim.x;
-  for (int e = tid; e < l * l; e += nt) {
-    const int a = e / l, b = e - a * l;
-    G[a * kWideLd + b] = (a <= b) ? gram[packed_index(a, b, l)] : gram[packed_index(b, a, l)];
-  }
   if (MODE == 1) {
-    // Rm doubles as T (identity to start); R itself is not needed for X
-    for (int e = tid; e < NB; e += nt) Rm[e] = 0.0;
-    __syncthreads();
-    for (int a = tid; a < l; a += nt) Rm[a * kWideLd + a] = 1.0;
     for (int e = tid; e < l * l; e += nt) Xinv[e] = 0.f;
-    __syncthreads();
-    chol_lds(G, nullptr, Rm, Xinv, l, scratch);
+    chol_wide<true>(gram, l, nullptr, Xinv, rowbuf, scratch);
     return;
   }
-  __syncthreads();
-  chol_lds(G, Rm, nullptr, nullptr, l, scratch);
+  chol_wide<false>(gram, l, Rm, nullptr, rowbuf, scratch);
   // K = 2^-e R (column c of K = column c of R), fp32, with 2^e at the scale of R's largest entry
   if (tid < 64) {
     double m = 0.0;
