@@ -52,7 +52,7 @@ __device__ __forceinline__ float4 load_run4(const float* __restrict__ p, int64_t
 // Launch shapes (compile-time per tile count NT = ceil(l / 16)).
 template <int NT>
 struct NnCfg {
-  static constexpr int RT = NT <= 2 ? 1 : 2;   // 16-row MFMA tiles per wave
+  static constexpr int RT = 2;                 // 16-row MFMA tiles per wave (each X fragment feeds both)
   static constexpr int D = NT <= 2 ? 4 : 2;    // register ring depth (K steps of 16)
   static constexpr int WR = NT <= 2 ? 4 : 2;   // waves along rows
   static constexpr int WK = NT <= 2 ? 1 : 2;   // waves splitting the workgroup's K range
@@ -60,7 +60,8 @@ struct NnCfg {
 template <int NT>
 struct TnCfg {
   static constexpr int D = 2;
-  static constexpr int WC = 2;                 // waves along columns (64 columns each)
+  static constexpr int CW = 1;                 // 64-column groups per wave (each Y fragment feeds all)
+  static constexpr int WC = 2;                 // waves along columns
   static constexpr int WR = 2;                 // waves splitting the workgroup's rows
 };
 
@@ -159,19 +160,20 @@ __global__ __launch_bounds__(64 * NnCfg<NT>::WR * NnCfg<NT>::WK) void gemm_nn_ke
 }
 
 // ---------------------------------------------------------------------------
-// gemm_tn.  Wave (wc, wr) owns columns c0 .. c0 + 63 and its share of the
-// workgroup's rows: [rb, rb + rper / WR).  Lane (li, g) covers columns c0 + 4 li
-// .. + 3, which belong to four interleaved 16-column MFMA tiles (tile jm holds
-// columns c0 + 4 m + jm).  Row step j covers rows rb + 16 j .. + 15; MFMA i of
-// the step takes rows rb + 16 j + 4 g + i (K index g), matching component i of
-// the fragment-order Y float4.
+// gemm_tn.  Wave (wc, wr) owns columns c0 .. c0 + 64 CW - 1 and its share of
+// the workgroup's rows: [rb, rb + rper / WR).  In column group cw, lane (li, g)
+// covers columns c0 + 64 cw + 4 li .. + 3, which belong to four interleaved
+// 16-column MFMA tiles (tile jm holds columns c0 + 64 cw + 4 m + jm).  Row step
+// j covers rows rb + 16 j .. + 15; MFMA i of the step takes rows
+// rb + 16 j + 4 g + i (K index g), matching component i of the fragment-order
+// Y float4, which serves all CW groups.
 template <int NT, bool VEC, int LMJ>
 __global__ __launch_bounds__(64 * TnCfg<NT>::WC * TnCfg<NT>::WR) void gemm_tn_kernel(
     const float* __restrict__ E, int64_t d, int64_t k, const float* __restrict__ Yf, int64_t rper,
     float* __restrict__ part, CholJob job) {
   using C = TnCfg<NT>;
-  constexpr int LP = 16 * NT, D = C::D, WC = C::WC, WR = C::WR;
-  constexpr int kRedFloats = (WR > 1 ? WR - 1 : 1) * WC * 64 * LP;
+  constexpr int LP = 16 * NT, D = C::D, CW = C::CW, WC = C::WC, WR = C::WR;
+  constexpr int kRedFloats = (WR > 1 ? WR - 1 : 1) * WC * 64 * CW * LP;
   constexpr int kJobDoubles = LMJ > 0 ? 5 * (LMJ * (LMJ + 1) / 2) + 64 : 1;
   constexpr int kLdsBytes = 4 * kRedFloats > 8 * kJobDoubles ? 4 * kRedFloats : 8 * kJobDoubles;
   __shared__ __align__(16) char lds_raw[kLdsBytes];
@@ -192,24 +194,27 @@ __global__ __launch_bounds__(64 * TnCfg<NT>::WC * TnCfg<NT>::WR) void gemm_tn_ke
   }
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, wc = w % WC, wr = w / WC;
   const int g = lane >> 4, li = lane & 15;
-  const int64_t c0 = (static_cast<int64_t>(blockIdx.x) * WC + wc) * 64;
+  const int64_t c0 = (static_cast<int64_t>(blockIdx.x) * WC + wc) * 64 * CW;
   const int64_t cl = c0 + 4 * li;
   const int64_t rw = rper / WR;
   const int64_t rb = static_cast<int64_t>(blockIdx.y) * rper + wr * rw;
   const int nsteps = static_cast<int>(rw / 16);   // a multiple of D
   const float* yp = Yf + (rb / 16) * NT * 256 + lane * 4;
-  floatx4 acc[4][NT];
+  floatx4 acc[CW][4][NT];
 #pragma unroll
-  for (int a = 0; a < 4; ++a)
+  for (int cw = 0; cw < CW; ++cw)
 #pragma unroll
-    for (int b = 0; b < NT; ++b) acc[a][b] = floatx4{0.f, 0.f, 0.f, 0.f};
-  float4 eb[D][4], yb[D][NT];
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+      for (int b = 0; b < NT; ++b) acc[cw][a][b] = floatx4{0.f, 0.f, 0.f, 0.f};
+  float4 eb[D][CW][4], yb[D][NT];
   auto load = [&](int u, int j) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       int64_t r = rb + 16 * j + 4 * g + i;
       r = r < d ? r : d - 1;
-      eb[u][i] = load_run4<VEC>(E + r * k, cl, k);
+#pragma unroll
+      for (int cw = 0; cw < CW; ++cw) eb[u][cw][i] = load_run4<VEC>(E + r * k, cl + 64 * cw, k);
     }
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt)
@@ -219,9 +224,12 @@ __global__ __launch_bounds__(64 * TnCfg<NT>::WC * TnCfg<NT>::WR) void gemm_tn_ke
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int jm = 0; jm < 4; ++jm)
+      for (int cw = 0; cw < CW; ++cw)
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) acc[jm][nt] = mfma16x16x4(comp(eb[u][i], jm), comp(yb[u][nt], i), acc[jm][nt]);
+        for (int jm = 0; jm < 4; ++jm)
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt)
+            acc[cw][jm][nt] = mfma16x16x4(comp(eb[u][cw][i], jm), comp(yb[u][nt], i), acc[cw][jm][nt]);
   };
 #pragma unroll
   for (int u = 0; u < D; ++u) load(u, u);
@@ -235,45 +243,54 @@ __global__ __launch_bounds__(64 * TnCfg<NT>::WC * TnCfg<NT>::WR) void gemm_tn_ke
   }
 #pragma unroll
   for (int u = 0; u < D; ++u) compute(u);
-  // lane (li, g), tile jm, component v holds column c0 + 4 (4 g + v) + jm, output n = 16 nt + li
+  // lane (li, g), group cw, tile jm, component v holds column c0 + 64 cw + 4 (4 g + v) + jm,
+  // output n = 16 nt + li
   if (WR > 1) {
     if (wr > 0) {
 #pragma unroll
-      for (int jm = 0; jm < 4; ++jm)
+      for (int cw = 0; cw < CW; ++cw)
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt)
+        for (int jm = 0; jm < 4; ++jm)
 #pragma unroll
-          for (int v = 0; v < 4; ++v)
-            red[(((wr - 1) * WC + wc) * 64 + 4 * (4 * g + v) + jm) * LP + nt * 16 + li] = acc[jm][nt][v];
+          for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+            for (int v = 0; v < 4; ++v)
+              red[(((wr - 1) * WC + wc) * 64 * CW + 64 * cw + 4 * (4 * g + v) + jm) * LP + nt * 16 + li] =
+                  acc[cw][jm][nt][v];
     }
     __syncthreads();
     if (wr > 0) return;
 #pragma unroll
     for (int q = 1; q < WR; ++q)
 #pragma unroll
-      for (int jm = 0; jm < 4; ++jm)
+      for (int cw = 0; cw < CW; ++cw)
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt)
+        for (int jm = 0; jm < 4; ++jm)
 #pragma unroll
-          for (int v = 0; v < 4; ++v)
-            acc[jm][nt][v] += red[(((q - 1) * WC + wc) * 64 + 4 * (4 * g + v) + jm) * LP + nt * 16 + li];
+          for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+            for (int v = 0; v < 4; ++v)
+              acc[cw][jm][nt][v] +=
+                  red[(((q - 1) * WC + wc) * 64 * CW + 64 * cw + 4 * (4 * g + v) + jm) * LP + nt * 16 + li];
   }
 #pragma unroll
-  for (int jm = 0; jm < 4; ++jm)
+  for (int cw = 0; cw < CW; ++cw)
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt)
+    for (int jm = 0; jm < 4; ++jm)
 #pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int64_t col = c0 + 4 * (4 * g + v) + jm;
-        if (col < k) part[(static_cast<int64_t>(blockIdx.y) * k + col) * LP + nt * 16 + li] = acc[jm][nt][v];
-      }
+      for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const int64_t col = c0 + 64 * cw + 4 * (4 * g + v) + jm;
+          if (col < k) part[(static_cast<int64_t>(blockIdx.y) * k + col) * LP + nt * 16 + li] = acc[cw][jm][nt][v];
+        }
 }
 
 template <int NT>
 GemmShape shape_typed(bool transposed) {
   if (transposed) {
     using C = TnCfg<NT>;
-    return GemmShape{64 * C::WC, 16 * C::D * C::WR};
+    return GemmShape{64 * C::CW * C::WC, 16 * C::D * C::WR};
   }
   using C = NnCfg<NT>;
   return GemmShape{16 * C::RT * C::WR, 16 * C::D * C::WK};
