@@ -116,7 +116,6 @@ loftq_status_t loftq_init(const void* W, loftq_dtype_t wdt, int64_t rows, int64_
   double* wparts = reinterpret_cast<double*>(w + pl.off_wparts);
   char* svd_ws = w + pl.off_svd;
   const int64_t n = rows * cols;
-  const int64_t nb = (n + 63) / 64;
   const int r = cfg->rank;
   const int T = cfg->iterative_steps;
 
@@ -124,10 +123,10 @@ loftq_status_t loftq_init(const void* W, loftq_dtype_t wdt, int64_t rows, int64_
   // the first dequant also leaves the partials of ||W||^2 (W is read there anyway)
   auto quant_step = [&](const float* Bp, const float* Ap, bool first) -> hipError_t {
     hipError_t x = launch_nf4_quantize(W, wdt, rows, cols, Bp, Ap, r, packed, absmax, s);
-    if (x == hipSuccess && dq) x = launch_double_quant(absmax, nb, cfg->dq_blocksize, qabsmax, dq_scale, s);
+    // the double quant of the absmax is derived (and written) inside the dequant
     if (x == hipSuccess)
-      x = launch_nf4_dequantize(packed, dq ? nullptr : absmax, dq ? qabsmax : nullptr, dq ? dq_scale : nullptr, n,
-                                cfg->dq_blocksize, W, wdt, E, eparts, first ? wparts : nullptr, nullptr, s);
+      x = launch_nf4_dequantize(packed, absmax, nullptr, nullptr, n, cfg->dq_blocksize, W, wdt, E, eparts,
+                                first ? wparts : nullptr, nullptr, s, dq ? qabsmax : nullptr, dq ? dq_scale : nullptr);
     return x;
   };
   hipError_t e = hipSuccess;

@@ -74,10 +74,13 @@ hipError_t launch_double_quant(const float* absmax, int64_t nblocks, int dqbs, i
 // (dequant_num_partials(n) of them, summed in a fixed order by the consumer);
 // otherwise, with `sumsq`, accumulated into *sumsq with atomics (after zeroing it).
 // With W and `wpartials`, the same per-workgroup partials of sum W^2 as well.
+// With q_out / dqs_out (dq_blocksize 256), the double quant of `absmax` is
+// derived inside the dequant and written there (q and dqscale unused).
 hipError_t launch_nf4_dequantize(const uint8_t* packed, const float* absmax, const int8_t* q,
                                  const float* dqscale, int64_t n, int dqbs, const void* W,
                                  loftq_dtype_t wdt, float* out, double* partials, double* wpartials,
-                                 double* sumsq, hipStream_t s);
+                                 double* sumsq, hipStream_t s, int8_t* q_out = nullptr,
+                                 float* dqs_out = nullptr);
 int dequant_num_partials(int64_t n);
 hipError_t launch_sumsq_weight(const void* W, loftq_dtype_t wdt, int64_t n, double* partials, unsigned* counter,
                                double* sumsq, hipStream_t s);

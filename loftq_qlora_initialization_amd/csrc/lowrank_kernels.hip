@@ -771,7 +771,7 @@ __global__ __launch_bounds__(kReduceThreads) void reduce_gram_kernel(const float
   constexpr int LP = 16 * NT, PER = (kGramRows * LP + kReduceThreads - 1) / kReduceThreads, LDR = LP + 1;
   // wide panels (NT >= 3) keep fewer loads in flight and unroll less, so the
   // per-thread state fits the register file of a 512-thread workgroup
-  constexpr int QB = NT <= 2 ? 4 : 2, JU = NT <= 2 ? LP : 16, RU = NT <= 2 ? kGramRows : 16;
+  constexpr int QB = NT <= 2 ? 8 : 2, JU = NT <= 2 ? LP : 16, RU = NT <= 2 ? kGramRows : 16;
   __shared__ float rows[kGramRows * LDR];
   __shared__ float Xs[LP * LP];
   const int64_t r0 = static_cast<int64_t>(blockIdx.x) * kGramRows;

@@ -330,6 +330,14 @@ __global__ __launch_bounds__(kFusedThreads) __attribute__((amdgpu_waves_per_eu(R
 }
 
 // ---------------------------------------------------------------------------
+// Double quant of the absmax: group scale = max / 127 (IEEE division), code =
+// round-to-nearest-even of a / scale clamped to [0, 127] (0 for a zero group).
+// Shared by the double-quant kernel and the dequant that derives it on the fly.
+__device__ __forceinline__ float dq_group_scale(float m) { return m / 127.0f; }
+__device__ __forceinline__ int dq_code(float a, float sc) {
+  return sc != 0.f ? static_cast<int>(fminf(fmaxf(rintf(a / sc), 0.f), 127.f)) : 0;
+}
+
 // Double quant: one workgroup of 256 per group of dq_blocksize (= 256) absmax.
 __global__ __launch_bounds__(256) void double_quant_kernel(const float* __restrict__ absmax, int64_t nb, int dqbs,
                                                            int8_t* __restrict__ q, float* __restrict__ scale) {
@@ -343,13 +351,9 @@ __global__ __launch_bounds__(256) void double_quant_kernel(const float* __restri
   if ((tid & 63) == 0) red[tid >> 6] = m;
   __syncthreads();
   m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-  const float sc = m / 127.0f;
+  const float sc = dq_group_scale(m);
   if (tid == 0) scale[blockIdx.x] = sc;
-  if (ok) {
-    int v = 0;
-    if (sc != 0.f) v = static_cast<int>(fminf(fmaxf(rintf(a / sc), 0.f), 127.f));
-    q[base + tid] = static_cast<int8_t>(v);
-  }
+  if (ok) q[base + tid] = static_cast<int8_t>(dq_code(a, sc));
 }
 
 // ---------------------------------------------------------------------------
@@ -375,17 +379,30 @@ __device__ __forceinline__ void load4(const float* __restrict__ p, float v[4]) {
   v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
 }
 
-template <bool kDQ>
+// Dequant scale of block b.  kDQ 0: absmax; 1: qabsmax x dq_scale as given;
+// 2: derived from absmax on the fly (the group's maximum recomputed; ragged-end use only).
+template <int kDQ>
 __device__ __forceinline__ float block_scale(const float* __restrict__ absmax, const int8_t* __restrict__ qa,
-                                             const float* __restrict__ dqs, int dqbs, int64_t b) {
-  return kDQ ? static_cast<float>(qa[b]) * dqs[b / dqbs] : absmax[b];
+                                             const float* __restrict__ dqs, int dqbs, int64_t nb, int64_t b) {
+  if (kDQ == 0) return absmax[b];
+  if (kDQ == 1) return static_cast<float>(qa[b]) * dqs[b / dqbs];
+  const int64_t g0 = b / dqbs * dqbs, g1 = g0 + dqbs < nb ? g0 + dqbs : nb;
+  float m = 0.f;
+  for (int64_t i = g0; i < g1; ++i) m = fmaxf(m, absmax[i]);
+  const float sc = dq_group_scale(m);
+  return static_cast<float>(dq_code(absmax[b], sc)) * sc;
 }
 
-template <typename T, bool kHasW, bool kDQ>
+// kDQ 2 (dq_blocksize 256, 16 slices per group): each wave takes its group's
+// maximum over the 256 absmax, forms the scales of its slice itself, and the
+// wave of the group's first slice also writes the group's qabsmax and dq_scale;
+// groups that start in the ragged end are written by workgroup 0.
+template <typename T, bool kHasW, int kDQ>
 __global__ __launch_bounds__(kThreads) void dequant_kernel(const uint8_t* __restrict__ packed,
                                                            const float* __restrict__ absmax,
                                                            const int8_t* __restrict__ qa,
                                                            const float* __restrict__ dqs, int dqbs, int64_t n,
+                                                           int8_t* __restrict__ qa_out, float* __restrict__ dqs_out,
                                                            const T* __restrict__ W, float* __restrict__ out,
                                                            double* __restrict__ partials,
                                                            double* __restrict__ wpartials,
@@ -397,6 +414,7 @@ __global__ __launch_bounds__(kThreads) void dequant_kernel(const uint8_t* __rest
   __syncthreads();
   const int lane = threadIdx.x & 63;
   const int64_t nslices = n >> 10;
+  const int64_t nb = (n + 63) >> 6;
   const int64_t nwaves = static_cast<int64_t>(gridDim.x) * (kThreads / 64);
   double acc = 0.0, wacc = 0.0;
   for (int64_t sl = (static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x) >> 6; sl < nslices; sl += nwaves) {
@@ -407,8 +425,31 @@ __global__ __launch_bounds__(kThreads) void dequant_kernel(const uint8_t* __rest
     for (int q = 0; q < 4; ++q) {
       const int64_t e = base + 256 * q;
       cw[q] = reinterpret_cast<const uint16_t*>(packed)[e >> 2];
-      a[q] = block_scale<kDQ>(absmax, qa, dqs, dqbs, e >> 6);
+      if (kDQ != 2) a[q] = block_scale<kDQ>(absmax, qa, dqs, dqbs, nb, e >> 6);
       if (kHasW) load4(W + e, w[q]);
+    }
+    if (kDQ == 2) {
+      const int64_t g = sl >> 4, b0 = g << 8;
+      float am[4], m = 0.f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int64_t b = b0 + lane + 64 * i;
+        am[i] = b < nb ? absmax[b] : 0.f;
+        m = fmaxf(m, am[i]);
+      }
+#pragma unroll
+      for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+      const float sc = dq_group_scale(m);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) a[q] = static_cast<float>(dq_code(absmax[(base + 256 * q) >> 6], sc)) * sc;
+      if ((sl & 15) == 0) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int64_t b = b0 + lane + 64 * i;
+          if (b < nb) qa_out[b] = static_cast<int8_t>(dq_code(am[i], sc));
+        }
+        if (lane == 0) dqs_out[g] = sc;
+      }
     }
     float ss = 0.f, ws = 0.f;
 #pragma unroll
@@ -428,11 +469,23 @@ __global__ __launch_bounds__(kThreads) void dequant_kernel(const uint8_t* __rest
     wacc += static_cast<double>(ws);
   }
   // ragged end: whole groups of 16 by the threads of workgroup 0, then the last
-  // few elements by its thread 0
+  // few elements by its thread 0; with kDQ 2 also the double quant of the
+  // groups whose first slice is not whole
   if (blockIdx.x == 0) {
+    if (kDQ == 2) {
+      const int64_t ng = (nb + 255) >> 8;
+      for (int64_t g = ((nslices + 15) >> 4) + threadIdx.x; g < ng; g += kThreads) {
+        const int64_t g0 = g << 8, g1 = g0 + 256 < nb ? g0 + 256 : nb;
+        float m = 0.f;
+        for (int64_t b = g0; b < g1; ++b) m = fmaxf(m, absmax[b]);
+        const float sc = dq_group_scale(m);
+        for (int64_t b = g0; b < g1; ++b) qa_out[b] = static_cast<int8_t>(dq_code(absmax[b], sc));
+        dqs_out[g] = sc;
+      }
+    }
     const int64_t ngroups = n >> 4;
     for (int64_t g = (nslices << 6) + threadIdx.x; g < ngroups; g += kThreads) {
-      const float sc = block_scale<kDQ>(absmax, qa, dqs, dqbs, g >> 2);
+      const float sc = block_scale<kDQ>(absmax, qa, dqs, dqbs, nb, g >> 2);
       const uint2 pw = reinterpret_cast<const uint2*>(packed)[g];
       float ss = 0.f, ws = 0.f;
 #pragma unroll
@@ -451,7 +504,7 @@ __global__ __launch_bounds__(kThreads) void dequant_kernel(const uint8_t* __rest
     if (threadIdx.x == 0) {
       float ss = 0.f, ws = 0.f;
       for (int64_t i = ngroups * 16; i < n; ++i) {
-        const float sc = block_scale<kDQ>(absmax, qa, dqs, dqbs, i >> 6);
+        const float sc = block_scale<kDQ>(absmax, qa, dqs, dqbs, nb, i >> 6);
         const uint32_t code = (packed[i >> 1] >> ((i & 1) ? 0 : 4)) & 0xFu;
         const float d = lvl[code] * sc;
         const float wv = kHasW ? load1(W, i) : 0.f;
@@ -578,19 +631,19 @@ hipError_t quantize_typed(const T* W, int64_t rows, int64_t cols, const float* B
 
 template <typename T>
 hipError_t dequant_typed(const uint8_t* packed, const float* absmax, const int8_t* q, const float* dqs, int64_t n,
-                         int dqbs, const T* W, float* out, double* partials, double* wpartials, double* sumsq,
-                         hipStream_t s) {
+                         int dqbs, int8_t* q_out, float* dqs_out, const T* W, float* out, double* partials,
+                         double* wpartials, double* sumsq, hipStream_t s) {
   const Nf4Tables& tab = nf4_tables();
   const int grid = dequant_num_partials(n);
   if (partials == nullptr && sumsq != nullptr) LQ_LAUNCH("zero", zero_double_kernel, dim3(1), dim3(1), 0, s, sumsq);
-  const bool dq = q != nullptr;
+  const int mode = q_out != nullptr ? 2 : (q != nullptr ? 1 : 0);
 #define LQ_DEQ(HW, DQ)                                                                                            \
   LQ_LAUNCH("nf4_dequantize", (dequant_kernel<T, HW, DQ>), dim3(grid), dim3(kThreads), 0, s, packed, absmax, q,   \
-            dqs, dqbs, n, W, out, partials, wpartials, sumsq, tab)
+            dqs, dqbs, n, q_out, dqs_out, W, out, partials, wpartials, sumsq, tab)
   if (W != nullptr) {
-    if (dq) LQ_DEQ(true, true); else LQ_DEQ(true, false);
+    if (mode == 2) LQ_DEQ(true, 2); else if (mode == 1) LQ_DEQ(true, 1); else LQ_DEQ(true, 0);
   } else {
-    if (dq) LQ_DEQ(false, true); else LQ_DEQ(false, false);
+    if (mode == 2) LQ_DEQ(false, 2); else if (mode == 1) LQ_DEQ(false, 1); else LQ_DEQ(false, 0);
   }
 #undef LQ_DEQ
   return hipGetLastError();
@@ -621,16 +674,17 @@ hipError_t launch_double_quant(const float* absmax, int64_t nblocks, int dqbs, i
 
 hipError_t launch_nf4_dequantize(const uint8_t* packed, const float* absmax, const int8_t* q, const float* dqscale,
                                  int64_t n, int dqbs, const void* W, loftq_dtype_t wdt, float* out, double* partials,
-                                 double* wpartials, double* sumsq, hipStream_t s) {
+                                 double* wpartials, double* sumsq, hipStream_t s, int8_t* q_out, float* dqs_out) {
   if (n == 0) {
     if (sumsq) LQ_LAUNCH("zero", zero_double_kernel, dim3(1), dim3(1), 0, s, sumsq);
     return hipGetLastError();
   }
+  if (q_out != nullptr && dqbs != 256) return hipErrorInvalidValue;
   if (wdt == LOFTQ_BF16)
-    return dequant_typed(packed, absmax, q, dqscale, n, dqbs, static_cast<const uint16_t*>(W), out, partials,
-                         wpartials, sumsq, s);
-  return dequant_typed(packed, absmax, q, dqscale, n, dqbs, static_cast<const float*>(W), out, partials, wpartials,
-                       sumsq, s);
+    return dequant_typed(packed, absmax, q, dqscale, n, dqbs, q_out, dqs_out, static_cast<const uint16_t*>(W), out,
+                         partials, wpartials, sumsq, s);
+  return dequant_typed(packed, absmax, q, dqscale, n, dqbs, q_out, dqs_out, static_cast<const float*>(W), out,
+                       partials, wpartials, sumsq, s);
 }
 
 hipError_t launch_sumsq_weight(const void* W, loftq_dtype_t wdt, int64_t n, double* partials, unsigned* counter,
