@@ -179,14 +179,21 @@ template <int CTRL>
 __device__ __forceinline__ float dpp_f32(float v) {
   return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, true));
 }
-// fp32 sum over an aligned 16-lane row; every lane ends with the same total.
+// fp32 sum over an aligned group of G = 16, 8 or 4 lanes; every lane of the
+// group ends with the same total.
 template <int G>
 __device__ __forceinline__ float group_sumf(float v) {
-  static_assert(G == 16, "16-lane rows only");
-  v += dpp_f32<0x128>(v);   // row_ror:8
-  v += dpp_f32<0x124>(v);   // row_ror:4
-  v += dpp_f32<0x122>(v);   // row_ror:2
-  v += dpp_f32<0x121>(v);   // row_ror:1
+  static_assert(G == 16 || G == 8 || G == 4, "16-, 8- or 4-lane groups");
+  if (G == 16) {
+    v += dpp_f32<0x128>(v);   // row_ror:8
+    v += dpp_f32<0x124>(v);   // row_ror:4
+    v += dpp_f32<0x122>(v);   // row_ror:2
+    v += dpp_f32<0x121>(v);   // row_ror:1
+  } else {
+    v += dpp_f32<0xB1>(v);    // quad_perm xor 1
+    v += dpp_f32<0x4E>(v);    // quad_perm xor 2
+    if (G == 8) v += dpp_f32<0x141>(v);   // row_half_mirror: the other quad of the 8
+  }
   return v;
 }
 
@@ -530,7 +537,7 @@ __global__ __launch_bounds__(256) void core_small_kernel(const double* __restric
 }
 
 // ---------------------------------------------------------------------------
-// The two solves for 32 < l <= kMaxL, by one workgroup of kWideThreads = 640
+// The two solves for 32 < l <= kMaxL, by one workgroup of 640 threads
 // threads (pair i of a Jacobi round on lanes 16 i .. 16 i + 15).
 //
 // chol_wide: right-looking Cholesky of the fp64 Gram with the matrix in
@@ -542,14 +549,16 @@ __global__ __launch_bounds__(256) void core_small_kernel(const double* __restric
 // are never read again.  R's rows go to Rm when given; with INV the same steps
 // build X = R^-1 the way chol_wave does (T = R^-T, lane c holding its columns
 // of T's rows), each finished row of T written straight into X's column.
-constexpr int kWideThreads = 640;
 constexpr int kWideLd = kMaxL + 1;
-constexpr int kWideWaves = kWideThreads / 64;
-constexpr int kWideRows = (kMaxL + kWideWaves - 1) / kWideWaves;
+// measured on MI355X at l = 80: more lanes per pair and more waves win (4-lane
+// pairs on 3 waves: 2.5x slower core; 4 Cholesky waves: 1.35x slower)
+constexpr int kWideCholWaves = 10;   // waves of the l > 32 Cholesky workgroup
+constexpr int kWideGroup = 16;       // lanes per Jacobi pair of the l > 32 core
 
-template <bool INV>
+template <bool INV, int NW>
 __device__ void chol_wide(const double* __restrict__ gram, int l, double* Rm, float* __restrict__ X, double* rowbuf,
                           double* scratch) {
+  constexpr int kWideWaves = NW, kWideRows = (kMaxL + NW - 1) / NW;
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
   double g[kWideRows][2], t[kWideRows][2];
 #pragma unroll
@@ -629,8 +638,10 @@ __device__ void chol_wide(const double* __restrict__ gram, int l, double* Rm, fl
   __syncthreads();
 }
 
-template <int MODE>
-__global__ __launch_bounds__(kWideThreads) void solve_wide_kernel(const double* __restrict__ gram, int l,
+// MODE 1: Cholesky and X = R^-1 on NW waves; MODE 2: the core, Jacobi pairs on
+// GW-lane groups (NW = 40 GW / 64 rounded up).
+template <int MODE, int NW, int GW>
+__global__ __launch_bounds__(64 * NW) void solve_wide_kernel(const double* __restrict__ gram, int l,
                                                                   float* __restrict__ Xinv, int r,
                                                                   float* __restrict__ SB, float* __restrict__ SA,
                                                                   float* __restrict__ sigma, double* __restrict__ stats,
@@ -646,10 +657,10 @@ __global__ __launch_bounds__(kWideThreads) void solve_wide_kernel(const double* 
   const int tid = threadIdx.x, nt = blockDim.x;
   if (MODE == 1) {
     for (int e = tid; e < l * l; e += nt) Xinv[e] = 0.f;
-    chol_wide<true>(gram, l, nullptr, Xinv, rowbuf, scratch);
+    chol_wide<true, NW>(gram, l, nullptr, Xinv, rowbuf, scratch);
     return;
   }
-  chol_wide<false>(gram, l, Rm, nullptr, rowbuf, scratch);
+  chol_wide<false, NW>(gram, l, Rm, nullptr, rowbuf, scratch);
   // K = 2^-e R (column c of K = column c of R), fp32, with 2^e at the scale of R's largest entry
   if (tid < 64) {
     double m = 0.0;
@@ -667,9 +678,9 @@ __global__ __launch_bounds__(kWideThreads) void solve_wide_kernel(const double* 
     V[e] = (row == c) ? 1.f : 0.f;
   }
   __syncthreads();
-  // one-sided Jacobi, fp32, 16 lanes per pair (rows sub + 16 i)
-  constexpr int RL = (kMaxL + 15) / 16;
-  const int pair = tid >> 4, sub = tid & 15;
+  // one-sided Jacobi, fp32, GW lanes per pair (rows sub + GW i)
+  constexpr int RL = (kMaxL + GW - 1) / GW;
+  const int pair = tid / GW, sub = tid % GW;
   const bool active = pair < n / 2;
   int pa = pair, pb = n - 1 - pair;
   int sweeps = 0;
@@ -686,18 +697,18 @@ __global__ __launch_bounds__(kWideThreads) void solve_wide_kernel(const double* 
         float al = 0.f, be = 0.f, ga = 0.f;
 #pragma unroll
         for (int i = 0; i < RL; ++i) {
-          const bool in = sub + 16 * i < n;
-          xp[i] = in ? kp[16 * i] : 0.f;
-          xq[i] = in ? kq[16 * i] : 0.f;
-          yp[i] = in ? vp[16 * i] : 0.f;
-          yq[i] = in ? vq[16 * i] : 0.f;
+          const bool in = sub + GW * i < n;
+          xp[i] = in ? kp[GW * i] : 0.f;
+          xq[i] = in ? kq[GW * i] : 0.f;
+          yp[i] = in ? vp[GW * i] : 0.f;
+          yq[i] = in ? vq[GW * i] : 0.f;
           al = fmaf(xp[i], xp[i], al);
           be = fmaf(xq[i], xq[i], be);
           ga = fmaf(xp[i], xq[i], ga);
         }
-        al = group_sumf<16>(al);
-        be = group_sumf<16>(be);
-        ga = group_sumf<16>(ga);
+        al = group_sumf<GW>(al);
+        be = group_sumf<GW>(be);
+        ga = group_sumf<GW>(ga);
         const float g2 = ga * ga, ab = al * be;
         const bool doit = q < l && g2 > 1e-14f * ab && ga != 0.f;
         const float dd = be - al;
@@ -707,11 +718,11 @@ __global__ __launch_bounds__(kWideThreads) void solve_wide_kernel(const double* 
         const float sn = doit ? (dd >= 0.f ? ga : -ga) * ri * __builtin_amdgcn_rsqf(hc) : 0.f;
 #pragma unroll
         for (int i = 0; i < RL; ++i) {
-          if (sub + 16 * i < n) {
-            kp[16 * i] = c * xp[i] - sn * xq[i];
-            kq[16 * i] = sn * xp[i] + c * xq[i];
-            vp[16 * i] = c * yp[i] - sn * yq[i];
-            vq[16 * i] = sn * yp[i] + c * yq[i];
+          if (sub + GW * i < n) {
+            kp[GW * i] = c * xp[i] - sn * xq[i];
+            kq[GW * i] = sn * xp[i] + c * xq[i];
+            vp[GW * i] = c * yp[i] - sn * yq[i];
+            vq[GW * i] = sn * yp[i] + c * yq[i];
           }
         }
         big |= (doit && g2 > 1e-8f * ab) ? 1 : 0;
@@ -1247,11 +1258,11 @@ hipError_t run_lowrank(const float* E, const SvdPlan& pl, int q, const float* om
     if (l <= 32)
       launch_small_wave(mode, gtotal, l, Xinv, r, SB, SA, sigma, stats, mode == 2 ? obj : none, s);
     else if (mode == 1)
-      LQ_LAUNCH("chol_inv", solve_wide_kernel<1>, dim3(1), dim3(kWideThreads), 0, s, gtotal, l, Xinv, r, SB, SA, sigma,
-                stats, none);
+      LQ_LAUNCH("chol_inv", (solve_wide_kernel<1, kWideCholWaves, 16>), dim3(1), dim3(64 * kWideCholWaves), 0, s, gtotal,
+                l, Xinv, r, SB, SA, sigma, stats, none);
     else
-      LQ_LAUNCH("core_svd", solve_wide_kernel<2>, dim3(1), dim3(kWideThreads), 0, s, gtotal, l, Xinv, r, SB, SA, sigma,
-                stats, obj);
+      LQ_LAUNCH("core_svd", (solve_wide_kernel<2, (40 * kWideGroup + 63) / 64, kWideGroup>), dim3(1),
+                dim3(64 * ((40 * kWideGroup + 63) / 64)), 0, s, gtotal, l, Xinv, r, SB, SA, sigma, stats, obj);
   };
   // Y = E Omega; X = R^-1 of its Gram.  Each power iteration multiplies by E^T
   // and E and re-orthonormalises Y only: span(E Z) does not depend on Z's basis,
