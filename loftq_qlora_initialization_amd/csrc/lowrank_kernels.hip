@@ -15,8 +15,9 @@
 //   sketch        counter-based +-1 test matrix (SplitMix64)
 //   reduce_gram   fixed-order sum of the split-K partials (+ fp64 Gram partials)
 //   gram_sum      fixed-order sum of the Gram partials
-//   small_kernel  single workgroup: Cholesky and R^-1 (orthonormalisation), or
-//                 the l x l core solve (one-sided Jacobi)
+//   chol_inv      Cholesky of the Gram and X = R^-1 (orthonormalisation); for
+//                 l <= 32 it usually rides along with the next E^T Y product
+//   core_svd      the l x l core solve: Cholesky, one-sided Jacobi, S_B, S_A
 //   panel_small   P S for a row panel P and a small S: B = Q S_B, A = (C S_A)^T
 //   exact_jacobi  single-workgroup one-sided Jacobi SVD for tiny matrices
 // Every reduction runs in a fixed order, so results are deterministic.
@@ -67,42 +68,6 @@ __global__ void to_frag_kernel(const float* __restrict__ src, int64_t n, int l, 
   out[idx] = (i < n && j < l) ? src[i * l + j] : 0.f;
 }
 
-// Full symmetric l x l (row stride ld) from a packed upper triangle in global memory.
-__device__ void unpack_sym(const double* __restrict__ pk, int l, double* M, int ld) {
-  for (int e = threadIdx.x; e < l * l; e += blockDim.x) {
-    const int a = e / l, b = e - a * l;
-    M[a * ld + b] = (a <= b) ? pk[packed_index(a, b, l)] : pk[packed_index(b, a, l)];
-  }
-}
-
-// In-place upper Cholesky G = R^T R.  R's strict upper triangle replaces G's;
-// its diagonal goes to rdiag.  A pivot at or below 1e-13 of the largest diagonal
-// gives a zero row (that direction of the panel is dropped).  Threads form a
-// 16 x 16 grid over the trailing submatrix (blockDim 256).
-__device__ void chol_upper(double* G, int ld, int l, double* rdiag, double* scratch1) {
-  const int tid = threadIdx.x, ty = tid >> 4, tx = tid & 15;
-  if (tid == 0) {
-    double m = 0.0;
-    for (int a = 0; a < l; ++a) m = fmax(m, G[a * ld + a]);
-    scratch1[0] = m;
-  }
-  __syncthreads();
-  const double tol = 1e-13 * scratch1[0];
-  for (int j = 0; j < l; ++j) {
-    const double piv = G[j * ld + j];
-    const double rjj = (piv > tol && piv > 0.0) ? sqrt(piv) : 0.0;
-    const double inv = rjj > 0.0 ? 1.0 / rjj : 0.0;
-    for (int c = j + 1 + tid; c < l; c += blockDim.x) G[j * ld + c] *= inv;
-    if (tid == 0) rdiag[j] = rjj;
-    __syncthreads();
-    for (int a = j + 1 + ty; a < l; a += 16) {
-      const double rja = G[j * ld + a];
-      for (int b = a + tx; b < l; b += 16) G[a * ld + b] -= rja * G[j * ld + b];
-    }
-    __syncthreads();
-  }
-}
-
 // Round-robin (circle) schedule: position 0 is fixed, the others rotate.
 __device__ __forceinline__ int rr_player(int pos, int rnd, int n) {
   return pos == 0 ? 0 : 1 + (pos - 1 + rnd) % (n - 1);
@@ -151,30 +116,6 @@ __global__ __launch_bounds__(1024) void gram_sum_kernel(const double* __restrict
   }
 }
 
-// fp64 lane exchange inside a DPP row (16 lanes) or quad.
-template <int CTRL>
-__device__ __forceinline__ double dpp_f64(double v) {
-  const int lo = __builtin_amdgcn_mov_dpp(__double2loint(v), CTRL, 0xF, 0xF, true);
-  const int hi = __builtin_amdgcn_mov_dpp(__double2hiint(v), CTRL, 0xF, 0xF, true);
-  return __hiloint2double(hi, lo);
-}
-
-// Sum over an aligned group of G lanes (G = 16: row rotations; G = 4: quad
-// exchanges).  Every lane of the group ends with the bit-identical total.
-template <int G>
-__device__ __forceinline__ double group_sum(double v) {
-  if (G == 16) {
-    v += dpp_f64<0x128>(v);   // row_ror:8
-    v += dpp_f64<0x124>(v);   // row_ror:4
-    v += dpp_f64<0x122>(v);   // row_ror:2
-    v += dpp_f64<0x121>(v);   // row_ror:1
-  } else {
-    v += dpp_f64<0xB1>(v);    // quad_perm xor 1
-    v += dpp_f64<0x4E>(v);    // quad_perm xor 2
-  }
-  return v;
-}
-
 template <int CTRL>
 __device__ __forceinline__ float dpp_f32(float v) {
   return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, true));
@@ -197,194 +138,6 @@ __device__ __forceinline__ float group_sumf(float v) {
   return v;
 }
 
-// Rows per lane of the Jacobi groups: 16-lane groups serve n <= 32, 4-lane
-// groups n <= kMaxL.  K and V keep ld >= G * rows(G) rows, zero beyond n.
-template <int G>
-constexpr int jacobi_rows() { return G == 16 ? 2 : (kMaxL + 3) / 4; }
-
-// One-sided Jacobi sweeps on the n columns of K (column-major, LDS, column
-// stride ld), rotations accumulated in V (fp32, same layout).  Pair i of a round
-// is owned by lanes [G i, G i + G); lane `sub` holds rows sub, sub + G, ... of
-// the pair's two columns in registers for the round.  A pair rotates while
-// |k_p . k_q| > 1e-7 |k_p| |k_q|.
-template <int G>
-__device__ void jacobi_sweeps(double* K, float* V, const uint16_t* sched, int n, int ld, int l, int* flags) {
-  constexpr int RMAX = jacobi_rows<G>();
-  const int tid = threadIdx.x;
-  const int pair = tid / G, sub = tid - pair * G;
-  const bool active = pair < n / 2;   // G * (n / 2) <= blockDim.x
-  for (int sweep = 0; sweep < 30; ++sweep) {
-    if (tid == 0) { flags[0] = 0; flags[1] = sweep + 1; }
-    __syncthreads();
-    for (int rnd = 0; rnd < n - 1; ++rnd) {
-      if (active) {
-        const int pq = sched[rnd * (n / 2) + pair];
-        const int p = pq & 0xFF, q = pq >> 8;
-        double* kp = K + p * ld + sub;
-        double* kq = K + q * ld + sub;
-        float* vp = V + p * ld + sub;
-        float* vq = V + q * ld + sub;
-        double xp[RMAX], xq[RMAX];
-        float yp[RMAX], yq[RMAX];
-        double al = 0.0, be = 0.0, ga = 0.0;
-#pragma unroll
-        for (int i = 0; i < RMAX; ++i) {
-          xp[i] = kp[G * i];
-          xq[i] = kq[G * i];
-          yp[i] = vp[G * i];
-          yq[i] = vq[G * i];
-        }
-#pragma unroll
-        for (int i = 0; i < RMAX; ++i) {
-          al = fma(xp[i], xp[i], al);
-          be = fma(xq[i], xq[i], be);
-          ga = fma(xp[i], xq[i], ga);
-        }
-        al = group_sum<G>(al);
-        be = group_sum<G>(be);
-        ga = group_sum<G>(ga);
-        if (q < l && ga * ga > 1e-14 * (al * be) && ga != 0.0) {
-          const double zeta = 0.5 * (be - al) * rcp_f64(ga);
-          const double az = fabs(zeta);
-          double t = (az > 1e8) ? 0.5 * rcp_f64(az) : rcp_f64(az + (1.0 + zeta * zeta) * rsq_f64(1.0 + zeta * zeta));
-          t = zeta >= 0.0 ? t : -t;
-          const double c = rsq_f64(1.0 + t * t), s = c * t;
-          const float cf = static_cast<float>(c), sf = static_cast<float>(s);
-#pragma unroll
-          for (int i = 0; i < RMAX; ++i) {
-            kp[G * i] = c * xp[i] - s * xq[i];
-            kq[G * i] = s * xp[i] + c * xq[i];
-            vp[G * i] = cf * yp[i] - sf * yq[i];
-            vq[G * i] = sf * yp[i] + cf * yq[i];
-          }
-          if (sub == 0) flags[0] = 1;
-        }
-      }
-      __syncthreads();
-    }
-    const int rotated = flags[0];
-    __syncthreads();
-    if (!rotated) break;
-  }
-}
-
-// LDS of small_kernel (doubles): G (l x l), X or K (l x l), V (fp32 l x l), small arrays.
-constexpr int kSmallDoubles = 2 * kMaxL * (kMaxL + 1) + (kMaxL * (kMaxL + 1)) / 2 + 4 * kMaxL + 64 + (kMaxL * kMaxL) / 8;
-
-// Single workgroup (256 threads) on the l x l Gram of a panel.
-//   mode 1: X = R^-1 for the Cholesky factor R of the Gram (G = R^T R), written
-//     to Xinv as fp32 (l x l row-major, upper triangular).  A direction whose
-//     pivot was dropped gets a zero column, so Y X matches forward substitution
-//     with that component set to zero.
-//   mode 2: the core solve.  Q is orthonormal (fp64 Gram and Cholesky; its fp32
-//     rounding leaves Q^T Q = I to ~1e-7), so Q^T E = C^T and its singular values
-//     are those of K, the Cholesky factor of H = C^T C (H = K^T K).  One-sided
-//     Jacobi orthogonalises K's columns, K V = U diag(sigma), accumulating V (the
-//     eigenvectors of H); round-robin pairs, each pair's two columns owned by a
-//     group of g lanes.  sigma descending; S_A = V_r diag(sigma^-1/2) so that
-//     A = (C S_A)^T, and SB = X V_r diag(sigma^1/2) with Xinv the R^-1 of the
-//     panel Y (Q = Y X), so that B = Y SB.
-__global__ __launch_bounds__(256) void small_kernel(const double* __restrict__ gram, int l, int mode,
-                                                    float* __restrict__ Xinv, int r, float* __restrict__ SB,
-                                                    float* __restrict__ SA, float* __restrict__ sigma,
-                                                    double* __restrict__ stats, ObjectiveArgs obj) {
-  __shared__ double smem[kSmallDoubles];
-  const int tid = threadIdx.x;
-  // odd leading dimensions (in doubles) keep rows/columns on distinct LDS banks
-  const int ldg = l | 1;
-  const int n = l + (l & 1);
-  const bool wide = blockDim.x >= 16 * (n / 2);                 // 16-lane Jacobi groups
-  const int kr = wide ? 16 * jacobi_rows<16>() : 4 * jacobi_rows<4>();
-  const int ldk = (kr > n ? kr : n) + 1;
-  double* G = smem;                                   // l x ldg, then R (strict upper)
-  double* K = G + kMaxL * (kMaxL + 1);                // mode 1: X = R^-1 (l x ldg); mode 2: K column-major (n x ldk)
-  float* V = reinterpret_cast<float*>(K + kMaxL * (kMaxL + 1));   // n x ldk column-major
-  double* rdiag = reinterpret_cast<double*>(V + kMaxL * (kMaxL + 1));
-  double* norm2 = rdiag + kMaxL;
-  int* order = reinterpret_cast<int*>(norm2 + kMaxL);
-  int* flags = order + kMaxL;
-  double* tmp = reinterpret_cast<double*>(flags + 4);
-  unpack_sym(gram, l, G, ldg);
-  __syncthreads();
-  chol_upper(G, ldg, l, rdiag, tmp);
-  if (mode == 1) {
-    // 1/R[c][c] (0 for a dropped direction) in norm2; row b of X by thread b:
-    // X[b][c] = (delta_bc - sum_{b <= a < c} X[b][a] R[a][c]) / R[c][c]
-    for (int c = tid; c < l; c += blockDim.x) norm2[c] = rdiag[c] > 0.0 ? 1.0 / rdiag[c] : 0.0;
-    __syncthreads();
-    double* X = K;
-    for (int b = tid; b < l; b += blockDim.x) {
-      for (int c = 0; c < b; ++c) X[b * ldg + c] = 0.0;
-      for (int c = b; c < l; ++c) {
-        double s0 = (c == b) ? 1.0 : 0.0, s1 = 0.0;
-        int a = b;
-        for (; a + 1 < c; a += 2) {
-          s0 = fma(-X[b * ldg + a], G[a * ldg + c], s0);
-          s1 = fma(-X[b * ldg + a + 1], G[(a + 1) * ldg + c], s1);
-        }
-        if (a < c) s0 = fma(-X[b * ldg + a], G[a * ldg + c], s0);
-        X[b * ldg + c] = (s0 + s1) * norm2[c];
-      }
-    }
-    __syncthreads();
-    for (int e = tid; e < l * l; e += blockDim.x) {
-      const int a = e / l, b = e - a * l;
-      Xinv[e] = static_cast<float>(X[a * ldg + b]);
-    }
-    return;
-  }
-  // K(:, c) = R(:, c): column-major, K[c * ldk + row]; rows n..ldk-1 stay zero
-  for (int e = tid; e < n * ldk; e += blockDim.x) {
-    const int c = e / ldk, row = e - c * ldk;
-    double v = 0.0;
-    if (c < l && row < l) v = (row == c) ? rdiag[c] : (row < c ? G[row * ldg + c] : 0.0);
-    K[e] = v;
-    V[e] = (row == c) ? 1.f : 0.f;
-  }
-  uint16_t* sched = reinterpret_cast<uint16_t*>(tmp + 8);   // [rnd][pair] -> p | q << 8
-  for (int e = tid; e < (n - 1) * (n / 2); e += blockDim.x) {
-    const int rnd = e / (n / 2), i = e - rnd * (n / 2);
-    const int pa = rr_player(i, rnd, n), pb = rr_player(n - 1 - i, rnd, n);
-    sched[e] = static_cast<uint16_t>(min(pa, pb) | (max(pa, pb) << 8));
-  }
-  if (tid == 0) flags[1] = 0;
-  __syncthreads();
-  if (wide) jacobi_sweeps<16>(K, V, sched, n, ldk, l, flags);
-  else jacobi_sweeps<4>(K, V, sched, n, ldk, l, flags);
-  for (int c = tid; c < l; c += blockDim.x) {
-    double s = 0.0;
-    for (int row = 0; row < n; ++row) s += K[c * ldk + row] * K[c * ldk + row];
-    norm2[c] = s;
-  }
-  __syncthreads();
-  for (int a = tid; a < l; a += blockDim.x) {
-    const double la = norm2[a];
-    int rank = 0;
-    for (int b = 0; b < l; ++b) rank += (norm2[b] > la || (norm2[b] == la && b < a)) ? 1 : 0;
-    order[rank] = a;
-  }
-  __syncthreads();
-  for (int idx = tid; idx < l * r; idx += blockDim.x) {
-    const int row = idx / r, c = idx - row * r;
-    const int a = order[c];
-    const double sg = sqrt(norm2[a]);
-    const double sq = sqrt(sg);
-    // SB[row][c] = sum_{j >= row} X[row][j] V[j][a] sqrt(sigma)
-    double acc = 0.0;
-    for (int j = row; j < l; ++j) acc = fma(static_cast<double>(Xinv[row * l + j]), static_cast<double>(V[a * ldk + j]), acc);
-    SB[row * r + c] = static_cast<float>(acc * sq);
-    SA[row * r + c] = sg > 0.0 ? static_cast<float>(V[a * ldk + row] / sq) : 0.f;
-  }
-  for (int c = tid; c < r; c += blockDim.x) sigma[c] = static_cast<float>(sqrt(norm2[order[c]]));
-  double s2 = 0.0;
-  for (int c = 0; c < r; ++c) s2 += norm2[order[c]];
-  if (tid == 0 && stats) {
-    stats[0] = s2;
-    stats[1] = static_cast<double>(flags[1]);
-  }
-  write_objective(obj, s2);
-}
-
 // ---------------------------------------------------------------------------
 // The same two solves for l <= 32, on the register Cholesky of chol_wave.
 //
@@ -403,130 +156,135 @@ __global__ __launch_bounds__(64) void chol_inv_wave_kernel(const double* __restr
   }
 }
 
-// mode 2 for l <= LM (LM <= 32), 256 threads.  Wave 0 factors H = R^T R in
-// fp64; K = R scaled by a power of two (exact) is then swept in fp32 by
-// one-sided Jacobi on its columns, with pair i of a round owned by lanes
-// 16 i .. 16 i + 15 (rows sub and sub + 16).  Round-robin positions advance by
-// one per round, so each lane tracks its pair's two players in registers.
-// One-sided Jacobi keeps high relative accuracy of the singular values in the
-// working precision, so fp32 sweeps hold the top-r values to ~1e-6 relative;
-// the column norms are summed in fp64 at the end.  V (fp32) accumulates the
-// rotations.  Pairs with |cos| <= 1e-7 are left alone (c = 1, s = 0); the
-// sweeps stop after one in which no pair had |cos| > 1e-4.
-template <int LM>
-__global__ __launch_bounds__(256) void core_small_kernel(const double* __restrict__ gram, int l,
-                                                         const float* __restrict__ Xinv, int r, float* __restrict__ SB,
-                                                         float* __restrict__ SA, float* __restrict__ sigma,
-                                                         double* __restrict__ stats, ObjectiveArgs obj) {
-  constexpr int LD = 33;
-  __shared__ double Kd[32 * LD / 2 + 32];   // row buffer of the Cholesky
-  __shared__ float K[32 * LD];
-  __shared__ float V[32 * LD];
-  __shared__ float Xs[32 * 32];
-  __shared__ double norm2[32];
-  __shared__ int order[32];
-  __shared__ double kscale;
-  const int tid = threadIdx.x;
-  for (int e = tid; e < 32 * LD; e += blockDim.x) {
-    const int c = e / LD, row = e - c * LD;
-    V[e] = (row == c) ? 1.f : 0.f;
-  }
-  for (int e = tid; e < l * l; e += blockDim.x) Xs[e] = Xinv[e];
-  if (tid < 64) {
-    double g[LM], t[LM];
-    chol_wave<LM, false>(gram, l, g, t, Kd);
-    // K = 2^-e R with 2^e at the scale of R's largest entry, so the fp32 sweeps
-    // neither overflow nor underflow whatever the magnitude of E
-    double m = 0.0;
-#pragma unroll
-    for (int a = 0; a < LM; ++a) m = fmax(m, (a <= tid && tid < l) ? fabs(g[a]) : 0.0);
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) m = fmax(m, __shfl_xor(m, off));
-    const double sc = m > 0.0 ? ldexp(1.0, -ilogb(m)) : 1.0;
-    if (tid == 0) kscale = sc;
-    if (tid < 32) {
-#pragma unroll
-      for (int a = 0; a < 32; ++a)
-        K[tid * LD + a] = (a < LM && a <= tid && tid < l) ? static_cast<float>(g[a < LM ? a : 0] * sc) : 0.f;
+// ---------------------------------------------------------------------------
+// The core solve.  Q is orthonormal (fp64 Gram and Cholesky; its fp32 rounding
+// leaves Q^T Q = I to ~1e-7), so Q^T E = C^T and its singular values are those
+// of R, the Cholesky factor of H = C^T C = R^T R.  With R = U_R diag(sigma) V_R^T,
+// one-sided Jacobi on the columns of K = R^T (scaled by a power of two, exact)
+// converges to K J = V_R diag(sigma) 2^-e: V_R is K's normalised columns, so no
+// rotation needs accumulating.  B = Q V_R diag(sigma)^1/2 and
+// A = diag(sigma)^1/2 (C R^-1 U_R)^T = (C V_R diag(sigma)^-1/2)^T.
+
+// Round-robin (circle) pairing of the n columns: in round rnd, slot i < n / 2
+// pairs the players at positions i and n - 1 - i.  sched[rnd * np + i] holds the
+// byte offsets (column times ld floats) of the slot's lower and higher column in
+// its low and high 16 bits.  Slots n / 2 .. np - 1 (lanes that pad the last
+// wave) get columns 2 np - 2 and 2 np - 1, which the caller keeps zero.
+__device__ void build_schedule(uint32_t* sched, int n, int np, int ld) {
+  for (int e = threadIdx.x; e < (n - 1) * np; e += blockDim.x) {
+    const int rnd = e / np, i = e - rnd * np;
+    int p = 2 * np - 2, q = 2 * np - 1;
+    if (i < n / 2) {
+      const int x = rr_player(i, rnd, n), y = rr_player(n - 1 - i, rnd, n);
+      p = x < y ? x : y;
+      q = x < y ? y : x;
     }
+    sched[e] = static_cast<uint32_t>(p * ld * 4) | (static_cast<uint32_t>(q * ld * 4) << 16);
   }
-  __syncthreads();
-  const int n = l + (l & 1);
-  const int pair = tid >> 4, sub = tid & 15;
-  const bool active = pair < n / 2;
-  int pa = pair, pb = n - 1 - pair;   // round 0 players
+}
+
+// One-sided Jacobi sweeps on the columns of K (fp32, LDS; rows GW * RL and
+// beyond the matrix are zero), GW lanes per column pair: lane `sub` holds rows
+// sub + GW i (i < RL) of both columns for the round.  With alpha, beta the
+// squared norms and gamma the dot product, the rotation by theta,
+// tan 2 theta = 2 gamma / (beta - alpha), |theta| <= pi / 4, is taken in the
+// branch-free form cos 2 theta = |beta - alpha| / h, h = hypot(beta - alpha,
+// 2 gamma), c = sqrt((1 + cos 2 theta) / 2), s = sin 2 theta / (2 c).  A pair
+// is left alone while gamma^2 <= 1e-14 alpha beta.  The sweeps stop after one in
+// which every pair had gamma^2 <= 1e-8 alpha beta (|cos| <= 1e-4).  Convergence is
+// quadratic once the couplings are below the relative gaps of the singular
+// values; with the nearly flat spectra of quantization residuals (neighbouring
+// values ~1% apart) a 1e-3 cut left couplings near 1e-5, visible in the
+// orthogonality of A, while 1e-4 leaves them at the fp32 rounding level.  All
+// threads call it; returns the sweeps.
+template <int GW, int RL>
+__device__ int jacobi_columns(float* K, const uint32_t* sched, int n, int max_sweeps) {
+  const int np = __builtin_amdgcn_readfirstlane(blockDim.x / GW);   // uniform: next row's offset is scalar
+  const int pair = threadIdx.x / GW, sub = threadIdx.x - pair * GW;
+  char* base = reinterpret_cast<char*>(K + sub);
+  const int rounds = n - 1;
+  uint32_t pq = sched[pair];
   int sweeps = 0;
-  for (int sweep = 0; sweep < 30; ++sweep) {
-    int big = 0;   // a rotation with |cos| above 1e-4 in this sweep
-    for (int rnd = 0; rnd < n - 1; ++rnd) {
-      if (active) {
-        const int p = pa < pb ? pa : pb, q = pa < pb ? pb : pa;
-        float* kp = K + p * LD + sub;
-        float* kq = K + q * LD + sub;
-        float* vp = V + p * LD + sub;
-        float* vq = V + q * LD + sub;
-        const float xp0 = kp[0], xp1 = kp[16], xq0 = kq[0], xq1 = kq[16];
-        const float yp0 = vp[0], yp1 = vp[16], yq0 = vq[0], yq1 = vq[16];
-        float al = fmaf(xp1, xp1, xp0 * xp0);
-        float be = fmaf(xq1, xq1, xq0 * xq0);
-        float ga = fmaf(xp1, xq1, xp0 * xq0);
-        al = group_sumf<16>(al);
-        be = group_sumf<16>(be);
-        ga = group_sumf<16>(ga);
-        const float g2 = ga * ga, ab = al * be;
-        // rotation by theta with tan 2 theta = 2 ga / (be - al), |theta| <= pi / 4:
-        // cos 2 theta = |be - al| / h, sin 2 theta = sgn(be - al) 2 ga / h with
-        // h = hypot(be - al, 2 ga); c = sqrt((1 + cos 2 theta) / 2), s = sin 2 theta / (2 c)
-        const bool doit = q < l && g2 > 1e-14f * ab && ga != 0.f;
-        const float dd = be - al;
-        const float ri = __builtin_amdgcn_rsqf(fmaf(dd, dd, 4.f * g2));
-        const float hc = fmaf(0.5f * fabsf(dd), ri, 0.5f);
-        const float c = doit ? __builtin_amdgcn_sqrtf(hc) : 1.f;
-        const float sn = doit ? (dd >= 0.f ? ga : -ga) * ri * __builtin_amdgcn_rsqf(hc) : 0.f;
-        kp[0] = c * xp0 - sn * xq0;
-        kq[0] = sn * xp0 + c * xq0;
-        kp[16] = c * xp1 - sn * xq1;
-        kq[16] = sn * xp1 + c * xq1;
-        vp[0] = c * yp0 - sn * yq0;
-        vq[0] = sn * yp0 + c * yq0;
-        vp[16] = c * yp1 - sn * yq1;
-        vq[16] = sn * yp1 + c * yq1;
-        big |= (doit && g2 > 1e-8f * ab) ? 1 : 0;
+  for (int sweep = 0; sweep < max_sweeps; ++sweep) {
+    int big = 0;
+    for (int rnd = 0; rnd < rounds; ++rnd) {
+      const uint32_t pq_next = sched[(rnd + 1 < rounds ? rnd + 1 : 0) * np + pair];
+      float* kp = reinterpret_cast<float*>(base + (pq & 0xFFFFu));
+      float* kq = reinterpret_cast<float*>(base + (pq >> 16));
+      float xp[RL], xq[RL];
+      float al = 0.f, be = 0.f, ga = 0.f;
+#pragma unroll
+      for (int i = 0; i < RL; ++i) {
+        xp[i] = kp[GW * i];
+        xq[i] = kq[GW * i];
       }
-  // advance the circle: players 1 .. n-1 move up one position
-      pa = pa == 0 ? 0 : (pa == n - 1 ? 1 : pa + 1);
-      pb = pb == 0 ? 0 : (pb == n - 1 ? 1 : pb + 1);
+#pragma unroll
+      for (int i = 0; i < RL; ++i) {
+        al = fmaf(xp[i], xp[i], al);
+        be = fmaf(xq[i], xq[i], be);
+        ga = fmaf(xp[i], xq[i], ga);
+      }
+      al = group_sumf<GW>(al);
+      be = group_sumf<GW>(be);
+      ga = group_sumf<GW>(ga);
+      const float g2 = ga * ga, ab = al * be;
+      const bool doit = g2 > 1e-14f * ab && ga != 0.f;
+      const float dd = be - al;
+      const float ri = __builtin_amdgcn_rsqf(fmaf(dd, dd, 4.f * g2));
+      const float hc = fmaf(0.5f * fabsf(dd), ri, 0.5f);
+      const float rh = __builtin_amdgcn_rsqf(hc);
+      const float c = doit ? hc * rh : 1.f;
+      const float sn = doit ? (dd >= 0.f ? ga : -ga) * ri * rh : 0.f;
+#pragma unroll
+      for (int i = 0; i < RL; ++i) {
+        kp[GW * i] = c * xp[i] - sn * xq[i];
+        kq[GW * i] = sn * xp[i] + c * xq[i];
+      }
+      big |= g2 > 1e-8f * ab ? 1 : 0;
+      pq = pq_next;
       __syncthreads();
     }
     sweeps = sweep + 1;
-    // quadratic convergence: after a sweep whose rotations all had |cos| <= 1e-4
-    // the remaining coupling is ~1e-8 relative, so no verification sweep is run
     if (!__syncthreads_or(big)) break;
   }
-  if (tid < l) {
+  return sweeps;
+}
+
+// Outputs of the core from the swept K (column a: 2^-e sigma_a V_R[:, a], column
+// stride ld, n rows): columns ranked by sigma (ties by index); for rank c < r,
+// column a, S_B[row][c] = (X V_R)[row][a] sigma_a^1/2 and S_A[row][c] =
+// V_R[row][a] sigma_a^-1/2 (X = R_Y^-1, l x l row-major upper triangular, so
+// that B = Y S_B), sigma, the stats (sum of the r sigma^2, sweeps) and the
+// objective.  All threads call it.
+__device__ void core_finish(const float* K, int ld, int l, int n, double ksc, const float* X, int r, float* SB,
+                            float* SA, float* sigma, double* stats, const ObjectiveArgs& obj, int sweeps,
+                            double* norm2, int* order) {
+  const int tid = threadIdx.x, nt = blockDim.x;
+  for (int a = tid; a < l; a += nt) {
     double s = 0.0;
-    for (int row = 0; row < n; ++row) s += static_cast<double>(K[tid * LD + row]) * static_cast<double>(K[tid * LD + row]);
-    norm2[tid] = s / (kscale * kscale);
+    for (int row = 0; row < n; ++row) s += static_cast<double>(K[a * ld + row]) * static_cast<double>(K[a * ld + row]);
+    norm2[a] = s / (ksc * ksc);
   }
   __syncthreads();
-  if (tid < l) {
-    const double la = norm2[tid];
+  for (int a = tid; a < l; a += nt) {
+    const double la = norm2[a];
     int rank = 0;
-    for (int b = 0; b < l; ++b) rank += (norm2[b] > la || (norm2[b] == la && b < tid)) ? 1 : 0;
-    order[rank] = tid;
+    for (int b = 0; b < l; ++b) rank += (norm2[b] > la || (norm2[b] == la && b < a)) ? 1 : 0;
+    order[rank] = a;
   }
   __syncthreads();
-  for (int idx = tid; idx < l * r; idx += blockDim.x) {
+  for (int idx = tid; idx < l * r; idx += nt) {
     const int row = idx / r, c = idx - row * r;
     const int a = order[c];
     const double sg = sqrt(norm2[a]);
     const double sq = sqrt(sg);
+    const double kn = sg * ksc;   // |K_a|
     double acc = 0.0;
-    for (int j = row; j < l; ++j) acc = fma(static_cast<double>(Xs[row * l + j]), static_cast<double>(V[a * LD + j]), acc);
-    SB[row * r + c] = static_cast<float>(acc * sq);
-    SA[row * r + c] = sg > 0.0 ? static_cast<float>(V[a * LD + row] / sq) : 0.f;
+    for (int j = row; j < l; ++j) acc = fma(static_cast<double>(X[row * l + j]), static_cast<double>(K[a * ld + j]), acc);
+    SB[row * r + c] = kn > 0.0 ? static_cast<float>(acc * sq / kn) : 0.f;
+    SA[row * r + c] = kn > 0.0 ? static_cast<float>(static_cast<double>(K[a * ld + row]) / (kn * sq)) : 0.f;
   }
-  if (tid < r) sigma[tid] = static_cast<float>(sqrt(norm2[order[tid]]));
+  for (int c = tid; c < r; c += nt) sigma[c] = static_cast<float>(sqrt(norm2[order[c]]));
   double s2 = 0.0;
   for (int c = 0; c < r; ++c) s2 += norm2[order[c]];
   if (tid == 0 && stats) {
@@ -536,8 +294,51 @@ __global__ __launch_bounds__(256) void core_small_kernel(const double* __restric
   write_objective(obj, s2);
 }
 
+// mode 2 for l <= LM (LM <= 32), 16 lanes per pair: 16 ceil(l / 2) threads
+// rounded up to whole waves.  Wave 0 factors H in fp64 and writes K = 2^-e R^T.
+template <int LM>
+__global__ __launch_bounds__(256) void core_small_kernel(const double* __restrict__ gram, int l,
+                                                         const float* __restrict__ Xinv, int r, float* __restrict__ SB,
+                                                         float* __restrict__ SA, float* __restrict__ sigma,
+                                                         double* __restrict__ stats, ObjectiveArgs obj) {
+  constexpr int LD = 33;
+  __shared__ double rowbuf[64];
+  __shared__ float K[32 * LD];
+  __shared__ float Xs[32 * 32];
+  __shared__ uint32_t sched[31 * 16];
+  __shared__ double norm2[32];
+  __shared__ int order[32];
+  __shared__ double kscale;
+  const int tid = threadIdx.x;
+  const int n = l + (l & 1);
+  for (int e = tid; e < l * l; e += blockDim.x) Xs[e] = Xinv[e];
+  build_schedule(sched, n, blockDim.x / 16, LD);
+  if (tid < 64) {
+    double g[LM], t[LM];
+    chol_wave<LM, false>(gram, l, g, t, rowbuf);
+    // 2^-e with 2^e at the scale of R's largest entry, so the fp32 sweeps
+    // neither overflow nor underflow whatever the magnitude of E
+    double m = 0.0;
+#pragma unroll
+    for (int a = 0; a < LM; ++a) m = fmax(m, (a <= tid && tid < l) ? fabs(g[a]) : 0.0);
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) m = fmax(m, __shfl_xor(m, off));
+    const double sc = m > 0.0 ? ldexp(1.0, -ilogb(m)) : 1.0;
+    if (tid == 0) kscale = sc;
+    // lane b holds column b of R: K[a][b] = R[a][b] (column a of K = row a of R)
+    if (tid < LD) {
+#pragma unroll
+      for (int a = 0; a < 32; ++a)
+        K[a * LD + tid] = (a < LM && a <= tid && tid < l) ? static_cast<float>(g[a < LM ? a : 0] * sc) : 0.f;
+    }
+  }
+  __syncthreads();
+  const int sweeps = jacobi_columns<16, 2>(K, sched, n, 30);
+  core_finish(K, LD, l, n, kscale, Xs, r, SB, SA, sigma, stats, obj, sweeps, norm2, order);
+}
+
 // ---------------------------------------------------------------------------
-// The two solves for 32 < l <= kMaxL, by one workgroup of 640 threads
+// The two solves for 32 < l <= kMaxL, by one workgroup of 640
 // threads (pair i of a Jacobi round on lanes 16 i .. 16 i + 15).
 //
 // chol_wide: right-looking Cholesky of the fp64 Gram with the matrix in
@@ -647,9 +448,11 @@ __global__ __launch_bounds__(64 * NW) void solve_wide_kernel(const double* __res
                                                                   float* __restrict__ sigma, double* __restrict__ stats,
                                                                   ObjectiveArgs obj) {
   constexpr int NB = kMaxL * kWideLd;
+  constexpr int NP = 64 * NW / GW;   // pair slots
+  static_assert(2 * NP <= kMaxL, "the padding slots' zero columns lie inside K");
   __shared__ double Rm[MODE == 2 ? NB : 1];
   __shared__ float Kf[MODE == 2 ? NB : 1];
-  __shared__ float V[MODE == 2 ? NB : 1];
+  __shared__ uint32_t sched[MODE == 2 ? (kMaxL - 1) * NP : 1];
   __shared__ double rowbuf[4 * kWideLd];
   __shared__ double norm2[kMaxL];
   __shared__ int order[kMaxL];
@@ -660,8 +463,10 @@ __global__ __launch_bounds__(64 * NW) void solve_wide_kernel(const double* __res
     chol_wide<true, NW>(gram, l, nullptr, Xinv, rowbuf, scratch);
     return;
   }
+  const int n = l + (l & 1);
+  build_schedule(sched, n, NP, kWideLd);
   chol_wide<false, NW>(gram, l, Rm, nullptr, rowbuf, scratch);
-  // K = 2^-e R (column c of K = column c of R), fp32, with 2^e at the scale of R's largest entry
+  // K = 2^-e R^T (column c of K = row c of R), fp32, with 2^e at the scale of R's largest entry
   if (tid < 64) {
     double m = 0.0;
     for (int a = tid; a < l; a += 64) m = fmax(m, fabs(Rm[a * kWideLd + a]));
@@ -671,101 +476,14 @@ __global__ __launch_bounds__(64 * NW) void solve_wide_kernel(const double* __res
   }
   __syncthreads();
   const double ksc = scratch[1];
-  const int n = l + (l & 1);
-  for (int e = tid; e < kMaxL * kWideLd; e += nt) {
-    const int c = e / kWideLd, row = e - c * kWideLd;
-    Kf[e] = (c < l && row <= c) ? static_cast<float>(Rm[row * kWideLd + c] * ksc) : 0.f;
-    V[e] = (row == c) ? 1.f : 0.f;
+  for (int e = tid; e < NB; e += nt) {
+    const int c = e / kWideLd, j = e - c * kWideLd;
+    Kf[e] = (c < l && j >= c && j < l) ? static_cast<float>(Rm[c * kWideLd + j] * ksc) : 0.f;
   }
   __syncthreads();
-  // one-sided Jacobi, fp32, GW lanes per pair (rows sub + GW i)
   constexpr int RL = (kMaxL + GW - 1) / GW;
-  const int pair = tid / GW, sub = tid % GW;
-  const bool active = pair < n / 2;
-  int pa = pair, pb = n - 1 - pair;
-  int sweeps = 0;
-  for (int sweep = 0; sweep < 40; ++sweep) {
-    int big = 0;
-    for (int rnd = 0; rnd < n - 1; ++rnd) {
-      if (active) {
-        const int p = pa < pb ? pa : pb, q = pa < pb ? pb : pa;
-        float* kp = Kf + p * kWideLd + sub;
-        float* kq = Kf + q * kWideLd + sub;
-        float* vp = V + p * kWideLd + sub;
-        float* vq = V + q * kWideLd + sub;
-        float xp[RL], xq[RL], yp[RL], yq[RL];
-        float al = 0.f, be = 0.f, ga = 0.f;
-#pragma unroll
-        for (int i = 0; i < RL; ++i) {
-          const bool in = sub + GW * i < n;
-          xp[i] = in ? kp[GW * i] : 0.f;
-          xq[i] = in ? kq[GW * i] : 0.f;
-          yp[i] = in ? vp[GW * i] : 0.f;
-          yq[i] = in ? vq[GW * i] : 0.f;
-          al = fmaf(xp[i], xp[i], al);
-          be = fmaf(xq[i], xq[i], be);
-          ga = fmaf(xp[i], xq[i], ga);
-        }
-        al = group_sumf<GW>(al);
-        be = group_sumf<GW>(be);
-        ga = group_sumf<GW>(ga);
-        const float g2 = ga * ga, ab = al * be;
-        const bool doit = q < l && g2 > 1e-14f * ab && ga != 0.f;
-        const float dd = be - al;
-        const float ri = __builtin_amdgcn_rsqf(fmaf(dd, dd, 4.f * g2));
-        const float hc = fmaf(0.5f * fabsf(dd), ri, 0.5f);
-        const float c = doit ? __builtin_amdgcn_sqrtf(hc) : 1.f;
-        const float sn = doit ? (dd >= 0.f ? ga : -ga) * ri * __builtin_amdgcn_rsqf(hc) : 0.f;
-#pragma unroll
-        for (int i = 0; i < RL; ++i) {
-          if (sub + GW * i < n) {
-            kp[GW * i] = c * xp[i] - sn * xq[i];
-            kq[GW * i] = sn * xp[i] + c * xq[i];
-            vp[GW * i] = c * yp[i] - sn * yq[i];
-            vq[GW * i] = sn * yp[i] + c * yq[i];
-          }
-        }
-        big |= (doit && g2 > 1e-8f * ab) ? 1 : 0;
-      }
-      pa = pa == 0 ? 0 : (pa == n - 1 ? 1 : pa + 1);
-      pb = pb == 0 ? 0 : (pb == n - 1 ? 1 : pb + 1);
-      __syncthreads();
-    }
-    sweeps = sweep + 1;
-    if (!__syncthreads_or(big)) break;
-  }
-  if (tid < l) {
-    double sum = 0.0;
-    for (int row = 0; row < n; ++row)
-      sum += static_cast<double>(Kf[tid * kWideLd + row]) * static_cast<double>(Kf[tid * kWideLd + row]);
-    norm2[tid] = sum / (ksc * ksc);
-  }
-  __syncthreads();
-  if (tid < l) {
-    const double la = norm2[tid];
-    int rank = 0;
-    for (int b = 0; b < l; ++b) rank += (norm2[b] > la || (norm2[b] == la && b < tid)) ? 1 : 0;
-    order[rank] = tid;
-  }
-  __syncthreads();
-  for (int idx = tid; idx < l * r; idx += nt) {
-    const int row = idx / r, c = idx - row * r;
-    const int a = order[c];
-    const double sg = sqrt(norm2[a]);
-    const double sq = sqrt(sg);
-    double acc = 0.0;
-    for (int j = row; j < l; ++j) acc = fma(static_cast<double>(Xinv[row * l + j]), static_cast<double>(V[a * kWideLd + j]), acc);
-    SB[row * r + c] = static_cast<float>(acc * sq);
-    SA[row * r + c] = sg > 0.0 ? static_cast<float>(V[a * kWideLd + row] / sq) : 0.f;
-  }
-  if (tid < r) sigma[tid] = static_cast<float>(sqrt(norm2[order[tid]]));
-  double s2 = 0.0;
-  for (int c = 0; c < r; ++c) s2 += norm2[order[c]];
-  if (tid == 0 && stats) {
-    stats[0] = s2;
-    stats[1] = static_cast<double>(sweeps);
-  }
-  write_objective(obj, s2);
+  const int sweeps = jacobi_columns<GW, RL>(Kf, sched, n, 40);
+  core_finish(Kf, kWideLd, l, n, ksc, Xinv, r, SB, SA, sigma, stats, obj, sweeps, norm2, order);
 }
 
 // Sum of the split-K partials, sum_s part[s], in fixed order for a tile of
@@ -1072,7 +790,8 @@ void small_wave_typed(int mode, const double* gram, int l, float* Xinv, int r, f
   if (mode == 1)
     LQ_LAUNCH("chol_inv", chol_inv_wave_kernel<LM>, dim3(1), dim3(64), 0, s, gram, l, Xinv);
   else
-    LQ_LAUNCH("core_svd", core_small_kernel<LM>, dim3(1), dim3(256), 0, s, gram, l, Xinv, r, SB, SA, sigma, stats, obj);
+    LQ_LAUNCH("core_svd", core_small_kernel<LM>, dim3(1), dim3(static_cast<unsigned>(round_up(16 * ((l + 1) / 2), 64))), 0,
+              s, gram, l, Xinv, r, SB, SA, sigma, stats, obj);
 }
 
 // l <= 32: the register Cholesky is unrolled for the smallest of 8/16/24/32 rows that holds l.
