@@ -490,21 +490,30 @@ __global__ __launch_bounds__(64 * NW) void solve_wide_kernel(const double* __res
 // kGramRows rows, optionally right-multiplied by X (l x l fp32, upper
 // triangular; entries below the diagonal are ignored), written in fragment
 // order (zero-padded to m_pad rows), plus the fp64 Gram partial (packed upper
-// triangle) of the tile when gram_parts is given.  Every loop over the tile's
-// rows or X's rows has a compile-time trip count, so its LDS reads issue
-// back to back.
+// triangle) of the tile when gram_parts is given.  The two small contractions
+// run on the matrix cores, one 16 x 16 output tile per wave at a time: the X
+// product with fp32 MFMA (16x16x4), the Gram with fp64 MFMA (16x16x4) over the
+// tile's rows; each accumulates its K steps in ascending order, so results are
+// deterministic.
+typedef float mfma_f4 __attribute__((ext_vector_type(4)));
+typedef double mfma_d4 __attribute__((ext_vector_type(4)));
+
 template <int NT>
 __global__ __launch_bounds__(kReduceThreads) void reduce_gram_kernel(const float* __restrict__ part, int S, int64_t m,
                                                           int64_t m_pad, int l, const float* __restrict__ X,
                                                           float* __restrict__ out, double* __restrict__ gram_parts) {
   constexpr int LP = 16 * NT, PER = (kGramRows * LP + kReduceThreads - 1) / kReduceThreads, LDR = LP + 1;
-  // wide panels (NT >= 3) keep fewer loads in flight and unroll less, so the
-  // per-thread state fits the register file of a 512-thread workgroup
-  constexpr int QB = NT <= 2 ? 8 : 2, JU = NT <= 2 ? LP : 16, RU = NT <= 2 ? kGramRows : 16;
+  constexpr int NW = kReduceThreads / 64;
+  static_assert(kGramRows % 16 == 0, "whole 16-row MFMA tiles");
+  // wide panels (NT >= 3) keep fewer loads in flight, so the per-thread state
+  // fits the register file of a 512-thread workgroup
+  constexpr int QB = NT <= 2 ? 8 : 2;
   __shared__ float rows[kGramRows * LDR];
+  __shared__ float rowsx[kGramRows * LDR];
   __shared__ float Xs[LP * LP];
   const int64_t r0 = static_cast<int64_t>(blockIdx.x) * kGramRows;
   const int64_t stride = m * LP;
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, li = lane & 15, lk = lane >> 4;
   if (X) {
     for (int e = threadIdx.x; e < LP * LP; e += blockDim.x) {
       const int a = e / LP, b = e - a * LP;
@@ -545,26 +554,22 @@ __global__ __launch_bounds__(kReduceThreads) void reduce_gram_kernel(const float
     if (idx < kGramRows * LP) rows[(idx / LP) * LDR + idx % LP] = acc[u];
   }
   __syncthreads();
+  const float* R = rows;
   if (X) {
-    // the products go back into acc (all reads of `rows` finish before the barrier)
+    // tile (rt, ct) of rows x X: lane (li, lk) supplies A[li][lk] = rows[16 rt + li][4 ks + lk] and
+    // B[lk][li] = X[4 ks + lk][16 ct + li]; D[4 lk + v][li] comes back in element v
+    for (int t = w; t < (kGramRows / 16) * NT; t += NW) {
+      const int rt = t / NT, ct = t - rt * NT;
+      mfma_f4 dacc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int u = 0; u < PER; ++u) {
-      const int idx = threadIdx.x + kReduceThreads * u;
-      float a = 0.f;
-      if (idx < kGramRows * LP) {
-        const int rr = idx / LP, n = idx - rr * LP;
-#pragma unroll JU
-        for (int j = 0; j < LP; ++j) a = fmaf(rows[rr * LDR + j], Xs[j * LP + n], a);
-      }
-      acc[u] = a;
+      for (int ks = 0; ks < LP / 4; ++ks)
+        dacc = __builtin_amdgcn_mfma_f32_16x16x4f32(rows[(16 * rt + li) * LDR + 4 * ks + lk],
+                                                    Xs[(4 * ks + lk) * LP + 16 * ct + li], dacc, 0, 0, 0);
+#pragma unroll
+      for (int v = 0; v < 4; ++v) rowsx[(16 * rt + 4 * lk + v) * LDR + 16 * ct + li] = dacc[v];
     }
     __syncthreads();
-#pragma unroll
-    for (int u = 0; u < PER; ++u) {
-      const int idx = threadIdx.x + kReduceThreads * u;
-      if (idx < kGramRows * LP) rows[(idx / LP) * LDR + idx % LP] = acc[u];
-    }
-    __syncthreads();
+    R = rowsx;
   }
   // fragment-order output: a thread writes rows 4 q .. 4 q + 3 of one column as one float4
   for (int qd = threadIdx.x; qd < (kGramRows / 4) * LP; qd += blockDim.x) {
@@ -572,20 +577,32 @@ __global__ __launch_bounds__(kReduceThreads) void reduce_gram_kernel(const float
     const int64_t row = r0 + 4 * q;
     if (row < m_pad)
       *reinterpret_cast<float4*>(out + frag_index(row, n, NT)) =
-          make_float4(rows[(4 * q) * LDR + n], rows[(4 * q + 1) * LDR + n], rows[(4 * q + 2) * LDR + n],
-                      rows[(4 * q + 3) * LDR + n]);
+          make_float4(R[(4 * q) * LDR + n], R[(4 * q + 1) * LDR + n], R[(4 * q + 2) * LDR + n],
+                      R[(4 * q + 3) * LDR + n]);
   }
   if (gram_parts == nullptr || r0 >= m) return;
-  // Gram partial: entry (a, b), a <= b, summed over the tile's rows in order
+  // Gram partial, tiles (ta, tb), ta <= tb: A[li][lk] = R[4 ks + lk][16 ta + li],
+  // B[lk][li] = R[4 ks + lk][16 tb + li]; the fp64 MFMA returns D[lk + 4 v][li] in
+  // element v.  Rows beyond m and columns beyond l are zero in R.
   double* gp = gram_parts + static_cast<int64_t>(blockIdx.x) * (l * (l + 1) / 2);
-  for (int e = threadIdx.x; e < l * l; e += blockDim.x) {
-    const int a = e / l, b = e - a * l;
-    if (b < a) continue;
-    double sum = 0.0;
-#pragma unroll RU
-    for (int rr = 0; rr < kGramRows; ++rr)
-      sum = fma(static_cast<double>(rows[rr * LDR + a]), static_cast<double>(rows[rr * LDR + b]), sum);
-    gp[packed_index(a, b, l)] = sum;
+  for (int t = w; t < NT * (NT + 1) / 2; t += NW) {
+    int ta = 0, rem = t;
+    while (rem >= NT - ta) {
+      rem -= NT - ta;
+      ++ta;
+    }
+    const int tb = ta + rem;
+    mfma_d4 dacc = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+    for (int ks = 0; ks < kGramRows / 4; ++ks)
+      dacc = __builtin_amdgcn_mfma_f64_16x16x4f64(static_cast<double>(R[(4 * ks + lk) * LDR + 16 * ta + li]),
+                                                  static_cast<double>(R[(4 * ks + lk) * LDR + 16 * tb + li]), dacc,
+                                                  0, 0, 0);
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int a = 16 * ta + lk + 4 * v, b = 16 * tb + li;
+      if (a <= b && b < l) gp[packed_index(a, b, l)] = dacc[v];
+    }
   }
 }
 
