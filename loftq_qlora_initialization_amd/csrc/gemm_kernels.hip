@@ -53,7 +53,7 @@ __device__ __forceinline__ float4 load_run4(const float* __restrict__ p, int64_t
 template <int NT>
 struct NnCfg {
   static constexpr int RT = 2;                 // 16-row MFMA tiles per wave (each X fragment feeds both)
-  static constexpr int D = NT <= 2 ? 4 : 2;    // register ring depth (K steps of 16)
+  static constexpr int D = NT <= 2 ? 3 : 2;    // register ring depth (K steps of 16)
   static constexpr int WR = NT <= 2 ? 4 : 2;   // waves along rows
   static constexpr int WK = NT <= 2 ? 1 : 2;   // waves splitting the workgroup's K range
 };
@@ -122,6 +122,10 @@ __global__ __launch_bounds__(64 * NnCfg<NT>::WR * NnCfg<NT>::WK) void gemm_nn_ke
     for (int u = 0; u < D; ++u) {
       compute(u);
       load(u, (rd + 1) * D + u);
+      // keep the slot's reload here: left to itself the scheduler sinks every
+      // load below the last compute of the round, and the ring then hides no
+      // memory latency behind the MFMAs
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
 #pragma unroll
@@ -239,6 +243,10 @@ __global__ __launch_bounds__(64 * TnCfg<NT>::WC * TnCfg<NT>::WR) void gemm_tn_ke
     for (int u = 0; u < D; ++u) {
       compute(u);
       load(u, (rd + 1) * D + u);
+      // keep the slot's reload here: left to itself the scheduler sinks every
+      // load below the last compute of the round, and the ring then hides no
+      // memory latency behind the MFMAs
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
 #pragma unroll
