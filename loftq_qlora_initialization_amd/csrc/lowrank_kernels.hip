@@ -295,13 +295,15 @@ __device__ void core_finish(const float* K, int ld, int l, int n, double ksc, co
 }
 
 // mode 2 for l <= LM (LM <= 32), 16 lanes per pair: 16 ceil(l / 2) threads
-// rounded up to whole waves.  Wave 0 factors H in fp64 and writes K = 2^-e R^T.
+// rounded up to whole waves.  The workgroup sums the P Gram partials of C
+// (gram_sum_block), wave 0 factors H in fp64 and writes K = 2^-e R^T.
 template <int LM>
-__global__ __launch_bounds__(256) void core_small_kernel(const double* __restrict__ gram, int l,
+__global__ __launch_bounds__(256) void core_small_kernel(const double* __restrict__ gparts, int P, int l,
                                                          const float* __restrict__ Xinv, int r, float* __restrict__ SB,
                                                          float* __restrict__ SA, float* __restrict__ sigma,
                                                          double* __restrict__ stats, ObjectiveArgs obj) {
   constexpr int LD = 33;
+  __shared__ double gsum[5 * (LM * (LM + 1) / 2)];   // (waves + 1) E_ doubles, at most 4 waves
   __shared__ double rowbuf[64];
   __shared__ float K[32 * LD];
   __shared__ float Xs[32 * 32];
@@ -313,6 +315,7 @@ __global__ __launch_bounds__(256) void core_small_kernel(const double* __restric
   const int n = l + (l & 1);
   for (int e = tid; e < l * l; e += blockDim.x) Xs[e] = Xinv[e];
   build_schedule(sched, n, blockDim.x / 16, LD);
+  const double* gram = gram_sum_block<LM>(gparts, P, l, gsum);
   if (tid < 64) {
     double g[LM], t[LM];
     chol_wave<LM, false>(gram, l, g, t, rowbuf);
@@ -801,23 +804,24 @@ void launch_reduce(int nt, const float* part, int S, int64_t m, int64_t m_pad, i
   }
 }
 
+// mode 1 factors the summed Gram `gram`; mode 2 sums the P partials `gparts` itself.
 template <int LM>
-void small_wave_typed(int mode, const double* gram, int l, float* Xinv, int r, float* SB, float* SA, float* sigma,
-                      double* stats, const ObjectiveArgs& obj, hipStream_t s) {
+void small_wave_typed(int mode, const double* gram, const double* gparts, int P, int l, float* Xinv, int r, float* SB,
+                      float* SA, float* sigma, double* stats, const ObjectiveArgs& obj, hipStream_t s) {
   if (mode == 1)
     LQ_LAUNCH("chol_inv", chol_inv_wave_kernel<LM>, dim3(1), dim3(64), 0, s, gram, l, Xinv);
   else
     LQ_LAUNCH("core_svd", core_small_kernel<LM>, dim3(1), dim3(static_cast<unsigned>(round_up(16 * ((l + 1) / 2), 64))), 0,
-              s, gram, l, Xinv, r, SB, SA, sigma, stats, obj);
+              s, gparts, P, l, Xinv, r, SB, SA, sigma, stats, obj);
 }
 
 // l <= 32: the register Cholesky is unrolled for the smallest of 8/16/24/32 rows that holds l.
-void launch_small_wave(int mode, const double* gram, int l, float* Xinv, int r, float* SB, float* SA, float* sigma,
-                       double* stats, const ObjectiveArgs& obj, hipStream_t s) {
-  if (l <= 8) small_wave_typed<8>(mode, gram, l, Xinv, r, SB, SA, sigma, stats, obj, s);
-  else if (l <= 16) small_wave_typed<16>(mode, gram, l, Xinv, r, SB, SA, sigma, stats, obj, s);
-  else if (l <= 24) small_wave_typed<24>(mode, gram, l, Xinv, r, SB, SA, sigma, stats, obj, s);
-  else small_wave_typed<32>(mode, gram, l, Xinv, r, SB, SA, sigma, stats, obj, s);
+void launch_small_wave(int mode, const double* gram, const double* gparts, int P, int l, float* Xinv, int r, float* SB,
+                       float* SA, float* sigma, double* stats, const ObjectiveArgs& obj, hipStream_t s) {
+  if (l <= 8) small_wave_typed<8>(mode, gram, gparts, P, l, Xinv, r, SB, SA, sigma, stats, obj, s);
+  else if (l <= 16) small_wave_typed<16>(mode, gram, gparts, P, l, Xinv, r, SB, SA, sigma, stats, obj, s);
+  else if (l <= 24) small_wave_typed<24>(mode, gram, gparts, P, l, Xinv, r, SB, SA, sigma, stats, obj, s);
+  else small_wave_typed<32>(mode, gram, gparts, P, l, Xinv, r, SB, SA, sigma, stats, obj, s);
 }
 
 void panels(const PanelJob& j0, const PanelJob& j1, int l, int nt, int w, hipStream_t s) {
@@ -990,9 +994,13 @@ hipError_t run_lowrank(const float* E, const SvdPlan& pl, int q, const float* om
       return;
     }
     const int P = transposed ? pl.gram_parts_k : pl.gram_parts_d;
+    if (l <= 32 && mode == 2) {
+      launch_small_wave(2, nullptr, gparts, P, l, Xinv, r, SB, SA, sigma, stats, obj, s);
+      return;
+    }
     LQ_LAUNCH("gram_sum", gram_sum_kernel, dim3((E_ + 63) / 64), dim3(1024), 0, s, gparts, P, E_, gtotal);
     if (l <= 32)
-      launch_small_wave(mode, gtotal, l, Xinv, r, SB, SA, sigma, stats, mode == 2 ? obj : none, s);
+      launch_small_wave(1, gtotal, nullptr, 0, l, Xinv, r, SB, SA, sigma, stats, none, s);
     else if (mode == 1)
       LQ_LAUNCH("chol_inv", (solve_wide_kernel<1, kWideCholWaves, 16>), dim3(1), dim3(64 * kWideCholWaves), 0, s, gtotal,
                 l, Xinv, r, SB, SA, sigma, stats, none);

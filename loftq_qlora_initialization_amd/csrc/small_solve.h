@@ -85,29 +85,27 @@ __device__ __forceinline__ void chol_wave(const double* __restrict__ gram, int l
 }
 
 // Sum of the P fp64 Gram partials (packed upper triangles of E_ = l (l + 1) / 2
-// entries, partial p at parts + p E_) and its Cholesky with X = R^-1 (fp32,
-// row-major l x l, entries below the diagonal unspecified), by one workgroup
-// of 256 threads.  Wave w sums partials w, w + 4, w + 8, ... of each entry in
-// that order; the four wave sums are added in wave order, so the total is
-// deterministic.  lds holds at least 5 E_ doubles.
-// Sum of the P fp64 Gram partials into lds[4 E_ ..): wave w sums partials
-// w, w + 4, ... of each entry in that order, then the four wave sums are added
-// in wave order.  Returns the total's address.
+// entries, partial p at parts + p E_) by one workgroup of NW = blockDim / 64
+// waves.  Wave w sums partials w, w + NW, w + 2 NW, ... of each entry in that
+// order; the NW wave sums are then added in wave order, so the total is
+// deterministic.  lds holds at least (NW + 1) E_ doubles; returns the address
+// of the total (lds + NW E_).
 template <int LM>
 __device__ __forceinline__ double* gram_sum_block(const double* __restrict__ parts, int P, int l, double* lds) {
   constexpr int EPL = (LM * (LM + 1) / 2 + 63) / 64;
   const int E_ = l * (l + 1) / 2;
+  const int NW = static_cast<int>(blockDim.x >> 6);
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
   double s[EPL];
 #pragma unroll
   for (int i = 0; i < EPL; ++i) s[i] = 0.0;
-  for (int p = w; p < P; p += 32) {
+  for (int p = w; p < P; p += 8 * NW) {
     double v[8][EPL];
 #pragma unroll
     for (int q = 0; q < 8; ++q)
 #pragma unroll
       for (int i = 0; i < EPL; ++i) {
-        const int pp = p + 4 * q, e = lane + 64 * i;
+        const int pp = p + NW * q, e = lane + 64 * i;
         v[q][i] = (pp < P && e < E_) ? parts[static_cast<int64_t>(pp) * E_ + e] : 0.0;
       }
 #pragma unroll
@@ -121,8 +119,12 @@ __device__ __forceinline__ double* gram_sum_block(const double* __restrict__ par
     if (e < E_) lds[w * E_ + e] = s[i];
   }
   __syncthreads();
-  double* gram = lds + 4 * E_;
-  for (int e = tid; e < E_; e += blockDim.x) gram[e] = ((lds[e] + lds[E_ + e]) + lds[2 * E_ + e]) + lds[3 * E_ + e];
+  double* gram = lds + NW * E_;
+  for (int e = tid; e < E_; e += blockDim.x) {
+    double t = lds[e];
+    for (int q = 1; q < NW; ++q) t += lds[q * E_ + e];
+    gram[e] = t;
+  }
   __syncthreads();
   return gram;
 }
