@@ -73,16 +73,39 @@ __device__ __forceinline__ int rr_player(int pos, int rnd, int n) {
   return pos == 0 ? 0 : 1 + (pos - 1 + rnd) % (n - 1);
 }
 
+// Relative objective sqrt((|E|^2 - sum sigma^2) / |W|^2) from the two sums
+// (and sqrt(|E|^2 / |W|^2) into out0); the caller's thread 0 only.
+__device__ void objective_from_sums(const ObjectiveArgs& o, double es, double ws, double sig2) {
+  const double num = es - sig2;
+  *o.out = ws > 0.0 ? sqrt((num > 0.0 ? num : 0.0) / ws) : 0.0;
+  if (o.out0 != nullptr) *o.out0 = ws > 0.0 ? sqrt(es / ws) : 0.0;
+}
+
 // All threads of the workgroup call this; thread 0 writes the objective.
 __device__ void write_objective(const ObjectiveArgs& o, double sig2) {
   if (o.out == nullptr) return;
   const double es = block_sum_fixed(o.e_parts, o.ne);
   const double ws = block_sum_fixed(o.w_parts, o.nw);
-  if (threadIdx.x == 0) {
-    const double num = es - sig2;
-    *o.out = ws > 0.0 ? sqrt((num > 0.0 ? num : 0.0) / ws) : 0.0;
-    if (o.out0 != nullptr) *o.out0 = ws > 0.0 ? sqrt(es / ws) : 0.0;
+  if (threadIdx.x == 0) objective_from_sums(o, es, ws, sig2);
+}
+
+// Sum of p[0 .. n) by one wave in a fixed order (lane-strided partial sums,
+// four in flight, then a butterfly over the lanes); every lane gets the total.
+__device__ double wave_sum_fixed(const double* __restrict__ p, int n) {
+  const int lane = threadIdx.x & 63;
+  double a0 = 0.0, a1 = 0.0, a2 = 0.0, a3 = 0.0;
+  int i = lane;
+  for (; i + 192 < n; i += 256) {
+    a0 += p[i];
+    a1 += p[i + 64];
+    a2 += p[i + 128];
+    a3 += p[i + 192];
   }
+  for (; i < n; i += 64) a0 += p[i];
+  double s = (a0 + a1) + (a2 + a3);
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) s += __shfl_xor(s, off);
+  return s;
 }
 
 // Sum of P Gram partials (packed upper triangles, E = l(l+1)/2 doubles each)
@@ -206,7 +229,7 @@ __device__ int jacobi_columns(float* K, const uint32_t* sched, int n, int max_sw
   uint32_t pq = sched[pair];
   int sweeps = 0;
   for (int sweep = 0; sweep < max_sweeps; ++sweep) {
-    int big = 0;
+    uint64_t big = 0;
     for (int rnd = 0; rnd < rounds; ++rnd) {
       const uint32_t pq_next = sched[(rnd + 1 < rounds ? rnd + 1 : 0) * np + pair];
       float* kp = reinterpret_cast<float*>(base + (pq & 0xFFFFu));
@@ -228,7 +251,8 @@ __device__ int jacobi_columns(float* K, const uint32_t* sched, int n, int max_sw
       be = group_sumf<GW>(be);
       ga = group_sumf<GW>(ga);
       const float g2 = ga * ga, ab = al * be;
-      const bool doit = g2 > 1e-14f * ab && ga != 0.f;
+      // g2 > 0 here also keeps dd^2 + 4 g2 > 0 (alpha beta >= 0)
+      const bool doit = g2 > 1e-14f * ab;
       const float dd = be - al;
       const float ri = __builtin_amdgcn_rsqf(fmaf(dd, dd, 4.f * g2));
       const float hc = fmaf(0.5f * fabsf(dd), ri, 0.5f);
@@ -240,12 +264,12 @@ __device__ int jacobi_columns(float* K, const uint32_t* sched, int n, int max_sw
         kp[GW * i] = c * xp[i] - sn * xq[i];
         kq[GW * i] = sn * xp[i] + c * xq[i];
       }
-      big |= g2 > 1e-8f * ab ? 1 : 0;
+      big |= __builtin_amdgcn_ballot_w64(g2 > 1e-8f * ab);   // wave-uniform, kept in scalar registers
       pq = pq_next;
       __syncthreads();
     }
     sweeps = sweep + 1;
-    if (!__syncthreads_or(big)) break;
+    if (!__syncthreads_or(big != 0)) break;
   }
   return sweeps;
 }
@@ -258,7 +282,7 @@ __device__ int jacobi_columns(float* K, const uint32_t* sched, int n, int max_sw
 // objective.  All threads call it.
 __device__ void core_finish(const float* K, int ld, int l, int n, double ksc, const float* X, int r, float* SB,
                             float* SA, float* sigma, double* stats, const ObjectiveArgs& obj, int sweeps,
-                            double* norm2, int* order) {
+                            double* norm2, int* order, const double* objsums = nullptr) {
   const int tid = threadIdx.x, nt = blockDim.x;
   for (int a = tid; a < l; a += nt) {
     double s = 0.0;
@@ -291,12 +315,15 @@ __device__ void core_finish(const float* K, int ld, int l, int n, double ksc, co
     stats[0] = s2;
     stats[1] = static_cast<double>(sweeps);
   }
-  write_objective(obj, s2);
+  if (objsums == nullptr) write_objective(obj, s2);
+  else if (tid == 0 && obj.out != nullptr) objective_from_sums(obj, objsums[0], objsums[1], s2);
 }
 
 // mode 2 for l <= LM (LM <= 32), 16 lanes per pair: 16 ceil(l / 2) threads
 // rounded up to whole waves.  The workgroup sums the P Gram partials of C
-// (gram_sum_block), wave 0 factors H in fp64 and writes K = 2^-e R^T.
+// (gram_sum_block), wave 0 factors H in fp64 and writes K = 2^-e R^T while
+// wave 1 (wave 0 afterwards when it is alone) sums the |E|^2 and |W|^2
+// partials of the objective.
 template <int LM>
 __global__ __launch_bounds__(256) void core_small_kernel(const double* __restrict__ gparts, int P, int l,
                                                          const float* __restrict__ Xinv, int r, float* __restrict__ SB,
@@ -311,11 +338,20 @@ __global__ __launch_bounds__(256) void core_small_kernel(const double* __restric
   __shared__ double norm2[32];
   __shared__ int order[32];
   __shared__ double kscale;
+  __shared__ double objsums[2];
   const int tid = threadIdx.x;
   const int n = l + (l & 1);
   for (int e = tid; e < l * l; e += blockDim.x) Xs[e] = Xinv[e];
   build_schedule(sched, n, blockDim.x / 16, LD);
   const double* gram = gram_sum_block<LM>(gparts, P, l, gsum);
+  const int sum_wave = blockDim.x > 64 ? 1 : 0;
+  if (obj.out != nullptr && sum_wave == 1 && (tid >> 6) == 1) {
+    const double es = wave_sum_fixed(obj.e_parts, obj.ne), ws = wave_sum_fixed(obj.w_parts, obj.nw);
+    if (tid == 64) {
+      objsums[0] = es;
+      objsums[1] = ws;
+    }
+  }
   if (tid < 64) {
     double g[LM], t[LM];
     chol_wave<LM, false>(gram, l, g, t, rowbuf);
@@ -334,10 +370,17 @@ __global__ __launch_bounds__(256) void core_small_kernel(const double* __restric
       for (int a = 0; a < 32; ++a)
         K[a * LD + tid] = (a < LM && a <= tid && tid < l) ? static_cast<float>(g[a < LM ? a : 0] * sc) : 0.f;
     }
+    if (obj.out != nullptr && sum_wave == 0) {
+      const double es = wave_sum_fixed(obj.e_parts, obj.ne), ws = wave_sum_fixed(obj.w_parts, obj.nw);
+      if (tid == 0) {
+        objsums[0] = es;
+        objsums[1] = ws;
+      }
+    }
   }
   __syncthreads();
   const int sweeps = jacobi_columns<16, 2>(K, sched, n, 30);
-  core_finish(K, LD, l, n, kscale, Xs, r, SB, SA, sigma, stats, obj, sweeps, norm2, order);
+  core_finish(K, LD, l, n, kscale, Xs, r, SB, SA, sigma, stats, obj, sweeps, norm2, order, objsums);
 }
 
 // ---------------------------------------------------------------------------

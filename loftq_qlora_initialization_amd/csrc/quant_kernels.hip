@@ -321,9 +321,14 @@ __global__ __launch_bounds__(kFusedThreads) __attribute__((amdgpu_waves_per_eu(R
   load_tile(t0, raw0, bop0);
   int64_t tile = t0;
   for (; tile + 1 < t1; tile += 2) {
+    // the prefetch is unconditional (at the end of the run a harmless repeat of
+    // the last tile) and pinned before the compute, so the wait before each
+    // tile's MFMA covers that tile's loads only and the next tile's stay in flight
     load_tile(tile + 1, raw1, bop1);
+    __builtin_amdgcn_sched_barrier(0);
     do_tile(tile, raw0, bop0);
-    if (tile + 2 < t1) load_tile(tile + 2, raw0, bop0);
+    load_tile(tile + 2 < t1 ? tile + 2 : t1 - 1, raw0, bop0);
+    __builtin_amdgcn_sched_barrier(0);
     do_tile(tile + 1, raw1, bop1);
   }
   if (tile < t1) do_tile(tile, raw0, bop0);
