@@ -77,7 +77,11 @@ def test_sketch_matches_oracle_generator(lib, d, k, r, p):
 
 
 @pytest.mark.parametrize("d,k,r,p,q", [(520, 384, 8, 8, 2), (300, 700, 16, 8, 2), (1030, 260, 64, 16, 2),
-                                       (257, 333, 4, 4, 0), (768, 512, 16, 8, 3)])
+                                       (257, 333, 4, 4, 0), (768, 512, 16, 8, 3),
+                                       # odd l (a zero padding column), l = 28 (padding lanes rotate two zero
+                                       # columns), l = 48 and odd l = 41 on the wide solver (padding pairs)
+                                       (400, 300, 5, 4, 2), (600, 500, 20, 8, 2), (700, 600, 32, 16, 2),
+                                       (650, 520, 33, 8, 1)])
 def test_randomized_svd_step_parity(lib, d, k, r, p, q):
     E = nf4_residual(synth.Workload("t", d, k, "f32", r, 1, False, p, q, False, 7 * d + k, "outliers"))
     om = oracle.rademacher_sketch(42, 1, k, r + p)
@@ -188,6 +192,24 @@ def test_pipeline_free_running_objective(lib):
     assert abs(obj[-1] - ref["objective"][-1]) <= 1e-3 * ref["objective"][-1]
     assert obj[-1] < obj[0]
     # device objective identity: recompute ||W - deq(Q_T) - B A|| / ||W|| from the device outputs
+    d, k = W.shape
+    codes = oracle.unpack_nibbles(host(out["packed"]), d * k)
+    scale = oracle.dq_scales_expand(host(out["qabsmax"]), host(out["dq_scale"]))
+    direct = oracle.objective(W, codes, scale, host(out["B"]), host(out["A"]))
+    assert abs(direct - obj[-1]) <= 1e-4 * direct
+
+
+@pytest.mark.parametrize("r,p", [(4, 4), (5, 4), (13, 8), (20, 8)])
+def test_init_objective_small_sketches(lib, r, p):
+    """l = 8 (one-wave core: the objective sums run on wave 0 after the Cholesky), odd l = 9 and 21,
+    l = 28: free-running objective against the oracle and the device objective identity."""
+    w = synth.Workload("t", 384, 320, "bf16", r, 3, True, p, 2, False, 11 * r + p, "outliers")
+    bits, W = synth.make_weight(w)
+    out = lib.loftq_init(dev_w(bits, w), _cfg(lib, w))
+    ref = oracle.loftq_init(W, **_oracle_kw(w))
+    obj = host(out["objective"])
+    assert abs(obj[0] - ref["objective"][0]) <= 1e-6 * ref["objective"][0]
+    assert abs(obj[-1] - ref["objective"][-1]) <= 1e-3 * ref["objective"][-1]
     d, k = W.shape
     codes = oracle.unpack_nibbles(host(out["packed"]), d * k)
     scale = oracle.dq_scales_expand(host(out["qabsmax"]), host(out["dq_scale"]))
