@@ -10,6 +10,7 @@ objective) with W already resident in HBM.  `value` is matrix elements per secon
                 records around each launch on its own stream during a separate
                 profiled pass over the same steps;
   nf4_quantize  the same for the NF4 quantize kernel (the metric's second part);
+  nf4_merge     the adapter merge of the init's own B, A into its Q, timed the same way;
   cpu_baseline  the CPU oracle on a bounded row sample of the same workload.
 """
 from __future__ import annotations
@@ -81,6 +82,8 @@ def algorithmic_bytes(name, w, rows, cols):
         "gemm_nn": 4 * n + 4 * cols * l + 4 * rows * l,
         "gemm_tn": 4 * n + 4 * rows * l + 4 * cols * l,
         "sumsq_weight": n * wb,
+        # adapter merge: codes and scales in, codes and fp32 absmax out, B and A
+        "nf4_merge": -(-n // 2) + scales + -(-n // 2) + 4 * nb + 4 * w.rank * (rows + cols),
     }
     return table.get(name)
 
@@ -193,6 +196,37 @@ def main():
                                      "avg_us": kernels["nf4_quantize_fused"]["avg_us"]}
 
     obj = bufs.objective.cpu().numpy().tolist()
+
+    # adapter merge (the PEFT guide's merge_adapter on NF4: dequantize, add B A,
+    # quantize again) of this init's own B, A into its Q, into separate buffers
+    merge = None
+    if w.rank > 0 and not w.exact_svd and w.cols % 64 == 0:
+        dq = bool(w.double_quant)
+        nb = (w.numel + 63) // 64
+        mout = {"packed": torch.empty_like(bufs.packed), "absmax": torch.empty_like(bufs.absmax)}
+        if dq:
+            mout.update(qabsmax=torch.empty_like(bufs.qabsmax), dq_scale=torch.empty_like(bufs.dq_scale))
+        scales = dict(qabsmax=bufs.qabsmax, dq_scale=bufs.dq_scale) if dq else dict(absmax=bufs.absmax)
+        for _ in range(2):
+            lq.loftq_nf4_merge(bufs.packed, (w.rows, w.cols), bufs.B, bufs.A, 1.0, **scales, double_quant=dq, out=mout)
+        torch.cuda.synchronize()
+        lq.profile_enable(True)
+        for _ in range(args.steps):
+            lq.loftq_nf4_merge(bufs.packed, (w.rows, w.cols), bufs.B, bufs.A, 1.0, **scales, double_quant=dq, out=mout)
+        torch.cuda.synchronize()
+        lq.profile_enable(False)
+        mprof = lq.profile_collect()
+        if "nf4_merge" in mprof:
+            launches, total_ms = mprof["nf4_merge"]
+            avg_us = 1e3 * total_ms / launches
+            gb = algorithmic_bytes("nf4_merge", w, w.rows, w.cols) / (avg_us * 1e-6) / 1e9
+            step_us = 1e3 * sum(v[1] for v in mprof.values()) / args.steps
+            merge = {"kernel": "nf4_merge", "bound": "alu", "avg_us": round(avg_us, 3),
+                     "achieved": round(gb, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gb / HBM_PEAK_GBS, 4),
+                     "bytes_per_launch": algorithmic_bytes("nf4_merge", w, w.rows, w.cols),
+                     "us_per_merge_with_double_quant": round(step_us, 3),
+                     "elements_per_s": round(w.numel / (step_us * 1e-6))}
     line = {
         "metric": METRIC, "value": value, "unit": "elements/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak",
@@ -200,7 +234,7 @@ def main():
         "config": {"workload": w.name, "rows": w.rows, "cols": w.cols, "storage": w.dtype, "rank": w.rank,
                    "iterative_steps": w.iterative_steps, "oversample": w.oversample, "power_iters": w.power_iters,
                    "double_quant": w.double_quant, "blocksize": 64, "dq_blocksize": 256},
-        "roofline": roofline, "nf4_quantize": nf4, "objective": obj, "kernels": kernels,
+        "roofline": roofline, "nf4_quantize": nf4, "nf4_merge": merge, "objective": obj, "kernels": kernels,
     }
     if not args.skip_cpu:
         line["cpu_baseline"] = cpu_baseline(w, args.cpu_rows)

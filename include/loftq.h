@@ -105,6 +105,36 @@ loftq_status_t loftq_nf4_dequantize(const uint8_t* packed, const float* absmax, 
                                     int32_t dq_blocksize, const void* W, loftq_dtype_t wdt, float* out,
                                     double* sumsq, void* stream);
 
+/* Merging a LoRA adapter into NF4 weights and taking it out again (PEFT guide
+ * "量化", merging adapters into quantized weights: dequantize the base weight, add
+ * the adapter, quantize the sum again; unmerge does the reverse and is not an
+ * exact inverse, so rounding accumulates over cycles).
+ *   merge:   Q' = NF4(deq(Q) + alpha B A)        unmerge: Q' = NF4(deq(Q) - alpha B A)
+ * deq(Q) as in loftq_nf4_dequantize; the sum is formed in fp32 (B A on fp32 matrix
+ * cores) and quantized like any residual (blockwise-64 absmax, nearest level).
+ *   packed                     [device] input codes
+ *   absmax                     [device] input scales, or NULL when qabsmax/dq_scale are given
+ *   qabsmax, dq_scale          [device] double-quantized input scales, or both NULL
+ *   B, A                       [device] fp32 rows x r and r x cols (r <= 64), or both NULL
+ *                              (then the codes are only requantized)
+ *   alpha                      [host] adapter scale (finite)
+ *   packed_out                 [device] ceil(rows*cols/2) bytes out; may be `packed`
+ *   absmax_out                 [device] ceil(rows*cols/64) fp32 out (the new absmax); may be `absmax`
+ *   qabsmax_out, dq_scale_out  [device] the double quant of absmax_out, or both NULL; may be
+ *                              the input qabsmax / dq_scale
+ * Buffers given as "may be" are either identical to the input or disjoint from it.
+ * UNSUPPORTED: cols % 64 != 0, r > 64, blocksize != 64, dq_blocksize != 256. */
+loftq_status_t loftq_nf4_merge(const uint8_t* packed, const float* absmax, const int8_t* qabsmax,
+                               const float* dq_scale, int64_t rows, int64_t cols, int32_t blocksize,
+                               int32_t dq_blocksize, const float* B, const float* A, int32_t r, float alpha,
+                               uint8_t* packed_out, float* absmax_out, int8_t* qabsmax_out, float* dq_scale_out,
+                               void* stream);
+loftq_status_t loftq_nf4_unmerge(const uint8_t* packed, const float* absmax, const int8_t* qabsmax,
+                                 const float* dq_scale, int64_t rows, int64_t cols, int32_t blocksize,
+                                 int32_t dq_blocksize, const float* B, const float* A, int32_t r, float alpha,
+                                 uint8_t* packed_out, float* absmax_out, int8_t* qabsmax_out, float* dq_scale_out,
+                                 void* stream);
+
 /* Low-rank step ("LoftQ...", §2.3: best rank-r approximation of W - Q from its
  * r largest singular triplets, Delta = U_r S_r V_r^T).  exact = 1: the SVD of E
  * itself (one-sided Jacobi, min(rows, cols) <= 512).  exact = 0: randomized

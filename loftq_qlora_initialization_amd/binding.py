@@ -30,7 +30,8 @@ LOFTQ_F32, LOFTQ_BF16 = 0, 1
 STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported configuration", 3: "workspace too small",
           4: "HIP runtime error"}
 
-EXPORTS = ["loftq_nf4_quantize", "loftq_double_quant", "loftq_nf4_dequantize", "loftq_lowrank_svd",
+EXPORTS = ["loftq_nf4_quantize", "loftq_double_quant", "loftq_nf4_dequantize", "loftq_nf4_merge",
+           "loftq_nf4_unmerge", "loftq_lowrank_svd",
            "loftq_lowrank_svd_workspace_bytes", "loftq_init", "loftq_workspace_bytes", "loftq_default_config",
            "loftq_status_string", "loftq_nf4_codebook", "loftq_profile_enable", "loftq_profile_collect"]
 
@@ -57,6 +58,9 @@ _c_quant = _sig("loftq_nf4_quantize", ctypes.c_int, [_P, ctypes.c_int, _I64, _I6
 _c_dq = _sig("loftq_double_quant", ctypes.c_int, [_P, _I64, _I32, _P, _P, _P])
 _c_deq = _sig("loftq_nf4_dequantize", ctypes.c_int,
               [_P, _P, _P, _P, _I64, _I64, _I32, _I32, _P, ctypes.c_int, _P, _P, _P])
+_MERGE_ARGS = [_P, _P, _P, _P, _I64, _I64, _I32, _I32, _P, _P, _I32, ctypes.c_float, _P, _P, _P, _P, _P]
+_c_merge = _sig("loftq_nf4_merge", ctypes.c_int, _MERGE_ARGS)
+_c_unmerge = _sig("loftq_nf4_unmerge", ctypes.c_int, _MERGE_ARGS)
 _c_svd = _sig("loftq_lowrank_svd", ctypes.c_int,
               [_P, _I64, _I64, _I32, _I32, _I32, _I32, _P, _U64, _I32, _P, _P, _P, _P, _SZ, _P])
 _c_svd_ws = _sig("loftq_lowrank_svd_workspace_bytes", _SZ, [_I64, _I64, _I32, _I32, _I32])
@@ -166,6 +170,45 @@ def loftq_nf4_dequantize(packed: torch.Tensor, shape, absmax: Optional[torch.Ten
            _c_deq(_ptr(packed), _ptr(absmax), _ptr(qabsmax), _ptr(dq_scale), rows, cols, 64, 256, _ptr(W), wdt,
                   _ptr(out), _ptr(ss), _stream(stream)))
     return (out, ss) if with_sumsq else out
+
+
+def _merge_call(fn, c_fn, packed, shape, absmax, qabsmax, dq_scale, B, A, alpha, double_quant, out, stream):
+    rows, cols = shape
+    n = rows * cols
+    r = 0
+    if B is not None:
+        _contig(B, "B"), _contig(A, "A")
+        r = B.shape[1]
+    dev = packed.device
+    if out is None:
+        out = {"packed": torch.empty((n + 1) // 2, dtype=torch.uint8, device=dev),
+               "absmax": torch.empty((n + 63) // 64, dtype=torch.float32, device=dev)}
+        if double_quant:
+            out["qabsmax"] = torch.empty((n + 63) // 64, dtype=torch.int8, device=dev)
+            out["dq_scale"] = torch.empty(((n + 63) // 64 + 255) // 256, dtype=torch.float32, device=dev)
+    _check(fn, c_fn(_ptr(packed), _ptr(absmax), _ptr(qabsmax), _ptr(dq_scale), rows, cols, 64, 256, _ptr(B), _ptr(A),
+                    r, float(alpha), _ptr(out["packed"]), _ptr(out["absmax"]), _ptr(out.get("qabsmax")),
+                    _ptr(out.get("dq_scale")), _stream(stream)))
+    return out
+
+
+def loftq_nf4_merge(packed: torch.Tensor, shape, B: Optional[torch.Tensor], A: Optional[torch.Tensor],
+                    alpha: float = 1.0, absmax: Optional[torch.Tensor] = None, qabsmax: Optional[torch.Tensor] = None,
+                    dq_scale: Optional[torch.Tensor] = None, double_quant: bool = False, out: Optional[dict] = None,
+                    stream=None) -> dict:
+    """Q' = NF4(deq(Q) + alpha B A): dict of packed, absmax (and qabsmax, dq_scale with double_quant).
+    `out` may hold the input tensors themselves (in place)."""
+    return _merge_call("loftq_nf4_merge", _c_merge, packed, shape, absmax, qabsmax, dq_scale, B, A, alpha,
+                       double_quant, out, stream)
+
+
+def loftq_nf4_unmerge(packed: torch.Tensor, shape, B: Optional[torch.Tensor], A: Optional[torch.Tensor],
+                      alpha: float = 1.0, absmax: Optional[torch.Tensor] = None, qabsmax: Optional[torch.Tensor] = None,
+                      dq_scale: Optional[torch.Tensor] = None, double_quant: bool = False, out: Optional[dict] = None,
+                      stream=None) -> dict:
+    """Q' = NF4(deq(Q) - alpha B A), the reverse of loftq_nf4_merge (not an exact inverse)."""
+    return _merge_call("loftq_nf4_unmerge", _c_unmerge, packed, shape, absmax, qabsmax, dq_scale, B, A, alpha,
+                       double_quant, out, stream)
 
 
 def lowrank_workspace_bytes(rows: int, cols: int, r: int, oversample: int, exact: bool) -> int:

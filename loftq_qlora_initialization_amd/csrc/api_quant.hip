@@ -1,4 +1,5 @@
-// C-ABI entry points for the NF4 codec: argument validation, then launches.
+// C-ABI entry points for the NF4 codec and the adapter merge: argument validation, then launches.
+#include <cmath>
 #include <cstring>
 
 #include "internal.h"
@@ -98,6 +99,54 @@ loftq_status_t loftq_nf4_dequantize(const uint8_t* packed, const float* absmax, 
   return from_hip(launch_nf4_dequantize(packed, dq ? nullptr : absmax, dq ? qabsmax : nullptr,
                                         dq ? dq_scale : nullptr, n, dq_blocksize, W, wdt, out, nullptr, nullptr,
                                         sumsq, static_cast<hipStream_t>(stream)));
+}
+
+static loftq_status_t merge_impl(const uint8_t* packed, const float* absmax, const int8_t* qabsmax,
+                                 const float* dq_scale, int64_t rows, int64_t cols, int32_t blocksize,
+                                 int32_t dq_blocksize, const float* B, const float* A, int32_t r, float alpha,
+                                 uint8_t* packed_out, float* absmax_out, int8_t* qabsmax_out, float* dq_scale_out,
+                                 void* stream) {
+  if (!shape_ok(rows, cols)) return LOFTQ_ERR_INVALID_ARG;
+  if (blocksize != 64) return LOFTQ_ERR_UNSUPPORTED;
+  if (!nf4_tables().valid) return LOFTQ_ERR_UNSUPPORTED;
+  const bool dq_in = qabsmax != nullptr || dq_scale != nullptr;
+  const bool dq_out = qabsmax_out != nullptr || dq_scale_out != nullptr;
+  if (dq_in && (!qabsmax || !dq_scale)) return LOFTQ_ERR_INVALID_ARG;
+  if (dq_out && (!qabsmax_out || !dq_scale_out)) return LOFTQ_ERR_INVALID_ARG;
+  if ((dq_in || dq_out) && dq_blocksize != 256) return LOFTQ_ERR_UNSUPPORTED;
+  if ((B == nullptr) != (A == nullptr)) return LOFTQ_ERR_INVALID_ARG;
+  if (B != nullptr && r < 1) return LOFTQ_ERR_INVALID_ARG;
+  if (!std::isfinite(alpha)) return LOFTQ_ERR_INVALID_ARG;
+  const int64_t n = rows * cols;
+  if (n == 0) return LOFTQ_OK;
+  if (cols % 64 != 0 || (B != nullptr && r > 64)) return LOFTQ_ERR_UNSUPPORTED;
+  if (!packed || !packed_out || !absmax_out || (!dq_in && !absmax)) return LOFTQ_ERR_INVALID_ARG;
+  if (!aligned16(packed) || !aligned16(packed_out) || !aligned16(absmax_out)) return LOFTQ_ERR_INVALID_ARG;
+  if (dq_in ? (!aligned16(qabsmax) || !aligned16(dq_scale)) : !aligned16(absmax)) return LOFTQ_ERR_INVALID_ARG;
+  if (dq_out && (!aligned16(qabsmax_out) || !aligned16(dq_scale_out))) return LOFTQ_ERR_INVALID_ARG;
+  if (B && (!aligned16(B) || !aligned16(A))) return LOFTQ_ERR_INVALID_ARG;
+  return from_hip(launch_nf4_merge(packed, dq_in ? nullptr : absmax, dq_in ? qabsmax : nullptr,
+                                   dq_in ? dq_scale : nullptr, rows, cols, B, A, B ? r : 0, alpha, packed_out,
+                                   absmax_out, dq_out ? qabsmax_out : nullptr, dq_out ? dq_scale_out : nullptr,
+                                   static_cast<hipStream_t>(stream)));
+}
+
+loftq_status_t loftq_nf4_merge(const uint8_t* packed, const float* absmax, const int8_t* qabsmax,
+                               const float* dq_scale, int64_t rows, int64_t cols, int32_t blocksize,
+                               int32_t dq_blocksize, const float* B, const float* A, int32_t r, float alpha,
+                               uint8_t* packed_out, float* absmax_out, int8_t* qabsmax_out, float* dq_scale_out,
+                               void* stream) {
+  return merge_impl(packed, absmax, qabsmax, dq_scale, rows, cols, blocksize, dq_blocksize, B, A, r, alpha,
+                    packed_out, absmax_out, qabsmax_out, dq_scale_out, stream);
+}
+
+loftq_status_t loftq_nf4_unmerge(const uint8_t* packed, const float* absmax, const int8_t* qabsmax,
+                                 const float* dq_scale, int64_t rows, int64_t cols, int32_t blocksize,
+                                 int32_t dq_blocksize, const float* B, const float* A, int32_t r, float alpha,
+                                 uint8_t* packed_out, float* absmax_out, int8_t* qabsmax_out, float* dq_scale_out,
+                                 void* stream) {
+  return merge_impl(packed, absmax, qabsmax, dq_scale, rows, cols, blocksize, dq_blocksize, B, A, r, -alpha,
+                    packed_out, absmax_out, qabsmax_out, dq_scale_out, stream);
 }
 
 }  // extern "C"

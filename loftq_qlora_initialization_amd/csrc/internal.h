@@ -70,6 +70,11 @@ hipError_t launch_nf4_quantize(const void* W, loftq_dtype_t wdt, int64_t rows, i
                                hipStream_t s);
 hipError_t launch_double_quant(const float* absmax, int64_t nblocks, int dqbs, int8_t* q, float* scale,
                                hipStream_t s);
+// Q' = NF4(deq(Q) + alpha B A); input scales absmax or (q, dqscale); output
+// absmax_out and, with q_out / dqs_out, its double quant (dq_blocksize 256).
+hipError_t launch_nf4_merge(const uint8_t* packed, const float* absmax, const int8_t* q, const float* dqscale,
+                            int64_t rows, int64_t cols, const float* B, const float* A, int r, float alpha,
+                            uint8_t* packed_out, float* absmax_out, int8_t* q_out, float* dqs_out, hipStream_t s);
 // Sum of squares of the output: with `partials`, one fp64 partial per workgroup
 // (dequant_num_partials(n) of them, summed in a fixed order by the consumer);
 // otherwise, with `sumsq`, accumulated into *sumsq with atomics (after zeroing it).

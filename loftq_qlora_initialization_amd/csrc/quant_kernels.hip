@@ -222,6 +222,44 @@ __device__ __forceinline__ void raw_to_f32(const uint4 (&raw)[4], float v[16]) {
   }
 }
 
+// Where the fused kernel takes the base of its residual from.  load() fetches
+// the 16 elements e0 .. e0 + 15 of one lane (raw words), to_f32() turns them
+// into fp32 values; lvl is the NF4 level table in LDS.  kScaleB: the B operand
+// is multiplied by the kernel's bscale when loaded.
+template <typename T>
+struct WeightSource {   // the weight W itself (bf16 or fp32): R = W - B A
+  const T* W;
+  static constexpr bool kScaleB = false;
+  __device__ __forceinline__ void load(int64_t e0, uint4 (&raw)[4]) const { load16_raw(W + e0, raw); }
+  __device__ __forceinline__ void to_f32(const uint4 (&raw)[4], float v[16], const float*) const {
+    raw_to_f32<T>(raw, v);
+  }
+};
+template <bool kDQ>
+struct Nf4Source {      // deq(Q) of existing codes: R = deq(Q) - bscale B A
+  const uint8_t* packed;
+  const float* absmax;  // per-block scale (no double quant)
+  const int8_t* qa;     // or qabsmax and dq_scale per dq group
+  const float* dqs;
+  int dqbs;
+  static constexpr bool kScaleB = true;
+  // 16 codes (8 bytes) and the block's dequant scale a', as in the dequant kernel
+  __device__ __forceinline__ void load(int64_t e0, uint4 (&raw)[4]) const {
+    const uint2 c = *reinterpret_cast<const uint2*>(packed + (e0 >> 1));
+    const int64_t b = e0 >> 6;
+    const float a = kDQ ? static_cast<float>(qa[b]) * dqs[b / dqbs] : absmax[b];
+    raw[0] = make_uint4(c.x, c.y, __float_as_uint(a), 0u);
+  }
+  __device__ __forceinline__ void to_f32(const uint4 (&raw)[4], float v[16], const float* lvl) const {
+    const float a = __uint_as_float(raw[0].z);
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const uint32_t code = ((e < 8 ? raw[0].x : raw[0].y) >> nib_shift(e)) & 0xFu;
+      v[e] = lvl[code] * a;   // deq = fl32(c[code] a'), one rounding
+    }
+  }
+};
+
 // Fused residual R = W - B A (cols % 64 == 0, r <= 64).  Each wave owns one
 // 64-column block column and walks a run of 16-row tiles of it; waves share
 // nothing, so there is no LDS tile and no barrier after the table fill.
@@ -241,15 +279,17 @@ constexpr int64_t kFusedWaves = 3072;
 
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 
-template <typename T, int R16, bool kFullR>
-__global__ __launch_bounds__(kFusedThreads) __attribute__((amdgpu_waves_per_eu(R16 <= 16 ? 4 : 2))) void quantize_fused_kernel(const T* __restrict__ W, int64_t rows,
+template <typename Src, int R16, bool kFullR>
+__global__ __launch_bounds__(kFusedThreads) __attribute__((amdgpu_waves_per_eu(R16 <= 16 ? 4 : 2))) void quantize_fused_kernel(Src src, int64_t rows,
                                                                        int64_t cols, const float* __restrict__ B,
-                                                                       const float* __restrict__ A, int r, int tpw,
-                                                                       uint8_t* __restrict__ packed,
+                                                                       const float* __restrict__ A, int r, float bscale,
+                                                                       int tpw, uint8_t* __restrict__ packed,
                                                                        float* __restrict__ absmax, Nf4Tables tab) {
   constexpr int KK = R16 / 4;
   __shared__ EncodeLds s;
+  __shared__ float lvl[16];
   fill_lds(s, tab);
+  if (threadIdx.x < 16) lvl[threadIdx.x] = tab.level[threadIdx.x];
   __syncthreads();
   const int lane = threadIdx.x & 63, li = lane & 15, g = lane >> 4;
   const int64_t nbc = cols >> 6;
@@ -273,7 +313,7 @@ __global__ __launch_bounds__(kFusedThreads) __attribute__((amdgpu_waves_per_eu(R
   auto load_tile = [&](int64_t tile, uint4 (&raw)[4], float (&bop)[KK]) {
     const int64_t row = (tile << 4) + li;
     const int64_t rc = row < rows ? row : rows - 1;
-    load16_raw(W + rc * cols + col0 + 16 * g, raw);
+    src.load(rc * cols + col0 + 16 * g, raw);
     if (kFullR) {
 #pragma unroll
       for (int q = 0; q < KK / 4; ++q) {
@@ -287,6 +327,10 @@ __global__ __launch_bounds__(kFusedThreads) __attribute__((amdgpu_waves_per_eu(R
         bop[kk] = (p < r) ? B[rc * r + p] : 0.f;
       }
     }
+    if (Src::kScaleB) {
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) bop[kk] *= bscale;
+    }
   };
   auto do_tile = [&](int64_t tile, const uint4 (&raw)[4], const float (&bop)[KK]) {
     floatx4 acc[4];
@@ -297,7 +341,7 @@ __global__ __launch_bounds__(kFusedThreads) __attribute__((amdgpu_waves_per_eu(R
 #pragma unroll
       for (int t = 0; t < 4; ++t) acc[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(aop[kk][t], bop[kk], acc[t], 0, 0, 0);
     float v[16];
-    raw_to_f32<T>(raw, v);
+    src.to_f32(raw, v, lvl);
     float m = 0.f;
 #pragma unroll
     for (int t = 0; t < 4; ++t)
@@ -583,6 +627,18 @@ int grid_for_groups(int64_t ngroups, int per_thread) {
   return static_cast<int>(blocks);
 }
 
+// Grid of the fused kernel: about kFusedWaves waves in all, each a run of tpw
+// 16-row tiles of one 64-column block column.
+dim3 fused_grid(int64_t rows, int64_t cols, int& tpw_out) {
+  const int64_t nbc = cols / 64, ntiles = (rows + 15) / 16;
+  int64_t tpw = (nbc * ntiles + kFusedWaves - 1) / kFusedWaves;
+  if (tpw < 1) tpw = 1;
+  const int64_t chunks = (ntiles + tpw - 1) / tpw;
+  const int64_t waves = nbc * chunks;
+  tpw_out = static_cast<int>(tpw);
+  return dim3(static_cast<unsigned>((waves + 3) / 4));
+}
+
 template <typename T>
 hipError_t quantize_typed(const T* W, int64_t rows, int64_t cols, const float* B, const float* A, int r,
                           uint8_t* packed, float* absmax, hipStream_t s) {
@@ -603,22 +659,18 @@ hipError_t quantize_typed(const T* W, int64_t rows, int64_t cols, const float* B
     }
   } else if (cols % 64 == 0 && r <= kFusedMaxR) {
     const int r16 = (r + 15) / 16 * 16;
-    const int64_t nbc = cols / 64, ntiles = (rows + 15) / 16;
-    // about kFusedWaves waves in all, each a run of tiles of one block column
-    int64_t tpw = (nbc * ntiles + kFusedWaves - 1) / kFusedWaves;
-    if (tpw < 1) tpw = 1;
-    const int64_t chunks = (ntiles + tpw - 1) / tpw;
-    const int64_t waves = nbc * chunks;
-    const dim3 grid(static_cast<unsigned>((waves + 3) / 4));
+    int tpw = 0;
+    const dim3 grid = fused_grid(rows, cols, tpw);
     const bool full = (r == r16);
+    const WeightSource<T> src{W};
 #define LQ_FUSED(R16)                                                                                              \
   do {                                                                                                             \
     if (full)                                                                                                      \
-      LQ_LAUNCH("nf4_quantize_fused", (quantize_fused_kernel<T, R16, true>), grid, dim3(kFusedThreads), 0, s, W,   \
-                rows, cols, B, A, r, static_cast<int>(tpw), packed, absmax, tab);                                  \
+      LQ_LAUNCH("nf4_quantize_fused", (quantize_fused_kernel<WeightSource<T>, R16, true>), grid,                  \
+                dim3(kFusedThreads), 0, s, src, rows, cols, B, A, r, 1.f, tpw, packed, absmax, tab);               \
     else                                                                                                           \
-      LQ_LAUNCH("nf4_quantize_fused", (quantize_fused_kernel<T, R16, false>), grid, dim3(kFusedThreads), 0, s, W,  \
-                rows, cols, B, A, r, static_cast<int>(tpw), packed, absmax, tab);                                  \
+      LQ_LAUNCH("nf4_quantize_fused", (quantize_fused_kernel<WeightSource<T>, R16, false>), grid,                 \
+                dim3(kFusedThreads), 0, s, src, rows, cols, B, A, r, 1.f, tpw, packed, absmax, tab);               \
   } while (0)
     if (r16 == 16) LQ_FUSED(16);
     else if (r16 == 32) LQ_FUSED(32);
@@ -666,6 +718,54 @@ hipError_t launch_nf4_quantize(const void* W, loftq_dtype_t wdt, int64_t rows, i
   if (wdt == LOFTQ_BF16)
     return quantize_typed(static_cast<const uint16_t*>(W), rows, cols, B, A, r, packed, absmax, s);
   return quantize_typed(static_cast<const float*>(W), rows, cols, B, A, r, packed, absmax, s);
+}
+
+// Adapter merge Q' = NF4(deq(Q) + alpha B A) (alpha < 0 takes it out again):
+// the fused kernel with deq(Q) as the residual's base, so codes, scales and the
+// adapter are read once and deq(Q) never reaches memory; then, when q_out is
+// given, the double quant of the new absmax.  Requires cols % 64 == 0 and
+// 0 <= r <= 64 (r = 0: B, A unused).  Each block is read and written by one
+// wave, codes before scales, so packed_out / absmax_out may be packed / absmax.
+hipError_t launch_nf4_merge(const uint8_t* packed, const float* absmax, const int8_t* qa, const float* dqs,
+                            int64_t rows, int64_t cols, const float* B, const float* A, int r, float alpha,
+                            uint8_t* packed_out, float* absmax_out, int8_t* q_out, float* dqs_out, hipStream_t s) {
+  const Nf4Tables& tab = nf4_tables();
+  const int64_t n = rows * cols;
+  if (n == 0) return hipSuccess;
+  if (cols % 64 != 0 || r < 0 || r > kFusedMaxR) return hipErrorInvalidValue;
+  const int r16 = r <= 16 ? 16 : (r + 15) / 16 * 16;
+  int tpw = 0;
+  const dim3 grid = fused_grid(rows, cols, tpw);
+  const bool full = (r == r16);
+  const float bscale = -alpha;
+#define LQ_MERGE(SRC, R16)                                                                                         \
+  do {                                                                                                             \
+    if (full)                                                                                                      \
+      LQ_LAUNCH("nf4_merge", (quantize_fused_kernel<SRC, R16, true>), grid, dim3(kFusedThreads), 0, s, src, rows, \
+                cols, B, A, r, bscale, tpw, packed_out, absmax_out, tab);                                          \
+    else                                                                                                           \
+      LQ_LAUNCH("nf4_merge", (quantize_fused_kernel<SRC, R16, false>), grid, dim3(kFusedThreads), 0, s, src, rows,\
+                cols, B, A, r, bscale, tpw, packed_out, absmax_out, tab);                                          \
+  } while (0)
+#define LQ_MERGE_R(SRC)                \
+  do {                                 \
+    if (r16 == 16) LQ_MERGE(SRC, 16);  \
+    else if (r16 == 32) LQ_MERGE(SRC, 32); \
+    else if (r16 == 48) LQ_MERGE(SRC, 48); \
+    else LQ_MERGE(SRC, 64);            \
+  } while (0)
+  if (qa != nullptr) {
+    const Nf4Source<true> src{packed, nullptr, qa, dqs, 256};
+    LQ_MERGE_R(Nf4Source<true>);
+  } else {
+    const Nf4Source<false> src{packed, absmax, nullptr, nullptr, 256};
+    LQ_MERGE_R(Nf4Source<false>);
+  }
+#undef LQ_MERGE_R
+#undef LQ_MERGE
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || q_out == nullptr) return e;
+  return launch_double_quant(absmax_out, (n + 63) / 64, 256, q_out, dqs_out, s);
 }
 
 hipError_t launch_double_quant(const float* absmax, int64_t nblocks, int dqbs, int8_t* q, float* scale,

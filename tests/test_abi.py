@@ -73,3 +73,35 @@ def test_double_quant_validation(clib):
     assert f(None, 10, 256, FAKE, FAKE, None) == 1
     assert f(FAKE, -1, 256, FAKE, FAKE, None) == 1
     assert f(None, 0, 256, None, None, None) == 0
+
+
+def _merge(clib, name, packed, absmax, qa, dqs, rows, cols, bs, dqbs, B, A, r, alpha, po, ao, qo, so):
+    f = getattr(clib, name)
+    f.restype = ctypes.c_int
+    P, I64, I32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32
+    f.argtypes = [P, P, P, P, I64, I64, I32, I32, P, P, I32, ctypes.c_float, P, P, P, P, P]
+    return f(packed, absmax, qa, dqs, rows, cols, bs, dqbs, B, A, r, alpha, po, ao, qo, so, None)
+
+
+@pytest.mark.parametrize("name", ["loftq_nf4_merge", "loftq_nf4_unmerge"])
+def test_merge_validation(clib, name):
+    F = FAKE
+    ok = (F, F, None, None, 64, 128, 64, 256, F, F, 8, 1.0, F, F, None, None)
+    def call(**kw):
+        args = list(ok)
+        keys = ["packed", "absmax", "qa", "dqs", "rows", "cols", "bs", "dqbs", "B", "A", "r", "alpha", "po", "ao", "qo", "so"]
+        for k, v in kw.items():
+            args[keys.index(k)] = v
+        return _merge(clib, name, *args)
+    assert call(bs=32) == 2                                   # blocksize != 64
+    assert call(cols=96) == 2                                 # cols % 64 != 0
+    assert call(r=65) == 2                                    # r > 64
+    assert call(B=None) == 1                                  # B without A
+    assert call(absmax=None) == 1                             # no input scales
+    assert call(qa=F) == 1                                    # qabsmax without dq_scale
+    assert call(qo=F) == 1                                    # qabsmax_out without dq_scale_out
+    assert call(qa=F, dqs=F, dqbs=128) == 2                   # dq_blocksize != 256
+    assert call(po=None) == 1                                 # no output codes
+    assert call(ao=F + 4) == 1                                # misaligned output absmax
+    assert call(alpha=float("inf")) == 1                      # non-finite scale
+    assert call(rows=0) == 0                                  # empty: nothing to do
