@@ -39,6 +39,32 @@ MEASURED_TRAFFIC = {
     },
 }
 
+# VALU wave-instructions per dispatch from an SQ_INSTS_VALU counter run of this
+# command (summary under profiles/), keyed to the kernel source; the adapter merge
+# is VALU-bound, so its roofline is this count over its launch time against the
+# non-packed VALU peak (256 CUs x 4 SIMDs x 2.4 GHz / 4 cycles per wave64 op).
+VALU_PEAK_GWIS = 256 * 4 * 2.4 / 4
+MEASURED_VALU = {
+    "c2_4096x4096_bf16": {
+        "nf4_merge": {"valu": 5614232, "source": "quant_kernels.hip", "sha256": "654850248de71eaf"},
+    },
+}
+
+
+def measured_valu(workload, kernel):
+    import hashlib
+    rec = MEASURED_VALU.get(workload, {}).get(kernel)
+    if rec is None:
+        return None
+    path = os.path.join(ROOT, "loftq_qlora_initialization_amd", "csrc", rec["source"])
+    try:
+        with open(path, "rb") as f:
+            sha = hashlib.sha256(f.read()).hexdigest()[:16]
+    except OSError:
+        return None
+    return rec["valu"] if sha == rec["sha256"] else None
+
+
 def measured_traffic(workload, kernel):
     import hashlib
     rec = MEASURED_TRAFFIC.get(workload, {}).get(kernel)
@@ -221,10 +247,15 @@ def main():
             avg_us = 1e3 * total_ms / launches
             gb = algorithmic_bytes("nf4_merge", w, w.rows, w.cols) / (avg_us * 1e-6) / 1e9
             step_us = 1e3 * sum(v[1] for v in mprof.values()) / args.steps
+            valu = measured_valu(w.name, "nf4_merge")
             merge = {"kernel": "nf4_merge", "bound": "alu", "avg_us": round(avg_us, 3),
-                     "achieved": round(gb, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(gb / HBM_PEAK_GBS, 4),
-                     "bytes_per_launch": algorithmic_bytes("nf4_merge", w, w.rows, w.cols),
+                     "achieved": None if valu is None else round(valu / (avg_us * 1e-6) / 1e9, 1),
+                     "peak": VALU_PEAK_GWIS, "unit": "G VALU wave-instructions/s",
+                     "frac": None if valu is None else round(valu / (avg_us * 1e-6) / 1e9 / VALU_PEAK_GWIS, 4),
+                     "valu_per_launch": valu,
+                     "hbm": {"achieved": round(gb, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                             "frac": round(gb / HBM_PEAK_GBS, 4),
+                             "bytes_per_launch": algorithmic_bytes("nf4_merge", w, w.rows, w.cols)},
                      "us_per_merge_with_double_quant": round(step_us, 3),
                      "elements_per_s": round(w.numel / (step_us * 1e-6))}
     line = {
