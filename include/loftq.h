@@ -61,7 +61,11 @@ typedef struct {
   int32_t oversample;       /* p >= 0; sketch width l = r + p (randomized SVD) */
   int32_t power_iters;      /* q >= 0 subspace iterations (randomized SVD) */
   int32_t exact_svd;        /* 1: exact SVD (min(rows, cols) <= 512); 0: randomized */
-  int32_t reserved;         /* must be 0 */
+  int32_t warm_start;       /* 0: a fresh +-1 sketch every alternation (the pages' method);
+                               1: alternations t >= 2 start the subspace iteration from the
+                               previous right singular vectors, Omega_t = [sqrt(cols) V_{t-1} |
+                               the last oversample columns of the fresh sketch] (a variant, to be
+                               paired with fewer power_iters; ignored with exact_svd) */
   uint64_t seed;            /* sketch seed (loftq_config seed, default 42) */
 } loftq_config_t;
 

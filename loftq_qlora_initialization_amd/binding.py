@@ -40,7 +40,7 @@ class LoftqConfig(ctypes.Structure):
     _fields_ = [("bits", ctypes.c_int32), ("iterative_steps", ctypes.c_int32), ("rank", ctypes.c_int32),
                 ("blocksize", ctypes.c_int32), ("double_quant", ctypes.c_int32), ("dq_blocksize", ctypes.c_int32),
                 ("oversample", ctypes.c_int32), ("power_iters", ctypes.c_int32), ("exact_svd", ctypes.c_int32),
-                ("reserved", ctypes.c_int32), ("seed", ctypes.c_uint64)]
+                ("warm_start", ctypes.c_int32), ("seed", ctypes.c_uint64)]
 
 
 _P, _I64, _I32, _U64, _SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_uint64, ctypes.c_size_t

@@ -53,7 +53,7 @@ loftq_status_t check_config(int64_t rows, int64_t cols, const loftq_config_t* c)
   if (c == nullptr) return LOFTQ_ERR_INVALID_ARG;
   if (c->bits != 4 || c->blocksize != 64 || c->dq_blocksize != 256) return LOFTQ_ERR_UNSUPPORTED;
   if (c->iterative_steps < 0 || c->iterative_steps > 1000 || c->power_iters < 0 || c->power_iters > 64 ||
-      c->reserved != 0 || (c->double_quant != 0 && c->double_quant != 1))
+      (c->warm_start != 0 && c->warm_start != 1) || (c->double_quant != 0 && c->double_quant != 1))
     return LOFTQ_ERR_INVALID_ARG;
   return check_svd_shape(rows, cols, c->rank, c->oversample, c->exact_svd);
 }
@@ -151,6 +151,10 @@ loftq_status_t loftq_init(const void* W, loftq_dtype_t wdt, int64_t rows, int64_
         e = run_sketch(cfg->seed, t, count, cols, pl.svd.l, pl.svd.nt, pl.svd.k_pad, sketches, s);
       }
       om = sketches + slot * pl.sketch_floats;
+      // warm start: from alternation 2 on, the first r columns come from the
+      // previous alternation's A and sigma (still in their buffers here)
+      if (cfg->warm_start != 0 && t > 1 && e == hipSuccess)
+        e = run_warm_columns(A, sigma, cols, r, pl.svd.nt, sketches + slot * pl.sketch_floats, s);
     }
     if (e == hipSuccess)
       e = run_lowrank(E, pl.svd, cfg->power_iters, nullptr, om, cfg->seed, t, B, A, sigma, svd_ws, objt, s);

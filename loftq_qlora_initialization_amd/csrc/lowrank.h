@@ -68,6 +68,8 @@ hipError_t run_lowrank(const float* E, const SvdPlan& pl, int q, const float* om
 // Sketches of alternations t .. t + count - 1, each rows x 16 nt floats in fragment order, back to back.
 hipError_t run_sketch(uint64_t seed, int t, int count, int64_t k, int l, int nt, int64_t rows, float* out,
                       hipStream_t s);
+// Columns j < r of one fragment-order sketch (k rows) <- sqrt(k) A^T diag(sigma)^-1/2.
+hipError_t run_warm_columns(const float* A, const float* sigma, int64_t k, int r, int nt, float* out, hipStream_t s);
 hipError_t run_fill(float* p, int64_t n, float v, hipStream_t s);
 hipError_t run_objective(const ObjectiveArgs& obj, hipStream_t s);
 GemmShape gemm_shape(bool transposed, int nt);

@@ -55,6 +55,21 @@ __global__ void sketch_kernel(uint64_t seed, int t0, int64_t k, int l, int nt, i
   out[idx] = v;
 }
 
+// Warm start of the subspace iteration (a variant the pages do not describe):
+// columns j < r of a fragment-order sketch become sqrt(k) V[i][j], V = A^T
+// diag(sigma)^-1/2 being the right singular vectors of the previous alternation
+// (A = diag(sigma)^1/2 V^T); a column with sigma_j = 0 keeps its +-1 values.
+__global__ void warm_columns_kernel(const float* __restrict__ A, const float* __restrict__ sigma, int64_t k, int r,
+                                    int nt, float* __restrict__ out) {
+  const int64_t idx = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (idx >= k * r) return;
+  const int j = static_cast<int>(idx / k);
+  const int64_t i = idx - static_cast<int64_t>(j) * k;
+  const float sg = sigma[j];
+  if (!(sg > 0.f)) return;
+  out[frag_index(i, j, nt)] = sqrtf(static_cast<float>(k)) * (A[idx] / sqrtf(sg));
+}
+
 // Row-major n x l panel to fragment order over `rows` rows (zero padding).
 __global__ void to_frag_kernel(const float* __restrict__ src, int64_t n, int l, int nt, int64_t rows,
                                float* __restrict__ out) {
@@ -967,6 +982,14 @@ hipError_t run_sketch(uint64_t seed, int t, int count, int64_t k, int l, int nt,
   const int64_t n = rows * 16 * nt;
   LQ_LAUNCH("sketch", sketch_kernel, dim3(static_cast<unsigned>(cdiv(n, 256)), static_cast<unsigned>(count)), dim3(256),
             0, s, seed, t, k, l, nt, rows, out);
+  return hipGetLastError();
+}
+
+hipError_t run_warm_columns(const float* A, const float* sigma, int64_t k, int r, int nt, float* out, hipStream_t s) {
+  const int64_t n = k * r;
+  if (n <= 0) return hipSuccess;
+  LQ_LAUNCH("warm_sketch", warm_columns_kernel, dim3(static_cast<unsigned>(cdiv(n, 256))), dim3(256), 0, s, A, sigma, k,
+            r, nt, out);
   return hipGetLastError();
 }
 

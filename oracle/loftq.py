@@ -30,7 +30,23 @@ from .double_quant import double_quant, dq_scales_expand
 from .rng import rademacher_sketch
 from .lowrank import exact_svd, randomized_svd, lora_factors
 
-__all__ = ["loftq_step", "loftq_init", "objective"]
+__all__ = ["loftq_step", "loftq_init", "objective", "warm_sketch"]
+
+
+def warm_sketch(V_prev: np.ndarray, seed: int, t: int, k: int, l: int) -> np.ndarray:
+    """Sketch of a warm-started alternation t >= 2: [sqrt(k) V_{t-1} | the last l - r
+    columns of the +-1 sketch of (seed, t)], k x l.
+
+    A performance variant the pages do not describe (subspace iteration started
+    from the previous alternation's right singular vectors, so fewer power
+    iterations reach the same accuracy); the V columns are scaled to the norm of
+    a +-1 column.  Only the span of E Omega matters to the randomized SVD, so the
+    signs of V's columns are immaterial.
+    """
+    om = rademacher_sketch(seed, t, k, l)
+    r = V_prev.shape[1]
+    om[:, :r] = np.sqrt(float(k)) * np.asarray(V_prev, dtype=np.float64)
+    return om
 
 
 def _residual(W32: np.ndarray, B, A) -> np.ndarray:
@@ -84,8 +100,13 @@ def objective(W32: np.ndarray, codes: np.ndarray, scale: np.ndarray, B, A, block
 
 def loftq_init(W32: np.ndarray, *, rank: int, iterative_steps: int = 5, blocksize: int = 64,
                double_quant_on: bool = True, dq_blocksize: int = 256, exact: bool = False,
-               oversample: int = 8, power_iters: int = 2, seed: int = 42, keep_steps: bool = False) -> dict:
-    """The whole initialisation: T alternations from Delta_0 = 0, objective per alternation."""
+               oversample: int = 8, power_iters: int = 2, seed: int = 42, keep_steps: bool = False,
+               warm_start: bool = False) -> dict:
+    """The whole initialisation: T alternations from Delta_0 = 0, objective per alternation.
+
+    warm_start: alternations t >= 2 of the randomized SVD use warm_sketch(V_{t-1}, ...)
+    instead of the fresh sketch of (seed, t) (a variant; off reproduces the pages' method).
+    """
     W32 = np.asarray(W32, dtype=np.float32)
     d, k = W32.shape
     T = int(iterative_steps)
@@ -108,7 +129,10 @@ def loftq_init(W32: np.ndarray, *, rank: int, iterative_steps: int = 5, blocksiz
         return res
     last = None
     for t in range(1, T + 1):
-        st = loftq_step(W32, B, A, t=t, **kw)
+        om = None
+        if warm_start and not exact and last is not None:
+            om = warm_sketch(last["V"], seed, t, k, rank + oversample)
+        st = loftq_step(W32, B, A, t=t, omega=om, **kw)
         if t == 1:
             obj[0] = objective(W32, st["codes"], st["scale"], None, None, blocksize)
         obj[t] = objective(W32, st["codes"], st["scale"], st["B"], st["A"], blocksize)

@@ -217,6 +217,42 @@ def test_init_objective_small_sketches(lib, r, p):
     assert abs(direct - obj[-1]) <= 1e-4 * direct
 
 
+@pytest.mark.parametrize("q", [0, 1])
+def test_init_warm_start_against_oracle(lib, q):
+    """Warm-started subspace iteration (a variant: from alternation 2 the sketch starts from
+    the previous right singular vectors): free-running objective against the oracle's warm
+    mode, and the device objective identity."""
+    w = synth.Workload("t", 640, 512, "bf16", 16, 4, True, 8, q, False, 41, "outliers")
+    bits, W = synth.make_weight(w)
+    out = lib.loftq_init(dev_w(bits, w), lib.default_config(
+        iterative_steps=w.iterative_steps, rank=w.rank, oversample=w.oversample, power_iters=q, double_quant=1,
+        exact_svd=0, seed=w.sketch_seed, warm_start=1))
+    ref = oracle.loftq_init(W, warm_start=True, **_oracle_kw(w))
+    obj = host(out["objective"])
+    assert abs(obj[-1] - ref["objective"][-1]) <= 1e-3 * ref["objective"][-1]
+    d, k = W.shape
+    codes = oracle.unpack_nibbles(host(out["packed"]), d * k)
+    scale = oracle.dq_scales_expand(host(out["qabsmax"]), host(out["dq_scale"]))
+    direct = oracle.objective(W, codes, scale, host(out["B"]), host(out["A"]))
+    assert abs(direct - obj[-1]) <= 1e-4 * direct
+    # the warm start earns its keep: better than the cold start at the same q
+    cold = oracle.loftq_init(W, **_oracle_kw(w))
+    assert obj[-1] < cold["objective"][-1]
+
+
+def test_init_warm_start_single_alternation_is_cold(lib):
+    w = synth.Workload("t", 256, 320, "bf16", 8, 1, True, 8, 1, False, 43, "outliers")
+    bits, _ = synth.make_weight(w)
+    outs = []
+    for ws in (0, 1):
+        o = lib.loftq_init(dev_w(bits, w), lib.default_config(
+            iterative_steps=1, rank=8, oversample=8, power_iters=1, double_quant=1, exact_svd=0, seed=42,
+            warm_start=ws))
+        outs.append({k: host(v).copy() for k, v in o.items()})
+    for key in outs[0]:
+        assert np.array_equal(outs[0][key], outs[1][key]), key
+
+
 def test_init_t0_plain_nf4(lib):
     w = synth.Workload("t", 128, 192, "bf16", 8, 0, True, 8, 2, False, 5, "gauss")
     bits, W = synth.make_weight(w)

@@ -133,3 +133,30 @@ def test_loftq_randomized_dq_projection_identity():
         lhs = (res["objective"][t] ** 2) * np.sum(W64 ** 2)
         assert abs(lhs - (st["E_sumsq"] - np.sum(st["sigma"] ** 2))) <= 1e-9 * st["E_sumsq"]
     assert res["objective"][2] < res["objective"][0]
+
+
+def test_warm_sketch_recovers_exact_svd_of_rank_r_matrix():
+    # E of exact rank r: a sketch whose first r columns span E's row space gives
+    # range(E Omega) = range(E), so with no power iteration the randomized SVD is exact
+    g = np.random.default_rng(21)
+    d, k, r, p = 60, 40, 5, 3
+    E = g.standard_normal((d, r)) @ g.standard_normal((r, k))
+    _, s_ex, V_ex = oracle.exact_svd(E, r)
+    om = oracle.warm_sketch(V_ex, 42, 2, k, r + p)
+    assert np.allclose(om[:, :r], np.sqrt(k) * V_ex) and set(np.unique(om[:, r:])) <= {-1.0, 1.0}
+    _, s_w, _ = oracle.randomized_svd(E, r, om, 0)
+    assert np.allclose(s_w, s_ex, rtol=1e-11, atol=0)
+    # a cold sketch needs the power iterations to get as close on a noisy version
+    En = E + 1e-3 * g.standard_normal((d, k))
+    _, s_ref, V_ref = oracle.exact_svd(En, r)
+    _, s_w, _ = oracle.randomized_svd(En, r, oracle.warm_sketch(V_ref, 42, 2, k, r + p), 0)
+    assert np.max(np.abs(s_w - s_ref) / s_ref) < 1e-9
+
+
+def test_warm_start_with_one_alternation_is_the_cold_start():
+    g = np.random.default_rng(22)
+    W = (0.02 * g.standard_normal((96, 128))).astype(np.float32)
+    kw = dict(rank=4, iterative_steps=1, oversample=4, power_iters=1, double_quant_on=True)
+    a = oracle.loftq_init(W, **kw)
+    b = oracle.loftq_init(W, warm_start=True, **kw)
+    assert np.array_equal(a["sigma"], b["sigma"]) and np.array_equal(a["objective"], b["objective"])
