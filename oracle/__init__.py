@@ -18,6 +18,8 @@ Pages cited (their titles; sections as printed on each page):
 
 Parity status of each function (pins live in tests/test_oracle_*.py):
   nf4_codebook            pinned (printed values, exact zero, quantile definition)
+  nf_codebook (2, 3 bits) pinned (reduces to NF4 at 4 bits; the 2-bit levels in
+                          closed form from library normal quantiles)
   nf4_encode              pinned (round trip, midpoint transitions, ties, monotone)
   absmax / pack / unpack  pinned (closed forms, hand-computed fixture)
   double_quant            parity unpinned against any external format (the pages
@@ -34,7 +36,7 @@ Parity status of each function (pins live in tests/test_oracle_*.py):
                           spanning a rank-r E's row space recovers the exact SVD
                           with no power iteration)
 """
-from .nf4 import (nf4_codebook, norm_ppf, nf4_midpoints, block_absmax, nf4_encode,
+from .nf4 import (nf4_codebook, nf_codebook, nf_delta, norm_ppf, nf4_midpoints, block_absmax, nf4_encode,
                   pack_nibbles, unpack_nibbles, dequantize, quantize_residual)
 from .double_quant import double_quant, dq_scales_expand
 from .rng import splitmix64_stream, rademacher_sketch
@@ -43,7 +45,7 @@ from .loftq import loftq_step, loftq_init, objective, warm_sketch
 from .merge import merge_adapter, unmerge_adapter
 
 __all__ = [
-    "nf4_codebook", "norm_ppf", "nf4_midpoints", "block_absmax", "nf4_encode", "pack_nibbles",
+    "nf4_codebook", "nf_codebook", "nf_delta", "norm_ppf", "nf4_midpoints", "block_absmax", "nf4_encode", "pack_nibbles",
     "unpack_nibbles", "dequantize", "quantize_residual", "double_quant", "dq_scales_expand",
     "splitmix64_stream", "rademacher_sketch", "householder_qr", "jacobi_svd", "randomized_svd",
     "exact_svd", "lora_factors", "loftq_step", "loftq_init", "objective", "merge_adapter", "unmerge_adapter", "warm_sketch",

@@ -25,7 +25,7 @@ from __future__ import annotations
 
 import numpy as np
 
-from .nf4 import quantize_residual, dequantize
+from .nf4 import quantize_residual, dequantize, nf_codebook
 from .double_quant import double_quant, dq_scales_expand
 from .rng import rademacher_sketch
 from .lowrank import exact_svd, randomized_svd, lora_factors
@@ -58,12 +58,13 @@ def _residual(W32: np.ndarray, B, A) -> np.ndarray:
 
 def loftq_step(W32: np.ndarray, B_prev, A_prev, *, rank: int, t: int = 1, blocksize: int = 64,
                double_quant_on: bool = True, dq_blocksize: int = 256, exact: bool = False,
-               oversample: int = 8, power_iters: int = 2, seed: int = 42, omega=None) -> dict:
-    """One alternation: Q_t = NF4(W - B_prev A_prev), then (B_t, A_t) = SVD_r(W - deq Q_t)."""
+               oversample: int = 8, power_iters: int = 2, seed: int = 42, omega=None, bits: int = 4) -> dict:
+    """One alternation: Q_t = NF_bits(W - B_prev A_prev), then (B_t, A_t) = SVD_r(W - deq Q_t)."""
     W32 = np.asarray(W32, dtype=np.float32)
     d, k = W32.shape
+    cb = nf_codebook(bits)
     R = _residual(W32, B_prev, A_prev)
-    codes, absmax = quantize_residual(R.ravel(), blocksize)
+    codes, absmax = quantize_residual(R.ravel(), blocksize, cb)
     out = dict(R=R, codes=codes, absmax=absmax)
     if double_quant_on:
         qa, s = double_quant(absmax, dq_blocksize)
@@ -72,7 +73,7 @@ def loftq_step(W32: np.ndarray, B_prev, A_prev, *, rank: int, t: int = 1, blocks
     else:
         scale = absmax
     out["scale"] = scale
-    E = dequantize(codes, scale, blocksize, W=W32.ravel()).reshape(d, k)
+    E = dequantize(codes, scale, blocksize, W=W32.ravel(), codebook=cb).reshape(d, k)
     out["E"] = E
     out["E_sumsq"] = float(np.sum(E.astype(np.float64) ** 2))
     if exact:
@@ -88,10 +89,11 @@ def loftq_step(W32: np.ndarray, B_prev, A_prev, *, rank: int, t: int = 1, blocks
     return out
 
 
-def objective(W32: np.ndarray, codes: np.ndarray, scale: np.ndarray, B, A, blocksize: int = 64) -> float:
+def objective(W32: np.ndarray, codes: np.ndarray, scale: np.ndarray, B, A, blocksize: int = 64,
+              bits: int = 4) -> float:
     """||W - deq(Q) - BA||_F / ||W||_F in fp64."""
     W = np.asarray(W32, dtype=np.float64)
-    deq = dequantize(codes, scale, blocksize).astype(np.float64).reshape(W.shape)
+    deq = dequantize(codes, scale, blocksize, codebook=nf_codebook(bits)).astype(np.float64).reshape(W.shape)
     res = W - deq
     if B is not None:
         res = res - np.asarray(B, dtype=np.float64) @ np.asarray(A, dtype=np.float64)
@@ -101,7 +103,7 @@ def objective(W32: np.ndarray, codes: np.ndarray, scale: np.ndarray, B, A, block
 def loftq_init(W32: np.ndarray, *, rank: int, iterative_steps: int = 5, blocksize: int = 64,
                double_quant_on: bool = True, dq_blocksize: int = 256, exact: bool = False,
                oversample: int = 8, power_iters: int = 2, seed: int = 42, keep_steps: bool = False,
-               warm_start: bool = False) -> dict:
+               warm_start: bool = False, bits: int = 4) -> dict:
     """The whole initialisation: T alternations from Delta_0 = 0, objective per alternation.
 
     warm_start: alternations t >= 2 of the randomized SVD use warm_sketch(V_{t-1}, ...)
@@ -110,13 +112,13 @@ def loftq_init(W32: np.ndarray, *, rank: int, iterative_steps: int = 5, blocksiz
     W32 = np.asarray(W32, dtype=np.float32)
     d, k = W32.shape
     T = int(iterative_steps)
-    kw = dict(rank=rank, blocksize=blocksize, double_quant_on=double_quant_on, dq_blocksize=dq_blocksize,
+    kw = dict(rank=rank, blocksize=blocksize, double_quant_on=double_quant_on, dq_blocksize=dq_blocksize, bits=bits,
               exact=exact, oversample=oversample, power_iters=power_iters, seed=seed)
     obj = np.zeros(T + 1)
     steps = []
     B = A = None
     if T == 0:
-        codes, absmax = quantize_residual(W32.ravel(), blocksize)
+        codes, absmax = quantize_residual(W32.ravel(), blocksize, nf_codebook(bits))
         res = dict(codes=codes, absmax=absmax)
         if double_quant_on:
             qa, s = double_quant(absmax, dq_blocksize)
@@ -124,7 +126,7 @@ def loftq_init(W32: np.ndarray, *, rank: int, iterative_steps: int = 5, blocksiz
             scale = dq_scales_expand(qa, s, dq_blocksize)
         else:
             scale = absmax
-        obj[0] = objective(W32, codes, scale, None, None, blocksize)
+        obj[0] = objective(W32, codes, scale, None, None, blocksize, bits)
         res.update(B=np.zeros((d, rank)), A=np.zeros((rank, k)), sigma=np.zeros(rank), objective=obj)
         return res
     last = None
@@ -134,8 +136,8 @@ def loftq_init(W32: np.ndarray, *, rank: int, iterative_steps: int = 5, blocksiz
             om = warm_sketch(last["V"], seed, t, k, rank + oversample)
         st = loftq_step(W32, B, A, t=t, omega=om, **kw)
         if t == 1:
-            obj[0] = objective(W32, st["codes"], st["scale"], None, None, blocksize)
-        obj[t] = objective(W32, st["codes"], st["scale"], st["B"], st["A"], blocksize)
+            obj[0] = objective(W32, st["codes"], st["scale"], None, None, blocksize, bits)
+        obj[t] = objective(W32, st["codes"], st["scale"], st["B"], st["A"], blocksize, bits)
         B, A = st["B"], st["A"]
         last = st
         if keep_steps:

@@ -27,6 +27,11 @@ Readings where the pages are silent or garbled:
     exact-zero code (no 0/0).
   * Ties (x exactly at a midpoint) go to the lower code (argmin keeps the first).
   * Two codes per byte, element 2i in the high nibble.
+  * Lower-bit NormalFloat (k = 2, 3 bits; [LoftQ blog] reports 2- and 3-bit
+    LoftQ but gives no codebook): the same construction with 2^(k-1) positive
+    and 2^(k-1) - 1 negative quantile levels and
+    delta_k = 1 - (1/2^(k+1) + 1/(2 (2^k - 1)))/2, which is delta at k = 4.
+    A k-bit code is stored in a nibble like an NF4 code.
 """
 from __future__ import annotations
 
@@ -34,10 +39,15 @@ import math
 
 import numpy as np
 
-__all__ = ["DELTA", "norm_ppf", "nf4_codebook", "nf4_midpoints", "block_absmax", "nf4_encode",
-           "pack_nibbles", "unpack_nibbles", "dequantize", "quantize_residual"]
+__all__ = ["DELTA", "nf_delta", "norm_ppf", "nf4_codebook", "nf_codebook", "nf4_midpoints", "block_absmax",
+           "nf4_encode", "pack_nibbles", "unpack_nibbles", "dequantize", "quantize_residual"]
 
 DELTA = 1.0 - 0.5 * (1.0 / 32.0 + 1.0 / 30.0)
+
+
+def nf_delta(bits: int) -> float:
+    """delta_k = 1 - (1/2^(k+1) + 1/(2 (2^k - 1))) / 2 (= DELTA at k = 4)."""
+    return 1.0 - 0.5 * (1.0 / 2.0 ** (bits + 1) + 1.0 / (2.0 * (2.0 ** bits - 1.0)))
 
 
 def _phi(x: float) -> float:
@@ -71,8 +81,23 @@ def norm_ppf(p: float) -> float:
 
 def nf4_codebook(delta: float = DELTA) -> np.ndarray:
     """The 16 NF4 levels, ascending, as fp32 (index 0 = -1, index 7 = 0, index 15 = +1)."""
-    pos_p = np.linspace(delta, 0.5, 9)[:-1]
-    neg_p = np.linspace(delta, 0.5, 8)[:-1]
+    return _normal_float_levels(8, 7, delta)
+
+
+def nf_codebook(bits: int = 4) -> np.ndarray:
+    """The 2^bits k-bit NormalFloat levels, ascending, fp32 (bits = 2, 3 or 4; 4 is NF4)."""
+    if bits not in (2, 3, 4):
+        raise ValueError("bits must be 2, 3 or 4")
+    half = 2 ** (bits - 1)
+    return _normal_float_levels(half, half - 1, nf_delta(bits))
+
+
+def _normal_float_levels(npos: int, nneg: int, delta: float) -> np.ndarray:
+    """npos levels Phi^-1 of npos + 1 evenly spaced probabilities from delta to 1/2
+    (1/2 dropped), nneg levels -Phi^-1 of nneg + 1 such probabilities (1/2 dropped),
+    an exact zero; normalised by the largest magnitude; ascending fp32."""
+    pos_p = np.linspace(delta, 0.5, npos + 1)[:-1]
+    neg_p = np.linspace(delta, 0.5, nneg + 1)[:-1]
     levels = [norm_ppf(float(p)) for p in pos_p] + [-norm_ppf(float(p)) for p in neg_p] + [0.0]
     v = np.array(sorted(levels), dtype=np.float64)
     v = v / np.max(np.abs(v))
@@ -121,10 +146,10 @@ def nf4_encode(R: np.ndarray, absmax: np.ndarray, blocksize: int = 64,
     return codes
 
 
-def quantize_residual(R: np.ndarray, blocksize: int = 64):
+def quantize_residual(R: np.ndarray, blocksize: int = 64, codebook: np.ndarray | None = None):
     """(codes, absmax) of an fp32 residual: blockwise absmax then nearest-level encode."""
     am = block_absmax(R, blocksize)
-    return nf4_encode(R, am, blocksize), am
+    return nf4_encode(R, am, blocksize, codebook), am
 
 
 def pack_nibbles(codes: np.ndarray) -> np.ndarray:

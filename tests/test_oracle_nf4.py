@@ -165,3 +165,37 @@ def test_nf4_relative_error_on_gaussian():
 def test_non_finite_rejected(bad):
     with pytest.raises(ValueError):
         oracle.quantize_residual(np.array([1.0, bad], np.float32))
+
+
+def test_lower_bit_codebooks_reduce_to_nf4_and_closed_forms():
+    assert oracle.nf_delta(4) == DELTA
+    assert np.array_equal(oracle.nf_codebook(4).view(np.uint32), oracle.nf4_codebook().view(np.uint32))
+    # 2 bits: one negative level (-1), zero, and two positive quantiles of
+    # {delta_2, (delta_2 + 1/2) / 2}, normalised by the larger one (library quantiles)
+    d2 = 1.0 - 0.5 * (1.0 / 8.0 + 1.0 / 6.0)
+    assert oracle.nf_delta(2) == d2
+    hi, lo = norm.ppf(d2), norm.ppf(0.5 * (d2 + 0.5))
+    assert np.allclose(oracle.nf_codebook(2), [-1.0, 0.0, lo / hi, 1.0], rtol=0, atol=1e-7)
+    # 3 bits from the same definition written with library quantiles
+    d3 = 1.0 - 0.5 * (1.0 / 16.0 + 1.0 / 14.0)
+    pos = norm.ppf(np.linspace(d3, 0.5, 5)[:-1])
+    neg = -norm.ppf(np.linspace(d3, 0.5, 4)[:-1])
+    ref = np.sort(np.concatenate([pos, neg, [0.0]]))
+    assert np.allclose(oracle.nf_codebook(3), ref / np.max(np.abs(ref)), rtol=0, atol=1e-7)
+
+
+@pytest.mark.parametrize("bits", [2, 3])
+def test_lower_bit_codebook_structure_and_round_trip(bits):
+    cb = oracle.nf_codebook(bits)
+    n = 2 ** bits
+    assert cb.shape == (n,) and cb.dtype == np.float32
+    assert np.all(np.diff(cb.astype(np.float64)) > 0)
+    assert cb[0] == -1.0 and cb[-1] == 1.0 and cb[n // 2 - 1] == 0.0
+    # every level quantizes to its own index (absmax 1 via the +1 level in each block)
+    R = np.tile(np.concatenate([cb, np.ones(64 - n, np.float32)]), 3)
+    codes, am = oracle.quantize_residual(R, 64, cb)
+    assert np.all(am == 1.0)
+    assert np.array_equal(codes.reshape(3, 64)[:, :n], np.tile(np.arange(n), (3, 1)))
+    # a zero block encodes as the zero level
+    z, za = oracle.quantize_residual(np.zeros(64, np.float32), 64, cb)
+    assert np.all(z == n // 2 - 1) and za[0] == 0.0
