@@ -13,6 +13,7 @@ objective) with W already resident in HBM.  `value` is matrix elements per secon
   nf4_merge     the adapter merge of the init's own B, A into its Q, timed the same way;
   warm_start_variant  the same init with a warm-started subspace iteration and one
                 power iteration fewer (a variant; `value` stays the pages' method);
+  lower_bit     the same init with the 3- and 2-bit NormalFloat codebooks;
   cpu_baseline  the CPU oracle on a bounded row sample of the same workload.
 """
 from __future__ import annotations
@@ -282,6 +283,26 @@ def main():
                 "cold_final_objective": obj[-1], "cold_power_iters": w.power_iters}
         del wbufs
 
+    # lower-bit LoftQ: the same init with the 3- and 2-bit NormalFloat codebooks
+    lower = {}
+    for b in (3, 2):
+        bcfg = lq.default_config(iterative_steps=w.iterative_steps, rank=w.rank, oversample=w.oversample,
+                                 power_iters=w.power_iters, double_quant=int(w.double_quant),
+                                 exact_svd=int(w.exact_svd), seed=w.sketch_seed, bits=b)
+        bbufs = lq.InitBuffers(w.rows, w.cols, bcfg)
+        lq.loftq_init(Wd, bcfg, buffers=bbufs)
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        for _ in range(args.steps):
+            lq.loftq_init(Wd, bcfg, buffers=bbufs)
+        torch.cuda.synchronize()
+        bel = time.perf_counter() - t1
+        bobj = bbufs.objective.cpu().numpy().tolist()
+        lower[f"nf{b}"] = {"value": w.numel * args.steps / bel, "unit": "elements/s",
+                           "ms_per_step": 1e3 * bel / args.steps, "objective_plain": bobj[0],
+                           "objective_final": bobj[-1]}
+        del bbufs
+
     line = {
         "metric": METRIC, "value": value, "unit": "elements/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak",
@@ -290,6 +311,7 @@ def main():
                    "iterative_steps": w.iterative_steps, "oversample": w.oversample, "power_iters": w.power_iters,
                    "double_quant": w.double_quant, "blocksize": 64, "dq_blocksize": 256},
         "roofline": roofline, "nf4_quantize": nf4, "nf4_merge": merge, "warm_start_variant": warm,
+        "lower_bit": lower,
         "objective": obj, "kernels": kernels,
     }
     if not args.skip_cpu:

@@ -52,7 +52,7 @@ typedef enum { LOFTQ_F32 = 0, LOFTQ_BF16 = 1 } loftq_dtype_t;
 /* Mirrors loftq_config {bits, iterative_steps, seed} and LoraConfig.r from the
  * LoftQ blog (§3.2) and bnb_4bit_use_double_quant from the PEFT guide. */
 typedef struct {
-  int32_t bits;             /* must be 4 */
+  int32_t bits;             /* 4 (NF4), or 3 / 2 for lower-bit LoftQ (see loftq_nf_codebook) */
   int32_t iterative_steps;  /* T >= 0 alternations; 0 = plain NF4 (B = A = 0) */
   int32_t rank;             /* r >= 1 */
   int32_t blocksize;        /* must be 64 */
@@ -184,6 +184,14 @@ const char* loftq_status_string(loftq_status_t status);
 
 /* The 16 NF4 levels the library uses, ascending (index 7 = 0). [host] out16 */
 void loftq_nf4_codebook(float* out16);
+
+/* The 2^bits k-bit NormalFloat levels (bits = 2, 3, 4; 4 is NF4), ascending, index
+ * 2^(bits-1) - 1 = 0: NF4's quantile construction with 2^(bits-1) positive and
+ * 2^(bits-1) - 1 negative levels and delta = 1 - (1/2^(bits+1) + 1/(2 (2^bits - 1)))/2
+ * (the LoftQ blog, §3.2 and §4.3, reports 2- and 3-bit LoftQ without a codebook).
+ * loftq_init with cfg->bits = 2 or 3 quantizes with these levels; each code is
+ * stored in a nibble like an NF4 code. [host] out: 2^bits floats */
+loftq_status_t loftq_nf_codebook(int32_t bits, float* out);
 
 /* Kernel timing for measurement.  While enabled, every kernel the library
  * enqueues is bracketed by two HIP events recorded on that launch's stream

@@ -12,7 +12,7 @@ import importlib
 _BINDING_NAMES = {
     "loftq_nf4_quantize", "loftq_double_quant", "loftq_nf4_dequantize", "loftq_nf4_merge", "loftq_nf4_unmerge",
     "loftq_lowrank_svd", "loftq_init",
-    "default_config", "nf4_codebook", "exported_symbols", "workspace_bytes", "lowrank_workspace_bytes",
+    "default_config", "nf4_codebook", "nf_codebook", "exported_symbols", "workspace_bytes", "lowrank_workspace_bytes",
     "InitBuffers", "LoftqConfig", "LoftqError", "LIB_PATH", "EXPORTS", "profile_enable", "profile_collect",
 }
 

@@ -33,7 +33,8 @@ STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported configuration", 3: "wo
 EXPORTS = ["loftq_nf4_quantize", "loftq_double_quant", "loftq_nf4_dequantize", "loftq_nf4_merge",
            "loftq_nf4_unmerge", "loftq_lowrank_svd",
            "loftq_lowrank_svd_workspace_bytes", "loftq_init", "loftq_workspace_bytes", "loftq_default_config",
-           "loftq_status_string", "loftq_nf4_codebook", "loftq_profile_enable", "loftq_profile_collect"]
+           "loftq_status_string", "loftq_nf4_codebook", "loftq_nf_codebook", "loftq_profile_enable",
+           "loftq_profile_collect"]
 
 
 class LoftqConfig(ctypes.Structure):
@@ -71,6 +72,7 @@ _c_init_ws = _sig("loftq_workspace_bytes", _SZ, [_I64, _I64, ctypes.POINTER(Loft
 _c_defaults = _sig("loftq_default_config", None, [ctypes.POINTER(LoftqConfig)])
 _c_status = _sig("loftq_status_string", ctypes.c_char_p, [ctypes.c_int])
 _c_codebook = _sig("loftq_nf4_codebook", None, [ctypes.POINTER(ctypes.c_float)])
+_c_nf_codebook = _sig("loftq_nf_codebook", ctypes.c_int, [_I32, ctypes.POINTER(ctypes.c_float)])
 _c_prof_on = _sig("loftq_profile_enable", None, [ctypes.c_int])
 _c_prof_get = _sig("loftq_profile_collect", ctypes.c_int, [ctypes.c_int, ctypes.c_char_p, _P, _P])
 
@@ -118,6 +120,13 @@ def nf4_codebook() -> list:
     buf = (ctypes.c_float * 16)()
     _c_codebook(buf)
     return list(buf)
+
+
+def nf_codebook(bits: int) -> list:
+    """The 2^bits k-bit NormalFloat levels (bits 2, 3 or 4)."""
+    buf = (ctypes.c_float * 16)()
+    _check("loftq_nf_codebook", _c_nf_codebook(int(bits), buf))
+    return list(buf)[: 1 << int(bits)]
 
 
 def default_config(**overrides) -> LoftqConfig:

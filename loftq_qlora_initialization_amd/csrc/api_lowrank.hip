@@ -51,7 +51,8 @@ InitPlan make_init_plan(int64_t rows, int64_t cols, const loftq_config_t& c) {
 
 loftq_status_t check_config(int64_t rows, int64_t cols, const loftq_config_t* c) {
   if (c == nullptr) return LOFTQ_ERR_INVALID_ARG;
-  if (c->bits != 4 || c->blocksize != 64 || c->dq_blocksize != 256) return LOFTQ_ERR_UNSUPPORTED;
+  if ((c->bits != 2 && c->bits != 3 && c->bits != 4) || c->blocksize != 64 || c->dq_blocksize != 256)
+    return LOFTQ_ERR_UNSUPPORTED;
   if (c->iterative_steps < 0 || c->iterative_steps > 1000 || c->power_iters < 0 || c->power_iters > 64 ||
       (c->warm_start != 0 && c->warm_start != 1) || (c->double_quant != 0 && c->double_quant != 1))
     return LOFTQ_ERR_INVALID_ARG;
@@ -98,7 +99,7 @@ loftq_status_t loftq_init(const void* W, loftq_dtype_t wdt, int64_t rows, int64_
   loftq_status_t st = check_config(rows, cols, cfg);
   if (st != LOFTQ_OK) return st;
   if (wdt != LOFTQ_F32 && wdt != LOFTQ_BF16) return LOFTQ_ERR_INVALID_ARG;
-  if (!nf4_tables().valid) return LOFTQ_ERR_UNSUPPORTED;
+  if (!nf_tables(cfg->bits).valid) return LOFTQ_ERR_UNSUPPORTED;
   const bool dq = cfg->double_quant != 0;
   if (!W || !packed || !absmax || !B || !A || !objective || !sigma || !ws) return LOFTQ_ERR_INVALID_ARG;
   if (dq && (!qabsmax || !dq_scale)) return LOFTQ_ERR_INVALID_ARG;
@@ -122,11 +123,12 @@ loftq_status_t loftq_init(const void* W, loftq_dtype_t wdt, int64_t rows, int64_
   float* sketches = reinterpret_cast<float*>(w + pl.off_sketch);
   // the first dequant also leaves the partials of ||W||^2 (W is read there anyway)
   auto quant_step = [&](const float* Bp, const float* Ap, bool first) -> hipError_t {
-    hipError_t x = launch_nf4_quantize(W, wdt, rows, cols, Bp, Ap, r, packed, absmax, s);
+    hipError_t x = launch_nf4_quantize(W, wdt, rows, cols, Bp, Ap, r, packed, absmax, s, cfg->bits);
     // the double quant of the absmax is derived (and written) inside the dequant
     if (x == hipSuccess)
       x = launch_nf4_dequantize(packed, absmax, nullptr, nullptr, n, cfg->dq_blocksize, W, wdt, E, eparts,
-                                first ? wparts : nullptr, nullptr, s, dq ? qabsmax : nullptr, dq ? dq_scale : nullptr);
+                                first ? wparts : nullptr, nullptr, s, dq ? qabsmax : nullptr, dq ? dq_scale : nullptr,
+                                cfg->bits);
     return x;
   };
   hipError_t e = hipSuccess;

@@ -35,6 +35,14 @@ void loftq_nf4_codebook(float* out16) {
   if (out16) std::memcpy(out16, nf4_tables().level, 16 * sizeof(float));
 }
 
+loftq_status_t loftq_nf_codebook(int32_t bits, float* out) {
+  if (bits != 2 && bits != 3 && bits != 4) return LOFTQ_ERR_UNSUPPORTED;
+  if (!out) return LOFTQ_ERR_INVALID_ARG;
+  if (!nf_tables(bits).valid) return LOFTQ_ERR_UNSUPPORTED;   // an encoder grid invariant failed
+  std::memcpy(out, nf_tables(bits).level, (size_t(1) << bits) * sizeof(float));
+  return LOFTQ_OK;
+}
+
 void loftq_default_config(loftq_config_t* cfg) {
   if (!cfg) return;
   std::memset(cfg, 0, sizeof(*cfg));

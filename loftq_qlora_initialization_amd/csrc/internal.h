@@ -47,12 +47,15 @@ struct Nf4Tables {
   float level[16];      // ascending NF4 levels, fp32
   float thr[15];        // thr[j]: for fp32 x, x > thr[j]  <=>  x > (level[j]+level[j+1])/2
   float cell_thr[33];
-  float cell_thr16[33]; // fl32(16 cell_thr + 16) (+inf where cell_thr is +inf)
+  float cell_thr16[33]; // fl32(16 cell_thr + cell_origin) (+inf where cell_thr is +inf)
   int32_t cell_base[33];
+  float cell_origin;    // y = 16 x + cell_origin selects the cell (16 for NF4)
   int32_t valid;        // 1 if every grid invariant held at construction
 };
 
 const Nf4Tables& nf4_tables();
+// k-bit NormalFloat tables, k = 2, 3 or 4 (4: the NF4 tables); codes are stored in nibbles either way.
+const Nf4Tables& nf_tables(int bits);
 
 // Window (absolute, in x units) inside which the fast path's x' = R * (1/a)
 // may disagree with fl32(R / a) about a threshold; such elements are redone with
@@ -67,7 +70,7 @@ constexpr float kDangerWindow16 = 1.52587890625e-05f;  // 2^-16
 // ---- launchers (quant_kernels.hip) ----
 hipError_t launch_nf4_quantize(const void* W, loftq_dtype_t wdt, int64_t rows, int64_t cols,
                                const float* B, const float* A, int r, uint8_t* packed, float* absmax,
-                               hipStream_t s);
+                               hipStream_t s, int bits = 4);
 hipError_t launch_double_quant(const float* absmax, int64_t nblocks, int dqbs, int8_t* q, float* scale,
                                hipStream_t s);
 // Q' = NF4(deq(Q) + alpha B A); input scales absmax or (q, dqscale); output
@@ -85,7 +88,7 @@ hipError_t launch_nf4_dequantize(const uint8_t* packed, const float* absmax, con
                                  const float* dqscale, int64_t n, int dqbs, const void* W,
                                  loftq_dtype_t wdt, float* out, double* partials, double* wpartials,
                                  double* sumsq, hipStream_t s, int8_t* q_out = nullptr,
-                                 float* dqs_out = nullptr);
+                                 float* dqs_out = nullptr, int bits = 4);
 int dequant_num_partials(int64_t n);
 hipError_t launch_sumsq_weight(const void* W, loftq_dtype_t wdt, int64_t n, double* partials, unsigned* counter,
                                double* sumsq, hipStream_t s);

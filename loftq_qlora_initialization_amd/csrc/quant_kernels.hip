@@ -57,9 +57,10 @@ __device__ __forceinline__ float load1(const uint16_t* p, int64_t i) {
 __device__ __forceinline__ float load1(const float* p, int64_t i) { return p[i]; }
 
 struct EncodeLds {
-  float2 cell[33];  // (fl32(16 threshold + 16), base code as int bits); +inf where the cell has none
+  float2 cell[33];  // (fl32(16 threshold + origin), base code as int bits); +inf where the cell has none
   float thr[15];
   float level[16];
+  float origin;     // y = 16 x + origin picks the cell (16 for NF4)
 };
 
 __device__ __forceinline__ void fill_lds(EncodeLds& s, const Nf4Tables& t) {
@@ -67,6 +68,7 @@ __device__ __forceinline__ void fill_lds(EncodeLds& s, const Nf4Tables& t) {
   if (tid < 33) s.cell[tid] = make_float2(t.cell_thr16[tid], __int_as_float(t.cell_base[tid]));
   if (tid < 15) s.thr[tid] = t.thr[tid];
   if (tid < 16) s.level[tid] = t.level[tid];
+  if (tid == 0) s.origin = t.cell_origin;
 }
 
 // Exact reference decision for one value: count of thresholds strictly below x.
@@ -81,21 +83,23 @@ __device__ __forceinline__ uint32_t exact_code(float r, float a, const EncodeLds
 __device__ __forceinline__ int nib_shift(int e) { return 8 * ((e >> 1) & 3) + ((e & 1) ? 0 : 4); }
 
 // Encode 16 residual values sharing absmax a into two packed 32-bit words.
-// y = 16 x + 16 is formed straight from the value, y = fma(v, 16 rcp(a), 16), and
-// lands in cell int(y) of the grid (unsigned conversion saturates below 0, and
-// x <= 1 + 2^-22 keeps y below 33); the cell stores (fl32(16 thr + 16), base)
-// and code = base + (y > thr16).  y differs from 16 fl32(v / a) + 16 by less
-// than 2^-18 and thr16 from 16 thr + 16 by at most 2^-19, so outside the
-// window |y - thr16| < 2^-16 the comparison decides exactly as fl32(v / a) >
-// thr; elements inside it (and every element of a subnormal-absmax block) are
-// redone with an IEEE division and a full threshold count.
+// y = 16 x + o (o = the grid origin, 16 for NF4) is formed straight from the
+// value, y = fma(v, 16 rcp(a), o), and lands in cell int(y) of the grid
+// (unsigned conversion saturates below 0, and x <= 1 + 2^-22 keeps y below 33);
+// the cell stores (fl32(16 thr + o), base) and code = base + (y > thr16).  y
+// differs from 16 fl32(v / a) + o by less than 2^-18 and thr16 from 16 thr + o
+// by at most 2^-19, so outside the window |y - thr16| < 2^-16 the comparison
+// decides exactly as fl32(v / a) > thr; elements inside it (and every element
+// of a subnormal-absmax block) are redone with an IEEE division and a full
+// threshold count.
 __device__ __forceinline__ uint2 encode16(const float v[16], float a, const EncodeLds& s) {
   const float inv16 = (a > 0.f) ? 16.f * __builtin_amdgcn_rcpf(a) : 0.f;
+  const float origin = s.origin;
   uint32_t danger = (a > 0.f && a < FLT_MIN) ? 0xFFFFu : 0u;
   uint32_t w0 = 0, w1 = 0;
 #pragma unroll
   for (int e = 0; e < 16; ++e) {
-    const float y = fmaf(v[e], inv16, 16.f);
+    const float y = fmaf(v[e], inv16, origin);
     const float2 c = s.cell[static_cast<uint32_t>(y)];
     const float d = y - c.x;
     const uint32_t code = static_cast<uint32_t>(__float_as_int(c.y)) + ((d > 0.f) ? 1u : 0u);
@@ -641,8 +645,8 @@ dim3 fused_grid(int64_t rows, int64_t cols, int& tpw_out) {
 
 template <typename T>
 hipError_t quantize_typed(const T* W, int64_t rows, int64_t cols, const float* B, const float* A, int r,
-                          uint8_t* packed, float* absmax, hipStream_t s) {
-  const Nf4Tables& tab = nf4_tables();
+                          uint8_t* packed, float* absmax, hipStream_t s, int bits) {
+  const Nf4Tables& tab = nf_tables(bits);
   const int64_t n = rows * cols;
   if (n == 0) return hipSuccess;
   const int64_t nblocks = (n + 63) / 64;
@@ -689,8 +693,8 @@ hipError_t quantize_typed(const T* W, int64_t rows, int64_t cols, const float* B
 template <typename T>
 hipError_t dequant_typed(const uint8_t* packed, const float* absmax, const int8_t* q, const float* dqs, int64_t n,
                          int dqbs, int8_t* q_out, float* dqs_out, const T* W, float* out, double* partials,
-                         double* wpartials, double* sumsq, hipStream_t s) {
-  const Nf4Tables& tab = nf4_tables();
+                         double* wpartials, double* sumsq, hipStream_t s, int bits) {
+  const Nf4Tables& tab = nf_tables(bits);
   const int grid = dequant_num_partials(n);
   if (partials == nullptr && sumsq != nullptr) LQ_LAUNCH("zero", zero_double_kernel, dim3(1), dim3(1), 0, s, sumsq);
   const int mode = q_out != nullptr ? 2 : (q != nullptr ? 1 : 0);
@@ -714,10 +718,10 @@ int dequant_num_partials(int64_t n) {
 }
 
 hipError_t launch_nf4_quantize(const void* W, loftq_dtype_t wdt, int64_t rows, int64_t cols, const float* B,
-                               const float* A, int r, uint8_t* packed, float* absmax, hipStream_t s) {
+                               const float* A, int r, uint8_t* packed, float* absmax, hipStream_t s, int bits) {
   if (wdt == LOFTQ_BF16)
-    return quantize_typed(static_cast<const uint16_t*>(W), rows, cols, B, A, r, packed, absmax, s);
-  return quantize_typed(static_cast<const float*>(W), rows, cols, B, A, r, packed, absmax, s);
+    return quantize_typed(static_cast<const uint16_t*>(W), rows, cols, B, A, r, packed, absmax, s, bits);
+  return quantize_typed(static_cast<const float*>(W), rows, cols, B, A, r, packed, absmax, s, bits);
 }
 
 // Adapter merge Q' = NF4(deq(Q) + alpha B A) (alpha < 0 takes it out again):
@@ -779,7 +783,8 @@ hipError_t launch_double_quant(const float* absmax, int64_t nblocks, int dqbs, i
 
 hipError_t launch_nf4_dequantize(const uint8_t* packed, const float* absmax, const int8_t* q, const float* dqscale,
                                  int64_t n, int dqbs, const void* W, loftq_dtype_t wdt, float* out, double* partials,
-                                 double* wpartials, double* sumsq, hipStream_t s, int8_t* q_out, float* dqs_out) {
+                                 double* wpartials, double* sumsq, hipStream_t s, int8_t* q_out, float* dqs_out,
+                                 int bits) {
   if (n == 0) {
     if (sumsq) LQ_LAUNCH("zero", zero_double_kernel, dim3(1), dim3(1), 0, s, sumsq);
     return hipGetLastError();
@@ -787,9 +792,9 @@ hipError_t launch_nf4_dequantize(const uint8_t* packed, const float* absmax, con
   if (q_out != nullptr && dqbs != 256) return hipErrorInvalidValue;
   if (wdt == LOFTQ_BF16)
     return dequant_typed(packed, absmax, q, dqscale, n, dqbs, q_out, dqs_out, static_cast<const uint16_t*>(W), out,
-                         partials, wpartials, sumsq, s);
+                         partials, wpartials, sumsq, s, bits);
   return dequant_typed(packed, absmax, q, dqscale, n, dqbs, q_out, dqs_out, static_cast<const float*>(W), out,
-                       partials, wpartials, sumsq, s);
+                       partials, wpartials, sumsq, s, bits);
 }
 
 hipError_t launch_sumsq_weight(const void* W, loftq_dtype_t wdt, int64_t n, double* partials, unsigned* counter,

@@ -253,6 +253,68 @@ def test_init_warm_start_single_alternation_is_cold(lib):
         assert np.array_equal(outs[0][key], outs[1][key]), key
 
 
+def _bits_cfg(lib, w, bits):
+    return lib.default_config(iterative_steps=w.iterative_steps, rank=w.rank, oversample=w.oversample,
+                              power_iters=w.power_iters, double_quant=int(w.double_quant), exact_svd=0,
+                              seed=w.sketch_seed, bits=bits)
+
+
+@pytest.mark.parametrize("bits", [2, 3])
+def test_init_lower_bit_t0_bit_exact(lib, bits):
+    """T = 0 with the k-bit NormalFloat codebook: codes, absmax and double quant bit-exact."""
+    w = synth.Workload("t", 256, 384, "bf16", 8, 0, True, 8, 2, False, 50 + bits, "outliers")
+    bits_w, W = synth.make_weight(w)
+    out = lib.loftq_init(dev_w(bits_w, w), _bits_cfg(lib, w, bits))
+    ref = oracle.loftq_init(W, bits=bits, **_oracle_kw(w))
+    assert np.array_equal(host(out["packed"]), oracle.pack_nibbles(ref["codes"]))
+    assert int(oracle.unpack_nibbles(host(out["packed"]), W.size).max()) < 2 ** bits
+    assert np.array_equal(host(out["qabsmax"]), ref["qabsmax"])
+    # the device sums the fp32-rounded E, the oracle the exact fp64 differences
+    assert abs(host(out["objective"])[0] - ref["objective"][0]) <= 1e-7 * ref["objective"][0]
+
+
+@pytest.mark.parametrize("bits", [2, 3])
+def test_init_lower_bit_near_thresholds_bit_exact(lib, bits):
+    """fp32 weights within a few ulps of every k-bit midpoint under random block scales,
+    so the encoder's fast path must defer to the exact division."""
+    rng = np.random.default_rng(60 + bits)
+    cb = oracle.nf_codebook(bits).astype(np.float64)
+    mids = 0.5 * (cb[:-1] + cb[1:])
+    rows, cols = 64, 512
+    W = np.empty(rows * cols, np.float32)
+    for b in range(rows * cols // 64):
+        a = np.float32(2.0 ** rng.uniform(-8, 2))
+        blk = (rng.choice(mids, 64) * np.float64(a)).astype(np.float32)
+        toward = (rng.choice([-1.0, 1.0], 64) * np.inf).astype(np.float32)
+        for _ in range(int(rng.integers(0, 3))):
+            blk = np.nextafter(blk, toward)
+        blk[0] = a
+        W[64 * b: 64 * b + 64] = blk
+    W = W.reshape(rows, cols)
+    w = synth.Workload("t", rows, cols, "f32", 8, 0, False, 8, 2, False, 1, "gauss")
+    out = lib.loftq_init(dev_f32(W), _bits_cfg(lib, w, bits))
+    codes, am = oracle.quantize_residual(W.ravel(), 64, oracle.nf_codebook(bits))
+    assert np.array_equal(host(out["absmax"]).view(np.uint32), am.view(np.uint32))
+    assert np.array_equal(host(out["packed"]), oracle.pack_nibbles(codes))
+
+
+@pytest.mark.parametrize("bits", [2, 3])
+def test_init_lower_bit_free_running(lib, bits):
+    w = synth.Workload("t", 512, 384, "bf16", 16, 3, True, 8, 2, False, 70 + bits, "outliers")
+    bits_w, W = synth.make_weight(w)
+    out = lib.loftq_init(dev_w(bits_w, w), _bits_cfg(lib, w, bits))
+    ref = oracle.loftq_init(W, bits=bits, **_oracle_kw(w))
+    obj = host(out["objective"])
+    assert abs(obj[0] - ref["objective"][0]) <= 1e-6 * ref["objective"][0]
+    assert abs(obj[-1] - ref["objective"][-1]) <= 1e-3 * ref["objective"][-1]
+    assert obj[-1] < obj[0]
+    d, k = W.shape
+    codes = oracle.unpack_nibbles(host(out["packed"]), d * k)
+    scale = oracle.dq_scales_expand(host(out["qabsmax"]), host(out["dq_scale"]))
+    direct = oracle.objective(W, codes, scale, host(out["B"]), host(out["A"]), 64, bits)
+    assert abs(direct - obj[-1]) <= 1e-4 * direct
+
+
 def test_init_t0_plain_nf4(lib):
     w = synth.Workload("t", 128, 192, "bf16", 8, 0, True, 8, 2, False, 5, "gauss")
     bits, W = synth.make_weight(w)
