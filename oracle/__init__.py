@@ -32,6 +32,9 @@ Parity status of each function (pins live in tests/test_oracle_*.py):
   loftq_init              pinned (T=0 = plain NF4 error; objective identity)
   merge / unmerge_adapter pinned (zero adapter requantizes to the same codes,
                           doubling and cancelling closed forms, hand-worked block)
+  bf16_round              pinned (hand values, ties to even, torch's own conversion)
+  qlora_forward           pinned (bf16-exact weights give X W^T + alpha X A^T B^T computed
+                          directly; linear in X)
   warm_sketch             pinned (T = 1 reduces to the cold start; a warm sketch
                           spanning a rank-r E's row space recovers the exact SVD
                           with no power iteration)
@@ -43,10 +46,11 @@ from .rng import splitmix64_stream, rademacher_sketch
 from .lowrank import householder_qr, jacobi_svd, randomized_svd, exact_svd, lora_factors
 from .loftq import loftq_step, loftq_init, objective, warm_sketch
 from .merge import merge_adapter, unmerge_adapter
+from .forward import bf16_round, qlora_forward
 
 __all__ = [
     "nf4_codebook", "nf_codebook", "nf_delta", "norm_ppf", "nf4_midpoints", "block_absmax", "nf4_encode", "pack_nibbles",
     "unpack_nibbles", "dequantize", "quantize_residual", "double_quant", "dq_scales_expand",
     "splitmix64_stream", "rademacher_sketch", "householder_qr", "jacobi_svd", "randomized_svd",
-    "exact_svd", "lora_factors", "loftq_step", "loftq_init", "objective", "merge_adapter", "unmerge_adapter", "warm_sketch",
+    "exact_svd", "lora_factors", "loftq_step", "loftq_init", "objective", "merge_adapter", "unmerge_adapter", "warm_sketch", "bf16_round", "qlora_forward",
 ]
