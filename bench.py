@@ -14,6 +14,8 @@ objective) with W already resident in HBM.  `value` is matrix elements per secon
   warm_start_variant  the same init with a warm-started subspace iteration and one
                 power iteration fewer (a variant; `value` stays the pages' method);
   lower_bit     the same init with the 3- and 2-bit NormalFloat codebooks;
+  qlora_forward the QLoRA forward of the adapted layer on this init's Q, B, A for a
+                2048-token (matrix-core bound) and a 16-token (HBM bound) batch;
   cpu_baseline  the CPU oracle on a bounded row sample of the same workload.
 """
 from __future__ import annotations
@@ -31,6 +33,7 @@ if ROOT not in sys.path:
 
 METRIC = "LoftQ init matrix-elements/s (T alternations) + NF4 quantize GB/s vs HBM peak"
 HBM_PEAK_GBS = 8000.0   # MI355X HBM3E
+MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 matrix cores
 
 # HBM bytes per dispatch measured with rocprofv3 FETCH_SIZE / WRITE_SIZE passes (calibrated
 # against a 256 MiB device copy) on the 4096x4096 workload, valid while the kernel source
@@ -113,6 +116,8 @@ def algorithmic_bytes(name, w, rows, cols):
         "sumsq_weight": n * wb,
         # adapter merge: codes and scales in, codes and fp32 absmax out, B and A
         "nf4_merge": -(-n // 2) + scales + -(-n // 2) + 4 * nb + 4 * w.rank * (rows + cols),
+        # the quantized weight a forward reads (codes and scales); activations are added per batch
+        "qlora_weight": -(-n // 2) + scales,
     }
     return table.get(name)
 
@@ -303,6 +308,58 @@ def main():
                            "objective_final": bobj[-1]}
         del bbufs
 
+    # QLoRA forward of the adapted layer (the consumer of this init's Q, B, A): a prefill
+    # batch, a product for the bf16 matrix cores, and a decode-sized batch, bound by reading Q
+    fwd = {}
+    if w.rank > 0 and w.cols % 64 == 0:
+        dq = bool(w.double_quant)
+        scales = dict(qabsmax=bufs.qabsmax, dq_scale=bufs.dq_scale) if dq else dict(absmax=bufs.absmax)
+        gx = np.random.Generator(np.random.PCG64(np.random.SeedSequence(2024)))
+        for label, ntok in (("prefill", 2048), ("decode", 16)):
+            xb = synth.f32_to_bf16_bits(gx.standard_normal((ntok, w.cols)).astype(np.float32))
+            X = torch.from_numpy(xb.view(np.int16)).cuda().view(torch.bfloat16)
+            Y = torch.empty((ntok, w.rows), dtype=torch.float32, device="cuda")
+            ws = torch.empty(max(lq.qlora_forward_workspace_bytes(ntok, w.rank), 16), dtype=torch.uint8,
+                             device="cuda")
+
+            def call():
+                lq.loftq_qlora_forward(X, bufs.packed, (w.rows, w.cols), **scales, B=bufs.B, A=bufs.A, out=Y, ws=ws)
+            reps = 10 * args.steps
+            for _ in range(3):
+                call()
+            torch.cuda.synchronize()
+            t1 = time.perf_counter()
+            for _ in range(reps):
+                call()
+            torch.cuda.synchronize()
+            fel = time.perf_counter() - t1
+            lq.profile_enable(True)
+            for _ in range(reps):
+                call()
+            torch.cuda.synchronize()
+            lq.profile_enable(False)
+            fprof = lq.profile_collect()
+            gl, gms = fprof["nf4_gemm"]
+            g_us = 1e3 * gms / gl
+            d_us = 1e3 * fprof["lora_down"][1] / fprof["lora_down"][0] if "lora_down" in fprof else 0.0
+            flops = 2.0 * ntok * w.rows * w.cols
+            lora_flops = 2.0 * ntok * w.rank * (w.rows + w.cols)
+            qbytes = algorithmic_bytes("qlora_weight", w, w.rows, w.cols)
+            gbytes = qbytes + 2 * ntok * w.cols + 4 * ntok * w.rows + 4 * ntok * w.rank + 4 * w.rank * w.rows
+            ent = {"tokens": ntok, "us_per_forward": round(1e6 * fel / reps, 3),
+                   "tokens_per_s": round(ntok * reps / fel),
+                   "TFLOPs": round((flops + lora_flops) / (fel / reps) / 1e12, 2),
+                   "nf4_gemm_us": round(g_us, 3), "lora_down_us": round(d_us, 3)}
+            tf = flops / (g_us * 1e-6) / 1e12
+            gbs = gbytes / (g_us * 1e-6) / 1e9
+            ent["mfma"] = {"achieved": round(tf, 2), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                           "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4), "flops_per_launch": flops}
+            ent["hbm"] = {"achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                          "frac": round(gbs / HBM_PEAK_GBS, 4), "bytes_per_launch": gbytes}
+            ent["bound"] = "mfma" if label == "prefill" else "hbm"
+            fwd[label] = ent
+            del X, Y, ws
+
     line = {
         "metric": METRIC, "value": value, "unit": "elements/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak",
@@ -311,7 +368,7 @@ def main():
                    "iterative_steps": w.iterative_steps, "oversample": w.oversample, "power_iters": w.power_iters,
                    "double_quant": w.double_quant, "blocksize": 64, "dq_blocksize": 256},
         "roofline": roofline, "nf4_quantize": nf4, "nf4_merge": merge, "warm_start_variant": warm,
-        "lower_bit": lower,
+        "lower_bit": lower, "qlora_forward": fwd,
         "objective": obj, "kernels": kernels,
     }
     if not args.skip_cpu:

@@ -139,6 +139,32 @@ loftq_status_t loftq_nf4_unmerge(const uint8_t* packed, const float* absmax, con
                                  uint8_t* packed_out, float* absmax_out, int8_t* qabsmax_out, float* dq_scale_out,
                                  void* stream);
 
+/* QLoRA forward of one adapted layer, the consumer of the initialisation
+ * ("参数高效微调：LoRA、Adapter 与 QLoRA" §2.2: the adapter's output adds to the
+ * frozen weight's, h = W x + B A x; §4.3: the 4-bit base computes in bfloat16):
+ *   Y = X bf16(deq(Q))^T + alpha (X bf16(A)^T) bf16(B)^T
+ * Tokens are rows.  deq(Q) is formed as in loftq_nf4_dequantize (bits-bit
+ * NormalFloat codes in nibbles), then rounded to bf16; A and B are rounded to
+ * bf16 (nearest, ties to even); products accumulate in fp32 on the bf16 matrix
+ * cores; X A^T and Y stay fp32.
+ *   X                  [device] n_tok x cols bf16, row-major
+ *   packed             [device] codes of the rows x cols weight, as loftq_nf4_quantize
+ *   absmax             [device] fp32 block scales, or NULL when qabsmax/dq_scale are given
+ *   qabsmax, dq_scale  [device] double-quantized scales (groups of 256), or both NULL
+ *   bits               [host] 2, 3 or 4 (the codebook of loftq_nf_codebook)
+ *   B, A               [device] fp32 rows x r and r x cols (1 <= r <= 64), or both NULL
+ *                      (then Y is the base product alone and ws may be NULL)
+ *   alpha              [host] LoRA scaling (finite)
+ *   Y                  [device] n_tok x rows fp32 out
+ *   ws                 [device] loftq_qlora_forward_workspace_bytes(n_tok, r) bytes (X A^T)
+ * All device pointers 16-byte aligned.  n_tok = 0 or rows = 0 writes nothing.
+ * UNSUPPORTED: cols % 64 != 0, r > 64, more than 65535 * 128 tokens. */
+loftq_status_t loftq_qlora_forward(const void* X, int64_t n_tok, int64_t rows, int64_t cols,
+                                   const uint8_t* packed, const float* absmax, const int8_t* qabsmax,
+                                   const float* dq_scale, int32_t bits, const float* B, const float* A,
+                                   int32_t r, float alpha, float* Y, void* ws, size_t ws_bytes, void* stream);
+size_t loftq_qlora_forward_workspace_bytes(int64_t n_tok, int32_t r);
+
 /* Low-rank step ("LoftQ...", §2.3: best rank-r approximation of W - Q from its
  * r largest singular triplets, Delta = U_r S_r V_r^T).  exact = 1: the SVD of E
  * itself (one-sided Jacobi, min(rows, cols) <= 512).  exact = 0: randomized

@@ -11,7 +11,7 @@ import importlib
 
 _BINDING_NAMES = {
     "loftq_nf4_quantize", "loftq_double_quant", "loftq_nf4_dequantize", "loftq_nf4_merge", "loftq_nf4_unmerge",
-    "loftq_lowrank_svd", "loftq_init",
+    "loftq_lowrank_svd", "loftq_init", "loftq_qlora_forward", "qlora_forward_workspace_bytes",
     "default_config", "nf4_codebook", "nf_codebook", "exported_symbols", "workspace_bytes", "lowrank_workspace_bytes",
     "InitBuffers", "LoftqConfig", "LoftqError", "LIB_PATH", "EXPORTS", "profile_enable", "profile_collect",
 }

@@ -33,8 +33,8 @@ STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported configuration", 3: "wo
 EXPORTS = ["loftq_nf4_quantize", "loftq_double_quant", "loftq_nf4_dequantize", "loftq_nf4_merge",
            "loftq_nf4_unmerge", "loftq_lowrank_svd",
            "loftq_lowrank_svd_workspace_bytes", "loftq_init", "loftq_workspace_bytes", "loftq_default_config",
-           "loftq_status_string", "loftq_nf4_codebook", "loftq_nf_codebook", "loftq_profile_enable",
-           "loftq_profile_collect"]
+           "loftq_status_string", "loftq_nf4_codebook", "loftq_nf_codebook", "loftq_qlora_forward",
+           "loftq_qlora_forward_workspace_bytes", "loftq_profile_enable", "loftq_profile_collect"]
 
 
 class LoftqConfig(ctypes.Structure):
@@ -62,6 +62,9 @@ _c_deq = _sig("loftq_nf4_dequantize", ctypes.c_int,
 _MERGE_ARGS = [_P, _P, _P, _P, _I64, _I64, _I32, _I32, _P, _P, _I32, ctypes.c_float, _P, _P, _P, _P, _P]
 _c_merge = _sig("loftq_nf4_merge", ctypes.c_int, _MERGE_ARGS)
 _c_unmerge = _sig("loftq_nf4_unmerge", ctypes.c_int, _MERGE_ARGS)
+_c_fwd = _sig("loftq_qlora_forward", ctypes.c_int,
+              [_P, _I64, _I64, _I64, _P, _P, _P, _P, _I32, _P, _P, _I32, ctypes.c_float, _P, _P, _SZ, _P])
+_c_fwd_ws = _sig("loftq_qlora_forward_workspace_bytes", _SZ, [_I64, _I32])
 _c_svd = _sig("loftq_lowrank_svd", ctypes.c_int,
               [_P, _I64, _I64, _I32, _I32, _I32, _I32, _P, _U64, _I32, _P, _P, _P, _P, _SZ, _P])
 _c_svd_ws = _sig("loftq_lowrank_svd_workspace_bytes", _SZ, [_I64, _I64, _I32, _I32, _I32])
@@ -218,6 +221,40 @@ def loftq_nf4_unmerge(packed: torch.Tensor, shape, B: Optional[torch.Tensor], A:
     """Q' = NF4(deq(Q) - alpha B A), the reverse of loftq_nf4_merge (not an exact inverse)."""
     return _merge_call("loftq_nf4_unmerge", _c_unmerge, packed, shape, absmax, qabsmax, dq_scale, B, A, alpha,
                        double_quant, out, stream)
+
+
+def qlora_forward_workspace_bytes(n_tok: int, r: int) -> int:
+    return int(_c_fwd_ws(n_tok, r))
+
+
+def loftq_qlora_forward(X: torch.Tensor, packed: torch.Tensor, shape, absmax: Optional[torch.Tensor] = None,
+                        qabsmax: Optional[torch.Tensor] = None, dq_scale: Optional[torch.Tensor] = None,
+                        B: Optional[torch.Tensor] = None, A: Optional[torch.Tensor] = None, alpha: float = 1.0,
+                        bits: int = 4, out: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None,
+                        stream=None) -> torch.Tensor:
+    """Y = X bf16(deq(Q))^T + alpha (X bf16(A)^T) bf16(B)^T for bf16 X (n_tok x cols); Y fp32 n_tok x rows."""
+    _contig(X, "X")
+    if X.dtype != torch.bfloat16:
+        raise TypeError("X must be bfloat16")
+    rows, cols = shape
+    n_tok = X.shape[0]
+    r = 0
+    if B is not None:
+        _contig(B, "B"), _contig(A, "A")
+        r = B.shape[1]
+    if out is None:
+        out = torch.empty((n_tok, rows), dtype=torch.float32, device=X.device)
+    ws_bytes = 0
+    if B is not None:
+        ws_bytes = qlora_forward_workspace_bytes(n_tok, r)
+        if ws is None:
+            ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=X.device)
+        else:
+            ws_bytes = ws.numel() * ws.element_size()
+    _check("loftq_qlora_forward",
+           _c_fwd(_ptr(X), n_tok, rows, cols, _ptr(packed), _ptr(absmax), _ptr(qabsmax), _ptr(dq_scale), int(bits),
+                  _ptr(B), _ptr(A), r, float(alpha), _ptr(out), _ptr(ws), ws_bytes, _stream(stream)))
+    return out
 
 
 def lowrank_workspace_bytes(rows: int, cols: int, r: int, oversample: int, exact: bool) -> int:

@@ -157,4 +157,36 @@ loftq_status_t loftq_nf4_unmerge(const uint8_t* packed, const float* absmax, con
                     packed_out, absmax_out, qabsmax_out, dq_scale_out, stream);
 }
 
+size_t loftq_qlora_forward_workspace_bytes(int64_t n_tok, int32_t r) {
+  if (n_tok < 0 || n_tok >= (int64_t(1) << 31) || r < 0 || r > 64) return 0;
+  return qlora_forward_workspace_bytes(n_tok, r);
+}
+
+loftq_status_t loftq_qlora_forward(const void* X, int64_t n_tok, int64_t rows, int64_t cols, const uint8_t* packed,
+                                   const float* absmax, const int8_t* qabsmax, const float* dq_scale, int32_t bits,
+                                   const float* B, const float* A, int32_t r, float alpha, float* Y, void* ws,
+                                   size_t ws_bytes, void* stream) {
+  if (!shape_ok(rows, cols) || n_tok < 0 || n_tok >= (int64_t(1) << 31)) return LOFTQ_ERR_INVALID_ARG;
+  if (bits != 2 && bits != 3 && bits != 4) return LOFTQ_ERR_UNSUPPORTED;
+  if (!nf_tables(bits).valid) return LOFTQ_ERR_UNSUPPORTED;
+  const bool dq = qabsmax != nullptr || dq_scale != nullptr;
+  if (dq && (!qabsmax || !dq_scale)) return LOFTQ_ERR_INVALID_ARG;
+  if ((B == nullptr) != (A == nullptr)) return LOFTQ_ERR_INVALID_ARG;
+  if (B != nullptr && r < 1) return LOFTQ_ERR_INVALID_ARG;
+  if (!std::isfinite(alpha)) return LOFTQ_ERR_INVALID_ARG;
+  if (n_tok == 0 || rows == 0) return LOFTQ_OK;   // nothing to write
+  if (cols == 0 || cols % 64 != 0 || (B != nullptr && r > 64)) return LOFTQ_ERR_UNSUPPORTED;
+  if ((n_tok + 127) / 128 > 65535) return LOFTQ_ERR_UNSUPPORTED;   // token tiles on grid y
+  if (!X || !packed || !Y || (!dq && !absmax)) return LOFTQ_ERR_INVALID_ARG;
+  if (!aligned16(X) || !aligned16(packed) || !aligned16(Y)) return LOFTQ_ERR_INVALID_ARG;
+  if (dq ? (!aligned16(qabsmax) || !aligned16(dq_scale)) : !aligned16(absmax)) return LOFTQ_ERR_INVALID_ARG;
+  if (B != nullptr) {
+    if (!aligned16(B) || !aligned16(A) || !ws || !aligned16(ws)) return LOFTQ_ERR_INVALID_ARG;
+    if (ws_bytes < qlora_forward_workspace_bytes(n_tok, r)) return LOFTQ_ERR_WORKSPACE;
+  }
+  return from_hip(launch_qlora_forward(X, n_tok, rows, cols, packed, dq ? nullptr : absmax, dq ? qabsmax : nullptr,
+                                       dq ? dq_scale : nullptr, bits, B, A, B ? r : 0, alpha, Y,
+                                       static_cast<float*>(ws), static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

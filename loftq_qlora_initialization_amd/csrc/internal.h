@@ -73,6 +73,12 @@ hipError_t launch_nf4_quantize(const void* W, loftq_dtype_t wdt, int64_t rows, i
                                hipStream_t s, int bits = 4);
 hipError_t launch_double_quant(const float* absmax, int64_t nblocks, int dqbs, int8_t* q, float* scale,
                                hipStream_t s);
+// QLoRA forward Y = X bf16(deq(Q))^T + alpha (X bf16(A)^T) bf16(B)^T (forward_kernels.hip);
+// Tws: n_tok x r fp32 scratch for X A^T (qlora_forward_workspace_bytes), unused without B.
+size_t qlora_forward_workspace_bytes(int64_t n_tok, int r);
+hipError_t launch_qlora_forward(const void* X, int64_t n_tok, int64_t rows, int64_t cols, const uint8_t* packed,
+                                const float* absmax, const int8_t* qa, const float* dqs, int bits, const float* B,
+                                const float* A, int r, float alpha, float* Y, float* Tws, hipStream_t s);
 // Q' = NF4(deq(Q) + alpha B A); input scales absmax or (q, dqscale); output
 // absmax_out and, with q_out / dqs_out, its double quant (dq_blocksize 256).
 hipError_t launch_nf4_merge(const uint8_t* packed, const float* absmax, const int8_t* q, const float* dqscale,

@@ -112,3 +112,38 @@ def test_merge_validation(clib, name):
     assert call(ao=F + 4) == 1                                # misaligned output absmax
     assert call(alpha=float("inf")) == 1                      # non-finite scale
     assert call(rows=0) == 0                                  # empty: nothing to do
+
+
+def test_qlora_forward_validation(clib):
+    f = clib.loftq_qlora_forward
+    P, I64, I32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32
+    f.restype = ctypes.c_int
+    f.argtypes = [P, I64, I64, I64, P, P, P, P, I32, P, P, I32, ctypes.c_float, P, P, ctypes.c_size_t, P]
+    clib.loftq_qlora_forward_workspace_bytes.restype = ctypes.c_size_t
+    clib.loftq_qlora_forward_workspace_bytes.argtypes = [I64, I32]
+    F = FAKE
+    ws_need = clib.loftq_qlora_forward_workspace_bytes(32, 8)
+    assert ws_need >= 32 * 8 * 4 and ws_need % 256 == 0
+    keys = ["X", "n", "rows", "cols", "packed", "absmax", "qa", "dqs", "bits", "B", "A", "r", "alpha", "Y", "ws",
+            "wsb"]
+    ok = (F, 32, 64, 128, F, F, None, None, 4, F, F, 8, 1.0, F, F, ws_need)
+
+    def call(**kw):
+        args = list(ok)
+        for k, v in kw.items():
+            args[keys.index(k)] = v
+        return f(*args, None)
+    assert call(bits=5) == 2                                  # no such codebook
+    assert call(cols=96) == 2                                 # rows of the weight split a 64-block
+    assert call(r=65) == 2                                    # rank above 64
+    assert call(n=128 * 65536) == 2                           # token tiles beyond grid y
+    assert call(A=None) == 1                                  # B without A
+    assert call(absmax=None) == 1                             # no scales
+    assert call(qa=F) == 1                                    # qabsmax without dq_scale
+    assert call(X=None) == 1
+    assert call(Y=F + 4) == 1                                 # misaligned output
+    assert call(alpha=float("nan")) == 1
+    assert call(n=-1) == 1
+    assert call(wsb=ws_need - 1) == 3                         # workspace too small
+    assert call(ws=None) == 1                                 # adapter without workspace
+    assert call(n=0) == 0 and call(rows=0) == 0               # empty: nothing to write
