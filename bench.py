@@ -339,7 +339,7 @@ def main():
             torch.cuda.synchronize()
             lq.profile_enable(False)
             fprof = lq.profile_collect()
-            gl, gms = fprof["nf4_gemm"]
+            gl, gms = fprof["nf4_gemm"] if "nf4_gemm" in fprof else fprof["nf4_gemm_skinny"]
             g_us = 1e3 * gms / gl
             d_us = 1e3 * fprof["lora_down"][1] / fprof["lora_down"][0] if "lora_down" in fprof else 0.0
             flops = 2.0 * ntok * w.rows * w.cols

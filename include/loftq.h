@@ -156,7 +156,8 @@ loftq_status_t loftq_nf4_unmerge(const uint8_t* packed, const float* absmax, con
  *                      (then Y is the base product alone and ws may be NULL)
  *   alpha              [host] LoRA scaling (finite)
  *   Y                  [device] n_tok x rows fp32 out
- *   ws                 [device] loftq_qlora_forward_workspace_bytes(n_tok, r) bytes (X A^T)
+ *   ws                 [device] loftq_qlora_forward_workspace_bytes(n_tok, r) bytes (partial
+ *                      products X A^T over K ranges)
  * All device pointers 16-byte aligned.  n_tok = 0 or rows = 0 writes nothing.
  * UNSUPPORTED: cols % 64 != 0, r > 64, more than 65535 * 128 tokens. */
 loftq_status_t loftq_qlora_forward(const void* X, int64_t n_tok, int64_t rows, int64_t cols,

@@ -4,16 +4,20 @@
 // weight's, h = W x + B A x; §4.3: the 4-bit base computes in bfloat16).
 // Tokens are rows: X n x cols (bf16), Y n x rows (fp32), W = deq(Q) rows x cols.
 //
-// lora_down_kernel  T = X bf16(A)^T (n x r, fp32) on bf16 MFMA (16x16x32), one
-//                   16-token tile and all r columns per wave, straight from global.
-// nf4_gemm_kernel   Y = X bf16(W)^T + alpha T bf16(B)^T: a 128 x 128 output tile per
-//                   workgroup of 4 waves (64 x 64 each, 4 x 4 MFMA tiles), K in
-//                   steps of 32.  Each step the workgroup stages X (bf16) and the
-//                   weight decoded from NF4 codes (deq = fl32(c[code] a') exactly as
-//                   in the dequantization, then rounded to bf16) in LDS, double
-//                   buffered with one barrier per step; the next step's global
-//                   loads are in flight while the current step's MFMAs run.  The
-//                   epilogue adds the LoRA term in fp32.
+// lora_down_kernel   T = X bf16(A)^T (n x r, fp32) on bf16 MFMA (16x16x32) as up
+//                    to 8 partial products over K ranges (16 tokens and one range
+//                    per workgroup, the range split over its 16 waves); the GEMM
+//                    kernels sum the partials of their tokens once, into LDS.
+// nf4_gemm_kernel    more than 64 tokens: Y = X bf16(W)^T + alpha T bf16(B)^T, a
+//                    128 x 128 output tile per workgroup of 4 waves (64 x 64 each,
+//                    4 x 4 MFMA tiles), K in steps of 64.  Each step the workgroup
+//                    stages X (bf16) and the weight decoded from its codes (deq =
+//                    fl32(c[code] a') exactly as in the dequantization, then rounded
+//                    to bf16) in LDS, double buffered with one barrier per step,
+//                    while the global loads of two steps ahead are in flight.  The
+//                    epilogue adds the LoRA term in fp32.
+// nf4_skinny_kernel  up to 64 tokens: bound by reading Q; decodes codes straight
+//                    into matrix-core operands, K split over the workgroup's waves.
 //
 // v_mfma_f32_16x16x32_bf16: lane L supplies A[L%16][8(L/16) + j] and
 // B[8(L/16) + j][L%16] (j = 0..7) and receives D[4(L/16) + v][L%16] in element v.
@@ -24,88 +28,139 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float mfma_f4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
-constexpr int kBM = 128, kBN = 128, kBK = 32, kLdsRow = kBK + 8;   // +8 bf16 per row against bank conflicts
+constexpr int kBM = 128, kBN = 128, kBK = 64, kLdsRow = kBK + 8;   // +8 bf16 per row against bank conflicts
 constexpr int kGemmThreads = 256;
 
 __device__ __forceinline__ int nib_shift16(int e) { return 8 * ((e >> 1) & 3) + ((e & 1) ? 0 : 4); }
 
+// Workgroups are dealt to the 8 XCDs round-robin by id.  Tile t = xcd * per + slot
+// gives each XCD a contiguous run of tiles (token tile outer, feature tile inner),
+// so the activations of its token tiles stay in that XCD's L2; ids past the last
+// full round keep their own index.
+__device__ __forceinline__ int64_t xcd_tile(int64_t wg, int64_t total) {
+  const int64_t per = total / 8;
+  return wg < per * 8 ? (wg % 8) * per + wg / 8 : wg;
+}
+
 template <bool kDQ>
-__global__ __launch_bounds__(kGemmThreads) void nf4_gemm_kernel(const __bf16* __restrict__ X, int64_t M, int64_t N,
+__global__ __launch_bounds__(kGemmThreads, 2) void nf4_gemm_kernel(const __bf16* __restrict__ X, int64_t M, int64_t N,
                                                                 int64_t K, const uint8_t* __restrict__ packed,
                                                                 const float* __restrict__ absmax,
                                                                 const int8_t* __restrict__ qa,
                                                                 const float* __restrict__ dqs,
-                                                                const float* __restrict__ T, const float* __restrict__ B,
-                                                                int r, float alpha, float* __restrict__ Y, Nf4Tables tab) {
+                                                                const float* __restrict__ T, int ks,
+                                                                const float* __restrict__ B, int r, float alpha,
+                                                                float* __restrict__ Y, Nf4Tables tab) {
   __shared__ __align__(16) __bf16 Xs[2][kBM][kLdsRow];
   __shared__ __align__(16) __bf16 Ws[2][kBN][kLdsRow];
   __shared__ float lvl[16];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, wm = w & 1, wn = w >> 1;
   const int li = lane & 15, lg = lane >> 4;
   if (tid < 16) lvl[tid] = tab.level[tid];
-  const int64_t m0 = static_cast<int64_t>(blockIdx.y) * kBM, n0 = static_cast<int64_t>(blockIdx.x) * kBN;
-  // this thread's share of one step: row `row` of the X and W tiles, 16 elements at column 16 half
+  const int64_t ntn = (N + kBN - 1) / kBN, ntm = (M + kBM - 1) / kBM;
+  const int64_t tile = xcd_tile(blockIdx.x, ntn * ntm);
+  const int64_t m0 = (tile / ntn) * kBM, n0 = (tile % ntn) * kBN;
+  // this thread's share of one step: row `row` of the X and W tiles, 32 elements at column 32 half
   const int row = tid >> 1, half = tid & 1;
   const int64_t xr = (m0 + row < M) ? m0 + row : M - 1;   // clamped rows: loaded, never stored
   const int64_t wr = (n0 + row < N) ? n0 + row : N - 1;
-  const uint4* xsrc = reinterpret_cast<const uint4*>(X + xr * K + 16 * half);
-  const int64_t we0 = wr * K + 16 * half;                  // element index of this thread's 16 weights
-  uint4 xv[2];
-  uint2 wc;
-  float sc;
-  auto load = [&](int kt) {
-    const int64_t k0 = static_cast<int64_t>(kt) * kBK;
-    xv[0] = xsrc[k0 / 8];
-    xv[1] = xsrc[k0 / 8 + 1];
-    const int64_t e = we0 + k0;
-    wc = *reinterpret_cast<const uint2*>(packed + (e >> 1));
-    const int64_t b = e >> 6;
-    sc = kDQ ? static_cast<float>(qa[b]) * dqs[b >> 8] : absmax[b];
+  const u32x4* xsrc = reinterpret_cast<const u32x4*>(X + xr * K + 32 * half);
+  const int64_t we0 = wr * K + 32 * half;                  // element index of this thread's 32 weights
+  // one step's global data in registers; two of them keep the loads of step kt + 2
+  // in flight while step kt computes and step kt + 1 goes from registers to LDS
+  struct Stage {
+    u32x4 x[4];
+    u32x4 wc;
+    float sc;
   };
-  auto store = [&](int buf) {
-    uint4* xd = reinterpret_cast<uint4*>(&Xs[buf][row][16 * half]);
-    xd[0] = xv[0];
-    xd[1] = xv[1];
-    bf16x8 o[2];
+  auto load = [&](Stage& st, int kt) __attribute__((always_inline)) {
+    const int64_t k0 = static_cast<int64_t>(kt) * kBK;
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const uint32_t code = ((e < 8 ? wc.x : wc.y) >> nib_shift16(e)) & 0xFu;
-      o[e >> 3][e & 7] = static_cast<__bf16>(lvl[code] * sc);   // exact fp32 deq, then RNE to bf16
+    for (int q = 0; q < 4; ++q) st.x[q] = xsrc[k0 / 8 + q];
+    const int64_t e = we0 + k0;
+    st.wc = *reinterpret_cast<const u32x4*>(packed + (e >> 1));
+    const int64_t b = e >> 6;
+    st.sc = kDQ ? static_cast<float>(qa[b]) * dqs[b >> 8] : absmax[b];
+  };
+  auto store = [&](const Stage& st, int buf) __attribute__((always_inline)) {
+    u32x4* xd = reinterpret_cast<u32x4*>(&Xs[buf][row][32 * half]);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) xd[q] = st.x[q];
+    bf16x8 o[4];
+#pragma unroll
+    for (int e = 0; e < 32; ++e) {
+      const uint32_t code = (st.wc[e >> 3] >> nib_shift16(e)) & 0xFu;
+      o[e >> 3][e & 7] = static_cast<__bf16>(lvl[code] * st.sc);   // exact fp32 deq, then RNE to bf16
     }
-    bf16x8* wd = reinterpret_cast<bf16x8*>(&Ws[buf][row][16 * half]);
-    wd[0] = o[0];
-    wd[1] = o[1];
+    bf16x8* wd = reinterpret_cast<bf16x8*>(&Ws[buf][row][32 * half]);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) wd[q] = o[q];
   };
   mfma_f4 acc[4][4];
 #pragma unroll
   for (int a = 0; a < 4; ++a)
 #pragma unroll
     for (int b = 0; b < 4; ++b) acc[a][b] = mfma_f4{0.f, 0.f, 0.f, 0.f};
-  const int KT = static_cast<int>(K / kBK);
-  __syncthreads();   // lvl
-  load(0);
-  store(0);
-  __syncthreads();
-  for (int kt = 0; kt < KT; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < KT) load(kt + 1);
-    bf16x8 af[4], bfr[4];
+  auto compute = [&](int buf) __attribute__((always_inline)) {
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt) af[mt] = *reinterpret_cast<const bf16x8*>(&Xs[buf][wm * 64 + mt * 16 + li][8 * lg]);
+    for (int kk = 0; kk < kBK; kk += 32) {
+      bf16x8 af[4], bfr[4];
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt) bfr[nt] = *reinterpret_cast<const bf16x8*>(&Ws[buf][wn * 64 + nt * 16 + li][8 * lg]);
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
+      for (int mt = 0; mt < 4; ++mt)
+        af[mt] = *reinterpret_cast<const bf16x8*>(&Xs[buf][wm * 64 + mt * 16 + li][kk + 8 * lg]);
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt)
-        acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[mt], bfr[nt], acc[mt][nt], 0, 0, 0);
-    if (kt + 1 < KT) store(buf ^ 1);
+        bfr[nt] = *reinterpret_cast<const bf16x8*>(&Ws[buf][wn * 64 + nt * 16 + li][kk + 8 * lg]);
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt)
+          acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[mt], bfr[nt], acc[mt][nt], 0, 0, 0);
+    }
+  };
+  const int KT = static_cast<int>(K / kBK);
+  Stage s0, s1;
+  __syncthreads();   // lvl
+  load(s0, 0);
+  load(s1, KT > 1 ? 1 : 0);
+  store(s0, 0);
+  __syncthreads();
+  // Even steps read LDS buffer 0, odd steps buffer 1.  Each half of the loop is one
+  // basic block (loads of two steps ahead, this step's products, the decode and
+  // store of the next step), so the decode can issue between the matrix ops; past
+  // the last step the loads repeat step KT - 1 and the store fills the idle buffer.
+  int kt = 0;
+  for (; kt + 1 < KT; kt += 2) {
+    load(s0, kt + 2 < KT ? kt + 2 : KT - 1);
+    compute(0);
+    store(s1, 1);
+    __syncthreads();
+    load(s1, kt + 3 < KT ? kt + 3 : KT - 1);
+    compute(1);
+    store(s0, 0);
     __syncthreads();
   }
+  if (kt < KT) compute(0);   // odd step count: the last step sits in buffer 0
   // Epilogue.  Element v of tile (mt, nt) is token m = .. + 4 lg + v, feature n = .. + li.
-  // The LoRA term T bf16(B)^T of the same 16 x 16 tile is one fp32 MFMA (16x16x4)
-  // per 4 of r: lane L supplies T[m0 + L%16][p0 + L/16] and bf16(B)[n0 + L%16][p0 + L/16].
+  // The tile's rows of X A^T (the sum of the ks K-split partials, in split order) go to
+  // LDS, over the now idle X buffers.  The LoRA term T bf16(B)^T of a 16 x 16 tile is
+  // one fp32 MFMA (16x16x4) per 4 of r: lane L supplies T[m0 + L%16][p0 + L/16] and
+  // bf16(B)[n0 + L%16][p0 + L/16].
+  float* Ts = reinterpret_cast<float*>(&Xs[0][0][0]);   // kBM x r fp32, r <= 64
+  if (T != nullptr) {
+    __syncthreads();
+    for (int idx = tid; idx < kBM * r; idx += kGemmThreads) {
+      const int i = idx / r, p = idx - i * r;
+      float t = 0.f;
+      if (m0 + i < M)
+        for (int q = 0; q < ks; ++q) t += T[(q * M + m0 + i) * r + p];
+      Ts[idx] = t;
+    }
+    __syncthreads();
+  }
   const int64_t mw = m0 + wm * 64, nw = n0 + wn * 64;
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt) {
@@ -113,10 +168,10 @@ __global__ __launch_bounds__(kGemmThreads) void nf4_gemm_kernel(const __bf16* __
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt) lora[nt] = mfma_f4{0.f, 0.f, 0.f, 0.f};
     if (T != nullptr) {
-      const int64_t tm = mw + mt * 16 + li;
+      const int tl = wm * 64 + mt * 16 + li;
       for (int p0 = 0; p0 < r; p0 += 4) {
         const int p = p0 + lg;
-        const float tv = (tm < M && p < r) ? T[tm * r + p] : 0.f;
+        const float tv = p < r ? Ts[tl * r + p] : 0.f;
 #pragma unroll
         for (int nt = 0; nt < 4; ++nt) {
           const int64_t bn = nw + nt * 16 + li;
@@ -138,51 +193,215 @@ __global__ __launch_bounds__(kGemmThreads) void nf4_gemm_kernel(const __bf16* __
   }
 }
 
-// T = X bf16(A)^T: wave = one 16-token tile, NT 16-column tiles of r.
+// Partial products P_q = X bf16(A)^T over the q-th of ks K ranges, for one 16-token
+// tile per workgroup (workgroup = tile * ks + q); P_q lands at T + q n r.  The 16
+// waves split the range (wave w takes U consecutive 32-wide steps from 16 U w on,
+// then every 16 U steps) and their partial 16 x r products are summed through LDS
+// in a fixed order.  Consumers add the ks partials in order q = 0, 1, ...
 template <int NT>
-__global__ __launch_bounds__(256) void lora_down_kernel(const __bf16* __restrict__ X, int64_t M, int64_t K,
-                                                        const float* __restrict__ A, int r, float* __restrict__ T) {
-  const int lane = threadIdx.x & 63, li = lane & 15, lg = lane >> 4;
-  const int64_t tile = (static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x) >> 6;
+__global__ __launch_bounds__(1024) void lora_down_kernel(const __bf16* __restrict__ X, int64_t M, int64_t K,
+                                                         const float* __restrict__ A, int r, int ks,
+                                                         float* __restrict__ T) {
+  __shared__ float part[8][NT * 256];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, li = lane & 15, lg = lane >> 4;
+  const int64_t tile = blockIdx.x / ks;
+  const int q = static_cast<int>(blockIdx.x - tile * ks);
   const int64_t m0 = tile * 16;
-  if (m0 >= M) return;
   const int64_t xr = (m0 + li < M) ? m0 + li : M - 1;
   mfma_f4 acc[NT];
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) acc[nt] = mfma_f4{0.f, 0.f, 0.f, 0.f};
-  for (int64_t k0 = 0; k0 < K; k0 += 32) {
-    const bf16x8 a = *reinterpret_cast<const bf16x8*>(X + xr * K + k0 + 8 * lg);
+  // each wave takes U consecutive 32-wide steps per round and issues all their loads
+  // before the first product (rows p >= r load row r - 1 and are zeroed)
+  constexpr int U = NT == 1 ? 8 : (NT == 2 ? 4 : 2);
+  const int KT = static_cast<int>(K / 32);
+  const int per = (KT + ks - 1) / ks;
+  const int k_begin = q * per, k_end = k_begin + per < KT ? k_begin + per : KT;
+  for (int base = k_begin + w * U; base < k_end; base += 16 * U) {
+    bf16x8 a[U];
+    float4 ua[U][NT], ub[U][NT];
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      const int p = nt * 16 + li;
-      bf16x8 b;
-      if (p < r) {
-        const float4* src = reinterpret_cast<const float4*>(A + static_cast<int64_t>(p) * K + k0 + 8 * lg);
-        const float4 u = src[0], q = src[1];
-        b[0] = static_cast<__bf16>(u.x); b[1] = static_cast<__bf16>(u.y);
-        b[2] = static_cast<__bf16>(u.z); b[3] = static_cast<__bf16>(u.w);
-        b[4] = static_cast<__bf16>(q.x); b[5] = static_cast<__bf16>(q.y);
-        b[6] = static_cast<__bf16>(q.z); b[7] = static_cast<__bf16>(q.w);
-      } else {
-        for (int j = 0; j < 8; ++j) b[j] = static_cast<__bf16>(0.f);
+    for (int i = 0; i < U; ++i) {
+      const int kt = base + i < KT ? base + i : KT - 1;
+      const int64_t k0 = static_cast<int64_t>(kt) * 32 + 8 * lg;
+      a[i] = *reinterpret_cast<const bf16x8*>(X + xr * K + k0);
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        const int p = nt * 16 + li < r ? nt * 16 + li : r - 1;
+        const float4* src = reinterpret_cast<const float4*>(A + static_cast<int64_t>(p) * K + k0);
+        ua[i][nt] = src[0];
+        ub[i][nt] = src[1];
       }
-      acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc[nt], 0, 0, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);   // every load of the round is in flight before the first wait
+#pragma unroll
+    for (int i = 0; i < U; ++i) {
+      // steps past the range (clamped loads) and rows p >= r contribute exact zeros
+      const bool live = base + i < k_end;
+      const bf16x8 ai = live ? a[i] : bf16x8{};
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        const float z = (live && nt * 16 + li < r) ? 1.f : 0.f;
+        const float4 u = ua[i][nt], q = ub[i][nt];
+        bf16x8 b;
+        b[0] = static_cast<__bf16>(u.x * z); b[1] = static_cast<__bf16>(u.y * z);
+        b[2] = static_cast<__bf16>(u.z * z); b[3] = static_cast<__bf16>(u.w * z);
+        b[4] = static_cast<__bf16>(q.x * z); b[5] = static_cast<__bf16>(q.y * z);
+        b[6] = static_cast<__bf16>(q.z * z); b[7] = static_cast<__bf16>(q.w * z);
+        acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ai, b, acc[nt], 0, 0, 0);
+      }
     }
   }
+  // waves 8..15 park their partials, waves 0..7 add theirs, then one thread per
+  // element sums the 8 pair sums in wave order
+  if (w >= 8) {
 #pragma unroll
-  for (int nt = 0; nt < NT; ++nt)
+    for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int64_t m = m0 + 4 * lg + v;
-      const int p = nt * 16 + li;
-      if (m < M && p < r) T[m * r + p] = acc[nt][v];
+      for (int v = 0; v < 4; ++v) part[w - 8][(nt * 4 + v) * 64 + lane] = acc[nt][v];
+  }
+  __syncthreads();
+  if (w < 8) {
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) part[w][(nt * 4 + v) * 64 + lane] += acc[nt][v];
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < NT * 256; e += 1024) {
+    float sum = 0.f;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) sum += part[q][e];
+    const int ln = e & 63, v = (e >> 6) & 3, nt = e >> 8;
+    const int64_t m = m0 + 4 * (ln >> 4) + v;
+    const int p = nt * 16 + (ln & 15);
+    if (m < M && p < r) T[(q * M + m) * r + p] = sum;
+  }
+}
+
+// Few tokens (<= 64): the product is bound by reading Q, so each workgroup owns 16
+// output features and every token, and its NW waves split K in 128-wide chunks
+// (wave w takes chunks w, w + NW, ...; NW = 16, or 8 for 3-4 token tiles, whose
+// operands need more registers).  Lane L decodes the 32 codes of feature
+// n0 + L%16 at k = 128 c + 32 (L/16) .. + 31 (one 16-byte load, one block scale)
+// straight into matrix-core operands: MFMA s (0..3) of a chunk contracts the k
+// 128 c + 32 g + 8 s + j of lane group g, and the token operand is loaded at the
+// same k, so each chunk covers its 128 k exactly once.  Partial sums meet in LDS in
+// a fixed order, then the LoRA term is added in fp32.
+template <int NTT, int NW, bool kDQ>
+__global__ __launch_bounds__(NW * 64) void nf4_skinny_kernel(const __bf16* __restrict__ X, int64_t M, int64_t N,
+                                                          int64_t K, const uint8_t* __restrict__ packed,
+                                                          const float* __restrict__ absmax,
+                                                          const int8_t* __restrict__ qa,
+                                                          const float* __restrict__ dqs,
+                                                          const float* __restrict__ T, int ks,
+                                                          const float* __restrict__ B, int r, float alpha,
+                                                          float* __restrict__ Y, Nf4Tables tab) {
+  __shared__ float part[NW / 2][NTT * 256];
+  __shared__ float Ts[NTT * 16 * 64];   // the tokens' rows of X A^T, r <= 64
+  __shared__ float lvl[16];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, li = lane & 15, lg = lane >> 4;
+  if (tid < 16) lvl[tid] = tab.level[tid];
+  __syncthreads();
+  const int64_t n0 = static_cast<int64_t>(blockIdx.x) * 16;
+  const int64_t wr = (n0 + li < N) ? n0 + li : N - 1;
+  int64_t xr[NTT];
+#pragma unroll
+  for (int t = 0; t < NTT; ++t) xr[t] = (t * 16 + li < M) ? t * 16 + li : M - 1;
+  mfma_f4 acc[NTT];
+#pragma unroll
+  for (int t = 0; t < NTT; ++t) acc[t] = mfma_f4{0.f, 0.f, 0.f, 0.f};
+  // U chunks per round (w + NW i, i < U) with every load issued before the first
+  // product; chunks past the end and lane groups past K (a 64-wide tail chunk) load
+  // a valid address and are zeroed: scale 0 for the weight, a select for the tokens
+  constexpr int U = NTT <= 2 ? 2 : 1;
+  const int KC = static_cast<int>((K + 127) / 128);
+  for (int c0 = w; c0 < KC; c0 += NW * U) {
+    u32x4 code[U];
+    float sc[U];
+    u32x4 xv[U][NTT][4];
+#pragma unroll
+    for (int i = 0; i < U; ++i) {
+      const int c = c0 + NW * i < KC ? c0 + NW * i : KC - 1;
+      int64_t k = static_cast<int64_t>(c) * 128 + 32 * lg;
+      const bool live = c0 + NW * i < KC && k < K;
+      if (!live) k = K - 32;
+      const int64_t e = wr * K + k;
+      code[i] = *reinterpret_cast<const u32x4*>(packed + (e >> 1));
+      const int64_t b = e >> 6;
+      const float a = kDQ ? static_cast<float>(qa[b]) * dqs[b >> 8] : absmax[b];
+      sc[i] = live ? a : 0.f;
+#pragma unroll
+      for (int t = 0; t < NTT; ++t)
+#pragma unroll
+        for (int s4 = 0; s4 < 4; ++s4) {
+          const u32x4 v = *reinterpret_cast<const u32x4*>(X + xr[t] * K + k + 8 * s4);
+          xv[i][t][s4] = live ? v : u32x4{0u, 0u, 0u, 0u};
+        }
     }
+    __builtin_amdgcn_sched_barrier(0);   // every load of the round is in flight before the first wait
+#pragma unroll
+    for (int i = 0; i < U; ++i) {
+      bf16x8 wf[4];
+#pragma unroll
+      for (int s4 = 0; s4 < 4; ++s4)
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+          wf[s4][j] = static_cast<__bf16>(lvl[(code[i][s4] >> nib_shift16(j)) & 0xFu] * sc[i]);
+#pragma unroll
+      for (int s4 = 0; s4 < 4; ++s4)
+#pragma unroll
+        for (int t = 0; t < NTT; ++t)
+          acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, xv[i][t][s4]), wf[s4], acc[t],
+                                                           0, 0, 0);
+    }
+  }
+  if (w >= NW / 2) {
+#pragma unroll
+    for (int t = 0; t < NTT; ++t)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) part[w - NW / 2][(t * 4 + v) * 64 + lane] = acc[t][v];
+  }
+  __syncthreads();
+  if (w < NW / 2) {
+#pragma unroll
+    for (int t = 0; t < NTT; ++t)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) part[w][(t * 4 + v) * 64 + lane] += acc[t][v];
+  }
+  // X A^T of every token (the ks K-split partials summed in order)
+  if (T != nullptr)
+    for (int idx = tid; idx < M * r; idx += NW * 64) {
+      float t = 0.f;
+      for (int q = 0; q < ks; ++q) t += T[q * M * r + idx];
+      Ts[idx] = t;
+    }
+  __syncthreads();
+  // element (t, v, lane): token t*16 + 4 (lane/16) + v, feature n0 + lane%16
+  for (int e = tid; e < NTT * 256; e += NW * 64) {
+    const int ln = e & 63, v = (e >> 6) & 3, t = e >> 8;
+    const int64_t m = t * 16 + 4 * (ln >> 4) + v, n = n0 + (ln & 15);
+    if (m >= M || n >= N) continue;
+    float y = 0.f;
+#pragma unroll
+    for (int q = 0; q < NW / 2; ++q) y += part[q][e];
+    if (T != nullptr) {
+      float lora = 0.f;
+      for (int p = 0; p < r; ++p)
+        lora = fmaf(Ts[m * r + p], static_cast<float>(static_cast<__bf16>(B[n * r + p])), lora);
+      y = fmaf(alpha, lora, y);
+    }
+    Y[m * N + n] = y;
+  }
 }
 
 }  // namespace
 
+// X A^T is formed as up to kMaxSplits partial products over K ranges.
+constexpr int kMaxSplits = 8;
+
 size_t qlora_forward_workspace_bytes(int64_t n_tok, int r) {
-  return static_cast<size_t>((n_tok * r * 4 + 255) / 256 * 256);
+  return static_cast<size_t>((kMaxSplits * n_tok * r * 4 + 255) / 256 * 256);
 }
 
 hipError_t launch_qlora_forward(const void* X, int64_t n_tok, int64_t rows, int64_t cols, const uint8_t* packed,
@@ -191,23 +410,51 @@ hipError_t launch_qlora_forward(const void* X, int64_t n_tok, int64_t rows, int6
   if (n_tok == 0 || rows == 0) return hipSuccess;
   if (cols % 64 != 0 || cols == 0) return hipErrorInvalidValue;
   const __bf16* Xb = static_cast<const __bf16*>(X);
+  // enough workgroups to spread the reads of A and X (about 512), each with at
+  // least 16 of the 32-wide K steps
+  const int64_t tiles = (n_tok + 15) / 16;
+  const int64_t kt = cols / 32;
+  int ks = static_cast<int>((512 + tiles - 1) / tiles);
+  if (ks > kt / 16) ks = static_cast<int>(kt / 16);
+  if (ks > kMaxSplits) ks = kMaxSplits;
+  if (ks < 1) ks = 1;
   if (B != nullptr) {
-    const int64_t tiles = (n_tok + 15) / 16;
-    const dim3 grid(static_cast<unsigned>((tiles + 3) / 4));
-    if (r <= 16) LQ_LAUNCH("lora_down", lora_down_kernel<1>, grid, dim3(256), 0, s, Xb, n_tok, cols, A, r, Tws);
-    else if (r <= 32) LQ_LAUNCH("lora_down", lora_down_kernel<2>, grid, dim3(256), 0, s, Xb, n_tok, cols, A, r, Tws);
-    else if (r <= 48) LQ_LAUNCH("lora_down", lora_down_kernel<3>, grid, dim3(256), 0, s, Xb, n_tok, cols, A, r, Tws);
-    else LQ_LAUNCH("lora_down", lora_down_kernel<4>, grid, dim3(256), 0, s, Xb, n_tok, cols, A, r, Tws);
+    const dim3 grid(static_cast<unsigned>(tiles * ks));
+    if (r <= 16) LQ_LAUNCH("lora_down", lora_down_kernel<1>, grid, dim3(1024), 0, s, Xb, n_tok, cols, A, r, ks, Tws);
+    else if (r <= 32) LQ_LAUNCH("lora_down", lora_down_kernel<2>, grid, dim3(1024), 0, s, Xb, n_tok, cols, A, r, ks, Tws);
+    else if (r <= 48) LQ_LAUNCH("lora_down", lora_down_kernel<3>, grid, dim3(1024), 0, s, Xb, n_tok, cols, A, r, ks, Tws);
+    else LQ_LAUNCH("lora_down", lora_down_kernel<4>, grid, dim3(1024), 0, s, Xb, n_tok, cols, A, r, ks, Tws);
   }
-  const dim3 grid(static_cast<unsigned>((rows + kBN - 1) / kBN), static_cast<unsigned>((n_tok + kBM - 1) / kBM));
   const Nf4Tables& tab = nf_tables(bits);
   const float* T = B != nullptr ? Tws : nullptr;
+  if (n_tok <= 64) {
+    const dim3 grid(static_cast<unsigned>((rows + 15) / 16));
+    const int ntt = static_cast<int>((n_tok + 15) / 16);
+#define LQ_SKINNY(NTT, DQ)                                                                              \
+  LQ_LAUNCH("nf4_gemm_skinny", (nf4_skinny_kernel<NTT, (NTT <= 2 ? 16 : 8), DQ>), grid,                      \
+            dim3(NTT <= 2 ? 1024 : 512), 0, s, Xb, n_tok, rows, cols, packed, absmax, qa, dqs, T, ks, B, r, alpha, Y, \
+            tab)
+    const bool dq = qa != nullptr;
+    switch (ntt * 2 + (dq ? 1 : 0)) {
+      case 2: LQ_SKINNY(1, false); break;
+      case 3: LQ_SKINNY(1, true); break;
+      case 4: LQ_SKINNY(2, false); break;
+      case 5: LQ_SKINNY(2, true); break;
+      case 6: LQ_SKINNY(3, false); break;
+      case 7: LQ_SKINNY(3, true); break;
+      case 8: LQ_SKINNY(4, false); break;
+      default: LQ_SKINNY(4, true); break;
+    }
+#undef LQ_SKINNY
+    return hipGetLastError();
+  }
+  const dim3 grid(static_cast<unsigned>(((rows + kBN - 1) / kBN) * ((n_tok + kBM - 1) / kBM)));
   if (qa != nullptr)
     LQ_LAUNCH("nf4_gemm", nf4_gemm_kernel<true>, grid, dim3(kGemmThreads), 0, s, Xb, n_tok, rows, cols, packed, absmax,
-              qa, dqs, T, B, r, alpha, Y, tab);
+              qa, dqs, T, ks, B, r, alpha, Y, tab);
   else
     LQ_LAUNCH("nf4_gemm", nf4_gemm_kernel<false>, grid, dim3(kGemmThreads), 0, s, Xb, n_tok, rows, cols, packed,
-              absmax, qa, dqs, T, B, r, alpha, Y, tab);
+              absmax, qa, dqs, T, ks, B, r, alpha, Y, tab);
   return hipGetLastError();
 }
 

@@ -74,7 +74,8 @@ hipError_t launch_nf4_quantize(const void* W, loftq_dtype_t wdt, int64_t rows, i
 hipError_t launch_double_quant(const float* absmax, int64_t nblocks, int dqbs, int8_t* q, float* scale,
                                hipStream_t s);
 // QLoRA forward Y = X bf16(deq(Q))^T + alpha (X bf16(A)^T) bf16(B)^T (forward_kernels.hip);
-// Tws: n_tok x r fp32 scratch for X A^T (qlora_forward_workspace_bytes), unused without B.
+// Tws: up to 8 K-split partials of X A^T, n_tok x r fp32 each (qlora_forward_workspace_bytes);
+// unused without B.
 size_t qlora_forward_workspace_bytes(int64_t n_tok, int r);
 hipError_t launch_qlora_forward(const void* X, int64_t n_tok, int64_t rows, int64_t cols, const uint8_t* packed,
                                 const float* absmax, const int8_t* qa, const float* dqs, int bits, const float* B,

@@ -92,7 +92,10 @@ def check(Y, ref, tol):
     assert np.linalg.norm(err) <= 1e-5 * np.linalg.norm(ref) + 1e-30
 
 
-@pytest.mark.parametrize("n_tok,rows,cols", [(1, 64, 64), (5, 200, 320), (130, 257, 128), (300, 130, 640),
+# up to 64 tokens take the few-token kernel (1-4 token tiles, K chunks of 128 with a
+# 64-wide tail when cols % 128 = 64), more take the 128 x 128 tiled kernel
+@pytest.mark.parametrize("n_tok,rows,cols", [(1, 64, 64), (5, 200, 320), (17, 300, 256), (40, 96, 448),
+                                             (64, 130, 128), (65, 70, 192), (130, 257, 128), (300, 130, 640),
                                              (128, 128, 64), (257, 384, 192)])
 @pytest.mark.parametrize("adapter", [False, True])
 def test_forward_matches_oracle(lib, n_tok, rows, cols, adapter):
@@ -113,6 +116,17 @@ def test_forward_bits_and_double_quant(lib, bits, dq):
     Y = run_device(lib, c, rows, cols, bits, alpha, dq)
     ref = oracle.qlora_forward(c["X"], c["codes"], c["scale"], rows, cols, c["B"], c["A"], alpha, bits=bits)
     check(Y, ref, bound(c, rows, cols, bits, alpha, r))
+
+
+@pytest.mark.parametrize("n_tok,rows,cols", [(20, 100, 1600), (200, 90, 2048), (3, 40, 4096)])
+def test_forward_k_split_lora(lib, n_tok, rows, cols):
+    """X A^T formed as several partial products over K ranges (uneven ranges for
+    1600 columns: 50 steps of 32 in 3 ranges), summed by both GEMM kernels."""
+    r, alpha = 24, 0.75
+    c = make_case(n_tok, rows, cols, r, 4, True, n_tok + cols)
+    Y = run_device(lib, c, rows, cols, 4, alpha, True)
+    ref = oracle.qlora_forward(c["X"], c["codes"], c["scale"], rows, cols, c["B"], c["A"], alpha)
+    check(Y, ref, bound(c, rows, cols, 4, alpha, r))
 
 
 @pytest.mark.parametrize("r", [1, 3, 17, 33, 64])
