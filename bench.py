@@ -42,6 +42,9 @@ MEASURED_TRAFFIC = {
     "c2_4096x4096_bf16": {
         "gemm_nn": {"bytes": 77784775, "source": "gemm_kernels.hip", "sha256": "4322c77aea1b6c85"},
         "gemm_tn": {"bytes": 75687250, "source": "gemm_kernels.hip", "sha256": "4322c77aea1b6c85"},
+        # the QLoRA forward on this layer: 2048 tokens (tiled kernel), 16 tokens (few-token kernel)
+        "nf4_gemm": {"bytes": 147256072, "source": "forward_kernels.hip", "sha256": "042203e048f155b2"},
+        "nf4_gemm_skinny": {"bytes": 10406022, "source": "forward_kernels.hip", "sha256": "042203e048f155b2"},
     },
 }
 
@@ -52,7 +55,7 @@ MEASURED_TRAFFIC = {
 VALU_PEAK_GWIS = 256 * 4 * 2.4 / 4
 MEASURED_VALU = {
     "c2_4096x4096_bf16": {
-        "nf4_merge": {"valu": 5614232, "source": "quant_kernels.hip", "sha256": "654850248de71eaf"},
+        "nf4_merge": {"valu": 5614232, "source": "quant_kernels.hip", "sha256": "e0b79bad4ca7e0cd"},
     },
 }
 
@@ -339,7 +342,8 @@ def main():
             torch.cuda.synchronize()
             lq.profile_enable(False)
             fprof = lq.profile_collect()
-            gl, gms = fprof["nf4_gemm"] if "nf4_gemm" in fprof else fprof["nf4_gemm_skinny"]
+            gname = "nf4_gemm" if "nf4_gemm" in fprof else "nf4_gemm_skinny"
+            gl, gms = fprof[gname]
             g_us = 1e3 * gms / gl
             d_us = 1e3 * fprof["lora_down"][1] / fprof["lora_down"][0] if "lora_down" in fprof else 0.0
             flops = 2.0 * ntok * w.rows * w.cols
@@ -355,7 +359,9 @@ def main():
             ent["mfma"] = {"achieved": round(tf, 2), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                            "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4), "flops_per_launch": flops}
             ent["hbm"] = {"achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                          "frac": round(gbs / HBM_PEAK_GBS, 4), "bytes_per_launch": gbytes}
+                          "frac": round(gbs / HBM_PEAK_GBS, 4), "bytes_per_launch": gbytes,
+                          "traffic": measured_traffic(w.name, gname)}
+            ent["kernel"] = gname
             ent["bound"] = "mfma" if label == "prefill" else "hbm"
             fwd[label] = ent
             del X, Y, ws

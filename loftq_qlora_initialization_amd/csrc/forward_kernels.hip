@@ -31,7 +31,7 @@ typedef float mfma_f4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
-constexpr int kBM = 128, kBN = 128, kBK = 64, kLdsRow = kBK + 8;   // +8 bf16 per row against bank conflicts
+constexpr int kBM = 128, kBN = 128;
 constexpr int kGemmThreads = 256;
 
 __device__ __forceinline__ int nib_shift16(int e) { return 8 * ((e >> 1) & 3) + ((e & 1) ? 0 : 4); }
@@ -45,8 +45,8 @@ __device__ __forceinline__ int64_t xcd_tile(int64_t wg, int64_t total) {
   return wg < per * 8 ? (wg % 8) * per + wg / 8 : wg;
 }
 
-template <bool kDQ>
-__global__ __launch_bounds__(kGemmThreads, 2) void nf4_gemm_kernel(const __bf16* __restrict__ X, int64_t M, int64_t N,
+template <bool kDQ, int kBK>
+__global__ __launch_bounds__(kGemmThreads, kBK == 64 ? 2 : 3) void nf4_gemm_kernel(const __bf16* __restrict__ X, int64_t M, int64_t N,
                                                                 int64_t K, const uint8_t* __restrict__ packed,
                                                                 const float* __restrict__ absmax,
                                                                 const int8_t* __restrict__ qa,
@@ -54,8 +54,13 @@ __global__ __launch_bounds__(kGemmThreads, 2) void nf4_gemm_kernel(const __bf16*
                                                                 const float* __restrict__ T, int ks,
                                                                 const float* __restrict__ B, int r, float alpha,
                                                                 float* __restrict__ Y, Nf4Tables tab) {
-  __shared__ __align__(16) __bf16 Xs[2][kBM][kLdsRow];
-  __shared__ __align__(16) __bf16 Ws[2][kBN][kLdsRow];
+  constexpr int kLdsRow = kBK + 8;   // +8 bf16 per row against bank conflicts
+  constexpr int EPT = kBK / 2;         // elements of X and of W per thread and step
+  typedef uint32_t WcT __attribute__((ext_vector_type(EPT / 8)));
+  // double-buffered X and W tiles in one array (the epilogue reuses all of it)
+  __shared__ __align__(16) __bf16 lds[2 * (kBM + kBN) * kLdsRow];
+  __bf16(*Xs)[kBM][kLdsRow] = reinterpret_cast<__bf16(*)[kBM][kLdsRow]>(lds);
+  __bf16(*Ws)[kBN][kLdsRow] = reinterpret_cast<__bf16(*)[kBN][kLdsRow]>(lds + 2 * kBM * kLdsRow);
   __shared__ float lvl[16];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, wm = w & 1, wn = w >> 1;
   const int li = lane & 15, lg = lane >> 4;
@@ -63,41 +68,42 @@ __global__ __launch_bounds__(kGemmThreads, 2) void nf4_gemm_kernel(const __bf16*
   const int64_t ntn = (N + kBN - 1) / kBN, ntm = (M + kBM - 1) / kBM;
   const int64_t tile = xcd_tile(blockIdx.x, ntn * ntm);
   const int64_t m0 = (tile / ntn) * kBM, n0 = (tile % ntn) * kBN;
-  // this thread's share of one step: row `row` of the X and W tiles, 32 elements at column 32 half
+  // this thread's share of one step: row `row` of the X and W tiles, EPT elements at
+  // column EPT half (inside one 64-element scale block, since K % 64 = 0)
   const int row = tid >> 1, half = tid & 1;
   const int64_t xr = (m0 + row < M) ? m0 + row : M - 1;   // clamped rows: loaded, never stored
   const int64_t wr = (n0 + row < N) ? n0 + row : N - 1;
-  const u32x4* xsrc = reinterpret_cast<const u32x4*>(X + xr * K + 32 * half);
-  const int64_t we0 = wr * K + 32 * half;                  // element index of this thread's 32 weights
+  const u32x4* xsrc = reinterpret_cast<const u32x4*>(X + xr * K + EPT * half);
+  const int64_t we0 = wr * K + EPT * half;                 // element index of this thread's weights
   // one step's global data in registers; two of them keep the loads of step kt + 2
   // in flight while step kt computes and step kt + 1 goes from registers to LDS
   struct Stage {
-    u32x4 x[4];
-    u32x4 wc;
+    u32x4 x[EPT / 8];
+    WcT wc;
     float sc;
   };
   auto load = [&](Stage& st, int kt) __attribute__((always_inline)) {
     const int64_t k0 = static_cast<int64_t>(kt) * kBK;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) st.x[q] = xsrc[k0 / 8 + q];
+    for (int q = 0; q < EPT / 8; ++q) st.x[q] = xsrc[k0 / 8 + q];
     const int64_t e = we0 + k0;
-    st.wc = *reinterpret_cast<const u32x4*>(packed + (e >> 1));
+    st.wc = *reinterpret_cast<const WcT*>(packed + (e >> 1));
     const int64_t b = e >> 6;
     st.sc = kDQ ? static_cast<float>(qa[b]) * dqs[b >> 8] : absmax[b];
   };
   auto store = [&](const Stage& st, int buf) __attribute__((always_inline)) {
-    u32x4* xd = reinterpret_cast<u32x4*>(&Xs[buf][row][32 * half]);
+    u32x4* xd = reinterpret_cast<u32x4*>(&Xs[buf][row][EPT * half]);
 #pragma unroll
-    for (int q = 0; q < 4; ++q) xd[q] = st.x[q];
-    bf16x8 o[4];
+    for (int q = 0; q < EPT / 8; ++q) xd[q] = st.x[q];
+    bf16x8 o[EPT / 8];
 #pragma unroll
-    for (int e = 0; e < 32; ++e) {
+    for (int e = 0; e < EPT; ++e) {
       const uint32_t code = (st.wc[e >> 3] >> nib_shift16(e)) & 0xFu;
       o[e >> 3][e & 7] = static_cast<__bf16>(lvl[code] * st.sc);   // exact fp32 deq, then RNE to bf16
     }
-    bf16x8* wd = reinterpret_cast<bf16x8*>(&Ws[buf][row][32 * half]);
+    bf16x8* wd = reinterpret_cast<bf16x8*>(&Ws[buf][row][EPT * half]);
 #pragma unroll
-    for (int q = 0; q < 4; ++q) wd[q] = o[q];
+    for (int q = 0; q < EPT / 8; ++q) wd[q] = o[q];
   };
   mfma_f4 acc[4][4];
 #pragma unroll
@@ -146,10 +152,11 @@ __global__ __launch_bounds__(kGemmThreads, 2) void nf4_gemm_kernel(const __bf16*
   if (kt < KT) compute(0);   // odd step count: the last step sits in buffer 0
   // Epilogue.  Element v of tile (mt, nt) is token m = .. + 4 lg + v, feature n = .. + li.
   // The tile's rows of X A^T (the sum of the ks K-split partials, in split order) go to
-  // LDS, over the now idle X buffers.  The LoRA term T bf16(B)^T of a 16 x 16 tile is
+  // LDS, over the now idle tile buffers.  The LoRA term T bf16(B)^T of a 16 x 16 tile is
   // one fp32 MFMA (16x16x4) per 4 of r: lane L supplies T[m0 + L%16][p0 + L/16] and
   // bf16(B)[n0 + L%16][p0 + L/16].
-  float* Ts = reinterpret_cast<float*>(&Xs[0][0][0]);   // kBM x r fp32, r <= 64
+  static_assert(sizeof(lds) >= kBM * 64 * sizeof(float), "the T tile reuses the tile buffers");
+  float* Ts = reinterpret_cast<float*>(lds);   // kBM x r fp32, r <= 64
   if (T != nullptr) {
     __syncthreads();
     for (int idx = tid; idx < kBM * r; idx += kGemmThreads) {
@@ -299,11 +306,25 @@ __global__ __launch_bounds__(NW * 64) void nf4_skinny_kernel(const __bf16* __res
                                                           float* __restrict__ Y, Nf4Tables tab) {
   __shared__ float part[NW / 2][NTT * 256];
   __shared__ float Ts[NTT * 16 * 64];   // the tokens' rows of X A^T, r <= 64
+  __shared__ float Bs[16 * 64];         // bf16(B) of the workgroup's 16 features
   __shared__ float lvl[16];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, li = lane & 15, lg = lane >> 4;
-  if (tid < 16) lvl[tid] = tab.level[tid];
-  __syncthreads();
   const int64_t n0 = static_cast<int64_t>(blockIdx.x) * 16;
+  if (tid < 16) lvl[tid] = tab.level[tid];
+  // the epilogue's LoRA operands, staged first so their loads overlap the main loop:
+  // X A^T of every token (the ks K-split partials summed in order) and bf16(B)
+  if (T != nullptr) {
+    for (int idx = tid; idx < M * r; idx += NW * 64) {
+      float t = 0.f;
+      for (int q = 0; q < ks; ++q) t += T[q * M * r + idx];
+      Ts[idx] = t;
+    }
+    for (int idx = tid; idx < 16 * r; idx += NW * 64) {
+      const int64_t n = n0 + idx / r < N ? n0 + idx / r : N - 1;
+      Bs[idx] = static_cast<float>(static_cast<__bf16>(B[n * r + idx % r]));
+    }
+  }
+  __syncthreads();
   const int64_t wr = (n0 + li < N) ? n0 + li : N - 1;
   int64_t xr[NTT];
 #pragma unroll
@@ -369,13 +390,6 @@ __global__ __launch_bounds__(NW * 64) void nf4_skinny_kernel(const __bf16* __res
 #pragma unroll
       for (int v = 0; v < 4; ++v) part[w][(t * 4 + v) * 64 + lane] += acc[t][v];
   }
-  // X A^T of every token (the ks K-split partials summed in order)
-  if (T != nullptr)
-    for (int idx = tid; idx < M * r; idx += NW * 64) {
-      float t = 0.f;
-      for (int q = 0; q < ks; ++q) t += T[q * M * r + idx];
-      Ts[idx] = t;
-    }
   __syncthreads();
   // element (t, v, lane): token t*16 + 4 (lane/16) + v, feature n0 + lane%16
   for (int e = tid; e < NTT * 256; e += NW * 64) {
@@ -388,7 +402,7 @@ __global__ __launch_bounds__(NW * 64) void nf4_skinny_kernel(const __bf16* __res
     if (T != nullptr) {
       float lora = 0.f;
       for (int p = 0; p < r; ++p)
-        lora = fmaf(Ts[m * r + p], static_cast<float>(static_cast<__bf16>(B[n * r + p])), lora);
+        lora = fmaf(Ts[m * r + p], Bs[(ln & 15) * r + p], lora);
       y = fmaf(alpha, lora, y);
     }
     Y[m * N + n] = y;
@@ -399,6 +413,8 @@ __global__ __launch_bounds__(NW * 64) void nf4_skinny_kernel(const __bf16* __res
 
 // X A^T is formed as up to kMaxSplits partial products over K ranges.
 constexpr int kMaxSplits = 8;
+// K step of the tiled kernel (steps of 32 with three workgroups per CU measured slower)
+constexpr int kGemmBK = 64;
 
 size_t qlora_forward_workspace_bytes(int64_t n_tok, int r) {
   return static_cast<size_t>((kMaxSplits * n_tok * r * 4 + 255) / 256 * 256);
@@ -450,10 +466,10 @@ hipError_t launch_qlora_forward(const void* X, int64_t n_tok, int64_t rows, int6
   }
   const dim3 grid(static_cast<unsigned>(((rows + kBN - 1) / kBN) * ((n_tok + kBM - 1) / kBM)));
   if (qa != nullptr)
-    LQ_LAUNCH("nf4_gemm", nf4_gemm_kernel<true>, grid, dim3(kGemmThreads), 0, s, Xb, n_tok, rows, cols, packed, absmax,
+    LQ_LAUNCH("nf4_gemm", (nf4_gemm_kernel<true, kGemmBK>), grid, dim3(kGemmThreads), 0, s, Xb, n_tok, rows, cols, packed, absmax,
               qa, dqs, T, ks, B, r, alpha, Y, tab);
   else
-    LQ_LAUNCH("nf4_gemm", nf4_gemm_kernel<false>, grid, dim3(kGemmThreads), 0, s, Xb, n_tok, rows, cols, packed,
+    LQ_LAUNCH("nf4_gemm", (nf4_gemm_kernel<false, kGemmBK>), grid, dim3(kGemmThreads), 0, s, Xb, n_tok, rows, cols, packed,
               absmax, qa, dqs, T, ks, B, r, alpha, Y, tab);
   return hipGetLastError();
 }
