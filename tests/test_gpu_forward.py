@@ -118,6 +118,16 @@ def test_forward_bits_and_double_quant(lib, bits, dq):
     check(Y, ref, bound(c, rows, cols, bits, alpha, r))
 
 
+def test_forward_256_token_tiles_ragged(lib):
+    """Enough output tiles for 256-token workgroups (2 x 129 >= 256 CUs) with ragged
+    tokens (300 = 256 + 44) and features (16400 = 128 * 128 + 16)."""
+    n_tok, rows, cols, r, alpha = 300, 16400, 128, 8, 1.25
+    c = make_case(n_tok, rows, cols, r, 4, False, 2560)
+    Y = run_device(lib, c, rows, cols, 4, alpha, False)
+    ref = oracle.qlora_forward(c["X"], c["codes"], c["scale"], rows, cols, c["B"], c["A"], alpha)
+    check(Y, ref, bound(c, rows, cols, 4, alpha, r))
+
+
 @pytest.mark.parametrize("n_tok,rows,cols", [(20, 100, 1600), (200, 90, 2048), (3, 40, 4096)])
 def test_forward_k_split_lora(lib, n_tok, rows, cols):
     """X A^T formed as several partial products over K ranges (uneven ranges for
