@@ -33,7 +33,25 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kBN = 128, kBK = 64;   // tiled kernel: output features and K per step
 
-__device__ __forceinline__ int nib_shift16(int e) { return 8 * ((e >> 1) & 3) + ((e & 1) ? 0 : 4); }
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// Byte-pair decode: a byte holds two codes (element 2j in the high nibble), and all
+// codes a thread decodes in one go share one block scale, so a 256-entry LDS table
+// of level pairs (c[b >> 4], c[b & 15]) serves two elements per lookup.  Each value
+// is still fl32(c[code] a') rounded to bf16 (nearest even), as the dequantization.
+__device__ __forceinline__ void fill_level_pairs(f32x2* lvl2, const Nf4Tables& tab, int tid, int nthreads) {
+  for (int i = tid; i < 256; i += nthreads) lvl2[i] = f32x2{tab.level[i >> 4], tab.level[i & 15]};
+}
+__device__ __forceinline__ bf16x8 decode8(const f32x2* lvl2, uint32_t word, float sc) {
+  bf16x8 o;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const f32x2 c = lvl2[(word >> (8 * j)) & 0xFFu];
+    o[2 * j] = static_cast<__bf16>(c.x * sc);
+    o[2 * j + 1] = static_cast<__bf16>(c.y * sc);
+  }
+  return o;
+}
 
 // Workgroups are dealt to the 8 XCDs round-robin by id.  Tile t = xcd * per + slot
 // gives each XCD a contiguous run of tiles (token tile outer, feature tile inner),
@@ -63,10 +81,10 @@ __global__ __launch_bounds__(2 * kBM, kBM == 128 ? 2 : 1) void nf4_gemm_kernel(c
   __shared__ __align__(16) __bf16 lds[2 * (kBM + kBN) * kLdsRow];
   __bf16(*Xs)[kBM][kLdsRow] = reinterpret_cast<__bf16(*)[kBM][kLdsRow]>(lds);
   __bf16(*Ws)[kBN][kLdsRow] = reinterpret_cast<__bf16(*)[kBN][kLdsRow]>(lds + 2 * kBM * kLdsRow);
-  __shared__ float lvl[16];
+  __shared__ f32x2 lvl2[256];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, wm = w % kWM, wn = w / kWM;
   const int li = lane & 15, lg = lane >> 4;
-  if (tid < 16) lvl[tid] = tab.level[tid];
+  fill_level_pairs(lvl2, tab, tid, kThreads);
   const int64_t ntn = (N + kBN - 1) / kBN, ntm = (M + kBM - 1) / kBM;
   const int64_t tile = xcd_tile(blockIdx.x, ntn * ntm);
   const int64_t m0 = (tile / ntn) * kBM, n0 = (tile % ntn) * kBN;
@@ -98,15 +116,9 @@ __global__ __launch_bounds__(2 * kBM, kBM == 128 ? 2 : 1) void nf4_gemm_kernel(c
     u32x4* xd = reinterpret_cast<u32x4*>(&Xs[buf][xrow][xcol]);
 #pragma unroll
     for (int q = 0; q < XPT / 8; ++q) xd[q] = st.x[q];
-    bf16x8 o[WPT / 8];
-#pragma unroll
-    for (int e = 0; e < WPT; ++e) {
-      const uint32_t code = (st.wc[e >> 3] >> nib_shift16(e)) & 0xFu;
-      o[e >> 3][e & 7] = static_cast<__bf16>(lvl[code] * st.sc);   // exact fp32 deq, then RNE to bf16
-    }
     bf16x8* wd = reinterpret_cast<bf16x8*>(&Ws[buf][wrow][wcol]);
 #pragma unroll
-    for (int q = 0; q < WPT / 8; ++q) wd[q] = o[q];
+    for (int q = 0; q < WPT / 8; ++q) wd[q] = decode8(lvl2, st.wc[q], st.sc);
   };
   mfma_f4 acc[4][4];
 #pragma unroll
@@ -132,7 +144,7 @@ __global__ __launch_bounds__(2 * kBM, kBM == 128 ? 2 : 1) void nf4_gemm_kernel(c
   };
   const int KT = static_cast<int>(K / kBK);
   Stage s0, s1;
-  __syncthreads();   // lvl
+  __syncthreads();   // level pairs
   load(s0, 0);
   load(s1, KT > 1 ? 1 : 0);
   store(s0, 0);
@@ -310,10 +322,10 @@ __global__ __launch_bounds__(NW * 64) void nf4_skinny_kernel(const __bf16* __res
   __shared__ float part[NW / 2][NTT * 256];
   __shared__ float Ts[NTT * 16 * 64];   // the tokens' rows of X A^T, r <= 64
   __shared__ float Bs[16 * 64];         // bf16(B) of the workgroup's 16 features
-  __shared__ float lvl[16];
+  __shared__ f32x2 lvl2[256];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, li = lane & 15, lg = lane >> 4;
   const int64_t n0 = static_cast<int64_t>(blockIdx.x) * 16;
-  if (tid < 16) lvl[tid] = tab.level[tid];
+  fill_level_pairs(lvl2, tab, tid, NW * 64);
   // the epilogue's LoRA operands, staged first so their loads overlap the main loop:
   // X A^T of every token (the ks K-split partials summed in order) and bf16(B)
   if (T != nullptr) {
@@ -368,10 +380,7 @@ __global__ __launch_bounds__(NW * 64) void nf4_skinny_kernel(const __bf16* __res
     for (int i = 0; i < U; ++i) {
       bf16x8 wf[4];
 #pragma unroll
-      for (int s4 = 0; s4 < 4; ++s4)
-#pragma unroll
-        for (int j = 0; j < 8; ++j)
-          wf[s4][j] = static_cast<__bf16>(lvl[(code[i][s4] >> nib_shift16(j)) & 0xFu] * sc[i]);
+      for (int s4 = 0; s4 < 4; ++s4) wf[s4] = decode8(lvl2, code[i][s4], sc[i]);
 #pragma unroll
       for (int s4 = 0; s4 < 4; ++s4)
 #pragma unroll
