@@ -159,7 +159,8 @@ loftq_status_t loftq_nf4_unmerge(const uint8_t* packed, const float* absmax, con
  *   ws                 [device] loftq_qlora_forward_workspace_bytes(n_tok, r) bytes (partial
  *                      products X A^T over K ranges)
  * All device pointers 16-byte aligned.  n_tok = 0 or rows = 0 writes nothing.
- * UNSUPPORTED: cols % 64 != 0, r > 64, more than 65535 * 128 tokens. */
+ * UNSUPPORTED: cols % 64 != 0, r > 64, or a shape whose launches would exceed 2^32 work-items
+ * (about 8.4 million tokens, or 2^26 output features with at most 64 tokens). */
 loftq_status_t loftq_qlora_forward(const void* X, int64_t n_tok, int64_t rows, int64_t cols,
                                    const uint8_t* packed, const float* absmax, const int8_t* qabsmax,
                                    const float* dq_scale, int32_t bits, const float* B, const float* A,

@@ -434,22 +434,59 @@ size_t qlora_forward_workspace_bytes(int64_t n_tok, int r) {
   return static_cast<size_t>((kMaxSplits * n_tok * r * 4 + 255) / 256 * 256);
 }
 
+// Launch shapes of one forward call (shared by the launcher and the argument check).
+struct ForwardPlan {
+  int64_t tiles;     // 16-token tiles of LoRA down
+  int ks;            // K ranges of LoRA down
+  bool skinny;       // <= 64 tokens: few-token kernel
+  int ntt;           // its 16-token tiles
+  int bm;            // tiled kernel: tokens per workgroup
+  int64_t grid_down, grid_gemm;
+  int block_gemm;
+};
+
+ForwardPlan plan_forward(int64_t n_tok, int64_t rows, int64_t cols) {
+  ForwardPlan p{};
+  // enough workgroups to spread the reads of A and X (about 512), each with at
+  // least 16 of the 32-wide K steps
+  p.tiles = (n_tok + 15) / 16;
+  const int64_t kt = cols / 32;
+  int64_t ks = (512 + p.tiles - 1) / p.tiles;
+  if (ks > kt / 16) ks = kt / 16;
+  if (ks > kMaxSplits) ks = kMaxSplits;
+  p.ks = ks < 1 ? 1 : static_cast<int>(ks);
+  p.grid_down = p.tiles * p.ks;
+  p.skinny = n_tok <= 64;
+  p.ntt = static_cast<int>((n_tok + 15) / 16);
+  if (p.skinny) {
+    p.grid_gemm = (rows + 15) / 16;
+    p.block_gemm = p.ntt <= 2 ? 1024 : 512;
+  } else {
+    const int64_t ntn = (rows + kBN - 1) / kBN;
+    p.bm = ntn * ((n_tok + 255) / 256) >= kCUs ? 256 : 128;
+    p.grid_gemm = ntn * ((n_tok + p.bm - 1) / p.bm);
+    p.block_gemm = 2 * p.bm;
+  }
+  return p;
+}
+
+bool qlora_forward_shape_ok(int64_t n_tok, int64_t rows, int64_t cols) {
+  if (n_tok <= 0 || rows <= 0) return true;   // nothing is launched
+  const ForwardPlan p = plan_forward(n_tok, rows, cols);
+  const int64_t limit = int64_t(1) << 32;        // work-items of one launch
+  return p.grid_down * 1024 < limit && p.grid_gemm * p.block_gemm < limit;
+}
+
 hipError_t launch_qlora_forward(const void* X, int64_t n_tok, int64_t rows, int64_t cols, const uint8_t* packed,
                                 const float* absmax, const int8_t* qa, const float* dqs, int bits, const float* B,
                                 const float* A, int r, float alpha, float* Y, float* Tws, hipStream_t s) {
   if (n_tok == 0 || rows == 0) return hipSuccess;
-  if (cols % 64 != 0 || cols == 0) return hipErrorInvalidValue;
+  if (cols % 64 != 0 || cols == 0 || !qlora_forward_shape_ok(n_tok, rows, cols)) return hipErrorInvalidValue;
   const __bf16* Xb = static_cast<const __bf16*>(X);
-  // enough workgroups to spread the reads of A and X (about 512), each with at
-  // least 16 of the 32-wide K steps
-  const int64_t tiles = (n_tok + 15) / 16;
-  const int64_t kt = cols / 32;
-  int ks = static_cast<int>((512 + tiles - 1) / tiles);
-  if (ks > kt / 16) ks = static_cast<int>(kt / 16);
-  if (ks > kMaxSplits) ks = kMaxSplits;
-  if (ks < 1) ks = 1;
+  const ForwardPlan pl = plan_forward(n_tok, rows, cols);
+  const int ks = pl.ks;
   if (B != nullptr) {
-    const dim3 grid(static_cast<unsigned>(tiles * ks));
+    const dim3 grid(static_cast<unsigned>(pl.grid_down));
     if (r <= 16) LQ_LAUNCH("lora_down", lora_down_kernel<1>, grid, dim3(1024), 0, s, Xb, n_tok, cols, A, r, ks, Tws);
     else if (r <= 32) LQ_LAUNCH("lora_down", lora_down_kernel<2>, grid, dim3(1024), 0, s, Xb, n_tok, cols, A, r, ks, Tws);
     else if (r <= 48) LQ_LAUNCH("lora_down", lora_down_kernel<3>, grid, dim3(1024), 0, s, Xb, n_tok, cols, A, r, ks, Tws);
@@ -457,15 +494,14 @@ hipError_t launch_qlora_forward(const void* X, int64_t n_tok, int64_t rows, int6
   }
   const Nf4Tables& tab = nf_tables(bits);
   const float* T = B != nullptr ? Tws : nullptr;
-  if (n_tok <= 64) {
-    const dim3 grid(static_cast<unsigned>((rows + 15) / 16));
-    const int ntt = static_cast<int>((n_tok + 15) / 16);
+  const dim3 grid(static_cast<unsigned>(pl.grid_gemm));
+  const bool dq = qa != nullptr;
+  if (pl.skinny) {
 #define LQ_SKINNY(NTT, DQ)                                                                              \
   LQ_LAUNCH("nf4_gemm_skinny", (nf4_skinny_kernel<NTT, (NTT <= 2 ? 16 : 8), DQ>), grid,                      \
             dim3(NTT <= 2 ? 1024 : 512), 0, s, Xb, n_tok, rows, cols, packed, absmax, qa, dqs, T, ks, B, r, alpha, Y, \
             tab)
-    const bool dq = qa != nullptr;
-    switch (ntt * 2 + (dq ? 1 : 0)) {
+    switch (pl.ntt * 2 + (dq ? 1 : 0)) {
       case 2: LQ_SKINNY(1, false); break;
       case 3: LQ_SKINNY(1, true); break;
       case 4: LQ_SKINNY(2, false); break;
@@ -478,18 +514,14 @@ hipError_t launch_qlora_forward(const void* X, int64_t n_tok, int64_t rows, int6
 #undef LQ_SKINNY
     return hipGetLastError();
   }
-  const int64_t ntn = (rows + kBN - 1) / kBN;
-  const bool big = ntn * ((n_tok + 255) / 256) >= kCUs;
-  const int bm = big ? 256 : 128;
-  const dim3 grid(static_cast<unsigned>(ntn * ((n_tok + bm - 1) / bm)));
 #define LQ_TILED(BM, DQ)                                                                                        \
   LQ_LAUNCH("nf4_gemm", (nf4_gemm_kernel<DQ, BM>), grid, dim3(2 * BM), 0, s, Xb, n_tok, rows, cols, packed, absmax, \
             qa, dqs, T, ks, B, r, alpha, Y, tab)
-  if (qa != nullptr) {
-    if (big) LQ_TILED(256, true);
+  if (dq) {
+    if (pl.bm == 256) LQ_TILED(256, true);
     else LQ_TILED(128, true);
   } else {
-    if (big) LQ_TILED(256, false);
+    if (pl.bm == 256) LQ_TILED(256, false);
     else LQ_TILED(128, false);
   }
 #undef LQ_TILED

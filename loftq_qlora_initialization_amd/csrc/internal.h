@@ -77,6 +77,8 @@ hipError_t launch_double_quant(const float* absmax, int64_t nblocks, int dqbs, i
 // Tws: up to 8 K-split partials of X A^T, n_tok x r fp32 each (qlora_forward_workspace_bytes);
 // unused without B.
 size_t qlora_forward_workspace_bytes(int64_t n_tok, int r);
+// false when one of the call's launches would exceed 2^32 work-items
+bool qlora_forward_shape_ok(int64_t n_tok, int64_t rows, int64_t cols);
 hipError_t launch_qlora_forward(const void* X, int64_t n_tok, int64_t rows, int64_t cols, const uint8_t* packed,
                                 const float* absmax, const int8_t* qa, const float* dqs, int bits, const float* B,
                                 const float* A, int r, float alpha, float* Y, float* Tws, hipStream_t s);
