@@ -217,10 +217,10 @@ __global__ __launch_bounds__(2 * kBM, kBM == 128 ? 2 : 1) void nf4_gemm_kernel(c
 
 // Partial products P_q = X bf16(A)^T over the q-th of ks K ranges, for one 16-token
 // tile per workgroup (workgroup = tile * ks + q); P_q lands at T + q n r.  The 16
-// waves split the range (wave w takes U consecutive 32-wide steps from 16 U w on,
-// then every 16 U steps) and their partial 16 x r products are summed through LDS
-// in a fixed order.  Consumers add the ks partials in order q = 0, 1, ...
-template <int NT>
+// waves split the range (wave w takes its 32-wide steps w, w + 16, ...) and their
+// partial 16 x r products are summed through LDS in a fixed order.  Consumers add
+// the ks partials in order q = 0, 1, ...
+template <int NT, int U>
 __global__ __launch_bounds__(1024) void lora_down_kernel(const __bf16* __restrict__ X, int64_t M, int64_t K,
                                                          const float* __restrict__ A, int r, int ks,
                                                          float* __restrict__ T) {
@@ -233,18 +233,18 @@ __global__ __launch_bounds__(1024) void lora_down_kernel(const __bf16* __restric
   mfma_f4 acc[NT];
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) acc[nt] = mfma_f4{0.f, 0.f, 0.f, 0.f};
-  // each wave takes U consecutive 32-wide steps per round and issues all their loads
+  // wave w takes the steps w, w + 16, ... of the range, U of them per round (U covers
+  // a wave's share of the range when registers allow) with all their loads issued
   // before the first product (rows p >= r load row r - 1 and are zeroed)
-  constexpr int U = NT == 1 ? 8 : (NT == 2 ? 4 : 2);
   const int KT = static_cast<int>(K / 32);
   const int per = (KT + ks - 1) / ks;
   const int k_begin = q * per, k_end = k_begin + per < KT ? k_begin + per : KT;
-  for (int base = k_begin + w * U; base < k_end; base += 16 * U) {
+  for (int base = k_begin + w; base < k_end; base += 16 * U) {
     bf16x8 a[U];
     float4 ua[U][NT], ub[U][NT];
 #pragma unroll
     for (int i = 0; i < U; ++i) {
-      const int kt = base + i < KT ? base + i : KT - 1;
+      const int kt = base + 16 * i < KT ? base + 16 * i : KT - 1;
       const int64_t k0 = static_cast<int64_t>(kt) * 32 + 8 * lg;
       a[i] = *reinterpret_cast<const bf16x8*>(X + xr * K + k0);
 #pragma unroll
@@ -259,7 +259,7 @@ __global__ __launch_bounds__(1024) void lora_down_kernel(const __bf16* __restric
 #pragma unroll
     for (int i = 0; i < U; ++i) {
       // steps past the range (clamped loads) and rows p >= r contribute exact zeros
-      const bool live = base + i < k_end;
+      const bool live = base + 16 * i < k_end;
       const bf16x8 ai = live ? a[i] : bf16x8{};
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
@@ -487,10 +487,29 @@ hipError_t launch_qlora_forward(const void* X, int64_t n_tok, int64_t rows, int6
   const int ks = pl.ks;
   if (B != nullptr) {
     const dim3 grid(static_cast<unsigned>(pl.grid_down));
-    if (r <= 16) LQ_LAUNCH("lora_down", lora_down_kernel<1>, grid, dim3(1024), 0, s, Xb, n_tok, cols, A, r, ks, Tws);
-    else if (r <= 32) LQ_LAUNCH("lora_down", lora_down_kernel<2>, grid, dim3(1024), 0, s, Xb, n_tok, cols, A, r, ks, Tws);
-    else if (r <= 48) LQ_LAUNCH("lora_down", lora_down_kernel<3>, grid, dim3(1024), 0, s, Xb, n_tok, cols, A, r, ks, Tws);
-    else LQ_LAUNCH("lora_down", lora_down_kernel<4>, grid, dim3(1024), 0, s, Xb, n_tok, cols, A, r, ks, Tws);
+    // steps per wave in one K range, rounded up to a power of two, capped by registers
+    const int64_t per = ((cols / 32) + ks - 1) / ks;
+    const int64_t spw = (per + 15) / 16;
+    const int nt = (r + 15) / 16;
+    const int umax = nt == 1 ? 8 : (nt == 2 ? 4 : 2);
+    int u = spw <= 1 ? 1 : spw <= 2 ? 2 : spw <= 4 ? 4 : 8;
+    if (u > umax) u = umax;
+#define LQ_DOWN(NT, U) \
+  LQ_LAUNCH("lora_down", (lora_down_kernel<NT, U>), grid, dim3(1024), 0, s, Xb, n_tok, cols, A, r, ks, Tws)
+    switch (nt * 16 + u) {
+      case 16 + 1: LQ_DOWN(1, 1); break;
+      case 16 + 2: LQ_DOWN(1, 2); break;
+      case 16 + 4: LQ_DOWN(1, 4); break;
+      case 16 + 8: LQ_DOWN(1, 8); break;
+      case 32 + 1: LQ_DOWN(2, 1); break;
+      case 32 + 2: LQ_DOWN(2, 2); break;
+      case 32 + 4: LQ_DOWN(2, 4); break;
+      case 48 + 1: LQ_DOWN(3, 1); break;
+      case 48 + 2: LQ_DOWN(3, 2); break;
+      case 64 + 1: LQ_DOWN(4, 1); break;
+      default: LQ_DOWN(4, 2); break;
+    }
+#undef LQ_DOWN
   }
   const Nf4Tables& tab = nf_tables(bits);
   const float* T = B != nullptr ? Tws : nullptr;

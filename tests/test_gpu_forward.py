@@ -139,6 +139,17 @@ def test_forward_k_split_lora(lib, n_tok, rows, cols):
     check(Y, ref, bound(c, rows, cols, 4, alpha, r))
 
 
+@pytest.mark.parametrize("cols,r", [(2048, 16), (4096, 16), (2048, 40)])
+def test_forward_lora_down_rounds(lib, cols, r):
+    """Over 8192 tokens LoRA down keeps one K range, so each wave runs 4 or 8 steps per
+    round (2 where a wider rank leaves fewer registers)."""
+    n_tok, rows, alpha = 8200, 32, 1.0
+    c = make_case(n_tok, rows, cols, r, 4, False, cols + r)
+    Y = run_device(lib, c, rows, cols, 4, alpha, False)
+    ref = oracle.qlora_forward(c["X"], c["codes"], c["scale"], rows, cols, c["B"], c["A"], alpha)
+    check(Y, ref, bound(c, rows, cols, 4, alpha, r))
+
+
 @pytest.mark.parametrize("r", [1, 3, 17, 33, 64])
 def test_forward_ranks(lib, r):
     """Every LoRA-down width (1-4 column tiles) and ranks that are not multiples of 4."""
