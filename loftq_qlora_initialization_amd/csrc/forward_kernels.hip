@@ -62,6 +62,60 @@ __device__ __forceinline__ int64_t xcd_tile(int64_t wg, int64_t total) {
   return wg < per * 8 ? (wg % 8) * per + wg / 8 : wg;
 }
 
+// Epilogue of the tiled kernels (kBM token rows, kThreads threads, waves of 64 x 64).
+// Element v of tile (mt, nt) is token m = .. + 4 lg + v, feature n = .. + li.  The
+// tile's rows of X A^T (the sum of the ks K-split partials, in split order) go to LDS
+// (Ts, kBM x r fp32 over the idle tile buffers).  The LoRA term T bf16(B)^T of a 16 x 16
+// tile is one fp32 MFMA (16x16x4) per 4 of r: lane L supplies T[m0 + L%16][p0 + L/16]
+// and bf16(B)[n0 + L%16][p0 + L/16].
+template <int kBM, int kThreads>
+__device__ __forceinline__ void tile_epilogue(float* Ts, mfma_f4 (&acc)[4][4], int tid, int wm, int wn, int li,
+                                              int lg, int64_t m0, int64_t n0, int64_t M, int64_t N,
+                                              const float* __restrict__ T, int ks, const float* __restrict__ B,
+                                              int r, float alpha, float* __restrict__ Y) {
+  if (T != nullptr) {
+    __syncthreads();
+    for (int idx = tid; idx < kBM * r; idx += kThreads) {
+      const int i = idx / r, p = idx - i * r;
+      float t = 0.f;
+      if (m0 + i < M)
+        for (int q = 0; q < ks; ++q) t += T[(q * M + m0 + i) * r + p];
+      Ts[idx] = t;
+    }
+    __syncthreads();
+  }
+  const int64_t mw = m0 + wm * 64, nw = n0 + wn * 64;
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt) {
+    mfma_f4 lora[4];
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) lora[nt] = mfma_f4{0.f, 0.f, 0.f, 0.f};
+    if (T != nullptr) {
+      const int tl = wm * 64 + mt * 16 + li;
+      for (int p0 = 0; p0 < r; p0 += 4) {
+        const int p = p0 + lg;
+        const float tv = p < r ? Ts[tl * r + p] : 0.f;
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt) {
+          const int64_t bn = nw + nt * 16 + li;
+          const float bv = (bn < N && p < r) ? static_cast<float>(static_cast<__bf16>(B[bn * r + p])) : 0.f;
+          lora[nt] = __builtin_amdgcn_mfma_f32_16x16x4f32(tv, bv, lora[nt], 0, 0, 0);
+        }
+      }
+    }
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int64_t m = mw + mt * 16 + 4 * lg + v;
+      if (m >= M) continue;
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) {
+        const int64_t n = nw + nt * 16 + li;
+        if (n < N) Y[m * N + n] = fmaf(alpha, lora[nt][v], acc[mt][nt][v]);
+      }
+    }
+  }
+}
+
 template <bool kDQ, int kBM>
 __global__ __launch_bounds__(2 * kBM, kBM == 128 ? 2 : 1) void nf4_gemm_kernel(const __bf16* __restrict__ X, int64_t M, int64_t N,
                                                        int64_t K, const uint8_t* __restrict__ packed,
@@ -165,54 +219,9 @@ __global__ __launch_bounds__(2 * kBM, kBM == 128 ? 2 : 1) void nf4_gemm_kernel(c
     __syncthreads();
   }
   if (kt < KT) compute(0);   // odd step count: the last step sits in buffer 0
-  // Epilogue.  Element v of tile (mt, nt) is token m = .. + 4 lg + v, feature n = .. + li.
-  // The tile's rows of X A^T (the sum of the ks K-split partials, in split order) go to
-  // LDS, over the now idle tile buffers.  The LoRA term T bf16(B)^T of a 16 x 16 tile is
-  // one fp32 MFMA (16x16x4) per 4 of r: lane L supplies T[m0 + L%16][p0 + L/16] and
-  // bf16(B)[n0 + L%16][p0 + L/16].
   static_assert(sizeof(lds) >= kBM * 64 * sizeof(float), "the T tile reuses the tile buffers");
-  float* Ts = reinterpret_cast<float*>(lds);   // kBM x r fp32, r <= 64
-  if (T != nullptr) {
-    __syncthreads();
-    for (int idx = tid; idx < kBM * r; idx += kThreads) {
-      const int i = idx / r, p = idx - i * r;
-      float t = 0.f;
-      if (m0 + i < M)
-        for (int q = 0; q < ks; ++q) t += T[(q * M + m0 + i) * r + p];
-      Ts[idx] = t;
-    }
-    __syncthreads();
-  }
-  const int64_t mw = m0 + wm * 64, nw = n0 + wn * 64;
-#pragma unroll
-  for (int mt = 0; mt < 4; ++mt) {
-    mfma_f4 lora[4];
-#pragma unroll
-    for (int nt = 0; nt < 4; ++nt) lora[nt] = mfma_f4{0.f, 0.f, 0.f, 0.f};
-    if (T != nullptr) {
-      const int tl = wm * 64 + mt * 16 + li;
-      for (int p0 = 0; p0 < r; p0 += 4) {
-        const int p = p0 + lg;
-        const float tv = p < r ? Ts[tl * r + p] : 0.f;
-#pragma unroll
-        for (int nt = 0; nt < 4; ++nt) {
-          const int64_t bn = nw + nt * 16 + li;
-          const float bv = (bn < N && p < r) ? static_cast<float>(static_cast<__bf16>(B[bn * r + p])) : 0.f;
-          lora[nt] = __builtin_amdgcn_mfma_f32_16x16x4f32(tv, bv, lora[nt], 0, 0, 0);
-        }
-      }
-    }
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int64_t m = mw + mt * 16 + 4 * lg + v;
-      if (m >= M) continue;
-#pragma unroll
-      for (int nt = 0; nt < 4; ++nt) {
-        const int64_t n = nw + nt * 16 + li;
-        if (n < N) Y[m * N + n] = fmaf(alpha, lora[nt][v], acc[mt][nt][v]);
-      }
-    }
-  }
+  tile_epilogue<kBM, kThreads>(reinterpret_cast<float*>(lds), acc, tid, wm, wn, li, lg, m0, n0, M, N, T, ks, B, r,
+                               alpha, Y);
 }
 
 // Partial products P_q = X bf16(A)^T over the q-th of ks K ranges, for one 16-token
@@ -310,7 +319,7 @@ __global__ __launch_bounds__(1024) void lora_down_kernel(const __bf16* __restric
 // 128 c + 32 g + 8 s + j of lane group g, and the token operand is loaded at the
 // same k, so each chunk covers its 128 k exactly once.  Partial sums meet in LDS in
 // a fixed order, then the LoRA term is added in fp32.
-template <int NTT, int NW, bool kDQ>
+template <int NTT, int NW, int U, bool kDQ>
 __global__ __launch_bounds__(NW * 64) void nf4_skinny_kernel(const __bf16* __restrict__ X, int64_t M, int64_t N,
                                                           int64_t K, const uint8_t* __restrict__ packed,
                                                           const float* __restrict__ absmax,
@@ -350,7 +359,6 @@ __global__ __launch_bounds__(NW * 64) void nf4_skinny_kernel(const __bf16* __res
   // U chunks per round (w + NW i, i < U) with every load issued before the first
   // product; chunks past the end and lane groups past K (a 64-wide tail chunk) load
   // a valid address and are zeroed: scale 0 for the weight, a select for the tokens
-  constexpr int U = NTT <= 2 ? 2 : 1;
   const int KC = static_cast<int>((K + 127) / 128);
   for (int c0 = w; c0 < KC; c0 += NW * U) {
     u32x4 code[U];
@@ -516,8 +524,10 @@ hipError_t launch_qlora_forward(const void* X, int64_t n_tok, int64_t rows, int6
   const dim3 grid(static_cast<unsigned>(pl.grid_gemm));
   const bool dq = qa != nullptr;
   if (pl.skinny) {
-#define LQ_SKINNY(NTT, DQ)                                                                              \
-  LQ_LAUNCH("nf4_gemm_skinny", (nf4_skinny_kernel<NTT, (NTT <= 2 ? 16 : 8), DQ>), grid,                      \
+// 16 waves with two chunks each per round (1-2 token tiles; 8 waves x 4 chunks and 4 x 4
+// measured slower), 8 waves with one chunk for 3-4 token tiles (registers)
+#define LQ_SKINNY(NTT, DQ)                                                                                    \
+  LQ_LAUNCH("nf4_gemm_skinny", (nf4_skinny_kernel<NTT, (NTT <= 2 ? 16 : 8), (NTT <= 2 ? 2 : 1), DQ>), grid,      \
             dim3(NTT <= 2 ? 1024 : 512), 0, s, Xb, n_tok, rows, cols, packed, absmax, qa, dqs, T, ks, B, r, alpha, Y, \
             tab)
     switch (pl.ntt * 2 + (dq ? 1 : 0)) {
