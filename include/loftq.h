@@ -9,7 +9,10 @@
  * 实现高效大语言模型微调", §2.2-2.3).  Q is QLoRA's 4-bit NormalFloat with
  * blockwise absmax scaling and optional double quantization of the absmax
  * constants ("QLoRA论文概述", NF4 and double-quantization bullets; PEFT guide
- * "量化", BitsAndBytesConfig bullets).
+ * "量化", BitsAndBytesConfig bullets).  Around the initialisation the library
+ * also merges an adapter into the quantized weights and takes it out again
+ * (PEFT guide "量化"), and runs the QLoRA forward of an adapted layer on the
+ * bf16 matrix cores ("参数高效微调：LoRA、Adapter 与 QLoRA", §2.2 and §4.3).
  *
  * Conventions for every call:
  *   - Matrices are row-major.  W is rows x cols (d x k); B is rows x r and A is

@@ -7,8 +7,10 @@ built library raises ImportError: there is no CPU fallback.
 
 The functions carry the C entry points' names (see include/loftq.h):
     loftq_nf4_quantize, loftq_double_quant, loftq_nf4_dequantize,
-    loftq_lowrank_svd, loftq_init
-and return freshly allocated torch tensors on the input's device.
+    loftq_nf4_merge, loftq_nf4_unmerge, loftq_lowrank_svd, loftq_init,
+    loftq_qlora_forward
+and return freshly allocated torch tensors on the input's device (or fill the
+caller's ``out`` / ``buffers`` where those are given).
 """
 from __future__ import annotations
 
