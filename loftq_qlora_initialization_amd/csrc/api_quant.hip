@@ -176,7 +176,7 @@ loftq_status_t loftq_qlora_forward(const void* X, int64_t n_tok, int64_t rows, i
   if (!std::isfinite(alpha)) return LOFTQ_ERR_INVALID_ARG;
   if (n_tok == 0 || rows == 0) return LOFTQ_OK;   // nothing to write
   if (cols == 0 || cols % 64 != 0 || (B != nullptr && r > 64)) return LOFTQ_ERR_UNSUPPORTED;
-  if (!qlora_forward_shape_ok(n_tok, rows, cols)) return LOFTQ_ERR_UNSUPPORTED;   // launch size limits
+  if (!qlora_forward_shape_ok(n_tok, rows, cols, B ? r : 0)) return LOFTQ_ERR_UNSUPPORTED;   // launch sizes
   if (!X || !packed || !Y || (!dq && !absmax)) return LOFTQ_ERR_INVALID_ARG;
   if (!aligned16(X) || !aligned16(packed) || !aligned16(Y)) return LOFTQ_ERR_INVALID_ARG;
   if (dq ? (!aligned16(qabsmax) || !aligned16(dq_scale)) : !aligned16(absmax)) return LOFTQ_ERR_INVALID_ARG;

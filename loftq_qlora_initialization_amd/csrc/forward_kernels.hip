@@ -224,24 +224,29 @@ __global__ __launch_bounds__(2 * kBM, kBM == 128 ? 2 : 1) void nf4_gemm_kernel(c
                                alpha, Y);
 }
 
-// Partial products P_q = X bf16(A)^T over the q-th of ks K ranges, for one 16-token
-// tile per workgroup (workgroup = tile * ks + q); P_q lands at T + q n r.  The 16
-// waves split the range (wave w takes its 32-wide steps w, w + 16, ...) and their
-// partial 16 x r products are summed through LDS in a fixed order.  Consumers add
-// the ks partials in order q = 0, 1, ...
-template <int NT, int U>
+// Partial products P_q = X bf16(A)^T over the q-th of ks K ranges, for TT 16-token
+// tiles per workgroup (workgroup = group * ks + q); P_q lands at T + q n r.  The 16
+// waves split the range (wave w takes its 32-wide steps w, w + 16, ...); each step's
+// A operand serves all TT tiles.  The waves' partial products are summed through LDS
+// in a fixed order.  Consumers add the ks partials in order q = 0, 1, ...
+template <int NT, int U, int TT>
 __global__ __launch_bounds__(1024) void lora_down_kernel(const __bf16* __restrict__ X, int64_t M, int64_t K,
                                                          const float* __restrict__ A, int r, int ks,
                                                          float* __restrict__ T) {
-  __shared__ float part[8][NT * 256];
+  constexpr int kOut = TT * NT * 256;   // accumulator floats per wave
+  __shared__ float part[8][kOut];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, li = lane & 15, lg = lane >> 4;
-  const int64_t tile = blockIdx.x / ks;
-  const int q = static_cast<int>(blockIdx.x - tile * ks);
-  const int64_t m0 = tile * 16;
-  const int64_t xr = (m0 + li < M) ? m0 + li : M - 1;
-  mfma_f4 acc[NT];
+  const int64_t group = blockIdx.x / ks;
+  const int q = static_cast<int>(blockIdx.x - group * ks);
+  const int64_t m0 = group * 16 * TT;
+  int64_t xr[TT];
 #pragma unroll
-  for (int nt = 0; nt < NT; ++nt) acc[nt] = mfma_f4{0.f, 0.f, 0.f, 0.f};
+  for (int tt = 0; tt < TT; ++tt) xr[tt] = (m0 + 16 * tt + li < M) ? m0 + 16 * tt + li : M - 1;
+  mfma_f4 acc[TT][NT];
+#pragma unroll
+  for (int tt = 0; tt < TT; ++tt)
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) acc[tt][nt] = mfma_f4{0.f, 0.f, 0.f, 0.f};
   // wave w takes the steps w, w + 16, ... of the range, U of them per round (U covers
   // a wave's share of the range when registers allow) with all their loads issued
   // before the first product (rows p >= r load row r - 1 and are zeroed)
@@ -249,13 +254,14 @@ __global__ __launch_bounds__(1024) void lora_down_kernel(const __bf16* __restric
   const int per = (KT + ks - 1) / ks;
   const int k_begin = q * per, k_end = k_begin + per < KT ? k_begin + per : KT;
   for (int base = k_begin + w; base < k_end; base += 16 * U) {
-    bf16x8 a[U];
+    bf16x8 a[U][TT];
     float4 ua[U][NT], ub[U][NT];
 #pragma unroll
     for (int i = 0; i < U; ++i) {
       const int kt = base + 16 * i < KT ? base + 16 * i : KT - 1;
       const int64_t k0 = static_cast<int64_t>(kt) * 32 + 8 * lg;
-      a[i] = *reinterpret_cast<const bf16x8*>(X + xr * K + k0);
+#pragma unroll
+      for (int tt = 0; tt < TT; ++tt) a[i][tt] = *reinterpret_cast<const bf16x8*>(X + xr[tt] * K + k0);
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
         const int p = nt * 16 + li < r ? nt * 16 + li : r - 1;
@@ -269,42 +275,49 @@ __global__ __launch_bounds__(1024) void lora_down_kernel(const __bf16* __restric
     for (int i = 0; i < U; ++i) {
       // steps past the range (clamped loads) and rows p >= r contribute exact zeros
       const bool live = base + 16 * i < k_end;
-      const bf16x8 ai = live ? a[i] : bf16x8{};
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
         const float z = (live && nt * 16 + li < r) ? 1.f : 0.f;
-        const float4 u = ua[i][nt], q = ub[i][nt];
+        const float4 u = ua[i][nt], v4 = ub[i][nt];
         bf16x8 b;
         b[0] = static_cast<__bf16>(u.x * z); b[1] = static_cast<__bf16>(u.y * z);
         b[2] = static_cast<__bf16>(u.z * z); b[3] = static_cast<__bf16>(u.w * z);
-        b[4] = static_cast<__bf16>(q.x * z); b[5] = static_cast<__bf16>(q.y * z);
-        b[6] = static_cast<__bf16>(q.z * z); b[7] = static_cast<__bf16>(q.w * z);
-        acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ai, b, acc[nt], 0, 0, 0);
+        b[4] = static_cast<__bf16>(v4.x * z); b[5] = static_cast<__bf16>(v4.y * z);
+        b[6] = static_cast<__bf16>(v4.z * z); b[7] = static_cast<__bf16>(v4.w * z);
+#pragma unroll
+        for (int tt = 0; tt < TT; ++tt) {
+          const bf16x8 ai = live ? a[i][tt] : bf16x8{};
+          acc[tt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ai, b, acc[tt][nt], 0, 0, 0);
+        }
       }
     }
   }
   // waves 8..15 park their partials, waves 0..7 add theirs, then one thread per
-  // element sums the 8 pair sums in wave order
+  // element sums the 8 pair sums in wave order; element ((tt NT + nt) 4 + v) 64 + lane
   if (w >= 8) {
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt)
+    for (int tt = 0; tt < TT; ++tt)
 #pragma unroll
-      for (int v = 0; v < 4; ++v) part[w - 8][(nt * 4 + v) * 64 + lane] = acc[nt][v];
+      for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) part[w - 8][((tt * NT + nt) * 4 + v) * 64 + lane] = acc[tt][nt][v];
   }
   __syncthreads();
   if (w < 8) {
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt)
+    for (int tt = 0; tt < TT; ++tt)
 #pragma unroll
-      for (int v = 0; v < 4; ++v) part[w][(nt * 4 + v) * 64 + lane] += acc[nt][v];
+      for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) part[w][((tt * NT + nt) * 4 + v) * 64 + lane] += acc[tt][nt][v];
   }
   __syncthreads();
-  for (int e = threadIdx.x; e < NT * 256; e += 1024) {
+  for (int e = threadIdx.x; e < kOut; e += 1024) {
     float sum = 0.f;
 #pragma unroll
-    for (int q = 0; q < 8; ++q) sum += part[q][e];
-    const int ln = e & 63, v = (e >> 6) & 3, nt = e >> 8;
-    const int64_t m = m0 + 4 * (ln >> 4) + v;
+    for (int qq = 0; qq < 8; ++qq) sum += part[qq][e];
+    const int ln = e & 63, v = (e >> 6) & 3, tn = e >> 8, tt = tn / NT, nt = tn - tt * NT;
+    const int64_t m = m0 + 16 * tt + 4 * (ln >> 4) + v;
     const int p = nt * 16 + (ln & 15);
     if (m < M && p < r) T[(q * M + m) * r + p] = sum;
   }
@@ -444,8 +457,9 @@ size_t qlora_forward_workspace_bytes(int64_t n_tok, int r) {
 
 // Launch shapes of one forward call (shared by the launcher and the argument check).
 struct ForwardPlan {
-  int64_t tiles;     // 16-token tiles of LoRA down
-  int ks;            // K ranges of LoRA down
+  int64_t tiles;     // 16-token tiles
+  int tt;            // LoRA down: tiles per workgroup (4 for r <= 16 and many tokens: A is read once per 4)
+  int ks;            // LoRA down: K ranges
   bool skinny;       // <= 64 tokens: few-token kernel
   int ntt;           // its 16-token tiles
   int bm;            // tiled kernel: tokens per workgroup
@@ -453,17 +467,20 @@ struct ForwardPlan {
   int block_gemm;
 };
 
-ForwardPlan plan_forward(int64_t n_tok, int64_t rows, int64_t cols) {
+ForwardPlan plan_forward(int64_t n_tok, int64_t rows, int64_t cols, int r) {
   ForwardPlan p{};
-  // enough workgroups to spread the reads of A and X (about 512), each with at
-  // least 16 of the 32-wide K steps
   p.tiles = (n_tok + 15) / 16;
+  p.tt = (r <= 16 && p.tiles >= 64) ? 4 : 1;
+  const int64_t groups = (p.tiles + p.tt - 1) / p.tt;
+  // enough workgroups to spread the reads of A and X (about 512, or 256 with four
+  // tiles each), each with at least 16 of the 32-wide K steps
+  const int64_t target = p.tt == 4 ? 256 : 512;
   const int64_t kt = cols / 32;
-  int64_t ks = (512 + p.tiles - 1) / p.tiles;
+  int64_t ks = (target + groups - 1) / groups;
   if (ks > kt / 16) ks = kt / 16;
   if (ks > kMaxSplits) ks = kMaxSplits;
   p.ks = ks < 1 ? 1 : static_cast<int>(ks);
-  p.grid_down = p.tiles * p.ks;
+  p.grid_down = groups * p.ks;
   p.skinny = n_tok <= 64;
   p.ntt = static_cast<int>((n_tok + 15) / 16);
   if (p.skinny) {
@@ -478,9 +495,9 @@ ForwardPlan plan_forward(int64_t n_tok, int64_t rows, int64_t cols) {
   return p;
 }
 
-bool qlora_forward_shape_ok(int64_t n_tok, int64_t rows, int64_t cols) {
+bool qlora_forward_shape_ok(int64_t n_tok, int64_t rows, int64_t cols, int r) {
   if (n_tok <= 0 || rows <= 0) return true;   // nothing is launched
-  const ForwardPlan p = plan_forward(n_tok, rows, cols);
+  const ForwardPlan p = plan_forward(n_tok, rows, cols, r);
   const int64_t limit = int64_t(1) << 32;        // work-items of one launch
   return p.grid_down * 1024 < limit && p.grid_gemm * p.block_gemm < limit;
 }
@@ -489,33 +506,40 @@ hipError_t launch_qlora_forward(const void* X, int64_t n_tok, int64_t rows, int6
                                 const float* absmax, const int8_t* qa, const float* dqs, int bits, const float* B,
                                 const float* A, int r, float alpha, float* Y, float* Tws, hipStream_t s) {
   if (n_tok == 0 || rows == 0) return hipSuccess;
-  if (cols % 64 != 0 || cols == 0 || !qlora_forward_shape_ok(n_tok, rows, cols)) return hipErrorInvalidValue;
+  if (cols % 64 != 0 || cols == 0 || !qlora_forward_shape_ok(n_tok, rows, cols, r)) return hipErrorInvalidValue;
   const __bf16* Xb = static_cast<const __bf16*>(X);
-  const ForwardPlan pl = plan_forward(n_tok, rows, cols);
+  const ForwardPlan pl = plan_forward(n_tok, rows, cols, r);
   const int ks = pl.ks;
   if (B != nullptr) {
     const dim3 grid(static_cast<unsigned>(pl.grid_down));
     // steps per wave in one K range, rounded up to a power of two, capped by registers
+    // (1024-thread workgroups: at most 128 VGPRs)
     const int64_t per = ((cols / 32) + ks - 1) / ks;
     const int64_t spw = (per + 15) / 16;
     const int nt = (r + 15) / 16;
-    const int umax = nt == 1 ? 8 : (nt == 2 ? 4 : 2);
+    const int umax = pl.tt == 4 ? 2 : (nt == 1 ? 8 : (nt == 2 ? 4 : 2));
     int u = spw <= 1 ? 1 : spw <= 2 ? 2 : spw <= 4 ? 4 : 8;
     if (u > umax) u = umax;
-#define LQ_DOWN(NT, U) \
-  LQ_LAUNCH("lora_down", (lora_down_kernel<NT, U>), grid, dim3(1024), 0, s, Xb, n_tok, cols, A, r, ks, Tws)
-    switch (nt * 16 + u) {
-      case 16 + 1: LQ_DOWN(1, 1); break;
-      case 16 + 2: LQ_DOWN(1, 2); break;
-      case 16 + 4: LQ_DOWN(1, 4); break;
-      case 16 + 8: LQ_DOWN(1, 8); break;
-      case 32 + 1: LQ_DOWN(2, 1); break;
-      case 32 + 2: LQ_DOWN(2, 2); break;
-      case 32 + 4: LQ_DOWN(2, 4); break;
-      case 48 + 1: LQ_DOWN(3, 1); break;
-      case 48 + 2: LQ_DOWN(3, 2); break;
-      case 64 + 1: LQ_DOWN(4, 1); break;
-      default: LQ_DOWN(4, 2); break;
+#define LQ_DOWN(NT, U, TT)                                                                                 \
+  LQ_LAUNCH("lora_down", (lora_down_kernel<NT, U, TT>), grid, dim3(1024), 0, s, Xb, n_tok, cols, A, r, ks, \
+            Tws)
+    if (pl.tt == 4) {
+      if (u == 1) LQ_DOWN(1, 1, 4);
+      else LQ_DOWN(1, 2, 4);
+    } else {
+      switch (nt * 16 + u) {
+        case 16 + 1: LQ_DOWN(1, 1, 1); break;
+        case 16 + 2: LQ_DOWN(1, 2, 1); break;
+        case 16 + 4: LQ_DOWN(1, 4, 1); break;
+        case 16 + 8: LQ_DOWN(1, 8, 1); break;
+        case 32 + 1: LQ_DOWN(2, 1, 1); break;
+        case 32 + 2: LQ_DOWN(2, 2, 1); break;
+        case 32 + 4: LQ_DOWN(2, 4, 1); break;
+        case 48 + 1: LQ_DOWN(3, 1, 1); break;
+        case 48 + 2: LQ_DOWN(3, 2, 1); break;
+        case 64 + 1: LQ_DOWN(4, 1, 1); break;
+        default: LQ_DOWN(4, 2, 1); break;
+      }
     }
 #undef LQ_DOWN
   }

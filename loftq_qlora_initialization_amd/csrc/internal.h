@@ -78,7 +78,7 @@ hipError_t launch_double_quant(const float* absmax, int64_t nblocks, int dqbs, i
 // unused without B.
 size_t qlora_forward_workspace_bytes(int64_t n_tok, int r);
 // false when one of the call's launches would exceed 2^32 work-items
-bool qlora_forward_shape_ok(int64_t n_tok, int64_t rows, int64_t cols);
+bool qlora_forward_shape_ok(int64_t n_tok, int64_t rows, int64_t cols, int r);
 hipError_t launch_qlora_forward(const void* X, int64_t n_tok, int64_t rows, int64_t cols, const uint8_t* packed,
                                 const float* absmax, const int8_t* qa, const float* dqs, int bits, const float* B,
                                 const float* A, int r, float alpha, float* Y, float* Tws, hipStream_t s);

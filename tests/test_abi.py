@@ -136,7 +136,8 @@ def test_qlora_forward_validation(clib):
     assert call(bits=5) == 2                                  # no such codebook
     assert call(cols=96) == 2                                 # rows of the weight split a 64-block
     assert call(r=65) == 2                                    # rank above 64
-    assert call(n=1 << 26) == 2                               # LoRA down beyond 2^32 work-items
+    assert call(n=1 << 26, r=24) == 2                         # LoRA down beyond 2^32 work-items
+    assert call(n=(1 << 31) - 16) == 2                        # even with four token tiles per workgroup
     assert call(n=16, rows=1 << 26) == 2                      # few-token kernel beyond 2^32 work-items
     assert call(n=4096, rows=1 << 30, B=None, A=None) == 2    # tiled kernel beyond 2^32 work-items
     assert call(A=None) == 1                                  # B without A
