@@ -155,8 +155,8 @@ def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path (the per-GPU kernels are what "
-              "one device runs; run with --gpus 1)", file=sys.stderr)
+        print("bench.py measures one GPU: libloftq has no multi-GPU path (its kernels are what one device runs "
+              "on its share of the matrices; run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
