@@ -82,6 +82,14 @@ __device__ __forceinline__ uint32_t exact_code(float r, float a, const EncodeLds
 
 __device__ __forceinline__ int nib_shift(int e) { return 8 * ((e >> 1) & 3) + ((e & 1) ? 0 : 4); }
 
+// A byte of packed codes holds two elements (element 2i in the high nibble), so the
+// decoders look up level pairs (c[b >> 4], c[b & 15]) by whole bytes: one LDS read
+// per two elements, each then multiplied by the block scale as before.
+typedef float lvpair __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ void fill_level_pairs(lvpair* lvl2, const Nf4Tables& tab, int tid, int nthreads) {
+  for (int i = tid; i < 256; i += nthreads) lvl2[i] = lvpair{tab.level[i >> 4], tab.level[i & 15]};
+}
+
 // Encode 16 residual values sharing absmax a into two packed 32-bit words.
 // y = 16 x + o (o = the grid origin, 16 for NF4) is formed straight from the
 // value, y = fma(v, 16 rcp(a), o), and lands in cell int(y) of the grid
@@ -228,14 +236,14 @@ __device__ __forceinline__ void raw_to_f32(const uint4 (&raw)[4], float v[16]) {
 
 // Where the fused kernel takes the base of its residual from.  load() fetches
 // the 16 elements e0 .. e0 + 15 of one lane (raw words), to_f32() turns them
-// into fp32 values; lvl is the NF4 level table in LDS.  kScaleB: the B operand
-// is multiplied by the kernel's bscale when loaded.
+// into fp32 values; lvl2 is the level-pair table in LDS (kCodes sources only).
+// kScaleB: the B operand is multiplied by the kernel's bscale when loaded.
 template <typename T>
 struct WeightSource {   // the weight W itself (bf16 or fp32): R = W - B A
   const T* W;
-  static constexpr bool kScaleB = false;
+  static constexpr bool kScaleB = false, kCodes = false;
   __device__ __forceinline__ void load(int64_t e0, uint4 (&raw)[4]) const { load16_raw(W + e0, raw); }
-  __device__ __forceinline__ void to_f32(const uint4 (&raw)[4], float v[16], const float*) const {
+  __device__ __forceinline__ void to_f32(const uint4 (&raw)[4], float v[16], const lvpair*) const {
     raw_to_f32<T>(raw, v);
   }
 };
@@ -246,7 +254,7 @@ struct Nf4Source {      // deq(Q) of existing codes: R = deq(Q) - bscale B A
   const int8_t* qa;     // or qabsmax and dq_scale per dq group
   const float* dqs;
   int dqbs;
-  static constexpr bool kScaleB = true;
+  static constexpr bool kScaleB = true, kCodes = true;
   // 16 codes (8 bytes) and the block's dequant scale a', as in the dequant kernel
   __device__ __forceinline__ void load(int64_t e0, uint4 (&raw)[4]) const {
     const uint2 c = *reinterpret_cast<const uint2*>(packed + (e0 >> 1));
@@ -254,12 +262,13 @@ struct Nf4Source {      // deq(Q) of existing codes: R = deq(Q) - bscale B A
     const float a = kDQ ? static_cast<float>(qa[b]) * dqs[b / dqbs] : absmax[b];
     raw[0] = make_uint4(c.x, c.y, __float_as_uint(a), 0u);
   }
-  __device__ __forceinline__ void to_f32(const uint4 (&raw)[4], float v[16], const float* lvl) const {
+  __device__ __forceinline__ void to_f32(const uint4 (&raw)[4], float v[16], const lvpair* lvl2) const {
     const float a = __uint_as_float(raw[0].z);
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const uint32_t code = ((e < 8 ? raw[0].x : raw[0].y) >> nib_shift(e)) & 0xFu;
-      v[e] = lvl[code] * a;   // deq = fl32(c[code] a'), one rounding
+    for (int j = 0; j < 8; ++j) {
+      const lvpair c = lvl2[((j < 4 ? raw[0].x : raw[0].y) >> (8 * (j & 3))) & 0xFFu];
+      v[2 * j] = c.x * a;       // deq = fl32(c[code] a'), one rounding
+      v[2 * j + 1] = c.y * a;
     }
   }
 };
@@ -291,9 +300,9 @@ __global__ __launch_bounds__(kFusedThreads) __attribute__((amdgpu_waves_per_eu(R
                                                                        float* __restrict__ absmax, Nf4Tables tab) {
   constexpr int KK = R16 / 4;
   __shared__ EncodeLds s;
-  __shared__ float lvl[16];
+  __shared__ lvpair lvl2[Src::kCodes ? 256 : 1];
   fill_lds(s, tab);
-  if (threadIdx.x < 16) lvl[threadIdx.x] = tab.level[threadIdx.x];
+  if constexpr (Src::kCodes) fill_level_pairs(lvl2, tab, threadIdx.x, kFusedThreads);
   __syncthreads();
   const int lane = threadIdx.x & 63, li = lane & 15, g = lane >> 4;
   const int64_t nbc = cols >> 6;
@@ -345,7 +354,7 @@ __global__ __launch_bounds__(kFusedThreads) __attribute__((amdgpu_waves_per_eu(R
 #pragma unroll
       for (int t = 0; t < 4; ++t) acc[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(aop[kk][t], bop[kk], acc[t], 0, 0, 0);
     float v[16];
-    src.to_f32(raw, v, lvl);
+    src.to_f32(raw, v, lvl2);
     float m = 0.f;
 #pragma unroll
     for (int t = 0; t < 4; ++t)
@@ -461,9 +470,11 @@ __global__ __launch_bounds__(kThreads) void dequant_kernel(const uint8_t* __rest
                                                            double* __restrict__ wpartials,
                                                            double* __restrict__ sumsq, Nf4Tables tab) {
   __shared__ float lvl[16];
+  __shared__ lvpair lvl2[256];
   __shared__ double red[2 * (kThreads / 64)];
   const bool wsum = kHasW && wpartials != nullptr;
   if (threadIdx.x < 16) lvl[threadIdx.x] = tab.level[threadIdx.x];
+  fill_level_pairs(lvl2, tab, threadIdx.x, kThreads);
   __syncthreads();
   const int lane = threadIdx.x & 63;
   const int64_t nslices = n >> 10;
@@ -508,10 +519,11 @@ __global__ __launch_bounds__(kThreads) void dequant_kernel(const uint8_t* __rest
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       float o[4];
+      const lvpair c01 = lvl2[cw[q] & 0xFFu], c23 = lvl2[(cw[q] >> 8) & 0xFFu];   // elements 0,1 and 2,3
+      const float lv[4] = {c01.x, c01.y, c23.x, c23.y};
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const uint32_t code = (cw[q] >> nib_shift(j)) & 0xFu;
-        const float d = lvl[code] * a[q];
+        const float d = lv[j] * a[q];
         o[j] = kHasW ? (w[q][j] - d) : d;
         ss = fmaf(o[j], o[j], ss);
         if (kHasW) ws = fmaf(w[q][j], w[q][j], ws);
