@@ -743,6 +743,70 @@ __global__ __launch_bounds__(1024) void exact_jacobi_kernel(const float* __restr
     __syncthreads();
     sweeps = sweep + 1;
     for (int rnd = 0; rnd < N - 1; ++rnd) {
+      if (len <= 256) {
+        // Vectors of <= 256: a wave takes its pairs four at a time with every load of
+        // the batch issued before the first reduction, and rotates in registers
+        // (lane holds elements lane + 64 j, j < 4): the same arithmetic and order as
+        // the loop below, with one memory round trip per batch instead of per pair.
+        constexpr int kPB = 4;
+        for (int i0 = wave; i0 < N / 2; i0 += nwaves * kPB) {
+          double u[kPB][4], w[kPB][4];
+          int pp[kPB], qq[kPB];
+#pragma unroll
+          for (int b = 0; b < kPB; ++b) {
+            const int i = i0 + b * nwaves;
+            int p = 0, q = 0;
+            if (i < N / 2) {
+              const int pa = rr_player(i, rnd, N), pb = rr_player(N - 1 - i, rnd, N);
+              p = min(pa, pb);
+              q = max(pa, pb);
+            }
+            pp[b] = p;
+            qq[b] = (i < N / 2 && q < n) ? q : -1;
+            const double* xp = Xw + static_cast<int64_t>(p) * len;
+            const double* xq = Xw + static_cast<int64_t>(qq[b] < 0 ? p : q) * len;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              const int64_t e = lane + 64 * j;
+              u[b][j] = e < len ? xp[e] : 0.0;
+              w[b][j] = e < len ? xq[e] : 0.0;
+            }
+          }
+#pragma unroll
+          for (int b = 0; b < kPB; ++b) {
+            if (qq[b] < 0) continue;   // wave-uniform
+            double al = 0.0, be = 0.0, ga = 0.0;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              al += u[b][j] * u[b][j];
+              be += w[b][j] * w[b][j];
+              ga += u[b][j] * w[b][j];
+            }
+            for (int off = 32; off > 0; off >>= 1) {
+              al += __shfl_xor(al, off);
+              be += __shfl_xor(be, off);
+              ga += __shfl_xor(ga, off);
+            }
+            if (ga == 0.0 || fabs(ga) <= 1e-14 * sqrt(al * be)) continue;
+            const double zeta = (be - al) / (2.0 * ga);
+            const double t = (zeta >= 0.0 ? 1.0 : -1.0) / (fabs(zeta) + sqrt(1.0 + zeta * zeta));
+            const double c = 1.0 / sqrt(1.0 + t * t), sn = c * t;
+            double* xp = Xw + static_cast<int64_t>(pp[b]) * len;
+            double* xq = Xw + static_cast<int64_t>(qq[b]) * len;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              const int64_t e = lane + 64 * j;
+              if (e < len) {
+                xp[e] = c * u[b][j] - sn * w[b][j];
+                xq[e] = sn * u[b][j] + c * w[b][j];
+              }
+            }
+            if (lane == 0) rotated = 1;
+          }
+        }
+        __syncthreads();
+        continue;
+      }
       for (int i = wave; i < N / 2; i += nwaves) {
         const int pa = rr_player(i, rnd, N), pb = rr_player(N - 1 - i, rnd, N);
         const int p = min(pa, pb), q = max(pa, pb);
