@@ -118,14 +118,16 @@ def test_forward_bits_and_double_quant(lib, bits, dq):
     check(Y, ref, bound(c, rows, cols, bits, alpha, r))
 
 
-def test_forward_256_token_tiles_ragged(lib):
+@pytest.mark.parametrize("cols,bits,dq", [(128, 4, False), (192, 3, True)])
+def test_forward_256_token_tiles_ragged(lib, cols, bits, dq):
     """Enough output tiles for 256-token workgroups (2 x 129 >= 256 CUs) with ragged
-    tokens (300 = 256 + 44) and features (16400 = 128 * 128 + 16)."""
-    n_tok, rows, cols, r, alpha = 300, 16400, 128, 8, 1.25
-    c = make_case(n_tok, rows, cols, r, 4, False, 2560)
-    Y = run_device(lib, c, rows, cols, 4, alpha, False)
-    ref = oracle.qlora_forward(c["X"], c["codes"], c["scale"], rows, cols, c["B"], c["A"], alpha)
-    check(Y, ref, bound(c, rows, cols, 4, alpha, r))
+    tokens (300 = 256 + 44) and features (16400 = 128 * 128 + 16); 192 columns give an
+    odd number of 64-wide K steps."""
+    n_tok, rows, r, alpha = 300, 16400, 8, 1.25
+    c = make_case(n_tok, rows, cols, r, bits, dq, 2560 + cols)
+    Y = run_device(lib, c, rows, cols, bits, alpha, dq)
+    ref = oracle.qlora_forward(c["X"], c["codes"], c["scale"], rows, cols, c["B"], c["A"], alpha, bits=bits)
+    check(Y, ref, bound(c, rows, cols, bits, alpha, r))
 
 
 @pytest.mark.parametrize("n_tok,rows,cols", [(20, 100, 1600), (200, 90, 2048), (3, 40, 4096)])
