@@ -127,7 +127,9 @@ __global__ __launch_bounds__(2 * kBM, kBM == 128 ? 2 : 1) void nf4_gemm_kernel(c
                                                        float* __restrict__ Y, Nf4Tables tab) {
   constexpr int kThreads = 2 * kBM;      // kBM / 64 x 2 waves, 64 x 64 outputs each
   constexpr int kWM = kBM / 64;
-  constexpr int kLdsRow = kBK + 8;       // +8 bf16 per row against bank conflicts
+  // padded rows against bank conflicts: +16 bf16 (40-dword rows) measured fewer conflicts than +8 for
+  // 256-token tiles; 128-token tiles keep +8 so that two workgroups fit a CU's LDS
+  constexpr int kLdsRow = kBK + (kBM == 256 ? 16 : 8);
   constexpr int XPT = kBM * kBK / kThreads;   // X elements per thread and step (32)
   constexpr int WPT = kBN * kBK / kThreads;   // weight codes per thread and step (32 or 16)
   typedef uint32_t WcT __attribute__((ext_vector_type(WPT / 8)));
