@@ -43,8 +43,8 @@ MEASURED_TRAFFIC = {
         "gemm_nn": {"bytes": 77784775, "source": "gemm_kernels.hip", "sha256": "4322c77aea1b6c85"},
         "gemm_tn": {"bytes": 75687250, "source": "gemm_kernels.hip", "sha256": "4322c77aea1b6c85"},
         # the QLoRA forward on this layer: 2048 tokens (tiled kernel), 16 tokens (few-token kernel)
-        "nf4_gemm": {"bytes": 122938590, "source": "forward_kernels.hip", "sha256": "30afa766b7152955"},
-        "nf4_gemm_skinny": {"bytes": 10397831, "source": "forward_kernels.hip", "sha256": "30afa766b7152955"},
+        "nf4_gemm": {"bytes": 122919263, "source": "forward_kernels.hip", "sha256": "59cd1a34f99baaac"},
+        "nf4_gemm_skinny": {"bytes": 10397831, "source": "forward_kernels.hip", "sha256": "59cd1a34f99baaac"},
     },
 }
 
