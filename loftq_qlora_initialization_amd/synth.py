@@ -34,7 +34,8 @@ import numpy as np
 
 __all__ = [
     "Workload", "WORKLOADS", "workload", "c4_matrix_specs", "make_weight",
-    "f32_to_bf16_bits", "bf16_bits_to_f32", "random_factors", "random_residual",
+    "f32_to_bf16_bits", "bf16_bits_to_f32", "random_factors", "random_residual", "spectral_matrix",
+    "tiny_scale_blocks",
 ]
 
 LORA_SEED = 42  # loftq_config default seed printed on the LoftQ blog (§3.2)
@@ -93,8 +94,9 @@ def c4_matrix_specs() -> List[Workload]:
 def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
     """Round fp32 to bf16 (round to nearest even); returns the uint16 bit patterns.
     Inputs here are finite, so no NaN handling is needed."""
-    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
-    u = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    # finite values stay below 0xFF800000, so the 32-bit sum cannot wrap
+    u = (u + np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))) >> np.uint32(16)
     return u.astype(np.uint16)
 
 
@@ -163,3 +165,37 @@ def random_residual(n: int, seed: int, std: float = 0.02) -> np.ndarray:
     """A flat fp32 array of n Gaussian values (a residual handed straight to the quantizer)."""
     g = np.random.Generator(np.random.PCG64(np.random.SeedSequence(seed)))
     return (std * g.standard_normal(n)).astype(np.float32)
+
+
+def spectral_matrix(rows: int, cols: int, sigma, seed: int, noise: float = 0.0) -> np.ndarray:
+    """fp32 U diag(sigma) V^T (+ noise * N(0,1) entries): U, V Haar-orthonormal.
+
+    ``sigma`` lists the singular values (length <= min(rows, cols)); fewer values than
+    min(rows, cols) give a matrix of that rank (before the fp32 rounding and noise).
+    """
+    s = np.asarray(sigma, dtype=np.float64)
+    ss = np.random.SeedSequence(seed)
+    gu, gv, gn = (np.random.Generator(np.random.PCG64(c)) for c in ss.spawn(3))
+    U = _haar(gu, rows, s.size)
+    V = _haar(gv, cols, s.size)
+    M = (U * s[None, :]) @ V.T
+    if noise:
+        M = M + noise * gn.standard_normal((rows, cols))
+    return M.astype(np.float32)
+
+
+def tiny_scale_blocks(scales, seed: int) -> np.ndarray:
+    """Blocks of 64 fp32 values, block b drawn as scales[b] * U[-1, 1] rounded to fp32,
+    with one element exactly +-scales[b] (so it is the block's absmax), a few exact
+    zeros and, where representable, values a few ulps either side of scales[b] * 2^-j."""
+    g = np.random.Generator(np.random.PCG64(np.random.SeedSequence(seed)))
+    out = np.empty((len(scales), 64), np.float32)
+    for b, a in enumerate(scales):
+        a = np.float32(a)
+        v = (np.float64(a) * g.uniform(-1.0, 1.0, 64)).astype(np.float32)
+        v[g.integers(0, 64)] = a if b % 2 == 0 else -a
+        for z in g.choice(64, 3, replace=False):
+            if abs(v[z]) != a:
+                v[z] = 0.0
+        out[b] = v
+    return out.ravel()

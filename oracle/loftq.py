@@ -20,6 +20,13 @@ Readings:
     quantization.
   * objective[0] = ||W - Q_1|| / ||W|| (plain NF4 error); objective[t] =
     ||W - Q_t - B_t A_t|| / ||W|| for t = 1..T, each computed directly.
+  * Resume ([LoftQ blog] §2.3: the initialisation is computed once and its
+    result kept): a run may start from the factors (B_k, A_k) of k completed
+    alternations instead of Delta_0 = 0 and carry on with alternations
+    k+1 .. k+T, the sketch counter continuing at k+1, so that k alternations
+    followed by T resumed ones take the same steps as k+T alternations in one
+    run.  objective[0] is then ||W - Q_{k+1}|| / ||W||, the error of the run's
+    first quantization alone (for k = 0 the plain NF4 error above).
 """
 from __future__ import annotations
 
@@ -103,20 +110,35 @@ def objective(W32: np.ndarray, codes: np.ndarray, scale: np.ndarray, B, A, block
 def loftq_init(W32: np.ndarray, *, rank: int, iterative_steps: int = 5, blocksize: int = 64,
                double_quant_on: bool = True, dq_blocksize: int = 256, exact: bool = False,
                oversample: int = 8, power_iters: int = 2, seed: int = 42, keep_steps: bool = False,
-               warm_start: bool = False, bits: int = 4) -> dict:
+               warm_start: bool = False, bits: int = 4, resume_from: int = 0, init_B=None, init_A=None,
+               init_sigma=None) -> dict:
     """The whole initialisation: T alternations from Delta_0 = 0, objective per alternation.
 
     warm_start: alternations t >= 2 of the randomized SVD use warm_sketch(V_{t-1}, ...)
     instead of the fresh sketch of (seed, t) (a variant; off reproduces the pages' method).
+    resume_from = k >= 1: start from init_B, init_A (B_k, A_k; with warm_start also
+    init_sigma = sigma_k) and run alternations k+1 .. k+T.
     """
     W32 = np.asarray(W32, dtype=np.float32)
     d, k = W32.shape
     T = int(iterative_steps)
+    k0 = int(resume_from)
+    if k0 < 0 or (k0 > 0 and (init_B is None or init_A is None or T == 0)):
+        raise ValueError("resume needs k >= 1, B_k, A_k and T >= 1")
     kw = dict(rank=rank, blocksize=blocksize, double_quant_on=double_quant_on, dq_blocksize=dq_blocksize, bits=bits,
               exact=exact, oversample=oversample, power_iters=power_iters, seed=seed)
     obj = np.zeros(T + 1)
     steps = []
     B = A = None
+    last = None
+    if k0 > 0:
+        B, A = np.asarray(init_B), np.asarray(init_A)
+        if warm_start and not exact:
+            if init_sigma is None:
+                raise ValueError("a warm-started resume needs sigma_k")
+            # A_k = diag(sqrt sigma) V^T  =>  V = A_k^T diag(sigma^-1/2)
+            sg = np.asarray(init_sigma, dtype=np.float64)
+            last = dict(V=np.asarray(A, dtype=np.float64).T / np.sqrt(sg)[None, :])
     if T == 0:
         codes, absmax = quantize_residual(W32.ravel(), blocksize, nf_codebook(bits))
         res = dict(codes=codes, absmax=absmax)
@@ -129,12 +151,11 @@ def loftq_init(W32: np.ndarray, *, rank: int, iterative_steps: int = 5, blocksiz
         obj[0] = objective(W32, codes, scale, None, None, blocksize, bits)
         res.update(B=np.zeros((d, rank)), A=np.zeros((rank, k)), sigma=np.zeros(rank), objective=obj)
         return res
-    last = None
     for t in range(1, T + 1):
         om = None
         if warm_start and not exact and last is not None:
-            om = warm_sketch(last["V"], seed, t, k, rank + oversample)
-        st = loftq_step(W32, B, A, t=t, omega=om, **kw)
+            om = warm_sketch(last["V"], seed, k0 + t, k, rank + oversample)
+        st = loftq_step(W32, B, A, t=k0 + t, omega=om, **kw)
         if t == 1:
             obj[0] = objective(W32, st["codes"], st["scale"], None, None, blocksize, bits)
         obj[t] = objective(W32, st["codes"], st["scale"], st["B"], st["A"], blocksize, bits)

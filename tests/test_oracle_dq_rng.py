@@ -62,3 +62,13 @@ def test_rademacher_sketch_layout():
     assert om[5, 7] == (1.0 if (int(z) >> 63) == 0 else -1.0)
     assert abs(om.mean()) < 0.05
     assert not np.array_equal(om, oracle.rademacher_sketch(42, 1, k, l))
+
+
+def test_double_quant_tie_rule_golden():
+    """Quotients exactly halfway between two codes go to the even code (hand-worked table)."""
+    rows = [ln.split() for ln in golden_rows("dq_tie_rounding.txt")]
+    a = np.array([float(r[0]) for r in rows], dtype=np.float32)
+    want = np.array([int(r[1]) for r in rows], dtype=np.int8)
+    q, s = oracle.double_quant(a, 256)
+    assert s[0] == np.float32(1.0)
+    assert np.array_equal(q, want)

@@ -160,3 +160,52 @@ def test_warm_start_with_one_alternation_is_the_cold_start():
     a = oracle.loftq_init(W, **kw)
     b = oracle.loftq_init(W, warm_start=True, **kw)
     assert np.array_equal(a["sigma"], b["sigma"]) and np.array_equal(a["objective"], b["objective"])
+
+
+def test_resume_continues_the_alternation():
+    """k alternations, then T resumed from (B_k, A_k), take the steps of one k + T run."""
+    w = synth.Workload("t", 192, 128, "bf16", 4, 5, True, 4, 1, False, 31, "outliers")
+    W = synth.make_weight(w)[1]
+    kw = dict(rank=4, oversample=4, power_iters=1, double_quant_on=True, seed=7)
+    full = oracle.loftq_init(W, iterative_steps=5, keep_steps=True, **kw)
+    head = oracle.loftq_init(W, iterative_steps=2, **kw)
+    tail = oracle.loftq_init(W, iterative_steps=3, resume_from=2, init_B=head["B"], init_A=head["A"],
+                             keep_steps=True, **kw)
+    assert np.array_equal(tail["codes"], full["codes"])
+    assert np.array_equal(tail["sigma"], full["sigma"])
+    assert np.array_equal(tail["objective"][1:], full["objective"][3:])
+    # objective[0] of the resumed run: the error of its first quantization alone
+    st = tail["steps"][0]
+    assert tail["objective"][0] == oracle.objective(W, st["codes"], st["scale"], None, None)
+    # the same with a warm-started subspace iteration (sigma_k given as well)
+    wfull = oracle.loftq_init(W, iterative_steps=4, warm_start=True, **kw)
+    whead = oracle.loftq_init(W, iterative_steps=1, warm_start=True, **kw)
+    wtail = oracle.loftq_init(W, iterative_steps=3, warm_start=True, resume_from=1, init_B=whead["B"],
+                              init_A=whead["A"], init_sigma=whead["sigma"], **kw)
+    assert np.allclose(wtail["sigma"], wfull["sigma"], rtol=1e-12, atol=0)
+    assert np.allclose(wtail["objective"][1:], wfull["objective"][2:], rtol=1e-12, atol=0)
+    with pytest.raises(ValueError):
+        oracle.loftq_init(W, iterative_steps=0, resume_from=1, init_B=head["B"], init_A=head["A"], **kw)
+
+
+def test_randomized_svd_of_rank_deficient_matrix():
+    """E of rank 5 < l: the top 5 triplets are E's own, the rest are zero (brute force: E itself)."""
+    s_true = np.array([3.0, 2.0, 1.5, 1.0, 0.5])
+    E = synth.spectral_matrix(300, 200, s_true, seed=3).astype(np.float64)
+    for l in (24, 48):
+        om = oracle.rademacher_sketch(42, 1, 200, l)
+        U, s, V = oracle.randomized_svd(E, 16, om, 2)
+        assert np.allclose(s[:5], s_true, rtol=1e-6)
+        assert np.all(s[5:] <= 1e-6)
+        assert np.linalg.norm((U * s) @ V.T - E) <= 1e-6 * np.linalg.norm(E)
+
+
+def test_randomized_svd_graded_spectrum():
+    """sigma_1 / sigma_l = 1e3 (geometric), flat tail: the top r match the exact SVD closely."""
+    l, r = 24, 16
+    s_true = np.concatenate([np.geomspace(1.0, 1e-3, l), np.full(40, 1e-3)])
+    E = synth.spectral_matrix(256, 192, s_true, seed=4).astype(np.float64)
+    _, s_ex, _ = oracle.exact_svd(E, r)
+    _, s, _ = oracle.randomized_svd(E, r, oracle.rademacher_sketch(42, 1, 192, l), 2)
+    assert np.allclose(s_ex, s_true[:r], rtol=1e-6)
+    assert np.max(np.abs(s - s_ex) / s_ex) < 1e-2
