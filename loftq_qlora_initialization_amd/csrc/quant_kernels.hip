@@ -97,13 +97,19 @@ __device__ __forceinline__ void fill_level_pairs(lvpair* lvl2, const Nf4Tables& 
 // the cell stores (fl32(16 thr + o), base) and code = base + (y > thr16).  y
 // differs from 16 fl32(v / a) + o by less than 2^-18 and thr16 from 16 thr + o
 // by at most 2^-19, so outside the window |y - thr16| < 2^-16 the comparison
-// decides exactly as fl32(v / a) > thr; elements inside it (and every element
-// of a subnormal-absmax block) are redone with an IEEE division and a full
-// threshold count.
+// decides exactly as fl32(v / a) > thr; elements inside it are redone with an
+// IEEE division and a full threshold count.
+// The reciprocal bound needs a normal rcp(a) whose 16-fold product stays finite,
+// so a block with a outside [2^-120, 2^120] (tiny normals and subnormals, where
+// 16 rcp(a) would overflow, and huge values, whose reciprocal is subnormal)
+// skips the fast path: inv16 = 0 keeps every y at the origin cell, in range,
+// and all 16 elements take the exact division.  With inv16 finite and
+// |v| <= a, 0 <= y < 33 for every finite v, so the cell index is in range.
 __device__ __forceinline__ uint2 encode16(const float v[16], float a, const EncodeLds& s) {
-  const float inv16 = (a > 0.f) ? 16.f * __builtin_amdgcn_rcpf(a) : 0.f;
+  const bool fast = a >= 0x1p-120f && a <= 0x1p+120f;
+  const float inv16 = fast ? 16.f * __builtin_amdgcn_rcpf(a) : 0.f;
   const float origin = s.origin;
-  uint32_t danger = (a > 0.f && a < FLT_MIN) ? 0xFFFFu : 0u;
+  uint32_t danger = (!fast && a > 0.f) ? 0xFFFFu : 0u;
   uint32_t w0 = 0, w1 = 0;
 #pragma unroll
   for (int e = 0; e < 16; ++e) {
