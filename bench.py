@@ -1,10 +1,13 @@
 #!/usr/bin/env python
 """LoftQ initialisation throughput on one AMD Instinct MI355X.
 
-A step is one loftq_init of the workload's weight (all T alternations: NF4
-quantize of the residual, double quant, dequant-subtract, randomized rank-r SVD,
-objective) with W already resident in HBM.  `value` is matrix elements per second
-(rows * cols per step).  The JSON line also carries:
+A step is one LoftQ initialisation of the whole workload (all T alternations of
+every matrix: NF4 quantize of the residual, double quant, dequant-subtract,
+randomized rank-r SVD, objective) with W already resident in HBM.  The default
+workload is the 224 matrices of a 32-layer 7B-class decoder (q, k, v, o, gate, up,
+down of every layer), initialised by one loftq_init_batch call over several
+streams; single-matrix workloads run one loftq_init.  `value` is matrix elements
+per second (sum of rows * cols per step).  The JSON line also carries:
   roofline      the dominant streaming kernel: algorithmic bytes per launch over
                 its average launch time, timed with HIP events that the library
                 records around each launch on its own stream during a separate
@@ -17,6 +20,8 @@ objective) with W already resident in HBM.  `value` is matrix elements per secon
   qlora_forward the QLoRA forward of the adapted layer on this init's Q, B, A for a
                 2048-token (matrix-core bound) and a 16-token (HBM bound) batch;
   cpu_baseline  the CPU oracle on a bounded row sample of the same workload.
+For the decoder batch the adapter merge, the variants and the forward run on its
+first matrix (layer 0's q projection, 4096 x 4096).
 """
 from __future__ import annotations
 
@@ -91,10 +96,13 @@ def measured_traffic(workload, kernel):
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="c2", help="c1, c2, c3 or c5")
-    ap.add_argument("--cpu-rows", type=int, default=4096, help="rows of the workload timed on the CPU oracle")
+    ap.add_argument("--steps", type=int, default=None, help="timed steps (default 3 for c4, else 20)")
+    ap.add_argument("--warmup", type=int, default=None, help="untimed steps (default 1 for c4, else 3)")
+    ap.add_argument("--workload", default="c4", help="c4 (the 224-matrix decoder batch), c1, c2, c3 or c5")
+    ap.add_argument("--streams", type=int, default=4, help="streams the batched call spreads its matrices over")
+    ap.add_argument("--layers", type=int, default=32, help="decoder layers of the c4 batch (fewer: a smaller batch)")
+    ap.add_argument("--cpu-rows", type=int, default=None,
+                    help="rows of each sampled matrix timed on the CPU oracle (default 1024 for c4, else 4096)")
     ap.add_argument("--skip-cpu", action="store_true", help="omit the CPU oracle leg")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="only run three device-to-device copies of this many MiB (HBM counter calibration)")
@@ -125,7 +133,9 @@ def algorithmic_bytes(name, w, rows, cols):
     return table.get(name)
 
 
-def cpu_baseline(w, rows):
+def cpu_baseline(specs, rows, extrapolated):
+    """The oracle's loftq_init on the first `rows` rows of each matrix in `specs`, repeated
+    until about 10 s of CPU work (at most 3 passes); elements per second."""
     import numpy as np
     import oracle
     from loftq_qlora_initialization_amd import synth
@@ -134,21 +144,65 @@ def cpu_baseline(w, rows):
         cores = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
     except Exception:   # threadpoolctl absent: report the interpreter's own thread
         cores = 1
-    rows = min(rows, w.rows)
-    _, W = synth.make_weight(w, rows=rows)
-    kw = dict(rank=w.rank, iterative_steps=w.iterative_steps, double_quant_on=w.double_quant, exact=w.exact_svd,
-              oversample=w.oversample, power_iters=w.power_iters, seed=w.sketch_seed)
-    # repeat the same initialisation until about 10 s of CPU work (at most 3 runs)
+    samples = []
+    for w in specs:
+        rr = min(rows, w.rows)
+        samples.append((w, rr, synth.make_weight(w, rows=rr)[1]))
     reps, dt = 0, 0.0
     while reps < 3 and (reps == 0 or dt < 10.0):
         t0 = time.perf_counter()
-        oracle.loftq_init(W, **kw)
+        for w, rr, W in samples:
+            oracle.loftq_init(W, rank=w.rank, iterative_steps=w.iterative_steps, double_quant_on=w.double_quant,
+                              exact=w.exact_svd, oversample=w.oversample, power_iters=w.power_iters,
+                              seed=w.sketch_seed)
         dt += time.perf_counter() - t0
         reps += 1
-    what = "all" if rows == w.rows else f"first {rows} of"
-    return {"value": reps * rows * w.cols / dt, "unit": "elements/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"{what} {w.rows} rows of {w.name}, same r/p/q/T/double-quant, {reps} loftq_init "
-                      f"run(s) in {dt:.1f} s"}
+    elems = sum(rr * w.cols for w, rr, _ in samples)
+    if len(specs) == 1:
+        w, rr, _ = samples[0]
+        what = f"{'all' if rr == w.rows else f'first {rr} of'} {w.rows} rows of {w.name}"
+    else:
+        what = f"the first {rows} rows of each of {len(specs)} matrices ({', '.join(w.name for w in specs)})"
+    out = {"value": reps * elems / dt, "unit": "elements/s", "cores": int(cores), "kind": "oracle",
+           "sample": f"{what}, same r/p/q/T/double-quant, {reps} pass(es) in {dt:.1f} s"}
+    if extrapolated:
+        out["sample"] += "; per-element rate extrapolated to the whole batch"
+        out["extrapolated"] = True
+    return out
+
+
+def device_weights(specs, workers):
+    """Generate every matrix on the host (seeded, threads in parallel) and copy it to the GPU."""
+    import concurrent.futures as cf
+    import numpy as np
+    import torch
+    from loftq_qlora_initialization_amd import synth
+
+    def one(w):
+        bits, _ = synth.make_weight(w)
+        if w.dtype == "bf16":
+            return torch.from_numpy(bits.view(np.int16)).cuda().view(torch.bfloat16)
+        return torch.from_numpy(bits).cuda()
+    if len(specs) == 1:
+        return [one(specs[0])]
+    with cf.ThreadPoolExecutor(max_workers=workers) as ex:
+        return list(ex.map(one, specs))
+
+
+def kernel_table(prof, steps, bytes_per_step):
+    """Per-kernel launches, average launch time, share and algorithmic GB/s from a profiled pass.
+    bytes_per_step(name) -> algorithmic bytes all launches of that kernel move in one step, or None."""
+    kernels = {}
+    total = sum(v[1] for v in prof.values())
+    for name, (launches, total_ms) in sorted(prof.items(), key=lambda kv: -kv[1][1]):
+        avg_us = 1e3 * total_ms / launches
+        entry = {"launches_per_step": launches / steps, "avg_us": round(avg_us, 3), "share": round(total_ms / total, 4)}
+        nbytes = bytes_per_step(name)
+        if nbytes is not None:
+            entry["GBps"] = round(nbytes * steps / (total_ms * 1e-3) / 1e9, 1)
+            entry["bytes_per_launch"] = round(nbytes * steps / launches)
+        kernels[name] = entry
+    return kernels
 
 
 def main():
@@ -177,50 +231,93 @@ def main():
     import loftq_qlora_initialization_amd as lq
     from loftq_qlora_initialization_amd import synth
 
-    w = synth.workload(args.workload)
-    bits, _ = synth.make_weight(w)
-    if w.dtype == "bf16":
-        Wd = torch.from_numpy(bits.view(np.int16)).cuda().view(torch.bfloat16)
+    batch = args.workload == "c4"
+    if batch:
+        specs = synth.c4_matrix_specs()[:7 * max(1, min(32, args.layers))]
+        wname = "c4_decoder_batch_224_bf16" if len(specs) == 224 else f"c4_decoder_batch_{len(specs)}_bf16"
     else:
-        Wd = torch.from_numpy(bits).cuda()
+        specs = [synth.workload(args.workload)]
+        wname = specs[0].name
+    steps = args.steps if args.steps is not None else (3 if batch else 20)
+    warmup = args.warmup if args.warmup is not None else (1 if batch else 3)
+    w = specs[0]                      # the configuration (shared by every matrix of the batch)
+    total_elems = sum(x.numel for x in specs)
+    t_gen = time.perf_counter()
+    Ws = device_weights(specs, workers=min(16, os.cpu_count() or 1))
+    t_gen = time.perf_counter() - t_gen
     cfg = lq.default_config(iterative_steps=w.iterative_steps, rank=w.rank, oversample=w.oversample,
                             power_iters=w.power_iters, double_quant=int(w.double_quant),
                             exact_svd=int(w.exact_svd), seed=w.sketch_seed)
-    bufs = lq.InitBuffers(w.rows, w.cols, cfg)
-    for _ in range(args.warmup):
-        lq.loftq_init(Wd, cfg, buffers=bufs)
+    if batch:
+        runner = lq.BatchRunner(Ws, cfg, nstreams=args.streams)
+        bufs = runner.buffers[0]
+
+        def step():
+            runner.run()
+    else:
+        bufs = lq.InitBuffers(w.rows, w.cols, cfg)
+
+        def step():
+            lq.loftq_init(Ws[0], cfg, buffers=bufs)
+    for _ in range(warmup):
+        step()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for _ in range(args.steps):
-        lq.loftq_init(Wd, cfg, buffers=bufs)
+    for _ in range(steps):
+        step()
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
-    ms_per_step = 1e3 * elapsed / args.steps
-    value = w.numel * args.steps / elapsed
+    ms_per_step = 1e3 * elapsed / steps
+    value = total_elems * steps / elapsed
 
-    # profiled pass: HIP events around every library launch, same steps on the same stream
+    # launches per init of each kernel for every distinct shape (one profiled init each), so
+    # the batch's algorithmic bytes per kernel can be summed over its matrices
+    shapes = {}
+    for x, W in zip(specs, Ws):
+        shapes.setdefault((x.rows, x.cols), [x, W, 0])[2] += 1
+    per_shape = {}
+    for key, (x, W, count) in shapes.items():
+        sb = lq.InitBuffers(x.rows, x.cols, cfg)
+        lq.loftq_init(W, cfg, buffers=sb)
+        torch.cuda.synchronize()
+        lq.profile_enable(True)
+        lq.loftq_init(W, cfg, buffers=sb)
+        torch.cuda.synchronize()
+        lq.profile_enable(False)
+        per_shape[key] = (x, count, {k: v[0] for k, v in lq.profile_collect().items()})
+        del sb
+
+    def bytes_per_step(name):
+        tot = 0
+        for (rows, cols), (x, count, launches) in per_shape.items():
+            b = algorithmic_bytes(name, x, rows, cols)
+            if b is None:
+                return None
+            tot += count * launches.get(name, 0) * b
+        return tot
+
+    # profiled pass: HIP events around every library launch, the same steps on the same streams
     lq.profile_enable(True)
-    for _ in range(args.steps):
-        lq.loftq_init(Wd, cfg, buffers=bufs)
+    for _ in range(steps):
+        step()
     torch.cuda.synchronize()
     lq.profile_enable(False)
     prof = lq.profile_collect()
-    kernels = {}
-    for name, (launches, total_ms) in sorted(prof.items(), key=lambda kv: -kv[1][1]):
-        avg_us = 1e3 * total_ms / launches
-        entry = {"launches_per_step": launches / args.steps, "avg_us": round(avg_us, 3),
-                 "share": round(total_ms / sum(v[1] for v in prof.values()), 4)}
-        nbytes = algorithmic_bytes(name, w, w.rows, w.cols)
-        if nbytes is not None:
-            entry["GBps"] = round(nbytes / (avg_us * 1e-6) / 1e9, 1)
-        kernels[name] = entry
+    kernels = kernel_table(prof, steps, bytes_per_step)
+    for name, e in kernels.items():   # every launch of the batch accounted for by the per-shape counts
+        want = sum(c * l.get(name, 0) for _, c, l in per_shape.values())
+        if want and abs(e["launches_per_step"] - want) > 1e-9:
+            e["launch_count_mismatch"] = want
     streaming = [k for k in kernels if "GBps" in kernels[k]]
     dom = max(streaming, key=lambda k: kernels[k]["share"])
     achieved = kernels[dom]["GBps"]
     roofline = {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(w.name, dom),
-                "bytes_per_launch": algorithmic_bytes(dom, w, w.rows, w.cols),
-                "avg_us": kernels[dom]["avg_us"]}
+                "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "traffic": measured_traffic(wname, dom),
+                "bytes_per_launch": kernels[dom]["bytes_per_launch"], "avg_us": kernels[dom]["avg_us"]}
+    if batch:
+        roofline["note"] = (f"durations measured with the batch's {args.streams} streams running at once, so a "
+                            "launch shares the device with the other streams' kernels")
     qname = "nf4_quantize" if "nf4_quantize" in kernels else None
     nf4 = None
     if qname:
@@ -233,6 +330,11 @@ def main():
                                      "avg_us": kernels["nf4_quantize_fused"]["avg_us"]}
 
     obj = bufs.objective.cpu().numpy().tolist()
+    Wd = Ws[0]
+    if batch:   # the extras below run on the batch's first matrix
+        del runner, shapes
+        Ws = Ws[:1]
+        torch.cuda.empty_cache()
 
     # adapter merge (the PEFT guide's merge_adapter on NF4: dequantize, add B A,
     # quantize again) of this init's own B, A into its Q, into separate buffers
@@ -248,7 +350,7 @@ def main():
             lq.loftq_nf4_merge(bufs.packed, (w.rows, w.cols), bufs.B, bufs.A, 1.0, **scales, double_quant=dq, out=mout)
         torch.cuda.synchronize()
         lq.profile_enable(True)
-        for _ in range(args.steps):
+        for _ in range(steps):
             lq.loftq_nf4_merge(bufs.packed, (w.rows, w.cols), bufs.B, bufs.A, 1.0, **scales, double_quant=dq, out=mout)
         torch.cuda.synchronize()
         lq.profile_enable(False)
@@ -257,7 +359,7 @@ def main():
             launches, total_ms = mprof["nf4_merge"]
             avg_us = 1e3 * total_ms / launches
             gb = algorithmic_bytes("nf4_merge", w, w.rows, w.cols) / (avg_us * 1e-6) / 1e9
-            step_us = 1e3 * sum(v[1] for v in mprof.values()) / args.steps
+            step_us = 1e3 * sum(v[1] for v in mprof.values()) / steps
             valu = measured_valu(w.name, "nf4_merge")
             merge = {"kernel": "nf4_merge", "bound": "alu", "avg_us": round(avg_us, 3),
                      "achieved": None if valu is None else round(valu / (avg_us * 1e-6) / 1e9, 1),
@@ -277,17 +379,17 @@ def main():
                                  power_iters=w.power_iters - 1, double_quant=int(w.double_quant), exact_svd=0,
                                  seed=w.sketch_seed, warm_start=1)
         wbufs = lq.InitBuffers(w.rows, w.cols, wcfg)
-        for _ in range(max(args.warmup, 1)):
+        for _ in range(max(warmup, 1)):
             lq.loftq_init(Wd, wcfg, buffers=wbufs)
         torch.cuda.synchronize()
         t1 = time.perf_counter()
-        for _ in range(args.steps):
+        for _ in range(steps):
             lq.loftq_init(Wd, wcfg, buffers=wbufs)
         torch.cuda.synchronize()
         wel = time.perf_counter() - t1
         wobj = wbufs.objective.cpu().numpy().tolist()
-        warm = {"power_iters": w.power_iters - 1, "value": w.numel * args.steps / wel, "unit": "elements/s",
-                "ms_per_step": 1e3 * wel / args.steps, "final_objective": wobj[-1],
+        warm = {"power_iters": w.power_iters - 1, "value": w.numel * steps / wel, "unit": "elements/s",
+                "ms_per_step": 1e3 * wel / steps, "final_objective": wobj[-1],
                 "cold_final_objective": obj[-1], "cold_power_iters": w.power_iters}
         del wbufs
 
@@ -301,13 +403,13 @@ def main():
         lq.loftq_init(Wd, bcfg, buffers=bbufs)
         torch.cuda.synchronize()
         t1 = time.perf_counter()
-        for _ in range(args.steps):
+        for _ in range(steps):
             lq.loftq_init(Wd, bcfg, buffers=bbufs)
         torch.cuda.synchronize()
         bel = time.perf_counter() - t1
         bobj = bbufs.objective.cpu().numpy().tolist()
-        lower[f"nf{b}"] = {"value": w.numel * args.steps / bel, "unit": "elements/s",
-                           "ms_per_step": 1e3 * bel / args.steps, "objective_plain": bobj[0],
+        lower[f"nf{b}"] = {"value": w.numel * steps / bel, "unit": "elements/s",
+                           "ms_per_step": 1e3 * bel / steps, "objective_plain": bobj[0],
                            "objective_final": bobj[-1]}
         del bbufs
 
@@ -327,7 +429,7 @@ def main():
 
             def call():
                 lq.loftq_qlora_forward(X, bufs.packed, (w.rows, w.cols), **scales, B=bufs.B, A=bufs.A, out=Y, ws=ws)
-            reps = 10 * args.steps
+            reps = 10 * steps
             for _ in range(3):
                 call()
             torch.cuda.synchronize()
@@ -366,19 +468,26 @@ def main():
             fwd[label] = ent
             del X, Y, ws
 
+    config = {"workload": wname, "matrices": len(specs), "elements": total_elems, "storage": w.dtype,
+              "rank": w.rank, "iterative_steps": w.iterative_steps, "oversample": w.oversample,
+              "power_iters": w.power_iters, "double_quant": w.double_quant, "blocksize": 64, "dq_blocksize": 256}
+    if batch:
+        config.update(shapes={f"{r}x{c}": n for (r, c), (_, n, _) in per_shape.items()}, streams=args.streams,
+                      call="loftq_init_batch", extras_on=specs[0].name)
+    else:
+        config.update(rows=w.rows, cols=w.cols, call="loftq_init")
     line = {
-        "metric": METRIC, "value": value, "unit": "elements/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak",
+        "metric": METRIC, "value": value, "unit": "elements/s", "n_gpus": 1, "steps": steps,
+        "warmup": warmup, "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "f32", "data": "synthetic",
-        "config": {"workload": w.name, "rows": w.rows, "cols": w.cols, "storage": w.dtype, "rank": w.rank,
-                   "iterative_steps": w.iterative_steps, "oversample": w.oversample, "power_iters": w.power_iters,
-                   "double_quant": w.double_quant, "blocksize": 64, "dq_blocksize": 256},
+        "config": config, "input_generation_s": round(t_gen, 1),
         "roofline": roofline, "nf4_quantize": nf4, "nf4_merge": merge, "warm_start_variant": warm,
         "lower_bit": lower, "qlora_forward": fwd,
         "objective": obj, "kernels": kernels,
     }
     if not args.skip_cpu:
-        line["cpu_baseline"] = cpu_baseline(w, args.cpu_rows)
+        rows = args.cpu_rows if args.cpu_rows is not None else (1024 if batch else 4096)
+        line["cpu_baseline"] = cpu_baseline(specs[:7] if batch else specs, rows, extrapolated=batch)
     print(json.dumps(line), flush=True)
 
 

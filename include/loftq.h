@@ -70,6 +70,13 @@ typedef struct {
                                the last oversample columns of the fresh sketch] (a variant, to be
                                paired with fewer power_iters; ignored with exact_svd) */
   uint64_t seed;            /* sketch seed (loftq_config seed, default 42) */
+  int32_t init_from_BA;     /* 0: start from Delta_0 = 0.  k >= 1: resume after k completed
+                               alternations (the LoftQ blog, §2.3, computes the initialisation once
+                               and keeps the result): B and A hold B_k, A_k on entry (with
+                               warm_start also sigma = sigma_k), and the call runs alternations
+                               k+1 .. k+T with the sketch counter continuing at k+1, so k
+                               alternations followed by a resumed call of T give the same results
+                               as one call of k+T.  Requires T >= 1. */
 } loftq_config_t;
 
 /* Quantization step ("LoftQ...", §2.3: quantize the residual W - Delta; the
@@ -177,6 +184,14 @@ size_t loftq_qlora_forward_workspace_bytes(int64_t n_tok, int32_t r);
  * l <= 80, r <= 64) and power_iters rounds; the sketch is `omega` (cols x l fp32) or, if
  * NULL, the +-1 SplitMix64 sketch of (seed, t).  Outputs B = U_r S_r^{1/2},
  * A = S_r^{1/2} V_r^T, sigma = S_r (descending).
+ * Accuracy of the randomized path: the sketch panel is re-orthonormalised by one
+ * Cholesky-QR pass per product (fp64 Gram and factor, fp32 panel), which holds
+ * the top-r singular values to ~1e-6 relative of the same algorithm in exact
+ * arithmetic while sigma_1 / sigma_l <= 1e3 (tested at that edge); beyond about
+ * 1e4 the fp32 panel loses the weak directions and the error grows quickly.
+ * Quantization residuals are far inside this range (nearly flat spectra).
+ * An E of rank below l is supported: directions whose Cholesky pivot falls
+ * under 1e-13 of the largest are dropped and their singular values come out 0.
  *   E      [device] rows x cols fp32
  *   B, A   [device] rows x r, r x cols fp32 out
  *   sigma  [device] r fp32 out
@@ -193,18 +208,63 @@ size_t loftq_lowrank_svd_workspace_bytes(int64_t rows, int64_t cols, int32_t r, 
  * (B_t, A_t) = rank-r SVD of W - deq(Q_t).  Outputs the final Q_T (packed,
  * absmax, and qabsmax/dq_scale when double_quant), B_T, A_T, sigma of
  * alternation T, and objective[t] = ||W - deq(Q_t) - B_t A_t||_F / ||W||_F for
- * t = 0..T (objective[0] = plain NF4 error ||W - deq(Q_1)|| / ||W||).
+ * t = 1..T; objective[0] = ||W - deq(Q_first)|| / ||W|| for the call's first
+ * quantization (the plain NF4 error when not resuming).  With cfg->init_from_BA
+ * = k the alternations are numbered k+1 .. k+T and B, A (sigma) are read first.
  *   cfg               [host]
  *   packed, absmax    [device] as loftq_nf4_quantize
  *   qabsmax, dq_scale [device] as loftq_double_quant (ignored if !double_quant)
- *   B, A, sigma       [device] as loftq_lowrank_svd
+ *   B, A, sigma       [device] as loftq_lowrank_svd (also inputs when resuming)
  *   objective         [device] T+1 doubles out
- *   ws                [device] loftq_workspace_bytes(rows, cols, cfg) bytes */
+ *   ws                [device] loftq_workspace_bytes(rows, cols, cfg) bytes
+ * The randomized SVD's accuracy limit of loftq_lowrank_svd applies per alternation. */
 loftq_status_t loftq_init(const void* W, loftq_dtype_t wdt, int64_t rows, int64_t cols,
                           const loftq_config_t* cfg, uint8_t* packed, float* absmax, int8_t* qabsmax,
                           float* dq_scale, float* B, float* A, double* objective, float* sigma, void* ws,
                           size_t ws_bytes, void* stream);
 size_t loftq_workspace_bytes(int64_t rows, int64_t cols, const loftq_config_t* cfg);
+
+/* One matrix of a batched initialisation: the device buffers loftq_init takes,
+ * with the same meaning, shapes and alignment. */
+typedef struct {
+  const void* W;
+  int64_t rows, cols;
+  uint8_t* packed;
+  float* absmax;
+  int8_t* qabsmax;    /* and dq_scale: NULL unless cfg->double_quant */
+  float* dq_scale;
+  float* B;
+  float* A;
+  double* objective;  /* T+1 doubles */
+  float* sigma;
+} loftq_matrix_t;
+
+/* LoftQ initialisation of every targeted linear layer of a model, one call for
+ * the batch (PEFT guide "LoftQ 初始化": LoftQ applies to each linear layer the
+ * LoRA config targets, all-linear advised; the LoftQ blog, §3.2, targets the
+ * q/k/v/o/gate/up/down projections).  Each matrix gets exactly the results of
+ * loftq_init with the same cfg (the same kernels; bit for bit).  The matrices
+ * are spread over nstreams streams, longest first, each to the stream with the
+ * least work so far; a stream runs its matrices one after another in its own
+ * workspace, so one matrix's single-workgroup solves overlap another's streaming
+ * kernels.  Nothing is synchronised: outputs are valid once every stream is.
+ *   mats      [host] count matrices; their output buffers must not overlap each
+ *             other (W may be shared)
+ *   wdt       storage type of every W
+ *   cfg       [host] one configuration for all (rank, T, double quant, ...)
+ *   nstreams  1 .. 16; all streams at the default priority
+ *   streams   [host] nstreams hipStream_t, or NULL (then every matrix runs on the
+ *             null stream, one after another)
+ *   ws        [host] nstreams distinct device workspaces of ws_bytes each, ws_bytes
+ *             >= loftq_batch_workspace_bytes(mats, count, cfg)
+ * Every matrix is validated before anything is enqueued; any error from
+ * loftq_init's list (for any matrix) returns that status and enqueues nothing. */
+loftq_status_t loftq_init_batch(const loftq_matrix_t* mats, int32_t count, loftq_dtype_t wdt,
+                                const loftq_config_t* cfg, int32_t nstreams, void* const* streams,
+                                void* const* ws, size_t ws_bytes);
+/* Bytes of one stream's workspace for loftq_init_batch (the largest loftq_workspace_bytes
+ * over the batch); 0 if any matrix's shape or cfg is invalid. */
+size_t loftq_batch_workspace_bytes(const loftq_matrix_t* mats, int32_t count, const loftq_config_t* cfg);
 
 /* Fills cfg with the defaults (bits 4, T 5, r 16, blocksize 64, double quant on,
  * dq_blocksize 256, p 8, q 2, randomized, seed 42). [host] */

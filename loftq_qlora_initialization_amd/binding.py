@@ -32,7 +32,7 @@ LOFTQ_F32, LOFTQ_BF16 = 0, 1
 STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported configuration", 3: "workspace too small",
           4: "HIP runtime error"}
 
-EXPORTS = ["loftq_nf4_quantize", "loftq_double_quant", "loftq_nf4_dequantize", "loftq_nf4_merge",
+EXPORTS = ["loftq_init_batch", "loftq_batch_workspace_bytes", "loftq_nf4_quantize", "loftq_double_quant", "loftq_nf4_dequantize", "loftq_nf4_merge",
            "loftq_nf4_unmerge", "loftq_lowrank_svd",
            "loftq_lowrank_svd_workspace_bytes", "loftq_init", "loftq_workspace_bytes", "loftq_default_config",
            "loftq_status_string", "loftq_nf4_codebook", "loftq_nf_codebook", "loftq_qlora_forward",
@@ -43,10 +43,15 @@ class LoftqConfig(ctypes.Structure):
     _fields_ = [("bits", ctypes.c_int32), ("iterative_steps", ctypes.c_int32), ("rank", ctypes.c_int32),
                 ("blocksize", ctypes.c_int32), ("double_quant", ctypes.c_int32), ("dq_blocksize", ctypes.c_int32),
                 ("oversample", ctypes.c_int32), ("power_iters", ctypes.c_int32), ("exact_svd", ctypes.c_int32),
-                ("warm_start", ctypes.c_int32), ("seed", ctypes.c_uint64)]
+                ("warm_start", ctypes.c_int32), ("seed", ctypes.c_uint64), ("init_from_BA", ctypes.c_int32)]
 
 
 _P, _I64, _I32, _U64, _SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_uint64, ctypes.c_size_t
+
+
+class LoftqMatrix(ctypes.Structure):
+    _fields_ = [("W", _P), ("rows", _I64), ("cols", _I64), ("packed", _P), ("absmax", _P), ("qabsmax", _P),
+                ("dq_scale", _P), ("B", _P), ("A", _P), ("objective", _P), ("sigma", _P)]
 
 
 def _sig(name, res, args):
@@ -74,6 +79,10 @@ _c_init = _sig("loftq_init", ctypes.c_int,
                [_P, ctypes.c_int, _I64, _I64, ctypes.POINTER(LoftqConfig), _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ,
                 _P])
 _c_init_ws = _sig("loftq_workspace_bytes", _SZ, [_I64, _I64, ctypes.POINTER(LoftqConfig)])
+_c_batch = _sig("loftq_init_batch", ctypes.c_int,
+                [ctypes.POINTER(LoftqMatrix), _I32, ctypes.c_int, ctypes.POINTER(LoftqConfig), _I32,
+                 ctypes.POINTER(_P), ctypes.POINTER(_P), _SZ])
+_c_batch_ws = _sig("loftq_batch_workspace_bytes", _SZ, [ctypes.POINTER(LoftqMatrix), _I32, ctypes.POINTER(LoftqConfig)])
 _c_defaults = _sig("loftq_default_config", None, [ctypes.POINTER(LoftqConfig)])
 _c_status = _sig("loftq_status_string", ctypes.c_char_p, [ctypes.c_int])
 _c_codebook = _sig("loftq_nf4_codebook", None, [ctypes.POINTER(ctypes.c_float)])
@@ -286,7 +295,7 @@ def workspace_bytes(rows: int, cols: int, cfg: LoftqConfig) -> int:
 class InitBuffers:
     """Caller-owned outputs and workspace for repeated loftq_init calls on one shape."""
 
-    def __init__(self, rows: int, cols: int, cfg: LoftqConfig, device="cuda"):
+    def __init__(self, rows: int, cols: int, cfg: LoftqConfig, device="cuda", workspace: bool = True):
         n = rows * cols
         nb = (n + 63) // 64
         self.cfg = cfg
@@ -298,8 +307,16 @@ class InitBuffers:
         self.A = torch.empty((cfg.rank, cols), dtype=torch.float32, device=device)
         self.sigma = torch.empty(cfg.rank, dtype=torch.float32, device=device)
         self.objective = torch.empty(cfg.iterative_steps + 1, dtype=torch.float64, device=device)
-        self.ws_bytes = workspace_bytes(rows, cols, cfg)
-        self.ws = torch.empty(max(self.ws_bytes, 16), dtype=torch.uint8, device=device)
+        self.ws_bytes = workspace_bytes(rows, cols, cfg) if workspace else 0
+        self.ws = torch.empty(max(self.ws_bytes, 16), dtype=torch.uint8, device=device) if workspace else None
+
+    def matrix(self, W: torch.Tensor) -> LoftqMatrix:
+        """This buffer set as one loftq_matrix_t of a batch, for weight W."""
+        rows, cols = W.shape
+        dq = bool(self.cfg.double_quant)
+        return LoftqMatrix(W.data_ptr(), rows, cols, self.packed.data_ptr(), self.absmax.data_ptr(),
+                           self.qabsmax.data_ptr() if dq else None, self.dq_scale.data_ptr() if dq else None,
+                           self.B.data_ptr(), self.A.data_ptr(), self.objective.data_ptr(), self.sigma.data_ptr())
 
 
 def loftq_init(W: torch.Tensor, cfg: Optional[LoftqConfig] = None, buffers: Optional[InitBuffers] = None,
@@ -319,6 +336,50 @@ def loftq_init(W: torch.Tensor, cfg: Optional[LoftqConfig] = None, buffers: Opti
     if cfg.double_quant:
         out.update(qabsmax=bufs.qabsmax, dq_scale=bufs.dq_scale)
     return out
+
+
+class BatchRunner:
+    """Caller-owned outputs, per-stream workspaces and streams for repeated loftq_init_batch
+    calls over one list of weights (all of one storage dtype)."""
+
+    def __init__(self, Ws, cfg: LoftqConfig, nstreams: int = 4, device="cuda"):
+        self.Ws = list(Ws)
+        for W in self.Ws:
+            _contig(W, "W")
+        self.wdt = _wdtype(self.Ws[0])
+        if any(_wdtype(W) != self.wdt for W in self.Ws):
+            raise TypeError("every W of a batch must have the same dtype")
+        self.cfg = cfg
+        self.buffers = [InitBuffers(W.shape[0], W.shape[1], cfg, device, workspace=False) for W in self.Ws]
+        n = len(self.Ws)
+        self.mats = (LoftqMatrix * n)(*[b.matrix(W) for b, W in zip(self.buffers, self.Ws)])
+        self.ws_bytes = int(_c_batch_ws(self.mats, n, ctypes.byref(cfg)))
+        if self.ws_bytes == 0:
+            raise LoftqError("loftq_batch_workspace_bytes", 1)
+        self.nstreams = int(nstreams)
+        # streams at the default priority
+        self.streams = [torch.cuda.Stream(device=device) for _ in range(self.nstreams)]
+        self.ws = [torch.empty(self.ws_bytes, dtype=torch.uint8, device=device) for _ in range(self.nstreams)]
+        self._c_streams = (_P * self.nstreams)(*[s.cuda_stream for s in self.streams])
+        self._c_ws = (_P * self.nstreams)(*[w.data_ptr() for w in self.ws])
+
+    def run(self):
+        """Enqueue the batch; the current stream then waits for every batch stream."""
+        cur = torch.cuda.current_stream()
+        for s in self.streams:
+            s.wait_stream(cur)
+        _check("loftq_init_batch", _c_batch(self.mats, len(self.Ws), self.wdt, ctypes.byref(self.cfg),
+                                            self.nstreams, self._c_streams, self._c_ws, self.ws_bytes))
+        for s in self.streams:
+            cur.wait_stream(s)
+        return self.buffers
+
+
+def loftq_init_batch(Ws, cfg: Optional[LoftqConfig] = None, nstreams: int = 4, **overrides):
+    """LoftQ initialisation of a list of weights in one batched call; returns one InitBuffers per weight."""
+    if cfg is None:
+        cfg = default_config(**overrides)
+    return BatchRunner(Ws, cfg, nstreams).run()
 
 
 def profile_enable(on: bool = True) -> None:

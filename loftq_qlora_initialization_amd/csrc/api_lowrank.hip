@@ -1,4 +1,7 @@
 // C-ABI entry points for the low-rank step and the whole alternating initialisation.
+#include <algorithm>
+#include <vector>
+
 #include "lowrank.h"
 
 namespace loftq {
@@ -24,6 +27,8 @@ loftq_status_t check_svd_shape(int64_t rows, int64_t cols, int32_t r, int32_t ov
 
 // Sketches drawn per launch: alternations t .. t + kSketchBatch - 1 at once.
 constexpr int kSketchBatch = 8;
+// Streams a batched call may spread its matrices over.
+constexpr int kMaxBatchStreams = 16;
 
 struct InitPlan {
   SvdPlan svd;
@@ -56,7 +61,111 @@ loftq_status_t check_config(int64_t rows, int64_t cols, const loftq_config_t* c)
   if (c->iterative_steps < 0 || c->iterative_steps > 1000 || c->power_iters < 0 || c->power_iters > 64 ||
       (c->warm_start != 0 && c->warm_start != 1) || (c->double_quant != 0 && c->double_quant != 1))
     return LOFTQ_ERR_INVALID_ARG;
+  // resume: k completed alternations (k + T stays within the sketch counter's range)
+  if (c->init_from_BA < 0 || c->init_from_BA > 1000000 || (c->init_from_BA > 0 && c->iterative_steps == 0))
+    return LOFTQ_ERR_INVALID_ARG;
   return check_svd_shape(rows, cols, c->rank, c->oversample, c->exact_svd);
+}
+
+// The device buffers of one initialisation (see loftq_init).
+struct InitArgs {
+  const void* W;
+  int64_t rows, cols;
+  uint8_t* packed;
+  float* absmax;
+  int8_t* qabsmax;
+  float* dq_scale;
+  float* B;
+  float* A;
+  double* objective;
+  float* sigma;
+};
+
+loftq_status_t check_init(const InitArgs& a, loftq_dtype_t wdt, const loftq_config_t* cfg, const void* ws,
+                          size_t ws_bytes) {
+  loftq_status_t st = check_config(a.rows, a.cols, cfg);
+  if (st != LOFTQ_OK) return st;
+  if (wdt != LOFTQ_F32 && wdt != LOFTQ_BF16) return LOFTQ_ERR_INVALID_ARG;
+  if (!nf_tables(cfg->bits).valid) return LOFTQ_ERR_UNSUPPORTED;
+  const bool dq = cfg->double_quant != 0;
+  if (!a.W || !a.packed || !a.absmax || !a.B || !a.A || !a.objective || !a.sigma || !ws) return LOFTQ_ERR_INVALID_ARG;
+  if (dq && (!a.qabsmax || !a.dq_scale)) return LOFTQ_ERR_INVALID_ARG;
+  const void* ptrs[] = {a.W, a.packed, a.absmax, a.B, a.A, a.objective, a.sigma, ws};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return LOFTQ_ERR_INVALID_ARG;
+  if (dq && (!aligned16(a.qabsmax) || !aligned16(a.dq_scale))) return LOFTQ_ERR_INVALID_ARG;
+  if (ws_bytes < static_cast<size_t>(make_init_plan(a.rows, a.cols, *cfg).bytes)) return LOFTQ_ERR_WORKSPACE;
+  return LOFTQ_OK;
+}
+
+// The alternation loop of one validated initialisation, enqueued on stream s.
+hipError_t run_init(const InitArgs& a, loftq_dtype_t wdt, const loftq_config_t& c, char* w, hipStream_t s) {
+  const loftq_config_t* cfg = &c;
+  const void* W = a.W;
+  const int64_t rows = a.rows, cols = a.cols;
+  uint8_t* packed = a.packed;
+  float* absmax = a.absmax;
+  int8_t* qabsmax = a.qabsmax;
+  float* dq_scale = a.dq_scale;
+  float* B = a.B;
+  float* A = a.A;
+  double* objective = a.objective;
+  float* sigma = a.sigma;
+  const bool dq = cfg->double_quant != 0;
+  const InitPlan pl = make_init_plan(rows, cols, *cfg);
+  float* E = reinterpret_cast<float*>(w + pl.off_e);
+  double* eparts = reinterpret_cast<double*>(w + pl.off_parts);
+  double* wparts = reinterpret_cast<double*>(w + pl.off_wparts);
+  char* svd_ws = w + pl.off_svd;
+  const int64_t n = rows * cols;
+  const int r = cfg->rank;
+  const int T = cfg->iterative_steps;
+  float* sketches = reinterpret_cast<float*>(w + pl.off_sketch);
+  // the first dequant also leaves the partials of ||W||^2 (W is read there anyway)
+  auto quant_step = [&](const float* Bp, const float* Ap, bool first) -> hipError_t {
+    hipError_t x = launch_nf4_quantize(W, wdt, rows, cols, Bp, Ap, r, packed, absmax, s, cfg->bits);
+    // the double quant of the absmax is derived (and written) inside the dequant
+    if (x == hipSuccess)
+      x = launch_nf4_dequantize(packed, absmax, nullptr, nullptr, n, cfg->dq_blocksize, W, wdt, E, eparts,
+                                first ? wparts : nullptr, nullptr, s, dq ? qabsmax : nullptr, dq ? dq_scale : nullptr,
+                                cfg->bits);
+    return x;
+  };
+  hipError_t e = hipSuccess;
+  if (T == 0) {
+    const ObjectiveArgs obj0{eparts, pl.nparts, wparts, pl.nparts, objective, nullptr};
+    if (e == hipSuccess) e = quant_step(nullptr, nullptr, true);
+    if (e == hipSuccess) e = run_objective(obj0, s);
+    if (e == hipSuccess) e = run_fill(B, rows * r, 0.f, s);
+    if (e == hipSuccess) e = run_fill(A, static_cast<int64_t>(r) * cols, 0.f, s);
+    if (e == hipSuccess) e = run_fill(sigma, r, 0.f, s);
+    return e;
+  }
+  // alternations k0+1 .. k0+T; with k0 > 0 (resume) the first one starts from the caller's B, A
+  const int k0 = cfg->init_from_BA;
+  for (int i = 1; i <= T && e == hipSuccess; ++i) {
+    const int t = k0 + i;   // the alternation's number: its sketch is that of (seed, t)
+    const bool fresh = (t == 1);
+    e = quant_step(fresh ? nullptr : B, fresh ? nullptr : A, i == 1);
+    // the call's first solve also writes objective[0] (the error of its first quantization)
+    const ObjectiveArgs objt{eparts, pl.nparts, wparts, pl.nparts, objective + i, i == 1 ? objective : nullptr};
+    const float* om = nullptr;
+    if (pl.sketch_floats > 0) {
+      const int slot = (i - 1) % kSketchBatch;
+      if (slot == 0 && e == hipSuccess) {
+        const int count = (T - i + 1) < kSketchBatch ? (T - i + 1) : kSketchBatch;
+        e = run_sketch(cfg->seed, t, count, cols, pl.svd.l, pl.svd.nt, pl.svd.k_pad, sketches, s);
+      }
+      om = sketches + slot * pl.sketch_floats;
+      // warm start: from alternation 2 on, the first r columns come from the
+      // previous alternation's A and sigma (still in their buffers here)
+      if (cfg->warm_start != 0 && t > 1 && e == hipSuccess)
+        e = run_warm_columns(A, sigma, cols, r, pl.svd.nt, sketches + slot * pl.sketch_floats, s);
+    }
+    if (e == hipSuccess)
+      e = run_lowrank(E, pl.svd, cfg->power_iters, nullptr, om, cfg->seed, t, B, A, sigma, svd_ws, objt, s);
+  }
+  return e;
 }
 
 }  // namespace
@@ -96,72 +205,62 @@ size_t loftq_workspace_bytes(int64_t rows, int64_t cols, const loftq_config_t* c
 loftq_status_t loftq_init(const void* W, loftq_dtype_t wdt, int64_t rows, int64_t cols, const loftq_config_t* cfg,
                           uint8_t* packed, float* absmax, int8_t* qabsmax, float* dq_scale, float* B, float* A,
                           double* objective, float* sigma, void* ws, size_t ws_bytes, void* stream) {
-  loftq_status_t st = check_config(rows, cols, cfg);
+  const InitArgs a{W, rows, cols, packed, absmax, qabsmax, dq_scale, B, A, objective, sigma};
+  loftq_status_t st = check_init(a, wdt, cfg, ws, ws_bytes);
   if (st != LOFTQ_OK) return st;
-  if (wdt != LOFTQ_F32 && wdt != LOFTQ_BF16) return LOFTQ_ERR_INVALID_ARG;
-  if (!nf_tables(cfg->bits).valid) return LOFTQ_ERR_UNSUPPORTED;
-  const bool dq = cfg->double_quant != 0;
-  if (!W || !packed || !absmax || !B || !A || !objective || !sigma || !ws) return LOFTQ_ERR_INVALID_ARG;
-  if (dq && (!qabsmax || !dq_scale)) return LOFTQ_ERR_INVALID_ARG;
-  const void* ptrs[] = {W, packed, absmax, B, A, objective, sigma, ws};
-  for (const void* p : ptrs)
-    if (!aligned16(p)) return LOFTQ_ERR_INVALID_ARG;
-  if (dq && (!aligned16(qabsmax) || !aligned16(dq_scale))) return LOFTQ_ERR_INVALID_ARG;
-  const InitPlan pl = make_init_plan(rows, cols, *cfg);
-  if (ws_bytes < static_cast<size_t>(pl.bytes)) return LOFTQ_ERR_WORKSPACE;
+  return from_hip(run_init(a, wdt, *cfg, static_cast<char*>(ws), static_cast<hipStream_t>(stream)));
+}
 
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  char* w = static_cast<char*>(ws);
-  float* E = reinterpret_cast<float*>(w + pl.off_e);
-  double* eparts = reinterpret_cast<double*>(w + pl.off_parts);
-  double* wparts = reinterpret_cast<double*>(w + pl.off_wparts);
-  char* svd_ws = w + pl.off_svd;
-  const int64_t n = rows * cols;
-  const int r = cfg->rank;
-  const int T = cfg->iterative_steps;
-
-  float* sketches = reinterpret_cast<float*>(w + pl.off_sketch);
-  // the first dequant also leaves the partials of ||W||^2 (W is read there anyway)
-  auto quant_step = [&](const float* Bp, const float* Ap, bool first) -> hipError_t {
-    hipError_t x = launch_nf4_quantize(W, wdt, rows, cols, Bp, Ap, r, packed, absmax, s, cfg->bits);
-    // the double quant of the absmax is derived (and written) inside the dequant
-    if (x == hipSuccess)
-      x = launch_nf4_dequantize(packed, absmax, nullptr, nullptr, n, cfg->dq_blocksize, W, wdt, E, eparts,
-                                first ? wparts : nullptr, nullptr, s, dq ? qabsmax : nullptr, dq ? dq_scale : nullptr,
-                                cfg->bits);
-    return x;
-  };
-  hipError_t e = hipSuccess;
-  if (T == 0) {
-    const ObjectiveArgs obj0{eparts, pl.nparts, wparts, pl.nparts, objective, nullptr};
-    if (e == hipSuccess) e = quant_step(nullptr, nullptr, true);
-    if (e == hipSuccess) e = run_objective(obj0, s);
-    if (e == hipSuccess) e = run_fill(B, rows * r, 0.f, s);
-    if (e == hipSuccess) e = run_fill(A, static_cast<int64_t>(r) * cols, 0.f, s);
-    if (e == hipSuccess) e = run_fill(sigma, r, 0.f, s);
-    return from_hip(e);
+size_t loftq_batch_workspace_bytes(const loftq_matrix_t* mats, int32_t count, const loftq_config_t* cfg) {
+  if (mats == nullptr || count < 1 || cfg == nullptr) return 0;
+  size_t need = 0;
+  for (int32_t i = 0; i < count; ++i) {
+    if (check_config(mats[i].rows, mats[i].cols, cfg) != LOFTQ_OK) return 0;
+    const size_t b = static_cast<size_t>(make_init_plan(mats[i].rows, mats[i].cols, *cfg).bytes);
+    need = b > need ? b : need;
   }
-  for (int t = 1; t <= T && e == hipSuccess; ++t) {
-    e = quant_step(t == 1 ? nullptr : B, t == 1 ? nullptr : A, t == 1);
-    // alternation 1's solve also writes objective[0] (the error of plain NF4)
-    const ObjectiveArgs objt{eparts, pl.nparts, wparts, pl.nparts, objective + t, t == 1 ? objective : nullptr};
-    const float* om = nullptr;
-    if (pl.sketch_floats > 0) {
-      const int slot = (t - 1) % kSketchBatch;
-      if (slot == 0 && e == hipSuccess) {
-        const int count = (T - t + 1) < kSketchBatch ? (T - t + 1) : kSketchBatch;
-        e = run_sketch(cfg->seed, t, count, cols, pl.svd.l, pl.svd.nt, pl.svd.k_pad, sketches, s);
-      }
-      om = sketches + slot * pl.sketch_floats;
-      // warm start: from alternation 2 on, the first r columns come from the
-      // previous alternation's A and sigma (still in their buffers here)
-      if (cfg->warm_start != 0 && t > 1 && e == hipSuccess)
-        e = run_warm_columns(A, sigma, cols, r, pl.svd.nt, sketches + slot * pl.sketch_floats, s);
+  return need;
+}
+
+loftq_status_t loftq_init_batch(const loftq_matrix_t* mats, int32_t count, loftq_dtype_t wdt,
+                                const loftq_config_t* cfg, int32_t nstreams, void* const* streams,
+                                void* const* ws, size_t ws_bytes) {
+  if (mats == nullptr || count < 0 || cfg == nullptr) return LOFTQ_ERR_INVALID_ARG;
+  if (count == 0) return LOFTQ_OK;
+  if (nstreams < 1 || nstreams > kMaxBatchStreams || ws == nullptr) return LOFTQ_ERR_INVALID_ARG;
+  for (int32_t j = 0; j < nstreams; ++j)
+    for (int32_t i = 0; i < j; ++i)
+      if (ws[i] == ws[j]) return LOFTQ_ERR_INVALID_ARG;   // each stream needs a workspace of its own
+  // every matrix is validated (with every stream's workspace) before anything is enqueued
+  for (int32_t i = 0; i < count; ++i) {
+    const InitArgs a{mats[i].W, mats[i].rows, mats[i].cols, mats[i].packed, mats[i].absmax, mats[i].qabsmax,
+                     mats[i].dq_scale, mats[i].B, mats[i].A, mats[i].objective, mats[i].sigma};
+    for (int32_t j = 0; j < nstreams; ++j) {
+      const loftq_status_t st = check_init(a, wdt, cfg, ws[j], ws_bytes);
+      if (st != LOFTQ_OK) return st;
     }
-    if (e == hipSuccess)
-      e = run_lowrank(E, pl.svd, cfg->power_iters, nullptr, om, cfg->seed, t, B, A, sigma, svd_ws, objt, s);
   }
-  return from_hip(e);
+  // longest-processing-time first: matrices by descending element count (ties by index), each to
+  // the stream with the least work so far; the enqueue order follows that list, so the streams
+  // are fed in turn and all start at once
+  std::vector<int32_t> order(count);
+  for (int32_t i = 0; i < count; ++i) order[i] = i;
+  std::stable_sort(order.begin(), order.end(), [&](int32_t x, int32_t y) {
+    return mats[x].rows * mats[x].cols > mats[y].rows * mats[y].cols;
+  });
+  std::vector<int64_t> load(nstreams, 0);
+  for (int32_t idx : order) {
+    int32_t j = 0;
+    for (int32_t c = 1; c < nstreams; ++c)
+      if (load[c] < load[j]) j = c;
+    load[j] += mats[idx].rows * mats[idx].cols;
+    const loftq_matrix_t& m = mats[idx];
+    const InitArgs a{m.W, m.rows, m.cols, m.packed, m.absmax, m.qabsmax, m.dq_scale, m.B, m.A, m.objective, m.sigma};
+    const hipError_t e = run_init(a, wdt, *cfg, static_cast<char*>(ws[j]),
+                                  static_cast<hipStream_t>(streams ? streams[j] : nullptr));
+    if (e != hipSuccess) return from_hip(e);
+  }
+  return LOFTQ_OK;
 }
 
 }  // extern "C"
