@@ -184,12 +184,15 @@ size_t loftq_qlora_forward_workspace_bytes(int64_t n_tok, int32_t r);
  * l <= 80, r <= 64) and power_iters rounds; the sketch is `omega` (cols x l fp32) or, if
  * NULL, the +-1 SplitMix64 sketch of (seed, t).  Outputs B = U_r S_r^{1/2},
  * A = S_r^{1/2} V_r^T, sigma = S_r (descending).
- * Accuracy of the randomized path: the sketch panel is re-orthonormalised by one
- * Cholesky-QR pass per product (fp64 Gram and factor, fp32 panel), which holds
- * the top-r singular values to ~1e-6 relative of the same algorithm in exact
- * arithmetic while sigma_1 / sigma_l <= 1e3 (tested at that edge); beyond about
- * 1e4 the fp32 panel loses the weak directions and the error grows quickly.
- * Quantization residuals are far inside this range (nearly flat spectra).
+ * Accuracy of the randomized path: the products accumulate in fp32 and the range
+ * panel is re-orthonormalised by one Cholesky-QR pass per power iteration (fp64
+ * Gram and factor; E^T Q is never re-orthonormalised), so the weak directions of
+ * the panel lose accuracy as the spectrum steepens.  The top-r singular values
+ * stay within 1e-5 relative of the same algorithm in exact arithmetic while
+ * sigma_1 / sigma_l <= 1e3 for l <= 32 (or power_iters >= 3) and <= 1e2 for
+ * 32 < l <= 80 with power_iters = 2 (all three edges tested); past them the error
+ * grows quickly (about 3e-4 at l = 80, q = 2, ratio 1e3).  Quantization
+ * residuals lie far inside this range (nearly flat spectra).
  * An E of rank below l is supported: directions whose Cholesky pivot falls
  * under 1e-13 of the largest are dropped and their singular values come out 0.
  *   E      [device] rows x cols fp32

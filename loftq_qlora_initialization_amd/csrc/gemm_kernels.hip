@@ -10,17 +10,32 @@
 // end; split-K partials across workgroups are summed in fixed order by
 // reduce_gram.
 //
+// Wide panels (l > 32, where fp32 matrix-core work, not HBM, bounds the fp32
+// products) use the bf16 matrix cores instead, as three products of split
+// operands: each fp32 value x of E and of the panel is split into
+// hi = bf16(x) and lo = bf16(x - hi) (both rounded to nearest even, so
+// |x - hi - lo| <= 2^-18 |x|), and E P is accumulated in fp32 as
+// E_hi P_hi + E_hi P_lo + E_lo P_hi (the dropped E_lo P_lo is below 2^-16 of
+// each term).  v_mfma_f32_16x16x32_bf16 takes K = 32 per instruction, so one K
+// step covers two 16-row blocks of the fragment-order panel; lane (li, g)
+// supplies K index 4 h + s (h = 0, 1; s = 0..3) <-> row 16 h + 4 g + s of the
+// step (its float4 of fragment block h), and E is loaded to match.  E is split in
+// registers as it arrives; the panel comes already split (split_index), written
+// so by the split-K reduction that produces it.
+//
 // Out-of-range rows/columns of E are clamped to valid addresses rather than
 // branched around: the matching rows of the skinny operand are zero (its
 // buffers are zero-padded to the splits' full extent), and garbage output
 // rows/columns are never stored.
 #include "lowrank.h"
 #include "small_solve.h"
+#include "split_bf16.h"
 
 namespace loftq {
 namespace {
 
 typedef float floatx4 __attribute__((ext_vector_type(4)));
+
 
 // v_mfma_f32_16x16x4_f32: lane L supplies A[L%16][L/16] and B[L/16][L%16];
 // lane L receives D[4*(L/16)+v][L%16] in accumulator component v.
@@ -294,20 +309,340 @@ __global__ __launch_bounds__(64 * TnCfg<NT>::WC * TnCfg<NT>::WR) void gemm_tn_ke
         }
 }
 
+// ---------------------------------------------------------------------------
+// Split-bf16 products (see the file comment).  v_mfma_f32_16x16x32_bf16: lane L
+// supplies A[L%16][8(L/16) + e] and B[8(L/16) + e][L%16] (e = 0..7) and receives
+// D[4(L/16) + v][L%16] in element v, the same output layout as the fp32 MFMA.
+__device__ __forceinline__ floatx4 mfma_bf16(const bf16x8& a, const bf16x8& b, floatx4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+template <int NT>
+struct Nn3Cfg {
+  static constexpr int RT = 2;                 // 16-row MFMA tiles per wave
+  static constexpr int D = 4;                  // E register ring depth (K steps of 32)
+  static constexpr int WR = 4;                 // waves along rows, sharing the staged panel
+  static constexpr int PU = NT * 128;          // 16-byte pieces of one K step of the split panel
+  static constexpr int PPT = (PU + 255) / 256; // of them per thread
+};
+template <int NT>
+struct Tn3Cfg {
+  static constexpr int D = 2;
+  static constexpr int WC = 2;                 // waves along columns (64 columns each)
+  static constexpr int WR = 2;                 // waves splitting the workgroup's rows
+};
+
+// gemm_nn on split bf16.  A workgroup of WR waves owns 16 RT WR rows and one
+// K range (its split); wave w owns rows row0 .. row0 + 16 RT.  Every wave needs
+// the same panel step, so the workgroup stages it once per K step in LDS (double
+// buffered, one barrier per step) and the waves read their B operands from there:
+// the panel then costs one L2 read per workgroup instead of one per wave.  E runs
+// through a D-deep register ring of its own.
+template <int NT, bool VEC>
+__global__ __launch_bounds__(64 * Nn3Cfg<NT>::WR) void gemm_nn3_kernel(
+    const float* __restrict__ E, int64_t d, int64_t k, const uint16_t* __restrict__ Xs, int64_t kper,
+    float* __restrict__ part) {
+  using C = Nn3Cfg<NT>;
+  constexpr int LP = 16 * NT, RT = C::RT, D = C::D, WR = C::WR, PU = C::PU, PPT = C::PPT;
+  static_assert(D % 2 == 0 && WR * 64 == 256, "ring parity and the 256-thread panel staging");
+  __shared__ uint4 pan[2][256 * PPT];   // rounded up to whole rounds of 256 pieces (the excess never read)
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int g = lane >> 4, li = lane & 15;
+  const int64_t row0 = (static_cast<int64_t>(blockIdx.x) * WR + w) * 16 * RT;
+  const int64_t kb = static_cast<int64_t>(blockIdx.y) * kper;
+  const int nsteps = static_cast<int>(kper / 32);   // a multiple of D
+  const float* erow[RT];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    int64_t r = row0 + rt * 16 + li;
+    r = r < d ? r : d - 1;
+    erow[rt] = E + r * k;
+  }
+  const uint4* xg = reinterpret_cast<const uint4*>(Xs) + (kb / 32) * PU;
+  floatx4 acc[RT][NT];
+#pragma unroll
+  for (int a = 0; a < RT; ++a)
+#pragma unroll
+    for (int b = 0; b < NT; ++b) acc[a][b] = floatx4{0.f, 0.f, 0.f, 0.f};
+  float4 eb[D][RT][2];
+  static_assert(PPT <= 3, "at most three panel pieces per thread");
+  // Two register sets (a, b, c pieces each) of staged panel steps, as plain
+  // variables: the pieces past PU (PU not a multiple of 256) load a duplicate of
+  // the last piece and land in the LDS padding.
+  uint4 pa0, pb0, pc0, pa1, pb1, pc1;
+  const int i0 = tid < PU ? tid : PU - 1;
+  const int i1 = tid + 256 < PU ? tid + 256 : PU - 1;
+  const int i2 = tid + 512 < PU ? tid + 512 : PU - 1;
+#define LQ_PANEL_LOAD(S, J)                                                              \
+  do {                                                                                   \
+    const int jj_ = (J) < nsteps ? (J) : nsteps - 1;                                     \
+    const uint4* src_ = xg + static_cast<int64_t>(jj_) * PU;                             \
+    pa##S = src_[i0];                                                                    \
+    if constexpr (PPT > 1) pb##S = src_[i1];                                             \
+    if constexpr (PPT > 2) pc##S = src_[i2];                                             \
+  } while (0)
+#define LQ_PANEL_STORE(S, BUF)                                                           \
+  do {                                                                                   \
+    pan[BUF][tid] = pa##S;                                                               \
+    if constexpr (PPT > 1) pan[BUF][tid + 256] = pb##S;                                  \
+    if constexpr (PPT > 2) pan[BUF][tid + 512] = pc##S;                                  \
+  } while (0)
+  auto load_e = [&](int u, int j) {
+    j = j < nsteps ? j : nsteps - 1;   // past the end: a harmless repeat of the last step
+    const int64_t c = kb + 32 * j + 4 * g;
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+      eb[u][rt][0] = load_run4<VEC>(erow[rt], c, k);
+      eb[u][rt][1] = load_run4<VEC>(erow[rt], c + 16, k);
+    }
+  };
+  auto compute = [&](int u, int buf) {
+    bf16x8 ah[RT], al[RT], bh[NT], bl[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      bh[nt] = __builtin_bit_cast(bf16x8, pan[buf][(2 * nt) * 64 + lane]);
+      bl[nt] = __builtin_bit_cast(bf16x8, pan[buf][(2 * nt + 1) * 64 + lane]);
+    }
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) split8(eb[u][rt][0], eb[u][rt][1], ah[rt], al[rt]);
+    // the three products interleaved over the RT x NT accumulators
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) acc[rt][nt] = mfma_bf16(ah[rt], bh[nt], acc[rt][nt]);
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) acc[rt][nt] = mfma_bf16(ah[rt], bl[nt], acc[rt][nt]);
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) acc[rt][nt] = mfma_bf16(al[rt], bh[nt], acc[rt][nt]);
+  };
+  // Issue order: the panel of step j + 3 right after step j's barrier, then the E
+  // step D ahead into the freed ring slot.  The panel is stored to LDS at the end of
+  // step j + 2, where waiting for it leaves the two younger E steps (and the next
+  // panel) in flight; the scheduling barriers keep this order.
+  {
+    LQ_PANEL_LOAD(0, 0);               // step 0 (straight to LDS below)
+    uint4 qa = pa0, qb = pb0, qc = pc0;
+    LQ_PANEL_LOAD(1, 1);
+    LQ_PANEL_LOAD(0, 2);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int u = 0; u < D; ++u) load_e(u, u);
+    __builtin_amdgcn_sched_barrier(0);
+    pan[0][tid] = qa;
+    if constexpr (PPT > 1) pan[0][tid + 256] = qb;
+    if constexpr (PPT > 2) pan[0][tid + 512] = qc;
+  }
+  __syncthreads();
+  const int rounds = nsteps / D;
+  for (int rd = 0; rd < rounds; ++rd) {
+#pragma unroll
+    for (int u = 0; u < D; u += 2) {
+      const int j = rd * D + u;   // even step j, then odd step j + 1
+      compute(u, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      LQ_PANEL_STORE(1, 1);          // the panel of step j + 1
+      __syncthreads();
+      LQ_PANEL_LOAD(1, j + 3);
+      __builtin_amdgcn_sched_barrier(0);
+      load_e(u, j + D);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(u + 1, 1);
+      __builtin_amdgcn_sched_barrier(0);
+      LQ_PANEL_STORE(0, 0);          // the panel of step j + 2
+      __syncthreads();
+      LQ_PANEL_LOAD(0, j + 4);
+      __builtin_amdgcn_sched_barrier(0);
+      load_e(u + 1, j + 1 + D);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+#undef LQ_PANEL_LOAD
+#undef LQ_PANEL_STORE
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int64_t row = row0 + rt * 16 + 4 * g + v;
+        if (row < d) part[(static_cast<int64_t>(blockIdx.y) * d + row) * LP + nt * 16 + li] = acc[rt][nt][v];
+      }
+}
+
+// gemm_tn on split bf16: as gemm_tn_kernel (one 64-column group per wave, its
+// four interleaved 16-column tiles jm), row steps of 32: lane (li, g) loads rows
+// 16 h + 4 g + s of the step (eight float4 of its four columns), and tile jm's A
+// operand is component jm of those eight.
+template <int NT, bool VEC, int LMJ>
+__global__ __launch_bounds__(64 * Tn3Cfg<NT>::WC * Tn3Cfg<NT>::WR) void gemm_tn3_kernel(
+    const float* __restrict__ E, int64_t d, int64_t k, const uint16_t* __restrict__ Ys, int64_t rper,
+    float* __restrict__ part, CholJob job) {
+  using C = Tn3Cfg<NT>;
+  constexpr int LP = 16 * NT, D = C::D, WC = C::WC, WR = C::WR;
+  constexpr int kRedFloats = (WR > 1 ? WR - 1 : 1) * WC * 64 * LP;
+  constexpr int kJobDoubles = LMJ > 0 ? 5 * (LMJ * (LMJ + 1) / 2) + 64 : 1;
+  constexpr int kLdsBytes = 4 * kRedFloats > 8 * kJobDoubles ? 4 * kRedFloats : 8 * kJobDoubles;
+  __shared__ __align__(16) char lds_raw[kLdsBytes];
+  float* red = reinterpret_cast<float*>(lds_raw);
+  if constexpr (LMJ > 0) {   // the ride-along Cholesky, as in gemm_tn_kernel
+    if (blockIdx.x == gridDim.x - 1) {
+      if (blockIdx.y == 0) {
+        double* lds = reinterpret_cast<double*>(lds_raw);
+        const double* gram = gram_sum_block<LMJ>(job.parts, job.P, job.l, lds);
+        if (threadIdx.x < 64) chol_inv_to<LMJ>(gram, job.l, job.Xinv, lds);
+      }
+      return;
+    }
+  }
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, wc = w % WC, wr = w / WC;
+  const int g = lane >> 4, li = lane & 15;
+  const int64_t bx = blockIdx.x, by = blockIdx.y;   // column block, row split
+  const int64_t c0 = (bx * WC + wc) * 64;
+  const int64_t cl = c0 + 4 * li;
+  const int64_t rw = rper / WR;
+  const int64_t rb = by * rper + wr * rw;
+  const int nsteps = static_cast<int>(rw / 32);   // a multiple of D
+  const uint4* yp = reinterpret_cast<const uint4*>(Ys) + (rb / 32) * NT * 128 + lane;
+  floatx4 acc[4][NT];
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int b = 0; b < NT; ++b) acc[a][b] = floatx4{0.f, 0.f, 0.f, 0.f};
+  float4 eb[D][2][4];
+  uint4 yb[D][NT][2];
+  auto load = [&](int u, int j) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        int64_t r = rb + 32 * j + 16 * h + 4 * g + i;
+        r = r < d ? r : d - 1;
+        eb[u][h][i] = load_run4<VEC>(E + r * k, cl, k);
+      }
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) yb[u][nt][h] = yp[((static_cast<int64_t>(j) * NT + nt) * 2 + h) * 64];
+  };
+  auto compute = [&](int u) {
+    bf16x8 bh[NT], bl[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      bh[nt] = __builtin_bit_cast(bf16x8, yb[u][nt][0]);
+      bl[nt] = __builtin_bit_cast(bf16x8, yb[u][nt][1]);
+    }
+#pragma unroll
+    for (int jm = 0; jm < 4; ++jm) {
+      const float x[8] = {comp(eb[u][0][0], jm), comp(eb[u][0][1], jm), comp(eb[u][0][2], jm), comp(eb[u][0][3], jm),
+                          comp(eb[u][1][0], jm), comp(eb[u][1][1], jm), comp(eb[u][1][2], jm), comp(eb[u][1][3], jm)};
+      bf16x8 ah, al;
+      split8(x, ah, al);
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) acc[jm][nt] = mfma_bf16(ah, bh[nt], acc[jm][nt]);
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) acc[jm][nt] = mfma_bf16(ah, bl[nt], acc[jm][nt]);
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) acc[jm][nt] = mfma_bf16(al, bh[nt], acc[jm][nt]);
+    }
+  };
+#pragma unroll
+  for (int u = 0; u < D; ++u) load(u, u);
+  const int rounds = nsteps / D;
+  for (int rd = 0; rd + 1 < rounds; ++rd) {
+#pragma unroll
+    for (int u = 0; u < D; ++u) {
+      compute(u);
+      load(u, (rd + 1) * D + u);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < D; ++u) compute(u);
+  // lane (li, g), tile jm, component v holds column c0 + 4 (4 g + v) + jm, output n = 16 nt + li
+  if (WR > 1) {
+    if (wr > 0) {
+#pragma unroll
+      for (int jm = 0; jm < 4; ++jm)
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+          for (int v = 0; v < 4; ++v)
+            red[(((wr - 1) * WC + wc) * 64 + 4 * (4 * g + v) + jm) * LP + nt * 16 + li] = acc[jm][nt][v];
+    }
+    __syncthreads();
+    if (wr > 0) return;
+#pragma unroll
+    for (int q = 1; q < WR; ++q)
+#pragma unroll
+      for (int jm = 0; jm < 4; ++jm)
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+          for (int v = 0; v < 4; ++v)
+            acc[jm][nt][v] += red[(((q - 1) * WC + wc) * 64 + 4 * (4 * g + v) + jm) * LP + nt * 16 + li];
+  }
+#pragma unroll
+  for (int jm = 0; jm < 4; ++jm)
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int64_t col = c0 + 4 * (4 * g + v) + jm;
+        if (col < k) part[(by * k + col) * LP + nt * 16 + li] = acc[jm][nt][v];
+      }
+}
+
 template <int NT>
 GemmShape shape_typed(bool transposed) {
   if (transposed) {
+    if constexpr (split_tn(NT)) {
+      using C = Tn3Cfg<NT>;
+      return GemmShape{64 * C::WC, 32 * C::D * C::WR};
+    }
     using C = TnCfg<NT>;
     return GemmShape{64 * C::CW * C::WC, 16 * C::D * C::WR};
+  }
+  if constexpr (split_nn(NT)) {
+    using C = Nn3Cfg<NT>;
+    return GemmShape{16 * C::RT * C::WR, 32 * C::D};
   }
   using C = NnCfg<NT>;
   return GemmShape{16 * C::RT * C::WR, 16 * C::D * C::WK};
 }
 
 template <int NT>
-void gemm_typed(bool transposed, const float* E, int64_t d, int64_t k, const float* panel, const SvdPlan& pl,
-                float* part, const CholJob& job, hipStream_t s) {
+void gemm_typed(bool transposed, const float* E, int64_t d, int64_t k, const float* panel, const uint16_t* panel_split,
+                const SvdPlan& pl, float* part, const CholJob& job, hipStream_t s) {
   const bool vec = (k & 3) == 0 && k >= 4;
+  if constexpr (split_tn(NT)) {
+    if (transposed) {
+      constexpr int threads = 64 * Tn3Cfg<NT>::WC * Tn3Cfg<NT>::WR;
+      const dim3 grid(pl.tn_col_blocks, pl.tn_splits);
+      if (vec)
+        LQ_LAUNCH("gemm_tn", (gemm_tn3_kernel<NT, true, 0>), grid, dim3(threads), 0, s, E, d, k, panel_split, pl.tn_rper,
+                  part, job);
+      else
+        LQ_LAUNCH("gemm_tn", (gemm_tn3_kernel<NT, false, 0>), grid, dim3(threads), 0, s, E, d, k, panel_split,
+                  pl.tn_rper, part, job);
+      return;
+    }
+  }
+  if constexpr (split_nn(NT)) {
+    if (!transposed) {
+      constexpr int threads = 64 * Nn3Cfg<NT>::WR;
+      const dim3 grid(pl.nn_row_blocks, pl.nn_splits);
+      if (vec)
+        LQ_LAUNCH("gemm_nn", (gemm_nn3_kernel<NT, true>), grid, dim3(threads), 0, s, E, d, k, panel_split, pl.nn_kper, part);
+      else
+        LQ_LAUNCH("gemm_nn", (gemm_nn3_kernel<NT, false>), grid, dim3(threads), 0, s, E, d, k, panel_split, pl.nn_kper,
+                  part);
+      return;
+    }
+  }
   if (transposed) {
     constexpr int threads = 64 * TnCfg<NT>::WC * TnCfg<NT>::WR;
     const dim3 grid(pl.tn_col_blocks + (job.parts != nullptr ? 1 : 0), pl.tn_splits);
@@ -345,16 +680,16 @@ GemmShape gemm_shape(bool transposed, int nt) {
   }
 }
 
-void launch_gemm(bool transposed, const float* E, int64_t d, int64_t k, const float* panel, const SvdPlan& pl,
-                 float* part, const CholJob& job, hipStream_t s) {
+void launch_gemm(bool transposed, const float* E, int64_t d, int64_t k, const float* panel,
+                 const uint16_t* panel_split, const SvdPlan& pl, float* part, const CholJob& job, hipStream_t s) {
   const CholJob none{nullptr, 0, 0, nullptr};
   const CholJob& j = (transposed && pl.nt <= 2) ? job : none;
   switch (pl.nt) {
-    case 1: gemm_typed<1>(transposed, E, d, k, panel, pl, part, j, s); break;
-    case 2: gemm_typed<2>(transposed, E, d, k, panel, pl, part, j, s); break;
-    case 3: gemm_typed<3>(transposed, E, d, k, panel, pl, part, j, s); break;
-    case 4: gemm_typed<4>(transposed, E, d, k, panel, pl, part, j, s); break;
-    default: gemm_typed<5>(transposed, E, d, k, panel, pl, part, j, s); break;
+    case 1: gemm_typed<1>(transposed, E, d, k, panel, panel_split, pl, part, j, s); break;
+    case 2: gemm_typed<2>(transposed, E, d, k, panel, panel_split, pl, part, j, s); break;
+    case 3: gemm_typed<3>(transposed, E, d, k, panel, panel_split, pl, part, j, s); break;
+    case 4: gemm_typed<4>(transposed, E, d, k, panel, panel_split, pl, part, j, s); break;
+    default: gemm_typed<5>(transposed, E, d, k, panel, panel_split, pl, part, j, s); break;
   }
 }
 

@@ -35,6 +35,19 @@ __host__ __device__ __forceinline__ int64_t frag_index(int64_t rho, int c, int n
   return ((rho >> 4) * nt + (c >> 4)) * 256 + ((rho & 15) >> 2) * 64 + (c & 15) * 4 + (rho & 3);
 }
 
+// Split panels feed the bf16 matrix-core products of wide panels: each fp32 value
+// v is stored as two bf16 pieces, hi = bf16(v) and lo = bf16(v - hi) (nearest,
+// ties to even), in 32-row K steps laid out as the operands of
+// v_mfma_f32_16x16x32_bf16.  For K step s, tile c / 16 and part (0 hi, 1 lo),
+// lane L = 16 g + li holds 8 bf16 (16 bytes): rows 16 h + 4 g + i (h = 0, 1;
+// i = 0..3) of the step, column 16 (c / 16) + li, i.e. the lane's float4 of the
+// two fragment-order blocks 2 s and 2 s + 1.  Same byte count as the fp32 panel.
+__host__ __device__ __forceinline__ int64_t split_index(int64_t rho, int c, int nt, int part) {
+  const int64_t step = rho >> 5;
+  const int h = static_cast<int>((rho >> 4) & 1), g = static_cast<int>((rho >> 2) & 3), i = static_cast<int>(rho & 3);
+  return (((step * nt + (c >> 4)) * 2 + part) * 64 + 16 * g + (c & 15)) * 8 + 4 * h + i;
+}
+
 // Workgroup tile of a thin product: rows (gemm_nn) or columns (gemm_tn) per
 // workgroup, and the granularity of its split of the contracted dimension.
 struct GemmShape {
@@ -54,7 +67,9 @@ struct SvdPlan {
   int gram_parts_d, gram_parts_k;
   bool ride;              // l <= 32 Cholesky rides along with E^T Y (see make_svd_plan)
   int64_t k_pad, d_pad;   // fragment-order panel rows: nn_splits * nn_kper and tn_splits * tn_rper
+  bool split_nn, split_tn; // products on the bf16 matrix cores (their panels also kept split, split_index)
   int64_t off_omega, off_y, off_z, off_part, off_gram_parts, off_gram_total, off_rinv, off_sb, off_sa;
+  int64_t off_omega_s, off_y_s, off_z_s;   // split copies: Omega and Z for split_nn, Y for split_tn
   int64_t off_stats, off_x;
   int64_t bytes;
 };
@@ -84,8 +99,13 @@ struct CholJob {
   int l;
   float* Xinv;
 };
-void launch_gemm(bool transposed, const float* E, int64_t d, int64_t k, const float* panel, const SvdPlan& pl,
-                 float* part, const CholJob& job, hipStream_t s);
+// panel: fragment-order fp32 (fp32 products); panel_split: its split copy (split plans)
+void launch_gemm(bool transposed, const float* E, int64_t d, int64_t k, const float* panel,
+                 const uint16_t* panel_split, const SvdPlan& pl, float* part, const CholJob& job, hipStream_t s);
+// Panel widths (tiles of 16 columns) whose products run on the split-bf16 path:
+// E P (every width) and E^T Y (wide panels; narrow ones stay on fp32 MFMA).
+constexpr bool split_nn(int nt) { return nt >= 1; }
+constexpr bool split_tn(int nt) { return nt >= 3; }
 
 bool aligned16(const void* p);
 bool shape_ok(int64_t rows, int64_t cols);

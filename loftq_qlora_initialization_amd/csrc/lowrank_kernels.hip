@@ -24,6 +24,7 @@
 #include "lowrank.h"
 #include "reduce.h"
 #include "small_solve.h"
+#include "split_bf16.h"
 
 namespace loftq {
 namespace {
@@ -68,6 +69,28 @@ __global__ void warm_columns_kernel(const float* __restrict__ A, const float* __
   const float sg = sigma[j];
   if (!(sg > 0.f)) return;
   out[frag_index(i, j, nt)] = sqrtf(static_cast<float>(k)) * (A[idx] / sqrtf(sg));
+}
+
+// Fragment-order fp32 panel (rows_pad rows, a multiple of 32) to its split copy
+// (split_index): one thread per (32-row step, tile, lane) reads the lane's float4
+// of fragment blocks 2 s and 2 s + 1 and writes the hi and lo pieces.
+__global__ void split_panel_kernel(const float* __restrict__ frag, int64_t rows_pad, int nt,
+                                   uint16_t* __restrict__ out) {
+  const int64_t u = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (u >= (rows_pad >> 5) * nt * 64) return;
+  const int L = static_cast<int>(u & 63);
+  const int64_t st_tile = u >> 6;
+  const int64_t st = st_tile / nt;
+  const int tile = static_cast<int>(st_tile - st * nt);
+  const float4* f4 = reinterpret_cast<const float4*>(frag);
+  const float4 a = f4[((2 * st) * nt + tile) * 64 + L];
+  const float4 b = f4[((2 * st + 1) * nt + tile) * 64 + L];
+  const float x[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+  uint4 hi, lo;
+  split8_u4(x, hi, lo);
+  uint4* o = reinterpret_cast<uint4*>(out) + (st_tile * 2) * 64 + L;
+  o[0] = hi;
+  o[64] = lo;
 }
 
 // Row-major n x l panel to fragment order over `rows` rows (zero padding).
@@ -562,7 +585,8 @@ typedef double mfma_d4 __attribute__((ext_vector_type(4)));
 template <int NT>
 __global__ __launch_bounds__(kReduceThreads) void reduce_gram_kernel(const float* __restrict__ part, int S, int64_t m,
                                                           int64_t m_pad, int l, const float* __restrict__ X,
-                                                          float* __restrict__ out, double* __restrict__ gram_parts) {
+                                                          float* __restrict__ out, uint16_t* __restrict__ out_split,
+                                                          double* __restrict__ gram_parts) {
   constexpr int LP = 16 * NT, PER = (kGramRows * LP + kReduceThreads - 1) / kReduceThreads, LDR = LP + 1;
   constexpr int NW = kReduceThreads / 64;
   static_assert(kGramRows % 16 == 0, "whole 16-row MFMA tiles");
@@ -640,6 +664,27 @@ __global__ __launch_bounds__(kReduceThreads) void reduce_gram_kernel(const float
       *reinterpret_cast<float4*>(out + frag_index(row, n, NT)) =
           make_float4(R[(4 * q) * LDR + n], R[(4 * q + 1) * LDR + n], R[(4 * q + 2) * LDR + n],
                       R[(4 * q + 3) * LDR + n]);
+  }
+  // the split copy for the bf16 products: per 32-row step, tile and lane, the lane's
+  // eight rows of its column as hi and lo pieces
+  if (out_split != nullptr) {
+    uint4* os = reinterpret_cast<uint4*>(out_split);
+    for (int ui = threadIdx.x; ui < 2 * NT * 64; ui += blockDim.x) {
+      const int L = ui & 63, tn = (ui >> 6) % NT, st = (ui >> 6) / NT;
+      const int64_t rs = r0 + 32 * st;
+      if (rs >= m_pad) continue;
+      const int gg = L >> 4, n = 16 * tn + (L & 15);
+      float x[8];
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) x[4 * h + i] = R[(32 * st + 16 * h + 4 * gg + i) * LDR + n];
+      uint4 hi, lo;
+      split8_u4(x, hi, lo);
+      const int64_t b = (((rs >> 5) * NT + tn) * 2) * 64 + L;
+      os[b] = hi;
+      os[b + 64] = lo;
+    }
   }
   if (gram_parts == nullptr || r0 >= m) return;
   // Gram partial, tiles (ta, tb), ta <= tb: A[li][lk] = R[4 ks + lk][16 ta + li],
@@ -909,20 +954,20 @@ int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 template <int NT>
 void reduce_typed(const float* part, int S, int64_t m, int64_t m_pad, int l, const float* X, float* out,
-                  double* gram_parts, hipStream_t s) {
+                  uint16_t* out_split, double* gram_parts, hipStream_t s) {
   const int blocks = static_cast<int>(cdiv(m_pad, kGramRows));
   LQ_LAUNCH("reduce_gram", (reduce_gram_kernel<NT>), dim3(blocks), dim3(kReduceThreads), 0, s, part, S, m, m_pad, l, X, out,
-            gram_parts);
+            out_split, gram_parts);
 }
 
 void launch_reduce(int nt, const float* part, int S, int64_t m, int64_t m_pad, int l, const float* X, float* out,
-                   double* gram_parts, hipStream_t s) {
+                   uint16_t* out_split, double* gram_parts, hipStream_t s) {
   switch (nt) {
-    case 1: reduce_typed<1>(part, S, m, m_pad, l, X, out, gram_parts, s); break;
-    case 2: reduce_typed<2>(part, S, m, m_pad, l, X, out, gram_parts, s); break;
-    case 3: reduce_typed<3>(part, S, m, m_pad, l, X, out, gram_parts, s); break;
-    case 4: reduce_typed<4>(part, S, m, m_pad, l, X, out, gram_parts, s); break;
-    default: reduce_typed<5>(part, S, m, m_pad, l, X, out, gram_parts, s); break;
+    case 1: reduce_typed<1>(part, S, m, m_pad, l, X, out, out_split, gram_parts, s); break;
+    case 2: reduce_typed<2>(part, S, m, m_pad, l, X, out, out_split, gram_parts, s); break;
+    case 3: reduce_typed<3>(part, S, m, m_pad, l, X, out, out_split, gram_parts, s); break;
+    case 4: reduce_typed<4>(part, S, m, m_pad, l, X, out, out_split, gram_parts, s); break;
+    default: reduce_typed<5>(part, S, m, m_pad, l, X, out, out_split, gram_parts, s); break;
   }
 }
 
@@ -1022,6 +1067,9 @@ SvdPlan make_svd_plan(int64_t d, int64_t k, int r, int oversample, bool exact) {
   }
   p.k_pad = p.nn_splits * p.nn_kper;
   p.d_pad = p.tn_splits * p.tn_rper;
+  // the split products step K by 32, so k_pad (split_nn) and d_pad (split_tn) are multiples of 32
+  p.split_nn = split_nn(p.nt);
+  p.split_tn = split_tn(p.nt);
   p.gram_parts_d = static_cast<int>(cdiv(d, kGramRows));
   p.gram_parts_k = static_cast<int>(cdiv(k, kGramRows));
   const int64_t gp = p.gram_parts_d > p.gram_parts_k ? p.gram_parts_d : p.gram_parts_k;
@@ -1037,6 +1085,11 @@ SvdPlan make_svd_plan(int64_t d, int64_t k, int r, int oversample, bool exact) {
   p.off_sb = take(static_cast<int64_t>(l) * r * 4);
   p.off_sa = take(static_cast<int64_t>(l) * r * 4);
   p.off_stats = take(64);
+  if (p.split_nn) {
+    p.off_omega_s = take(p.k_pad * LP * 4);
+    p.off_z_s = take(p.k_pad * LP * 4);
+  }
+  if (p.split_tn) p.off_y_s = take(p.d_pad * LP * 4);
   p.bytes = off;
   return p;
 }
@@ -1099,6 +1152,15 @@ hipError_t run_lowrank(const float* E, const SvdPlan& pl, int q, const float* om
     hipError_t e = run_sketch(seed, t, 1, k, l, pl.nt, pl.k_pad, Om_ws, s);
     if (e != hipSuccess) return e;
   }
+  // split copies of the panels for the bf16 products (split plans only)
+  uint16_t* Om_s = pl.split_nn ? reinterpret_cast<uint16_t*>(ws + pl.off_omega_s) : nullptr;
+  uint16_t* Y_s = pl.split_tn ? reinterpret_cast<uint16_t*>(ws + pl.off_y_s) : nullptr;
+  uint16_t* Z_s = pl.split_nn ? reinterpret_cast<uint16_t*>(ws + pl.off_z_s) : nullptr;
+  if (pl.split_nn) {
+    const int64_t units = (pl.k_pad / 32) * pl.nt * 64;
+    LQ_LAUNCH("split_panel", split_panel_kernel, dim3(static_cast<unsigned>(cdiv(units, 256))), dim3(256), 0, s, Om,
+              pl.k_pad, pl.nt, Om_s);
+  }
   double* gtotal = reinterpret_cast<double*>(ws + pl.off_gram_total);
   const int E_ = l * (l + 1) / 2;
   // product and split-K reduction; mode 1 then orthonormalises (Gram, Cholesky,
@@ -1110,14 +1172,15 @@ hipError_t run_lowrank(const float* E, const SvdPlan& pl, int q, const float* om
   // reduction is the first consumer of X.
   const bool ride = pl.ride;
   bool pending = false;
-  auto product = [&](bool transposed, const float* panel, int mode) {
+  auto product = [&](bool transposed, const float* panel, const uint16_t* panel_s, int mode) {
     const CholJob job{pending ? gparts : nullptr, pl.gram_parts_d, l, Xinv};
-    launch_gemm(transposed, E, d, k, panel, pl, part, job, s);
+    launch_gemm(transposed, E, d, k, panel, panel_s, pl, part, job, s);
     if (transposed) pending = false;
     if (transposed)
-      launch_reduce(pl.nt, part, pl.tn_splits, k, pl.k_pad, l, Xinv, Z, mode ? gparts : nullptr, s);
+      launch_reduce(pl.nt, part, pl.tn_splits, k, pl.k_pad, l, Xinv, Z, mode == 2 ? nullptr : Z_s,
+                    mode ? gparts : nullptr, s);
     else
-      launch_reduce(pl.nt, part, pl.nn_splits, d, pl.d_pad, l, nullptr, Y, mode ? gparts : nullptr, s);
+      launch_reduce(pl.nt, part, pl.nn_splits, d, pl.d_pad, l, nullptr, Y, Y_s, mode ? gparts : nullptr, s);
     if (mode == 0) return;
     if (mode == 1 && ride) {
       pending = true;
@@ -1141,13 +1204,13 @@ hipError_t run_lowrank(const float* E, const SvdPlan& pl, int q, const float* om
   // Y = E Omega; X = R^-1 of its Gram.  Each power iteration multiplies by E^T
   // and E and re-orthonormalises Y only: span(E Z) does not depend on Z's basis,
   // so orthonormalising Z as well would not change the subspace.
-  product(false, Om, 1);
+  product(false, Om, Om_s, 1);
   for (int it = 0; it < q; ++it) {
-    product(true, Y, 0);
-    product(false, Z, 1);
+    product(true, Y, Y_s, 0);
+    product(false, Z, Z_s, 1);
   }
   // C = E^T Q = (E^T Y) X, then the core solve on C^T C
-  product(true, Y, 2);
+  product(true, Y, Y_s, 2);
   panels(PanelJob{Y, d, SB, B, 0}, PanelJob{Z, k, SA, A, 1}, l, pl.nt, r, s);
   return hipGetLastError();
 }
