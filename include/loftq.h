@@ -177,6 +177,26 @@ loftq_status_t loftq_qlora_forward(const void* X, int64_t n_tok, int64_t rows, i
                                    int32_t r, float alpha, float* Y, void* ws, size_t ws_bytes, void* stream);
 size_t loftq_qlora_forward_workspace_bytes(int64_t n_tok, int32_t r);
 
+/* loftq_qlora_forward for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same computation and arguments without the workspace.  The partial products of
+ * X A^T go to a scratch array the library holds in device memory (one copy per
+ * GPU, kept until the process ends); its device address is looked up on the first
+ * call on each device.  Nothing is allocated or freed by any call.
+ *   Limit: loftq_qlora_forward_workspace_bytes(n_tok, r) <= loftq_qlora_forward_noalloc_max_bytes()
+ *          (8 MiB: n_tok * r <= 262144, e.g. 4096 tokens at r = 64); larger calls
+ *          return LOFTQ_ERR_WORKSPACE and enqueue nothing.
+ *   The current HIP device must be the one `stream` belongs to.  Calls on one GPU
+ *   share its scratch: calls that may run at the same time on that GPU (other
+ *   streams, other threads) race and must be ordered by the caller.  The scratch
+ *   needs no clearing (each call writes every partial before reading it).
+ * Errors otherwise as loftq_qlora_forward. */
+loftq_status_t loftq_qlora_forward_noalloc(const void* X, int64_t n_tok, int64_t rows, int64_t cols,
+                                           const uint8_t* packed, const float* absmax, const int8_t* qabsmax,
+                                           const float* dq_scale, int32_t bits, const float* B, const float* A,
+                                           int32_t r, float alpha, float* Y, void* stream);
+size_t loftq_qlora_forward_noalloc_max_bytes(void);
+
 /* Low-rank step ("LoftQ...", §2.3: best rank-r approximation of W - Q from its
  * r largest singular triplets, Delta = U_r S_r V_r^T).  exact = 1: the SVD of E
  * itself (one-sided Jacobi, min(rows, cols) <= 512).  exact = 0: randomized

@@ -36,7 +36,8 @@ EXPORTS = ["loftq_init_batch", "loftq_batch_workspace_bytes", "loftq_nf4_quantiz
            "loftq_nf4_unmerge", "loftq_lowrank_svd",
            "loftq_lowrank_svd_workspace_bytes", "loftq_init", "loftq_workspace_bytes", "loftq_default_config",
            "loftq_status_string", "loftq_nf4_codebook", "loftq_nf_codebook", "loftq_qlora_forward",
-           "loftq_qlora_forward_workspace_bytes", "loftq_profile_enable", "loftq_profile_collect"]
+           "loftq_qlora_forward_workspace_bytes", "loftq_qlora_forward_noalloc", "loftq_qlora_forward_noalloc_max_bytes",
+           "loftq_profile_enable", "loftq_profile_collect"]
 
 
 class LoftqConfig(ctypes.Structure):
@@ -72,6 +73,9 @@ _c_unmerge = _sig("loftq_nf4_unmerge", ctypes.c_int, _MERGE_ARGS)
 _c_fwd = _sig("loftq_qlora_forward", ctypes.c_int,
               [_P, _I64, _I64, _I64, _P, _P, _P, _P, _I32, _P, _P, _I32, ctypes.c_float, _P, _P, _SZ, _P])
 _c_fwd_ws = _sig("loftq_qlora_forward_workspace_bytes", _SZ, [_I64, _I32])
+_c_fwd_na = _sig("loftq_qlora_forward_noalloc", ctypes.c_int,
+                 [_P, _I64, _I64, _I64, _P, _P, _P, _P, _I32, _P, _P, _I32, ctypes.c_float, _P, _P])
+_c_fwd_na_max = _sig("loftq_qlora_forward_noalloc_max_bytes", _SZ, [])
 _c_svd = _sig("loftq_lowrank_svd", ctypes.c_int,
               [_P, _I64, _I64, _I32, _I32, _I32, _I32, _P, _U64, _I32, _P, _P, _P, _P, _SZ, _P])
 _c_svd_ws = _sig("loftq_lowrank_svd_workspace_bytes", _SZ, [_I64, _I64, _I32, _I32, _I32])
@@ -265,6 +269,34 @@ def loftq_qlora_forward(X: torch.Tensor, packed: torch.Tensor, shape, absmax: Op
     _check("loftq_qlora_forward",
            _c_fwd(_ptr(X), n_tok, rows, cols, _ptr(packed), _ptr(absmax), _ptr(qabsmax), _ptr(dq_scale), int(bits),
                   _ptr(B), _ptr(A), r, float(alpha), _ptr(out), _ptr(ws), ws_bytes, _stream(stream)))
+    return out
+
+
+def qlora_forward_noalloc_max_bytes() -> int:
+    return int(_c_fwd_na_max())
+
+
+def loftq_qlora_forward_noalloc(X: torch.Tensor, packed: torch.Tensor, shape, absmax: Optional[torch.Tensor] = None,
+                                qabsmax: Optional[torch.Tensor] = None, dq_scale: Optional[torch.Tensor] = None,
+                                B: Optional[torch.Tensor] = None, A: Optional[torch.Tensor] = None,
+                                alpha: float = 1.0, bits: int = 4, out: Optional[torch.Tensor] = None,
+                                stream=None) -> torch.Tensor:
+    """loftq_qlora_forward without a workspace: the library's own device scratch holds the
+    partial products (no allocation in the call; `out` is allocated here only if not given)."""
+    _contig(X, "X")
+    if X.dtype != torch.bfloat16:
+        raise TypeError("X must be bfloat16")
+    rows, cols = shape
+    n_tok = X.shape[0]
+    r = 0
+    if B is not None:
+        _contig(B, "B"), _contig(A, "A")
+        r = B.shape[1]
+    if out is None:
+        out = torch.empty((n_tok, rows), dtype=torch.float32, device=X.device)
+    _check("loftq_qlora_forward_noalloc",
+           _c_fwd_na(_ptr(X), n_tok, rows, cols, _ptr(packed), _ptr(absmax), _ptr(qabsmax), _ptr(dq_scale),
+                     int(bits), _ptr(B), _ptr(A), r, float(alpha), _ptr(out), _stream(stream)))
     return out
 
 

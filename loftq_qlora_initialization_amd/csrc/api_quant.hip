@@ -1,10 +1,42 @@
 // C-ABI entry points for the NF4 codec and the adapter merge: argument validation, then launches.
 #include <cmath>
 #include <cstring>
+#include <mutex>
 
 #include "internal.h"
 
 namespace loftq {
+
+// Scratch of the allocation-free QLoRA forward (loftq_qlora_forward_noalloc): a
+// file-scope device array, one copy per GPU the library runs on, held until the
+// process ends.  Host code never passes `scratch` itself to a kernel (on the host it
+// is only a stand-in for the symbol): its device address is looked up once per
+// device, with that device current, and kept in scratch_ptr.
+constexpr size_t kStaticScratchBytes = size_t(8) << 20;
+__device__ __align__(256) char scratch[kStaticScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The current device's copy of `scratch` (set up on the first call on that device).
+hipError_t scratch_ptr(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
+}
+}  // namespace
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -162,10 +194,15 @@ size_t loftq_qlora_forward_workspace_bytes(int64_t n_tok, int32_t r) {
   return qlora_forward_workspace_bytes(n_tok, r);
 }
 
-loftq_status_t loftq_qlora_forward(const void* X, int64_t n_tok, int64_t rows, int64_t cols, const uint8_t* packed,
-                                   const float* absmax, const int8_t* qabsmax, const float* dq_scale, int32_t bits,
-                                   const float* B, const float* A, int32_t r, float alpha, float* Y, void* ws,
-                                   size_t ws_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+// Every argument check of the QLoRA forward, before anything is enqueued; LOFTQ_OK
+// also for the empty shapes (n_tok = 0 or rows = 0), which launch nothing.
+loftq_status_t loftq_qlora_forward_check(const void* X, int64_t n_tok, int64_t rows, int64_t cols,
+                                         const uint8_t* packed, const float* absmax, const int8_t* qabsmax,
+                                         const float* dq_scale, int32_t bits, const float* B, const float* A,
+                                         int32_t r, float alpha, float* Y, void* ws, size_t ws_bytes) {
   if (!shape_ok(rows, cols) || n_tok < 0 || n_tok >= (int64_t(1) << 31)) return LOFTQ_ERR_INVALID_ARG;
   if (bits != 2 && bits != 3 && bits != 4) return LOFTQ_ERR_UNSUPPORTED;
   if (!nf_tables(bits).valid) return LOFTQ_ERR_UNSUPPORTED;
@@ -184,6 +221,50 @@ loftq_status_t loftq_qlora_forward(const void* X, int64_t n_tok, int64_t rows, i
     if (!aligned16(B) || !aligned16(A) || !ws || !aligned16(ws)) return LOFTQ_ERR_INVALID_ARG;
     if (ws_bytes < qlora_forward_workspace_bytes(n_tok, r)) return LOFTQ_ERR_WORKSPACE;
   }
+  return LOFTQ_OK;
+}
+}  // namespace
+
+extern "C" {
+
+loftq_status_t loftq_qlora_forward(const void* X, int64_t n_tok, int64_t rows, int64_t cols, const uint8_t* packed,
+                                   const float* absmax, const int8_t* qabsmax, const float* dq_scale, int32_t bits,
+                                   const float* B, const float* A, int32_t r, float alpha, float* Y, void* ws,
+                                   size_t ws_bytes, void* stream) {
+  const loftq_status_t st = loftq_qlora_forward_check(X, n_tok, rows, cols, packed, absmax, qabsmax, dq_scale, bits,
+                                                      B, A, r, alpha, Y, ws, ws_bytes);
+  if (st != LOFTQ_OK || n_tok == 0 || rows == 0) return st;
+  const bool dq = qabsmax != nullptr || dq_scale != nullptr;
+  return from_hip(launch_qlora_forward(X, n_tok, rows, cols, packed, dq ? nullptr : absmax, dq ? qabsmax : nullptr,
+                                       dq ? dq_scale : nullptr, bits, B, A, B ? r : 0, alpha, Y,
+                                       static_cast<float*>(ws), static_cast<hipStream_t>(stream)));
+}
+
+size_t loftq_qlora_forward_noalloc_max_bytes(void) { return kStaticScratchBytes; }
+
+loftq_status_t loftq_qlora_forward_noalloc(const void* X, int64_t n_tok, int64_t rows, int64_t cols,
+                                           const uint8_t* packed, const float* absmax, const int8_t* qabsmax,
+                                           const float* dq_scale, int32_t bits, const float* B, const float* A,
+                                           int32_t r, float alpha, float* Y, void* stream) {
+  // the adapter's partial products go to the library's own scratch instead of a
+  // caller workspace; every other check is loftq_qlora_forward's
+  size_t need = 0;
+  if (B != nullptr && A != nullptr && n_tok > 0 && n_tok < (int64_t(1) << 31) && r >= 1 && r <= 64) {
+    need = qlora_forward_workspace_bytes(n_tok, r);
+    if (need > kStaticScratchBytes) return LOFTQ_ERR_WORKSPACE;
+  }
+  // a stand-in for the workspace only to pass the shared validation, which never
+  // dereferences it; the launch below gets the scratch's device address
+  void* const probe = reinterpret_cast<void*>(uintptr_t(256));
+  loftq_status_t st = loftq_qlora_forward_check(X, n_tok, rows, cols, packed, absmax, qabsmax, dq_scale, bits, B, A,
+                                                r, alpha, Y, need > 0 ? probe : nullptr, need);
+  if (st != LOFTQ_OK || n_tok == 0 || rows == 0) return st;
+  void* ws = nullptr;
+  if (B != nullptr) {
+    const hipError_t e = scratch_ptr(&ws);
+    if (e != hipSuccess) return LOFTQ_ERR_HIP;
+  }
+  const bool dq = qabsmax != nullptr;
   return from_hip(launch_qlora_forward(X, n_tok, rows, cols, packed, dq ? nullptr : absmax, dq ? qabsmax : nullptr,
                                        dq ? dq_scale : nullptr, bits, B, A, B ? r : 0, alpha, Y,
                                        static_cast<float*>(ws), static_cast<hipStream_t>(stream)));

@@ -336,3 +336,30 @@ def test_init_batch_validation(clib):
     assert call(good, n=-1) == 1
     assert call(good, n=0) == 0                               # empty batch: nothing to do
     assert binding._c_batch_ws(arr, 0, ctypes.byref(cfg)) == 0
+
+
+def test_qlora_forward_noalloc_validation(clib):
+    """The allocation-free forward: the scratch limit and the forward's own checks, before any HIP call."""
+    P, I64, I32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32
+    f = clib.loftq_qlora_forward_noalloc
+    f.restype = ctypes.c_int
+    f.argtypes = [P, I64, I64, I64, P, P, P, P, I32, P, P, I32, ctypes.c_float, P, P]
+    clib.loftq_qlora_forward_noalloc_max_bytes.restype = ctypes.c_size_t
+    cap = clib.loftq_qlora_forward_noalloc_max_bytes()
+    assert cap == 8 << 20
+    F = FAKE
+    keys = ["X", "n", "rows", "cols", "packed", "absmax", "qa", "dqs", "bits", "B", "A", "r", "alpha", "Y"]
+    ok = (F, 32, 64, 128, F, F, None, None, 4, F, F, 8, 1.0, F)
+
+    def call(**kw):
+        args = list(ok)
+        for k, v in kw.items():
+            args[keys.index(k)] = v
+        return f(*args, None)
+    assert call(n=cap // (8 * 4 * 16) + 16, r=16) == 3      # partial products beyond the scratch
+    assert call(n=4096, r=65) == 2                          # rank above 64
+    assert call(bits=5) == 2
+    assert call(cols=96) == 2
+    assert call(A=None) == 1 and call(X=None) == 1 and call(Y=F + 4) == 1
+    assert call(alpha=float("inf")) == 1 and call(n=-1) == 1
+    assert call(n=0) == 0 and call(rows=0) == 0              # empty: nothing to write
