@@ -67,9 +67,8 @@ struct SvdPlan {
   int gram_parts_d, gram_parts_k;
   bool ride;              // l <= 32 Cholesky rides along with E^T Y (see make_svd_plan)
   int64_t k_pad, d_pad;   // fragment-order panel rows: nn_splits * nn_kper and tn_splits * tn_rper
-  bool split_nn, split_tn; // products on the bf16 matrix cores (their panels also kept split, split_index)
   int64_t off_omega, off_y, off_z, off_part, off_gram_parts, off_gram_total, off_rinv, off_sb, off_sa;
-  int64_t off_omega_s, off_y_s, off_z_s;   // split copies: Omega and Z for split_nn, Y for split_tn
+  int64_t off_omega_s, off_y_s, off_z_s;   // split copies of the panels (split_index), read by the products
   int64_t off_stats, off_x;
   int64_t bytes;
 };
@@ -99,13 +98,9 @@ struct CholJob {
   int l;
   float* Xinv;
 };
-// panel: fragment-order fp32 (fp32 products); panel_split: its split copy (split plans)
-void launch_gemm(bool transposed, const float* E, int64_t d, int64_t k, const float* panel,
-                 const uint16_t* panel_split, const SvdPlan& pl, float* part, const CholJob& job, hipStream_t s);
-// Panel widths (tiles of 16 columns) whose products run on the split-bf16 path:
-// E P (every width) and E^T Y (wide panels; narrow ones stay on fp32 MFMA).
-constexpr bool split_nn(int nt) { return nt >= 1; }
-constexpr bool split_tn(int nt) { return nt >= 3; }
+// panel: the split copy (split_index) of the skinny operand
+void launch_gemm(bool transposed, const float* E, int64_t d, int64_t k, const uint16_t* panel, const SvdPlan& pl,
+                 float* part, const CholJob& job, hipStream_t s);
 
 bool aligned16(const void* p);
 bool shape_ok(int64_t rows, int64_t cols);

@@ -1067,9 +1067,7 @@ SvdPlan make_svd_plan(int64_t d, int64_t k, int r, int oversample, bool exact) {
   }
   p.k_pad = p.nn_splits * p.nn_kper;
   p.d_pad = p.tn_splits * p.tn_rper;
-  // the split products step K by 32, so k_pad (split_nn) and d_pad (split_tn) are multiples of 32
-  p.split_nn = split_nn(p.nt);
-  p.split_tn = split_tn(p.nt);
+  // the products step K by 32, so k_pad and d_pad are multiples of 32
   p.gram_parts_d = static_cast<int>(cdiv(d, kGramRows));
   p.gram_parts_k = static_cast<int>(cdiv(k, kGramRows));
   const int64_t gp = p.gram_parts_d > p.gram_parts_k ? p.gram_parts_d : p.gram_parts_k;
@@ -1085,11 +1083,9 @@ SvdPlan make_svd_plan(int64_t d, int64_t k, int r, int oversample, bool exact) {
   p.off_sb = take(static_cast<int64_t>(l) * r * 4);
   p.off_sa = take(static_cast<int64_t>(l) * r * 4);
   p.off_stats = take(64);
-  if (p.split_nn) {
-    p.off_omega_s = take(p.k_pad * LP * 4);
-    p.off_z_s = take(p.k_pad * LP * 4);
-  }
-  if (p.split_tn) p.off_y_s = take(p.d_pad * LP * 4);
+  p.off_omega_s = take(p.k_pad * LP * 4);
+  p.off_z_s = take(p.k_pad * LP * 4);
+  p.off_y_s = take(p.d_pad * LP * 4);
   p.bytes = off;
   return p;
 }
@@ -1152,11 +1148,11 @@ hipError_t run_lowrank(const float* E, const SvdPlan& pl, int q, const float* om
     hipError_t e = run_sketch(seed, t, 1, k, l, pl.nt, pl.k_pad, Om_ws, s);
     if (e != hipSuccess) return e;
   }
-  // split copies of the panels for the bf16 products (split plans only)
-  uint16_t* Om_s = pl.split_nn ? reinterpret_cast<uint16_t*>(ws + pl.off_omega_s) : nullptr;
-  uint16_t* Y_s = pl.split_tn ? reinterpret_cast<uint16_t*>(ws + pl.off_y_s) : nullptr;
-  uint16_t* Z_s = pl.split_nn ? reinterpret_cast<uint16_t*>(ws + pl.off_z_s) : nullptr;
-  if (pl.split_nn) {
+  // split copies of the panels for the bf16 products
+  uint16_t* Om_s = reinterpret_cast<uint16_t*>(ws + pl.off_omega_s);
+  uint16_t* Y_s = reinterpret_cast<uint16_t*>(ws + pl.off_y_s);
+  uint16_t* Z_s = reinterpret_cast<uint16_t*>(ws + pl.off_z_s);
+  {
     const int64_t units = (pl.k_pad / 32) * pl.nt * 64;
     LQ_LAUNCH("split_panel", split_panel_kernel, dim3(static_cast<unsigned>(cdiv(units, 256))), dim3(256), 0, s, Om,
               pl.k_pad, pl.nt, Om_s);
@@ -1172,9 +1168,9 @@ hipError_t run_lowrank(const float* E, const SvdPlan& pl, int q, const float* om
   // reduction is the first consumer of X.
   const bool ride = pl.ride;
   bool pending = false;
-  auto product = [&](bool transposed, const float* panel, const uint16_t* panel_s, int mode) {
+  auto product = [&](bool transposed, const uint16_t* panel_s, int mode) {
     const CholJob job{pending ? gparts : nullptr, pl.gram_parts_d, l, Xinv};
-    launch_gemm(transposed, E, d, k, panel, panel_s, pl, part, job, s);
+    launch_gemm(transposed, E, d, k, panel_s, pl, part, job, s);
     if (transposed) pending = false;
     if (transposed)
       launch_reduce(pl.nt, part, pl.tn_splits, k, pl.k_pad, l, Xinv, Z, mode == 2 ? nullptr : Z_s,
@@ -1204,13 +1200,13 @@ hipError_t run_lowrank(const float* E, const SvdPlan& pl, int q, const float* om
   // Y = E Omega; X = R^-1 of its Gram.  Each power iteration multiplies by E^T
   // and E and re-orthonormalises Y only: span(E Z) does not depend on Z's basis,
   // so orthonormalising Z as well would not change the subspace.
-  product(false, Om, Om_s, 1);
+  product(false, Om_s, 1);
   for (int it = 0; it < q; ++it) {
-    product(true, Y, Y_s, 0);
-    product(false, Z, Z_s, 1);
+    product(true, Y_s, 0);
+    product(false, Z_s, 1);
   }
   // C = E^T Q = (E^T Y) X, then the core solve on C^T C
-  product(true, Y, Y_s, 2);
+  product(true, Y_s, 2);
   panels(PanelJob{Y, d, SB, B, 0}, PanelJob{Z, k, SA, A, 1}, l, pl.nt, r, s);
   return hipGetLastError();
 }
