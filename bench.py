@@ -99,7 +99,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=None, help="timed steps (default 3 for c4, else 20)")
     ap.add_argument("--warmup", type=int, default=None, help="untimed steps (default 1 for c4, else 3)")
     ap.add_argument("--workload", default="c4", help="c4 (the 224-matrix decoder batch), c1, c2, c3 or c5")
-    ap.add_argument("--streams", type=int, default=4, help="streams the batched call spreads its matrices over")
+    ap.add_argument("--streams", type=int, default=3, help="streams the batched call spreads its matrices over")
     ap.add_argument("--layers", type=int, default=32, help="decoder layers of the c4 batch (fewer: a smaller batch)")
     ap.add_argument("--cpu-rows", type=int, default=None,
                     help="rows of each sampled matrix timed on the CPU oracle (default 1024 for c4, else 4096)")
