@@ -70,6 +70,8 @@ struct SvdPlan {
   int64_t off_omega, off_y, off_z, off_part, off_gram_parts, off_gram_total, off_rinv, off_sb, off_sa;
   int64_t off_omega_s, off_y_s, off_z_s;   // split copies of the panels (split_index), read by the products
   int64_t off_stats, off_x;
+  int64_t off_sync;       // exact SVD, block Jacobi: grid-barrier and sweep counters
+  bool bj;                // exact SVD runs the block Jacobi (vectors fit its LDS tiles)
   int64_t bytes;
 };
 

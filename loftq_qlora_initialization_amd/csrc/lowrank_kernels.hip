@@ -759,6 +759,68 @@ __global__ __launch_bounds__(256) void panel_small_kernel(PanelJob j0, PanelJob 
 }
 
 // ---------------------------------------------------------------------------
+// Final stage of both exact paths: the n converged vectors x_j = sigma_j u_j
+// (stride ldx) give sigma_j = |x_j|; the r largest (ties: lower index first)
+// give the long-side factor x_j / sqrt(sigma_j) and the short-side factor
+// (E-product with x_j) * sigma_j^(-3/2).  Every thread of the workgroup calls it.
+template <typename T>
+__device__ void exact_finish(const float* __restrict__ E, int64_t d, int64_t k, int r, const T* __restrict__ Xw,
+                             int64_t ldx, int sweeps, float* __restrict__ B, float* __restrict__ A,
+                             float* __restrict__ sigma, double* __restrict__ stats, const ObjectiveArgs& obj,
+                             double* norm2, int* order) {
+  const bool trans = k > d;
+  const int n = static_cast<int>(trans ? d : k);
+  const int64_t len = trans ? k : d;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, nwaves = blockDim.x >> 6;
+  for (int v = wave; v < n; v += nwaves) {
+    const T* xv = Xw + static_cast<int64_t>(v) * ldx;
+    double s = 0.0;
+    for (int64_t e = lane; e < len; e += 64) s += static_cast<double>(xv[e]) * static_cast<double>(xv[e]);
+    for (int off = 32; off > 0; off >>= 1) s += __shfl_xor(s, off);
+    if (lane == 0) norm2[v] = s;
+  }
+  __syncthreads();
+  for (int a = tid; a < n; a += blockDim.x) {
+    const double la = norm2[a];
+    int rank = 0;
+    for (int b = 0; b < n; ++b) rank += (norm2[b] > la || (norm2[b] == la && b < a)) ? 1 : 0;
+    order[rank] = a;
+  }
+  __syncthreads();
+  const int64_t other = trans ? d : k;
+  for (int64_t e = tid; e < static_cast<int64_t>(r) * (len + other); e += blockDim.x) {
+    const int c = static_cast<int>(e / (len + other));
+    const int64_t i = e - static_cast<int64_t>(c) * (len + other);
+    const int j = order[c];
+    const double sg = sqrt(norm2[j]);
+    const T* xj = Xw + static_cast<int64_t>(j) * ldx;
+    if (i < len) {
+      const float val = sg > 0.0 ? static_cast<float>(static_cast<double>(xj[i]) / sqrt(sg)) : 0.f;
+      if (trans) A[static_cast<int64_t>(c) * k + i] = val;
+      else B[i * r + c] = val;
+    } else {
+      const int64_t o = i - len;
+      double s = 0.0;
+      if (trans) {
+        for (int64_t t2 = 0; t2 < k; ++t2) s += static_cast<double>(E[o * k + t2]) * static_cast<double>(xj[t2]);
+      } else {
+        for (int64_t t2 = 0; t2 < d; ++t2) s += static_cast<double>(E[t2 * k + o]) * static_cast<double>(xj[t2]);
+      }
+      const float val = sg > 0.0 ? static_cast<float>(s / (sg * sqrt(sg))) : 0.f;
+      if (trans) B[o * r + c] = val;
+      else A[static_cast<int64_t>(c) * k + o] = val;
+    }
+  }
+  if (tid < r) sigma[tid] = static_cast<float>(sqrt(norm2[order[tid]]));
+  double s2 = 0.0;
+  for (int c = 0; c < r; ++c) s2 += norm2[order[c]];
+  if (tid == 0 && stats) {
+    stats[0] = s2;
+    stats[1] = sweeps;
+  }
+  write_objective(obj, s2);
+}
+
 // Exact SVD for tiny matrices: one-sided (Hestenes) Jacobi in fp64 on the n =
 // min(d, k) vectors of length len = max(d, k) (columns of E when k <= d, rows of
 // E otherwise), round-robin pairs, one wave per pair.
@@ -885,55 +947,215 @@ __global__ __launch_bounds__(1024) void exact_jacobi_kernel(const float* __restr
     __syncthreads();
     if (!rot) break;
   }
-  for (int v = wave; v < n; v += nwaves) {
-    const double* xv = Xw + static_cast<int64_t>(v) * len;
-    double s = 0.0;
-    for (int64_t e = lane; e < len; e += 64) s += xv[e] * xv[e];
-    for (int off = 32; off > 0; off >>= 1) s += __shfl_xor(s, off);
-    if (lane == 0) norm2[v] = s;
-  }
-  __syncthreads();
-  for (int a = tid; a < n; a += blockDim.x) {
-    const double la = norm2[a];
-    int rank = 0;
-    for (int b = 0; b < n; ++b) rank += (norm2[b] > la || (norm2[b] == la && b < a)) ? 1 : 0;
-    order[rank] = a;
-  }
-  __syncthreads();
-  // Vector x_j = sigma_j u_j (u_j a unit singular vector on the long side).
-  // Long-side factor: x_j / sqrt(sigma_j).  Short side: E-product with x_j times sigma_j^(-3/2).
-  const int64_t other = trans ? d : k;
-  for (int64_t e = tid; e < static_cast<int64_t>(r) * (len + other); e += blockDim.x) {
-    const int c = static_cast<int>(e / (len + other));
-    const int64_t i = e - static_cast<int64_t>(c) * (len + other);
-    const int j = order[c];
-    const double sg = sqrt(norm2[j]);
-    const double* xj = Xw + static_cast<int64_t>(j) * len;
-    if (i < len) {
-      const float val = sg > 0.0 ? static_cast<float>(xj[i] / sqrt(sg)) : 0.f;
-      if (trans) A[static_cast<int64_t>(c) * k + i] = val;
-      else B[i * r + c] = val;
-    } else {
-      const int64_t o = i - len;
-      double s = 0.0;
-      if (trans) {
-        for (int64_t t2 = 0; t2 < k; ++t2) s += static_cast<double>(E[o * k + t2]) * xj[t2];
-      } else {
-        for (int64_t t2 = 0; t2 < d; ++t2) s += static_cast<double>(E[t2 * k + o]) * xj[t2];
-      }
-      const float val = sg > 0.0 ? static_cast<float>(s / (sg * sqrt(sg))) : 0.f;
-      if (trans) B[o * r + c] = val;
-      else A[static_cast<int64_t>(c) * k + o] = val;
+  exact_finish(E, d, k, r, Xw, len, sweeps, B, A, sigma, stats, obj, norm2, order);
+}
+
+// ---------------------------------------------------------------------------
+// Exact SVD, block one-sided Jacobi.  The n vectors (padded with zero vectors
+// to nb blocks of kBjW, nb even) live in fp32 in global memory, rows padded
+// with zeros to ldx = 64 * nq.  nb / 2 workgroups run concurrently (one
+// cooperative launch); in block round rho workgroup g holds the block pair
+// (rr_player(g, rho, nb), rr_player(nb - 1 - g, rho, nb)) in LDS and rotates
+// every cross pair of the two blocks (kBjW rounds of kBjW disjoint pairs;
+// pair c meets column (c + j) mod kBjW of the other block in round j); in
+// block round 0 it first rotates the pairs inside each of its two blocks
+// (round-robin, kBjW - 1 rounds).  nb - 1 block rounds make one sweep, in
+// which every pair of vectors meets once.  Between block rounds the
+// workgroups write their blocks back and meet at a grid barrier.  A pair is
+// rotated when |x_p . x_q| > kBjTol * |x_p| |x_q|: the three dots are summed
+// in fp64 (the fp32 products are exact), the rotation is computed in fp64 and
+// each rotated element is rounded to fp32 once.  The sweeps stop after the
+// first sweep without a rotation (at most kBjMaxSweeps).
+constexpr int kBjW = 16;
+constexpr int kBjThreads = 16 * kBjW;   // one 16-lane group per pair
+constexpr int kBjMaxSweeps = 60;
+constexpr double kBjTol = 1e-7;
+constexpr unsigned kBjSpinLimit = 1u << 20;
+
+struct BjSync {
+  unsigned bar;      // grid-barrier arrivals, monotone over the launch
+  unsigned err;      // set when a barrier wait gave up
+  unsigned sweeps;   // sweeps run
+  unsigned pad;
+  unsigned rot[kBjMaxSweeps];   // per sweep: workgroups that rotated
+};
+
+static_assert(sizeof(BjSync) <= 512, "BjSync");
+constexpr int64_t kBjMaxLds = 65536;
+// LDS of one workgroup: two blocks of (64 * ceil(len / 64) + 4)-float columns.
+inline int64_t bj_lds_bytes(int64_t len) { return 2 * kBjW * (64 * ((len + 63) / 64) + 4) * 4; }
+inline bool bj_fits(int64_t len) { return bj_lds_bytes(len) <= kBjMaxLds; }
+inline int64_t bj_blocks(int64_t n) {
+  const int64_t nb = (n + kBjW - 1) / kBjW;
+  return nb + (nb & 1);
+}
+
+// Sum over the 16 lanes of a DPP row; every lane of the row ends with the
+// same value (the pairings are symmetric, so each lane adds the same operands).
+template <int CTRL>
+__device__ __forceinline__ double bj_dpp(double v) {
+  const int lo = __builtin_amdgcn_mov_dpp(__double2loint(v), CTRL, 0xF, 0xF, false);
+  const int hi = __builtin_amdgcn_mov_dpp(__double2hiint(v), CTRL, 0xF, 0xF, false);
+  return __hiloint2double(hi, lo);
+}
+__device__ __forceinline__ double bj_sum16(double v) {
+  v += bj_dpp<0xB1>(v);    // quad_perm [1,0,3,2]
+  v += bj_dpp<0x4E>(v);    // quad_perm [2,3,0,1]
+  v += bj_dpp<0x141>(v);   // row_half_mirror
+  v += bj_dpp<0x140>(v);   // row_mirror
+  return v;
+}
+
+// Rotate LDS columns p and q (stride ldl floats, 64 * nq rows) by the 16 lanes
+// of one DPP row; l16 = lane within the row.  Returns 1 if it rotated.
+__device__ int bj_pair(float* lds, int ldl, int nq, int p, int q, int l16) {
+  const float4* up = reinterpret_cast<const float4*>(lds + p * ldl) + l16;
+  const float4* wp = reinterpret_cast<const float4*>(lds + q * ldl) + l16;
+  double al = 0.0, be = 0.0, ga = 0.0;
+  for (int j = 0; j < nq; ++j) {
+    const float4 u = up[16 * j], w = wp[16 * j];
+    const float uu[4] = {u.x, u.y, u.z, u.w}, ww[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const double a = uu[e], b = ww[e];
+      al = fma(a, a, al);
+      be = fma(b, b, be);
+      ga = fma(a, b, ga);
     }
   }
-  if (tid < r) sigma[tid] = static_cast<float>(sqrt(norm2[order[tid]]));
-  double s2 = 0.0;
-  for (int c = 0; c < r; ++c) s2 += norm2[order[c]];
-  if (tid == 0 && stats) {
-    stats[0] = s2;
-    stats[1] = sweeps;
+  al = bj_sum16(al);
+  be = bj_sum16(be);
+  ga = bj_sum16(ga);
+  if (ga == 0.0 || fabs(ga) <= kBjTol * sqrt(al * be)) return 0;
+  const double zeta = (be - al) / (2.0 * ga);
+  const double t = (zeta >= 0.0 ? 1.0 : -1.0) / (fabs(zeta) + sqrt(1.0 + zeta * zeta));
+  const double c = 1.0 / sqrt(1.0 + t * t), sn = c * t;
+  float4* uo = reinterpret_cast<float4*>(lds + p * ldl) + l16;
+  float4* wo = reinterpret_cast<float4*>(lds + q * ldl) + l16;
+  for (int j = 0; j < nq; ++j) {
+    const float4 u = uo[16 * j], w = wo[16 * j];
+    const float uu[4] = {u.x, u.y, u.z, u.w}, ww[4] = {w.x, w.y, w.z, w.w};
+    float xp[4], xq[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const double a = uu[e], b = ww[e];
+      xp[e] = static_cast<float>(fma(c, a, -(sn * b)));
+      xq[e] = static_cast<float>(fma(sn, a, c * b));
+    }
+    uo[16 * j] = make_float4(xp[0], xp[1], xp[2], xp[3]);
+    wo[16 * j] = make_float4(xq[0], xq[1], xq[2], xq[3]);
   }
-  write_objective(obj, s2);
+  return 1;
+}
+
+// Block pair (bp, bq) between X (stride ldx) and LDS (stride ldl).
+__device__ void bj_move(float* X, int64_t ldx, int nq, int ldl, int bp, int bq, bool load, float* lds) {
+  const int per_col = 16 * nq;
+  for (int idx = threadIdx.x; idx < 2 * kBjW * per_col; idx += kBjThreads) {
+    const int col = idx / per_col, q = idx - col * per_col;
+    const int64_t gc = col < kBjW ? static_cast<int64_t>(bp) * kBjW + col : static_cast<int64_t>(bq) * kBjW + col - kBjW;
+    float4* g = reinterpret_cast<float4*>(X + gc * ldx) + q;
+    float4* l = reinterpret_cast<float4*>(lds + col * ldl) + q;
+    if (load) *l = *g;
+    else *g = *l;
+  }
+}
+
+// Grid barrier for the co-resident workgroups of a cooperative launch: thread 0
+// publishes the workgroup's stores (device-scope fence), arrives, and waits until
+// `target` arrivals; the wait is bounded, and a wait that gives up (or sees that
+// another workgroup gave up) sets err and makes every workgroup leave.
+__device__ bool bj_grid_barrier(BjSync* sy, unsigned target) {
+  __shared__ int ok;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    __threadfence();
+    atomicAdd(&sy->bar, 1u);
+    int good = 1;
+    unsigned spins = 0;
+    while (__hip_atomic_load(&sy->bar, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
+      if (__hip_atomic_load(&sy->err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u || ++spins > kBjSpinLimit) {
+        atomicOr(&sy->err, 1u);
+        good = 0;
+        break;
+      }
+      __builtin_amdgcn_s_sleep(2);
+    }
+    __threadfence();
+    ok = good;
+  }
+  __syncthreads();
+  return ok != 0;
+}
+
+__global__ void bj_load_kernel(const float* __restrict__ E, int64_t d, int64_t k, int n, int64_t ncols, int64_t ldx,
+                               float* __restrict__ X) {
+  const int64_t e = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (e >= ncols * ldx) return;
+  const bool trans = k > d;
+  const int64_t len = trans ? k : d;
+  const int64_t c = e / ldx, i = e - c * ldx;
+  float v = 0.f;
+  if (c < n && i < len) v = trans ? E[c * k + i] : E[i * k + c];
+  X[e] = v;
+}
+
+__global__ __launch_bounds__(kBjThreads) void bj_sweep_kernel(float* __restrict__ X, int64_t ldx, int nq,
+                                                             BjSync* __restrict__ sy) {
+  extern __shared__ float4 bj_lds4[];
+  float* lds = reinterpret_cast<float*>(bj_lds4);
+  __shared__ int any_rot;
+  const int G = gridDim.x, nb = 2 * G, g = blockIdx.x;
+  const int tid = threadIdx.x, grp = tid >> 4, l16 = tid & 15;
+  const int ldl = 64 * nq + 4;
+  unsigned nbar = 0;
+  int sweep = 0;
+  for (; sweep < kBjMaxSweeps; ++sweep) {
+    if (tid == 0) any_rot = 0;
+    for (int rnd = 0; rnd < nb - 1; ++rnd) {
+      const int bp = rr_player(g, rnd, nb), bq = rr_player(nb - 1 - g, rnd, nb);
+      bj_move(X, ldx, nq, ldl, bp, bq, true, lds);
+      __syncthreads();
+      int rot = 0;
+      if (rnd == 0) {
+        const int blk = grp / (kBjW / 2), i = grp % (kBjW / 2);
+        for (int ir = 0; ir < kBjW - 1; ++ir) {
+          const int x = rr_player(i, ir, kBjW), y = rr_player(kBjW - 1 - i, ir, kBjW);
+          rot |= bj_pair(lds, ldl, nq, blk * kBjW + min(x, y), blk * kBjW + max(x, y), l16);
+          __syncthreads();
+        }
+      }
+      for (int j = 0; j < kBjW; ++j) {
+        const int a = grp, b = kBjW + (grp + j) % kBjW;   // a in block bp, b in block bq
+        rot |= bp < bq ? bj_pair(lds, ldl, nq, a, b, l16) : bj_pair(lds, ldl, nq, b, a, l16);
+        __syncthreads();
+      }
+      if (rot && l16 == 0) any_rot = 1;
+      bj_move(X, ldx, nq, ldl, bp, bq, false, lds);
+      if (rnd == nb - 2) {
+        __syncthreads();
+        if (tid == 0 && any_rot) atomicAdd(&sy->rot[sweep], 1u);
+      }
+      if (!bj_grid_barrier(sy, static_cast<unsigned>(G) * ++nbar)) return;
+    }
+    // every workgroup's count for this sweep arrived before the last barrier
+    if (__hip_atomic_load(&sy->rot[sweep], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0u) break;
+  }
+  if (g == 0 && tid == 0) sy->sweeps = static_cast<unsigned>(sweep < kBjMaxSweeps ? sweep + 1 : kBjMaxSweeps);
+}
+
+__global__ __launch_bounds__(1024) void bj_finish_kernel(const float* __restrict__ E, int64_t d, int64_t k, int r,
+                                                        const float* __restrict__ X, int64_t ldx,
+                                                        const BjSync* __restrict__ sy, float* __restrict__ B,
+                                                        float* __restrict__ A, float* __restrict__ sigma,
+                                                        double* __restrict__ stats, ObjectiveArgs obj) {
+  __shared__ double norm2[kMaxExact];
+  __shared__ int order[kMaxExact];
+  exact_finish(E, d, k, r, X, ldx, static_cast<int>(sy->sweeps), B, A, sigma, stats, obj, norm2, order);
+  if (sy->err != 0u) {   // a barrier wait gave up: no valid result
+    if (threadIdx.x < r) sigma[threadIdx.x] = __builtin_nanf("");
+    if (threadIdx.x == 0 && stats) stats[2] = 1.0;
+  }
 }
 
 __global__ __launch_bounds__(256) void objective_kernel(ObjectiveArgs obj) { write_objective(obj, 0.0); }
@@ -1006,8 +1228,17 @@ SvdPlan make_svd_plan(int64_t d, int64_t k, int r, int oversample, bool exact) {
   auto take = [&](int64_t bytes) { const int64_t o = off; off += round_up(bytes, 256); return o; };
   if (exact) {
     const int64_t n = d < k ? d : k;
+    const int64_t len = d > k ? d : k;
     p.l = static_cast<int>(n);
-    p.off_x = take((n + 1) * (d > k ? d : k) * 8);
+    p.bj = bj_fits(len);
+    int64_t xbytes = (n + 1) * len * 8;   // fp64 vectors of the single-workgroup Jacobi
+    if (p.bj) {
+      const int64_t nb = bj_blocks(n);
+      const int64_t bj_bytes = nb * kBjW * cdiv(len, 64) * 64 * 4;
+      if (bj_bytes > xbytes) xbytes = bj_bytes;
+    }
+    p.off_x = take(xbytes);
+    p.off_sync = take(sizeof(BjSync));
     p.off_stats = take(64);
     p.bytes = off;
     return p;
@@ -1122,6 +1353,32 @@ hipError_t run_lowrank(const float* E, const SvdPlan& pl, int q, const float* om
                        hipStream_t s) {
   const int64_t d = pl.d, k = pl.k;
   const int r = pl.r, l = pl.l;
+  if (pl.exact && pl.bj) {
+    const int64_t n = d < k ? d : k, len = d > k ? d : k;
+    int nq = static_cast<int>(cdiv(len, 64));
+    const int nb = static_cast<int>(bj_blocks(n));
+    int64_t ldx = 64 * static_cast<int64_t>(nq);
+    const int64_t ncols = static_cast<int64_t>(nb) * kBjW;
+    float* X = reinterpret_cast<float*>(ws + pl.off_x);
+    BjSync* sy = reinterpret_cast<BjSync*>(ws + pl.off_sync);
+    double* stats = reinterpret_cast<double*>(ws + pl.off_stats);
+    LQ_LAUNCH("zero_u32", zero_u32_kernel, dim3(1), dim3(256), 0, s, reinterpret_cast<unsigned*>(sy),
+              static_cast<int>(sizeof(BjSync) / 4));
+    LQ_LAUNCH("exact_load", bj_load_kernel, dim3(static_cast<unsigned>(cdiv(ncols * ldx, 256))), dim3(256), 0, s, E, d,
+              k, static_cast<int>(n), ncols, ldx, X);
+    {
+      ProfScope ps("exact_sweeps");
+      if (ps.start()) (void)hipEventRecord(ps.start(), s);
+      void* args[] = {&X, &ldx, &nq, &sy};
+      const hipError_t e = hipLaunchCooperativeKernel(reinterpret_cast<const void*>(bj_sweep_kernel), dim3(nb / 2),
+                                                      dim3(kBjThreads), args, bj_lds_bytes(len), s);
+      if (ps.stop()) (void)hipEventRecord(ps.stop(), s);
+      if (e != hipSuccess) return e;
+    }
+    LQ_LAUNCH("exact_finish", bj_finish_kernel, dim3(1), dim3(1024), 0, s, E, d, k, r, X, ldx, sy, B, A, sigma, stats,
+              obj);
+    return hipGetLastError();
+  }
   if (pl.exact) {
     double* Xw = reinterpret_cast<double*>(ws + pl.off_x);
     LQ_LAUNCH("exact_jacobi", exact_jacobi_kernel, dim3(1), dim3(1024), 0, s, E, d, k, r, Xw, B, A, sigma,
