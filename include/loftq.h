@@ -199,7 +199,11 @@ size_t loftq_qlora_forward_noalloc_max_bytes(void);
 
 /* Low-rank step ("LoftQ...", §2.3: best rank-r approximation of W - Q from its
  * r largest singular triplets, Delta = U_r S_r V_r^T).  exact = 1: the SVD of E
- * itself (one-sided Jacobi, min(rows, cols) <= 512).  exact = 0: randomized
+ * itself by one-sided (Hestenes) Jacobi on its min(rows, cols) <= 512 short-side
+ * vectors (fp64), swept until a sweep finds every pair orthogonal to tol times the
+ * product of their norms: when max(rows, cols) <= 576 the pairs are spread over
+ * co-resident workgroups of one cooperative launch (tol = 1e-7), else one
+ * workgroup runs them (tol = 1e-14).  exact = 0: randomized
  * subspace iteration with sketch width l = r + oversample (l <= min(rows, cols),
  * l <= 80, r <= 64) and power_iters rounds; the sketch is `omega` (cols x l fp32) or, if
  * NULL, the +-1 SplitMix64 sketch of (seed, t).  Outputs B = U_r S_r^{1/2},

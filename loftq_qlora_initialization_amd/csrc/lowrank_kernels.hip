@@ -952,22 +952,22 @@ __global__ __launch_bounds__(1024) void exact_jacobi_kernel(const float* __restr
 
 // ---------------------------------------------------------------------------
 // Exact SVD, block one-sided Jacobi.  The n vectors (padded with zero vectors
-// to nb blocks of kBjW, nb even) live in fp32 in global memory, rows padded
-// with zeros to ldx = 64 * nq.  nb / 2 workgroups run concurrently (one
+// to nb blocks of kBjW, nb even) live in fp64 in global memory, rows padded
+// with zeros to ldx = 64 * NQ.  nb / 2 workgroups run concurrently (one
 // cooperative launch); in block round rho workgroup g holds the block pair
 // (rr_player(g, rho, nb), rr_player(nb - 1 - g, rho, nb)) in LDS and rotates
-// every cross pair of the two blocks (kBjW rounds of kBjW disjoint pairs;
-// pair c meets column (c + j) mod kBjW of the other block in round j); in
-// block round 0 it first rotates the pairs inside each of its two blocks
-// (round-robin, kBjW - 1 rounds).  nb - 1 block rounds make one sweep, in
-// which every pair of vectors meets once.  Between block rounds the
-// workgroups write their blocks back and meet at a grid barrier.  A pair is
-// rotated when |x_p . x_q| > kBjTol * |x_p| |x_q|: the three dots are summed
-// in fp64 (the fp32 products are exact), the rotation is computed in fp64 and
-// each rotated element is rounded to fp32 once.  The sweeps stop after the
-// first sweep without a rotation (at most kBjMaxSweeps).
+// every cross pair of the two blocks: in round j the 16-lane group c rotates
+// column c of the first block (kept in its registers for all kBjW rounds)
+// against column (c + j) mod kBjW of the second.  In block round 0 it first
+// rotates the pairs inside each of its two blocks (round-robin, kBjW - 1
+// rounds).  nb - 1 block rounds make one sweep, in which every pair of
+// vectors meets once.  Between block rounds the workgroups write their blocks
+// back and meet at a grid barrier.  A pair is rotated when
+// |x_p . x_q| > kBjTol * |x_p| |x_q|.  The sweeps stop after the first sweep
+// without a rotation (at most kBjMaxSweeps).
 constexpr int kBjW = 16;
 constexpr int kBjThreads = 16 * kBjW;   // one 16-lane group per pair
+constexpr int kBjMaxNq = 9;             // vectors of up to 64 * kBjMaxNq = 576 elements
 constexpr int kBjMaxSweeps = 60;
 constexpr double kBjTol = 1e-7;
 constexpr unsigned kBjSpinLimit = 1u << 20;
@@ -979,12 +979,13 @@ struct BjSync {
   unsigned pad;
   unsigned rot[kBjMaxSweeps];   // per sweep: workgroups that rotated
 };
-
 static_assert(sizeof(BjSync) <= 512, "BjSync");
-constexpr int64_t kBjMaxLds = 65536;
-// LDS of one workgroup: two blocks of (64 * ceil(len / 64) + 4)-float columns.
-inline int64_t bj_lds_bytes(int64_t len) { return 2 * kBjW * (64 * ((len + 63) / 64) + 4) * 4; }
-inline bool bj_fits(int64_t len) { return bj_lds_bytes(len) <= kBjMaxLds; }
+
+// LDS of one workgroup: two blocks of (64 * NQ + 2)-double columns.
+inline int64_t bj_nq(int64_t len) { return (len + 63) / 64; }
+inline int64_t bj_lds_bytes(int64_t len) { return 2 * kBjW * (64 * bj_nq(len) + 2) * 8; }
+constexpr int64_t kBjMaxLds = 159 * 1024;
+inline bool bj_fits(int64_t len) { return bj_nq(len) <= kBjMaxNq && bj_lds_bytes(len) <= kBjMaxLds; }
 inline int64_t bj_blocks(int64_t n) {
   const int64_t nb = (n + kBjW - 1) / kBjW;
   return nb + (nb & 1);
@@ -1006,56 +1007,79 @@ __device__ __forceinline__ double bj_sum16(double v) {
   return v;
 }
 
-// Rotate LDS columns p and q (stride ldl floats, 64 * nq rows) by the 16 lanes
-// of one DPP row; l16 = lane within the row.  Returns 1 if it rotated.
-__device__ int bj_pair(float* lds, int ldl, int nq, int p, int q, int l16) {
-  const float4* up = reinterpret_cast<const float4*>(lds + p * ldl) + l16;
-  const float4* wp = reinterpret_cast<const float4*>(lds + q * ldl) + l16;
+// Lane l16 of a 16-lane group holds elements 64 j + 4 l16 + e (e < 4) of a column.
+template <int NQ>
+__device__ __forceinline__ void bj_get(const double* col, int l16, double (&v)[NQ][4]) {
+#pragma unroll
+  for (int j = 0; j < NQ; ++j) {
+    const double2* p = reinterpret_cast<const double2*>(col + 64 * j + 4 * l16);
+    const double2 x = p[0], y = p[1];
+    v[j][0] = x.x; v[j][1] = x.y; v[j][2] = y.x; v[j][3] = y.y;
+  }
+}
+template <int NQ>
+__device__ __forceinline__ void bj_put(double* col, int l16, const double (&v)[NQ][4]) {
+#pragma unroll
+  for (int j = 0; j < NQ; ++j) {
+    double2* p = reinterpret_cast<double2*>(col + 64 * j + 4 * l16);
+    p[0] = make_double2(v[j][0], v[j][1]);
+    p[1] = make_double2(v[j][2], v[j][3]);
+  }
+}
+
+// One Jacobi rotation of the pair (x_p, x_q) held by a 16-lane group; returns
+// true if it rotated.
+template <int NQ>
+__device__ __forceinline__ bool bj_rot(double (&xp)[NQ][4], double (&xq)[NQ][4]) {
   double al = 0.0, be = 0.0, ga = 0.0;
-  for (int j = 0; j < nq; ++j) {
-    const float4 u = up[16 * j], w = wp[16 * j];
-    const float uu[4] = {u.x, u.y, u.z, u.w}, ww[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+  for (int j = 0; j < NQ; ++j)
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const double a = uu[e], b = ww[e];
-      al = fma(a, a, al);
-      be = fma(b, b, be);
-      ga = fma(a, b, ga);
+      al = fma(xp[j][e], xp[j][e], al);
+      be = fma(xq[j][e], xq[j][e], be);
+      ga = fma(xp[j][e], xq[j][e], ga);
     }
-  }
   al = bj_sum16(al);
   be = bj_sum16(be);
   ga = bj_sum16(ga);
-  if (ga == 0.0 || fabs(ga) <= kBjTol * sqrt(al * be)) return 0;
-  const double zeta = (be - al) / (2.0 * ga);
-  const double t = (zeta >= 0.0 ? 1.0 : -1.0) / (fabs(zeta) + sqrt(1.0 + zeta * zeta));
-  const double c = 1.0 / sqrt(1.0 + t * t), sn = c * t;
-  float4* uo = reinterpret_cast<float4*>(lds + p * ldl) + l16;
-  float4* wo = reinterpret_cast<float4*>(lds + q * ldl) + l16;
-  for (int j = 0; j < nq; ++j) {
-    const float4 u = uo[16 * j], w = wo[16 * j];
-    const float uu[4] = {u.x, u.y, u.z, u.w}, ww[4] = {w.x, w.y, w.z, w.w};
-    float xp[4], xq[4];
+  if (ga == 0.0 || ga * ga <= (kBjTol * kBjTol) * (al * be)) return false;
+  // zeta = (be - al) / (2 ga) and t = sign(zeta) / (|zeta| + sqrt(1 + zeta^2)) only
+  // pick the angle, so t is formed in fp32 (an angle off by ~1e-7 of itself still
+  // shrinks the pair's dot by that factor); c = 1 / sqrt(1 + t^2) and s = c t are
+  // formed in fp64 from that t, so the rotation stays orthogonal to fp64 rounding.
+  const double g2 = 2.0 * ga;
+  double rg = __builtin_amdgcn_rcp(g2);
+  rg = fma(rg, fma(-g2, rg, 1.0), rg);
+  const float zf = static_cast<float>((be - al) * rg);
+  const float az = fabsf(zf);
+  float tf = az > 1e18f ? 0.5f * __builtin_amdgcn_rcpf(az)
+                        : __builtin_amdgcn_rcpf(az + __builtin_amdgcn_sqrtf(fmaf(az, az, 1.f)));
+  const double t = zf >= 0.f ? tf : -tf;
+  const double x = fma(t, t, 1.0);
+  double c = __builtin_amdgcn_rsq(x);
+  c = c * fma(-0.5 * x * c, c, 1.5);
+  c = c * fma(-0.5 * x * c, c, 1.5);
+  const double sn = c * t;
+#pragma unroll
+  for (int j = 0; j < NQ; ++j)
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const double a = uu[e], b = ww[e];
-      xp[e] = static_cast<float>(fma(c, a, -(sn * b)));
-      xq[e] = static_cast<float>(fma(sn, a, c * b));
+      const double u = xp[j][e], w = xq[j][e];
+      xp[j][e] = fma(c, u, -(sn * w));
+      xq[j][e] = fma(sn, u, c * w);
     }
-    uo[16 * j] = make_float4(xp[0], xp[1], xp[2], xp[3]);
-    wo[16 * j] = make_float4(xq[0], xq[1], xq[2], xq[3]);
-  }
-  return 1;
+  return true;
 }
 
-// Block pair (bp, bq) between X (stride ldx) and LDS (stride ldl).
-__device__ void bj_move(float* X, int64_t ldx, int nq, int ldl, int bp, int bq, bool load, float* lds) {
-  const int per_col = 16 * nq;
+// Block pair (bp, bq) between X (stride ldx doubles) and LDS (stride ldl).
+__device__ void bj_move(double* X, int64_t ldx, int ldl, int bp, int bq, bool load, double* lds) {
+  const int per_col = static_cast<int>(ldx / 2);   // double2 per column
   for (int idx = threadIdx.x; idx < 2 * kBjW * per_col; idx += kBjThreads) {
     const int col = idx / per_col, q = idx - col * per_col;
     const int64_t gc = col < kBjW ? static_cast<int64_t>(bp) * kBjW + col : static_cast<int64_t>(bq) * kBjW + col - kBjW;
-    float4* g = reinterpret_cast<float4*>(X + gc * ldx) + q;
-    float4* l = reinterpret_cast<float4*>(lds + col * ldl) + q;
+    double2* g = reinterpret_cast<double2*>(X + gc * ldx) + q;
+    double2* l = reinterpret_cast<double2*>(lds + col * ldl) + q;
     if (load) *l = *g;
     else *g = *l;
   }
@@ -1089,49 +1113,68 @@ __device__ bool bj_grid_barrier(BjSync* sy, unsigned target) {
 }
 
 __global__ void bj_load_kernel(const float* __restrict__ E, int64_t d, int64_t k, int n, int64_t ncols, int64_t ldx,
-                               float* __restrict__ X) {
+                               double* __restrict__ X) {
   const int64_t e = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
   if (e >= ncols * ldx) return;
   const bool trans = k > d;
   const int64_t len = trans ? k : d;
   const int64_t c = e / ldx, i = e - c * ldx;
-  float v = 0.f;
+  double v = 0.0;
   if (c < n && i < len) v = trans ? E[c * k + i] : E[i * k + c];
   X[e] = v;
 }
 
-__global__ __launch_bounds__(kBjThreads) void bj_sweep_kernel(float* __restrict__ X, int64_t ldx, int nq,
-                                                             BjSync* __restrict__ sy) {
-  extern __shared__ float4 bj_lds4[];
-  float* lds = reinterpret_cast<float*>(bj_lds4);
+template <int NQ>
+__global__ __launch_bounds__(kBjThreads) void bj_sweep_kernel(double* __restrict__ X, BjSync* __restrict__ sy) {
+  extern __shared__ double2 bj_lds2[];
+  double* lds = reinterpret_cast<double*>(bj_lds2);
+  constexpr int64_t ldx = 64 * NQ;
+  constexpr int ldl = 64 * NQ + 2;
   __shared__ int any_rot;
   const int G = gridDim.x, nb = 2 * G, g = blockIdx.x;
   const int tid = threadIdx.x, grp = tid >> 4, l16 = tid & 15;
-  const int ldl = 64 * nq + 4;
   unsigned nbar = 0;
   int sweep = 0;
   for (; sweep < kBjMaxSweeps; ++sweep) {
     if (tid == 0) any_rot = 0;
     for (int rnd = 0; rnd < nb - 1; ++rnd) {
       const int bp = rr_player(g, rnd, nb), bq = rr_player(nb - 1 - g, rnd, nb);
-      bj_move(X, ldx, nq, ldl, bp, bq, true, lds);
+      bj_move(X, ldx, ldl, bp, bq, true, lds);
       __syncthreads();
-      int rot = 0;
+      bool rot = false;
+      double xa[NQ][4], xb[NQ][4];
       if (rnd == 0) {
         const int blk = grp / (kBjW / 2), i = grp % (kBjW / 2);
         for (int ir = 0; ir < kBjW - 1; ++ir) {
           const int x = rr_player(i, ir, kBjW), y = rr_player(kBjW - 1 - i, ir, kBjW);
-          rot |= bj_pair(lds, ldl, nq, blk * kBjW + min(x, y), blk * kBjW + max(x, y), l16);
+          double* cp = lds + (blk * kBjW + min(x, y)) * ldl;
+          double* cq = lds + (blk * kBjW + max(x, y)) * ldl;
+          bj_get<NQ>(cp, l16, xa);
+          bj_get<NQ>(cq, l16, xb);
+          if (bj_rot<NQ>(xa, xb)) {
+            rot = true;
+            bj_put<NQ>(cp, l16, xa);
+            bj_put<NQ>(cq, l16, xb);
+          }
           __syncthreads();
         }
       }
+      // cross pairs: column grp of the first block stays in xa
+      double* ca = lds + grp * ldl;
+      bj_get<NQ>(ca, l16, xa);
       for (int j = 0; j < kBjW; ++j) {
-        const int a = grp, b = kBjW + (grp + j) % kBjW;   // a in block bp, b in block bq
-        rot |= bp < bq ? bj_pair(lds, ldl, nq, a, b, l16) : bj_pair(lds, ldl, nq, b, a, l16);
+        double* cb = lds + (kBjW + (grp + j) % kBjW) * ldl;
+        bj_get<NQ>(cb, l16, xb);
+        if (bp < bq ? bj_rot<NQ>(xa, xb) : bj_rot<NQ>(xb, xa)) {
+          rot = true;
+          bj_put<NQ>(cb, l16, xb);
+        }
         __syncthreads();
       }
+      bj_put<NQ>(ca, l16, xa);
       if (rot && l16 == 0) any_rot = 1;
-      bj_move(X, ldx, nq, ldl, bp, bq, false, lds);
+      __syncthreads();
+      bj_move(X, ldx, ldl, bp, bq, false, lds);
       if (rnd == nb - 2) {
         __syncthreads();
         if (tid == 0 && any_rot) atomicAdd(&sy->rot[sweep], 1u);
@@ -1144,8 +1187,13 @@ __global__ __launch_bounds__(kBjThreads) void bj_sweep_kernel(float* __restrict_
   if (g == 0 && tid == 0) sy->sweeps = static_cast<unsigned>(sweep < kBjMaxSweeps ? sweep + 1 : kBjMaxSweeps);
 }
 
+using BjSweepFn = void (*)(double*, BjSync*);
+constexpr BjSweepFn kBjSweep[kBjMaxNq] = {bj_sweep_kernel<1>, bj_sweep_kernel<2>, bj_sweep_kernel<3>,
+                                          bj_sweep_kernel<4>, bj_sweep_kernel<5>, bj_sweep_kernel<6>,
+                                          bj_sweep_kernel<7>, bj_sweep_kernel<8>, bj_sweep_kernel<9>};
+
 __global__ __launch_bounds__(1024) void bj_finish_kernel(const float* __restrict__ E, int64_t d, int64_t k, int r,
-                                                        const float* __restrict__ X, int64_t ldx,
+                                                        const double* __restrict__ X, int64_t ldx,
                                                         const BjSync* __restrict__ sy, float* __restrict__ B,
                                                         float* __restrict__ A, float* __restrict__ sigma,
                                                         double* __restrict__ stats, ObjectiveArgs obj) {
@@ -1234,7 +1282,7 @@ SvdPlan make_svd_plan(int64_t d, int64_t k, int r, int oversample, bool exact) {
     int64_t xbytes = (n + 1) * len * 8;   // fp64 vectors of the single-workgroup Jacobi
     if (p.bj) {
       const int64_t nb = bj_blocks(n);
-      const int64_t bj_bytes = nb * kBjW * cdiv(len, 64) * 64 * 4;
+      const int64_t bj_bytes = nb * kBjW * bj_nq(len) * 64 * 8;
       if (bj_bytes > xbytes) xbytes = bj_bytes;
     }
     p.off_x = take(xbytes);
@@ -1355,11 +1403,11 @@ hipError_t run_lowrank(const float* E, const SvdPlan& pl, int q, const float* om
   const int r = pl.r, l = pl.l;
   if (pl.exact && pl.bj) {
     const int64_t n = d < k ? d : k, len = d > k ? d : k;
-    int nq = static_cast<int>(cdiv(len, 64));
+    const int nq = static_cast<int>(bj_nq(len));
     const int nb = static_cast<int>(bj_blocks(n));
-    int64_t ldx = 64 * static_cast<int64_t>(nq);
+    const int64_t ldx = 64 * static_cast<int64_t>(nq);
     const int64_t ncols = static_cast<int64_t>(nb) * kBjW;
-    float* X = reinterpret_cast<float*>(ws + pl.off_x);
+    double* X = reinterpret_cast<double*>(ws + pl.off_x);
     BjSync* sy = reinterpret_cast<BjSync*>(ws + pl.off_sync);
     double* stats = reinterpret_cast<double*>(ws + pl.off_stats);
     LQ_LAUNCH("zero_u32", zero_u32_kernel, dim3(1), dim3(256), 0, s, reinterpret_cast<unsigned*>(sy),
@@ -1369,9 +1417,9 @@ hipError_t run_lowrank(const float* E, const SvdPlan& pl, int q, const float* om
     {
       ProfScope ps("exact_sweeps");
       if (ps.start()) (void)hipEventRecord(ps.start(), s);
-      void* args[] = {&X, &ldx, &nq, &sy};
-      const hipError_t e = hipLaunchCooperativeKernel(reinterpret_cast<const void*>(bj_sweep_kernel), dim3(nb / 2),
-                                                      dim3(kBjThreads), args, bj_lds_bytes(len), s);
+      void* args[] = {&X, &sy};
+      const hipError_t e = hipLaunchCooperativeKernel(reinterpret_cast<const void*>(kBjSweep[nq - 1]), dim3(nb / 2),
+                                                      dim3(kBjThreads), args, static_cast<unsigned>(bj_lds_bytes(len)), s);
       if (ps.stop()) (void)hipEventRecord(ps.stop(), s);
       if (e != hipSuccess) return e;
     }
