@@ -1072,28 +1072,48 @@ __device__ __forceinline__ bool bj_rot(double (&xp)[NQ][4], double (&xq)[NQ][4])
   return true;
 }
 
-// Block pair (bp, bq) between X (stride ldx doubles) and LDS (stride ldl).
-__device__ void bj_move(double* X, int64_t ldx, int ldl, int bp, int bq, bool load, double* lds) {
-  const int per_col = static_cast<int>(ldx / 2);   // double2 per column
-  for (int idx = threadIdx.x; idx < 2 * kBjW * per_col; idx += kBjThreads) {
+// Block pair (bp, bq) between X (stride 64 NQ doubles) and LDS (stride
+// 64 NQ + 2): each thread issues all of its loads before its first store.
+template <int NQ>
+__device__ __forceinline__ void bj_move(double* X, int bp, int bq, bool load, double* lds) {
+  constexpr int per_col = 32 * NQ;   // double2 per column
+  constexpr int ldl = 64 * NQ + 2;
+  constexpr int kPer = 2 * kBjW * per_col / kBjThreads;
+  static_assert(kPer * kBjThreads == 2 * kBjW * per_col, "block pair split");
+  double2 v[kPer];
+  double2* gp[kPer];
+  double2* lp[kPer];
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int idx = static_cast<int>(threadIdx.x) + i * kBjThreads;
     const int col = idx / per_col, q = idx - col * per_col;
     const int64_t gc = col < kBjW ? static_cast<int64_t>(bp) * kBjW + col : static_cast<int64_t>(bq) * kBjW + col - kBjW;
-    double2* g = reinterpret_cast<double2*>(X + gc * ldx) + q;
-    double2* l = reinterpret_cast<double2*>(lds + col * ldl) + q;
-    if (load) *l = *g;
-    else *g = *l;
+    gp[i] = reinterpret_cast<double2*>(X + gc * (64 * NQ)) + q;
+    lp[i] = reinterpret_cast<double2*>(lds + col * ldl) + q;
+  }
+  if (load) {
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) v[i] = *gp[i];
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) *lp[i] = v[i];
+  } else {
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) v[i] = *lp[i];
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) *gp[i] = v[i];
   }
 }
 
 // Grid barrier for the co-resident workgroups of a cooperative launch: thread 0
-// publishes the workgroup's stores (device-scope fence), arrives, and waits until
-// `target` arrivals; the wait is bounded, and a wait that gives up (or sees that
-// another workgroup gave up) sets err and makes every workgroup leave.
+// publishes the workgroup's stores (device-scope release), arrives, waits until
+// `target` arrivals and acquires the others' stores; the wait is bounded, and a
+// wait that gives up (or sees that another workgroup gave up) sets err and makes
+// every workgroup leave.
 __device__ bool bj_grid_barrier(BjSync* sy, unsigned target) {
   __shared__ int ok;
   __syncthreads();
   if (threadIdx.x == 0) {
-    __threadfence();
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
     atomicAdd(&sy->bar, 1u);
     int good = 1;
     unsigned spins = 0;
@@ -1105,7 +1125,7 @@ __device__ bool bj_grid_barrier(BjSync* sy, unsigned target) {
       }
       __builtin_amdgcn_s_sleep(2);
     }
-    __threadfence();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
     ok = good;
   }
   __syncthreads();
@@ -1128,7 +1148,6 @@ template <int NQ>
 __global__ __launch_bounds__(kBjThreads) void bj_sweep_kernel(double* __restrict__ X, BjSync* __restrict__ sy) {
   extern __shared__ double2 bj_lds2[];
   double* lds = reinterpret_cast<double*>(bj_lds2);
-  constexpr int64_t ldx = 64 * NQ;
   constexpr int ldl = 64 * NQ + 2;
   __shared__ int any_rot;
   const int G = gridDim.x, nb = 2 * G, g = blockIdx.x;
@@ -1139,7 +1158,7 @@ __global__ __launch_bounds__(kBjThreads) void bj_sweep_kernel(double* __restrict
     if (tid == 0) any_rot = 0;
     for (int rnd = 0; rnd < nb - 1; ++rnd) {
       const int bp = rr_player(g, rnd, nb), bq = rr_player(nb - 1 - g, rnd, nb);
-      bj_move(X, ldx, ldl, bp, bq, true, lds);
+      bj_move<NQ>(X, bp, bq, true, lds);
       __syncthreads();
       bool rot = false;
       double xa[NQ][4], xb[NQ][4];
@@ -1174,7 +1193,7 @@ __global__ __launch_bounds__(kBjThreads) void bj_sweep_kernel(double* __restrict
       bj_put<NQ>(ca, l16, xa);
       if (rot && l16 == 0) any_rot = 1;
       __syncthreads();
-      bj_move(X, ldx, ldl, bp, bq, false, lds);
+      bj_move<NQ>(X, bp, bq, false, lds);
       if (rnd == nb - 2) {
         __syncthreads();
         if (tid == 0 && any_rot) atomicAdd(&sy->rot[sweep], 1u);
