@@ -1,5 +1,6 @@
 // C-ABI entry points for the low-rank step and the whole alternating initialisation.
 #include <algorithm>
+#include <mutex>
 #include <vector>
 
 #include "lowrank.h"
@@ -99,7 +100,8 @@ loftq_status_t check_init(const InitArgs& a, loftq_dtype_t wdt, const loftq_conf
 }
 
 // The alternation loop of one validated initialisation, enqueued on stream s.
-hipError_t run_init(const InitArgs& a, loftq_dtype_t wdt, const loftq_config_t& c, char* w, hipStream_t s) {
+hipError_t run_init(const InitArgs& a, loftq_dtype_t wdt, const loftq_config_t& c, char* w, hipStream_t s,
+                    SideLane* side = nullptr) {
   const loftq_config_t* cfg = &c;
   const void* W = a.W;
   const int64_t rows = a.rows, cols = a.cols;
@@ -163,7 +165,7 @@ hipError_t run_init(const InitArgs& a, loftq_dtype_t wdt, const loftq_config_t& 
         e = run_warm_columns(A, sigma, cols, r, pl.svd.nt, sketches + slot * pl.sketch_floats, s);
     }
     if (e == hipSuccess)
-      e = run_lowrank(E, pl.svd, cfg->power_iters, nullptr, om, cfg->seed, t, B, A, sigma, svd_ws, objt, s);
+      e = run_lowrank(E, pl.svd, cfg->power_iters, nullptr, om, cfg->seed, t, B, A, sigma, svd_ws, objt, s, side);
   }
   return e;
 }
@@ -193,8 +195,12 @@ loftq_status_t loftq_lowrank_svd(const float* E, int64_t rows, int64_t cols, int
   const SvdPlan pl = make_svd_plan(rows, cols, r, oversample, exact != 0);
   if (ws_bytes < static_cast<size_t>(pl.bytes)) return LOFTQ_ERR_WORKSPACE;
   const ObjectiveArgs none{nullptr, 0, nullptr, 0, nullptr, nullptr};
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  SideLane* side = side_lane_for(s);
+  std::unique_lock<std::mutex> lk;
+  if (side != nullptr) lk = std::unique_lock<std::mutex>(*side->mu);
   return from_hip(run_lowrank(E, pl, power_iters, omega, nullptr, seed, t, B, A, sigma, static_cast<char*>(ws), none,
-                              static_cast<hipStream_t>(stream)));
+                              s, side));
 }
 
 size_t loftq_workspace_bytes(int64_t rows, int64_t cols, const loftq_config_t* cfg) {
@@ -208,7 +214,11 @@ loftq_status_t loftq_init(const void* W, loftq_dtype_t wdt, int64_t rows, int64_
   const InitArgs a{W, rows, cols, packed, absmax, qabsmax, dq_scale, B, A, objective, sigma};
   loftq_status_t st = check_init(a, wdt, cfg, ws, ws_bytes);
   if (st != LOFTQ_OK) return st;
-  return from_hip(run_init(a, wdt, *cfg, static_cast<char*>(ws), static_cast<hipStream_t>(stream)));
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  SideLane* side = side_lane_for(s);
+  std::unique_lock<std::mutex> lk;
+  if (side != nullptr) lk = std::unique_lock<std::mutex>(*side->mu);
+  return from_hip(run_init(a, wdt, *cfg, static_cast<char*>(ws), s, side));
 }
 
 size_t loftq_batch_workspace_bytes(const loftq_matrix_t* mats, int32_t count, const loftq_config_t* cfg) {

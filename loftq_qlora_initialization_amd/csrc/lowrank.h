@@ -1,6 +1,8 @@
 // Internal declarations for the low-rank step and the alternation driver.
 #pragma once
 
+#include <mutex>
+
 #include "internal.h"
 
 namespace loftq {
@@ -78,9 +80,22 @@ struct SvdPlan {
 SvdPlan make_svd_plan(int64_t d, int64_t k, int r, int oversample, bool exact);
 // omega: caller's k x l sketch (row-major), or omega_frag: a sketch already in
 // fragment order over k_pad rows, or neither: the sketch of alternation t is drawn.
+// A second stream that takes the orthonormalisation solves (Gram sum, Cholesky,
+// R^-1) off the main stream, so that each runs beside the E^T Y product that
+// follows it; the product's split-K reduction, their first consumer, waits for
+// `join`.  Both events are reused: each record is waited on before the next.
+struct SideLane {
+  hipStream_t stream;
+  hipEvent_t fork, join;
+  std::mutex* mu;   // held while a call enqueues through the lane (the events are shared)
+};
+// The side lane of main stream s on the current device (created on first use,
+// kept until the process ends), or null if one cannot be created.
+SideLane* side_lane_for(hipStream_t s);
+
 hipError_t run_lowrank(const float* E, const SvdPlan& pl, int q, const float* omega, const float* omega_frag,
                        uint64_t seed, int t, float* B, float* A, float* sigma, char* ws, const ObjectiveArgs& obj,
-                       hipStream_t s);
+                       hipStream_t s, SideLane* side = nullptr);
 // Sketches of alternations t .. t + count - 1, each rows x 16 nt floats in fragment order, back to back.
 hipError_t run_sketch(uint64_t seed, int t, int count, int64_t k, int l, int nt, int64_t rows, float* out,
                       hipStream_t s);

@@ -21,6 +21,10 @@
 //   panel_small   P S for a row panel P and a small S: B = Q S_B, A = (C S_A)^T
 //   exact_jacobi  single-workgroup one-sided Jacobi SVD for tiny matrices
 // Every reduction runs in a fixed order, so results are deterministic.
+#include <map>
+#include <mutex>
+#include <utility>
+
 #include "lowrank.h"
 #include "reduce.h"
 #include "small_solve.h"
@@ -182,20 +186,15 @@ __device__ __forceinline__ float dpp_f32(float v) {
   return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, true));
 }
 // fp32 sum over an aligned group of G = 16, 8 or 4 lanes; every lane of the
-// group ends with the same total.
+// group ends with the same total, bit for bit (each step pairs lanes
+// symmetrically, so both lanes of a pair add the same two operands).
 template <int G>
 __device__ __forceinline__ float group_sumf(float v) {
   static_assert(G == 16 || G == 8 || G == 4, "16-, 8- or 4-lane groups");
-  if (G == 16) {
-    v += dpp_f32<0x128>(v);   // row_ror:8
-    v += dpp_f32<0x124>(v);   // row_ror:4
-    v += dpp_f32<0x122>(v);   // row_ror:2
-    v += dpp_f32<0x121>(v);   // row_ror:1
-  } else {
-    v += dpp_f32<0xB1>(v);    // quad_perm xor 1
-    v += dpp_f32<0x4E>(v);    // quad_perm xor 2
-    if (G == 8) v += dpp_f32<0x141>(v);   // row_half_mirror: the other quad of the 8
-  }
+  v += dpp_f32<0xB1>(v);                   // quad_perm xor 1
+  v += dpp_f32<0x4E>(v);                   // quad_perm xor 2
+  if (G >= 8) v += dpp_f32<0x141>(v);      // row_half_mirror: the other quad of the 8
+  if (G == 16) v += dpp_f32<0x140>(v);     // row_mirror: the other 8 of the row
   return v;
 }
 
@@ -244,8 +243,8 @@ __device__ void build_schedule(uint32_t* sched, int n, int np, int ld) {
   }
 }
 
-// One-sided Jacobi sweeps on the columns of K (fp32, LDS; rows GW * RL and
-// beyond the matrix are zero), GW lanes per column pair: lane `sub` holds rows
+// One-sided Jacobi sweeps on the columns of K (fp32, LDS, column stride above
+// GW * RL; rows beyond the matrix are zero), GW lanes per column pair: lane `sub` holds rows
 // sub + GW i (i < RL) of both columns for the round.  With alpha, beta the
 // squared norms and gamma the dot product, the rotation by theta,
 // tan 2 theta = 2 gamma / (beta - alpha), |theta| <= pi / 4, is taken in the
@@ -256,13 +255,19 @@ __device__ void build_schedule(uint32_t* sched, int n, int np, int ld) {
 // quadratic once the couplings are below the relative gaps of the singular
 // values; with the nearly flat spectra of quantization residuals (neighbouring
 // values ~1% apart) a 1e-3 cut left couplings near 1e-5, visible in the
-// orthogonality of A, while 1e-4 leaves them at the fp32 rounding level.  All
-// threads call it; returns the sweeps.
+// orthogonality of A, while 1e-4 leaves them at the fp32 rounding level.
+// Row GW RL of each column (outside the matrix) carries the column's squared
+// norm: the first round of a sweep, which meets every column, forms all three
+// dot products; later rounds form gamma only and carry alpha and beta through
+// the rotation, alpha' = c^2 alpha - 2 c s gamma + s^2 beta and
+// beta' = s^2 alpha + 2 c s gamma + c^2 beta.  All threads call it; returns the
+// sweeps.
 template <int GW, int RL>
 __device__ int jacobi_columns(float* K, const uint32_t* sched, int n, int max_sweeps) {
   const int np = __builtin_amdgcn_readfirstlane(blockDim.x / GW);   // uniform: next row's offset is scalar
   const int pair = threadIdx.x / GW, sub = threadIdx.x - pair * GW;
   char* base = reinterpret_cast<char*>(K + sub);
+  char* nb = reinterpret_cast<char*>(K + GW * RL);   // row GW RL of a column: its squared norm
   const int rounds = n - 1;
   uint32_t pq = sched[pair];
   int sweeps = 0;
@@ -274,20 +279,31 @@ __device__ int jacobi_columns(float* K, const uint32_t* sched, int n, int max_sw
       float* kq = reinterpret_cast<float*>(base + (pq >> 16));
       float xp[RL], xq[RL];
       float al = 0.f, be = 0.f, ga = 0.f;
+      float* np_ = reinterpret_cast<float*>(nb + (pq & 0xFFFFu));
+      float* nq_ = reinterpret_cast<float*>(nb + (pq >> 16));
+      const float alc = *np_, bec = *nq_;   // carried norms, loaded with the columns
 #pragma unroll
       for (int i = 0; i < RL; ++i) {
         xp[i] = kp[GW * i];
         xq[i] = kq[GW * i];
       }
+      if (rnd == 0) {   // the sweep's first round meets every column: exact squared norms
 #pragma unroll
-      for (int i = 0; i < RL; ++i) {
-        al = fmaf(xp[i], xp[i], al);
-        be = fmaf(xq[i], xq[i], be);
-        ga = fmaf(xp[i], xq[i], ga);
+        for (int i = 0; i < RL; ++i) {
+          al = fmaf(xp[i], xp[i], al);
+          be = fmaf(xq[i], xq[i], be);
+          ga = fmaf(xp[i], xq[i], ga);
+        }
+        al = group_sumf<GW>(al);
+        be = group_sumf<GW>(be);
+        ga = group_sumf<GW>(ga);
+      } else {          // later rounds carry them along (updated below)
+#pragma unroll
+        for (int i = 0; i < RL; ++i) ga = fmaf(xp[i], xq[i], ga);
+        ga = group_sumf<GW>(ga);
+        al = alc;
+        be = bec;
       }
-      al = group_sumf<GW>(al);
-      be = group_sumf<GW>(be);
-      ga = group_sumf<GW>(ga);
       const float g2 = ga * ga, ab = al * be;
       // g2 > 0 here also keeps dd^2 + 4 g2 > 0 (alpha beta >= 0)
       const bool doit = g2 > 1e-14f * ab;
@@ -299,11 +315,139 @@ __device__ int jacobi_columns(float* K, const uint32_t* sched, int n, int max_sw
       const float sn = doit ? (dd >= 0.f ? ga : -ga) * ri * rh : 0.f;
 #pragma unroll
       for (int i = 0; i < RL; ++i) {
-        kp[GW * i] = c * xp[i] - sn * xq[i];
-        kq[GW * i] = sn * xp[i] + c * xq[i];
+        kp[GW * i] = fmaf(c, xp[i], -(sn * xq[i]));
+        kq[GW * i] = fmaf(sn, xp[i], c * xq[i]);
+      }
+      {   // squared norms after the rotation (every lane of the pair stores the same value)
+        const float cc = c * c, ss = sn * sn, cs2 = 2.f * c * sn * ga;
+        *np_ = fmaxf(fmaf(cc, al, fmaf(ss, be, -cs2)), 0.f);
+        *nq_ = fmaxf(fmaf(ss, al, fmaf(cc, be, cs2)), 0.f);
       }
       big |= __builtin_amdgcn_ballot_w64(g2 > 1e-8f * ab);   // wave-uniform, kept in scalar registers
       pq = pq_next;
+      __syncthreads();
+    }
+    sweeps = sweep + 1;
+    if (!__syncthreads_or(big != 0)) break;
+  }
+  return sweeps;
+}
+
+// The rotation of jacobi_columns for one pair held by a 16-lane group (rows
+// sub + 16 i of x_p and x_q in xp, xq; squared norms al, be; dot ga already
+// summed over the group): rotates xp, xq, updates al, be and returns whether
+// the pair was still coupled above the stopping threshold.
+template <int RL>
+__device__ __forceinline__ bool jacobi_rotate(float (&xp)[RL], float (&xq)[RL], float& al, float& be, float ga) {
+  const float g2 = ga * ga, ab = al * be;
+  const bool doit = g2 > 1e-14f * ab;
+  const float dd = be - al;
+  const float ri = __builtin_amdgcn_rsqf(fmaf(dd, dd, 4.f * g2));
+  const float hc = fmaf(0.5f * fabsf(dd), ri, 0.5f);
+  const float rh = __builtin_amdgcn_rsqf(hc);
+  const float c = doit ? hc * rh : 1.f;
+  const float sn = doit ? (dd >= 0.f ? ga : -ga) * ri * rh : 0.f;
+#pragma unroll
+  for (int i = 0; i < RL; ++i) {
+    const float u = xp[i], w = xq[i];
+    xp[i] = fmaf(c, u, -(sn * w));
+    xq[i] = fmaf(sn, u, c * w);
+  }
+  const float cc = c * c, ss = sn * sn, cs2 = 2.f * c * sn * ga;
+  const float a2 = fmaxf(fmaf(cc, al, fmaf(ss, be, -cs2)), 0.f);
+  be = fmaxf(fmaf(ss, al, fmaf(cc, be, cs2)), 0.f);
+  al = a2;
+  return g2 > 1e-8f * ab;
+}
+
+// The same sweeps as jacobi_columns for the wide core, in a block order that
+// needs a workgroup barrier only between block rounds.  The columns (n rounded
+// up to nbk blocks of 4, nbk even; columns beyond n are zero) form a round-robin
+// of blocks: in block round rho wave w holds blocks rr_player(w, rho, nbk) and
+// rr_player(nbk - 1 - w, rho, nbk); its 16-lane group g keeps column g of the
+// first block in registers and in sub-round j (j < 4) rotates it against
+// column (g + j) mod 4 of the second, which passes from group to group through
+// LDS within the wave.  Block round 0 first runs the pairs inside each of the
+// wave's two blocks (round-robin of 4, three sub-rounds; its first sub-round
+// meets every column and forms exact squared norms).  A sweep is 3 + 4 (nbk - 1)
+// sub-rounds and meets every pair once.  Squared norms ride in row 16 RL of
+// each column as in jacobi_columns.  All threads call it (10 waves, 16 lanes per
+// pair); returns the sweeps.
+template <int RL>
+__device__ int jacobi_blocks(float* K, int ld, int n, int max_sweeps) {
+  const int wave = threadIdx.x >> 6, g = (threadIdx.x >> 4) & 3, sub = threadIdx.x & 15;
+  const int nbk0 = (n + 3) / 4, nbk = nbk0 + (nbk0 & 1);
+  const bool active = wave < nbk / 2;
+  float* Ks = K + sub;
+  int sweeps = 0;
+  for (int sweep = 0; sweep < max_sweeps; ++sweep) {
+    uint64_t big = 0;
+    for (int rnd = 0; rnd < nbk - 1; ++rnd) {
+      if (active) {
+        const int ba = rr_player(wave, rnd, nbk), bb = rr_player(nbk - 1 - wave, rnd, nbk);
+        float xa[RL], xb[RL];
+        if (rnd == 0) {
+          const int blk = g < 2 ? ba : bb, slot = g & 1;
+#pragma unroll
+          for (int ir = 0; ir < 3; ++ir) {
+            const int x = rr_player(slot, ir, 4), y = rr_player(3 - slot, ir, 4);
+            float* cp = Ks + (blk * 4 + min(x, y)) * ld;
+            float* cq = Ks + (blk * 4 + max(x, y)) * ld;
+            float al = cp[16 * RL - sub], be = cq[16 * RL - sub], ga = 0.f;
+#pragma unroll
+            for (int i = 0; i < RL; ++i) {
+              xa[i] = cp[16 * i];
+              xb[i] = cq[16 * i];
+            }
+#pragma unroll
+            for (int i = 0; i < RL; ++i) ga = fmaf(xa[i], xb[i], ga);
+            ga = group_sumf<16>(ga);
+            if (ir == 0) {
+              float a2 = 0.f, b2 = 0.f;
+#pragma unroll
+              for (int i = 0; i < RL; ++i) {
+                a2 = fmaf(xa[i], xa[i], a2);
+                b2 = fmaf(xb[i], xb[i], b2);
+              }
+              al = group_sumf<16>(a2);
+              be = group_sumf<16>(b2);
+            }
+            big |= __builtin_amdgcn_ballot_w64(jacobi_rotate<RL>(xa, xb, al, be, ga));
+#pragma unroll
+            for (int i = 0; i < RL; ++i) {
+              cp[16 * i] = xa[i];
+              cq[16 * i] = xb[i];
+            }
+            cp[16 * RL - sub] = al;
+            cq[16 * RL - sub] = be;
+            __builtin_amdgcn_wave_barrier();
+          }
+        }
+        float* ca = Ks + (ba * 4 + g) * ld;
+        float al = ca[16 * RL - sub];
+#pragma unroll
+        for (int i = 0; i < RL; ++i) xa[i] = ca[16 * i];
+        const bool a_low = ba < bb;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          float* cb = Ks + (bb * 4 + ((g + j) & 3)) * ld;
+          float be = cb[16 * RL - sub], ga = 0.f;
+#pragma unroll
+          for (int i = 0; i < RL; ++i) xb[i] = cb[16 * i];
+#pragma unroll
+          for (int i = 0; i < RL; ++i) ga = fmaf(xa[i], xb[i], ga);
+          ga = group_sumf<16>(ga);
+          const bool coupled = a_low ? jacobi_rotate<RL>(xa, xb, al, be, ga) : jacobi_rotate<RL>(xb, xa, be, al, ga);
+          big |= __builtin_amdgcn_ballot_w64(coupled);
+#pragma unroll
+          for (int i = 0; i < RL; ++i) cb[16 * i] = xb[i];
+          cb[16 * RL - sub] = be;
+          __builtin_amdgcn_wave_barrier();
+        }
+#pragma unroll
+        for (int i = 0; i < RL; ++i) ca[16 * i] = xa[i];
+        ca[16 * RL - sub] = al;
+      }
       __syncthreads();
     }
     sweeps = sweep + 1;
@@ -422,41 +566,86 @@ __global__ __launch_bounds__(256) void core_small_kernel(const double* __restric
 }
 
 // ---------------------------------------------------------------------------
-// The two solves for 32 < l <= kMaxL, by one workgroup of 640
-// threads (pair i of a Jacobi round on lanes 16 i .. 16 i + 15).
+// The two solves for 32 < l <= kMaxL, by one workgroup of 640 threads.
 //
-// chol_wide: right-looking Cholesky of the fp64 Gram with the matrix in
-// registers: wave w owns rows w, w + 10, ..., lane c owns columns c and c + 64,
-// 16 entries per thread.  Step j: the owner of row j publishes it (and row j of
-// T) through a double-buffered LDS row, one barrier, then every thread takes the
-// pivot and updates its own entries with the outer product of row j.  Updates
-// are unconditional: entries of finished rows and columns pick up values that
-// are never read again.  R's rows go to Rm when given; with INV the same steps
-// build X = R^-1 the way chol_wave does (T = R^-T, lane c holding its columns
-// of T's rows), each finished row of T written straight into X's column.
+// chol_blocked: right-looking Cholesky H = R^T R of the fp64 Gram in 16 x 16
+// blocks, the matrix in LDS (A, stride kWideLd, zero beyond l).  Block step p:
+// wave 0 factors the diagonal block with the register recurrence of chol_wave
+// (lanes 0..15, lane b holding column b), giving R_pp and T_pp = R_pp^-T; the
+// waves then form the block row R[p, q] = T_pp A[p, q] (q > p) and subtract
+// R[p, q]^T R[p, s] from the trailing blocks (p < q <= s), one 16 x 16 block
+// per wave at a time, each lane four entries (rows ra + 4 i, column cb).  A
+// pivot at or below 1e-13 of the largest diagonal entry of H drops its
+// direction (zero row of R, zero row of T_pp).  Three barriers per block step
+// instead of one per row.
 constexpr int kWideLd = kMaxL + 1;
+constexpr int kCB = 16;                          // block of the blocked Cholesky
+constexpr int kCNB = (kMaxL + kCB - 1) / kCB;    // block rows at most
 // measured on MI355X at l = 80: more lanes per pair and more waves win (4-lane
-// pairs on 3 waves: 2.5x slower core; 4 Cholesky waves: 1.35x slower)
+// pairs on 3 waves: 2.5x slower core)
 constexpr int kWideCholWaves = 10;   // waves of the l > 32 Cholesky workgroup
 constexpr int kWideGroup = 16;       // lanes per Jacobi pair of the l > 32 core
 
-template <bool INV, int NW>
-__device__ void chol_wide(const double* __restrict__ gram, int l, double* Rm, float* __restrict__ X, double* rowbuf,
-                          double* scratch) {
-  constexpr int kWideWaves = NW, kWideRows = (kMaxL + NW - 1) / NW;
-  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
-  double g[kWideRows][2], t[kWideRows][2];
+// Diagonal block (LDS, stride ld) by one wave: lane (ra, cb) = (lane / 16,
+// lane % 16) keeps entries (ra + 4 i, cb), i < 4, of the block and of T (the
+// identity at first).  Step j: the lanes holding row j scale it by 1 / R[j][j]
+// (R's row j, T's row j) and publish both rows through LDS (rowbuf: 2 x 16
+// doubles); rows a > j then lose R[j][a] times them.  Writes R_pp over the
+// block's upper triangle and T_pp (row-major 16 x 16) to T.
+__device__ __forceinline__ void chol_diag16(double* D, int ld, double tol, double* T, double* rowbuf) {
+  const int lane = threadIdx.x & 63, ra = lane >> 4, cb = lane & 15;
+  double g[4], t[4];
 #pragma unroll
-  for (int i = 0; i < kWideRows; ++i)
+  for (int i = 0; i < 4; ++i) {
+    const int a = ra + 4 * i;
+    const double v = D[a * ld + cb];
+    g[i] = a <= cb ? v : 0.0;
+    t[i] = a == cb ? 1.0 : 0.0;
+  }
 #pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      const int a = w + kWideWaves * i, b = lane + 64 * c;
-      const bool in = a < l && b < l;
-      const int pi = !in ? 0 : (a <= b ? packed_index(a, b, l) : packed_index(b, a, l));
-      const double v = gram[pi];
-      g[i][c] = in ? v : 0.0;
-      if (INV) t[i][c] = (a == b) ? 1.0 : 0.0;
+  for (int j = 0; j < kCB; ++j) {
+    const int jr = j & 3, ji = j >> 2;
+    const double piv = bcast_lane(g[ji], jr * 16 + j);
+    const bool keep = piv > tol && piv > 0.0;
+    const double inv = keep ? rsq_f64(piv) : 0.0;   // 1 / R[j][j]
+    const double rjj = piv * inv;
+    if (ra == jr) {
+      const double v = g[ji];
+      g[ji] = cb > j ? v * inv : (cb == j ? rjj : v);
+      t[ji] *= inv;
+      rowbuf[cb] = g[ji];
+      rowbuf[kCB + cb] = t[ji];
     }
+    __builtin_amdgcn_wave_barrier();
+    const double rjb = rowbuf[cb], tjb = rowbuf[kCB + cb];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int a = ra + 4 * i;
+      const double rja = rowbuf[a];
+      const bool upd = a > j;
+      g[i] = upd ? fma(-rja, rjb, g[i]) : g[i];
+      t[i] = upd ? fma(-rja, tjb, t[i]) : t[i];
+    }
+    __builtin_amdgcn_wave_barrier();
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int a = ra + 4 * i;
+    if (a <= cb) D[a * ld + cb] = g[i];
+    T[a * kCB + cb] = t[i];
+  }
+}
+
+// All threads call it.  Td: kCNB blocks of 16 x 16 doubles (the T_pp).
+__device__ __forceinline__ void chol_blocked(const double* __restrict__ gram, int l, double* A, double* Td, double* rowbuf,
+                             double* scratch) {
+  const int tid = threadIdx.x, nt = blockDim.x, w = tid >> 6, lane = tid & 63, nw = nt >> 6;
+  const int nb = (l + kCB - 1) / kCB, lp = nb * kCB;
+  for (int e = tid; e < lp * lp; e += nt) {
+    const int a = e / lp, b = e - a * lp;
+    const bool in = a <= b && b < l;
+    A[a * kWideLd + b] = in ? gram[packed_index(a, b, l)] : 0.0;
+  }
   if (tid < 64) {
     double m = 0.0;
     for (int a = tid; a < l; a += 64) m = fmax(m, gram[packed_index(a, a, l)]);
@@ -466,65 +655,104 @@ __device__ void chol_wide(const double* __restrict__ gram, int l, double* Rm, fl
   }
   __syncthreads();
   const double tol = 1e-13 * scratch[0];
-  for (int j = 0; j < l; ++j) {
-    double* rb = rowbuf + (j & 1) * 2 * kWideLd;   // [G row j | T row j]
-    if (w == j % kWideWaves) {
-      const int ij = j / kWideWaves;
+  const int ra = lane >> 4, cb = lane & 15;
+  for (int p = 0; p < nb; ++p) {
+    const int p0 = p * kCB;
+    if (w == 0) chol_diag16(A + p0 * kWideLd + p0, kWideLd, tol, Td + p * kCB * kCB, rowbuf);
+    __syncthreads();
+    const double* T = Td + p * kCB * kCB;
+    for (int q = p + 1 + w; q < nb; q += nw) {   // R[p, q] = T_pp A[p, q]
+      double* Apq = A + p0 * kWideLd + q * kCB;
+      double acc[4] = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll 2
+      for (int c = 0; c < kCB; ++c) {
+        const double x = Apq[c * kWideLd + cb];
 #pragma unroll
-      for (int i = 0; i < kWideRows; ++i)
-        if (i == ij) {
+        for (int i = 0; i < 4; ++i) acc[i] = fma(T[(ra + 4 * i) * kCB + c], x, acc[i]);
+      }
+      __builtin_amdgcn_wave_barrier();   // the wave's reads of the block precede its writes
 #pragma unroll
-          for (int c = 0; c < 2; ++c) {
-            const int b = lane + 64 * c;
-            if (b < kWideLd) {
-              rb[b] = g[i][c];
-              if (INV) rb[kWideLd + b] = t[i][c];
-            }
-          }
-        }
+      for (int i = 0; i < 4; ++i) Apq[(ra + 4 * i) * kWideLd + cb] = acc[i];
     }
     __syncthreads();
-    const double piv = rb[j];
-    const bool keep = piv > tol && piv > 0.0;
-    const double inv = keep ? rsq_f64(piv) : 0.0;   // 1 / R[j][j]
-    double rjb[2], tjb[2];
-#pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      const int b = lane + 64 * c;
-      const int bb = b < kWideLd ? b : 0;
-      rjb[c] = rb[bb] * inv;                        // R[j][b] (b > j)
-      if (INV) tjb[c] = rb[kWideLd + bb] * inv;     // final T[j][b]
-    }
-    if (Rm != nullptr && w == 0) {
-#pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        const int b = lane + 64 * c;
-        if (b >= j && b < l) Rm[j * kWideLd + b] = (b == j) ? piv * inv : rjb[c];
+    const int m = nb - p - 1, nblk = m * (m + 1) / 2;
+    for (int bi = w; bi < nblk; bi += nw) {   // A[q, s] -= R[p, q]^T R[p, s]
+      int q = 0, rem = bi;
+      while (rem >= m - q) {
+        rem -= m - q;
+        ++q;
       }
-    }
-    if (INV && w == 0) {
+      const int Q = p + 1 + q, S = Q + rem;
+      const double* Rq = A + p0 * kWideLd + Q * kCB;
+      const double* Rs = A + p0 * kWideLd + S * kCB;
+      double* Aqs = A + Q * kCB * kWideLd + S * kCB;
+      double acc[4] = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll 2
+      for (int c = 0; c < kCB; ++c) {
+        const double y = Rs[c * kWideLd + cb];
 #pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        const int b = lane + 64 * c;
-        if (b <= j) X[b * l + j] = static_cast<float>(tjb[c]);   // X = T^T
+        for (int i = 0; i < 4; ++i) acc[i] = fma(Rq[c * kWideLd + ra + 4 * i], y, acc[i]);
       }
-    }
 #pragma unroll
-    for (int i = 0; i < kWideRows; ++i) {
-      const int a = w + kWideWaves * i;
-      const double rja = rb[a < kWideLd ? a : 0] * inv;   // R[j][a]
-#pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        g[i][c] = fma(-rja, rjb[c], g[i][c]);
-        if (INV) t[i][c] = fma(-rja, tjb[c], t[i][c]);
-      }
+      for (int i = 0; i < 4; ++i) Aqs[(ra + 4 * i) * kWideLd + cb] -= acc[i];
     }
+    __syncthreads();
+  }
+}
+
+// X = R^-1 = T^T from the factored A (upper blocks R) and Td: T = R^-T by block
+// forward substitution, T[p, p] = T_pp and, for block rows q in order,
+// T[q, p] = -T_qq sum_{s=p}^{q-1} R[s, q]^T T[s, p] (p < q; one block per wave,
+// the partial sum parked in the block's own place in Tm).  Writes X (l x l fp32,
+// row-major upper triangular, zero below).
+__device__ __forceinline__ void chol_inverse(const double* A, const double* Td, int l, double* Tm, float* __restrict__ X) {
+  const int tid = threadIdx.x, nt = blockDim.x, w = tid >> 6, lane = tid & 63, nw = nt >> 6;
+  const int nb = (l + kCB - 1) / kCB;
+  const int ra = lane >> 4, cb = lane & 15;
+  for (int e = tid; e < nb * kCB * kCB; e += nt) {
+    const int p = e / (kCB * kCB), a = (e / kCB) % kCB, b = e % kCB;
+    Tm[(p * kCB + a) * kWideLd + p * kCB + b] = Td[e];
   }
   __syncthreads();
+  for (int q = 1; q < nb; ++q) {
+    const double* Tq = Td + q * kCB * kCB;
+    for (int p = w; p < q; p += nw) {
+      double acc[4] = {0.0, 0.0, 0.0, 0.0};
+      for (int s = p; s < q; ++s) {
+        const double* Rsq = A + s * kCB * kWideLd + q * kCB;
+        const double* Tsp = Tm + s * kCB * kWideLd + p * kCB;
+#pragma unroll 2
+        for (int c = 0; c < kCB; ++c) {
+          const double y = Tsp[c * kWideLd + cb];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc[i] = fma(Rsq[c * kWideLd + ra + 4 * i], y, acc[i]);
+        }
+      }
+      double* Tqp = Tm + q * kCB * kWideLd + p * kCB;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) Tqp[(ra + 4 * i) * kWideLd + cb] = acc[i];
+      __builtin_amdgcn_wave_barrier();
+      double out[4] = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll 2
+      for (int c = 0; c < kCB; ++c) {
+        const double y = Tqp[c * kWideLd + cb];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) out[i] = fma(Tq[(ra + 4 * i) * kCB + c], y, out[i]);
+      }
+      __builtin_amdgcn_wave_barrier();
+#pragma unroll
+      for (int i = 0; i < 4; ++i) Tqp[(ra + 4 * i) * kWideLd + cb] = -out[i];
+    }
+    __syncthreads();
+  }
+  for (int e = tid; e < l * l; e += nt) {
+    const int a = e / l, b = e - a * l;
+    X[e] = a <= b ? static_cast<float>(Tm[b * kWideLd + a]) : 0.f;
+  }
 }
 
 // MODE 1: Cholesky and X = R^-1 on NW waves; MODE 2: the core, Jacobi pairs on
-// GW-lane groups (NW = 40 GW / 64 rounded up).
+// 16-lane groups of 10 waves (jacobi_blocks).
 template <int MODE, int NW, int GW>
 __global__ __launch_bounds__(64 * NW) void solve_wide_kernel(const double* __restrict__ gram, int l,
                                                                   float* __restrict__ Xinv, int r,
@@ -532,24 +760,22 @@ __global__ __launch_bounds__(64 * NW) void solve_wide_kernel(const double* __res
                                                                   float* __restrict__ sigma, double* __restrict__ stats,
                                                                   ObjectiveArgs obj) {
   constexpr int NB = kMaxL * kWideLd;
-  constexpr int NP = 64 * NW / GW;   // pair slots
-  static_assert(2 * NP <= kMaxL, "the padding slots' zero columns lie inside K");
-  __shared__ double Rm[MODE == 2 ? NB : 1];
+  static_assert(MODE == 1 || (GW == 16 && NW == 10), "the wide core's block Jacobi: 10 waves, 16-lane pairs");
+  __shared__ double Rm[NB];
+  __shared__ double Tm[MODE == 1 ? NB : 1];
+  __shared__ double Td[kCNB * kCB * kCB];
   __shared__ float Kf[MODE == 2 ? NB : 1];
-  __shared__ uint32_t sched[MODE == 2 ? (kMaxL - 1) * NP : 1];
-  __shared__ double rowbuf[4 * kWideLd];
+  __shared__ double rowbuf[2 * kCB];
   __shared__ double norm2[kMaxL];
   __shared__ int order[kMaxL];
   __shared__ double scratch[2];
   const int tid = threadIdx.x, nt = blockDim.x;
+  chol_blocked(gram, l, Rm, Td, rowbuf, scratch);
   if (MODE == 1) {
-    for (int e = tid; e < l * l; e += nt) Xinv[e] = 0.f;
-    chol_wide<true, NW>(gram, l, nullptr, Xinv, rowbuf, scratch);
+    chol_inverse(Rm, Td, l, Tm, Xinv);
     return;
   }
   const int n = l + (l & 1);
-  build_schedule(sched, n, NP, kWideLd);
-  chol_wide<false, NW>(gram, l, Rm, nullptr, rowbuf, scratch);
   // K = 2^-e R^T (column c of K = row c of R), fp32, with 2^e at the scale of R's largest entry
   if (tid < 64) {
     double m = 0.0;
@@ -566,7 +792,7 @@ __global__ __launch_bounds__(64 * NW) void solve_wide_kernel(const double* __res
   }
   __syncthreads();
   constexpr int RL = (kMaxL + GW - 1) / GW;
-  const int sweeps = jacobi_columns<GW, RL>(Kf, sched, n, 40);
+  const int sweeps = jacobi_blocks<RL>(Kf, kWideLd, n, 40);
   core_finish(Kf, kWideLd, l, n, ksc, Xinv, r, SB, SA, sigma, stats, obj, sweeps, norm2, order);
 }
 
@@ -1417,7 +1643,7 @@ hipError_t run_objective(const ObjectiveArgs& obj, hipStream_t s) {
 
 hipError_t run_lowrank(const float* E, const SvdPlan& pl, int q, const float* omega, const float* omega_frag,
                        uint64_t seed, int t, float* B, float* A, float* sigma, char* ws, const ObjectiveArgs& obj,
-                       hipStream_t s) {
+                       hipStream_t s, SideLane* side) {
   const int64_t d = pl.d, k = pl.k;
   const int r = pl.r, l = pl.l;
   if (pl.exact && pl.bj) {
@@ -1490,12 +1716,21 @@ hipError_t run_lowrank(const float* E, const SvdPlan& pl, int q, const float* om
   // For l <= 32 the Cholesky of Y's Gram (mode 1) needs no launch of its own:
   // it rides along with the E^T Y product that always follows, whose split-K
   // reduction is the first consumer of X.
+  // The fork and join between the streams cost tens of microseconds (measured
+  // on MI355X: a loss with the 45M-element E of an 11008 x 4096 layer, a gain
+  // with 235M elements), so the side lane is taken only for large E.
+  if (d * k < (int64_t(1) << 27)) side = nullptr;
   const bool ride = pl.ride;
-  bool pending = false;
+  bool pending = false, joining = false;
+  hipError_t serr = hipSuccess;
   auto product = [&](bool transposed, const uint16_t* panel_s, int mode) {
     const CholJob job{pending ? gparts : nullptr, pl.gram_parts_d, l, Xinv};
     launch_gemm(transposed, E, d, k, panel_s, pl, part, job, s);
     if (transposed) pending = false;
+    if (transposed && joining) {   // X = R^-1 from the side lane
+      if (serr == hipSuccess) serr = hipStreamWaitEvent(s, side->join, 0);
+      joining = false;
+    }
     if (transposed)
       launch_reduce(pl.nt, part, pl.tn_splits, k, pl.k_pad, l, Xinv, Z, mode == 2 ? nullptr : Z_s,
                     mode ? gparts : nullptr, s);
@@ -1511,15 +1746,26 @@ hipError_t run_lowrank(const float* E, const SvdPlan& pl, int q, const float* om
       launch_small_wave(2, nullptr, gparts, P, l, Xinv, r, SB, SA, sigma, stats, obj, s);
       return;
     }
-    LQ_LAUNCH("gram_sum", gram_sum_kernel, dim3((E_ + 63) / 64), dim3(1024), 0, s, gparts, P, E_, gtotal);
+    // mode 1 (always followed by an E^T Y product): on the side lane when there is one
+    hipStream_t ss = s;
+    if (mode == 1 && side != nullptr) {
+      if (serr == hipSuccess) serr = hipEventRecord(side->fork, s);
+      if (serr == hipSuccess) serr = hipStreamWaitEvent(side->stream, side->fork, 0);
+      ss = side->stream;
+    }
+    LQ_LAUNCH("gram_sum", gram_sum_kernel, dim3((E_ + 63) / 64), dim3(1024), 0, ss, gparts, P, E_, gtotal);
     if (l <= 32)
-      launch_small_wave(1, gtotal, nullptr, 0, l, Xinv, r, SB, SA, sigma, stats, none, s);
+      launch_small_wave(1, gtotal, nullptr, 0, l, Xinv, r, SB, SA, sigma, stats, none, ss);
     else if (mode == 1)
-      LQ_LAUNCH("chol_inv", (solve_wide_kernel<1, kWideCholWaves, 16>), dim3(1), dim3(64 * kWideCholWaves), 0, s, gtotal,
-                l, Xinv, r, SB, SA, sigma, stats, none);
+      LQ_LAUNCH("chol_inv", (solve_wide_kernel<1, kWideCholWaves, 16>), dim3(1), dim3(64 * kWideCholWaves), 0, ss,
+                gtotal, l, Xinv, r, SB, SA, sigma, stats, none);
     else
       LQ_LAUNCH("core_svd", (solve_wide_kernel<2, (40 * kWideGroup + 63) / 64, kWideGroup>), dim3(1),
                 dim3(64 * ((40 * kWideGroup + 63) / 64)), 0, s, gtotal, l, Xinv, r, SB, SA, sigma, stats, obj);
+    if (ss != s) {
+      if (serr == hipSuccess) serr = hipEventRecord(side->join, ss);
+      joining = true;
+    }
   };
   // Y = E Omega; X = R^-1 of its Gram.  Each power iteration multiplies by E^T
   // and E and re-orthonormalises Y only: span(E Z) does not depend on Z's basis,
@@ -1532,7 +1778,26 @@ hipError_t run_lowrank(const float* E, const SvdPlan& pl, int q, const float* om
   // C = E^T Q = (E^T Y) X, then the core solve on C^T C
   product(true, Y_s, 2);
   panels(PanelJob{Y, d, SB, B, 0}, PanelJob{Z, k, SA, A, 1}, l, pl.nt, r, s);
+  if (serr != hipSuccess) return serr;
   return hipGetLastError();
+}
+
+SideLane* side_lane_for(hipStream_t s) {
+  static std::mutex mu;
+  static std::map<std::pair<int, hipStream_t>, SideLane> lanes;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return nullptr;
+  std::lock_guard<std::mutex> lk(mu);
+  const auto key = std::make_pair(dev, s);
+  auto it = lanes.find(key);
+  if (it != lanes.end()) return &it->second;
+  SideLane lane{};
+  if (hipStreamCreateWithFlags(&lane.stream, hipStreamNonBlocking) != hipSuccess) return nullptr;
+  lane.mu = new std::mutex;
+  if (hipEventCreateWithFlags(&lane.fork, hipEventDisableTiming) != hipSuccess ||
+      hipEventCreateWithFlags(&lane.join, hipEventDisableTiming) != hipSuccess)
+    return nullptr;
+  return &lanes.emplace(key, lane).first->second;
 }
 
 }  // namespace loftq
