@@ -225,118 +225,21 @@ __global__ __launch_bounds__(64) void chol_inv_wave_kernel(const double* __restr
 // rotation needs accumulating.  B = Q V_R diag(sigma)^1/2 and
 // A = diag(sigma)^1/2 (C R^-1 U_R)^T = (C V_R diag(sigma)^-1/2)^T.
 
-// Round-robin (circle) pairing of the n columns: in round rnd, slot i < n / 2
-// pairs the players at positions i and n - 1 - i.  sched[rnd * np + i] holds the
-// byte offsets (column times ld floats) of the slot's lower and higher column in
-// its low and high 16 bits.  Slots n / 2 .. np - 1 (lanes that pad the last
-// wave) get columns 2 np - 2 and 2 np - 1, which the caller keeps zero.
-__device__ void build_schedule(uint32_t* sched, int n, int np, int ld) {
-  for (int e = threadIdx.x; e < (n - 1) * np; e += blockDim.x) {
-    const int rnd = e / np, i = e - rnd * np;
-    int p = 2 * np - 2, q = 2 * np - 1;
-    if (i < n / 2) {
-      const int x = rr_player(i, rnd, n), y = rr_player(n - 1 - i, rnd, n);
-      p = x < y ? x : y;
-      q = x < y ? y : x;
-    }
-    sched[e] = static_cast<uint32_t>(p * ld * 4) | (static_cast<uint32_t>(q * ld * 4) << 16);
-  }
-}
-
-// One-sided Jacobi sweeps on the columns of K (fp32, LDS, column stride above
-// GW * RL; rows beyond the matrix are zero), GW lanes per column pair: lane `sub` holds rows
-// sub + GW i (i < RL) of both columns for the round.  With alpha, beta the
-// squared norms and gamma the dot product, the rotation by theta,
+// One-sided Jacobi rotation of a pair held by a 16-lane group (rows sub + 16 i
+// of x_p and x_q in xp, xq).  With alpha, beta the squared norms and gamma the
+// dot product (already summed over the group), the rotation by theta,
 // tan 2 theta = 2 gamma / (beta - alpha), |theta| <= pi / 4, is taken in the
 // branch-free form cos 2 theta = |beta - alpha| / h, h = hypot(beta - alpha,
 // 2 gamma), c = sqrt((1 + cos 2 theta) / 2), s = sin 2 theta / (2 c).  A pair
-// is left alone while gamma^2 <= 1e-14 alpha beta.  The sweeps stop after one in
-// which every pair had gamma^2 <= 1e-8 alpha beta (|cos| <= 1e-4).  Convergence is
-// quadratic once the couplings are below the relative gaps of the singular
+// is left alone while gamma^2 <= 1e-14 alpha beta.  alpha and beta are carried
+// through the rotation, alpha' = c^2 alpha - 2 c s gamma + s^2 beta and
+// beta' = s^2 alpha + 2 c s gamma + c^2 beta.  Returns whether the pair was
+// still coupled above the stopping threshold, gamma^2 > 1e-8 alpha beta
+// (|cos| > 1e-4): the sweeps stop after one without such a pair.  Convergence
+// is quadratic once the couplings are below the relative gaps of the singular
 // values; with the nearly flat spectra of quantization residuals (neighbouring
 // values ~1% apart) a 1e-3 cut left couplings near 1e-5, visible in the
 // orthogonality of A, while 1e-4 leaves them at the fp32 rounding level.
-// Row GW RL of each column (outside the matrix) carries the column's squared
-// norm: the first round of a sweep, which meets every column, forms all three
-// dot products; later rounds form gamma only and carry alpha and beta through
-// the rotation, alpha' = c^2 alpha - 2 c s gamma + s^2 beta and
-// beta' = s^2 alpha + 2 c s gamma + c^2 beta.  All threads call it; returns the
-// sweeps.
-template <int GW, int RL>
-__device__ int jacobi_columns(float* K, const uint32_t* sched, int n, int max_sweeps) {
-  const int np = __builtin_amdgcn_readfirstlane(blockDim.x / GW);   // uniform: next row's offset is scalar
-  const int pair = threadIdx.x / GW, sub = threadIdx.x - pair * GW;
-  char* base = reinterpret_cast<char*>(K + sub);
-  char* nb = reinterpret_cast<char*>(K + GW * RL);   // row GW RL of a column: its squared norm
-  const int rounds = n - 1;
-  uint32_t pq = sched[pair];
-  int sweeps = 0;
-  for (int sweep = 0; sweep < max_sweeps; ++sweep) {
-    uint64_t big = 0;
-    for (int rnd = 0; rnd < rounds; ++rnd) {
-      const uint32_t pq_next = sched[(rnd + 1 < rounds ? rnd + 1 : 0) * np + pair];
-      float* kp = reinterpret_cast<float*>(base + (pq & 0xFFFFu));
-      float* kq = reinterpret_cast<float*>(base + (pq >> 16));
-      float xp[RL], xq[RL];
-      float al = 0.f, be = 0.f, ga = 0.f;
-      float* np_ = reinterpret_cast<float*>(nb + (pq & 0xFFFFu));
-      float* nq_ = reinterpret_cast<float*>(nb + (pq >> 16));
-      const float alc = *np_, bec = *nq_;   // carried norms, loaded with the columns
-#pragma unroll
-      for (int i = 0; i < RL; ++i) {
-        xp[i] = kp[GW * i];
-        xq[i] = kq[GW * i];
-      }
-      if (rnd == 0) {   // the sweep's first round meets every column: exact squared norms
-#pragma unroll
-        for (int i = 0; i < RL; ++i) {
-          al = fmaf(xp[i], xp[i], al);
-          be = fmaf(xq[i], xq[i], be);
-          ga = fmaf(xp[i], xq[i], ga);
-        }
-        al = group_sumf<GW>(al);
-        be = group_sumf<GW>(be);
-        ga = group_sumf<GW>(ga);
-      } else {          // later rounds carry them along (updated below)
-#pragma unroll
-        for (int i = 0; i < RL; ++i) ga = fmaf(xp[i], xq[i], ga);
-        ga = group_sumf<GW>(ga);
-        al = alc;
-        be = bec;
-      }
-      const float g2 = ga * ga, ab = al * be;
-      // g2 > 0 here also keeps dd^2 + 4 g2 > 0 (alpha beta >= 0)
-      const bool doit = g2 > 1e-14f * ab;
-      const float dd = be - al;
-      const float ri = __builtin_amdgcn_rsqf(fmaf(dd, dd, 4.f * g2));
-      const float hc = fmaf(0.5f * fabsf(dd), ri, 0.5f);
-      const float rh = __builtin_amdgcn_rsqf(hc);
-      const float c = doit ? hc * rh : 1.f;
-      const float sn = doit ? (dd >= 0.f ? ga : -ga) * ri * rh : 0.f;
-#pragma unroll
-      for (int i = 0; i < RL; ++i) {
-        kp[GW * i] = fmaf(c, xp[i], -(sn * xq[i]));
-        kq[GW * i] = fmaf(sn, xp[i], c * xq[i]);
-      }
-      {   // squared norms after the rotation (every lane of the pair stores the same value)
-        const float cc = c * c, ss = sn * sn, cs2 = 2.f * c * sn * ga;
-        *np_ = fmaxf(fmaf(cc, al, fmaf(ss, be, -cs2)), 0.f);
-        *nq_ = fmaxf(fmaf(ss, al, fmaf(cc, be, cs2)), 0.f);
-      }
-      big |= __builtin_amdgcn_ballot_w64(g2 > 1e-8f * ab);   // wave-uniform, kept in scalar registers
-      pq = pq_next;
-      __syncthreads();
-    }
-    sweeps = sweep + 1;
-    if (!__syncthreads_or(big != 0)) break;
-  }
-  return sweeps;
-}
-
-// The rotation of jacobi_columns for one pair held by a 16-lane group (rows
-// sub + 16 i of x_p and x_q in xp, xq; squared norms al, be; dot ga already
-// summed over the group): rotates xp, xq, updates al, be and returns whether
-// the pair was still coupled above the stopping threshold.
 template <int RL>
 __device__ __forceinline__ bool jacobi_rotate(float (&xp)[RL], float (&xq)[RL], float& al, float& be, float ga) {
   const float g2 = ga * ga, ab = al * be;
@@ -360,19 +263,21 @@ __device__ __forceinline__ bool jacobi_rotate(float (&xp)[RL], float (&xq)[RL], 
   return g2 > 1e-8f * ab;
 }
 
-// The same sweeps as jacobi_columns for the wide core, in a block order that
-// needs a workgroup barrier only between block rounds.  The columns (n rounded
-// up to nbk blocks of 4, nbk even; columns beyond n are zero) form a round-robin
-// of blocks: in block round rho wave w holds blocks rr_player(w, rho, nbk) and
+// One-sided Jacobi sweeps on the columns of K (fp32, LDS, column stride
+// ld > 16 RL; rows 16 RL and beyond the matrix are zero), 16 lanes per column
+// pair (lane sub holds rows sub + 16 i, i < RL), in a block order that needs a
+// workgroup barrier only between block rounds.  The columns (n rounded up to
+// nbk blocks of 4, nbk even; columns beyond n are zero) form a round-robin of
+// blocks: in block round rho wave w holds blocks rr_player(w, rho, nbk) and
 // rr_player(nbk - 1 - w, rho, nbk); its 16-lane group g keeps column g of the
 // first block in registers and in sub-round j (j < 4) rotates it against
 // column (g + j) mod 4 of the second, which passes from group to group through
 // LDS within the wave.  Block round 0 first runs the pairs inside each of the
 // wave's two blocks (round-robin of 4, three sub-rounds; its first sub-round
-// meets every column and forms exact squared norms).  A sweep is 3 + 4 (nbk - 1)
-// sub-rounds and meets every pair once.  Squared norms ride in row 16 RL of
-// each column as in jacobi_columns.  All threads call it (10 waves, 16 lanes per
-// pair); returns the sweeps.
+// meets every column and forms all three dot products, later sub-rounds form
+// gamma only).  A sweep is 3 + 4 (nbk - 1) sub-rounds and meets every pair
+// once.  Row 16 RL of each column carries its squared norm.  All threads call
+// it (at least nbk / 2 waves); returns the sweeps.
 template <int RL>
 __device__ int jacobi_blocks(float* K, int ld, int n, int max_sweeps) {
   const int wave = threadIdx.x >> 6, g = (threadIdx.x >> 4) & 3, sub = threadIdx.x & 15;
@@ -516,7 +421,6 @@ __global__ __launch_bounds__(256) void core_small_kernel(const double* __restric
   __shared__ double rowbuf[64];
   __shared__ float K[32 * LD];
   __shared__ float Xs[32 * 32];
-  __shared__ uint32_t sched[31 * 16];
   __shared__ double norm2[32];
   __shared__ int order[32];
   __shared__ double kscale;
@@ -524,7 +428,6 @@ __global__ __launch_bounds__(256) void core_small_kernel(const double* __restric
   const int tid = threadIdx.x;
   const int n = l + (l & 1);
   for (int e = tid; e < l * l; e += blockDim.x) Xs[e] = Xinv[e];
-  build_schedule(sched, n, blockDim.x / 16, LD);
   const double* gram = gram_sum_block<LM>(gparts, P, l, gsum);
   const int sum_wave = blockDim.x > 64 ? 1 : 0;
   if (obj.out != nullptr && sum_wave == 1 && (tid >> 6) == 1) {
@@ -561,7 +464,7 @@ __global__ __launch_bounds__(256) void core_small_kernel(const double* __restric
     }
   }
   __syncthreads();
-  const int sweeps = jacobi_columns<16, 2>(K, sched, n, 30);
+  const int sweeps = jacobi_blocks<2>(K, LD, n, 30);
   core_finish(K, LD, l, n, kscale, Xs, r, SB, SA, sigma, stats, obj, sweeps, norm2, order, objsums);
 }
 
