@@ -77,6 +77,11 @@ typedef struct {
                                k+1 .. k+T with the sketch counter continuing at k+1, so k
                                alternations followed by a resumed call of T give the same results
                                as one call of k+T.  Requires T >= 1. */
+  int32_t materialize_residual; /* 0 (default): the randomized SVD's products form E = W - deq(Q)
+                               element by element from W and the codes as they stream them (cols
+                               % 8 == 0; E is never stored, the workspace holds no copy of it);
+                               1: the dequant stores E and the products read it.  Both give the
+                               same results bit for bit; the exact SVD always stores E. */
 } loftq_config_t;
 
 /* Quantization step ("LoftQ...", §2.3: quantize the residual W - Delta; the

@@ -35,8 +35,13 @@ struct InitPlan {
   SvdPlan svd;
   int nparts;
   int64_t sketch_floats;   // one alternation's sketch in fragment order (0 for the exact SVD)
-  int64_t off_e, off_parts, off_wparts, off_sketch, off_svd, bytes;
+  int64_t off_e, off_parts, off_wparts, off_sketch, off_svd, off_ascale, bytes;
 };
+
+// Whether the products form E from W and the codes (E is then never stored).
+bool formed_residual(int64_t cols, const loftq_config_t& c) {
+  return c.materialize_residual == 0 && c.exact_svd == 0 && c.iterative_steps > 0 && (cols & 7) == 0;
+}
 
 InitPlan make_init_plan(int64_t rows, int64_t cols, const loftq_config_t& c) {
   InitPlan p{};
@@ -46,11 +51,13 @@ InitPlan make_init_plan(int64_t rows, int64_t cols, const loftq_config_t& c) {
   p.sketch_floats = p.svd.exact ? 0 : p.svd.k_pad * 16 * p.svd.nt;
   const int batch = c.iterative_steps < kSketchBatch ? c.iterative_steps : kSketchBatch;
   int64_t off = 0;
-  p.off_e = off;      off += align256(n * 4);
+  p.off_e = off;      off += formed_residual(cols, c) ? 0 : align256(n * 4);
   p.off_parts = off;  off += align256(static_cast<int64_t>(p.nparts) * 8);
   p.off_wparts = off; off += align256(static_cast<int64_t>(p.nparts) * 8);
   p.off_sketch = off; off += align256(p.sketch_floats * 4 * (batch > 0 ? batch : 0));
   p.off_svd = off;    off += align256(p.svd.bytes);
+  // formed residual with double quant: a' = fl32(qabsmax dq_scale) per block, written by the dequant
+  p.off_ascale = off; off += (formed_residual(cols, c) && c.double_quant) ? align256(((n + 63) / 64) * 4) : 0;
   p.bytes = off;
   return p;
 }
@@ -65,6 +72,7 @@ loftq_status_t check_config(int64_t rows, int64_t cols, const loftq_config_t* c)
   // resume: k completed alternations (k + T stays within the sketch counter's range)
   if (c->init_from_BA < 0 || c->init_from_BA > 1000000 || (c->init_from_BA > 0 && c->iterative_steps == 0))
     return LOFTQ_ERR_INVALID_ARG;
+  if (c->materialize_residual != 0 && c->materialize_residual != 1) return LOFTQ_ERR_INVALID_ARG;
   return check_svd_shape(rows, cols, c->rank, c->oversample, c->exact_svd);
 }
 
@@ -115,7 +123,11 @@ hipError_t run_init(const InitArgs& a, loftq_dtype_t wdt, const loftq_config_t& 
   float* sigma = a.sigma;
   const bool dq = cfg->double_quant != 0;
   const InitPlan pl = make_init_plan(rows, cols, *cfg);
-  float* E = reinterpret_cast<float*>(w + pl.off_e);
+  const bool formed = formed_residual(cols, *cfg);
+  float* E = formed ? nullptr : reinterpret_cast<float*>(w + pl.off_e);
+  float* ascale = formed && dq ? reinterpret_cast<float*>(w + pl.off_ascale) : nullptr;
+  VirtualE ve{W, wdt == LOFTQ_BF16 ? 1 : 0, packed, dq ? ascale : absmax, {}};
+  for (int i = 0; i < 16; ++i) ve.level[i] = nf_tables(cfg->bits).level[i];
   double* eparts = reinterpret_cast<double*>(w + pl.off_parts);
   double* wparts = reinterpret_cast<double*>(w + pl.off_wparts);
   char* svd_ws = w + pl.off_svd;
@@ -130,7 +142,7 @@ hipError_t run_init(const InitArgs& a, loftq_dtype_t wdt, const loftq_config_t& 
     if (x == hipSuccess)
       x = launch_nf4_dequantize(packed, absmax, nullptr, nullptr, n, cfg->dq_blocksize, W, wdt, E, eparts,
                                 first ? wparts : nullptr, nullptr, s, dq ? qabsmax : nullptr, dq ? dq_scale : nullptr,
-                                cfg->bits);
+                                cfg->bits, ascale);
     return x;
   };
   hipError_t e = hipSuccess;
@@ -165,7 +177,8 @@ hipError_t run_init(const InitArgs& a, loftq_dtype_t wdt, const loftq_config_t& 
         e = run_warm_columns(A, sigma, cols, r, pl.svd.nt, sketches + slot * pl.sketch_floats, s);
     }
     if (e == hipSuccess)
-      e = run_lowrank(E, pl.svd, cfg->power_iters, nullptr, om, cfg->seed, t, B, A, sigma, svd_ws, objt, s, side);
+      e = run_lowrank(E, pl.svd, cfg->power_iters, nullptr, om, cfg->seed, t, B, A, sigma, svd_ws, objt, s, side,
+                      formed ? &ve : nullptr);
   }
   return e;
 }

@@ -11,10 +11,10 @@
 // term).  Against fp32 matrix cores (v_mfma_f32_16x16x4_f32), whose work bounds
 // the wide panels (l = 80: 160 flop per 4 bytes of E), the three bf16 products
 // take about a fifth of the matrix-core time.  v_mfma_f32_16x16x32_bf16 takes
-// K = 32 per instruction, so one K step covers two 16-row blocks of the
-// fragment-order panel; lane (li, g) supplies K index 4 h + s (h = 0, 1;
-// s = 0..3) <-> row 16 h + 4 g + s of the step (its float4 of fragment block h),
-// and E is loaded to match.  E is split in registers as it arrives; the panel
+// K = 32 per instruction; lane (li, g) supplies K index 8 g + e (e = 0..7) <->
+// row 8 g + e of the step (the panel's split layout, split_index), and E is
+// loaded to match: gemm_nn reads 8 consecutive columns of a row per lane,
+// gemm_tn 4 columns of 8 consecutive rows.  E is split in registers as it arrives; the panel
 // comes already split (split_index), written so by the split-K reduction that
 // produces it.
 //
@@ -53,6 +53,111 @@ __device__ __forceinline__ float4 load_run4(const float* __restrict__ p, int64_t
   return make_float4(o[0], o[1], o[2], o[3]);
 }
 
+typedef float lvpair2 __attribute__((ext_vector_type(2)));
+
+// Where the products take E from: a stored E, or the weight and the codes
+// (VirtualE).  fetch4 / fetch8 issue the loads of E[row][c ..] (4 or 8
+// consecutive columns; past the last column the addresses are clamped as in
+// load_run4, and the skinny operand's matching rows are zero) into a Raw held in
+// the register ring; decode, at the step that consumes it, turns the Raw into
+// values (a formed E through the level-pair table in LDS), so the loads stay in
+// flight as long as a stored E's do.
+template <bool VEC>
+struct StoredE {
+  static constexpr bool kVirtual = false;
+  typedef float4 Raw4;
+  struct Raw8 { float4 a, b; };
+  const float* E;
+  __device__ __forceinline__ Raw4 fetch4(int64_t row, int64_t c, int64_t k) const {
+    return load_run4<VEC>(E + row * k, c, k);
+  }
+  __device__ __forceinline__ Raw8 fetch8(int64_t row, int64_t c, int64_t k) const {
+    return Raw8{load_run4<VEC>(E + row * k, c, k), load_run4<VEC>(E + row * k, c + 4, k)};
+  }
+  __device__ __forceinline__ float4 decode4(const Raw4& r, const lvpair2*) const { return r; }
+  __device__ __forceinline__ void decode8(const Raw8& r, float (&x)[8], const lvpair2*) const {
+    x[0] = r.a.x; x[1] = r.a.y; x[2] = r.a.z; x[3] = r.a.w;
+    x[4] = r.b.x; x[5] = r.b.y; x[6] = r.b.z; x[7] = r.b.w;
+  }
+};
+// cols % 8 == 0: an 8-column fetch never straddles the last column.  The block
+// scale a' comes from one array (absmax, or the double-quantized scales the
+// dequant writes out).
+template <bool BF16>
+struct FormedE {
+  static constexpr bool kVirtual = true;
+  struct Raw4 {
+    uint32_t w[BF16 ? 2 : 4];   // four weights (bf16 pairs or fp32)
+    uint32_t cw;                // their two code bytes
+    float a;
+  };
+  struct Raw8 {
+    uint32_t w[BF16 ? 4 : 8];
+    uint32_t cw;                // four code bytes
+    float a;
+  };
+  VirtualE v;
+  __device__ __forceinline__ Raw4 fetch4(int64_t row, int64_t c, int64_t k) const {
+    c = c < k - 4 ? c : k - 4;
+    const int64_t e = row * k + c;   // e % 4 == 0: one 64-block, two code bytes
+    Raw4 r;
+    if constexpr (BF16) {
+      const uint2 u = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(v.W) + e);
+      r.w[0] = u.x; r.w[1] = u.y;
+    } else {
+      const uint4 u = *reinterpret_cast<const uint4*>(static_cast<const float*>(v.W) + e);
+      r.w[0] = u.x; r.w[1] = u.y; r.w[2] = u.z; r.w[3] = u.w;
+    }
+    r.cw = reinterpret_cast<const uint16_t*>(v.packed)[e >> 2];
+    r.a = v.scale[e >> 6];
+    return r;
+  }
+  __device__ __forceinline__ Raw8 fetch8(int64_t row, int64_t c, int64_t k) const {
+    c = c < k - 8 ? c : k - 8;
+    const int64_t e = row * k + c;   // e % 8 == 0: one 64-block, four code bytes
+    Raw8 r;
+    if constexpr (BF16) {
+      const uint4 u = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(v.W) + e);
+      r.w[0] = u.x; r.w[1] = u.y; r.w[2] = u.z; r.w[3] = u.w;
+    } else {
+      const uint4 u0 = *reinterpret_cast<const uint4*>(static_cast<const float*>(v.W) + e);
+      const uint4 u1 = *reinterpret_cast<const uint4*>(static_cast<const float*>(v.W) + e + 4);
+      r.w[0] = u0.x; r.w[1] = u0.y; r.w[2] = u0.z; r.w[3] = u0.w;
+      r.w[4] = u1.x; r.w[5] = u1.y; r.w[6] = u1.z; r.w[7] = u1.w;
+    }
+    r.cw = reinterpret_cast<const uint32_t*>(v.packed)[e >> 3];
+    r.a = v.scale[e >> 6];
+    return r;
+  }
+  // e = fl32(w - fl32(level[code] a')), element by element as the dequant forms it
+  __device__ __forceinline__ static float wval(const uint32_t* w, int j) {
+    if constexpr (BF16) return __uint_as_float((j & 1) ? (w[j >> 1] & 0xFFFF0000u) : (w[j >> 1] << 16));
+    else return __uint_as_float(w[j]);
+  }
+  __device__ __forceinline__ float4 decode4(const Raw4& r, const lvpair2* lvl2) const {
+    const lvpair2 c01 = lvl2[r.cw & 0xFFu], c23 = lvl2[(r.cw >> 8) & 0xFFu];
+    const float d0 = c01.x * r.a, d1 = c01.y * r.a, d2 = c23.x * r.a, d3 = c23.y * r.a;
+    return make_float4(wval(r.w, 0) - d0, wval(r.w, 1) - d1, wval(r.w, 2) - d2, wval(r.w, 3) - d3);
+  }
+  __device__ __forceinline__ void decode8(const Raw8& r, float (&x)[8], const lvpair2* lvl2) const {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const lvpair2 c = lvl2[(r.cw >> (8 * q)) & 0xFFu];
+      const float d0 = c.x * r.a, d1 = c.y * r.a;
+      x[2 * q] = wval(r.w, 2 * q) - d0;
+      x[2 * q + 1] = wval(r.w, 2 * q + 1) - d1;
+    }
+  }
+};
+// Level pairs (level[b >> 4], level[b & 15]) of a code byte b (element 2i in the
+// high nibble); all threads of the workgroup call it, a barrier follows.
+template <typename Src>
+__device__ __forceinline__ void fill_level_pairs(const Src& src, lvpair2* lvl2) {
+  if constexpr (Src::kVirtual) {
+    for (int i = threadIdx.x; i < 256; i += blockDim.x) lvl2[i] = lvpair2{src.v.level[i >> 4], src.v.level[i & 15]};
+  }
+}
+
 // ---------------------------------------------------------------------------
 // v_mfma_f32_16x16x32_bf16: lane L supplies A[L%16][8(L/16) + e] and
 // B[8(L/16) + e][L%16] (e = 0..7) and receives D[4(L/16) + v][L%16] in element v.
@@ -81,25 +186,26 @@ struct Tn3Cfg {
 // buffered, one barrier per step) and the waves read their B operands from there:
 // the panel then costs one L2 read per workgroup instead of one per wave.  E runs
 // through a D-deep register ring of its own.
-template <int NT, bool VEC>
+template <int NT, typename Src>
 __global__ __launch_bounds__(64 * Nn3Cfg<NT>::WR) void gemm_nn3_kernel(
-    const float* __restrict__ E, int64_t d, int64_t k, const uint16_t* __restrict__ Xs, int64_t kper,
+    Src src, int64_t d, int64_t k, const uint16_t* __restrict__ Xs, int64_t kper,
     float* __restrict__ part) {
   using C = Nn3Cfg<NT>;
   constexpr int LP = 16 * NT, RT = C::RT, D = C::D, WR = C::WR, PU = C::PU, PPT = C::PPT;
   static_assert(D % 2 == 0 && WR * 64 == 256, "ring parity and the 256-thread panel staging");
   __shared__ uint4 pan[2][256 * PPT];   // rounded up to whole rounds of 256 pieces (the excess never read)
+  __shared__ lvpair2 lvl2[Src::kVirtual ? 256 : 1];
+  fill_level_pairs(src, lvl2);            // the barrier before the first step covers it
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int g = lane >> 4, li = lane & 15;
   const int64_t row0 = (static_cast<int64_t>(blockIdx.x) * WR + w) * 16 * RT;
   const int64_t kb = static_cast<int64_t>(blockIdx.y) * kper;
   const int nsteps = static_cast<int>(kper / 32);   // a multiple of D
-  const float* erow[RT];
+  int64_t erow[RT];
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
-    int64_t r = row0 + rt * 16 + li;
-    r = r < d ? r : d - 1;
-    erow[rt] = E + r * k;
+    const int64_t r = row0 + rt * 16 + li;
+    erow[rt] = r < d ? r : d - 1;
   }
   const uint4* xg = reinterpret_cast<const uint4*>(Xs) + (kb / 32) * PU;
   floatx4 acc[RT][NT];
@@ -107,7 +213,7 @@ __global__ __launch_bounds__(64 * Nn3Cfg<NT>::WR) void gemm_nn3_kernel(
   for (int a = 0; a < RT; ++a)
 #pragma unroll
     for (int b = 0; b < NT; ++b) acc[a][b] = floatx4{0.f, 0.f, 0.f, 0.f};
-  float4 eb[D][RT][2];
+  typename Src::Raw8 eb[D][RT];
   static_assert(PPT <= 3, "at most three panel pieces per thread");
   // Two register sets (a, b, c pieces each) of staged panel steps, as plain
   // variables: the pieces past PU (PU not a multiple of 256) load a duplicate of
@@ -132,12 +238,9 @@ __global__ __launch_bounds__(64 * Nn3Cfg<NT>::WR) void gemm_nn3_kernel(
   } while (0)
   auto load_e = [&](int u, int j) {
     j = j < nsteps ? j : nsteps - 1;   // past the end: a harmless repeat of the last step
-    const int64_t c = kb + 32 * j + 4 * g;
+    const int64_t c = kb + 32 * j + 8 * g;
 #pragma unroll
-    for (int rt = 0; rt < RT; ++rt) {
-      eb[u][rt][0] = load_run4<VEC>(erow[rt], c, k);
-      eb[u][rt][1] = load_run4<VEC>(erow[rt], c + 16, k);
-    }
+    for (int rt = 0; rt < RT; ++rt) eb[u][rt] = src.fetch8(erow[rt], c, k);
   };
   auto compute = [&](int u, int buf) {
     bf16x8 ah[RT], al[RT], bh[NT], bl[NT];
@@ -147,7 +250,11 @@ __global__ __launch_bounds__(64 * Nn3Cfg<NT>::WR) void gemm_nn3_kernel(
       bl[nt] = __builtin_bit_cast(bf16x8, pan[buf][(2 * nt + 1) * 64 + lane]);
     }
 #pragma unroll
-    for (int rt = 0; rt < RT; ++rt) split8(eb[u][rt][0], eb[u][rt][1], ah[rt], al[rt]);
+    for (int rt = 0; rt < RT; ++rt) {
+      float x[8];
+      src.decode8(eb[u][rt], x, lvl2);
+      split8(x, ah[rt], al[rt]);
+    }
     // the three products interleaved over the RT x NT accumulators
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt)
@@ -219,11 +326,11 @@ __global__ __launch_bounds__(64 * Nn3Cfg<NT>::WR) void gemm_nn3_kernel(
 // gemm_tn.  Wave (wc, wr) owns one 64-column group (its four interleaved 16-column
 // MFMA tiles jm hold columns c0 + 4 m + jm) and its share of the workgroup's rows;
 // waves sharing columns are summed through LDS at the end.  Row steps of 32: lane (li, g) loads rows
-// 16 h + 4 g + s of the step (eight float4 of its four columns), and tile jm's A
+// 8 g + e of the step (eight float4 of its four columns), and tile jm's A
 // operand is component jm of those eight.
-template <int NT, bool VEC, int LMJ>
+template <int NT, typename Src, int LMJ>
 __global__ __launch_bounds__(64 * Tn3Cfg<NT>::WC * Tn3Cfg<NT>::WR) void gemm_tn3_kernel(
-    const float* __restrict__ E, int64_t d, int64_t k, const uint16_t* __restrict__ Ys, int64_t rper,
+    Src src, int64_t d, int64_t k, const uint16_t* __restrict__ Ys, int64_t rper,
     float* __restrict__ part, CholJob job) {
   using C = Tn3Cfg<NT>;
   constexpr int LP = 16 * NT, D = C::D, WC = C::WC, WR = C::WR;
@@ -246,6 +353,11 @@ __global__ __launch_bounds__(64 * Tn3Cfg<NT>::WC * Tn3Cfg<NT>::WR) void gemm_tn3
       return;
     }
   }
+  __shared__ lvpair2 lvl2[Src::kVirtual ? 256 : 1];
+  if constexpr (Src::kVirtual) {
+    fill_level_pairs(src, lvl2);
+    __syncthreads();
+  }
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, wc = w % WC, wr = w / WC;
   const int g = lane >> 4, li = lane & 15;
   const int64_t bx = blockIdx.x, by = blockIdx.y;   // column block, row split
@@ -260,23 +372,24 @@ __global__ __launch_bounds__(64 * Tn3Cfg<NT>::WC * Tn3Cfg<NT>::WR) void gemm_tn3
   for (int a = 0; a < 4; ++a)
 #pragma unroll
     for (int b = 0; b < NT; ++b) acc[a][b] = floatx4{0.f, 0.f, 0.f, 0.f};
-  float4 eb[D][2][4];
+  typename Src::Raw4 eb[D][8];
   uint4 yb[D][NT][2];
   auto load = [&](int u, int j) {
 #pragma unroll
-    for (int h = 0; h < 2; ++h)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        int64_t r = rb + 32 * j + 16 * h + 4 * g + i;
-        r = r < d ? r : d - 1;
-        eb[u][h][i] = load_run4<VEC>(E + r * k, cl, k);
-      }
+    for (int e = 0; e < 8; ++e) {
+      int64_t r = rb + 32 * j + 8 * g + e;
+      r = r < d ? r : d - 1;
+      eb[u][e] = src.fetch4(r, cl, k);
+    }
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
       for (int h = 0; h < 2; ++h) yb[u][nt][h] = yp[((static_cast<int64_t>(j) * NT + nt) * 2 + h) * 64];
   };
   auto compute = [&](int u) {
+    float4 ev[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) ev[e] = src.decode4(eb[u][e], lvl2);
     bf16x8 bh[NT], bl[NT];
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
@@ -285,8 +398,8 @@ __global__ __launch_bounds__(64 * Tn3Cfg<NT>::WC * Tn3Cfg<NT>::WR) void gemm_tn3
     }
 #pragma unroll
     for (int jm = 0; jm < 4; ++jm) {
-      const float x[8] = {comp(eb[u][0][0], jm), comp(eb[u][0][1], jm), comp(eb[u][0][2], jm), comp(eb[u][0][3], jm),
-                          comp(eb[u][1][0], jm), comp(eb[u][1][1], jm), comp(eb[u][1][2], jm), comp(eb[u][1][3], jm)};
+      const float x[8] = {comp(ev[0], jm), comp(ev[1], jm), comp(ev[2], jm), comp(ev[3], jm),
+                          comp(ev[4], jm), comp(ev[5], jm), comp(ev[6], jm), comp(ev[7], jm)};
       bf16x8 ah, al;
       split8(x, ah, al);
 #pragma unroll
@@ -354,30 +467,39 @@ GemmShape shape_typed(bool transposed) {
   return GemmShape{16 * C::RT * C::WR, 32 * C::D};
 }
 
-template <int NT>
-void gemm_typed(bool transposed, const float* E, int64_t d, int64_t k, const uint16_t* panel, const SvdPlan& pl,
-                float* part, const CholJob& job, hipStream_t s) {
-  const bool vec = (k & 3) == 0 && k >= 4;
+template <int NT, typename Src>
+void gemm_launch(bool transposed, const Src& src, int64_t d, int64_t k, const uint16_t* panel, const SvdPlan& pl,
+                 float* part, const CholJob& job, hipStream_t s) {
   if (transposed) {
     constexpr int threads = 64 * Tn3Cfg<NT>::WC * Tn3Cfg<NT>::WR;
     const dim3 grid(pl.tn_col_blocks + (job.parts != nullptr ? 1 : 0), pl.tn_splits);
-#define LQ_TN3(V, LMJ)                                                                                                \
-  LQ_LAUNCH("gemm_tn", (gemm_tn3_kernel<NT, V, LMJ>), grid, dim3(threads), 0, s, E, d, k, panel, pl.tn_rper, part, job)
+#define LQ_TN3(LMJ)                                                                                                   \
+  LQ_LAUNCH("gemm_tn", (gemm_tn3_kernel<NT, Src, LMJ>), grid, dim3(threads), 0, s, src, d, k, panel, pl.tn_rper, part, \
+            job)
     // register tile of the ride-along Cholesky (l <= 32 only): the smallest of 16 / 24 / 32 rows that holds l
     const int lmj = job.parts == nullptr ? 0 : (job.l <= 16 ? 16 : (job.l <= 24 ? 24 : 32));
     if constexpr (NT <= 2) {
-      if (vec) { if (lmj == 16) LQ_TN3(true, 16); else if (lmj == 24) LQ_TN3(true, 24); else if (lmj) LQ_TN3(true, 32); else LQ_TN3(true, 0); }
-      else { if (lmj == 16) LQ_TN3(false, 16); else if (lmj == 24) LQ_TN3(false, 24); else if (lmj) LQ_TN3(false, 32); else LQ_TN3(false, 0); }
+      if (lmj == 16) LQ_TN3(16); else if (lmj == 24) LQ_TN3(24); else if (lmj) LQ_TN3(32); else LQ_TN3(0);
     } else {
-      if (vec) LQ_TN3(true, 0); else LQ_TN3(false, 0);
+      LQ_TN3(0);
     }
 #undef LQ_TN3
     return;
   }
   constexpr int threads = 64 * Nn3Cfg<NT>::WR;
   const dim3 grid(pl.nn_row_blocks, pl.nn_splits);
-  if (vec) LQ_LAUNCH("gemm_nn", (gemm_nn3_kernel<NT, true>), grid, dim3(threads), 0, s, E, d, k, panel, pl.nn_kper, part);
-  else LQ_LAUNCH("gemm_nn", (gemm_nn3_kernel<NT, false>), grid, dim3(threads), 0, s, E, d, k, panel, pl.nn_kper, part);
+  LQ_LAUNCH("gemm_nn", (gemm_nn3_kernel<NT, Src>), grid, dim3(threads), 0, s, src, d, k, panel, pl.nn_kper, part);
+}
+
+template <int NT>
+void gemm_typed(bool transposed, const float* E, int64_t d, int64_t k, const uint16_t* panel, const SvdPlan& pl,
+                float* part, const CholJob& job, hipStream_t s, const VirtualE* ve) {
+  const bool vec = (k & 3) == 0 && k >= 4;
+  const bool vec8 = vec && k >= 8;
+  if (ve != nullptr && ve->w_bf16) gemm_launch<NT>(transposed, FormedE<true>{*ve}, d, k, panel, pl, part, job, s);
+  else if (ve != nullptr) gemm_launch<NT>(transposed, FormedE<false>{*ve}, d, k, panel, pl, part, job, s);
+  else if (vec8) gemm_launch<NT>(transposed, StoredE<true>{E}, d, k, panel, pl, part, job, s);
+  else gemm_launch<NT>(transposed, StoredE<false>{E}, d, k, panel, pl, part, job, s);
 }
 
 }  // namespace
@@ -393,15 +515,15 @@ GemmShape gemm_shape(bool transposed, int nt) {
 }
 
 void launch_gemm(bool transposed, const float* E, int64_t d, int64_t k, const uint16_t* panel, const SvdPlan& pl,
-                 float* part, const CholJob& job, hipStream_t s) {
+                 float* part, const CholJob& job, hipStream_t s, const VirtualE* ve) {
   const CholJob none{nullptr, 0, 0, nullptr};
   const CholJob& j = (transposed && pl.nt <= 2) ? job : none;
   switch (pl.nt) {
-    case 1: gemm_typed<1>(transposed, E, d, k, panel, pl, part, j, s); break;
-    case 2: gemm_typed<2>(transposed, E, d, k, panel, pl, part, j, s); break;
-    case 3: gemm_typed<3>(transposed, E, d, k, panel, pl, part, j, s); break;
-    case 4: gemm_typed<4>(transposed, E, d, k, panel, pl, part, j, s); break;
-    default: gemm_typed<5>(transposed, E, d, k, panel, pl, part, j, s); break;
+    case 1: gemm_typed<1>(transposed, E, d, k, panel, pl, part, j, s, ve); break;
+    case 2: gemm_typed<2>(transposed, E, d, k, panel, pl, part, j, s, ve); break;
+    case 3: gemm_typed<3>(transposed, E, d, k, panel, pl, part, j, s, ve); break;
+    case 4: gemm_typed<4>(transposed, E, d, k, panel, pl, part, j, s, ve); break;
+    default: gemm_typed<5>(transposed, E, d, k, panel, pl, part, j, s, ve); break;
   }
 }
 

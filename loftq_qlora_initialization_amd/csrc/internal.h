@@ -97,7 +97,7 @@ hipError_t launch_nf4_dequantize(const uint8_t* packed, const float* absmax, con
                                  const float* dqscale, int64_t n, int dqbs, const void* W,
                                  loftq_dtype_t wdt, float* out, double* partials, double* wpartials,
                                  double* sumsq, hipStream_t s, int8_t* q_out = nullptr,
-                                 float* dqs_out = nullptr, int bits = 4);
+                                 float* dqs_out = nullptr, int bits = 4, float* a_out = nullptr);
 int dequant_num_partials(int64_t n);
 hipError_t launch_sumsq_weight(const void* W, loftq_dtype_t wdt, int64_t n, double* partials, unsigned* counter,
                                double* sumsq, hipStream_t s);

@@ -41,13 +41,12 @@ __host__ __device__ __forceinline__ int64_t frag_index(int64_t rho, int c, int n
 // v is stored as two bf16 pieces, hi = bf16(v) and lo = bf16(v - hi) (nearest,
 // ties to even), in 32-row K steps laid out as the operands of
 // v_mfma_f32_16x16x32_bf16.  For K step s, tile c / 16 and part (0 hi, 1 lo),
-// lane L = 16 g + li holds 8 bf16 (16 bytes): rows 16 h + 4 g + i (h = 0, 1;
-// i = 0..3) of the step, column 16 (c / 16) + li, i.e. the lane's float4 of the
-// two fragment-order blocks 2 s and 2 s + 1.  Same byte count as the fp32 panel.
+// lane L = 16 g + li holds 8 bf16 (16 bytes): rows 8 g + e (e = 0..7) of the
+// step, column 16 (c / 16) + li.  Same byte count as the fp32 panel.
 __host__ __device__ __forceinline__ int64_t split_index(int64_t rho, int c, int nt, int part) {
   const int64_t step = rho >> 5;
-  const int h = static_cast<int>((rho >> 4) & 1), g = static_cast<int>((rho >> 2) & 3), i = static_cast<int>(rho & 3);
-  return (((step * nt + (c >> 4)) * 2 + part) * 64 + 16 * g + (c & 15)) * 8 + 4 * h + i;
+  const int g = static_cast<int>((rho >> 3) & 3), e = static_cast<int>(rho & 7);
+  return (((step * nt + (c >> 4)) * 2 + part) * 64 + 16 * g + (c & 15)) * 8 + e;
 }
 
 // Workgroup tile of a thin product: rows (gemm_nn) or columns (gemm_tn) per
@@ -80,6 +79,19 @@ struct SvdPlan {
 SvdPlan make_svd_plan(int64_t d, int64_t k, int r, int oversample, bool exact);
 // omega: caller's k x l sketch (row-major), or omega_frag: a sketch already in
 // fragment order over k_pad rows, or neither: the sketch of alternation t is drawn.
+// The residual E = W - deq(Q) formed inside the thin products from the weight
+// and the codes, element by element exactly as the dequant kernel forms it
+// (d = fl32(level[code] a'), e = fl32(w - d)), instead of being read from a
+// stored E: 2 + 0.5 bytes per element (bf16 W) instead of 4.  Needs
+// cols % 8 == 0.
+struct VirtualE {
+  const void* W;
+  int w_bf16;             // 1: W is bf16, 0: fp32
+  const uint8_t* packed;
+  const float* scale;     // a' per 64-block: absmax, or fl32(qabsmax dq_scale) with double quant
+  float level[16];        // the codebook of the codes
+};
+
 // A second stream that takes the orthonormalisation solves (Gram sum, Cholesky,
 // R^-1) off the main stream, so that each runs beside the E^T Y product that
 // follows it; the product's split-K reduction, their first consumer, waits for
@@ -95,7 +107,7 @@ SideLane* side_lane_for(hipStream_t s);
 
 hipError_t run_lowrank(const float* E, const SvdPlan& pl, int q, const float* omega, const float* omega_frag,
                        uint64_t seed, int t, float* B, float* A, float* sigma, char* ws, const ObjectiveArgs& obj,
-                       hipStream_t s, SideLane* side = nullptr);
+                       hipStream_t s, SideLane* side = nullptr, const VirtualE* ve = nullptr);
 // Sketches of alternations t .. t + count - 1, each rows x 16 nt floats in fragment order, back to back.
 hipError_t run_sketch(uint64_t seed, int t, int count, int64_t k, int l, int nt, int64_t rows, float* out,
                       hipStream_t s);
@@ -117,7 +129,7 @@ struct CholJob {
 };
 // panel: the split copy (split_index) of the skinny operand
 void launch_gemm(bool transposed, const float* E, int64_t d, int64_t k, const uint16_t* panel, const SvdPlan& pl,
-                 float* part, const CholJob& job, hipStream_t s);
+                 float* part, const CholJob& job, hipStream_t s, const VirtualE* ve = nullptr);
 
 bool aligned16(const void* p);
 bool shape_ok(int64_t rows, int64_t cols);

@@ -76,8 +76,8 @@ __global__ void warm_columns_kernel(const float* __restrict__ A, const float* __
 }
 
 // Fragment-order fp32 panel (rows_pad rows, a multiple of 32) to its split copy
-// (split_index): one thread per (32-row step, tile, lane) reads the lane's float4
-// of fragment blocks 2 s and 2 s + 1 and writes the hi and lo pieces.
+// (split_index): one thread per (32-row step, tile, lane) reads the lane's eight
+// rows (two float4 of the fragment order) and writes the hi and lo pieces.
 __global__ void split_panel_kernel(const float* __restrict__ frag, int64_t rows_pad, int nt,
                                    uint16_t* __restrict__ out) {
   const int64_t u = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
@@ -86,9 +86,11 @@ __global__ void split_panel_kernel(const float* __restrict__ frag, int64_t rows_
   const int64_t st_tile = u >> 6;
   const int64_t st = st_tile / nt;
   const int tile = static_cast<int>(st_tile - st * nt);
-  const float4* f4 = reinterpret_cast<const float4*>(frag);
-  const float4 a = f4[((2 * st) * nt + tile) * 64 + L];
-  const float4 b = f4[((2 * st + 1) * nt + tile) * 64 + L];
+  // rows 8 g .. 8 g + 7 of the step: quads 2 (g & 1) and 2 (g & 1) + 1 of fragment block 2 st + g / 2
+  const int g = L >> 4, li = L & 15;
+  const float4* f4 = reinterpret_cast<const float4*>(frag) + ((2 * st + (g >> 1)) * nt + tile) * 64 + li;
+  const float4 a = f4[(2 * (g & 1)) * 16];
+  const float4 b = f4[(2 * (g & 1) + 1) * 16];
   const float x[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
   uint4 hi, lo;
   split8_u4(x, hi, lo);
@@ -805,9 +807,7 @@ __global__ __launch_bounds__(kReduceThreads) void reduce_gram_kernel(const float
       const int gg = L >> 4, n = 16 * tn + (L & 15);
       float x[8];
 #pragma unroll
-      for (int h = 0; h < 2; ++h)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) x[4 * h + i] = R[(32 * st + 16 * h + 4 * gg + i) * LDR + n];
+      for (int e = 0; e < 8; ++e) x[e] = R[(32 * st + 8 * gg + e) * LDR + n];
       uint4 hi, lo;
       split8_u4(x, hi, lo);
       const int64_t b = (((rs >> 5) * NT + tn) * 2) * 64 + L;
@@ -1546,7 +1546,7 @@ hipError_t run_objective(const ObjectiveArgs& obj, hipStream_t s) {
 
 hipError_t run_lowrank(const float* E, const SvdPlan& pl, int q, const float* omega, const float* omega_frag,
                        uint64_t seed, int t, float* B, float* A, float* sigma, char* ws, const ObjectiveArgs& obj,
-                       hipStream_t s, SideLane* side) {
+                       hipStream_t s, SideLane* side, const VirtualE* ve) {
   const int64_t d = pl.d, k = pl.k;
   const int r = pl.r, l = pl.l;
   if (pl.exact && pl.bj) {
@@ -1628,7 +1628,7 @@ hipError_t run_lowrank(const float* E, const SvdPlan& pl, int q, const float* om
   hipError_t serr = hipSuccess;
   auto product = [&](bool transposed, const uint16_t* panel_s, int mode) {
     const CholJob job{pending ? gparts : nullptr, pl.gram_parts_d, l, Xinv};
-    launch_gemm(transposed, E, d, k, panel_s, pl, part, job, s);
+    launch_gemm(transposed, E, d, k, panel_s, pl, part, job, s, ve);
     if (transposed) pending = false;
     if (transposed && joining) {   // X = R^-1 from the side lane
       if (serr == hipSuccess) serr = hipStreamWaitEvent(s, side->join, 0);

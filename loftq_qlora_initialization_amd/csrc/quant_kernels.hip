@@ -471,6 +471,7 @@ __global__ __launch_bounds__(kThreads) void dequant_kernel(const uint8_t* __rest
                                                            const int8_t* __restrict__ qa,
                                                            const float* __restrict__ dqs, int dqbs, int64_t n,
                                                            int8_t* __restrict__ qa_out, float* __restrict__ dqs_out,
+                                                           float* __restrict__ a_out,
                                                            const T* __restrict__ W, float* __restrict__ out,
                                                            double* __restrict__ partials,
                                                            double* __restrict__ wpartials,
@@ -516,7 +517,11 @@ __global__ __launch_bounds__(kThreads) void dequant_kernel(const uint8_t* __rest
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int64_t b = b0 + lane + 64 * i;
-          if (b < nb) qa_out[b] = static_cast<int8_t>(dq_code(am[i], sc));
+          if (b < nb) {
+            const int qc = dq_code(am[i], sc);
+            qa_out[b] = static_cast<int8_t>(qc);
+            if (a_out != nullptr) a_out[b] = static_cast<float>(qc) * sc;
+          }
         }
         if (lane == 0) dqs_out[g] = sc;
       }
@@ -534,7 +539,7 @@ __global__ __launch_bounds__(kThreads) void dequant_kernel(const uint8_t* __rest
         ss = fmaf(o[j], o[j], ss);
         if (kHasW) ws = fmaf(w[q][j], w[q][j], ws);
       }
-      *reinterpret_cast<float4*>(out + base + 256 * q) = make_float4(o[0], o[1], o[2], o[3]);
+      if (out != nullptr) *reinterpret_cast<float4*>(out + base + 256 * q) = make_float4(o[0], o[1], o[2], o[3]);
     }
     acc += static_cast<double>(ss);
     wacc += static_cast<double>(ws);
@@ -550,7 +555,11 @@ __global__ __launch_bounds__(kThreads) void dequant_kernel(const uint8_t* __rest
         float m = 0.f;
         for (int64_t b = g0; b < g1; ++b) m = fmaxf(m, absmax[b]);
         const float sc = dq_group_scale(m);
-        for (int64_t b = g0; b < g1; ++b) qa_out[b] = static_cast<int8_t>(dq_code(absmax[b], sc));
+        for (int64_t b = g0; b < g1; ++b) {
+          const int qc = dq_code(absmax[b], sc);
+          qa_out[b] = static_cast<int8_t>(qc);
+          if (a_out != nullptr) a_out[b] = static_cast<float>(qc) * sc;
+        }
         dqs_out[g] = sc;
       }
     }
@@ -565,7 +574,7 @@ __global__ __launch_bounds__(kThreads) void dequant_kernel(const uint8_t* __rest
         const float d = lvl[code] * sc;
         const float wv = kHasW ? load1(W, g * 16 + e) : 0.f;
         const float o = kHasW ? (wv - d) : d;
-        out[g * 16 + e] = o;
+        if (out != nullptr) out[g * 16 + e] = o;
         ss = fmaf(o, o, ss);
         ws = fmaf(wv, wv, ws);
       }
@@ -580,7 +589,7 @@ __global__ __launch_bounds__(kThreads) void dequant_kernel(const uint8_t* __rest
         const float d = lvl[code] * sc;
         const float wv = kHasW ? load1(W, i) : 0.f;
         const float o = kHasW ? (wv - d) : d;
-        out[i] = o;
+        if (out != nullptr) out[i] = o;
         ss = fmaf(o, o, ss);
         ws = fmaf(wv, wv, ws);
       }
@@ -711,14 +720,14 @@ hipError_t quantize_typed(const T* W, int64_t rows, int64_t cols, const float* B
 template <typename T>
 hipError_t dequant_typed(const uint8_t* packed, const float* absmax, const int8_t* q, const float* dqs, int64_t n,
                          int dqbs, int8_t* q_out, float* dqs_out, const T* W, float* out, double* partials,
-                         double* wpartials, double* sumsq, hipStream_t s, int bits) {
+                         double* wpartials, double* sumsq, hipStream_t s, int bits, float* a_out) {
   const Nf4Tables& tab = nf_tables(bits);
   const int grid = dequant_num_partials(n);
   if (partials == nullptr && sumsq != nullptr) LQ_LAUNCH("zero", zero_double_kernel, dim3(1), dim3(1), 0, s, sumsq);
   const int mode = q_out != nullptr ? 2 : (q != nullptr ? 1 : 0);
 #define LQ_DEQ(HW, DQ)                                                                                            \
   LQ_LAUNCH("nf4_dequantize", (dequant_kernel<T, HW, DQ>), dim3(grid), dim3(kThreads), 0, s, packed, absmax, q,   \
-            dqs, dqbs, n, q_out, dqs_out, W, out, partials, wpartials, sumsq, tab)
+            dqs, dqbs, n, q_out, dqs_out, a_out, W, out, partials, wpartials, sumsq, tab)
   if (W != nullptr) {
     if (mode == 2) LQ_DEQ(true, 2); else if (mode == 1) LQ_DEQ(true, 1); else LQ_DEQ(true, 0);
   } else {
@@ -802,7 +811,7 @@ hipError_t launch_double_quant(const float* absmax, int64_t nblocks, int dqbs, i
 hipError_t launch_nf4_dequantize(const uint8_t* packed, const float* absmax, const int8_t* q, const float* dqscale,
                                  int64_t n, int dqbs, const void* W, loftq_dtype_t wdt, float* out, double* partials,
                                  double* wpartials, double* sumsq, hipStream_t s, int8_t* q_out, float* dqs_out,
-                                 int bits) {
+                                 int bits, float* a_out) {
   if (n == 0) {
     if (sumsq) LQ_LAUNCH("zero", zero_double_kernel, dim3(1), dim3(1), 0, s, sumsq);
     return hipGetLastError();
@@ -810,9 +819,9 @@ hipError_t launch_nf4_dequantize(const uint8_t* packed, const float* absmax, con
   if (q_out != nullptr && dqbs != 256) return hipErrorInvalidValue;
   if (wdt == LOFTQ_BF16)
     return dequant_typed(packed, absmax, q, dqscale, n, dqbs, q_out, dqs_out, static_cast<const uint16_t*>(W), out,
-                         partials, wpartials, sumsq, s, bits);
+                         partials, wpartials, sumsq, s, bits, a_out);
   return dequant_typed(packed, absmax, q, dqscale, n, dqbs, q_out, dqs_out, static_cast<const float*>(W), out,
-                       partials, wpartials, sumsq, s, bits);
+                       partials, wpartials, sumsq, s, bits, a_out);
 }
 
 hipError_t launch_sumsq_weight(const void* W, loftq_dtype_t wdt, int64_t n, double* partials, unsigned* counter,
