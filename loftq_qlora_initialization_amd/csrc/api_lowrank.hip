@@ -164,21 +164,30 @@ hipError_t run_init(const InitArgs& a, loftq_dtype_t wdt, const loftq_config_t& 
     // the call's first solve also writes objective[0] (the error of its first quantization)
     const ObjectiveArgs objt{eparts, pl.nparts, wparts, pl.nparts, objective + i, i == 1 ? objective : nullptr};
     const float* om = nullptr;
+    const uint16_t* om_split = nullptr;
     if (pl.sketch_floats > 0) {
       const int slot = (i - 1) % kSketchBatch;
+      // without warm start the +-1 sketches go straight to the products' split layout
+      const bool split = cfg->warm_start == 0;
       if (slot == 0 && e == hipSuccess) {
         const int count = (T - i + 1) < kSketchBatch ? (T - i + 1) : kSketchBatch;
-        e = run_sketch(cfg->seed, t, count, cols, pl.svd.l, pl.svd.nt, pl.svd.k_pad, sketches, s);
+        e = split ? run_sketch_split(cfg->seed, t, count, cols, pl.svd.l, pl.svd.nt, pl.svd.k_pad,
+                                     reinterpret_cast<uint16_t*>(sketches), s)
+                  : run_sketch(cfg->seed, t, count, cols, pl.svd.l, pl.svd.nt, pl.svd.k_pad, sketches, s);
       }
-      om = sketches + slot * pl.sketch_floats;
-      // warm start: from alternation 2 on, the first r columns come from the
-      // previous alternation's A and sigma (still in their buffers here)
-      if (cfg->warm_start != 0 && t > 1 && e == hipSuccess)
-        e = run_warm_columns(A, sigma, cols, r, pl.svd.nt, sketches + slot * pl.sketch_floats, s);
+      if (split) {
+        om_split = reinterpret_cast<const uint16_t*>(sketches + slot * pl.sketch_floats);
+      } else {
+        om = sketches + slot * pl.sketch_floats;
+        // warm start: from alternation 2 on, the first r columns come from the
+        // previous alternation's A and sigma (still in their buffers here)
+        if (t > 1 && e == hipSuccess)
+          e = run_warm_columns(A, sigma, cols, r, pl.svd.nt, sketches + slot * pl.sketch_floats, s);
+      }
     }
     if (e == hipSuccess)
       e = run_lowrank(E, pl.svd, cfg->power_iters, nullptr, om, cfg->seed, t, B, A, sigma, svd_ws, objt, s, side,
-                      formed ? &ve : nullptr);
+                      formed ? &ve : nullptr, om_split);
   }
   return e;
 }

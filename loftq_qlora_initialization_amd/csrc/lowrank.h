@@ -107,10 +107,14 @@ SideLane* side_lane_for(hipStream_t s);
 
 hipError_t run_lowrank(const float* E, const SvdPlan& pl, int q, const float* omega, const float* omega_frag,
                        uint64_t seed, int t, float* B, float* A, float* sigma, char* ws, const ObjectiveArgs& obj,
-                       hipStream_t s, SideLane* side = nullptr, const VirtualE* ve = nullptr);
-// Sketches of alternations t .. t + count - 1, each rows x 16 nt floats in fragment order, back to back.
+                       hipStream_t s, SideLane* side = nullptr, const VirtualE* ve = nullptr,
+                       const uint16_t* omega_split = nullptr);
+// Sketches of alternations t .. t + count - 1, each rows x 16 nt floats in fragment order, back to back;
+// run_sketch_split writes them in the products' split layout instead (the same bytes per sketch).
 hipError_t run_sketch(uint64_t seed, int t, int count, int64_t k, int l, int nt, int64_t rows, float* out,
                       hipStream_t s);
+hipError_t run_sketch_split(uint64_t seed, int t, int count, int64_t k, int l, int nt, int64_t rows, uint16_t* out,
+                            hipStream_t s);
 // Columns j < r of one fragment-order sketch (k rows) <- sqrt(k) A^T diag(sigma)^-1/2.
 hipError_t run_warm_columns(const float* A, const float* sigma, int64_t k, int r, int nt, float* out, hipStream_t s);
 hipError_t run_fill(float* p, int64_t n, float v, hipStream_t s);

@@ -37,6 +37,46 @@ namespace {
 // Element (i, j) of the k x l test matrix of alternation t is drawn from
 // counter ((t - 1) k + i) l + j; written in fragment order over `rows` rows
 // (zero beyond k and l).
+__device__ __forceinline__ float rademacher(uint64_t seed, int t, int64_t k, int l, int64_t i, int j) {
+  const uint64_t c = (static_cast<uint64_t>(t - 1) * static_cast<uint64_t>(k) + static_cast<uint64_t>(i)) *
+                         static_cast<uint64_t>(l) + static_cast<uint64_t>(j);
+  uint64_t z = seed + (c + 1) * 0x9E3779B97F4A7C15ull;
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+  z ^= z >> 31;
+  return (z >> 63) ? -1.f : 1.f;
+}
+
+// The same test matrices straight in the split layout of the bf16 products
+// (split_index over `rows` rows, a multiple of 32): +-1 is exact in bf16, so
+// hi = the value and lo = 0.  One thread per (step, tile, part, lane): 8 values.
+__global__ void sketch_split_kernel(uint64_t seed, int t0, int64_t k, int l, int nt, int64_t rows,
+                                    uint16_t* __restrict__ out) {
+  const int64_t u = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  const int64_t per = (rows >> 5) * nt * 2 * 64;
+  if (u >= per) return;
+  const int t = t0 + static_cast<int>(blockIdx.y);
+  const int L = static_cast<int>(u & 63);
+  const int64_t stp = u >> 6;                     // (step * nt + tile) * 2 + part
+  const int part = static_cast<int>(stp & 1);
+  const int64_t st_tile = stp >> 1;
+  const int64_t step = st_tile / nt;
+  const int tile = static_cast<int>(st_tile - step * nt);
+  const int j = 16 * tile + (L & 15);
+  uint32_t h[4] = {0u, 0u, 0u, 0u};
+  if (part == 0 && j < l) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int64_t i = 32 * step + 8 * (L >> 4) + e;
+      if (i < k) {
+        const uint32_t b = rademacher(seed, t, k, l, i, j) > 0.f ? 0x3F80u : 0xBF80u;   // bf16(+1), bf16(-1)
+        h[e >> 1] |= b << (16 * (e & 1));
+      }
+    }
+  }
+  reinterpret_cast<uint4*>(out + static_cast<int64_t>(blockIdx.y) * per * 8)[u] = make_uint4(h[0], h[1], h[2], h[3]);
+}
+
 __global__ void sketch_kernel(uint64_t seed, int t0, int64_t k, int l, int nt, int64_t rows, float* __restrict__ out) {
   const int64_t idx = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
   if (idx >= rows * 16 * nt) return;
@@ -47,17 +87,7 @@ __global__ void sketch_kernel(uint64_t seed, int t0, int64_t k, int l, int nt, i
   const int tile = e >> 8, f = e & 255;
   const int64_t i = blk * 16 + ((f >> 6) << 2) + (f & 3);
   const int j = tile * 16 + ((f >> 2) & 15);
-  float v = 0.f;
-  if (i < k && j < l) {
-    const uint64_t c = (static_cast<uint64_t>(t - 1) * static_cast<uint64_t>(k) + static_cast<uint64_t>(i)) *
-                           static_cast<uint64_t>(l) + static_cast<uint64_t>(j);
-    uint64_t z = seed + (c + 1) * 0x9E3779B97F4A7C15ull;
-    z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
-    z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
-    z ^= z >> 31;
-    v = (z >> 63) ? -1.f : 1.f;
-  }
-  out[idx] = v;
+  out[idx] = (i < k && j < l) ? rademacher(seed, t, k, l, i, j) : 0.f;
 }
 
 // Warm start of the subspace iteration (a variant the pages do not describe):
@@ -1525,6 +1555,14 @@ hipError_t run_sketch(uint64_t seed, int t, int count, int64_t k, int l, int nt,
   return hipGetLastError();
 }
 
+hipError_t run_sketch_split(uint64_t seed, int t, int count, int64_t k, int l, int nt, int64_t rows, uint16_t* out,
+                            hipStream_t s) {
+  const int64_t n = (rows / 32) * nt * 2 * 64;
+  LQ_LAUNCH("sketch", sketch_split_kernel, dim3(static_cast<unsigned>(cdiv(n, 256)), static_cast<unsigned>(count)),
+            dim3(256), 0, s, seed, t, k, l, nt, rows, out);
+  return hipGetLastError();
+}
+
 hipError_t run_warm_columns(const float* A, const float* sigma, int64_t k, int r, int nt, float* out, hipStream_t s) {
   const int64_t n = k * r;
   if (n <= 0) return hipSuccess;
@@ -1546,7 +1584,7 @@ hipError_t run_objective(const ObjectiveArgs& obj, hipStream_t s) {
 
 hipError_t run_lowrank(const float* E, const SvdPlan& pl, int q, const float* omega, const float* omega_frag,
                        uint64_t seed, int t, float* B, float* A, float* sigma, char* ws, const ObjectiveArgs& obj,
-                       hipStream_t s, SideLane* side, const VirtualE* ve) {
+                       hipStream_t s, SideLane* side, const VirtualE* ve, const uint16_t* omega_split) {
   const int64_t d = pl.d, k = pl.k;
   const int r = pl.r, l = pl.l;
   if (pl.exact && pl.bj) {
@@ -1593,22 +1631,24 @@ hipError_t run_lowrank(const float* E, const SvdPlan& pl, int q, const float* om
   double* stats = reinterpret_cast<double*>(ws + pl.off_stats);
   const ObjectiveArgs none{nullptr, 0, nullptr, 0, nullptr, nullptr};
   const int64_t nfrag = pl.k_pad * 16 * pl.nt;
-  if (omega != nullptr) {
+  if (omega != nullptr && omega_split == nullptr) {
     LQ_LAUNCH("to_frag", to_frag_kernel, dim3(static_cast<unsigned>(cdiv(nfrag, 256))), dim3(256), 0, s, omega, k, l,
               pl.nt, pl.k_pad, Om_ws);
     Om = Om_ws;
-  } else if (omega_frag == nullptr) {
+  } else if (omega_frag == nullptr && omega_split == nullptr) {
     hipError_t e = run_sketch(seed, t, 1, k, l, pl.nt, pl.k_pad, Om_ws, s);
     if (e != hipSuccess) return e;
   }
-  // split copies of the panels for the bf16 products
-  uint16_t* Om_s = reinterpret_cast<uint16_t*>(ws + pl.off_omega_s);
+  // split copies of the panels for the bf16 products (a sketch may come split already)
+  const uint16_t* Om_s = omega_split;
   uint16_t* Y_s = reinterpret_cast<uint16_t*>(ws + pl.off_y_s);
   uint16_t* Z_s = reinterpret_cast<uint16_t*>(ws + pl.off_z_s);
-  {
+  if (Om_s == nullptr) {
+    uint16_t* os = reinterpret_cast<uint16_t*>(ws + pl.off_omega_s);
     const int64_t units = (pl.k_pad / 32) * pl.nt * 64;
     LQ_LAUNCH("split_panel", split_panel_kernel, dim3(static_cast<unsigned>(cdiv(units, 256))), dim3(256), 0, s, Om,
-              pl.k_pad, pl.nt, Om_s);
+              pl.k_pad, pl.nt, os);
+    Om_s = os;
   }
   double* gtotal = reinterpret_cast<double*>(ws + pl.off_gram_total);
   const int E_ = l * (l + 1) / 2;
