@@ -109,6 +109,12 @@ def parse():
     return ap.parse_args()
 
 
+def formed_residual(w, cols):
+    """Whether loftq_init's products form E from W and the codes (the library's default,
+    materialize_residual = 0) rather than read a stored E: randomized SVD, T >= 1, cols % 8 == 0."""
+    return (not w.exact_svd) and w.iterative_steps > 0 and cols % 8 == 0
+
+
 def algorithmic_bytes(name, w, rows, cols):
     """Bytes the method must move per launch of a kernel (inputs read once, outputs written once)."""
     n = rows * cols
@@ -117,13 +123,18 @@ def algorithmic_bytes(name, w, rows, cols):
     wb = 2 if w.dtype == "bf16" else 4
     l = w.rank + w.oversample
     scales = (nb + 4 * ng) if w.double_quant else 4 * nb
+    formed = formed_residual(w, cols)
+    # the residual a product streams: a stored fp32 E, or W, the codes and one fp32 scale per block
+    e_in = (n * wb + -(-n // 2) + 4 * nb) if formed else 4 * n
+    # the dequant-subtract writes E, or (formed, double quant) only the blocks' scales
+    e_out = (4 * nb if w.double_quant else 0) if formed else 4 * n
     table = {
         "nf4_quantize": n * wb + -(-n // 2) + 4 * nb,
         "nf4_quantize_fused": n * wb + -(-n // 2) + 4 * nb + 4 * w.rank * (rows + cols),
         "double_quant": 4 * nb + nb + 4 * ng,
-        "nf4_dequantize": n * wb + -(-n // 2) + scales + 4 * n,
-        "gemm_nn": 4 * n + 4 * cols * l + 4 * rows * l,
-        "gemm_tn": 4 * n + 4 * rows * l + 4 * cols * l,
+        "nf4_dequantize": n * wb + -(-n // 2) + scales + e_out,
+        "gemm_nn": e_in + 4 * cols * l + 4 * rows * l,
+        "gemm_tn": e_in + 4 * rows * l + 4 * cols * l,
         "sumsq_weight": n * wb,
         # adapter merge: codes and scales in, codes and fp32 absmax out, B and A
         "nf4_merge": -(-n // 2) + scales + -(-n // 2) + 4 * nb + 4 * w.rank * (rows + cols),
@@ -296,14 +307,27 @@ def main():
             tot += count * launches.get(name, 0) * b
         return tot
 
-    # profiled pass: HIP events around every library launch, the same steps on the same streams
+    # profiled pass: HIP events around every library launch.  The batch is profiled in one pass
+    # on a single stream, so that a launch's events bracket that launch alone (with several
+    # streams a launch can sit behind another stream's kernel between its start event and its
+    # first wave); a single matrix repeats the timed steps.
+    prof_steps = 1 if batch else steps
+    if batch:
+        prof_runner = lq.BatchRunner(Ws, cfg, nstreams=1)
+        prof_runner.run()
+        torch.cuda.synchronize()
+        prof_step = prof_runner.run
+    else:
+        prof_step = step
     lq.profile_enable(True)
-    for _ in range(steps):
-        step()
+    for _ in range(prof_steps):
+        prof_step()
     torch.cuda.synchronize()
     lq.profile_enable(False)
     prof = lq.profile_collect()
-    kernels = kernel_table(prof, steps, bytes_per_step)
+    if batch:
+        del prof_runner
+    kernels = kernel_table(prof, prof_steps, bytes_per_step)
     for name, e in kernels.items():   # every launch of the batch accounted for by the per-shape counts
         want = sum(c * l.get(name, 0) for _, c, l in per_shape.values())
         if want and abs(e["launches_per_step"] - want) > 1e-9:
@@ -316,8 +340,8 @@ def main():
                 "traffic": measured_traffic(wname, dom),
                 "bytes_per_launch": kernels[dom]["bytes_per_launch"], "avg_us": kernels[dom]["avg_us"]}
     if batch:
-        roofline["note"] = (f"durations measured with the batch's {args.streams} streams running at once, so a "
-                            "launch shares the device with the other streams' kernels")
+        roofline["note"] = ("launch durations from one profiled pass of the whole batch on a single stream "
+                            f"(the timed steps run on {args.streams} streams)")
     qname = "nf4_quantize" if "nf4_quantize" in kernels else None
     nf4 = None
     if qname:
@@ -470,7 +494,9 @@ def main():
 
     config = {"workload": wname, "matrices": len(specs), "elements": total_elems, "storage": w.dtype,
               "rank": w.rank, "iterative_steps": w.iterative_steps, "oversample": w.oversample,
-              "power_iters": w.power_iters, "double_quant": w.double_quant, "blocksize": 64, "dq_blocksize": 256}
+              "power_iters": w.power_iters, "double_quant": w.double_quant, "blocksize": 64, "dq_blocksize": 256,
+              "residual": "formed in the products from W and the codes"
+              if all(formed_residual(x, x.cols) for x in specs) else "stored E"}
     if batch:
         config.update(shapes={f"{r}x{c}": n for (r, c), (_, n, _) in per_shape.items()}, streams=args.streams,
                       call="loftq_init_batch", extras_on=specs[0].name)
