@@ -750,7 +750,7 @@ __global__ __launch_bounds__(kReduceThreads) void reduce_gram_kernel(const float
                                                           double* __restrict__ gram_parts) {
   constexpr int LP = 16 * NT, PER = (kGramRows * LP + kReduceThreads - 1) / kReduceThreads, LDR = LP + 1;
   constexpr int NW = kReduceThreads / 64;
-  static_assert(kGramRows % 16 == 0, "whole 16-row MFMA tiles");
+  static_assert(kGramRows % 32 == 0, "whole 32-row steps of the split copy (and 16-row MFMA tiles)");
   // wide panels (NT >= 3) keep fewer loads in flight, so the per-thread state
   // fits the register file of a 512-thread workgroup
   constexpr int QB = NT <= 2 ? 8 : 2;
@@ -830,7 +830,7 @@ __global__ __launch_bounds__(kReduceThreads) void reduce_gram_kernel(const float
   // eight rows of its column as hi and lo pieces
   if (out_split != nullptr) {
     uint4* os = reinterpret_cast<uint4*>(out_split);
-    for (int ui = threadIdx.x; ui < 2 * NT * 64; ui += blockDim.x) {
+    for (int ui = threadIdx.x; ui < (kGramRows / 32) * NT * 64; ui += blockDim.x) {
       const int L = ui & 63, tn = (ui >> 6) % NT, st = (ui >> 6) / NT;
       const int64_t rs = r0 + 32 * st;
       if (rs >= m_pad) continue;
