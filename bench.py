@@ -11,7 +11,8 @@ per second (sum of rows * cols per step).  The JSON line also carries:
   roofline      the dominant streaming kernel: algorithmic bytes per launch over
                 its average launch time, timed with HIP events that the library
                 records around each launch on its own stream during a separate
-                profiled pass over the same steps;
+                profiled pass over the same steps, less what the events read for
+                an empty kernel bracketed the same way (event_overhead_us);
   nf4_quantize  the same for the NF4 quantize kernel (the metric's second part);
   nf4_merge     the adapter merge of the init's own B, A into its Q, timed the same way;
   warm_start_variant  the same init with a warm-started subspace iteration and one
@@ -41,9 +42,14 @@ HBM_PEAK_GBS = 8000.0   # MI355X HBM3E
 MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 matrix cores
 
 # HBM bytes per dispatch measured with rocprofv3 FETCH_SIZE / WRITE_SIZE passes (calibrated
-# against a 256 MiB device copy) on the 4096x4096 workload, valid while the kernel source
-# is unchanged (sha256 prefix of the file the kernel lives in); reported as null otherwise.
+# against a 256 MiB device copy), valid while the kernel source is unchanged (sha256 prefix of
+# the file the kernel lives in); reported as null otherwise.
 MEASURED_TRAFFIC = {
+    # the decoder batch: means over the dispatches of a one-layer batch (the same seven shapes in the
+    # same proportions), residual formed from W and the codes
+    "c4_decoder_batch_224_bf16": {
+        "gemm_nn": {"bytes": 126353691, "source": "gemm_kernels.hip", "sha256": "af5f283d0fd2e9cf"},
+    },
     "c2_4096x4096_bf16": {
         "gemm_nn": {"bytes": 77784775, "source": "gemm_kernels.hip", "sha256": "4322c77aea1b6c85"},
         "gemm_tn": {"bytes": 75687250, "source": "gemm_kernels.hip", "sha256": "4322c77aea1b6c85"},
@@ -200,20 +206,35 @@ def device_weights(specs, workers):
         return list(ex.map(one, specs))
 
 
-def kernel_table(prof, steps, bytes_per_step):
+def kernel_table(prof, steps, bytes_per_step, overhead_us=0.0):
     """Per-kernel launches, average launch time, share and algorithmic GB/s from a profiled pass.
-    bytes_per_step(name) -> algorithmic bytes all launches of that kernel move in one step, or None."""
+    bytes_per_step(name) -> algorithmic bytes all launches of that kernel move in one step, or None.
+    overhead_us: what a bracketed launch's events read beyond its kernel (an empty kernel's bracketed
+    time, profile_calibrate); avg_us is net of it, event_us the raw event average."""
     kernels = {}
     total = sum(v[1] for v in prof.values())
     for name, (launches, total_ms) in sorted(prof.items(), key=lambda kv: -kv[1][1]):
-        avg_us = 1e3 * total_ms / launches
-        entry = {"launches_per_step": launches / steps, "avg_us": round(avg_us, 3), "share": round(total_ms / total, 4)}
+        event_us = 1e3 * total_ms / launches
+        avg_us = max(event_us - overhead_us, 1e-3)
+        entry = {"launches_per_step": launches / steps, "avg_us": round(avg_us, 3), "event_us": round(event_us, 3),
+                 "share": round(total_ms / total, 4)}
         nbytes = bytes_per_step(name)
         if nbytes is not None:
-            entry["GBps"] = round(nbytes * steps / (total_ms * 1e-3) / 1e9, 1)
+            entry["GBps"] = round(nbytes * steps / (launches * avg_us * 1e-6) / 1e9, 1)
             entry["bytes_per_launch"] = round(nbytes * steps / launches)
         kernels[name] = entry
     return kernels
+
+
+def event_overhead_us(lq, torch):
+    """Average bracketed time of an empty kernel on the current stream (256 launches)."""
+    lq.profile_collect()
+    lq.profile_enable(True)
+    lq.profile_calibrate(256)
+    torch.cuda.synchronize()
+    lq.profile_enable(False)
+    rec = lq.profile_collect().get("event_overhead")
+    return 1e3 * rec[1] / rec[0] if rec else 0.0
 
 
 def main():
@@ -327,7 +348,8 @@ def main():
     prof = lq.profile_collect()
     if batch:
         del prof_runner
-    kernels = kernel_table(prof, prof_steps, bytes_per_step)
+    overhead = event_overhead_us(lq, torch)
+    kernels = kernel_table(prof, prof_steps, bytes_per_step, overhead)
     for name, e in kernels.items():   # every launch of the batch accounted for by the per-shape counts
         want = sum(c * l.get(name, 0) for _, c, l in per_shape.values())
         if want and abs(e["launches_per_step"] - want) > 1e-9:
@@ -338,7 +360,8 @@ def main():
     roofline = {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4),
                 "traffic": measured_traffic(wname, dom),
-                "bytes_per_launch": kernels[dom]["bytes_per_launch"], "avg_us": kernels[dom]["avg_us"]}
+                "bytes_per_launch": kernels[dom]["bytes_per_launch"], "avg_us": kernels[dom]["avg_us"],
+                "event_us": kernels[dom]["event_us"], "event_overhead_us": round(overhead, 3)}
     if batch:
         roofline["note"] = ("launch durations from one profiled pass of the whole batch on a single stream "
                             f"(the timed steps run on {args.streams} streams)")
@@ -381,7 +404,7 @@ def main():
         mprof = lq.profile_collect()
         if "nf4_merge" in mprof:
             launches, total_ms = mprof["nf4_merge"]
-            avg_us = 1e3 * total_ms / launches
+            avg_us = max(1e3 * total_ms / launches - overhead, 1e-3)
             gb = algorithmic_bytes("nf4_merge", w, w.rows, w.cols) / (avg_us * 1e-6) / 1e9
             step_us = 1e3 * sum(v[1] for v in mprof.values()) / steps
             valu = measured_valu(w.name, "nf4_merge")
@@ -470,8 +493,8 @@ def main():
             fprof = lq.profile_collect()
             gname = "nf4_gemm" if "nf4_gemm" in fprof else "nf4_gemm_skinny"
             gl, gms = fprof[gname]
-            g_us = 1e3 * gms / gl
-            d_us = 1e3 * fprof["lora_down"][1] / fprof["lora_down"][0] if "lora_down" in fprof else 0.0
+            g_us = max(1e3 * gms / gl - overhead, 1e-3)
+            d_us = max(1e3 * fprof["lora_down"][1] / fprof["lora_down"][0] - overhead, 0.0) if "lora_down" in fprof else 0.0
             flops = 2.0 * ntok * w.rows * w.cols
             lora_flops = 2.0 * ntok * w.rank * (w.rows + w.cols)
             qbytes = algorithmic_bytes("qlora_weight", w, w.rows, w.cols)

@@ -326,6 +326,10 @@ loftq_status_t loftq_nf_codebook(int32_t bits, float* out);
  *   total_ms [host] max_entries summed durations in milliseconds, or NULL */
 void loftq_profile_enable(int on);
 int loftq_profile_collect(int max_entries, char* names, int64_t* launches, double* total_ms);
+/* n launches of an empty kernel on `stream`, bracketed like the library's launches (recorded as
+ * "event_overhead" while timing is enabled): the time a bracketed launch's events add to its kernel.
+ * Returns 0, or 1 if a launch failed. */
+int loftq_profile_calibrate(int n, void* stream);
 
 #ifdef __cplusplus
 }

@@ -13,7 +13,7 @@ _BINDING_NAMES = {
     "loftq_nf4_quantize", "loftq_double_quant", "loftq_nf4_dequantize", "loftq_nf4_merge", "loftq_nf4_unmerge",
     "loftq_lowrank_svd", "loftq_init", "loftq_qlora_forward", "qlora_forward_workspace_bytes",
     "default_config", "nf4_codebook", "nf_codebook", "exported_symbols", "workspace_bytes", "lowrank_workspace_bytes",
-    "InitBuffers", "LoftqConfig", "LoftqError", "LIB_PATH", "EXPORTS", "profile_enable", "profile_collect",
+    "InitBuffers", "LoftqConfig", "LoftqError", "LIB_PATH", "EXPORTS", "profile_enable", "profile_collect", "profile_calibrate",
     "loftq_init_batch", "BatchRunner", "LoftqMatrix", "loftq_qlora_forward_noalloc", "qlora_forward_noalloc_max_bytes",
 }
 

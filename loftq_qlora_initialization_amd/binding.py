@@ -37,7 +37,7 @@ EXPORTS = ["loftq_init_batch", "loftq_batch_workspace_bytes", "loftq_nf4_quantiz
            "loftq_lowrank_svd_workspace_bytes", "loftq_init", "loftq_workspace_bytes", "loftq_default_config",
            "loftq_status_string", "loftq_nf4_codebook", "loftq_nf_codebook", "loftq_qlora_forward",
            "loftq_qlora_forward_workspace_bytes", "loftq_qlora_forward_noalloc", "loftq_qlora_forward_noalloc_max_bytes",
-           "loftq_profile_enable", "loftq_profile_collect"]
+           "loftq_profile_enable", "loftq_profile_collect", "loftq_profile_calibrate"]
 
 
 class LoftqConfig(ctypes.Structure):
@@ -94,6 +94,7 @@ _c_codebook = _sig("loftq_nf4_codebook", None, [ctypes.POINTER(ctypes.c_float)])
 _c_nf_codebook = _sig("loftq_nf_codebook", ctypes.c_int, [_I32, ctypes.POINTER(ctypes.c_float)])
 _c_prof_on = _sig("loftq_profile_enable", None, [ctypes.c_int])
 _c_prof_get = _sig("loftq_profile_collect", ctypes.c_int, [ctypes.c_int, ctypes.c_char_p, _P, _P])
+_c_prof_cal = _sig("loftq_profile_calibrate", ctypes.c_int, [ctypes.c_int, _P])
 
 
 class LoftqError(RuntimeError):
@@ -418,6 +419,11 @@ def loftq_init_batch(Ws, cfg: Optional[LoftqConfig] = None, nstreams: int = 4, *
 def profile_enable(on: bool = True) -> None:
     """Bracket every library kernel launch with HIP events on its stream (measurement only)."""
     _c_prof_on(1 if on else 0)
+
+
+def profile_calibrate(n: int = 256, stream=None) -> None:
+    """n bracketed launches of an empty kernel (recorded as "event_overhead" while timing is enabled)."""
+    _check("loftq_profile_calibrate", _c_prof_cal(n, _stream(stream)))
 
 
 def profile_collect(max_entries: int = 64) -> dict:

@@ -45,11 +45,26 @@ ProfScope::~ProfScope() {
 
 }  // namespace loftq
 
+namespace loftq {
+namespace {
+__global__ void lq_empty_kernel(int) {}
+}  // namespace
+}  // namespace loftq
+
 using namespace loftq;
 
 extern "C" {
 
 void loftq_profile_enable(int on) { g_enabled.store(on ? 1 : 0); }
+
+// n launches of an empty kernel on `stream`, bracketed like every library launch (while timing is
+// enabled, under the name "event_overhead"): what a bracketed launch's events read beyond its
+// kernel, to be subtracted from the averages.
+int loftq_profile_calibrate(int n, void* stream) {
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  for (int i = 0; i < n; ++i) LQ_LAUNCH("event_overhead", lq_empty_kernel, dim3(1), dim3(64), 0, s, 0);
+  return hipGetLastError() == hipSuccess ? 0 : 1;
+}
 
 int loftq_profile_collect(int max_entries, char* names, int64_t* launches, double* total_ms) {
   std::vector<Rec> recs;
