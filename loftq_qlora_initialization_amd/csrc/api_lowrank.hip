@@ -35,7 +35,8 @@ struct InitPlan {
   SvdPlan svd;
   int nparts;
   int64_t sketch_floats;   // one alternation's sketch in fragment order (0 for the exact SVD)
-  int64_t off_e, off_parts, off_wparts, off_sketch, off_svd, off_ascale, bytes;
+  int64_t off_e, off_parts, off_wparts, off_sketch, off_svd, off_ascale, off_nparts, bytes;
+  int nn_parts;            // ||E||^2 partials of the first product E Omega (alternations after the first)
 };
 
 // Whether the products form E from W and the codes (E is then never stored).
@@ -58,6 +59,8 @@ InitPlan make_init_plan(int64_t rows, int64_t cols, const loftq_config_t& c) {
   p.off_svd = off;    off += align256(p.svd.bytes);
   // formed residual with double quant: a' = fl32(qabsmax dq_scale) per block, written by the dequant
   p.off_ascale = off; off += (formed_residual(cols, c) && c.double_quant) ? align256(((n + 63) / 64) * 4) : 0;
+  p.nn_parts = p.svd.exact ? 0 : p.svd.nn_row_blocks * p.svd.nn_splits;
+  p.off_nparts = off; off += align256(static_cast<int64_t>(p.nn_parts) * 8);
   p.bytes = off;
   return p;
 }
@@ -135,15 +138,24 @@ hipError_t run_init(const InitArgs& a, loftq_dtype_t wdt, const loftq_config_t& 
   const int r = cfg->rank;
   const int T = cfg->iterative_steps;
   float* sketches = reinterpret_cast<float*>(w + pl.off_sketch);
-  // the first dequant also leaves the partials of ||W||^2 (W is read there anyway)
+  double* nparts = reinterpret_cast<double*>(w + pl.off_nparts);
+  // ||E||^2 of an alternation of the randomized path comes from its first product
+  // E Omega, which forms (or reads) every element of E anyway; the dequant sums it
+  // only for T = 0 and the exact SVD.  So the dequant runs in the call's first
+  // alternation (for the partials of ||W||^2, W being read there anyway) and
+  // wherever E is stored; with E formed in the products the later alternations
+  // only need the double quant (with each block's a').
+  const bool dq_norms = T == 0 || pl.svd.exact;
   auto quant_step = [&](const float* Bp, const float* Ap, bool first) -> hipError_t {
     hipError_t x = launch_nf4_quantize(W, wdt, rows, cols, Bp, Ap, r, packed, absmax, s, cfg->bits);
+    if (x != hipSuccess) return x;
+    if (!first && formed)
+      return dq ? launch_double_quant(absmax, (n + 63) / 64, cfg->dq_blocksize, qabsmax, dq_scale, s, ascale)
+                : hipSuccess;
     // the double quant of the absmax is derived (and written) inside the dequant
-    if (x == hipSuccess)
-      x = launch_nf4_dequantize(packed, absmax, nullptr, nullptr, n, cfg->dq_blocksize, W, wdt, E, eparts,
-                                first ? wparts : nullptr, nullptr, s, dq ? qabsmax : nullptr, dq ? dq_scale : nullptr,
-                                cfg->bits, ascale);
-    return x;
+    return launch_nf4_dequantize(packed, absmax, nullptr, nullptr, n, cfg->dq_blocksize, W, wdt, E,
+                                 dq_norms ? eparts : nullptr, first ? wparts : nullptr, nullptr, s,
+                                 dq ? qabsmax : nullptr, dq ? dq_scale : nullptr, cfg->bits, ascale);
   };
   hipError_t e = hipSuccess;
   if (T == 0) {
@@ -162,7 +174,8 @@ hipError_t run_init(const InitArgs& a, loftq_dtype_t wdt, const loftq_config_t& 
     const bool fresh = (t == 1);
     e = quant_step(fresh ? nullptr : B, fresh ? nullptr : A, i == 1);
     // the call's first solve also writes objective[0] (the error of its first quantization)
-    const ObjectiveArgs objt{eparts, pl.nparts, wparts, pl.nparts, objective + i, i == 1 ? objective : nullptr};
+    const ObjectiveArgs objt{dq_norms ? eparts : nparts, dq_norms ? pl.nparts : pl.nn_parts, wparts, pl.nparts,
+                             objective + i, i == 1 ? objective : nullptr};
     const float* om = nullptr;
     const uint16_t* om_split = nullptr;
     if (pl.sketch_floats > 0) {
@@ -187,7 +200,7 @@ hipError_t run_init(const InitArgs& a, loftq_dtype_t wdt, const loftq_config_t& 
     }
     if (e == hipSuccess)
       e = run_lowrank(E, pl.svd, cfg->power_iters, nullptr, om, cfg->seed, t, B, A, sigma, svd_ws, objt, s, side,
-                      formed ? &ve : nullptr, om_split);
+                      formed ? &ve : nullptr, om_split, dq_norms ? nullptr : nparts);
   }
   return e;
 }

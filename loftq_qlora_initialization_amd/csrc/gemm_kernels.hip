@@ -11,10 +11,11 @@
 // term).  Against fp32 matrix cores (v_mfma_f32_16x16x4_f32), whose work bounds
 // the wide panels (l = 80: 160 flop per 4 bytes of E), the three bf16 products
 // take about a fifth of the matrix-core time.  v_mfma_f32_16x16x32_bf16 takes
-// K = 32 per instruction; lane (li, g) supplies K index 8 g + e (e = 0..7) <->
-// row 8 g + e of the step (the panel's split layout, split_index), and E is
-// loaded to match: gemm_nn reads 8 consecutive columns of a row per lane,
-// gemm_tn 4 columns of 8 consecutive rows.  E is split in registers as it arrives; the panel
+// K = 32 per instruction; in K step s lane (li, g) supplies K index 8 g + e
+// (e = 0..7) <-> row split_row(s, g, e) of the panel (its split layout,
+// split_index: row 32 s + 8 g + e for E P's operand; the rows of each pair of
+// steps interleaved for E^T Y's), and E is loaded to match: gemm_nn reads 8
+// consecutive columns of a row per lane, gemm_tn 4 columns of 8 rows.  E is split in registers as it arrives; the panel
 // comes already split (split_index), written so by the split-K reduction that
 // produces it.
 //
@@ -165,9 +166,23 @@ __device__ __forceinline__ floatx4 mfma_bf16(const bf16x8& a, const bf16x8& b, f
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
+// Workgroups are handed to the 8 XCDs round-robin in launch order, each XCD with
+// an L2 of its own.  The tile of a workgroup comes from its launch index so that
+// every XCD takes one contiguous run of tiles (X_FAST: x varies fastest in the
+// run): neighbouring tiles that read the same code and scale lines then meet in
+// one L2 instead of fetching those lines once per XCD.
+template <bool X_FAST>
+__device__ __forceinline__ void xcd_tile(int& bx, int& by) {
+  const int gx = static_cast<int>(gridDim.x), gy = static_cast<int>(gridDim.y);
+  const int i = static_cast<int>(blockIdx.x) + static_cast<int>(blockIdx.y) * gx;
+  const int n = gx * gy, q = n >> 3, rem = n & 7, x = i & 7, p = i >> 3;
+  const int L = x * q + (x < rem ? x : rem) + p;
+  if (X_FAST) { bx = L % gx; by = L / gx; } else { by = L % gy; bx = L / gy; }
+}
+
 template <int NT>
 struct Nn3Cfg {
-  static constexpr int RT = 2;                 // 16-row MFMA tiles per wave
+  static constexpr int RT = 1;                 // 16-row MFMA tiles per wave
   static constexpr int D = 4;                  // E register ring depth (K steps of 32)
   static constexpr int WR = 4;                 // waves along rows, sharing the staged panel
   static constexpr int PU = NT * 128;          // 16-byte pieces of one K step of the split panel
@@ -186,10 +201,14 @@ struct Tn3Cfg {
 // buffered, one barrier per step) and the waves read their B operands from there:
 // the panel then costs one L2 read per workgroup instead of one per wave.  E runs
 // through a D-deep register ring of its own.
-template <int NT, typename Src>
+// NORMS: the workgroup also sums the squares of the elements of E it forms (each
+// exactly once: clamped rows and columns are left out; eight at a time in fp32,
+// those sums in fp64) and writes the sum to nparts[workgroup tile]; in a fixed
+// order, so the partials are deterministic.
+template <int NT, typename Src, bool NORMS>
 __global__ __launch_bounds__(64 * Nn3Cfg<NT>::WR) void gemm_nn3_kernel(
     Src src, int64_t d, int64_t k, const uint16_t* __restrict__ Xs, int64_t kper,
-    float* __restrict__ part) {
+    float* __restrict__ part, double* __restrict__ nparts) {
   using C = Nn3Cfg<NT>;
   constexpr int LP = 16 * NT, RT = C::RT, D = C::D, WR = C::WR, PU = C::PU, PPT = C::PPT;
   static_assert(D % 2 == 0 && WR * 64 == 256, "ring parity and the 256-thread panel staging");
@@ -198,15 +217,20 @@ __global__ __launch_bounds__(64 * Nn3Cfg<NT>::WR) void gemm_nn3_kernel(
   fill_level_pairs(src, lvl2);            // the barrier before the first step covers it
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int g = lane >> 4, li = lane & 15;
-  const int64_t row0 = (static_cast<int64_t>(blockIdx.x) * WR + w) * 16 * RT;
-  const int64_t kb = static_cast<int64_t>(blockIdx.y) * kper;
+  int tbx, tby;
+  xcd_tile<false>(tbx, tby);   // the splits of one row block share their scale lines
+  const int64_t row0 = (static_cast<int64_t>(tbx) * WR + w) * 16 * RT;
+  const int64_t kb = static_cast<int64_t>(tby) * kper;
   const int nsteps = static_cast<int>(kper / 32);   // a multiple of D
   int64_t erow[RT];
+  bool rok[RT];
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
     const int64_t r = row0 + rt * 16 + li;
     erow[rt] = r < d ? r : d - 1;
+    rok[rt] = r < d;
   }
+  double sq = 0.0;
   const uint4* xg = reinterpret_cast<const uint4*>(Xs) + (kb / 32) * PU;
   floatx4 acc[RT][NT];
 #pragma unroll
@@ -242,7 +266,8 @@ __global__ __launch_bounds__(64 * Nn3Cfg<NT>::WR) void gemm_nn3_kernel(
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) eb[u][rt] = src.fetch8(erow[rt], c, k);
   };
-  auto compute = [&](int u, int buf) {
+  // step j from ring slot u and LDS buffer buf
+  auto compute = [&](int u, int buf, int j) {
     bf16x8 ah[RT], al[RT], bh[NT], bl[NT];
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
@@ -253,6 +278,20 @@ __global__ __launch_bounds__(64 * Nn3Cfg<NT>::WR) void gemm_nn3_kernel(
     for (int rt = 0; rt < RT; ++rt) {
       float x[8];
       src.decode8(eb[u][rt], x, lvl2);
+      if constexpr (NORMS) {
+        // the eight squares summed in fp32 (relative error below 2^-21), then in fp64
+        const int64_t nv = rok[rt] ? k - (kb + 32 * j + 8 * g) : 0;   // valid columns of the eight
+        float s8 = 0.f;
+        if (nv >= 8) {
+#pragma unroll
+          for (int i = 0; i < 8; ++i) s8 = fmaf(x[i], x[i], s8);
+        } else {
+#pragma unroll
+          for (int i = 0; i < 8; ++i)
+            if (i < nv) s8 = fmaf(x[i], x[i], s8);
+        }
+        sq += static_cast<double>(s8);
+      }
       split8(x, ah[rt], al[rt]);
     }
     // the three products interleaved over the RT x NT accumulators
@@ -292,7 +331,7 @@ __global__ __launch_bounds__(64 * Nn3Cfg<NT>::WR) void gemm_nn3_kernel(
 #pragma unroll
     for (int u = 0; u < D; u += 2) {
       const int j = rd * D + u;   // even step j, then odd step j + 1
-      compute(u, 0);
+      compute(u, 0, j);
       __builtin_amdgcn_sched_barrier(0);
       LQ_PANEL_STORE(1, 1);          // the panel of step j + 1
       __syncthreads();
@@ -300,7 +339,7 @@ __global__ __launch_bounds__(64 * Nn3Cfg<NT>::WR) void gemm_nn3_kernel(
       __builtin_amdgcn_sched_barrier(0);
       load_e(u, j + D);
       __builtin_amdgcn_sched_barrier(0);
-      compute(u + 1, 1);
+      compute(u + 1, 1, j + 1);
       __builtin_amdgcn_sched_barrier(0);
       LQ_PANEL_STORE(0, 0);          // the panel of step j + 2
       __syncthreads();
@@ -319,15 +358,28 @@ __global__ __launch_bounds__(64 * Nn3Cfg<NT>::WR) void gemm_nn3_kernel(
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
         const int64_t row = row0 + rt * 16 + 4 * g + v;
-        if (row < d) part[(static_cast<int64_t>(blockIdx.y) * d + row) * LP + nt * 16 + li] = acc[rt][nt][v];
+        if (row < d) part[(static_cast<int64_t>(tby) * d + row) * LP + nt * 16 + li] = acc[rt][nt][v];
       }
+  if constexpr (NORMS) {
+    __shared__ double wsq[WR];
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) sq += __shfl_xor(sq, off);
+    if (lane == 0) wsq[w] = sq;
+    __syncthreads();
+    if (tid == 0) {
+      double t = 0.0;
+#pragma unroll
+      for (int q = 0; q < WR; ++q) t += wsq[q];
+      nparts[static_cast<int64_t>(tby) * gridDim.x + tbx] = t;
+    }
+  }
 }
 
 // gemm_tn.  Wave (wc, wr) owns one 64-column group (its four interleaved 16-column
 // MFMA tiles jm hold columns c0 + 4 m + jm) and its share of the workgroup's rows;
 // waves sharing columns are summed through LDS at the end.  Row steps of 32: lane (li, g) loads rows
-// 8 g + e of the step (eight float4 of its four columns), and tile jm's A
-// operand is component jm of those eight.
+// split_row(j, g, e, paired) of its range (eight runs of its four columns), and
+// tile jm's A operand is component jm of those eight.
 template <int NT, typename Src, int LMJ>
 __global__ __launch_bounds__(64 * Tn3Cfg<NT>::WC * Tn3Cfg<NT>::WR) void gemm_tn3_kernel(
     Src src, int64_t d, int64_t k, const uint16_t* __restrict__ Ys, int64_t rper,
@@ -339,13 +391,15 @@ __global__ __launch_bounds__(64 * Tn3Cfg<NT>::WC * Tn3Cfg<NT>::WR) void gemm_tn3
   constexpr int kLdsBytes = 4 * kRedFloats > 8 * kJobDoubles ? 4 * kRedFloats : 8 * kJobDoubles;
   __shared__ __align__(16) char lds_raw[kLdsBytes];
   float* red = reinterpret_cast<float*>(lds_raw);
+  int tbx, tby;
+  xcd_tile<true>(tbx, tby);   // neighbouring column blocks share their code and scale lines
   // LMJ > 0: the extra last column of workgroups carries a Cholesky job; its
   // row 0 sums the Gram partials of Y and factors them (X = R^-1 for the
   // reduction that follows this product), l <= LMJ.  The plan leaves a CU free
   // for it.
   if constexpr (LMJ > 0) {
-    if (blockIdx.x == gridDim.x - 1) {
-      if (blockIdx.y == 0) {
+    if (tbx == static_cast<int>(gridDim.x) - 1) {
+      if (tby == 0) {
         double* lds = reinterpret_cast<double*>(lds_raw);
         const double* gram = gram_sum_block<LMJ>(job.parts, job.P, job.l, lds);
         if (threadIdx.x < 64) chol_inv_to<LMJ>(gram, job.l, job.Xinv, lds);
@@ -360,7 +414,7 @@ __global__ __launch_bounds__(64 * Tn3Cfg<NT>::WC * Tn3Cfg<NT>::WR) void gemm_tn3
   }
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, wc = w % WC, wr = w / WC;
   const int g = lane >> 4, li = lane & 15;
-  const int64_t bx = blockIdx.x, by = blockIdx.y;   // column block, row split
+  const int64_t bx = tbx, by = tby;   // column block, row split
   const int64_t c0 = (bx * WC + wc) * 64;
   const int64_t cl = c0 + 4 * li;
   const int64_t rw = rper / WR;
@@ -377,7 +431,7 @@ __global__ __launch_bounds__(64 * Tn3Cfg<NT>::WC * Tn3Cfg<NT>::WR) void gemm_tn3
   auto load = [&](int u, int j) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      int64_t r = rb + 32 * j + 8 * g + e;
+      int64_t r = rb + split_row(j, g, e, true);
       r = r < d ? r : d - 1;
       eb[u][e] = src.fetch4(r, cl, k);
     }
@@ -469,7 +523,7 @@ GemmShape shape_typed(bool transposed) {
 
 template <int NT, typename Src>
 void gemm_launch(bool transposed, const Src& src, int64_t d, int64_t k, const uint16_t* panel, const SvdPlan& pl,
-                 float* part, const CholJob& job, hipStream_t s) {
+                 float* part, const CholJob& job, hipStream_t s, double* nparts) {
   if (transposed) {
     constexpr int threads = 64 * Tn3Cfg<NT>::WC * Tn3Cfg<NT>::WR;
     const dim3 grid(pl.tn_col_blocks + (job.parts != nullptr ? 1 : 0), pl.tn_splits);
@@ -488,18 +542,23 @@ void gemm_launch(bool transposed, const Src& src, int64_t d, int64_t k, const ui
   }
   constexpr int threads = 64 * Nn3Cfg<NT>::WR;
   const dim3 grid(pl.nn_row_blocks, pl.nn_splits);
-  LQ_LAUNCH("gemm_nn", (gemm_nn3_kernel<NT, Src>), grid, dim3(threads), 0, s, src, d, k, panel, pl.nn_kper, part);
+  if (nparts != nullptr)
+    LQ_LAUNCH("gemm_nn", (gemm_nn3_kernel<NT, Src, true>), grid, dim3(threads), 0, s, src, d, k, panel, pl.nn_kper, part,
+              nparts);
+  else
+    LQ_LAUNCH("gemm_nn", (gemm_nn3_kernel<NT, Src, false>), grid, dim3(threads), 0, s, src, d, k, panel, pl.nn_kper,
+              part, nparts);
 }
 
 template <int NT>
 void gemm_typed(bool transposed, const float* E, int64_t d, int64_t k, const uint16_t* panel, const SvdPlan& pl,
-                float* part, const CholJob& job, hipStream_t s, const VirtualE* ve) {
+                float* part, const CholJob& job, hipStream_t s, const VirtualE* ve, double* np) {
   const bool vec = (k & 3) == 0 && k >= 4;
   const bool vec8 = vec && k >= 8;
-  if (ve != nullptr && ve->w_bf16) gemm_launch<NT>(transposed, FormedE<true>{*ve}, d, k, panel, pl, part, job, s);
-  else if (ve != nullptr) gemm_launch<NT>(transposed, FormedE<false>{*ve}, d, k, panel, pl, part, job, s);
-  else if (vec8) gemm_launch<NT>(transposed, StoredE<true>{E}, d, k, panel, pl, part, job, s);
-  else gemm_launch<NT>(transposed, StoredE<false>{E}, d, k, panel, pl, part, job, s);
+  if (ve != nullptr && ve->w_bf16) gemm_launch<NT>(transposed, FormedE<true>{*ve}, d, k, panel, pl, part, job, s, np);
+  else if (ve != nullptr) gemm_launch<NT>(transposed, FormedE<false>{*ve}, d, k, panel, pl, part, job, s, np);
+  else if (vec8) gemm_launch<NT>(transposed, StoredE<true>{E}, d, k, panel, pl, part, job, s, np);
+  else gemm_launch<NT>(transposed, StoredE<false>{E}, d, k, panel, pl, part, job, s, np);
 }
 
 }  // namespace
@@ -515,15 +574,16 @@ GemmShape gemm_shape(bool transposed, int nt) {
 }
 
 void launch_gemm(bool transposed, const float* E, int64_t d, int64_t k, const uint16_t* panel, const SvdPlan& pl,
-                 float* part, const CholJob& job, hipStream_t s, const VirtualE* ve) {
+                 float* part, const CholJob& job, hipStream_t s, const VirtualE* ve, double* nparts) {
   const CholJob none{nullptr, 0, 0, nullptr};
   const CholJob& j = (transposed && pl.nt <= 2) ? job : none;
+  double* np = transposed ? nullptr : nparts;
   switch (pl.nt) {
-    case 1: gemm_typed<1>(transposed, E, d, k, panel, pl, part, j, s, ve); break;
-    case 2: gemm_typed<2>(transposed, E, d, k, panel, pl, part, j, s, ve); break;
-    case 3: gemm_typed<3>(transposed, E, d, k, panel, pl, part, j, s, ve); break;
-    case 4: gemm_typed<4>(transposed, E, d, k, panel, pl, part, j, s, ve); break;
-    default: gemm_typed<5>(transposed, E, d, k, panel, pl, part, j, s, ve); break;
+    case 1: gemm_typed<1>(transposed, E, d, k, panel, pl, part, j, s, ve, np); break;
+    case 2: gemm_typed<2>(transposed, E, d, k, panel, pl, part, j, s, ve, np); break;
+    case 3: gemm_typed<3>(transposed, E, d, k, panel, pl, part, j, s, ve, np); break;
+    case 4: gemm_typed<4>(transposed, E, d, k, panel, pl, part, j, s, ve, np); break;
+    default: gemm_typed<5>(transposed, E, d, k, panel, pl, part, j, s, ve, np); break;
   }
 }
 

@@ -71,8 +71,9 @@ constexpr float kDangerWindow16 = 1.52587890625e-05f;  // 2^-16
 hipError_t launch_nf4_quantize(const void* W, loftq_dtype_t wdt, int64_t rows, int64_t cols,
                                const float* B, const float* A, int r, uint8_t* packed, float* absmax,
                                hipStream_t s, int bits = 4);
+// a_out (optional): each block's dequantization scale a' = fl32(q scale) as well
 hipError_t launch_double_quant(const float* absmax, int64_t nblocks, int dqbs, int8_t* q, float* scale,
-                               hipStream_t s);
+                               hipStream_t s, float* a_out = nullptr);
 // QLoRA forward Y = X bf16(deq(Q))^T + alpha (X bf16(A)^T) bf16(B)^T (forward_kernels.hip);
 // Tws: up to 8 K-split partials of X A^T, n_tok x r fp32 each (qlora_forward_workspace_bytes);
 // unused without B.

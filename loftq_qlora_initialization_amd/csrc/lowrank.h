@@ -48,6 +48,13 @@ __host__ __device__ __forceinline__ int64_t split_index(int64_t rho, int c, int 
   const int g = static_cast<int>((rho >> 3) & 3), e = static_cast<int>(rho & 7);
   return (((step * nt + (c >> 4)) * 2 + part) * 64 + 16 * g + (c & 15)) * 8 + e;
 }
+// The operand of E^T Y (Y, over the rows of E) uses the same pieces with the rows
+// of each pair of K steps interleaved: row 64 m + 16 g + 8 h + e is element e of
+// lane group g in step 2 m + h (measured faster for the product's reads of E).
+// Row of a K step's lane group g, element e, in either layout:
+__host__ __device__ __forceinline__ int64_t split_row(int64_t s, int g, int e, bool paired) {
+  return paired ? 64 * (s >> 1) + 16 * g + 8 * (s & 1) + e : 32 * s + 8 * g + e;
+}
 
 // Workgroup tile of a thin product: rows (gemm_nn) or columns (gemm_tn) per
 // workgroup, and the granularity of its split of the contracted dimension.
@@ -105,10 +112,13 @@ struct SideLane {
 // kept until the process ends), or null if one cannot be created.
 SideLane* side_lane_for(hipStream_t s);
 
+// norm_parts (randomized path only, optional): the first product E Omega also leaves
+// the partial sums of ||E||^2 there (nn_row_blocks x nn_splits fp64), which obj
+// may then name as its e_parts.
 hipError_t run_lowrank(const float* E, const SvdPlan& pl, int q, const float* omega, const float* omega_frag,
                        uint64_t seed, int t, float* B, float* A, float* sigma, char* ws, const ObjectiveArgs& obj,
                        hipStream_t s, SideLane* side = nullptr, const VirtualE* ve = nullptr,
-                       const uint16_t* omega_split = nullptr);
+                       const uint16_t* omega_split = nullptr, double* norm_parts = nullptr);
 // Sketches of alternations t .. t + count - 1, each rows x 16 nt floats in fragment order, back to back;
 // run_sketch_split writes them in the products' split layout instead (the same bytes per sketch).
 hipError_t run_sketch(uint64_t seed, int t, int count, int64_t k, int l, int nt, int64_t rows, float* out,
@@ -131,9 +141,12 @@ struct CholJob {
   int l;
   float* Xinv;
 };
-// panel: the split copy (split_index) of the skinny operand
+// panel: the split copy (split_index) of the skinny operand.  nparts (E P only,
+// optional): the sums of squares of E's elements, one fp64 per workgroup tile
+// (nn_row_blocks x nn_splits of them).
 void launch_gemm(bool transposed, const float* E, int64_t d, int64_t k, const uint16_t* panel, const SvdPlan& pl,
-                 float* part, const CholJob& job, hipStream_t s, const VirtualE* ve = nullptr);
+                 float* part, const CholJob& job, hipStream_t s, const VirtualE* ve = nullptr,
+                 double* nparts = nullptr);
 
 bool aligned16(const void* p);
 bool shape_ok(int64_t rows, int64_t cols);

@@ -747,10 +747,10 @@ template <int NT>
 __global__ __launch_bounds__(kReduceThreads) void reduce_gram_kernel(const float* __restrict__ part, int S, int64_t m,
                                                           int64_t m_pad, int l, const float* __restrict__ X,
                                                           float* __restrict__ out, uint16_t* __restrict__ out_split,
-                                                          double* __restrict__ gram_parts) {
+                                                          double* __restrict__ gram_parts, int paired) {
   constexpr int LP = 16 * NT, PER = (kGramRows * LP + kReduceThreads - 1) / kReduceThreads, LDR = LP + 1;
   constexpr int NW = kReduceThreads / 64;
-  static_assert(kGramRows % 32 == 0, "whole 32-row steps of the split copy (and 16-row MFMA tiles)");
+  static_assert(kGramRows % 64 == 0, "whole pairs of 32-row steps of the split copy (and 16-row MFMA tiles)");
   // wide panels (NT >= 3) keep fewer loads in flight, so the per-thread state
   // fits the register file of a 512-thread workgroup
   constexpr int QB = NT <= 2 ? 8 : 2;
@@ -837,7 +837,7 @@ __global__ __launch_bounds__(kReduceThreads) void reduce_gram_kernel(const float
       const int gg = L >> 4, n = 16 * tn + (L & 15);
       float x[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) x[e] = R[(32 * st + 8 * gg + e) * LDR + n];
+      for (int e = 0; e < 8; ++e) x[e] = R[split_row(st, gg, e, paired != 0) * LDR + n];
       uint4 hi, lo;
       split8_u4(x, hi, lo);
       const int64_t b = (((rs >> 5) * NT + tn) * 2) * 64 + L;
@@ -1402,20 +1402,20 @@ int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 template <int NT>
 void reduce_typed(const float* part, int S, int64_t m, int64_t m_pad, int l, const float* X, float* out,
-                  uint16_t* out_split, double* gram_parts, hipStream_t s) {
+                  uint16_t* out_split, double* gram_parts, bool paired, hipStream_t s) {
   const int blocks = static_cast<int>(cdiv(m_pad, kGramRows));
   LQ_LAUNCH("reduce_gram", (reduce_gram_kernel<NT>), dim3(blocks), dim3(kReduceThreads), 0, s, part, S, m, m_pad, l, X, out,
-            out_split, gram_parts);
+            out_split, gram_parts, paired ? 1 : 0);
 }
 
 void launch_reduce(int nt, const float* part, int S, int64_t m, int64_t m_pad, int l, const float* X, float* out,
-                   uint16_t* out_split, double* gram_parts, hipStream_t s) {
+                   uint16_t* out_split, double* gram_parts, bool paired, hipStream_t s) {
   switch (nt) {
-    case 1: reduce_typed<1>(part, S, m, m_pad, l, X, out, out_split, gram_parts, s); break;
-    case 2: reduce_typed<2>(part, S, m, m_pad, l, X, out, out_split, gram_parts, s); break;
-    case 3: reduce_typed<3>(part, S, m, m_pad, l, X, out, out_split, gram_parts, s); break;
-    case 4: reduce_typed<4>(part, S, m, m_pad, l, X, out, out_split, gram_parts, s); break;
-    default: reduce_typed<5>(part, S, m, m_pad, l, X, out, out_split, gram_parts, s); break;
+    case 1: reduce_typed<1>(part, S, m, m_pad, l, X, out, out_split, gram_parts, paired, s); break;
+    case 2: reduce_typed<2>(part, S, m, m_pad, l, X, out, out_split, gram_parts, paired, s); break;
+    case 3: reduce_typed<3>(part, S, m, m_pad, l, X, out, out_split, gram_parts, paired, s); break;
+    case 4: reduce_typed<4>(part, S, m, m_pad, l, X, out, out_split, gram_parts, paired, s); break;
+    default: reduce_typed<5>(part, S, m, m_pad, l, X, out, out_split, gram_parts, paired, s); break;
   }
 }
 
@@ -1524,7 +1524,7 @@ SvdPlan make_svd_plan(int64_t d, int64_t k, int r, int oversample, bool exact) {
   }
   p.k_pad = p.nn_splits * p.nn_kper;
   p.d_pad = p.tn_splits * p.tn_rper;
-  // the products step K by 32, so k_pad and d_pad are multiples of 32
+  // the products step K by 32 (E^T Y by pairs of steps), so k_pad and d_pad are multiples of 64
   p.gram_parts_d = static_cast<int>(cdiv(d, kGramRows));
   p.gram_parts_k = static_cast<int>(cdiv(k, kGramRows));
   const int64_t gp = p.gram_parts_d > p.gram_parts_k ? p.gram_parts_d : p.gram_parts_k;
@@ -1584,7 +1584,8 @@ hipError_t run_objective(const ObjectiveArgs& obj, hipStream_t s) {
 
 hipError_t run_lowrank(const float* E, const SvdPlan& pl, int q, const float* omega, const float* omega_frag,
                        uint64_t seed, int t, float* B, float* A, float* sigma, char* ws, const ObjectiveArgs& obj,
-                       hipStream_t s, SideLane* side, const VirtualE* ve, const uint16_t* omega_split) {
+                       hipStream_t s, SideLane* side, const VirtualE* ve, const uint16_t* omega_split,
+                       double* norm_parts) {
   const int64_t d = pl.d, k = pl.k;
   const int r = pl.r, l = pl.l;
   if (pl.exact && pl.bj) {
@@ -1666,9 +1667,9 @@ hipError_t run_lowrank(const float* E, const SvdPlan& pl, int q, const float* om
   const bool ride = pl.ride;
   bool pending = false, joining = false;
   hipError_t serr = hipSuccess;
-  auto product = [&](bool transposed, const uint16_t* panel_s, int mode) {
+  auto product = [&](bool transposed, const uint16_t* panel_s, int mode, double* nparts = nullptr) {
     const CholJob job{pending ? gparts : nullptr, pl.gram_parts_d, l, Xinv};
-    launch_gemm(transposed, E, d, k, panel_s, pl, part, job, s, ve);
+    launch_gemm(transposed, E, d, k, panel_s, pl, part, job, s, ve, nparts);
     if (transposed) pending = false;
     if (transposed && joining) {   // X = R^-1 from the side lane
       if (serr == hipSuccess) serr = hipStreamWaitEvent(s, side->join, 0);
@@ -1676,9 +1677,9 @@ hipError_t run_lowrank(const float* E, const SvdPlan& pl, int q, const float* om
     }
     if (transposed)
       launch_reduce(pl.nt, part, pl.tn_splits, k, pl.k_pad, l, Xinv, Z, mode == 2 ? nullptr : Z_s,
-                    mode ? gparts : nullptr, s);
+                    mode ? gparts : nullptr, false, s);
     else
-      launch_reduce(pl.nt, part, pl.nn_splits, d, pl.d_pad, l, nullptr, Y, Y_s, mode ? gparts : nullptr, s);
+      launch_reduce(pl.nt, part, pl.nn_splits, d, pl.d_pad, l, nullptr, Y, Y_s, mode ? gparts : nullptr, true, s);
     if (mode == 0) return;
     if (mode == 1 && ride) {
       pending = true;
@@ -1713,7 +1714,7 @@ hipError_t run_lowrank(const float* E, const SvdPlan& pl, int q, const float* om
   // Y = E Omega; X = R^-1 of its Gram.  Each power iteration multiplies by E^T
   // and E and re-orthonormalises Y only: span(E Z) does not depend on Z's basis,
   // so orthonormalising Z as well would not change the subspace.
-  product(false, Om_s, 1);
+  product(false, Om_s, 1, norm_parts);
   for (int it = 0; it < q; ++it) {
     product(true, Y_s, 0);
     product(false, Z_s, 1);

@@ -407,8 +407,11 @@ __device__ __forceinline__ int dq_code(float a, float sc) {
 }
 
 // Double quant: one workgroup of 256 per group of dq_blocksize (= 256) absmax.
+// a_out (optional): each block's dequantization scale a' = fl32(q scale), as the
+// dequant forms it.
 __global__ __launch_bounds__(256) void double_quant_kernel(const float* __restrict__ absmax, int64_t nb, int dqbs,
-                                                           int8_t* __restrict__ q, float* __restrict__ scale) {
+                                                           int8_t* __restrict__ q, float* __restrict__ scale,
+                                                           float* __restrict__ a_out) {
   __shared__ float red[4];
   const int64_t base = static_cast<int64_t>(blockIdx.x) * dqbs;
   const int tid = threadIdx.x;
@@ -421,7 +424,11 @@ __global__ __launch_bounds__(256) void double_quant_kernel(const float* __restri
   m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
   const float sc = dq_group_scale(m);
   if (tid == 0) scale[blockIdx.x] = sc;
-  if (ok) q[base + tid] = static_cast<int8_t>(dq_code(a, sc));
+  if (ok) {
+    const int c = dq_code(a, sc);
+    q[base + tid] = static_cast<int8_t>(c);
+    if (a_out != nullptr) a_out[base + tid] = static_cast<float>(c) * sc;
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -800,11 +807,11 @@ hipError_t launch_nf4_merge(const uint8_t* packed, const float* absmax, const in
 }
 
 hipError_t launch_double_quant(const float* absmax, int64_t nblocks, int dqbs, int8_t* q, float* scale,
-                               hipStream_t s) {
+                               hipStream_t s, float* a_out) {
   if (nblocks == 0) return hipSuccess;
   const int64_t groups = (nblocks + dqbs - 1) / dqbs;
   LQ_LAUNCH("double_quant", double_quant_kernel, dim3(static_cast<unsigned>(groups)), dim3(256), 0, s, absmax, nblocks,
-                     dqbs, q, scale);
+                     dqbs, q, scale, a_out);
   return hipGetLastError();
 }
 
