@@ -188,6 +188,14 @@ struct Nn3Cfg {
   static constexpr int PU = NT * 128;          // 16-byte pieces of one K step of the split panel
   static constexpr int PPT = (PU + 255) / 256; // of them per thread
 };
+// gemm_nnd_kernel: the panel read by every wave itself, two 16-row tiles per wave
+template <int NT>
+struct NndCfg {
+  static constexpr int RT = 2;
+  static constexpr int D = 4;
+  static constexpr int WR = 4;
+  static constexpr int PU = NT * 128;
+};
 template <int NT>
 struct Tn3Cfg {
   static constexpr int D = 2;
@@ -375,6 +383,132 @@ __global__ __launch_bounds__(64 * Nn3Cfg<NT>::WR) void gemm_nn3_kernel(
   }
 }
 
+// gemm_nn, panel read per wave: every wave loads its own B operands (16 bytes
+// per lane and piece; the four waves of a workgroup hit the same lines) into a
+// register ring beside E's, so the K loop runs without LDS staging or barriers.
+// It reads the panel four times from L2 where gemm_nn3_kernel reads it once, and
+// wins while the panel stays small (nn_direct).
+template <int NT, typename Src, bool NORMS>
+__global__ __launch_bounds__(64 * NndCfg<NT>::WR) void gemm_nnd_kernel(
+    Src src, int64_t d, int64_t k, const uint16_t* __restrict__ Xs, int64_t kper,
+    float* __restrict__ part, double* __restrict__ nparts) {
+  using C = NndCfg<NT>;
+  constexpr int LP = 16 * NT, RT = C::RT, D = C::D, WR = C::WR, PU = C::PU;
+  __shared__ lvpair2 lvl2[Src::kVirtual ? 256 : 1];
+  if constexpr (Src::kVirtual) {
+    fill_level_pairs(src, lvl2);
+    __syncthreads();
+  }
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int g = lane >> 4, li = lane & 15;
+  int tbx, tby;
+  xcd_tile<false>(tbx, tby);
+  const int64_t row0 = (static_cast<int64_t>(tbx) * WR + w) * 16 * RT;
+  const int64_t kb = static_cast<int64_t>(tby) * kper;
+  const int nsteps = static_cast<int>(kper / 32);   // a multiple of D
+  int64_t erow[RT];
+  bool rok[RT];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    const int64_t r = row0 + rt * 16 + li;
+    erow[rt] = r < d ? r : d - 1;
+    rok[rt] = r < d;
+  }
+  double sq = 0.0;
+  const uint4* xg = reinterpret_cast<const uint4*>(Xs) + (kb / 32) * PU + lane;
+  floatx4 acc[RT][NT];
+#pragma unroll
+  for (int a = 0; a < RT; ++a)
+#pragma unroll
+    for (int b = 0; b < NT; ++b) acc[a][b] = floatx4{0.f, 0.f, 0.f, 0.f};
+  typename Src::Raw8 eb[D][RT];
+  uint4 pb[D][NT][2];
+  auto load = [&](int u, int j) {
+    j = j < nsteps ? j : nsteps - 1;
+    const int64_t c = kb + 32 * j + 8 * g;
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) eb[u][rt] = src.fetch8(erow[rt], c, k);
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) pb[u][nt][h] = xg[static_cast<int64_t>(j) * PU + (2 * nt + h) * 64];
+  };
+  auto compute = [&](int u, int j) {
+    bf16x8 ah[RT], al[RT], bh[NT], bl[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      bh[nt] = __builtin_bit_cast(bf16x8, pb[u][nt][0]);
+      bl[nt] = __builtin_bit_cast(bf16x8, pb[u][nt][1]);
+    }
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+      float x[8];
+      src.decode8(eb[u][rt], x, lvl2);
+      if constexpr (NORMS) {
+        const int64_t nv = rok[rt] ? k - (kb + 32 * j + 8 * g) : 0;
+        float s8 = 0.f;
+        if (nv >= 8) {
+#pragma unroll
+          for (int i = 0; i < 8; ++i) s8 = fmaf(x[i], x[i], s8);
+        } else {
+#pragma unroll
+          for (int i = 0; i < 8; ++i)
+            if (i < nv) s8 = fmaf(x[i], x[i], s8);
+        }
+        sq += static_cast<double>(s8);
+      }
+      split8(x, ah[rt], al[rt]);
+    }
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) acc[rt][nt] = mfma_bf16(ah[rt], bh[nt], acc[rt][nt]);
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) acc[rt][nt] = mfma_bf16(ah[rt], bl[nt], acc[rt][nt]);
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) acc[rt][nt] = mfma_bf16(al[rt], bh[nt], acc[rt][nt]);
+  };
+#pragma unroll
+  for (int u = 0; u < D; ++u) load(u, u);
+  const int rounds = nsteps / D;
+  for (int rd = 0; rd + 1 < rounds; ++rd) {
+#pragma unroll
+    for (int u = 0; u < D; ++u) {
+      compute(u, rd * D + u);
+      load(u, (rd + 1) * D + u);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < D; ++u) compute(u, (rounds - 1) * D + u);
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int64_t row = row0 + rt * 16 + 4 * g + v;
+        if (row < d) part[(static_cast<int64_t>(tby) * d + row) * LP + nt * 16 + li] = acc[rt][nt][v];
+      }
+  if constexpr (NORMS) {
+    __shared__ double wsq[WR];
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) sq += __shfl_xor(sq, off);
+    if (lane == 0) wsq[w] = sq;
+    __syncthreads();
+    if (tid == 0) {
+      double t = 0.0;
+#pragma unroll
+      for (int q = 0; q < WR; ++q) t += wsq[q];
+      nparts[static_cast<int64_t>(tby) * gridDim.x + tbx] = t;
+    }
+  }
+}
+
 // gemm_tn.  Wave (wc, wr) owns one 64-column group (its four interleaved 16-column
 // MFMA tiles jm hold columns c0 + 4 m + jm) and its share of the workgroup's rows;
 // waves sharing columns are summed through LDS at the end.  Row steps of 32: lane (li, g) loads rows
@@ -512,10 +646,14 @@ __global__ __launch_bounds__(64 * Tn3Cfg<NT>::WC * Tn3Cfg<NT>::WR) void gemm_tn3
 }
 
 template <int NT>
-GemmShape shape_typed(bool transposed) {
+GemmShape shape_typed(bool transposed, int64_t k) {
   if (transposed) {
     using C = Tn3Cfg<NT>;
     return GemmShape{64 * C::WC, 32 * C::D * C::WR};
+  }
+  if (nn_direct(NT, k)) {
+    using C = NndCfg<NT>;
+    return GemmShape{16 * C::RT * C::WR, 32 * C::D};
   }
   using C = Nn3Cfg<NT>;
   return GemmShape{16 * C::RT * C::WR, 32 * C::D};
@@ -542,7 +680,14 @@ void gemm_launch(bool transposed, const Src& src, int64_t d, int64_t k, const ui
   }
   constexpr int threads = 64 * Nn3Cfg<NT>::WR;
   const dim3 grid(pl.nn_row_blocks, pl.nn_splits);
-  if (nparts != nullptr)
+  const bool direct = nn_direct(NT, k);
+  if (direct && nparts != nullptr)
+    LQ_LAUNCH("gemm_nn", (gemm_nnd_kernel<NT, Src, true>), grid, dim3(threads), 0, s, src, d, k, panel, pl.nn_kper, part,
+              nparts);
+  else if (direct)
+    LQ_LAUNCH("gemm_nn", (gemm_nnd_kernel<NT, Src, false>), grid, dim3(threads), 0, s, src, d, k, panel, pl.nn_kper,
+              part, nparts);
+  else if (nparts != nullptr)
     LQ_LAUNCH("gemm_nn", (gemm_nn3_kernel<NT, Src, true>), grid, dim3(threads), 0, s, src, d, k, panel, pl.nn_kper, part,
               nparts);
   else
@@ -563,13 +708,13 @@ void gemm_typed(bool transposed, const float* E, int64_t d, int64_t k, const uin
 
 }  // namespace
 
-GemmShape gemm_shape(bool transposed, int nt) {
+GemmShape gemm_shape(bool transposed, int nt, int64_t k) {
   switch (nt) {
-    case 1: return shape_typed<1>(transposed);
-    case 2: return shape_typed<2>(transposed);
-    case 3: return shape_typed<3>(transposed);
-    case 4: return shape_typed<4>(transposed);
-    default: return shape_typed<5>(transposed);
+    case 1: return shape_typed<1>(transposed, k);
+    case 2: return shape_typed<2>(transposed, k);
+    case 3: return shape_typed<3>(transposed, k);
+    case 4: return shape_typed<4>(transposed, k);
+    default: return shape_typed<5>(transposed, k);
   }
 }
 

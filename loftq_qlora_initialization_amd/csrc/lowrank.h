@@ -129,7 +129,13 @@ hipError_t run_sketch_split(uint64_t seed, int t, int count, int64_t k, int l, i
 hipError_t run_warm_columns(const float* A, const float* sigma, int64_t k, int r, int nt, float* out, hipStream_t s);
 hipError_t run_fill(float* p, int64_t n, float v, hipStream_t s);
 hipError_t run_objective(const ObjectiveArgs& obj, hipStream_t s);
-GemmShape gemm_shape(bool transposed, int nt);
+// k: columns of E (the product E P picks its kernel by the size of P, nn_direct)
+GemmShape gemm_shape(bool transposed, int nt, int64_t k);
+// E P with every wave reading the panel itself (no LDS staging): for the narrow
+// panels (l <= 32) while the split panel (k rows of 64 nt bytes) stays within
+// 1 MiB; measured on MI355X, the staged kernel wins beyond (4096 x 11008 at
+// l = 24, every l = 80 panel).
+constexpr bool nn_direct(int nt, int64_t k) { return nt <= 2 && int64_t(64) * nt * k <= (int64_t(1) << 20); }
 
 // A Cholesky that rides along with a thin product E^T Y (l <= 32 only): one
 // extra workgroup sums the P fp64 Gram partials of Y (parts) and writes

@@ -12,14 +12,17 @@
 // Tiny matrices use an exact one-sided Jacobi SVD of E itself.
 //
 // Kernels (besides the thin products in gemm_kernels.hip):
-//   sketch        counter-based +-1 test matrix (SplitMix64)
-//   reduce_gram   fixed-order sum of the split-K partials (+ fp64 Gram partials)
+//   sketch        counter-based +-1 test matrix (SplitMix64), in fragment order
+//                 or straight in the products' split layout
+//   reduce_gram   fixed-order sum of the split-K partials, the X = R^-1 product,
+//                 fp64 Gram partials and the next product's split operand
 //   gram_sum      fixed-order sum of the Gram partials
 //   chol_inv      Cholesky of the Gram and X = R^-1 (orthonormalisation); for
 //                 l <= 32 it usually rides along with the next E^T Y product
 //   core_svd      the l x l core solve: Cholesky, one-sided Jacobi, S_B, S_A
 //   panel_small   P S for a row panel P and a small S: B = Q S_B, A = (C S_A)^T
-//   exact_jacobi  single-workgroup one-sided Jacobi SVD for tiny matrices
+//   exact SVD     block one-sided Jacobi over co-resident workgroups (bj_*), or
+//                 one workgroup (exact_jacobi) for vectors too long for its LDS
 // Every reduction runs in a fixed order, so results are deterministic.
 #include <map>
 #include <mutex>
@@ -1503,7 +1506,7 @@ SvdPlan make_svd_plan(int64_t d, int64_t k, int r, int oversample, bool exact) {
     per = round_up(cdiv(len, best_s), unit);
     return static_cast<int>(cdiv(len, per));
   };
-  const GemmShape nn = gemm_shape(false, p.nt), tn = gemm_shape(true, p.nt);
+  const GemmShape nn = gemm_shape(false, p.nt, k), tn = gemm_shape(true, p.nt, k);
   p.nn_row_blocks = static_cast<int>(cdiv(d, nn.tile));
   p.nn_splits = choose(p.nn_row_blocks, k, nn.unit, 0, p.nn_kper);
   p.tn_col_blocks = static_cast<int>(cdiv(k, tn.tile));
