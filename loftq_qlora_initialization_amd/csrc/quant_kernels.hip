@@ -17,6 +17,7 @@
 
 #include "internal.h"
 #include "reduce.h"
+#include "split_bf16.h"
 
 namespace loftq {
 namespace {
@@ -283,18 +284,21 @@ struct Nf4Source {      // deq(Q) of existing codes: R = deq(Q) - bscale B A
 // 64-column block column and walks a run of 16-row tiles of it; waves share
 // nothing, so there is no LDS tile and no barrier after the table fill.
 //
-// B A of a tile comes from fp32 MFMA (v_mfma_f32_16x16x4_f32: lane L supplies
-// A_op[L%16][L/16] and B_op[L/16][L%16] and receives D[4(L/16)+v][L%16]) with
-// M = 16 columns, N = 16 rows and K = 4 rank indices p = KK k + kk (K-step kk,
-// slot k).  MFMA tile t maps its M index m to block column
-// 16 (m >> 2) + 4 t + (m & 3), so lane (li, g) ends up holding row li, columns
-// 16 g .. 16 g + 15 of the block: exactly the 16-element group it loaded from W,
-// with the block's four groups in lanes li, li + 16, li + 32, li + 48.  A's
-// operands (4 tiles x KK values per lane) stay in registers for the whole run;
-// the next tile's W and B operands are loaded before the current tile is
-// computed.
+// B A of a tile comes from the bf16 matrix cores (v_mfma_f32_16x16x32_bf16:
+// lane L supplies A_op[L%16][8(L/16)+e] and B_op[8(L/16)+e][L%16], e = 0..7, and
+// receives D[4(L/16)+v][L%16]) with M = 16 columns, N = 16 rows and K = 32 rank
+// indices p = 32 s + 8 (L/16) + e (K step s; zero past r); for r <= 16 the
+// 16x16x16 form, K = 16 rank indices p = 4 (L/16) + e, e = 0..3.  Both operands are
+// split into bf16 pieces, hi = bf16(x) and lo = bf16(x - hi), and B A is
+// accumulated in fp32 as A_hi B_hi + A_hi B_lo + A_lo B_hi (the dropped lo lo
+// term is below 2^-16 of each product).  MFMA tile t maps its M index m to block
+// column 16 (m >> 2) + 4 t + (m & 3), so lane (li, g) ends up holding row li,
+// columns 16 g .. 16 g + 15 of the block: exactly the 16-element group it loaded
+// from W, with the block's four groups in lanes li, li + 16, li + 32, li + 48.
+// A's split operands (4 tiles per K step) stay in registers for the whole run;
+// the next tile's W and B values are loaded before the current tile is
+// computed, and B is split when its tile is.
 constexpr int kFusedThreads = 256, kFusedMaxR = 64;
-constexpr int64_t kFusedWaves = 3072;
 
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 
@@ -304,7 +308,9 @@ __global__ __launch_bounds__(kFusedThreads) __attribute__((amdgpu_waves_per_eu(R
                                                                        const float* __restrict__ A, int r, float bscale,
                                                                        int tpw, uint8_t* __restrict__ packed,
                                                                        float* __restrict__ absmax, Nf4Tables tab) {
-  constexpr int KK = R16 / 4;
+  constexpr bool K16 = R16 == 16;            // one K step of 16 rank indices (16x16x16 MFMA)
+  constexpr int KS = K16 ? 1 : (R16 + 31) / 32;   // else K steps of 32
+  constexpr int KW = K16 ? 4 : 8;            // rank indices per lane and K step
   __shared__ EncodeLds s;
   __shared__ lvpair lvl2[Src::kCodes ? 256 : 1];
   fill_lds(s, tab);
@@ -319,46 +325,74 @@ __global__ __launch_bounds__(kFusedThreads) __attribute__((amdgpu_waves_per_eu(R
   if (t0 >= ntiles) return;
   const int64_t t1 = (t0 + tpw < ntiles) ? t0 + tpw : ntiles;
   const int64_t col0 = bc << 6;
-  float aop[KK][4];
+  // split operands as packed bf16 pairs: KW / 2 words each
+  uint32_t aoh[KS][4][KW / 2], aol[KS][4][KW / 2];
   {
     const int64_t cbase = col0 + 16 * (li >> 2) + (li & 3);
 #pragma unroll
-    for (int kk = 0; kk < KK; ++kk) {
-      const int p = KK * g + kk;
+    for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-      for (int t = 0; t < 4; ++t) aop[kk][t] = (kFullR || p < r) ? A[static_cast<int64_t>(p) * cols + cbase + 4 * t] : 0.f;
-    }
+      for (int t = 0; t < 4; ++t) {
+        float x[KW];
+#pragma unroll
+        for (int e = 0; e < KW; ++e) {
+          const int p = 32 * ks + KW * g + e;
+          x[e] = p < r ? A[static_cast<int64_t>(p) * cols + cbase + 4 * t] : 0.f;
+        }
+        split_pairs<KW>(x, aoh[ks][t], aol[ks][t]);
+      }
   }
-  auto load_tile = [&](int64_t tile, uint4 (&raw)[4], float (&bop)[KK]) {
+  // B[row][32 ks + KW g .. + KW - 1] of the lane's row (bscale applied), zero past r
+  auto load_tile = [&](int64_t tile, uint4 (&raw)[4], float (&bop)[KS][KW]) {
     const int64_t row = (tile << 4) + li;
     const int64_t rc = row < rows ? row : rows - 1;
     src.load(rc * cols + col0 + 16 * g, raw);
-    if (kFullR) {
 #pragma unroll
-      for (int q = 0; q < KK / 4; ++q) {
-        const float4 b4 = *reinterpret_cast<const float4*>(B + rc * R16 + KK * g + 4 * q);
-        bop[4 * q] = b4.x; bop[4 * q + 1] = b4.y; bop[4 * q + 2] = b4.z; bop[4 * q + 3] = b4.w;
+    for (int ks = 0; ks < KS; ++ks) {
+      const int p0 = 32 * ks + KW * g;
+      if (kFullR) {   // r == R16, a multiple of 16: the lane's values are all in range or all past r
+#pragma unroll
+        for (int q = 0; q < KW / 4; ++q) {
+          float4 b = make_float4(0.f, 0.f, 0.f, 0.f);
+          if (p0 < R16) b = *reinterpret_cast<const float4*>(B + rc * R16 + p0 + 4 * q);
+          bop[ks][4 * q] = b.x; bop[ks][4 * q + 1] = b.y; bop[ks][4 * q + 2] = b.z; bop[ks][4 * q + 3] = b.w;
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < KW; ++e) bop[ks][e] = (p0 + e < r) ? B[rc * r + p0 + e] : 0.f;
       }
-    } else {
+      if (Src::kScaleB) {
 #pragma unroll
-      for (int kk = 0; kk < KK; ++kk) {
-        const int p = KK * g + kk;
-        bop[kk] = (p < r) ? B[rc * r + p] : 0.f;
+        for (int e = 0; e < KW; ++e) bop[ks][e] *= bscale;
       }
-    }
-    if (Src::kScaleB) {
-#pragma unroll
-      for (int kk = 0; kk < KK; ++kk) bop[kk] *= bscale;
     }
   };
-  auto do_tile = [&](int64_t tile, const uint4 (&raw)[4], const float (&bop)[KK]) {
+  auto mfma = [](const uint32_t (&a)[KW / 2], const uint32_t (&b)[KW / 2], floatx4 c) -> floatx4 {
+    if constexpr (K16) {
+      typedef short short4v __attribute__((ext_vector_type(4)));
+      return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(short4v, uint2{a[0], a[1]}),
+                                                      __builtin_bit_cast(short4v, uint2{b[0], b[1]}), c, 0, 0, 0);
+    } else {
+      return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, uint4{a[0], a[1], a[2], a[3]}),
+                                                     __builtin_bit_cast(bf16x8, uint4{b[0], b[1], b[2], b[3]}), c, 0,
+                                                     0, 0);
+    }
+  };
+  auto do_tile = [&](int64_t tile, const uint4 (&raw)[4], const float (&bop)[KS][KW]) {
     floatx4 acc[4];
 #pragma unroll
     for (int t = 0; t < 4; ++t) acc[t] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int kk = 0; kk < KK; ++kk)
+    for (int ks = 0; ks < KS; ++ks) {
+      uint32_t bh[KW / 2], bl[KW / 2];
+      split_pairs<KW>(bop[ks], bh, bl);
 #pragma unroll
-      for (int t = 0; t < 4; ++t) acc[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(aop[kk][t], bop[kk], acc[t], 0, 0, 0);
+      for (int t = 0; t < 4; ++t) acc[t] = mfma(aoh[ks][t], bh, acc[t]);
+#pragma unroll
+      for (int t = 0; t < 4; ++t) acc[t] = mfma(aoh[ks][t], bl, acc[t]);
+#pragma unroll
+      for (int t = 0; t < 4; ++t) acc[t] = mfma(aol[ks][t], bh, acc[t]);
+    }
     float v[16];
     src.to_f32(raw, v, lvl2);
     float m = 0.f;
@@ -380,7 +414,7 @@ __global__ __launch_bounds__(kFusedThreads) __attribute__((amdgpu_waves_per_eu(R
     }
   };
   uint4 raw0[4], raw1[4];
-  float bop0[KK], bop1[KK];
+  float bop0[KS][KW], bop1[KS][KW];
   load_tile(t0, raw0, bop0);
   int64_t tile = t0;
   for (; tile + 1 < t1; tile += 2) {
@@ -665,16 +699,28 @@ int grid_for_groups(int64_t ngroups, int per_thread) {
   return static_cast<int>(blocks);
 }
 
-// Grid of the fused kernel: about kFusedWaves waves in all, each a run of tpw
-// 16-row tiles of one 64-column block column.
-dim3 fused_grid(int64_t rows, int64_t cols, int& tpw_out) {
+// Grid of the fused kernel: every block column is cut into c runs of tpw 16-row
+// tiles, one wave each.  The chip holds 1024 x occ waves at once (occ: waves per
+// SIMD the kernel's registers allow for this r16), so the kernel takes
+// ceil(nbc c / (1024 occ)) rounds of a run each; a run costs about tpw + 2 tiles
+// (its set-up: A's operands, the tables), and c minimises the total, the fewest
+// waves on a tie.
+dim3 fused_grid(int64_t rows, int64_t cols, int r16, int& tpw_out) {
   const int64_t nbc = cols / 64, ntiles = (rows + 15) / 16;
-  int64_t tpw = (nbc * ntiles + kFusedWaves - 1) / kFusedWaves;
-  if (tpw < 1) tpw = 1;
-  const int64_t chunks = (ntiles + tpw - 1) / tpw;
-  const int64_t waves = nbc * chunks;
+  const int64_t slots = 1024 * static_cast<int64_t>(r16 <= 16 ? 4 : (r16 <= 32 ? 3 : 2));
+  int64_t best_c = 1, best = -1;
+  for (int64_t c = 1; c <= ntiles && c <= 4096; ++c) {
+    const int64_t tpw = (ntiles + c - 1) / c;
+    if ((ntiles + tpw - 1) / tpw != c) continue;   // same runs as a smaller c
+    const int64_t cost = ((nbc * c + slots - 1) / slots) * (tpw + 2);
+    if (best < 0 || cost < best) {
+      best = cost;
+      best_c = c;
+    }
+  }
+  const int64_t tpw = (ntiles + best_c - 1) / best_c;
   tpw_out = static_cast<int>(tpw);
-  return dim3(static_cast<unsigned>((waves + 3) / 4));
+  return dim3(static_cast<unsigned>((nbc * best_c + 3) / 4));
 }
 
 template <typename T>
@@ -698,7 +744,7 @@ hipError_t quantize_typed(const T* W, int64_t rows, int64_t cols, const float* B
   } else if (cols % 64 == 0 && r <= kFusedMaxR) {
     const int r16 = (r + 15) / 16 * 16;
     int tpw = 0;
-    const dim3 grid = fused_grid(rows, cols, tpw);
+    const dim3 grid = fused_grid(rows, cols, r16, tpw);
     const bool full = (r == r16);
     const WeightSource<T> src{W};
 #define LQ_FUSED(R16)                                                                                              \
@@ -773,7 +819,7 @@ hipError_t launch_nf4_merge(const uint8_t* packed, const float* absmax, const in
   if (cols % 64 != 0 || r < 0 || r > kFusedMaxR) return hipErrorInvalidValue;
   const int r16 = r <= 16 ? 16 : (r + 15) / 16 * 16;
   int tpw = 0;
-  const dim3 grid = fused_grid(rows, cols, tpw);
+  const dim3 grid = fused_grid(rows, cols, r16, tpw);
   const bool full = (r == r16);
   const float bscale = -alpha;
 #define LQ_MERGE(SRC, R16)                                                                                         \

@@ -33,6 +33,17 @@ __device__ __forceinline__ void split8(const float4& a, const float4& b, bf16x8&
   const float x[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
   split8(x, hi, lo);
 }
+// N values (N even) as N / 2 packed words of hi and of lo pieces
+template <int N>
+__device__ __forceinline__ void split_pairs(const float (&x)[N], uint32_t (&h)[N / 2], uint32_t (&l)[N / 2]) {
+#pragma unroll
+  for (int p = 0; p < N / 2; ++p) {
+    const uint32_t hp = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{x[2 * p], x[2 * p + 1]}, bf16x2));
+    const float h0 = __uint_as_float(hp << 16), h1 = __uint_as_float(hp & 0xFFFF0000u);
+    h[p] = hp;
+    l[p] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{x[2 * p] - h0, x[2 * p + 1] - h1}, bf16x2));
+  }
+}
 __device__ __forceinline__ void split8_u4(const float (&x)[8], uint4& hi, uint4& lo) {
   bf16x8 h, l;
   split8(x, h, l);
