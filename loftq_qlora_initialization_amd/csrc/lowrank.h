@@ -13,6 +13,10 @@ constexpr int kMaxExact = 512;   // exact SVD: min(rows, cols) limit
 constexpr int kGramRows = 64;    // rows per workgroup (and fp64 Gram partial) of reduce_gram
 constexpr int kReduceThreads = 512;
 constexpr int kPanelRows = 64;   // rows per workgroup (and Gram partial) of the panel x small kernel
+// Orthonormalisation solves on a side stream (SideLane) for E of at least this
+// many elements; below kSideFullGridElems E^T Y then keeps a CU free for them.
+constexpr int64_t kSideMinElems = int64_t(1) << 25;
+constexpr int64_t kSideFullGridElems = int64_t(1) << 27;
 
 // Where the objective of an alternation goes: ||E||^2 and ||W||^2 arrive as
 // per-workgroup partial sums (summed in a fixed order by the consumer);

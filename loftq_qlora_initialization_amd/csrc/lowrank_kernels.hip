@@ -1511,6 +1511,19 @@ SvdPlan make_svd_plan(int64_t d, int64_t k, int r, int oversample, bool exact) {
   p.nn_splits = choose(p.nn_row_blocks, k, nn.unit, 0, p.nn_kper);
   p.tn_col_blocks = static_cast<int>(cdiv(k, tn.tile));
   p.tn_splits = choose(p.tn_col_blocks, d, tn.unit, 0, p.tn_rper);
+  // Mid-size E with a wide panel takes its orthonormalisation solves on the side
+  // lane (run_lowrank); E^T Y then leaves a CU free for them, as for the ride-along
+  // Cholesky below (measured on MI355X: 11008 x 4096 at l = 80, 4.14 -> 4.04 ms
+  // per init; the larger E of 8192 x 28672 keeps its full grid, its E^T Y outlasts
+  // the solves anyway).
+  if (l > 32 && d * k >= kSideMinElems && d * k < kSideFullGridElems) {
+    int64_t rper = 0;
+    const int sc = choose(p.tn_col_blocks, d, tn.unit, kCUs - 1, rper);
+    if (sc > 0) {
+      p.tn_splits = sc;
+      p.tn_rper = rper;
+    }
+  }
   // The Cholesky that rides along with E^T Y (l <= 32) is a serial chain that
   // slows several-fold when a streaming workgroup shares its CU, so it rides
   // only where a split leaves a CU free while still covering at least three
@@ -1663,10 +1676,11 @@ hipError_t run_lowrank(const float* E, const SvdPlan& pl, int q, const float* om
   // For l <= 32 the Cholesky of Y's Gram (mode 1) needs no launch of its own:
   // it rides along with the E^T Y product that always follows, whose split-K
   // reduction is the first consumer of X.
-  // The fork and join between the streams cost tens of microseconds (measured
-  // on MI355X: a loss with the 45M-element E of an 11008 x 4096 layer, a gain
-  // with 235M elements), so the side lane is taken only for large E.
-  if (d * k < (int64_t(1) << 27)) side = nullptr;
+  // The fork and join between the streams cost several microseconds, and the
+  // solves slow down several-fold on a CU shared with the product's waves: the
+  // side lane is taken only for E of at least kSideMinElems elements, whose E^T Y
+  // leaves a CU free (make_svd_plan) or runs long enough to cover the solves.
+  if (d * k < kSideMinElems) side = nullptr;
   const bool ride = pl.ride;
   bool pending = false, joining = false;
   hipError_t serr = hipSuccess;
