@@ -906,16 +906,38 @@ __global__ __launch_bounds__(256) void panel_small_kernel(PanelJob j0, PanelJob 
   }
   for (int idx = threadIdx.x; idx < l * w; idx += blockDim.x) Ss[idx] = S[idx];
   __syncthreads();
-  for (int idx = threadIdx.x; idx < kPanelRows * w; idx += blockDim.x) {
-    int rr, c;
-    if (transpose_out) { rr = idx % kPanelRows; c = idx / kPanelRows; }
-    else { rr = idx / w; c = idx - rr * w; }
-    float acc = 0.f;
-    for (int a = 0; a < l; ++a) acc = fmaf(Ps[rr * ldp + a], Ss[a * w + c], acc);
-    const int64_t row = r0 + rr;
-    if (row < m) {
-      if (transpose_out) out[static_cast<int64_t>(c) * m + row] = acc;
-      else out[row * w + c] = acc;
+  // wave wv: rows 16 wv .. 16 wv + 15 of the panel times S on fp32 MFMA (16x16x4:
+  // lane L supplies A[L%16][L/16] and B[L/16][L%16], receives D[4(L/16)+v][L%16]),
+  // K steps of 4 over a < l (zero beyond), one 16-column tile of S per accumulator
+  static_assert(kPanelRows == 64, "four waves of 16 rows");
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, li = lane & 15, g = lane >> 4;
+  const int nct = (w + 15) >> 4;
+  mfma_f4 acc[kMaxR / 16];
+#pragma unroll
+  for (int ct = 0; ct < kMaxR / 16; ++ct) acc[ct] = mfma_f4{0.f, 0.f, 0.f, 0.f};
+  for (int kk = 0; kk < (l + 3) >> 2; ++kk) {
+    const int a = 4 * kk + g;
+    const float pa = a < l ? Ps[(16 * wv + li) * ldp + a] : 0.f;
+#pragma unroll
+    for (int ct = 0; ct < kMaxR / 16; ++ct) {
+      if (ct < nct) {
+        const int c = 16 * ct + li;
+        const float sb = (a < l && c < w) ? Ss[a * w + c] : 0.f;
+        acc[ct] = __builtin_amdgcn_mfma_f32_16x16x4f32(pa, sb, acc[ct], 0, 0, 0);
+      }
+    }
+  }
+#pragma unroll
+  for (int ct = 0; ct < kMaxR / 16; ++ct) {
+    if (ct >= nct) continue;
+    const int c = 16 * ct + li;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int64_t row = r0 + 16 * wv + 4 * g + v;
+      if (row < m && c < w) {
+        if (transpose_out) out[static_cast<int64_t>(c) * m + row] = acc[ct][v];
+        else out[row * w + c] = acc[ct][v];
+      }
     }
   }
 }
