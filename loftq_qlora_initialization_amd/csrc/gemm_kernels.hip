@@ -180,9 +180,9 @@ __device__ __forceinline__ void xcd_tile(int& bx, int& by) {
   if (X_FAST) { bx = L % gx; by = L / gx; } else { by = L % gy; bx = L / gy; }
 }
 
-template <int NT>
+template <int NT, int RTV = 1>
 struct Nn3Cfg {
-  static constexpr int RT = 1;                 // 16-row MFMA tiles per wave
+  static constexpr int RT = RTV;               // 16-row MFMA tiles per wave (nn_staged_rt)
   static constexpr int D = 4;                  // E register ring depth (K steps of 32)
   static constexpr int WR = 4;                 // waves along rows, sharing the staged panel
   static constexpr int PU = NT * 128;          // 16-byte pieces of one K step of the split panel
@@ -213,11 +213,11 @@ struct Tn3Cfg {
 // exactly once: clamped rows and columns are left out; eight at a time in fp32,
 // those sums in fp64) and writes the sum to nparts[workgroup tile]; in a fixed
 // order, so the partials are deterministic.
-template <int NT, typename Src, bool NORMS>
-__global__ __launch_bounds__(64 * Nn3Cfg<NT>::WR) void gemm_nn3_kernel(
+template <int NT, typename Src, bool NORMS, int RTV>
+__global__ __launch_bounds__(64 * (Nn3Cfg<NT, RTV>::WR)) void gemm_nn3_kernel(
     Src src, int64_t d, int64_t k, const uint16_t* __restrict__ Xs, int64_t kper,
     float* __restrict__ part, double* __restrict__ nparts) {
-  using C = Nn3Cfg<NT>;
+  using C = Nn3Cfg<NT, RTV>;
   constexpr int LP = 16 * NT, RT = C::RT, D = C::D, WR = C::WR, PU = C::PU, PPT = C::PPT;
   static_assert(D % 2 == 0 && WR * 64 == 256, "ring parity and the 256-thread panel staging");
   __shared__ uint4 pan[2][256 * PPT];   // rounded up to whole rounds of 256 pieces (the excess never read)
@@ -646,7 +646,7 @@ __global__ __launch_bounds__(64 * Tn3Cfg<NT>::WC * Tn3Cfg<NT>::WR) void gemm_tn3
 }
 
 template <int NT>
-GemmShape shape_typed(bool transposed, int64_t k) {
+GemmShape shape_typed(bool transposed, int64_t d, int64_t k) {
   if (transposed) {
     using C = Tn3Cfg<NT>;
     return GemmShape{64 * C::WC, 32 * C::D * C::WR};
@@ -655,7 +655,11 @@ GemmShape shape_typed(bool transposed, int64_t k) {
     using C = NndCfg<NT>;
     return GemmShape{16 * C::RT * C::WR, 32 * C::D};
   }
-  using C = Nn3Cfg<NT>;
+  if (nn_staged_rt(NT, d, k) == 2) {
+    using C = Nn3Cfg<NT, 2>;
+    return GemmShape{16 * C::RT * C::WR, 32 * C::D};
+  }
+  using C = Nn3Cfg<NT, 1>;
   return GemmShape{16 * C::RT * C::WR, 32 * C::D};
 }
 
@@ -679,6 +683,8 @@ void gemm_launch(bool transposed, const Src& src, int64_t d, int64_t k, const ui
     return;
   }
   constexpr int threads = 64 * Nn3Cfg<NT>::WR;
+  static_assert(NndCfg<NT>::WR == Nn3Cfg<NT>::WR && Nn3Cfg<NT, 2>::WR == Nn3Cfg<NT>::WR, "one workgroup size");
+  const bool two = nn_staged_rt(NT, d, k) == 2;
   const dim3 grid(pl.nn_row_blocks, pl.nn_splits);
   const bool direct = nn_direct(NT, k);
   if (direct && nparts != nullptr)
@@ -687,11 +693,17 @@ void gemm_launch(bool transposed, const Src& src, int64_t d, int64_t k, const ui
   else if (direct)
     LQ_LAUNCH("gemm_nn", (gemm_nnd_kernel<NT, Src, false>), grid, dim3(threads), 0, s, src, d, k, panel, pl.nn_kper,
               part, nparts);
+  else if (two && nparts != nullptr)
+    LQ_LAUNCH("gemm_nn", (gemm_nn3_kernel<NT, Src, true, 2>), grid, dim3(threads), 0, s, src, d, k, panel, pl.nn_kper,
+              part, nparts);
+  else if (two)
+    LQ_LAUNCH("gemm_nn", (gemm_nn3_kernel<NT, Src, false, 2>), grid, dim3(threads), 0, s, src, d, k, panel, pl.nn_kper,
+              part, nparts);
   else if (nparts != nullptr)
-    LQ_LAUNCH("gemm_nn", (gemm_nn3_kernel<NT, Src, true>), grid, dim3(threads), 0, s, src, d, k, panel, pl.nn_kper, part,
-              nparts);
+    LQ_LAUNCH("gemm_nn", (gemm_nn3_kernel<NT, Src, true, 1>), grid, dim3(threads), 0, s, src, d, k, panel, pl.nn_kper,
+              part, nparts);
   else
-    LQ_LAUNCH("gemm_nn", (gemm_nn3_kernel<NT, Src, false>), grid, dim3(threads), 0, s, src, d, k, panel, pl.nn_kper,
+    LQ_LAUNCH("gemm_nn", (gemm_nn3_kernel<NT, Src, false, 1>), grid, dim3(threads), 0, s, src, d, k, panel, pl.nn_kper,
               part, nparts);
 }
 
@@ -708,13 +720,13 @@ void gemm_typed(bool transposed, const float* E, int64_t d, int64_t k, const uin
 
 }  // namespace
 
-GemmShape gemm_shape(bool transposed, int nt, int64_t k) {
+GemmShape gemm_shape(bool transposed, int nt, int64_t d, int64_t k) {
   switch (nt) {
-    case 1: return shape_typed<1>(transposed, k);
-    case 2: return shape_typed<2>(transposed, k);
-    case 3: return shape_typed<3>(transposed, k);
-    case 4: return shape_typed<4>(transposed, k);
-    default: return shape_typed<5>(transposed, k);
+    case 1: return shape_typed<1>(transposed, d, k);
+    case 2: return shape_typed<2>(transposed, d, k);
+    case 3: return shape_typed<3>(transposed, d, k);
+    case 4: return shape_typed<4>(transposed, d, k);
+    default: return shape_typed<5>(transposed, d, k);
   }
 }
 

@@ -133,13 +133,22 @@ hipError_t run_sketch_split(uint64_t seed, int t, int count, int64_t k, int l, i
 hipError_t run_warm_columns(const float* A, const float* sigma, int64_t k, int r, int nt, float* out, hipStream_t s);
 hipError_t run_fill(float* p, int64_t n, float v, hipStream_t s);
 hipError_t run_objective(const ObjectiveArgs& obj, hipStream_t s);
-// k: columns of E (the product E P picks its kernel by the size of P, nn_direct)
-GemmShape gemm_shape(bool transposed, int nt, int64_t k);
+// d, k: rows and columns of E (E P picks its kernel and tile by nn_direct and nn_staged_rt)
+GemmShape gemm_shape(bool transposed, int nt, int64_t d, int64_t k);
 // E P with every wave reading the panel itself (no LDS staging): for the narrow
 // panels (l <= 32) while the split panel (k rows of 64 nt bytes) stays within
 // 1 MiB; measured on MI355X, the staged kernel wins beyond (4096 x 11008 at
 // l = 24, every l = 80 panel).
 constexpr bool nn_direct(int nt, int64_t k) { return nt <= 2 && int64_t(64) * nt * k <= (int64_t(1) << 20); }
+// 16-row tiles per wave of the staged E P: two for wide panels (l > 32) when the
+// 32-row blocks with the most split-K ranges allowed (k_pad partials within ~8 % of
+// a 4-byte E, whole 128-column steps) still give two workgroups per CU, else one
+// (measured on MI355X: 8192 x 28672 at l = 80, 250 -> 235 us; 11008 x 4096 slower
+// with two).
+constexpr int nn_staged_rt(int nt, int64_t d, int64_t k) {
+  return (nt >= 3 && ((d + 127) / 128) * (((k * 8) / (100 * 16 * nt)) < k / 128 ? (k * 8) / (100 * 16 * nt) : k / 128) >= 512)
+             ? 2 : 1;
+}
 
 // A Cholesky that rides along with a thin product E^T Y (l <= 32 only): one
 // extra workgroup sums the P fp64 Gram partials of Y (parts) and writes

@@ -299,24 +299,26 @@ __device__ __forceinline__ bool jacobi_rotate(float (&xp)[RL], float (&xq)[RL], 
 }
 
 // One-sided Jacobi sweeps on the columns of K (fp32, LDS, column stride
-// ld > 16 RL; rows 16 RL and beyond the matrix are zero), 16 lanes per column
-// pair (lane sub holds rows sub + 16 i, i < RL), in a block order that needs a
-// workgroup barrier only between block rounds.  The columns (n rounded up to
-// nbk blocks of 4, nbk even; columns beyond n are zero) form a round-robin of
-// blocks: in block round rho wave w holds blocks rr_player(w, rho, nbk) and
-// rr_player(nbk - 1 - w, rho, nbk); its 16-lane group g keeps column g of the
-// first block in registers and in sub-round j (j < 4) rotates it against
-// column (g + j) mod 4 of the second, which passes from group to group through
-// LDS within the wave.  Block round 0 first runs the pairs inside each of the
-// wave's two blocks (round-robin of 4, three sub-rounds; its first sub-round
-// meets every column and forms all three dot products, later sub-rounds form
-// gamma only).  A sweep is 3 + 4 (nbk - 1) sub-rounds and meets every pair
-// once.  Row 16 RL of each column carries its squared norm.  All threads call
-// it (at least nbk / 2 waves); returns the sweeps.
-template <int RL>
+// ld > GL RL with GL = 64 / BW lanes per column; rows GL RL and beyond the
+// matrix are zero), a column pair per GL-lane group (lane sub holds rows
+// sub + GL i, i < RL), in a block order that needs a workgroup barrier only
+// between block rounds.  The columns (n rounded up to nbk blocks of BW, nbk
+// even; columns beyond n are zero) form a round-robin of blocks: in block round
+// rho wave w holds blocks rr_player(w, rho, nbk) and rr_player(nbk - 1 - w, rho,
+// nbk); its lane group g keeps column g of the first block in registers and in
+// sub-round j (j < BW) rotates it against column (g + j) mod BW of the second,
+// which passes from group to group through LDS within the wave.  Block round 0
+// first runs the pairs inside each of the wave's two blocks (round-robin of BW,
+// BW - 1 sub-rounds; its first sub-round meets every column and forms all three
+// dot products, later sub-rounds form gamma only).  A sweep is BW - 1 + BW (nbk - 1)
+// sub-rounds and meets every pair once.  Row GL RL of each column carries its
+// squared norm.  All threads call it (at least nbk / 2 waves); returns the sweeps.
+template <int RL, int BW>
 __device__ int jacobi_blocks(float* K, int ld, int n, int max_sweeps) {
-  const int wave = threadIdx.x >> 6, g = (threadIdx.x >> 4) & 3, sub = threadIdx.x & 15;
-  const int nbk0 = (n + 3) / 4, nbk = nbk0 + (nbk0 & 1);
+  static_assert(BW == 4 || BW == 8, "4- or 8-column blocks");
+  constexpr int GL = 64 / BW;   // lanes per column pair
+  const int wave = threadIdx.x >> 6, g = (threadIdx.x / GL) % BW, sub = threadIdx.x % GL;
+  const int nbk0 = (n + BW - 1) / BW, nbk = nbk0 + (nbk0 & 1);
   const bool active = wave < nbk / 2;
   float* Ks = K + sub;
   int sweeps = 0;
@@ -327,21 +329,21 @@ __device__ int jacobi_blocks(float* K, int ld, int n, int max_sweeps) {
         const int ba = rr_player(wave, rnd, nbk), bb = rr_player(nbk - 1 - wave, rnd, nbk);
         float xa[RL], xb[RL];
         if (rnd == 0) {
-          const int blk = g < 2 ? ba : bb, slot = g & 1;
+          const int blk = g < BW / 2 ? ba : bb, slot = g % (BW / 2);
 #pragma unroll
-          for (int ir = 0; ir < 3; ++ir) {
-            const int x = rr_player(slot, ir, 4), y = rr_player(3 - slot, ir, 4);
-            float* cp = Ks + (blk * 4 + min(x, y)) * ld;
-            float* cq = Ks + (blk * 4 + max(x, y)) * ld;
-            float al = cp[16 * RL - sub], be = cq[16 * RL - sub], ga = 0.f;
+          for (int ir = 0; ir < BW - 1; ++ir) {
+            const int x = rr_player(slot, ir, BW), y = rr_player(BW - 1 - slot, ir, BW);
+            float* cp = Ks + (blk * BW + min(x, y)) * ld;
+            float* cq = Ks + (blk * BW + max(x, y)) * ld;
+            float al = cp[GL * RL - sub], be = cq[GL * RL - sub], ga = 0.f;
 #pragma unroll
             for (int i = 0; i < RL; ++i) {
-              xa[i] = cp[16 * i];
-              xb[i] = cq[16 * i];
+              xa[i] = cp[GL * i];
+              xb[i] = cq[GL * i];
             }
 #pragma unroll
             for (int i = 0; i < RL; ++i) ga = fmaf(xa[i], xb[i], ga);
-            ga = group_sumf<16>(ga);
+            ga = group_sumf<GL>(ga);
             if (ir == 0) {
               float a2 = 0.f, b2 = 0.f;
 #pragma unroll
@@ -349,44 +351,44 @@ __device__ int jacobi_blocks(float* K, int ld, int n, int max_sweeps) {
                 a2 = fmaf(xa[i], xa[i], a2);
                 b2 = fmaf(xb[i], xb[i], b2);
               }
-              al = group_sumf<16>(a2);
-              be = group_sumf<16>(b2);
+              al = group_sumf<GL>(a2);
+              be = group_sumf<GL>(b2);
             }
             big |= __builtin_amdgcn_ballot_w64(jacobi_rotate<RL>(xa, xb, al, be, ga));
 #pragma unroll
             for (int i = 0; i < RL; ++i) {
-              cp[16 * i] = xa[i];
-              cq[16 * i] = xb[i];
+              cp[GL * i] = xa[i];
+              cq[GL * i] = xb[i];
             }
-            cp[16 * RL - sub] = al;
-            cq[16 * RL - sub] = be;
+            cp[GL * RL - sub] = al;
+            cq[GL * RL - sub] = be;
             __builtin_amdgcn_wave_barrier();
           }
         }
-        float* ca = Ks + (ba * 4 + g) * ld;
-        float al = ca[16 * RL - sub];
+        float* ca = Ks + (ba * BW + g) * ld;
+        float al = ca[GL * RL - sub];
 #pragma unroll
-        for (int i = 0; i < RL; ++i) xa[i] = ca[16 * i];
+        for (int i = 0; i < RL; ++i) xa[i] = ca[GL * i];
         const bool a_low = ba < bb;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          float* cb = Ks + (bb * 4 + ((g + j) & 3)) * ld;
-          float be = cb[16 * RL - sub], ga = 0.f;
+        for (int j = 0; j < BW; ++j) {
+          float* cb = Ks + (bb * BW + (g + j) % BW) * ld;
+          float be = cb[GL * RL - sub], ga = 0.f;
 #pragma unroll
-          for (int i = 0; i < RL; ++i) xb[i] = cb[16 * i];
+          for (int i = 0; i < RL; ++i) xb[i] = cb[GL * i];
 #pragma unroll
           for (int i = 0; i < RL; ++i) ga = fmaf(xa[i], xb[i], ga);
-          ga = group_sumf<16>(ga);
+          ga = group_sumf<GL>(ga);
           const bool coupled = a_low ? jacobi_rotate<RL>(xa, xb, al, be, ga) : jacobi_rotate<RL>(xb, xa, be, al, ga);
           big |= __builtin_amdgcn_ballot_w64(coupled);
 #pragma unroll
-          for (int i = 0; i < RL; ++i) cb[16 * i] = xb[i];
-          cb[16 * RL - sub] = be;
+          for (int i = 0; i < RL; ++i) cb[GL * i] = xb[i];
+          cb[GL * RL - sub] = be;
           __builtin_amdgcn_wave_barrier();
         }
 #pragma unroll
-        for (int i = 0; i < RL; ++i) ca[16 * i] = xa[i];
-        ca[16 * RL - sub] = al;
+        for (int i = 0; i < RL; ++i) ca[GL * i] = xa[i];
+        ca[GL * RL - sub] = al;
       }
       __syncthreads();
     }
@@ -499,7 +501,7 @@ __global__ __launch_bounds__(256) void core_small_kernel(const double* __restric
     }
   }
   __syncthreads();
-  const int sweeps = jacobi_blocks<2>(K, LD, n, 30);
+  const int sweeps = jacobi_blocks<2, 4>(K, LD, n, 30);
   core_finish(K, LD, l, n, kscale, Xs, r, SB, SA, sigma, stats, obj, sweeps, norm2, order, objsums);
 }
 
@@ -522,7 +524,7 @@ constexpr int kCNB = (kMaxL + kCB - 1) / kCB;    // block rows at most
 // measured on MI355X at l = 80: more lanes per pair and more waves win (4-lane
 // pairs on 3 waves: 2.5x slower core)
 constexpr int kWideCholWaves = 10;   // waves of the l > 32 Cholesky workgroup
-constexpr int kWideGroup = 16;       // lanes per Jacobi pair of the l > 32 core
+constexpr int kWideGroup = 8;        // lanes per Jacobi pair of the l > 32 core (8: blocks of 8 columns)
 
 // Diagonal block (LDS, stride ld) by one wave: lane (ra, cb) = (lane / 16,
 // lane % 16) keeps entries (ra + 4 i, cb), i < 4, of the block and of T (the
@@ -689,8 +691,8 @@ __device__ __forceinline__ void chol_inverse(const double* A, const double* Td, 
   }
 }
 
-// MODE 1: Cholesky and X = R^-1 on NW waves; MODE 2: the core, Jacobi pairs on
-// 16-lane groups of 10 waves (jacobi_blocks).
+// MODE 1: Cholesky and X = R^-1 on NW waves; MODE 2: the core on 10 waves, the
+// Jacobi pairs on GW-lane groups (jacobi_blocks with blocks of 64 / GW columns).
 template <int MODE, int NW, int GW>
 __global__ __launch_bounds__(64 * NW) void solve_wide_kernel(const double* __restrict__ gram, int l,
                                                                   float* __restrict__ Xinv, int r,
@@ -698,7 +700,7 @@ __global__ __launch_bounds__(64 * NW) void solve_wide_kernel(const double* __res
                                                                   float* __restrict__ sigma, double* __restrict__ stats,
                                                                   ObjectiveArgs obj) {
   constexpr int NB = kMaxL * kWideLd;
-  static_assert(MODE == 1 || (GW == 16 && NW == 10), "the wide core's block Jacobi: 10 waves, 16-lane pairs");
+  static_assert(MODE == 1 || ((GW == 16 || GW == 8) && NW == 10), "the wide core: 10 waves, 16- or 8-lane pairs");
   __shared__ double Rm[NB];
   __shared__ double Tm[MODE == 1 ? NB : 1];
   __shared__ double Td[kCNB * kCB * kCB];
@@ -730,7 +732,7 @@ __global__ __launch_bounds__(64 * NW) void solve_wide_kernel(const double* __res
   }
   __syncthreads();
   constexpr int RL = (kMaxL + GW - 1) / GW;
-  const int sweeps = jacobi_blocks<RL>(Kf, kWideLd, n, 40);
+  const int sweeps = jacobi_blocks<RL, 64 / GW>(Kf, kWideLd, n, 40);
   core_finish(Kf, kWideLd, l, n, ksc, Xinv, r, SB, SA, sigma, stats, obj, sweeps, norm2, order);
 }
 
@@ -1528,7 +1530,7 @@ SvdPlan make_svd_plan(int64_t d, int64_t k, int r, int oversample, bool exact) {
     per = round_up(cdiv(len, best_s), unit);
     return static_cast<int>(cdiv(len, per));
   };
-  const GemmShape nn = gemm_shape(false, p.nt, k), tn = gemm_shape(true, p.nt, k);
+  const GemmShape nn = gemm_shape(false, p.nt, d, k), tn = gemm_shape(true, p.nt, d, k);
   p.nn_row_blocks = static_cast<int>(cdiv(d, nn.tile));
   p.nn_splits = choose(p.nn_row_blocks, k, nn.unit, 0, p.nn_kper);
   p.tn_col_blocks = static_cast<int>(cdiv(k, tn.tile));
@@ -1743,8 +1745,8 @@ hipError_t run_lowrank(const float* E, const SvdPlan& pl, int q, const float* om
       LQ_LAUNCH("chol_inv", (solve_wide_kernel<1, kWideCholWaves, 16>), dim3(1), dim3(64 * kWideCholWaves), 0, ss,
                 gtotal, l, Xinv, r, SB, SA, sigma, stats, none);
     else
-      LQ_LAUNCH("core_svd", (solve_wide_kernel<2, (40 * kWideGroup + 63) / 64, kWideGroup>), dim3(1),
-                dim3(64 * ((40 * kWideGroup + 63) / 64)), 0, s, gtotal, l, Xinv, r, SB, SA, sigma, stats, obj);
+      LQ_LAUNCH("core_svd", (solve_wide_kernel<2, 10, kWideGroup>), dim3(1), dim3(640), 0, s, gtotal, l, Xinv, r, SB,
+                SA, sigma, stats, obj);
     if (ss != s) {
       if (serr == hipSuccess) serr = hipEventRecord(side->join, ss);
       joining = true;
