@@ -32,6 +32,23 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kBN = 128, kBK = 64;   // tiled kernel: output features and K per step
+// X A^T is formed as up to kMaxSplits partial products over K ranges.
+constexpr int kMaxSplits = 8;
+
+// The sum of the ks (1 <= ks <= kMaxSplits) partials p[0], p[stride], ... added in the
+// order q = 0, 1, ..., with every load issued before the first add (a load-add chain
+// would wait a full memory latency per partial): the loads are unconditional, those
+// past ks repeating partial ks - 1, and their values are dropped.
+__device__ __forceinline__ float sum_partials(const float* __restrict__ p, int64_t stride, int ks) {
+  float v[kMaxSplits];
+#pragma unroll
+  for (int q = 0; q < kMaxSplits; ++q) v[q] = p[(q < ks ? q : ks - 1) * stride];
+  float t = 0.f;
+#pragma unroll
+  for (int q = 0; q < kMaxSplits; ++q)
+    if (q < ks) t += v[q];
+  return t;
+}
 
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 
@@ -64,23 +81,50 @@ __device__ __forceinline__ int64_t xcd_tile(int64_t wg, int64_t total) {
 
 // Epilogue of the tiled kernels (kBM token rows, kThreads threads, waves of 64 x 64).
 // Element v of tile (mt, nt) is token m = .. + 4 lg + v, feature n = .. + li.  The
-// tile's rows of X A^T (the sum of the ks K-split partials, in split order) go to LDS
-// (Ts, kBM x r fp32 over the idle tile buffers).  The LoRA term T bf16(B)^T of a 16 x 16
-// tile is one fp32 MFMA (16x16x4) per 4 of r: lane L supplies T[m0 + L%16][p0 + L/16]
-// and bf16(B)[n0 + L%16][p0 + L/16].
+// LoRA operands go to LDS over the idle tile buffers, rows padded to r + 1 floats:
+// the tile's rows of X A^T (Ts, the sum of the ks K-split partials in split order)
+// and bf16(B) of its kBN features (Bs), with the loads of eight elements per thread
+// in flight at once.  The LoRA term T bf16(B)^T of a 16 x 16 tile is one fp32 MFMA
+// (16x16x4) per 4 of r: lane L supplies T[m0 + L%16][p0 + L/16] and
+// bf16(B)[n0 + L%16][p0 + L/16].
 template <int kBM, int kThreads>
 __device__ __forceinline__ void tile_epilogue(float* Ts, mfma_f4 (&acc)[4][4], int tid, int wm, int wn, int li,
                                               int lg, int64_t m0, int64_t n0, int64_t M, int64_t N,
                                               const float* __restrict__ T, int ks, const float* __restrict__ B,
                                               int r, float alpha, float* __restrict__ Y) {
+  const int rp = r + 1;
+  float* Bs = Ts + kBM * rp;
   if (T != nullptr) {
     __syncthreads();
-    for (int idx = tid; idx < kBM * r; idx += kThreads) {
-      const int i = idx / r, p = idx - i * r;
-      float t = 0.f;
-      if (m0 + i < M)
-        for (int q = 0; q < ks; ++q) t += T[(q * M + m0 + i) * r + p];
-      Ts[idx] = t;
+    for (int base = 0; base < kBM * r; base += 8 * kThreads) {
+      float v[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int idx = base + e * kThreads + tid, i = idx / r, p = idx - i * r;
+        const bool ok = idx < kBM * r && m0 + i < M;
+        const float t = sum_partials(T + (ok ? (m0 + i) * r + p : 0), M * r, ks);
+        v[e] = ok ? t : 0.f;
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int idx = base + e * kThreads + tid, i = idx / r, p = idx - i * r;
+        if (idx < kBM * r) Ts[i * rp + p] = v[e];
+      }
+    }
+    for (int base = 0; base < kBN * r; base += 8 * kThreads) {
+      float v[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int idx = base + e * kThreads + tid, i = idx / r, p = idx - i * r;
+        const bool ok = idx < kBN * r && n0 + i < N;
+        const float b = B[ok ? (n0 + i) * r + p : 0];
+        v[e] = ok ? static_cast<float>(static_cast<__bf16>(b)) : 0.f;
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int idx = base + e * kThreads + tid, i = idx / r, p = idx - i * r;
+        if (idx < kBN * r) Bs[i * rp + p] = v[e];
+      }
     }
     __syncthreads();
   }
@@ -94,11 +138,10 @@ __device__ __forceinline__ void tile_epilogue(float* Ts, mfma_f4 (&acc)[4][4], i
       const int tl = wm * 64 + mt * 16 + li;
       for (int p0 = 0; p0 < r; p0 += 4) {
         const int p = p0 + lg;
-        const float tv = p < r ? Ts[tl * r + p] : 0.f;
+        const float tv = p < r ? Ts[tl * rp + p] : 0.f;
 #pragma unroll
         for (int nt = 0; nt < 4; ++nt) {
-          const int64_t bn = nw + nt * 16 + li;
-          const float bv = (bn < N && p < r) ? static_cast<float>(static_cast<__bf16>(B[bn * r + p])) : 0.f;
+          const float bv = p < r ? Bs[(wn * 64 + nt * 16 + li) * rp + p] : 0.f;
           lora[nt] = __builtin_amdgcn_mfma_f32_16x16x4f32(tv, bv, lora[nt], 0, 0, 0);
         }
       }
@@ -221,7 +264,7 @@ __global__ __launch_bounds__(2 * kBM, kBM == 128 ? 2 : 1) void nf4_gemm_kernel(c
     __syncthreads();
   }
   if (kt < KT) compute(0);   // odd step count: the last step sits in buffer 0
-  static_assert(sizeof(lds) >= kBM * 64 * sizeof(float), "the T tile reuses the tile buffers");
+  static_assert(sizeof(lds) >= (kBM + kBN) * 65 * sizeof(float), "the LoRA operands (r <= 64) reuse the tile buffers");
   tile_epilogue<kBM, kThreads>(reinterpret_cast<float*>(lds), acc, tid, wm, wn, li, lg, m0, n0, M, N, T, ks, B, r,
                                alpha, Y);
 }
@@ -353,11 +396,7 @@ __global__ __launch_bounds__(NW * 64) void nf4_skinny_kernel(const __bf16* __res
   // the epilogue's LoRA operands, staged first so their loads overlap the main loop:
   // X A^T of every token (the ks K-split partials summed in order) and bf16(B)
   if (T != nullptr) {
-    for (int idx = tid; idx < M * r; idx += NW * 64) {
-      float t = 0.f;
-      for (int q = 0; q < ks; ++q) t += T[q * M * r + idx];
-      Ts[idx] = t;
-    }
+    for (int idx = tid; idx < M * r; idx += NW * 64) Ts[idx] = sum_partials(T + idx, M * r, ks);
     for (int idx = tid; idx < 16 * r; idx += NW * 64) {
       const int64_t n = n0 + idx / r < N ? n0 + idx / r : N - 1;
       Bs[idx] = static_cast<float>(static_cast<__bf16>(B[n * r + idx % r]));
@@ -446,8 +485,6 @@ __global__ __launch_bounds__(NW * 64) void nf4_skinny_kernel(const __bf16* __res
 
 }  // namespace
 
-// X A^T is formed as up to kMaxSplits partial products over K ranges.
-constexpr int kMaxSplits = 8;
 // Token rows per tiled-kernel workgroup: 256 (8 waves) halves the weight decode per
 // product and measured 12 % faster at 2048 x 4096 outputs; it is taken while its
 // tiles still give every CU a workgroup, else 128 (4 waves).
