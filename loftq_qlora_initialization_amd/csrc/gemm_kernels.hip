@@ -65,7 +65,7 @@ typedef float lvpair2 __attribute__((ext_vector_type(2)));
 // flight as long as a stored E's do.
 template <bool VEC>
 struct StoredE {
-  static constexpr bool kVirtual = false;
+  static constexpr bool kVirtual = false, kCoalesced = false;
   typedef float4 Raw4;
   struct Raw8 { float4 a, b; };
   const float* E;
@@ -86,7 +86,7 @@ struct StoredE {
 // dequant writes out).
 template <bool BF16>
 struct FormedE {
-  static constexpr bool kVirtual = true;
+  static constexpr bool kVirtual = true, kCoalesced = false;
   struct Raw4 {
     uint32_t w[BF16 ? 2 : 4];   // four weights (bf16 pairs or fp32)
     uint32_t cw;                // their two code bytes
@@ -159,6 +159,74 @@ __device__ __forceinline__ void fill_level_pairs(const Src& src, lvpair2* lvl2) 
   }
 }
 
+// E P's formed residual with full-line loads (bf16 weight, cols % 64 == 0).  The
+// matrix-core operand ties lane L to row L % 16, so a direct operand load reads
+// only 64 bytes of each of 16 rows per instruction (half a 128-byte line).  Here
+// a 16-row x 64-column piece (two K steps) is loaded with eight lanes per row
+// (two instructions of 8 rows x 128 bytes for W, one of 16 rows x 32 bytes for
+// the codes), passed through a per-wave LDS slot (stash), and read back in
+// operand order (unstash): lane (li, g) gets row li, columns 32 s + 8 g .. + 7
+// of K step s, exactly what fetch8 would have loaded, so decode, split and the
+// products are unchanged.  The block scale (one per row of the piece) is loaded
+// in operand order directly.  Each wave's slot is written and read by that wave
+// only; its LDS operations run in order, and the fences below keep the compiler
+// from moving them across one another.
+struct CoRaw {
+  uint4 w[2];   // W: half h holds row 8 h + (lane >> 3), columns 8 (lane & 7) .. + 7
+  uint2 c;      // codes of row lane >> 2, elements 16 (lane & 3) .. + 15
+  float a;      // the block scale of row lane & 15
+};
+constexpr int kCoSlot = 160;   // uint4 per 16-row piece: 128 of W, 32 of codes
+struct FormedCo : FormedE<true> {
+  static constexpr bool kCoalesced = true;
+  typedef CoRaw Raw8;
+  // rows row0 .. row0 + 15 (clamped to d), columns c0 .. c0 + 63 (c0 % 64 == 0;
+  // past the last column the piece repeats the last 64 columns, whose panel rows are zero)
+  __device__ __forceinline__ CoRaw fetch_co(int64_t row0, int64_t c0, int64_t d, int64_t k, int lane) const {
+    c0 = c0 < k - 64 ? c0 : k - 64;
+    const uint16_t* W = static_cast<const uint16_t*>(v.W);
+    CoRaw r;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      int64_t rr = row0 + 8 * h + (lane >> 3);
+      rr = rr < d ? rr : d - 1;
+      r.w[h] = *reinterpret_cast<const uint4*>(W + rr * k + c0 + 8 * (lane & 7));
+    }
+    int64_t rc = row0 + (lane >> 2);
+    rc = rc < d ? rc : d - 1;
+    r.c = *reinterpret_cast<const uint2*>(v.packed + ((rc * k + c0) >> 1) + 8 * (lane & 3));
+    int64_t ra = row0 + (lane & 15);
+    ra = ra < d ? ra : d - 1;
+    r.a = v.scale[(ra * k + c0) >> 6];
+    return r;
+  }
+  // W piece p of row q goes to 16-byte slot 8 q + (p ^ (q & 7)): conflict-free
+  // writes, and the 16 rows an operand read touches spread over the banks
+  __device__ __forceinline__ static void stash(const CoRaw& r, uint4* slot, int lane) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int q = 8 * h + (lane >> 3);
+      slot[8 * q + ((lane & 7) ^ (q & 7))] = r.w[h];
+    }
+    reinterpret_cast<uint2*>(slot + 128)[lane] = r.c;
+  }
+  __device__ __forceinline__ static FormedE<true>::Raw8 unstash(const uint4* slot, int lane, int s, float a) {
+    const int m = lane & 15, g = lane >> 4;
+    const uint4 w = slot[8 * m + ((4 * s + g) ^ (m & 7))];
+    FormedE<true>::Raw8 r;
+    r.w[0] = w.x; r.w[1] = w.y; r.w[2] = w.z; r.w[3] = w.w;
+    r.cw = reinterpret_cast<const uint32_t*>(slot + 128)[8 * m + 4 * s + g];
+    r.a = a;
+    return r;
+  }
+};
+// orders a wave's LDS writes before its reads of other lanes' data (and reads before later writes)
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 // ---------------------------------------------------------------------------
 // v_mfma_f32_16x16x32_bf16: lane L supplies A[L%16][8(L/16) + e] and
 // B[8(L/16) + e][L%16] (e = 0..7) and receives D[4(L/16) + v][L%16] in element v.
@@ -222,6 +290,7 @@ __global__ __launch_bounds__(64 * (Nn3Cfg<NT, RTV>::WR)) void gemm_nn3_kernel(
   static_assert(D % 2 == 0 && WR * 64 == 256, "ring parity and the 256-thread panel staging");
   __shared__ uint4 pan[2][256 * PPT];   // rounded up to whole rounds of 256 pieces (the excess never read)
   __shared__ lvpair2 lvl2[Src::kVirtual ? 256 : 1];
+  __shared__ uint4 co_lds[Src::kCoalesced ? WR * RT * kCoSlot : 1];
   fill_level_pairs(src, lvl2);            // the barrier before the first step covers it
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int g = lane >> 4, li = lane & 15;
@@ -246,6 +315,21 @@ __global__ __launch_bounds__(64 * (Nn3Cfg<NT, RTV>::WR)) void gemm_nn3_kernel(
 #pragma unroll
     for (int b = 0; b < NT; ++b) acc[a][b] = floatx4{0.f, 0.f, 0.f, 0.f};
   typename Src::Raw8 eb[D][RT];
+  float co_a[RT];   // the block scales of the piece in the LDS slot
+  // at an even step: the piece of this step and the next into the wave's LDS slot
+  auto co_stash = [&](int u) {
+    if constexpr (Src::kCoalesced) {
+      if ((u & 1) == 0) {
+        wave_lds_sync();   // the last piece's reads are issued before it is overwritten
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+          Src::stash(eb[u][rt], co_lds + (w * RT + rt) * kCoSlot, lane);
+          co_a[rt] = eb[u][rt].a;
+        }
+        wave_lds_sync();
+      }
+    }
+  };
   static_assert(PPT <= 3, "at most three panel pieces per thread");
   // Two register sets (a, b, c pieces each) of staged panel steps, as plain
   // variables: the pieces past PU (PU not a multiple of 256) load a duplicate of
@@ -269,10 +353,18 @@ __global__ __launch_bounds__(64 * (Nn3Cfg<NT, RTV>::WR)) void gemm_nn3_kernel(
     if constexpr (PPT > 2) pan[BUF][tid + 512] = pc##S;                                  \
   } while (0)
   auto load_e = [&](int u, int j) {
-    j = j < nsteps ? j : nsteps - 1;   // past the end: a harmless repeat of the last step
-    const int64_t c = kb + 32 * j + 8 * g;
+    if constexpr (Src::kCoalesced) {
+      if ((u & 1) == 0) {   // an even slot takes the piece of steps j and j + 1
+        j = j < nsteps ? j : nsteps - 2;
 #pragma unroll
-    for (int rt = 0; rt < RT; ++rt) eb[u][rt] = src.fetch8(erow[rt], c, k);
+        for (int rt = 0; rt < RT; ++rt) eb[u][rt] = src.fetch_co(row0 + rt * 16, kb + 32 * j, d, k, lane);
+      }
+    } else {
+      j = j < nsteps ? j : nsteps - 1;   // past the end: a harmless repeat of the last step
+      const int64_t c = kb + 32 * j + 8 * g;
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) eb[u][rt] = src.fetch8(erow[rt], c, k);
+    }
   };
   // step j from ring slot u and LDS buffer buf
   auto compute = [&](int u, int buf, int j) {
@@ -282,10 +374,14 @@ __global__ __launch_bounds__(64 * (Nn3Cfg<NT, RTV>::WR)) void gemm_nn3_kernel(
       bh[nt] = __builtin_bit_cast(bf16x8, pan[buf][(2 * nt) * 64 + lane]);
       bl[nt] = __builtin_bit_cast(bf16x8, pan[buf][(2 * nt + 1) * 64 + lane]);
     }
+    if constexpr (Src::kCoalesced) co_stash(u);
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
       float x[8];
-      src.decode8(eb[u][rt], x, lvl2);
+      if constexpr (Src::kCoalesced)
+        src.decode8(Src::unstash(co_lds + (w * RT + rt) * kCoSlot, lane, u & 1, co_a[rt]), x, lvl2);
+      else
+        src.decode8(eb[u][rt], x, lvl2);
       if constexpr (NORMS) {
         // the eight squares summed in fp32 (relative error below 2^-21), then in fp64
         const int64_t nv = rok[rt] ? k - (kb + 32 * j + 8 * g) : 0;   // valid columns of the eight
@@ -395,6 +491,7 @@ __global__ __launch_bounds__(64 * NndCfg<NT>::WR) void gemm_nnd_kernel(
   using C = NndCfg<NT>;
   constexpr int LP = 16 * NT, RT = C::RT, D = C::D, WR = C::WR, PU = C::PU;
   __shared__ lvpair2 lvl2[Src::kVirtual ? 256 : 1];
+  __shared__ uint4 co_lds[Src::kCoalesced ? WR * RT * kCoSlot : 1];
   if constexpr (Src::kVirtual) {
     fill_level_pairs(src, lvl2);
     __syncthreads();
@@ -423,11 +520,34 @@ __global__ __launch_bounds__(64 * NndCfg<NT>::WR) void gemm_nnd_kernel(
     for (int b = 0; b < NT; ++b) acc[a][b] = floatx4{0.f, 0.f, 0.f, 0.f};
   typename Src::Raw8 eb[D][RT];
   uint4 pb[D][NT][2];
-  auto load = [&](int u, int j) {
-    j = j < nsteps ? j : nsteps - 1;
-    const int64_t c = kb + 32 * j + 8 * g;
+  float co_a[RT];   // the block scales of the piece in the LDS slot (as in gemm_nn3_kernel)
+  auto co_stash = [&](int u) {
+    if constexpr (Src::kCoalesced) {
+      if ((u & 1) == 0) {
+        wave_lds_sync();
 #pragma unroll
-    for (int rt = 0; rt < RT; ++rt) eb[u][rt] = src.fetch8(erow[rt], c, k);
+        for (int rt = 0; rt < RT; ++rt) {
+          Src::stash(eb[u][rt], co_lds + (w * RT + rt) * kCoSlot, lane);
+          co_a[rt] = eb[u][rt].a;
+        }
+        wave_lds_sync();
+      }
+    }
+  };
+  auto load = [&](int u, int j) {
+    if constexpr (Src::kCoalesced) {
+      if ((u & 1) == 0) {
+        const int jj = j < nsteps ? j : nsteps - 2;
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) eb[u][rt] = src.fetch_co(row0 + rt * 16, kb + 32 * jj, d, k, lane);
+      }
+    } else {
+      const int jj = j < nsteps ? j : nsteps - 1;
+      const int64_t c = kb + 32 * jj + 8 * g;
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) eb[u][rt] = src.fetch8(erow[rt], c, k);
+    }
+    j = j < nsteps ? j : nsteps - 1;
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
@@ -440,10 +560,14 @@ __global__ __launch_bounds__(64 * NndCfg<NT>::WR) void gemm_nnd_kernel(
       bh[nt] = __builtin_bit_cast(bf16x8, pb[u][nt][0]);
       bl[nt] = __builtin_bit_cast(bf16x8, pb[u][nt][1]);
     }
+    co_stash(u);
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
       float x[8];
-      src.decode8(eb[u][rt], x, lvl2);
+      if constexpr (Src::kCoalesced)
+        src.decode8(Src::unstash(co_lds + (w * RT + rt) * kCoSlot, lane, u & 1, co_a[rt]), x, lvl2);
+      else
+        src.decode8(eb[u][rt], x, lvl2);
       if constexpr (NORMS) {
         const int64_t nv = rok[rt] ? k - (kb + 32 * j + 8 * g) : 0;
         float s8 = 0.f;
@@ -666,7 +790,9 @@ GemmShape shape_typed(bool transposed, int64_t d, int64_t k) {
 template <int NT, typename Src>
 void gemm_launch(bool transposed, const Src& src, int64_t d, int64_t k, const uint16_t* panel, const SvdPlan& pl,
                  float* part, const CholJob& job, hipStream_t s, double* nparts) {
-  if (transposed) {
+  if constexpr (Src::kCoalesced) {
+    if (transposed) return;   // never asked: gemm_typed takes this source for E P only
+  } else if (transposed) {
     constexpr int threads = 64 * Tn3Cfg<NT>::WC * Tn3Cfg<NT>::WR;
     const dim3 grid(pl.tn_col_blocks + (job.parts != nullptr ? 1 : 0), pl.tn_splits);
 #define LQ_TN3(LMJ)                                                                                                   \
@@ -712,7 +838,9 @@ void gemm_typed(bool transposed, const float* E, int64_t d, int64_t k, const uin
                 float* part, const CholJob& job, hipStream_t s, const VirtualE* ve, double* np) {
   const bool vec = (k & 3) == 0 && k >= 4;
   const bool vec8 = vec && k >= 8;
-  if (ve != nullptr && ve->w_bf16) gemm_launch<NT>(transposed, FormedE<true>{*ve}, d, k, panel, pl, part, job, s, np);
+  if (ve != nullptr && ve->w_bf16 && !transposed && k % 64 == 0)
+    gemm_launch<NT>(false, FormedCo{FormedE<true>{*ve}}, d, k, panel, pl, part, job, s, np);
+  else if (ve != nullptr && ve->w_bf16) gemm_launch<NT>(transposed, FormedE<true>{*ve}, d, k, panel, pl, part, job, s, np);
   else if (ve != nullptr) gemm_launch<NT>(transposed, FormedE<false>{*ve}, d, k, panel, pl, part, job, s, np);
   else if (vec8) gemm_launch<NT>(transposed, StoredE<true>{E}, d, k, panel, pl, part, job, s, np);
   else gemm_launch<NT>(transposed, StoredE<false>{E}, d, k, panel, pl, part, job, s, np);

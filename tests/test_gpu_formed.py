@@ -5,8 +5,9 @@ The element arithmetic is the dequant's own, fl32(w - fl32(level[code] a')), so 
 give the same initialisation bit for bit: every output of loftq_init is compared exactly.
 Cases: the 24-wide and 80-wide sketches, double quant on and off, bf16 and fp32 W, a
 column count that is a multiple of 8 but not of 64 (blocks straddle rows), one that
-falls back to the stored E, 2-bit codes,
-and the batched call.
+falls back to the stored E, 2-bit codes, ragged row tiles with a split past the last
+column and a wide matrix whose E P stages its panel in LDS (both with the full-line
+loads E P uses when cols % 64 == 0), and the batched call.
 """
 import numpy as np
 import pytest
@@ -40,6 +41,8 @@ def _same(a, b):
     (640, 264, "bf16", 4, 4, 2, 1, 2, 4),        # 264 columns: 64-blocks straddle rows
     (640, 260, "bf16", 4, 4, 2, 1, 2, 4),        # 260 columns: E is stored either way (cols % 8 != 0)
     (512, 384, "bf16", 16, 8, 1, 1, 2, 2),       # 2-bit codes
+    (1000, 704, "bf16", 16, 8, 2, 1, 2, 4),      # ragged row tiles; the last split runs past the last column
+    (200, 8256, "bf16", 16, 8, 1, 1, 2, 4),      # l = 24 with a panel over 1 MiB (LDS-staged E P)
 ])
 def test_formed_residual_matches_stored(lib, rows, cols, dtype, r, p, q, dq, T, bits):
     W = _weight(rows, cols, dtype, rows + cols)
