@@ -282,7 +282,7 @@ struct Tn3Cfg {
 // those sums in fp64) and writes the sum to nparts[workgroup tile]; in a fixed
 // order, so the partials are deterministic.
 template <int NT, typename Src, bool NORMS, int RTV>
-__global__ __launch_bounds__(64 * (Nn3Cfg<NT, RTV>::WR)) void gemm_nn3_kernel(
+__global__ __launch_bounds__(64 * (Nn3Cfg<NT, RTV>::WR)) __attribute__((amdgpu_waves_per_eu(RTV == 1 && NT <= 2 ? 4 : 2))) void gemm_nn3_kernel(
     Src src, int64_t d, int64_t k, const uint16_t* __restrict__ Xs, int64_t kper,
     float* __restrict__ part, double* __restrict__ nparts) {
   using C = Nn3Cfg<NT, RTV>;
