@@ -51,6 +51,12 @@ MEASURED_TRAFFIC = {
         "gemm_nn": {"bytes": 87319733, "source": "gemm_kernels.hip", "sha256": "7d0a06e7b41d82fe"},
         "gemm_tn": {"bytes": 82502846, "source": "gemm_kernels.hip", "sha256": "7d0a06e7b41d82fe"},
     },
+    # the extras of the decoder batch run on its first matrix (layer 0's q projection, 4096 x 4096,
+    # r = 16): the QLoRA forward, 2048 tokens (tiled kernel) and 16 tokens (few-token kernel)
+    "c4_l0_q_4096x4096_bf16": {
+        "nf4_gemm": {"bytes": 123018591, "source": "forward_kernels.hip", "sha256": "816be8351946cd3b"},
+        "nf4_gemm_skinny": {"bytes": 10414080, "source": "forward_kernels.hip", "sha256": "816be8351946cd3b"},
+    },
     "c2_4096x4096_bf16": {
         "gemm_nn": {"bytes": 77784775, "source": "gemm_kernels.hip", "sha256": "4322c77aea1b6c85"},
         "gemm_tn": {"bytes": 75687250, "source": "gemm_kernels.hip", "sha256": "4322c77aea1b6c85"},
@@ -66,6 +72,9 @@ MEASURED_TRAFFIC = {
 # non-packed VALU peak (256 CUs x 4 SIMDs x 2.4 GHz / 4 cycles per wave64 op).
 VALU_PEAK_GWIS = 256 * 4 * 2.4 / 4
 MEASURED_VALU = {
+    "c4_l0_q_4096x4096_bf16": {
+        "nf4_merge": {"valu": 6362099, "source": "quant_kernels.hip", "sha256": "2b26247299f66d83"},
+    },
     "c2_4096x4096_bf16": {
         "nf4_merge": {"valu": 5250600, "source": "quant_kernels.hip", "sha256": "471627fbeb92a6bd"},
     },
