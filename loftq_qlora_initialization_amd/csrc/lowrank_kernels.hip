@@ -443,11 +443,11 @@ __device__ void core_finish(const float* K, int ld, int l, int n, double ksc, co
   else if (tid == 0 && obj.out != nullptr) objective_from_sums(obj, objsums[0], objsums[1], s2);
 }
 
-// mode 2 for l <= LM (LM <= 32), 16 lanes per pair: 16 ceil(l / 2) threads
-// rounded up to whole waves.  The workgroup sums the P Gram partials of C
-// (gram_sum_block), wave 0 factors H in fp64 and writes K = 2^-e R^T while
-// wave 1 (wave 0 afterwards when it is alone) sums the |E|^2 and |W|^2
-// partials of the objective.
+// mode 2 for l <= LM (LM <= 32), 16 lanes per pair, by 256 threads: the four
+// waves sum the P Gram partials of C (gram_sum_block, 16 partials in flight per
+// wave), wave 0 factors H in fp64 and writes K = 2^-e R^T while wave 1 sums the
+// |E|^2 and |W|^2 partials of the objective; the sweeps use the first
+// ceil(l / 8) waves.
 template <int LM>
 __global__ __launch_bounds__(256) void core_small_kernel(const double* __restrict__ gparts, int P, int l,
                                                          const float* __restrict__ Xinv, int r, float* __restrict__ SB,
@@ -465,7 +465,7 @@ __global__ __launch_bounds__(256) void core_small_kernel(const double* __restric
   const int tid = threadIdx.x;
   const int n = l + (l & 1);
   for (int e = tid; e < l * l; e += blockDim.x) Xs[e] = Xinv[e];
-  const double* gram = gram_sum_block<LM>(gparts, P, l, gsum);
+  const double* gram = gram_sum_block<LM, 16>(gparts, P, l, gsum);
   const int sum_wave = blockDim.x > 64 ? 1 : 0;
   if (obj.out != nullptr && sum_wave == 1 && (tid >> 6) == 1) {
     const double es = wave_sum_fixed(obj.e_parts, obj.ne), ws = wave_sum_fixed(obj.w_parts, obj.nw);
@@ -1453,7 +1453,7 @@ void small_wave_typed(int mode, const double* gram, const double* gparts, int P,
   if (mode == 1)
     LQ_LAUNCH("chol_inv", chol_inv_wave_kernel<LM>, dim3(1), dim3(64), 0, s, gram, l, Xinv);
   else
-    LQ_LAUNCH("core_svd", core_small_kernel<LM>, dim3(1), dim3(static_cast<unsigned>(round_up(16 * ((l + 1) / 2), 64))), 0,
+    LQ_LAUNCH("core_svd", core_small_kernel<LM>, dim3(1), dim3(256), 0,
               s, gparts, P, l, Xinv, r, SB, SA, sigma, stats, obj);
 }
 

@@ -87,10 +87,11 @@ __device__ __forceinline__ void chol_wave(const double* __restrict__ gram, int l
 // Sum of the P fp64 Gram partials (packed upper triangles of E_ = l (l + 1) / 2
 // entries, partial p at parts + p E_) by one workgroup of NW = blockDim / 64
 // waves.  Wave w sums partials w, w + NW, w + 2 NW, ... of each entry in that
-// order; the NW wave sums are then added in wave order, so the total is
-// deterministic.  lds holds at least (NW + 1) E_ doubles; returns the address
-// of the total (lds + NW E_).
-template <int LM>
+// order, QB partials' loads in flight at a time; the NW wave sums are then
+// added in wave order, so the total is deterministic (and independent of QB).
+// lds holds at least (NW + 1) E_ doubles; returns the address of the total
+// (lds + NW E_).
+template <int LM, int QB = 8>
 __device__ __forceinline__ double* gram_sum_block(const double* __restrict__ parts, int P, int l, double* lds) {
   constexpr int EPL = (LM * (LM + 1) / 2 + 63) / 64;
   const int E_ = l * (l + 1) / 2;
@@ -99,17 +100,17 @@ __device__ __forceinline__ double* gram_sum_block(const double* __restrict__ par
   double s[EPL];
 #pragma unroll
   for (int i = 0; i < EPL; ++i) s[i] = 0.0;
-  for (int p = w; p < P; p += 8 * NW) {
-    double v[8][EPL];
+  for (int p = w; p < P; p += QB * NW) {
+    double v[QB][EPL];
 #pragma unroll
-    for (int q = 0; q < 8; ++q)
+    for (int q = 0; q < QB; ++q)
 #pragma unroll
       for (int i = 0; i < EPL; ++i) {
         const int pp = p + NW * q, e = lane + 64 * i;
         v[q][i] = (pp < P && e < E_) ? parts[static_cast<int64_t>(pp) * E_ + e] : 0.0;
       }
 #pragma unroll
-    for (int q = 0; q < 8; ++q)
+    for (int q = 0; q < QB; ++q)
 #pragma unroll
       for (int i = 0; i < EPL; ++i) s[i] += v[q][i];
   }
