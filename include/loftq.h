@@ -276,10 +276,12 @@ typedef struct {
  * LoRA config targets, all-linear advised; the LoftQ blog, §3.2, targets the
  * q/k/v/o/gate/up/down projections).  Each matrix gets exactly the results of
  * loftq_init with the same cfg (the same kernels; bit for bit).  The matrices
- * are spread over nstreams streams, longest first, each to the stream with the
- * least work so far; a stream runs its matrices one after another in its own
- * workspace, so one matrix's single-workgroup solves overlap another's streaming
- * kernels.  Nothing is synchronised: outputs are valid once every stream is.
+ * are spread over nstreams streams in an order that mixes large and small ones
+ * (sorted by size, one from the large end and two from the small end in turn),
+ * each to the stream with the least work so far; a stream runs its matrices one
+ * after another in its own workspace, so one matrix's single-workgroup solves
+ * overlap another's streaming kernels.  Nothing is synchronised: outputs are
+ * valid once every stream is.
  *   mats      [host] count matrices; their output buffers must not overlap each
  *             other (W may be shared)
  *   wdt       storage type of every W

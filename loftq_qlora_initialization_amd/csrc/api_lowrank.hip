@@ -285,14 +285,23 @@ loftq_status_t loftq_init_batch(const loftq_matrix_t* mats, int32_t count, loftq
       if (st != LOFTQ_OK) return st;
     }
   }
-  // longest-processing-time first: matrices by descending element count (ties by index), each to
-  // the stream with the least work so far; the enqueue order follows that list, so the streams
-  // are fed in turn and all start at once
-  std::vector<int32_t> order(count);
-  for (int32_t i = 0; i < count; ++i) order[i] = i;
-  std::stable_sort(order.begin(), order.end(), [&](int32_t x, int32_t y) {
+  // Enqueue order: the matrices sorted by descending element count (ties by index), taken one from
+  // the front and two from the back in turn, each to the stream with the least work so far (the
+  // streams are fed in turn and all start at once).  The products re-read W and the codes six times
+  // per alternation, so the matrices in flight at one time share the 256 MB Infinity Cache; a mix of
+  // large and small ones keeps more of their bytes there than the largest side by side, as a plain
+  // longest-first order would run them (decoder batch, 3 streams: 178.1 -> 170.1 ms).
+  std::vector<int32_t> sorted(count);
+  for (int32_t i = 0; i < count; ++i) sorted[i] = i;
+  std::stable_sort(sorted.begin(), sorted.end(), [&](int32_t x, int32_t y) {
     return mats[x].rows * mats[x].cols > mats[y].rows * mats[y].cols;
   });
+  std::vector<int32_t> order;
+  order.reserve(count);
+  for (int32_t lo = 0, hi = count - 1; lo <= hi;) {
+    order.push_back(sorted[lo++]);
+    for (int t = 0; t < 2 && lo <= hi; ++t) order.push_back(sorted[hi--]);
+  }
   std::vector<int64_t> load(nstreams, 0);
   for (int32_t idx : order) {
     int32_t j = 0;
