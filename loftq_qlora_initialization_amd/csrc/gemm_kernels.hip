@@ -15,9 +15,10 @@
 // (e = 0..7) <-> row split_row(s, g, e) of the panel (its split layout,
 // split_index: row 32 s + 8 g + e for E P's operand; the rows of each pair of
 // steps interleaved for E^T Y's), and E is loaded to match: gemm_nn reads 8
-// consecutive columns of a row per lane, gemm_tn 4 columns of 8 rows.  E is split in registers as it arrives; the panel
-// comes already split (split_index), written so by the split-K reduction that
-// produces it.
+// consecutive columns of a row per lane (with a bf16 weight and cols % 64 == 0
+// whole 128-byte lines, reordered through LDS: FormedCo), gemm_tn 4 columns of
+// 8 rows.  E is split in registers as it arrives; the panel comes already split
+// (split_index), written so by the split-K reduction that produces it.
 //
 // Out-of-range rows/columns of E are clamped to valid addresses rather than
 // branched around: the matching rows of the skinny operand are zero (its
@@ -281,8 +282,12 @@ struct Tn3Cfg {
 // exactly once: clamped rows and columns are left out; eight at a time in fp32,
 // those sums in fp64) and writes the sum to nparts[workgroup tile]; in a fixed
 // order, so the partials are deterministic.
+// The waves-per-EU hint keeps two waves per SIMD for the wide panels and two row
+// tiles (at l = 80 the variant with the norm sums otherwise needs 268 registers)
+// and four for one row tile at l <= 32.
 template <int NT, typename Src, bool NORMS, int RTV>
-__global__ __launch_bounds__(64 * (Nn3Cfg<NT, RTV>::WR)) __attribute__((amdgpu_waves_per_eu(RTV == 1 && NT <= 2 ? 4 : 2))) void gemm_nn3_kernel(
+__global__ __launch_bounds__(64 * (Nn3Cfg<NT, RTV>::WR))
+__attribute__((amdgpu_waves_per_eu(RTV == 1 && NT <= 2 ? 4 : 2))) void gemm_nn3_kernel(
     Src src, int64_t d, int64_t k, const uint16_t* __restrict__ Xs, int64_t kper,
     float* __restrict__ part, double* __restrict__ nparts) {
   using C = Nn3Cfg<NT, RTV>;
