@@ -298,6 +298,18 @@ __device__ __forceinline__ bool jacobi_rotate(float (&xp)[RL], float (&xq)[RL], 
   return g2 > 1e-8f * ab;
 }
 
+// A value of the lane in the same position of the wave's other 16-lane row of its
+// pair (row XOR 1) or half (row XOR 2): v_permlane16_swap / v_permlane32_swap with
+// the value as both operands return the even and the odd row's (half's) copy.
+__device__ __forceinline__ float rows_xor1(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(((threadIdx.x >> 4) & 1) ? r[0] : r[1]);
+}
+__device__ __forceinline__ float rows_xor2(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(((threadIdx.x >> 5) & 1) ? r[0] : r[1]);
+}
+
 // One-sided Jacobi sweeps on the columns of K (fp32, LDS, column stride
 // ld > GL RL with GL = 64 / BW lanes per column; rows GL RL and beyond the
 // matrix are zero), a column pair per GL-lane group (lane sub holds rows
@@ -307,7 +319,8 @@ __device__ __forceinline__ bool jacobi_rotate(float (&xp)[RL], float (&xq)[RL], 
 // rho wave w holds blocks rr_player(w, rho, nbk) and rr_player(nbk - 1 - w, rho,
 // nbk); its lane group g keeps column g of the first block in registers and in
 // sub-round j (j < BW) rotates it against column (g + j) mod BW of the second,
-// which passes from group to group through LDS within the wave.  Block round 0
+// which passes from group to group through LDS within the wave (BW = 4: column
+// g ^ j, passed on by lane-row swaps, the groups being the wave's 16-lane rows).  Block round 0
 // first runs the pairs inside each of the wave's two blocks (round-robin of BW,
 // BW - 1 sub-rounds; its first sub-round meets every column and forms all three
 // dot products, later sub-rounds form gamma only).  A sweep is BW - 1 + BW (nbk - 1)
@@ -370,21 +383,50 @@ __device__ int jacobi_blocks(float* K, int ld, int n, int max_sweeps) {
 #pragma unroll
         for (int i = 0; i < RL; ++i) xa[i] = ca[GL * i];
         const bool a_low = ba < bb;
-#pragma unroll
-        for (int j = 0; j < BW; ++j) {
-          float* cb = Ks + (bb * BW + (g + j) % BW) * ld;
-          float be = cb[GL * RL - sub], ga = 0.f;
+        if constexpr (BW == 4) {
+          // the lane groups are the wave's four 16-lane rows: in sub-round j group g
+          // meets column g ^ j of the second block, which the rows pass on between
+          // sub-rounds with lane-row swaps (XOR 1, 3, 1) instead of through LDS
+          float* cb = Ks + (bb * BW + g) * ld;
+          float be = cb[GL * RL - sub];
 #pragma unroll
           for (int i = 0; i < RL; ++i) xb[i] = cb[GL * i];
 #pragma unroll
-          for (int i = 0; i < RL; ++i) ga = fmaf(xa[i], xb[i], ga);
-          ga = group_sumf<GL>(ga);
-          const bool coupled = a_low ? jacobi_rotate<RL>(xa, xb, al, be, ga) : jacobi_rotate<RL>(xb, xa, be, al, ga);
-          big |= __builtin_amdgcn_ballot_w64(coupled);
+          for (int j = 0; j < BW; ++j) {
+            if (j > 0) {
 #pragma unroll
-          for (int i = 0; i < RL; ++i) cb[GL * i] = xb[i];
-          cb[GL * RL - sub] = be;
-          __builtin_amdgcn_wave_barrier();
+              for (int i = 0; i < RL; ++i) xb[i] = j == 2 ? rows_xor2(rows_xor1(xb[i])) : rows_xor1(xb[i]);
+              be = j == 2 ? rows_xor2(rows_xor1(be)) : rows_xor1(be);
+            }
+            float ga = 0.f;
+#pragma unroll
+            for (int i = 0; i < RL; ++i) ga = fmaf(xa[i], xb[i], ga);
+            ga = group_sumf<GL>(ga);
+            const bool coupled = a_low ? jacobi_rotate<RL>(xa, xb, al, be, ga) : jacobi_rotate<RL>(xb, xa, be, al, ga);
+            big |= __builtin_amdgcn_ballot_w64(coupled);
+          }
+          // after the last sub-round group g holds column g ^ 3
+          float* ce = Ks + (bb * BW + (g ^ 3)) * ld;
+#pragma unroll
+          for (int i = 0; i < RL; ++i) ce[GL * i] = xb[i];
+          ce[GL * RL - sub] = be;
+        } else {
+#pragma unroll
+          for (int j = 0; j < BW; ++j) {
+            float* cb = Ks + (bb * BW + (g + j) % BW) * ld;
+            float be = cb[GL * RL - sub], ga = 0.f;
+#pragma unroll
+            for (int i = 0; i < RL; ++i) xb[i] = cb[GL * i];
+#pragma unroll
+            for (int i = 0; i < RL; ++i) ga = fmaf(xa[i], xb[i], ga);
+            ga = group_sumf<GL>(ga);
+            const bool coupled = a_low ? jacobi_rotate<RL>(xa, xb, al, be, ga) : jacobi_rotate<RL>(xb, xa, be, al, ga);
+            big |= __builtin_amdgcn_ballot_w64(coupled);
+#pragma unroll
+            for (int i = 0; i < RL; ++i) cb[GL * i] = xb[i];
+            cb[GL * RL - sub] = be;
+            __builtin_amdgcn_wave_barrier();
+          }
         }
 #pragma unroll
         for (int i = 0; i < RL; ++i) ca[GL * i] = xa[i];
