@@ -82,3 +82,24 @@ def test_batch_matrices_against_oracle(lib):
         check_groups(out, W, w, groups, prev["B"], prev["A"])
         assert out["objective"][-1] < out["objective"][0]
         check_last_svd(lib, out, W, w)
+
+
+@pytest.mark.timeout(300)
+def test_batch_of_mixed_shapes_equals_single_inits(lib):
+    """Five shapes in one call on 3 streams, so the size-mixing enqueue order spreads distinct
+    sizes: ragged row tiles, a wide short matrix, a column count that is a multiple of 8 but not
+    of 64 (E P's direct operand loads instead of the full-line ones) and one that is not a
+    multiple of 8 (E stored by the dequant).  Every matrix gets loftq_init's results bit for bit."""
+    shapes = [(700, 512), (640, 264), (256, 260), (1024, 768), (96, 4096)]
+    specs = [synth.Workload(f"mixed_{r}x{c}", r, c, "bf16", 8, 2, True, 8, 1, False, 300 + i, "outliers")
+             for i, (r, c) in enumerate(shapes)]
+    Ws = _weights(specs)
+    cfg = _cfg(lib, specs[0])
+    outs = [_host(b) for b in lib.loftq_init_batch(Ws, cfg, nstreams=3)]
+    for w, W, got in zip(specs, Ws, outs):
+        bufs = lib.InitBuffers(w.rows, w.cols, cfg)
+        lib.loftq_init(W, cfg, buffers=bufs)
+        ref = _host(bufs)
+        for k in KEYS:
+            assert np.array_equal(got[k], ref[k]), (w.name, k)
+        assert got["objective"][-1] <= got["objective"][0], w.name
